@@ -1,0 +1,398 @@
+"""CPU oracle for the per-layer GNN message-passing path.
+
+TEST INFRASTRUCTURE.  Only the tests (``tests/``), the smoke check
+(``__graft_entry__.smoke``) and the CPU-baseline leg of ``bench.py`` may
+import this package.  The library never imports it, and it imports nothing
+from the library: the two share no code.  The seeded generators in
+``sparse_message_passing_amd.synth`` are the only common input source, and
+they hold no method arithmetic.
+
+Layout
+  * ``oracle.c``  -- per-element arithmetic in plain C (double accumulation,
+    binary32 where the method fixes it), compiled with gcc into
+    ``oracle/_build/liboracle.so``.
+  * ``graph.py``  -- graph construction and GCN normalisation in numpy.
+  * this file     -- ctypes bindings, store-point rounding, dense products
+    (numpy ``@`` in float64 as the library routine) and the layer
+    compositions (GCN, GAT, loss, quantised exchange).
+
+Store points: every intermediate the method materialises is rounded to its
+storage type exactly where the GPU path stores it (binary32, or bfloat16
+round-to-nearest-even for the bf16 feature-storage mode); all sums in
+between are carried in float64.
+
+Parity-unpinned parts are listed in ``UNPINNED``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+from .graph import OracleGraph, build_graph  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "_build", "liboracle.so")
+
+# Functions without an independent pin (the oracle's own definition is the only reference).
+UNPINNED = {
+    "philox4x32_10": "exact output stream not pinned to published known-answer vectors "
+                     "(none available offline); pinned only statistically and by bijectivity",
+}
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (no fast-math, no contraction)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(os.path.join(_HERE, "oracle.c")):
+        os.makedirs(os.path.dirname(_SO), exist_ok=True)
+        tmp = _SO + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+                        "-shared", "-fPIC", os.path.join(_HERE, "oracle.c"), "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = C.CDLL(_SO)
+        P, I64, I32, F32, U64, U32 = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_uint64, C.c_uint32
+        sigs = {
+            "orc_spmm": [I64, P, P, P, I32, P, I64, I64, P],
+            "orc_spmm_t": [I64, P, P, P, I32, P, I64, I64, P],
+            "orc_sddmm_dot": [I64, P, P, P, I64, P, I64, I32, I64, P],
+            "orc_edge_softmax": [I64, P, P, I32, P],
+            "orc_edge_softmax_bwd": [I64, P, P, P, I32, P],
+            "orc_edge_reduce_dst": [I64, P, P, I32, P],
+            "orc_edge_reduce_src": [I64, P, P, P, I32, P],
+            "orc_philox4x32_10": [P, P, P],
+            "orc_philox_uniforms": [U64, U32, P, I64, I64, P],
+            "orc_quantize": [P, I64, I64, P, I64, I32, U64, U32, P, P, P],
+            "orc_dequantize": [P, P, P, I64, I64, I32, P, P, I64],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+# ---------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------
+def to_f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def to_bf16(x):
+    """Round to bfloat16 (round-to-nearest-even) through binary32; returns
+    float32 values that are exactly representable in bfloat16."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def store(x, dt):
+    """Round to the storage type: "f32", "bf16", or "f64" (no rounding; used
+    only by the finite-difference pins)."""
+    if dt == "f64":
+        return np.asarray(x, dtype=np.float64)
+    return to_bf16(x) if dt == "bf16" else to_f32(x)
+
+
+# ---------------------------------------------------------------------------
+# primitives (float64 results unless the step is fixed in binary32)
+# ---------------------------------------------------------------------------
+def spmm(g: OracleGraph, X, w=None, heads=1, transpose=False):
+    X = _c(X, np.float64)
+    n, d = g.n, X.shape[1]
+    if X.shape[0] != n:
+        raise ValueError("X rows != n")
+    wa = None if w is None else _c(w, np.float64)
+    Y = np.empty((n, d), dtype=np.float64)
+    fn = lib().orc_spmm_t if transpose else lib().orc_spmm
+    fn(n, _p(g.row_ptr), _p(g.col), _p(wa), heads, _p(X), d, d, _p(Y))
+    return Y
+
+
+def spmm_mag(g, X, w=None, heads=1, transpose=False):
+    """Sum of |terms| of each output entry (the scale of its rounding error)."""
+    return spmm(g, np.abs(X), None if w is None else np.abs(w), heads, transpose)
+
+
+def sddmm_add(g, S, D, slope):
+    """Tango, GAT running example, SDDMM with (+) = addition, then LeakyReLU:
+    E_pre[e, k] = S[src, k] + D[dst, k];  E = E_pre if E_pre > 0 else slope * E_pre.
+    One add and one multiply in the inputs' precision (IEEE binary32 for
+    binary32 inputs, so the result is exact to the bit)."""
+    S = np.asarray(S)
+    D = np.asarray(D)
+    E_pre = S[g.col] + D[g.dst]
+    E = np.where(E_pre > 0, E_pre, E_pre.dtype.type(slope) * E_pre)
+    return E_pre, E
+
+
+def sddmm_dot(g, A_dst, B_src, heads):
+    A = _c(A_dst, np.float64)
+    B = _c(B_src, np.float64)
+    dh = A.shape[1] // heads
+    out = np.empty((g.nnz, heads), dtype=np.float64)
+    lib().orc_sddmm_dot(g.n, _p(g.row_ptr), _p(g.col), _p(A), A.shape[1], _p(B), B.shape[1], heads, dh, _p(out))
+    return out
+
+
+def edge_softmax(g, E):
+    E = _c(E, np.float64)
+    h = E.shape[1]
+    a = np.empty((g.nnz, h), dtype=np.float64)
+    lib().orc_edge_softmax(g.n, _p(g.row_ptr), _p(E), h, _p(a))
+    return a
+
+
+def edge_softmax_bwd(g, alpha, dalpha):
+    alpha = _c(alpha, np.float64)
+    dalpha = _c(dalpha, np.float64)
+    h = alpha.shape[1]
+    dE = np.empty((g.nnz, h), dtype=np.float64)
+    lib().orc_edge_softmax_bwd(g.n, _p(g.row_ptr), _p(alpha), _p(dalpha), h, _p(dE))
+    return dE
+
+
+def edge_reduce(g, vals, by_src=False):
+    vals = _c(vals, np.float64)
+    h = vals.shape[1]
+    out = np.empty((g.n, h), dtype=np.float64)
+    if by_src:
+        lib().orc_edge_reduce_src(g.n, _p(g.row_ptr), _p(g.col), _p(vals), h, _p(out))
+    else:
+        lib().orc_edge_reduce_dst(g.n, _p(g.row_ptr), _p(vals), h, _p(out))
+    return out
+
+
+def gemm(A, B, transA=False, transB=False):
+    """op(A) @ op(B) in float64 (numpy matmul as the library routine)."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    return (A.T if transA else A) @ (B.T if transB else B)
+
+
+def softmax_xent(z, labels):
+    """Mean softmax cross-entropy over all rows and its gradient:
+    loss = (1/N) sum_v [logsumexp(z_v) - z_v[y_v]],  dz = (softmax(z) - onehot(y)) / N."""
+    z = np.asarray(z, dtype=np.float64)
+    n, c = z.shape
+    m = z.max(axis=1, keepdims=True)
+    ez = np.exp(z - m)
+    s = ez.sum(axis=1, keepdims=True)
+    lse = (m + np.log(s))[:, 0]
+    loss = float(np.mean(lse - z[np.arange(n), labels]))
+    dz = ez / s
+    dz[np.arange(n), labels] -= 1.0
+    return loss, dz / n
+
+
+def philox4x32_10(ctr, key):
+    c = np.asarray(ctr, dtype=np.uint32)
+    k = np.asarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def philox_uniforms(seed, stream, nodes, d):
+    nodes = _c(nodes, np.int32)
+    u = np.empty((nodes.size, d), dtype=np.float32)
+    lib().orc_philox_uniforms(int(seed), int(stream), _p(nodes), nodes.size, d, _p(u))
+    return u
+
+
+def quantize(H, rows, bits, seed, stream=0):
+    H = _c(H, np.float32)
+    rows = _c(rows, np.int32)
+    n_rows, d = rows.size, H.shape[1]
+    if bits not in (2, 4, 8) or (d * bits) % 8:
+        raise ValueError("bits must be 2, 4 or 8 and d*bits a multiple of 8")
+    packed = np.empty((n_rows, d * bits // 8), dtype=np.uint8)
+    scale = np.empty(n_rows, dtype=np.float32)
+    zero = np.empty(n_rows, dtype=np.float32)
+    lib().orc_quantize(_p(H), d, d, _p(rows), n_rows, bits, int(seed), int(stream),
+                       _p(packed), _p(scale), _p(zero))
+    return packed, scale, zero
+
+
+def dequantize(packed, scale, zero, rows, d, bits, H_out):
+    """Writes the dequantised rows into H_out (float32 [n, d]) in place."""
+    packed = _c(packed, np.uint8)
+    scale = _c(scale, np.float32)
+    zero = _c(zero, np.float32)
+    rows = _c(rows, np.int32)
+    assert H_out.dtype == np.float32 and H_out.flags.c_contiguous
+    lib().orc_dequantize(_p(packed), _p(scale), _p(zero), rows.size, d, bits, _p(rows), _p(H_out), H_out.shape[1])
+    return H_out
+
+
+def unpack_codes(packed, d, bits):
+    """Codes [n_rows, d] from the packed layout (test helper)."""
+    per = 8 // bits
+    j = np.arange(d)
+    b = packed[:, j // per].astype(np.uint32)
+    return (b >> ((j % per) * bits)) & ((1 << bits) - 1)
+
+
+# ---------------------------------------------------------------------------
+# GCN layer.  AdaQP Eqn. 3 / Sancus Sec. 2: H(l+1) = sigma(A_hat H(l) W).
+# Operand order: the GEMM runs first iff d_out <= d_in (the product with the
+# narrower width is aggregated); otherwise the aggregation runs first.
+# ---------------------------------------------------------------------------
+def _wdt(dt):
+    """Weights, weight gradients, logits and the loss stay binary32 in every
+    storage mode (float64 only in the unrounded finite-difference mode)."""
+    return "f64" if dt == "f64" else "f32"
+
+
+def gcn_layer_fwd(g, X, W, relu, dt="f32", out_dt=None):
+    """Returns (Y, saved) where saved is A_hat X for the aggregate-first order."""
+    out_dt = dt if out_dt is None else out_dt
+    _, w = g.gcn_norm()
+    d_in, d_out = W.shape
+    if d_out <= d_in:
+        Z = store(gemm(X, W), dt)
+        A = spmm(g, Z, w)
+        Y = store(np.maximum(A, 0.0) if relu else A, out_dt)
+        return Y, None
+    AX = store(spmm(g, X, w), dt)
+    P = gemm(AX, W)
+    Y = store(np.maximum(P, 0.0) if relu else P, out_dt)
+    return Y, AX
+
+
+def gcn_layer_bwd(g, X, saved, Y, dY, W, relu, need_dX=True, dt="f32"):
+    """Returns (dX or None, dW).  G = dY * [Y > 0] (ReLU'(0) = 0)."""
+    _, w = g.gcn_norm()
+    d_in, d_out = W.shape
+    # with ReLU the masked gradient is materialised in the storage type; without
+    # it the upstream gradient is consumed as it is
+    G = store(np.where(Y > 0, dY, 0.0), dt) if relu else np.asarray(dY)
+    if d_out <= d_in:
+        dZ = store(spmm(g, G, w), dt)          # A_hat symmetric: A_hat^T G = A_hat G
+        dW = store(gemm(X, dZ, transA=True), _wdt(dt))
+        dX = store(gemm(dZ, W, transB=True), dt) if need_dX else None
+        return dX, dW
+    dW = store(gemm(saved, G, transA=True), _wdt(dt))
+    if not need_dX:
+        return None, dW
+    T = store(gemm(G, W, transB=True), dt)
+    dX = store(spmm(g, T, w), dt)
+    return dX, dW
+
+
+def gcn_forward_backward(g, X, Ws, labels, dt="f32"):
+    """Multi-layer GCN: ReLU on hidden layers, none on the logits, mean softmax
+    cross-entropy; the first layer's input gradient is not formed.
+    Returns dict(loss, logits, dlogits, Y=[...], dW=[...])."""
+    L = len(Ws)
+    Hs, saved = [store(X, dt)], []
+    for li, W in enumerate(Ws):
+        last = li == L - 1
+        Y, s = gcn_layer_fwd(g, Hs[-1], W, relu=not last, dt=dt, out_dt=_wdt(dt) if last else dt)
+        Hs.append(Y)
+        saved.append(s)
+    loss, dz = softmax_xent(Hs[-1], labels)
+    dY = store(dz, _wdt(dt))
+    dWs = [None] * L
+    for li in reversed(range(L)):
+        last = li == L - 1
+        dX, dW = gcn_layer_bwd(g, Hs[li], saved[li], Hs[li + 1], dY, Ws[li], relu=not last,
+                               need_dX=li > 0, dt=dt)
+        dWs[li] = dW
+        dY = dX
+    return dict(loss=loss, logits=Hs[-1], dlogits=store(dz, _wdt(dt)), H=Hs, dW=dWs)
+
+
+# ---------------------------------------------------------------------------
+# GAT layer.  Tango, GAT running example (Fig. 1a forward, Fig. 1b backward).
+# ---------------------------------------------------------------------------
+def gat_scores(Hp, a, heads):
+    """S[v, k] = <H'[v, head k], a[k]> (float64)."""
+    n = Hp.shape[0]
+    dh = Hp.shape[1] // heads
+    return np.einsum("nkj,kj->nk", np.asarray(Hp, np.float64).reshape(n, heads, dh), np.asarray(a, np.float64))
+
+
+def gat_layer_fwd(g, X, W, a_src, a_dst, heads, slope, dt="f32"):
+    Hp = store(gemm(X, W), dt)
+    S = store(gat_scores(Hp, a_src, heads), dt)
+    D = store(gat_scores(Hp, a_dst, heads), dt)
+    E_pre, E = sddmm_add(g, S, D, slope)
+    alpha = store(edge_softmax(g, E), dt)
+    Y = store(spmm(g, Hp, alpha, heads), dt)
+    return dict(Hp=Hp, S=S, D=D, E_pre=E_pre, E=E, alpha=alpha, Y=Y)
+
+
+def gat_layer_bwd(g, fw, X, W, a_src, a_dst, dY, heads, slope, dt="f32"):
+    """Gradients of the GAT layer given the saved forward tensors ``fw``:
+      dalpha[e] = <dY[dst], H'[src]> per head           (SDDMM dot)
+      dE        = alpha (dalpha - P[dst]),  P = sum_in alpha dalpha
+      dEp       = dE * (E_pre > 0 ? 1 : slope)          (LeakyReLU')
+      dD[v]     = sum_in(v) dEp,  dS[u] = sum_out(u) dEp
+      dH'       = (G . alpha)^T dY + dS a_src + dD a_dst
+      da_src[k] = sum_v dS[v, k] H'[v, k, :]  (likewise da_dst)
+      dW = X^T dH',  dX = dH' W^T."""
+    n = g.n
+    Hp, alpha = fw["Hp"], fw["alpha"]
+    dh = Hp.shape[1] // heads
+    dalpha = store(sddmm_dot(g, dY, Hp, heads), dt)
+    dE = store(edge_softmax_bwd(g, alpha, dalpha), dt)
+    dEp = store(dE * np.where(fw["E_pre"] > 0, 1.0, float(np.float32(slope))), dt)
+    dD = store(edge_reduce(g, dEp, by_src=False), dt)
+    dS = store(edge_reduce(g, dEp, by_src=True), dt)
+    agg = spmm(g, dY, alpha, heads, transpose=True)
+    rank1 = (np.asarray(dS, np.float64)[:, :, None] * np.asarray(a_src, np.float64)[None]
+             + np.asarray(dD, np.float64)[:, :, None] * np.asarray(a_dst, np.float64)[None]).reshape(n, heads * dh)
+    dHp = store(agg + rank1, dt)
+    H3 = np.asarray(Hp, np.float64).reshape(n, heads, dh)
+    da_src = store(np.einsum("nk,nkj->kj", np.asarray(dS, np.float64), H3), dt)
+    da_dst = store(np.einsum("nk,nkj->kj", np.asarray(dD, np.float64), H3), dt)
+    dW = store(gemm(X, dHp, transA=True), dt)
+    dX = store(gemm(dHp, W, transB=True), dt)
+    return dict(dalpha=dalpha, dE=dE, dEp=dEp, dD=dD, dS=dS, dHp=dHp,
+                da_src=da_src, da_dst=da_dst, dW=dW, dX=dX)
+
+
+# ---------------------------------------------------------------------------
+# Quantised exchange of marginal rows (AdaQP Eqn. 4, 5 and 7): the marginal
+# rows of H are quantised, dequantised into a copy of H (central rows stay
+# binary32) and the mixed matrix is aggregated with A_hat.
+# ---------------------------------------------------------------------------
+def quantized_aggregate(g, H, rows, bits, seed, stream=0):
+    """bits: int (uniform) or int array per row (grouped into one call per width)."""
+    H = _c(H, np.float32)
+    Hmix = H.copy()
+    bits_arr = np.full(rows.size, bits, np.int32) if np.isscalar(bits) else np.asarray(bits, np.int32)
+    parts = {}
+    for b in (2, 4, 8):
+        sel = rows[bits_arr == b]
+        if sel.size == 0:
+            continue
+        pk, sc, zr = quantize(H, sel, b, seed, stream)
+        dequantize(pk, sc, zr, sel, H.shape[1], b, Hmix)
+        parts[b] = (sel, pk, sc, zr)
+    _, w = g.gcn_norm()
+    return Hmix, to_f32(spmm(g, Hmix, w)), parts

@@ -1,0 +1,129 @@
+"""Pins of the oracle's quantiser (AdaQP, stochastic integer quantisation,
+Eqn. 4-6) and of its counter-based generator (Philox4x32-10)."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_codes_range_min_and_error_bound(bits):
+    r = np.random.default_rng(bits)
+    H = r.standard_normal((64, 32)).astype(np.float32)
+    rows = np.arange(0, 64, 3, dtype=np.int32)
+    pk, sc, zr = oracle.quantize(H, rows, bits, seed=123)
+    q = oracle.unpack_codes(pk, 32, bits)
+    assert q.min() >= 0 and q.max() <= 2 ** bits - 1
+    for i, v in enumerate(rows):
+        assert zr[i] == H[v].min()
+        assert q[i, np.argmin(H[v])] == 0
+        assert np.isclose(sc[i], (H[v].max() - H[v].min()) / (2 ** bits - 1), rtol=1e-6)
+    out = H.copy()
+    oracle.dequantize(pk, sc, zr, rows, 32, bits, out)
+    err = np.abs(out[rows].astype(np.float64) - H[rows])
+    assert np.all(err <= sc[:, None] * (1 + 1e-5) + 1e-6)
+    others = np.setdiff1d(np.arange(64), rows)
+    assert np.array_equal(out[others], H[others])
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_lossless_grid_rows(bits):
+    # rows Z + k*S with S a power of two and both end levels present round-trip exactly
+    top = 2 ** bits - 1
+    d = 40
+    k = np.arange(d) % (top + 1)
+    k[0], k[1] = 0, top
+    H = np.stack([np.float32(-3.0) + k * np.float32(0.25), np.float32(1.5) + k * np.float32(2.0 ** -6)]).astype(np.float32)
+    rows = np.array([0, 1], np.int32)
+    pk, sc, zr = oracle.quantize(H, rows, bits, seed=7)
+    assert np.array_equal(oracle.unpack_codes(pk, d, bits)[0], k)
+    out = np.zeros_like(H)
+    oracle.dequantize(pk, sc, zr, rows, d, bits, out)
+    assert np.array_equal(out, H)
+
+
+def test_packing_layout_by_hand():
+    # 2-bit codes 0,1,2,3 -> one byte 0b11_10_01_00; 4-bit codes 0..15 pairwise
+    H = np.array([[0.0, 1.0, 2.0, 3.0, 3.0, 2.0, 1.0, 0.0]], np.float32)
+    pk, _, _ = oracle.quantize(H, np.array([0], np.int32), 2, seed=1)
+    assert pk.tolist() == [[0xE4, 0x1B]]
+    H4 = np.arange(16, dtype=np.float32)[None]
+    pk4, _, _ = oracle.quantize(H4, np.array([0], np.int32), 4, seed=1)
+    assert pk4.tolist() == [[0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]]
+
+
+def test_constant_row():
+    H = np.full((3, 16), 2.75, np.float32)
+    pk, sc, zr = oracle.quantize(H, np.array([1], np.int32), 4, seed=5)
+    assert sc[0] == 0.0 and zr[0] == 2.75 and not pk.any()
+    out = np.zeros_like(H)
+    oracle.dequantize(pk, sc, zr, np.array([1], np.int32), 16, 4, out)
+    assert np.all(out[1] == 2.75)
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+def test_unbiased_and_variance(bits):
+    # K copies of one row under different node ids draw independent uniforms
+    K, d = 4096, 48
+    r = np.random.default_rng(100 + bits)
+    row = r.standard_normal(d).astype(np.float32)
+    H = np.tile(row, (K, 1))
+    rows = np.arange(K, dtype=np.int32)
+    pk, sc, zr = oracle.quantize(H, rows, bits, seed=99)
+    out = np.zeros_like(H)
+    oracle.dequantize(pk, sc, zr, rows, d, bits, out)
+    S = float(sc[0])
+    x = (row.astype(np.float64) - row.min()) / S
+    f = x - np.floor(x)
+    err = out.astype(np.float64) - row
+    var = S * S * f * (1 - f)
+    mean = err.mean(0)
+    assert np.all(np.abs(mean) <= 4.5 * np.sqrt(var / K) + 1e-6 * S)
+    emp = (err ** 2).mean(0)
+    assert np.all(np.abs(emp - var) <= 6 * S * S * np.sqrt(1.0 / K) + 1e-6 * S * S)
+    assert np.all(var <= S * S / 4 + 1e-12)
+
+
+def test_row_variance_sixth():
+    # with fractional parts spread uniformly the row variance is about D*S^2/6
+    K, d = 256, 1024
+    r = np.random.default_rng(5)
+    H = r.uniform(-1, 1, (K, d)).astype(np.float32)
+    rows = np.arange(K, dtype=np.int32)
+    pk, sc, zr = oracle.quantize(H, rows, 2, seed=3)
+    out = np.zeros_like(H)
+    oracle.dequantize(pk, sc, zr, rows, d, 2, out)
+    tot = ((out.astype(np.float64) - H) ** 2).sum(1) / (d * sc.astype(np.float64) ** 2)
+    assert abs(tot.mean() - 1 / 6) < 0.01
+
+
+def test_philox_uniformity_and_independence():
+    nodes = np.arange(4096, dtype=np.int32)
+    u = oracle.philox_uniforms(2024, 0, nodes, 256).ravel()
+    assert u.min() >= 0 and u.max() < 1
+    assert np.all(u * 2 ** 24 == np.floor(u * 2 ** 24))
+    counts = np.bincount((u * 256).astype(int), minlength=256)
+    exp = u.size / 256
+    chi2 = ((counts - exp) ** 2 / exp).sum()
+    assert chi2 < 255 + 5 * np.sqrt(2 * 255)
+    x = u - 0.5
+    corr = np.dot(x[:-1], x[1:]) / np.dot(x, x)
+    assert abs(corr) < 4 / np.sqrt(u.size)
+    # another seed and another stream give other streams
+    assert not np.array_equal(u[:256], oracle.philox_uniforms(2025, 0, nodes[:1], 256).ravel())
+    assert not np.array_equal(u[:256], oracle.philox_uniforms(2024, 1, nodes[:1], 256).ravel())
+
+
+def test_philox_avalanche():
+    r = np.random.default_rng(17)
+    flips = []
+    for _ in range(400):
+        c = r.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)
+        k = r.integers(0, 2 ** 32, 2, dtype=np.uint64).astype(np.uint32)
+        b = int(r.integers(0, 128))
+        c2 = c.copy()
+        c2[b // 32] ^= np.uint32(1 << (b % 32))
+        o1 = oracle.philox4x32_10(c, k)
+        o2 = oracle.philox4x32_10(c2, k)
+        flips.append(sum(bin(int(a ^ bb)).count("1") for a, bb in zip(o1, o2)) / 128)
+    assert abs(np.mean(flips) - 0.5) < 0.02
