@@ -244,10 +244,12 @@ void orc_quantize(const float* H, int64_t ldh, int64_t d, const int32_t* rows,
         const int32_t node = rows[r];
         const float* h = H + (int64_t)node * ldh;
         uint8_t* out = packed + r * row_bytes;
+        /* min and max of the row; of two equal zeros the minimum is -0 and
+         * the maximum +0, so the result does not depend on the scan order */
         float mn = h[0], mx = h[0];
         for (int64_t f = 1; f < d; ++f) {
-            if (h[f] < mn) mn = h[f];
-            if (h[f] > mx) mx = h[f];
+            if (h[f] < mn || (h[f] == mn && signbit(h[f]))) mn = h[f];
+            if (h[f] > mx || (h[f] == mx && !signbit(h[f]))) mx = h[f];
         }
         const float R = mx - mn;
         memset(out, 0, (size_t)row_bytes);

@@ -127,3 +127,13 @@ def test_philox_avalanche():
         o2 = oracle.philox4x32_10(c2, k)
         flips.append(sum(bin(int(a ^ bb)).count("1") for a, bb in zip(o1, o2)) / 128)
     assert abs(np.mean(flips) - 0.5) < 0.02
+
+
+def test_signed_zero_extremes():
+    # of two equal zeros the minimum is -0 and the maximum +0, whatever the order
+    H = np.array([[0.0, -0.0, 0.0, 0.0], [-0.0, 0.0, -0.0, -0.0]], np.float32)
+    H[:, 0] = np.array([0.0, -0.0], np.float32)
+    pk, sc, zr = oracle.quantize(np.vstack([H, [[1.0, -0.0, 0.0, 2.0]]]).astype(np.float32),
+                                 np.array([0, 1, 2], np.int32), 8, seed=1)
+    assert np.signbit(zr[0]) and np.signbit(zr[1]) and sc[0] == 0 and sc[1] == 0
+    assert zr[2] == 0.0 and np.signbit(zr[2])
