@@ -1,0 +1,207 @@
+"""Benchmark of the per-layer GNN message-passing hot path on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+Default workload (config 2): 3-layer GCN forward + backward, binary32,
+R-MAT (a=0.57, b=c=0.19) with 2^20 nodes and average degree 16,
+symmetrised with self-loops and GCN normalisation; widths 128 -> 256 -> 256
+-> 41; mean softmax cross-entropy against random labels.  A step is one
+forward pass, the loss, and the backward pass down to the first layer's
+weight gradient, with every input resident in HBM.
+
+Printed value: GEdge*feat/s = (sum over the step's aggregations of
+nnz * width) / step time.  Beside it: the roofline of the dominant kernel
+(the aggregation of the 256-wide layers, HBM-bound), timed with HIP events
+on its own stream, and the CPU oracle timed on a bounded sample of the same
+workload.
+
+Other configs (timed the same way, for the record): 3 = one GAT layer
+(4 heads x 64, R-MAT 2^21, directed) forward + backward; 5 = one
+partition's quantised exchange (30% marginal rows of a 2^20-node R-MAT
+graph, 256 wide) followed by the aggregation.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def event_time(fn, reps, stream):
+    """Average duration (ms) of fn() over reps launches, HIP events on `stream`."""
+    import torch
+    with torch.cuda.stream(stream):
+        fn()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def spmm_compulsory_bytes(n, nnz, d, s_in=4, s_out=4):
+    """row_ptr (int64) + col (int32) + dinv (4 n) + each input row once + each output row once."""
+    return 8 * (n + 1) + 4 * nnz + 4 * n + s_in * n * d + s_out * n * d
+
+
+def cpu_baseline_gcn(scale_down):
+    import oracle
+    from oracle.graph import build_graph
+    from sparse_message_passing_amd import synth
+    inp = synth.config_inputs(2, scale_down=scale_down)
+    n = int(inp["n"])
+    og = build_graph(inp["src"], inp["dst"], n, True)
+    Ws = [inp["W0"], inp["W1"], inp["W2"]]
+    t0 = time.perf_counter()
+    oracle.gcn_forward_backward(og, inp["X"], Ws, inp["labels"])
+    dt = time.perf_counter() - t0
+    # same aggregation count as the GPU step: 128 + 256 + 41 forward, 256 + 41 backward
+    work = og.nnz * (128 + 256 + 41 + 256 + 41)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=work / dt / 1e9, unit="GEdge*feat/s", cores=threads, kind="oracle",
+                sample=f"full 3-layer forward+backward of the same generator at 2^{20 - scale_down} nodes "
+                       f"(nnz {og.nnz}), {dt:.2f} s")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (sharding is a design note, "
+              "not a measured path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_message_passing_amd import gnnmp, synth
+    from sparse_message_passing_amd.step import GatLayer, GcnStack, QuantExchange
+
+    if not os.path.exists(gnnmp.LIB_PATH):
+        from sparse_message_passing_amd import build as hb
+        hb.build(verbose=False)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream()
+    cfg = synth.CONFIGS[a.config]
+    t0 = time.time()
+    inp = synth.config_inputs(a.config)
+    n = int(inp["n"])
+    print(f"# inputs ready ({time.time() - t0:.1f} s)", file=sys.stderr, flush=True)
+    t0 = time.time()
+    g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=cfg["symmetric"], csc=cfg["kind"] == "gat")
+    print(f"# graph built: n={g.n} nnz={g.nnz} max_in_degree={g.max_in_degree} ({time.time() - t0:.1f} s)",
+          file=sys.stderr, flush=True)
+    T = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    extra = {}
+    with torch.cuda.stream(stream):
+        if cfg["kind"] == "gcn":
+            Ws = [T(inp[f"W{i}"]) for i in range(3)]
+            runner = GcnStack(g, T(inp["X"]), Ws, T(inp["labels"]))
+            work = runner.spmm_edge_feats()
+            metric_work = work
+        elif cfg["kind"] == "gat":
+            runner = GatLayer(g, T(inp["X"]), T(inp["W"]), T(inp["a_src"]), T(inp["a_dst"]), cfg["heads"],
+                              cfg["d_head"], cfg["slope"], T(inp["dY"]))
+            hd = cfg["heads"] * cfg["d_head"]
+            metric_work = g.nnz * hd * 3  # weighted SpMM, SDDMM dot, transposed SpMM
+        else:
+            runner = QuantExchange(g, T(inp["H"]), inp["rows"], inp["mixed_bits"], int(inp["philox_seed"]))
+            metric_work = g.nnz * cfg["d"]
+    for _ in range(a.warmup):
+        with torch.cuda.stream(stream):
+            runner.step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(a.steps):
+            runner.step()
+        end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / a.steps
+    print(f"# timed {a.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
+    value = metric_work / (ms * 1e-3) / 1e9
+
+    # --- dominant kernel: the aggregation (SpMM) ---------------------------
+    roofline = None
+    if cfg["kind"] == "gcn":
+        d = 256
+        X = runner.H[1]                       # a 256-wide activation
+        Y = torch.empty_like(X)
+        ws = torch.empty(max(gnnmp.lib().gnn_spmm_workspace_size(g.h, 0, d), 1), dtype=torch.uint8, device=dev)
+        spmm_ms = event_time(lambda: gnnmp.gnn_spmm(g, X, Y, ws=ws), a.kernel_reps, stream)
+        byts = spmm_compulsory_bytes(g.n, g.nnz, d)
+        ach = byts / (spmm_ms * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+        extra["spmm_d256_ms"] = round(spmm_ms, 4)
+        extra["spmm_d256_gedge_feat_s"] = round(g.nnz * d / (spmm_ms * 1e-3) / 1e9, 2)
+        extra["spmm_d256_compulsory_bytes"] = byts
+        # the update GEMM of the 256 -> 256 layer on the matrix cores
+        Wt = runner.Ws[1]
+        Z = torch.empty_like(X)
+        gws = torch.empty(max(gnnmp.lib().gnn_gemm_workspace_size(0, 0, g.n, d, d), 1), dtype=torch.uint8, device=dev)
+        gemm_ms = event_time(lambda: gnnmp.gnn_gemm(X, Wt, Z, ws=gws), a.kernel_reps, stream)
+        tf = 2.0 * g.n * d * d / (gemm_ms * 1e-3) / 1e12
+        extra["gemm_256x256_ms"] = round(gemm_ms, 4)
+        extra["gemm_256x256_tflops"] = round(tf, 2)
+        extra["gemm_256x256_frac_fp32_mfma"] = round(tf / FP32_MFMA_PEAK_TFLOPS, 4)
+        # the weight-gradient GEMM (K = number of nodes, split over K)
+        dW = torch.empty((d, d), device=dev)
+        gws2 = torch.empty(max(gnnmp.lib().gnn_gemm_workspace_size(1, 0, d, d, g.n), 1), dtype=torch.uint8,
+                           device=dev)
+        dw_ms = event_time(lambda: gnnmp.gnn_gemm(X, Z, dW, transA=True, ws=gws2), a.kernel_reps, stream)
+        extra["gemm_dW_256x256_ms"] = round(dw_ms, 4)
+        extra["gemm_dW_256x256_tflops"] = round(2.0 * g.n * d * d / (dw_ms * 1e-3) / 1e12, 2)
+    cpu = None
+    if not a.no_cpu_baseline and cfg["kind"] == "gcn":
+        print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_gcn(scale_down=3)
+    out = {
+        "metric": "GNN layer fwd+bwd GEdge*feat/s; SpMM/SDDMM HBM GB/s as % of peak",
+        "value": round(value, 3),
+        "unit": "GEdge*feat/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "nodes": g.n, "nnz": g.nnz, "max_in_degree": g.max_in_degree,
+                   "widths": cfg.get("widths"), "edge_feat_per_step": metric_work},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+/*
+ * gnnmp.h -- C ABI of the per-layer GNN message-passing library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations follow the pages' statement of the problem:
+ *   - AdaQP (arXiv 2306.01381): message passing as aggregation + update
+ *     (Sec. 2.1, Eqn. 1 and the weighted-sum form Eqn. 3), per-row stochastic
+ *     integer quantisation and dequantisation of exchanged messages
+ *     (Eqn. 4, 5), the local/remote split of the aggregation (Eqn. 7).
+ *   - Sancus (IJCAI'23 extended abstract), Sec. 2 Preliminaries: the GCN
+ *     operator A_hat = Dbar^-1/2 (A + I) Dbar^-1/2 and the layer
+ *     H(l+1) = sigma(A_hat H(l) W).
+ *   - Tango (SC'23, arXiv 2308.00890), GAT running example (Fig. 1a/1b): the
+ *     GAT forward and backward expressed with GEMM, SpMM and SDDMM.
+ *
+ * Conventions (all entry points)
+ *   - Graphs are CSR by destination: row v lists the sources u of the edges
+ *     u -> v in ascending order.  Edge-valued arrays are [nnz, heads]
+ *     row-major in CSR order.
+ *   - Dense matrices are row-major with a leading dimension in elements.
+ *   - Every pointer is device memory unless its comment says "host".  The
+ *     caller owns all device buffers; the library owns only graph handles.
+ *   - Compute calls are asynchronous on the caller's HIP stream (`stream`,
+ *     a hipStream_t; NULL = the default stream), never synchronise the host,
+ *     and use no floating-point atomics: results are bitwise reproducible.
+ *   - Arguments are validated before anything is launched.  On failure the
+ *     call returns a non-zero status, launches nothing, and
+ *     gnn_last_error() describes the problem (thread-local).
+ *   - Floating-point sums accumulate in binary32.  GNN_BF16 tensors hold
+ *     bfloat16 (round-to-nearest-even at every store).
+ */
+#ifndef GNNMP_H
+#define GNNMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GNN_OK = 0,
+    GNN_ERR_INVALID_ARG = 1,   /* a pointer, size, flag or leading dimension is invalid */
+    GNN_ERR_UNSUPPORTED = 2,   /* valid request the library does not implement          */
+    GNN_ERR_OUT_OF_MEMORY = 3, /* device or host allocation failed (graph creation)     */
+    GNN_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed            */
+    GNN_ERR_GRAPH = 5,         /* the graph lacks a view this call needs (e.g. CSC)     */
+    GNN_ERR_WORKSPACE = 6      /* the workspace is smaller than the size query returned */
+} gnn_status_t;
+
+typedef enum { GNN_F32 = 0, GNN_BF16 = 1 } gnn_dtype_t;
+
+/* Edge weights of an aggregation. */
+typedef enum {
+    GNN_W_GCN = 0,   /* A_hat entries dinv[u]*dinv[v] (Sancus Sec. 2), heads must be 1 */
+    GNN_W_ONES = 1,  /* every weight 1 (Tango's "ones" SpMM)                          */
+    GNN_W_EDGE = 2   /* caller's edge_w[nnz, heads] in CSR order (GAT attention)       */
+} gnn_weights_t;
+
+typedef struct gnn_graph* gnn_graph_t;
+
+/* Status text and the calling thread's last error detail (never NULL). */
+const char* gnn_status_string(gnn_status_t s);
+const char* gnn_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Graph layer
+ * ------------------------------------------------------------------------ */
+#define GNN_GRAPH_SYMMETRIZE 0x1u  /* add the reverse of every edge                */
+#define GNN_GRAPH_CSC        0x2u  /* also build the transposed (CSC + eid) view  */
+
+/* Build a graph from an edge list (Sancus Sec. 2: Abar = A + I; Tango,
+ * datasets paragraph: reverse edges and self-loops are added).  Self-loops
+ * and repeated edges of the input are dropped, the reverse edges are added
+ * when GNN_GRAPH_SYMMETRIZE is set, then exactly one self-loop per node is
+ * added, so the degree Dbar_vv is the CSR row length.  Also computes
+ * dinv[v] = 1/sqrt(Dbar_vv) (binary32, correctly rounded) and the order of
+ * rows by in-degree, descending, ties by id (and of CSC columns by
+ * out-degree when the CSC view is built).
+ *   n        number of nodes, 0 <= n < 2^31
+ *   m        number of input edges, m >= 0
+ *   src,dst  host int32[m]; ids must lie in [0, n)
+ *   flags    GNN_GRAPH_* bits
+ *   out      receives the handle (host)
+ * Synchronous: uploads the device arrays before it returns.  The result has
+ * nnz < 2^31.  Errors: GNN_ERR_INVALID_ARG (ids out of range, n < 0, ...),
+ * GNN_ERR_OUT_OF_MEMORY, GNN_ERR_HIP. */
+gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const int32_t* dst,
+                              uint32_t flags, gnn_graph_t* out);
+gnn_status_t gnn_graph_destroy(gnn_graph_t g);
+
+typedef struct {
+    int64_t n, nnz;
+    int64_t max_in_degree, max_out_degree;   /* max_out_degree = 0 without CSC */
+    int has_csc;
+    /* device views, owned by the graph */
+    const int64_t* row_ptr;   /* [n+1]                                      */
+    const int32_t* col;       /* [nnz]  source of each CSR slot             */
+    const float* dinv;        /* [n]    1/sqrt(row length)                  */
+    const int32_t* perm;      /* [n]    rows by in-degree desc, ties by id  */
+    const int64_t* col_ptr;   /* [n+1]  CSC (NULL without CSC)              */
+    const int32_t* csc_row;   /* [nnz]  destination of each CSC slot        */
+    const int32_t* csc_eid;   /* [nnz]  CSR slot of each CSC slot           */
+    const int32_t* perm_t;    /* [n]    columns by out-degree desc, ties by id */
+} gnn_graph_info_t;
+
+gnn_status_t gnn_graph_info(gnn_graph_t g, gnn_graph_info_t* out /* host */);
+
+/* Copy views back to host buffers (any pointer may be NULL to skip it).
+ * w receives the GCN edge weights dinv[src]*dinv[dst] in CSR order
+ * (binary32 product of the two binary32 factors).  Synchronous. */
+gnn_status_t gnn_graph_export(gnn_graph_t g, int64_t* row_ptr, int32_t* col, float* dinv, float* w,
+                              int32_t* perm, int64_t* col_ptr, int32_t* csc_row, int32_t* csc_eid,
+                              int32_t* perm_t /* all host */);
+
+/* ------------------------------------------------------------------------
+ * Primitives
+ * ------------------------------------------------------------------------ */
+
+/* Aggregation (SpMM).  AdaQP Eqn. 3 aggregation sum_u alpha_uv h_u; Tango
+ * GAT running example, "H(l) = (G . alpha) H'" (multi-head weighted SpMM):
+ *   transpose = 0:  Y[v, f] = sum_{u -> v} w(e, f / (d/heads)) * X[u, f]
+ *   transpose = 1:  Y[u, f] = sum_{u -> v} w(e, f / (d/heads)) * X[v, f]
+ *                   (needs the CSC view; the gradient over the reversed graph)
+ * then optionally ReLU (relu = 1).  X: [n, ldx] of x_dt, Y: [n, ldy] of y_dt,
+ * d features (d >= 1, ldx, ldy >= d), heads >= 1 dividing d.  X and Y must
+ * not overlap.  Needs a workspace of gnn_spmm_workspace_size() bytes for
+ * the split of high-degree rows (ws may be NULL when that size is 0). */
+size_t gnn_spmm_workspace_size(gnn_graph_t g, int transpose, int64_t d);
+gnn_status_t gnn_spmm(gnn_graph_t g, int transpose, gnn_weights_t wmode, const float* edge_w, int heads,
+                      const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                      int64_t d, int relu, void* ws, size_t ws_bytes, void* stream);
+
+/* Edge -> node sums (Tango: dD = (G . dE) 1 over in-edges, dS = (G^T . dE) 1
+ * over out-edges; the incidence-matrix SpMM).  by_src = 0 sums the in-edges
+ * of every node, by_src = 1 its out-edges (needs CSC).  vals [nnz, heads]
+ * f32, out [n, heads] f32. */
+gnn_status_t gnn_edge_reduce(gnn_graph_t g, int by_src, const float* vals, int heads, float* out,
+                             void* stream);
+
+/* SDDMM (Tango, GAT running example: E = G . (S (+) D^T)).
+ *   op = 0 (add):  out[e, k] = LReLU(src_feat[u, k] + dst_feat[v, k]) with
+ *                  slope `slope` (NaN: no activation), out_pre[e, k] the
+ *                  value before the activation (nullable).  d_head must be 1;
+ *                  src_feat, dst_feat are [n, ld] f32 with heads columns.
+ *                  One IEEE add and one multiply: bit-exact.
+ *   op = 1 (dot):  out[e, k] = sum_j src_feat[u, k*d_head + j] * dst_feat[v, k*d_head + j]
+ *                  (the attention gradient d(alpha) = dY[dst] . H'[src]);
+ *                  features of dt, out_pre must be NULL.
+ * out [nnz, heads] f32. */
+gnn_status_t gnn_sddmm(gnn_graph_t g, int op, const void* src_feat, int64_t ld_src, const void* dst_feat,
+                       int64_t ld_dst, gnn_dtype_t dt, int heads, int64_t d_head, float slope, float* out,
+                       float* out_pre, void* stream);
+
+/* Edge softmax over the in-edges of each destination, per head (Tango, GAT
+ * running example, softmax step, with the per-destination maximum
+ * subtracted first):  alpha[e,k] = exp(E[e,k] - m_vk) / sum_in(v) exp(E - m_vk).
+ * E, alpha [nnz, heads] f32 (may alias). */
+gnn_status_t gnn_edge_softmax(gnn_graph_t g, const float* E, float* alpha, int heads, void* stream);
+
+/* Its backward (Tango, Fig. 1b): P[v,k] = sum_in(v) alpha * dalpha;
+ * dE = alpha * (dalpha - P[dst]).  When lrelu_pre is not NULL the LeakyReLU
+ * derivative is applied too: dE *= (lrelu_pre > 0 ? 1 : slope).
+ * All [nnz, heads] f32; dE may alias dalpha. */
+gnn_status_t gnn_edge_softmax_bwd(gnn_graph_t g, const float* alpha, const float* dalpha,
+                                  const float* lrelu_pre, float slope, float* dE, int heads, void* stream);
+
+/* Dense product C = op(A) * op(B) (the update H W of AdaQP Eqn. 3 / Sancus
+ * Sec. 2, Tango's GEMM step; and its backward dW = H^T dZ, dH = dZ W^T),
+ * on the matrix cores.  op(A) is M x K, op(B) is K x N, C is M x N:
+ *   transA = 0: A is [M, lda] row-major;  1: A is [K, lda] (A^T used)
+ *   transB = 0: B is [K, ldb];            1: B is [N, ldb] (B^T used)
+ * Inputs of a_dt / b_dt (bf16 inputs are widened exactly), C of c_dt.
+ * Workspace: gnn_gemm_workspace_size() bytes (split-K partials and a
+ * transposed copy of a small B; 0 is possible). */
+size_t gnn_gemm_workspace_size(int transA, int transB, int64_t M, int64_t N, int64_t K);
+gnn_status_t gnn_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                      const void* A, gnn_dtype_t a_dt, int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb,
+                      void* C, gnn_dtype_t c_dt, int64_t ldc, void* ws, size_t ws_bytes, void* stream);
+
+/* Mean softmax cross-entropy over n rows of c logits and its gradient:
+ *   loss = (1/n) sum_v [logsumexp(z_v) - z_v[y_v]],  dz = (softmax(z_v) - onehot(y_v)) / n.
+ * logits [n, ld] f32, labels int32[n] in [0, c), loss: one device float,
+ * dlogits [n, ld_d] f32 (nullable).  The softmax and loss stay binary32
+ * (Tango keeps the layer feeding the softmax in full precision).
+ * Workspace gnn_softmax_xent_workspace_size(n) bytes. */
+size_t gnn_softmax_xent_workspace_size(int64_t n);
+gnn_status_t gnn_softmax_xent(const float* logits, int64_t n, int64_t c, int64_t ld, const int32_t* labels,
+                              float* loss, float* dlogits, int64_t ld_d, void* ws, size_t ws_bytes, void* stream);
+
+/* Per-row stochastic integer quantisation (AdaQP Eqn. 4).  For row r
+ * (node rows[r] of H), with b = bits in {2, 4, 8}:
+ *   Z = min, R = max - min, inv = (2^b-1)/R, S = R/(2^b-1)   (IEEE binary32)
+ *   x = (h - Z) * inv   (two rounded operations, no contraction)
+ *   q = min(floor(x) + [u < x - floor(x)], 2^b - 1)
+ * with u the uniform of Philox4x32-10 (Salmon et al., SC'11) at
+ * key (seed low, seed high), counter (rows[r], f/4, stream_id, 0), word f%4,
+ * u = (word >> 8) * 2^-24.  A constant row gives q = 0, S = 0.
+ * packed [n_rows, d*b/8] bytes (element j in byte j*b/8 at bit (j%(8/b))*b),
+ * scale, zero [n_rows] f32.  d*b must be a multiple of 8.  Codes are
+ * bit-exact against any other implementation of this definition. */
+gnn_status_t gnn_quantize(const float* H, int64_t ldh, int64_t d, const int32_t* rows, int64_t n_rows, int bits,
+                          uint64_t seed, uint32_t stream_id, uint8_t* packed, float* scale, float* zero, void* stream);
+
+/* Dequantisation (AdaQP Eqn. 5): H[rows[r], f] = fma(q, S_r, Z_r), one
+ * correctly rounded operation; rows not listed are untouched. */
+gnn_status_t gnn_dequantize(const uint8_t* packed, const float* scale, const float* zero, int64_t n_rows,
+                            int64_t d, int bits, const int32_t* rows, float* H, int64_t ldh, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Layers (GCN: AdaQP Eqn. 3 / Sancus Sec. 2; GAT: Tango Fig. 1a/1b)
+ * ------------------------------------------------------------------------ */
+
+/* GCN layer Y = sigma(A_hat X W), sigma = ReLU when relu = 1.  The GEMM runs
+ * first when d_out <= d_in, i.e. Y = sigma(A_hat (X W)); otherwise
+ * Y = sigma((A_hat X) W) and A_hat X is written to `saved` ([n, d_in] of
+ * x_dt, contiguous), which the backward needs.  X [n, d_in] of x_dt,
+ * W [d_in, d_out] f32, Y [n, d_out] of y_dt (contiguous).  Intermediates are
+ * stored in x_dt.  Workspace: gnn_gcn_workspace_size() bytes. */
+size_t gnn_gcn_workspace_size(gnn_graph_t g, int64_t d_in, int64_t d_out);
+gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, int64_t d_in, const float* W,
+                               int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, void* saved,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Its backward.  G = dY * [Y > 0] (ReLU'(0) = 0) when relu, else dY.
+ *   GEMM-first:     dZ = A_hat G;  dW = X^T dZ;  dX = dZ W^T
+ *   aggregate-first: dW = (A_hat X)^T G;  dX = A_hat (G W^T)
+ * (A_hat is symmetric).  dY, Y of y_dt; dX [n, d_in] of x_dt (NULL: not
+ * formed); dW [d_in, d_out] f32. */
+gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, int64_t d_in, const float* W,
+                               int64_t d_out, int relu, const void* Y, const void* dY, gnn_dtype_t y_dt,
+                               const void* saved, void* dX, float* dW, void* ws, size_t ws_bytes, void* stream);
+
+/* GAT layer forward (Tango, Fig. 1a):  H' = X W;  S = H' a_src, D = H' a_dst
+ * per head;  E = LReLU(S[src] + D[dst]);  alpha = edge softmax(E);
+ * Y[v, head k] = sum_in alpha[e,k] H'[u, head k] (heads concatenated, no bias,
+ * no output activation).  X [n, d_in] f32, W [d_in, heads*d_head] f32,
+ * a_src, a_dst [heads, d_head] f32, Y [n, heads*d_head] f32.
+ * saved: gnn_gat_saved_size() bytes holding H', S, D, E_pre, alpha for the
+ * backward.  Needs the CSC view only for the backward. */
+size_t gnn_gat_saved_size(gnn_graph_t g, int heads, int64_t d_head);
+size_t gnn_gat_workspace_size(gnn_graph_t g, int64_t d_in, int heads, int64_t d_head);
+gnn_status_t gnn_gat_layer_fwd(gnn_graph_t g, const float* X, int64_t d_in, const float* W, const float* a_src,
+                               const float* a_dst, int heads, int64_t d_head, float slope, float* Y, void* saved,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* GAT layer backward (Tango, Fig. 1b):
+ *   dalpha[e] = dY[dst] . H'[src] per head            (SDDMM dot)
+ *   dE = alpha (dalpha - P[dst]),  P = sum_in alpha dalpha,  then LReLU'
+ *   dD[v] = sum_in(v) dE,  dS[u] = sum_out(u) dE       (edge -> node sums)
+ *   dH' = (G . alpha)^T dY + dS a_src + dD a_dst        (SpMM on the CSC view)
+ *   da_src[k] = sum_v dS[v,k] H'[v, head k], likewise da_dst
+ *   dW = X^T dH',  dX = dH' W^T  (dX nullable).
+ * Requires the CSC view. */
+gnn_status_t gnn_gat_layer_bwd(gnn_graph_t g, const float* X, int64_t d_in, const float* W, const float* a_src,
+                               const float* a_dst, int heads, int64_t d_head, float slope, const float* dY,
+                               const void* saved, float* dX, float* dW, float* da_src, float* da_dst,
+                               void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GNNMP_H */

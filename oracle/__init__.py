@@ -123,8 +123,10 @@ def store(x, dt):
 def spmm(g: OracleGraph, X, w=None, heads=1, transpose=False):
     X = _c(X, np.float64)
     n, d = g.n, X.shape[1]
-    if X.shape[0] != n:
-        raise ValueError("X rows != n")
+    # the transposed product writes n rows from n input rows; the plain one
+    # reads the source rows named by col (a row-subset graph may have n < rows of X)
+    if (transpose and X.shape[0] != n) or (not transpose and g.nnz and X.shape[0] <= int(g.col.max())):
+        raise ValueError("X has too few rows for this graph")
     wa = None if w is None else _c(w, np.float64)
     Y = np.empty((n, d), dtype=np.float64)
     fn = lib().orc_spmm_t if transpose else lib().orc_spmm

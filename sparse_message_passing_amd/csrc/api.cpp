@@ -1,0 +1,350 @@
+// api.cpp -- the C ABI: errors, graph handles, argument checks and dispatch
+// of the primitives.  Every check runs before anything is launched.
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+namespace gnnmp {
+
+namespace {
+thread_local std::string g_last_error = "no error";
+}
+
+const char* last_error_cstr() { return g_last_error.c_str(); }
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+gnn_status_t fail(gnn_status_t s, const std::string& msg) {
+    set_error(msg);
+    return s;
+}
+
+gnn_status_t hip_fail(hipError_t e, const char* what) {
+    set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return e == hipErrorOutOfMemory ? GNN_ERR_OUT_OF_MEMORY : GNN_ERR_HIP;
+}
+
+gnn_status_t launch_status(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, what);
+    return GNN_OK;
+}
+
+AggView csr_view(const Graph& g) { return AggView{g.n, g.row_ptr, g.col, nullptr, &g.plan[0]}; }
+AggView csc_view(const Graph& g) { return AggView{g.n, g.col_ptr, g.csc_row, g.csc_eid, &g.plan[1]}; }
+
+namespace {
+
+template <typename T>
+gnn_status_t upload(Graph& g, const std::vector<T>& h, T** out) {
+    *out = nullptr;
+    if (h.empty()) return GNN_OK;
+    void* p = nullptr;
+    GNN_HIP(hipMalloc(&p, h.size() * sizeof(T)));
+    g.allocations.push_back(p);
+    GNN_HIP(hipMemcpy(p, h.data(), h.size() * sizeof(T), hipMemcpyHostToDevice));
+    *out = static_cast<T*>(p);
+    return GNN_OK;
+}
+
+gnn_status_t make_plan(Graph& g, const std::vector<int64_t>& ptr, RowPlan& p, std::vector<int32_t>* order_out) {
+    std::vector<int32_t> order;
+    degree_order(ptr, order);
+    const int64_t n = static_cast<int64_t>(order.size());
+    auto deg = [&](int64_t v) { return ptr[v + 1] - ptr[v]; };
+    p.max_degree = n ? deg(order[0]) : 0;
+    p.n_heavy = 0;
+    while (p.n_heavy < n && deg(order[p.n_heavy]) > kChunk) ++p.n_heavy;
+    p.n_block = 0;
+    while (p.n_block < n && deg(order[p.n_block]) > kBlockRow) ++p.n_block;
+    std::vector<int32_t> chunk_first(p.n_heavy + 1, 0), chunk_row;
+    for (int64_t i = 0; i < p.n_heavy; ++i) {
+        const int64_t c = (deg(order[i]) + kChunk - 1) / kChunk;
+        chunk_first[i + 1] = chunk_first[i] + static_cast<int32_t>(c);
+        for (int64_t j = 0; j < c; ++j) chunk_row.push_back(static_cast<int32_t>(i));
+    }
+    p.n_chunks = static_cast<int64_t>(chunk_row.size());
+    GNN_TRY(upload(g, order, &p.order));
+    GNN_TRY(upload(g, chunk_first, &p.chunk_first));
+    GNN_TRY(upload(g, chunk_row, &p.chunk_row));
+    if (order_out) *order_out = std::move(order);
+    return GNN_OK;
+}
+
+void free_graph(Graph& g) {
+    for (void* p : g.allocations) (void)hipFree(p);
+    g.allocations.clear();
+}
+
+bool bad_dt(gnn_dtype_t t) { return t != GNN_F32 && t != GNN_BF16; }
+
+gnn_status_t check_graph(const gnn_graph* g, const char* what) {
+    if (!g) return fail(GNN_ERR_INVALID_ARG, std::string(what) + ": graph handle is NULL");
+    return GNN_OK;
+}
+
+}  // namespace
+}  // namespace gnnmp
+
+using namespace gnnmp;
+
+extern "C" {
+
+const char* gnn_status_string(gnn_status_t s) {
+    switch (s) {
+        case GNN_OK: return "ok";
+        case GNN_ERR_INVALID_ARG: return "invalid argument";
+        case GNN_ERR_UNSUPPORTED: return "unsupported";
+        case GNN_ERR_OUT_OF_MEMORY: return "out of memory";
+        case GNN_ERR_HIP: return "HIP error";
+        case GNN_ERR_GRAPH: return "graph lacks the required view";
+        case GNN_ERR_WORKSPACE: return "workspace too small";
+    }
+    return "unknown status";
+}
+
+const char* gnn_last_error(void) { return last_error_cstr(); }
+
+// ---------------------------------------------------------------------------
+// graph
+// ---------------------------------------------------------------------------
+gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const int32_t* dst, uint32_t flags,
+                              gnn_graph_t* out) {
+    GNN_REQUIRE(out, "gnn_graph_create: out is NULL");
+    *out = nullptr;
+    GNN_REQUIRE(n >= 0 && n < (int64_t(1) << 31), "gnn_graph_create: n must be in [0, 2^31)");
+    GNN_REQUIRE(m >= 0, "gnn_graph_create: m must be >= 0");
+    GNN_REQUIRE(m == 0 || (src && dst), "gnn_graph_create: src/dst are NULL");
+    GNN_REQUIRE((flags & ~(GNN_GRAPH_SYMMETRIZE | GNN_GRAPH_CSC)) == 0, "gnn_graph_create: unknown flag bits");
+    gnn_graph* h = new (std::nothrow) gnn_graph();
+    if (!h) return fail(GNN_ERR_OUT_OF_MEMORY, "gnn_graph_create: host allocation failed");
+    Graph& g = h->g;
+    gnn_status_t s = GNN_OK;
+    try {
+        HostGraph hg;
+        s = build_host_graph(n, m, src, dst, (flags & GNN_GRAPH_SYMMETRIZE) != 0, (flags & GNN_GRAPH_CSC) != 0, hg);
+        if (s == GNN_OK) {
+            g.n = n;
+            g.nnz = n ? hg.row_ptr[n] : 0;
+            g.has_csc = (flags & GNN_GRAPH_CSC) != 0;
+            s = upload(g, hg.row_ptr, &g.row_ptr);
+            if (s == GNN_OK) s = upload(g, hg.col, &g.col);
+            if (s == GNN_OK) s = upload(g, hg.dinv, &g.dinv);
+            if (s == GNN_OK) s = make_plan(g, hg.row_ptr, g.plan[0], nullptr);
+            if (s == GNN_OK && g.has_csc) {
+                s = upload(g, hg.col_ptr, &g.col_ptr);
+                if (s == GNN_OK) s = upload(g, hg.csc_row, &g.csc_row);
+                if (s == GNN_OK) s = upload(g, hg.csc_eid, &g.csc_eid);
+                if (s == GNN_OK) s = make_plan(g, hg.col_ptr, g.plan[1], nullptr);
+            }
+        }
+    } catch (const std::bad_alloc&) {
+        s = fail(GNN_ERR_OUT_OF_MEMORY, "gnn_graph_create: host allocation failed");
+    }
+    if (s != GNN_OK) {
+        free_graph(g);
+        delete h;
+        return s;
+    }
+    *out = h;
+    return GNN_OK;
+}
+
+gnn_status_t gnn_graph_destroy(gnn_graph_t h) {
+    if (!h) return GNN_OK;
+    free_graph(h->g);
+    delete h;
+    return GNN_OK;
+}
+
+gnn_status_t gnn_graph_info(gnn_graph_t h, gnn_graph_info_t* out) {
+    GNN_TRY(check_graph(h, "gnn_graph_info"));
+    GNN_REQUIRE(out, "gnn_graph_info: out is NULL");
+    const Graph& g = h->g;
+    std::memset(out, 0, sizeof(*out));
+    out->n = g.n;
+    out->nnz = g.nnz;
+    out->max_in_degree = g.plan[0].max_degree;
+    out->max_out_degree = g.has_csc ? g.plan[1].max_degree : 0;
+    out->has_csc = g.has_csc;
+    out->row_ptr = g.row_ptr;
+    out->col = g.col;
+    out->dinv = g.dinv;
+    out->perm = g.plan[0].order;
+    out->col_ptr = g.col_ptr;
+    out->csc_row = g.csc_row;
+    out->csc_eid = g.csc_eid;
+    out->perm_t = g.plan[1].order;
+    return GNN_OK;
+}
+
+gnn_status_t gnn_graph_export(gnn_graph_t h, int64_t* row_ptr, int32_t* col, float* dinv, float* w, int32_t* perm,
+                              int64_t* col_ptr, int32_t* csc_row, int32_t* csc_eid, int32_t* perm_t) {
+    GNN_TRY(check_graph(h, "gnn_graph_export"));
+    const Graph& g = h->g;
+    if (!g.has_csc && (col_ptr || csc_row || csc_eid || perm_t))
+        return fail(GNN_ERR_GRAPH, "gnn_graph_export: the graph has no CSC view");
+    const size_t n1 = static_cast<size_t>(g.n + 1), n = static_cast<size_t>(g.n), e = static_cast<size_t>(g.nnz);
+    if (row_ptr && g.row_ptr) GNN_HIP(hipMemcpy(row_ptr, g.row_ptr, n1 * 8, hipMemcpyDeviceToHost));
+    if (col && e) GNN_HIP(hipMemcpy(col, g.col, e * 4, hipMemcpyDeviceToHost));
+    if (dinv && n) GNN_HIP(hipMemcpy(dinv, g.dinv, n * 4, hipMemcpyDeviceToHost));
+    if (perm && n) GNN_HIP(hipMemcpy(perm, g.plan[0].order, n * 4, hipMemcpyDeviceToHost));
+    if (col_ptr && g.col_ptr) GNN_HIP(hipMemcpy(col_ptr, g.col_ptr, n1 * 8, hipMemcpyDeviceToHost));
+    if (csc_row && e) GNN_HIP(hipMemcpy(csc_row, g.csc_row, e * 4, hipMemcpyDeviceToHost));
+    if (csc_eid && e) GNN_HIP(hipMemcpy(csc_eid, g.csc_eid, e * 4, hipMemcpyDeviceToHost));
+    if (perm_t && n) GNN_HIP(hipMemcpy(perm_t, g.plan[1].order, n * 4, hipMemcpyDeviceToHost));
+    if (w && e) {
+        std::vector<int64_t> rp(n1);
+        std::vector<int32_t> c(e);
+        std::vector<float> di(n);
+        GNN_HIP(hipMemcpy(rp.data(), g.row_ptr, n1 * 8, hipMemcpyDeviceToHost));
+        GNN_HIP(hipMemcpy(c.data(), g.col, e * 4, hipMemcpyDeviceToHost));
+        GNN_HIP(hipMemcpy(di.data(), g.dinv, n * 4, hipMemcpyDeviceToHost));
+        for (size_t v = 0; v < n; ++v)
+            for (int64_t k = rp[v]; k < rp[v + 1]; ++k) w[k] = di[c[k]] * di[v];
+    }
+    return GNN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// primitives
+// ---------------------------------------------------------------------------
+size_t gnn_spmm_workspace_size(gnn_graph_t h, int transpose, int64_t d) {
+    if (!h || d <= 0) return 0;
+    const Graph& g = h->g;
+    if (transpose && !g.has_csc) return 0;
+    return spmm_partial_bytes(g.plan[transpose ? 1 : 0], d);
+}
+
+gnn_status_t gnn_spmm(gnn_graph_t h, int transpose, gnn_weights_t wmode, const float* edge_w, int heads,
+                      const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                      int64_t d, int relu, void* ws, size_t ws_bytes, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_spmm"));
+    const Graph& g = h->g;
+    GNN_REQUIRE(d >= 1, "gnn_spmm: d must be >= 1");
+    GNN_REQUIRE(ldx >= d && ldy >= d, "gnn_spmm: leading dimensions must be >= d");
+    GNN_REQUIRE(heads >= 1 && d % heads == 0, "gnn_spmm: heads must divide d");
+    GNN_REQUIRE(!bad_dt(x_dt) && !bad_dt(y_dt), "gnn_spmm: unknown dtype");
+    GNN_REQUIRE(wmode == GNN_W_GCN || wmode == GNN_W_ONES || wmode == GNN_W_EDGE, "gnn_spmm: unknown weight mode");
+    GNN_REQUIRE(wmode != GNN_W_GCN || heads == 1, "gnn_spmm: GCN weights need heads == 1");
+    GNN_REQUIRE(wmode != GNN_W_EDGE || edge_w, "gnn_spmm: edge_w is NULL");
+    GNN_REQUIRE(relu == 0 || relu == 1, "gnn_spmm: relu must be 0 or 1");
+    GNN_REQUIRE(g.n == 0 || (X && Y), "gnn_spmm: X or Y is NULL");
+    GNN_REQUIRE(X != Y, "gnn_spmm: X and Y must not overlap");
+    if (transpose && !g.has_csc) return fail(GNN_ERR_GRAPH, "gnn_spmm: transpose needs the CSC view");
+    const RowPlan& p = g.plan[transpose ? 1 : 0];
+    const size_t need = spmm_partial_bytes(p, d);
+    if (need && (!ws || ws_bytes < need)) return fail(GNN_ERR_WORKSPACE, "gnn_spmm: workspace too small");
+    return launch_spmm(transpose ? csc_view(g) : csr_view(g), g.dinv, wmode, edge_w, heads, X, x_dt, ldx, Y, y_dt,
+                       ldy, d, relu, Rank1Epilogue{}, static_cast<float*>(ws), static_cast<hipStream_t>(stream));
+}
+
+gnn_status_t gnn_edge_reduce(gnn_graph_t h, int by_src, const float* vals, int heads, float* out, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_edge_reduce"));
+    const Graph& g = h->g;
+    GNN_REQUIRE(heads >= 1, "gnn_edge_reduce: heads must be >= 1");
+    GNN_REQUIRE(g.n == 0 || (vals && out), "gnn_edge_reduce: NULL pointer");
+    if (by_src && !g.has_csc) return fail(GNN_ERR_GRAPH, "gnn_edge_reduce: out-edge sums need the CSC view");
+    return launch_edge_reduce(by_src ? csc_view(g) : csr_view(g), vals, heads, out,
+                              static_cast<hipStream_t>(stream));
+}
+
+gnn_status_t gnn_sddmm(gnn_graph_t h, int op, const void* src_feat, int64_t ld_src, const void* dst_feat,
+                       int64_t ld_dst, gnn_dtype_t dt, int heads, int64_t d_head, float slope, float* out,
+                       float* out_pre, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_sddmm"));
+    const Graph& g = h->g;
+    GNN_REQUIRE(op == 0 || op == 1, "gnn_sddmm: op must be 0 (add) or 1 (dot)");
+    GNN_REQUIRE(heads >= 1 && d_head >= 1, "gnn_sddmm: heads and d_head must be >= 1");
+    GNN_REQUIRE(!bad_dt(dt), "gnn_sddmm: unknown dtype");
+    GNN_REQUIRE(g.n == 0 || (src_feat && dst_feat && out), "gnn_sddmm: NULL pointer");
+    GNN_REQUIRE(ld_src >= heads * d_head && ld_dst >= heads * d_head, "gnn_sddmm: leading dimension too small");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (op == 0) {
+        GNN_REQUIRE(d_head == 1, "gnn_sddmm(add): d_head must be 1 (one score per head)");
+        GNN_REQUIRE(dt == GNN_F32, "gnn_sddmm(add): scores are f32");
+        return launch_sddmm_add(csr_view(g), static_cast<const float*>(src_feat), ld_src,
+                                static_cast<const float*>(dst_feat), ld_dst, heads, slope, out, out_pre, st);
+    }
+    GNN_REQUIRE(out_pre == nullptr, "gnn_sddmm(dot): out_pre must be NULL");
+    return launch_sddmm_dot(csr_view(g), src_feat, ld_src, dst_feat, ld_dst, dt, heads, d_head, out, st);
+}
+
+gnn_status_t gnn_edge_softmax(gnn_graph_t h, const float* E, float* alpha, int heads, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_edge_softmax"));
+    const Graph& g = h->g;
+    GNN_REQUIRE(heads >= 1, "gnn_edge_softmax: heads must be >= 1");
+    GNN_REQUIRE(g.n == 0 || (E && alpha), "gnn_edge_softmax: NULL pointer");
+    return launch_edge_softmax(csr_view(g), E, alpha, heads, static_cast<hipStream_t>(stream));
+}
+
+gnn_status_t gnn_edge_softmax_bwd(gnn_graph_t h, const float* alpha, const float* dalpha, const float* lrelu_pre,
+                                  float slope, float* dE, int heads, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_edge_softmax_bwd"));
+    const Graph& g = h->g;
+    GNN_REQUIRE(heads >= 1, "gnn_edge_softmax_bwd: heads must be >= 1");
+    GNN_REQUIRE(g.n == 0 || (alpha && dalpha && dE), "gnn_edge_softmax_bwd: NULL pointer");
+    return launch_edge_softmax_bwd(csr_view(g), alpha, dalpha, lrelu_pre, slope, dE, heads,
+                                   static_cast<hipStream_t>(stream));
+}
+
+size_t gnn_gemm_workspace_size(int transA, int transB, int64_t M, int64_t N, int64_t K) {
+    return gemm_ws_bytes(transA, transB, M, N, K);
+}
+
+gnn_status_t gnn_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
+                      int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb, void* C, gnn_dtype_t c_dt,
+                      int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+    GNN_REQUIRE(M >= 0 && N >= 0 && K >= 0, "gnn_gemm: negative size");
+    GNN_REQUIRE(!bad_dt(a_dt) && !bad_dt(b_dt) && !bad_dt(c_dt), "gnn_gemm: unknown dtype");
+    GNN_REQUIRE((transA == 0 || transA == 1) && (transB == 0 || transB == 1), "gnn_gemm: trans flags must be 0/1");
+    GNN_REQUIRE(lda >= std::max<int64_t>(1, transA ? M : K), "gnn_gemm: lda too small");
+    GNN_REQUIRE(ldb >= std::max<int64_t>(1, transB ? K : N), "gnn_gemm: ldb too small");
+    GNN_REQUIRE(ldc >= std::max<int64_t>(1, N), "gnn_gemm: ldc too small");
+    GNN_REQUIRE(M * N == 0 || C, "gnn_gemm: C is NULL");
+    GNN_REQUIRE(M * N * K == 0 || (A && B), "gnn_gemm: A or B is NULL");
+    return launch_gemm(transA, transB, M, N, K, A, a_dt, lda, B, b_dt, ldb, C, c_dt, ldc, ws, ws_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+size_t gnn_softmax_xent_workspace_size(int64_t n) { return n > 0 ? xent_ws_bytes(n) : 256; }
+
+gnn_status_t gnn_softmax_xent(const float* logits, int64_t n, int64_t c, int64_t ld, const int32_t* labels,
+                              float* loss, float* dlogits, int64_t ld_d, void* ws, size_t ws_bytes, void* stream) {
+    GNN_REQUIRE(n >= 0 && c >= 1, "gnn_softmax_xent: need n >= 0, c >= 1");
+    GNN_REQUIRE(ld >= c && (!dlogits || ld_d >= c), "gnn_softmax_xent: leading dimension too small");
+    GNN_REQUIRE(loss && ws, "gnn_softmax_xent: loss or ws is NULL");
+    GNN_REQUIRE(n == 0 || (logits && labels), "gnn_softmax_xent: NULL pointer");
+    if (ws_bytes < gnn_softmax_xent_workspace_size(n))
+        return fail(GNN_ERR_WORKSPACE, "gnn_softmax_xent: workspace too small");
+    return launch_softmax_xent(logits, n, c, ld, labels, loss, dlogits, ld_d, static_cast<float*>(ws),
+                               static_cast<hipStream_t>(stream));
+}
+
+gnn_status_t gnn_quantize(const float* H, int64_t ldh, int64_t d, const int32_t* rows, int64_t n_rows, int bits,
+                          uint64_t seed, uint32_t stream_id, uint8_t* packed, float* scale, float* zero,
+                          void* stream) {
+    GNN_REQUIRE(bits == 2 || bits == 4 || bits == 8, "gnn_quantize: bits must be 2, 4 or 8");
+    GNN_REQUIRE(d >= 1 && (d * bits) % 8 == 0, "gnn_quantize: d*bits must be a positive multiple of 8");
+    GNN_REQUIRE(ldh >= d, "gnn_quantize: ldh must be >= d");
+    GNN_REQUIRE(n_rows >= 0, "gnn_quantize: n_rows must be >= 0");
+    GNN_REQUIRE(n_rows == 0 || (H && rows && packed && scale && zero), "gnn_quantize: NULL pointer");
+    return launch_quantize(H, ldh, d, rows, n_rows, bits, seed, stream_id, packed, scale, zero,
+                           static_cast<hipStream_t>(stream));
+}
+
+gnn_status_t gnn_dequantize(const uint8_t* packed, const float* scale, const float* zero, int64_t n_rows, int64_t d,
+                            int bits, const int32_t* rows, float* H, int64_t ldh, void* stream) {
+    GNN_REQUIRE(bits == 2 || bits == 4 || bits == 8, "gnn_dequantize: bits must be 2, 4 or 8");
+    GNN_REQUIRE(d >= 1 && (d * bits) % 8 == 0, "gnn_dequantize: d*bits must be a positive multiple of 8");
+    GNN_REQUIRE(ldh >= d, "gnn_dequantize: ldh must be >= d");
+    GNN_REQUIRE(n_rows >= 0, "gnn_dequantize: n_rows must be >= 0");
+    GNN_REQUIRE(n_rows == 0 || (H && rows && packed && scale && zero), "gnn_dequantize: NULL pointer");
+    return launch_dequantize(packed, scale, zero, n_rows, d, bits, rows, H, ldh, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

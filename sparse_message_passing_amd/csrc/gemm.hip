@@ -1,0 +1,345 @@
+// gemm.hip -- dense products on the CDNA4 matrix cores.
+//
+// The update step H W (AdaQP Eqn. 3; Sancus Sec. 2; Tango's GEMM step
+// "H' = H(l-1) W") and its backward dW = H^T dZ, dH = dZ W^T.
+//
+// Design (gfx950, wave64, v_mfma_f32_16x16x4_f32):
+//  * a 256-thread workgroup computes a BM x BN tile of C; its four waves
+//    split the tile WM x WN ways and each wave owns (BM/WM) x (BN/WN) as a
+//    grid of 16x16 MFMA blocks held in accumulation registers;
+//  * K advances in slabs of 16: the A and B slabs are staged through LDS in
+//    k-major layout (As[k][m], Bs[k][n]); an operand that is contiguous along
+//    k in global memory is transposed on the way in, one that is contiguous
+//    along m / n is stored with 16-byte writes;  the next slab's global loads
+//    are issued before the current slab's MFMAs;
+//  * operand fragments: lane l supplies A[m0 + l%16][k0 + l/16] and
+//    B[k0 + l/16][n0 + l%16]; the result block leaves lane l holding rows
+//    m0 + 4*(l/16) + r, r = 0..3, of column n0 + l%16;
+//  * the workgroup -> tile map keeps the tiles that share rows of A on one XCD
+//    (workgroups are dealt round-robin over the 8 XCDs, each with its own L2);
+//  * tall reductions (K = number of nodes, for dW) are split over K; each
+//    split writes a binary32 partial tile and a second pass adds the splits
+//    in order.  No atomics: bitwise reproducible.
+
+#include <algorithm>
+
+#include "device.h"
+#include "internal.h"
+
+namespace gnnmp {
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BK = 16;
+constexpr int PAD = 4;
+
+struct GemmArgs {
+    int64_t M, N, K;
+    const void* A;
+    int64_t lda;
+    const void* B;
+    int64_t ldb;
+    void* C;
+    int64_t ldc;
+    float* ws;       // split-K partials [splits][M][N]
+    int64_t kper;    // K range per split (multiple of BK)
+    int splits;
+    int64_t tiles_m, tiles_n;
+    int64_t nblocks; // real work items (tiles * splits)
+    int64_t per_xcd; // ceil(nblocks / 8)
+    int relu;        // ReLU epilogue (applied after the split-K sum)
+};
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void load4(const T* base, int64_t off, bool full, int valid, float (&r)[4]) {
+    if (VEC && full) {
+        float4 t = Elem<T>::load4(base + off);
+        r[0] = t.x, r[1] = t.y, r[2] = t.z, r[3] = t.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = i < valid ? Elem<T>::load(base + off + i) : 0.0f;
+    }
+}
+
+// TRANS_A: A given as [K][lda] (element (m,k) at A[k*lda+m]); else [M][lda].
+// TRANS_B: B given as [N][ldb] (element (k,n) at B[n*ldb+k]); else [K][ldb].
+template <int BM, int BN, int WM, int WN, bool TRANS_A, bool TRANS_B, bool VA, bool VB, typename TA, typename TB,
+          typename TC>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int A_LOADS = BM * BK / 4 / 256;  // float4-sized pieces per thread
+    constexpr int B_LOADS = BN * BK / 4 / 256;
+    static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
+    __shared__ float As[BK][BM + PAD];
+    __shared__ float Bs[BK][BN + PAD];
+
+    // XCD-aware tile map: the blocks dealt to one XCD take a contiguous range
+    const int64_t bid = blockIdx.x;
+    const int64_t L = (bid % 8) * g.per_xcd + bid / 8;
+    if (L >= g.nblocks) return;
+    const int64_t tiles = g.tiles_m * g.tiles_n;
+    const int64_t split = L / tiles;
+    const int64_t t = L % tiles;
+    const int64_t tm = t / g.tiles_n, tn = t % g.tiles_n;
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const int64_t kbeg = split * g.kper;
+    const int64_t kend = min(g.K, kbeg + g.kper);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const TA* A = static_cast<const TA*>(g.A);
+    const TB* B = static_cast<const TB*>(g.B);
+
+    v4f acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    float ra[A_LOADS][4], rb[B_LOADS][4];
+
+    auto load_slab = [&](int64_t k0) {
+#pragma unroll
+        for (int p = 0; p < A_LOADS; ++p) {
+            const int q = tid + p * 256;
+            if constexpr (!TRANS_A) {  // contiguous along k: q -> (m, k4)
+                const int mm = q / (BK / 4), kk = (q % (BK / 4)) * 4;
+                const int64_t m = m0 + mm, k = k0 + kk;
+                const int valid = (m < g.M) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, kend - k))) : 0;
+                load4<TA, VA>(A, m * g.lda + k, valid == 4, valid, ra[p]);
+            } else {                   // contiguous along m: q -> (k, m4)
+                const int kk = q / (BM / 4), mm = (q % (BM / 4)) * 4;
+                const int64_t m = m0 + mm, k = k0 + kk;
+                const int valid = (k < kend) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, g.M - m))) : 0;
+                load4<TA, VA>(A, k * g.lda + m, valid == 4, valid, ra[p]);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < B_LOADS; ++p) {
+            const int q = tid + p * 256;
+            if constexpr (!TRANS_B) {  // contiguous along n: q -> (k, n4)
+                const int kk = q / (BN / 4), nn = (q % (BN / 4)) * 4;
+                const int64_t n = n0 + nn, k = k0 + kk;
+                const int valid = (k < kend) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, g.N - n))) : 0;
+                load4<TB, VB>(B, k * g.ldb + n, valid == 4, valid, rb[p]);
+            } else {                   // contiguous along k: q -> (n, k4)
+                const int nn = q / (BK / 4), kk = (q % (BK / 4)) * 4;
+                const int64_t n = n0 + nn, k = k0 + kk;
+                const int valid = (n < g.N) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, kend - k))) : 0;
+                load4<TB, VB>(B, n * g.ldb + k, valid == 4, valid, rb[p]);
+            }
+        }
+    };
+    auto store_slab = [&]() {
+#pragma unroll
+        for (int p = 0; p < A_LOADS; ++p) {
+            const int q = tid + p * 256;
+            if constexpr (!TRANS_A) {
+                const int mm = q / (BK / 4), kk = (q % (BK / 4)) * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) As[kk + i][mm] = ra[p][i];
+            } else {
+                const int kk = q / (BM / 4), mm = (q % (BM / 4)) * 4;
+                *reinterpret_cast<float4*>(&As[kk][mm]) = make_float4(ra[p][0], ra[p][1], ra[p][2], ra[p][3]);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < B_LOADS; ++p) {
+            const int q = tid + p * 256;
+            if constexpr (!TRANS_B) {
+                const int kk = q / (BN / 4), nn = (q % (BN / 4)) * 4;
+                *reinterpret_cast<float4*>(&Bs[kk][nn]) = make_float4(rb[p][0], rb[p][1], rb[p][2], rb[p][3]);
+            } else {
+                const int nn = q / (BK / 4), kk = (q % (BK / 4)) * 4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Bs[kk + i][nn] = rb[p][i];
+            }
+        }
+    };
+
+    const int64_t nslab = (kend - kbeg + BK - 1) / BK;
+    if (nslab > 0) {
+        load_slab(kbeg);
+        store_slab();
+    }
+    __syncthreads();
+    for (int64_t s = 0; s < nslab; ++s) {
+        if (s + 1 < nslab) load_slab(kbeg + (s + 1) * BK);
+#pragma unroll
+        for (int kq = 0; kq < BK / 4; ++kq) {
+            const int kr = kq * 4 + (lane >> 4);
+            float af[FM], bf[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) af[i] = As[kr][wm * TM + i * 16 + (lane & 15)];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bf[j] = Bs[kr][wn * TN + j * 16 + (lane & 15)];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+        if (s + 1 < nslab) {
+            store_slab();
+            __syncthreads();
+        }
+    }
+
+    // epilogue
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * TN + j * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm * TM + i * 16 + 4 * (lane >> 4) + r;
+                if (m < g.M && n < g.N) {
+                    if (g.splits > 1)
+                        g.ws[(split * g.M + m) * g.N + n] = acc[i][j][r];
+                    else
+                        Elem<TC>::store(static_cast<TC*>(g.C) + m * g.ldc + n,
+                                        g.relu ? fmaxf(acc[i][j][r], 0.0f) : acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+template <typename TC>
+__global__ __launch_bounds__(256) void splitk_reduce(const float* ws, int splits, int64_t M, int64_t N, TC* C,
+                                                     int64_t ldc, int relu) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= M * N) return;
+    float s = 0.0f;
+    for (int z = 0; z < splits; ++z) s += ws[z * M * N + i];
+    Elem<TC>::store(C + (i / N) * ldc + (i % N), relu ? fmaxf(s, 0.0f) : s);
+}
+
+struct Plan {
+    int bm, bn, wm, wn;
+    int splits;
+    int64_t kper;
+};
+
+Plan make_plan(int64_t M, int64_t N, int64_t K) {
+    Plan p;
+    p.splits = 1;
+    p.kper = 0;
+    if (N <= 64) {
+        p.bm = 128, p.bn = 64, p.wm = 4, p.wn = 1;
+    } else {
+        p.bm = 128, p.bn = 128, p.wm = 2, p.wn = 2;
+    }
+    if (K <= 0) return p;
+    const int64_t tiles = ((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+    // split K when there are too few tiles to fill the chip and K is tall
+    if (tiles < 512 && K >= 4096) {
+        int64_t want = (1024 + tiles - 1) / tiles;
+        int64_t maxs = K / 2048;
+        p.splits = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(want, std::min<int64_t>(maxs, 512))));
+    }
+    const int64_t ks = (K + p.splits - 1) / p.splits;
+    p.kper = (ks + BK - 1) / BK * BK;
+    p.splits = static_cast<int>((K + p.kper - 1) / p.kper);
+    if (p.splits < 1) p.splits = 1;
+    return p;
+}
+
+template <int BM, int BN, int WM, int WN, bool TA_, bool TB_, typename TA, typename TB, typename TC>
+void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
+    const int64_t grid = 8 * g.per_xcd;
+    if (va && vb)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, TA, TB, TC>), dim3(grid), dim3(256), 0,
+                           st, g);
+    else if (va)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, false, TA, TB, TC>), dim3(grid), dim3(256), 0,
+                           st, g);
+    else if (vb)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, true, TA, TB, TC>), dim3(grid), dim3(256), 0,
+                           st, g);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, false, TA, TB, TC>), dim3(grid), dim3(256),
+                           0, st, g);
+}
+
+template <bool TA_, bool TB_, typename TA, typename TB, typename TC>
+void launch_types(GemmArgs& g, const Plan& p, bool va, bool vb, hipStream_t st) {
+    if (p.bn == 64)
+        launch_shape<128, 64, 4, 1, TA_, TB_, TA, TB, TC>(g, va, vb, st);
+    else
+        launch_shape<128, 128, 2, 2, TA_, TB_, TA, TB, TC>(g, va, vb, st);
+    if (g.splits > 1) {
+        const int64_t tot = g.M * g.N;
+        hipLaunchKernelGGL((splitk_reduce<TC>), dim3((tot + 255) / 256), dim3(256), 0, st, g.ws, g.splits, g.M, g.N,
+                           static_cast<TC*>(g.C), g.ldc, g.relu);
+    }
+}
+
+template <bool TA_, bool TB_>
+gnn_status_t launch_trans(GemmArgs& g, const Plan& p, gnn_dtype_t a, gnn_dtype_t b, gnn_dtype_t c, bool va, bool vb,
+                          hipStream_t st) {
+#define GNN_GEMM_CASE(TAt, TBt, TCt)                                                     \
+    launch_types<TA_, TB_, TAt, TBt, TCt>(g, p, va, vb, st);                             \
+    return launch_status("gnn_gemm");
+    if (a == GNN_F32 && b == GNN_F32 && c == GNN_F32) { GNN_GEMM_CASE(float, float, float) }
+    if (a == GNN_F32 && b == GNN_F32 && c == GNN_BF16) { GNN_GEMM_CASE(float, float, bf16_t) }
+    if (a == GNN_BF16 && b == GNN_F32 && c == GNN_F32) { GNN_GEMM_CASE(bf16_t, float, float) }
+    if (a == GNN_BF16 && b == GNN_F32 && c == GNN_BF16) { GNN_GEMM_CASE(bf16_t, float, bf16_t) }
+    if (a == GNN_BF16 && b == GNN_BF16 && c == GNN_F32) { GNN_GEMM_CASE(bf16_t, bf16_t, float) }
+    if (a == GNN_BF16 && b == GNN_BF16 && c == GNN_BF16) { GNN_GEMM_CASE(bf16_t, bf16_t, bf16_t) }
+    if (a == GNN_F32 && b == GNN_BF16 && c == GNN_F32) { GNN_GEMM_CASE(float, bf16_t, float) }
+    { GNN_GEMM_CASE(float, bf16_t, bf16_t) }
+#undef GNN_GEMM_CASE
+}
+
+}  // namespace
+
+size_t gemm_ws_bytes(int transA, int transB, int64_t M, int64_t N, int64_t K) {
+    (void)transA;
+    (void)transB;
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    Plan p = make_plan(M, N, K);
+    return p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * M * N * sizeof(float)) : 0;
+}
+
+gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
+                         int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb, void* C, gnn_dtype_t c_dt,
+                         int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu) {
+    if (M == 0 || N == 0) return GNN_OK;
+    Plan p = make_plan(M, N, K);
+    if (p.splits > 1 && ws_bytes < static_cast<size_t>(p.splits) * M * N * sizeof(float))
+        return fail(GNN_ERR_WORKSPACE, "gnn_gemm: workspace smaller than gnn_gemm_workspace_size()");
+    GemmArgs g;
+    g.M = M, g.N = N, g.K = K;
+    g.A = A, g.lda = lda, g.B = B, g.ldb = ldb, g.C = C, g.ldc = ldc;
+    g.ws = static_cast<float*>(ws);
+    g.relu = relu;
+    g.kper = p.kper;
+    g.splits = p.splits;
+    g.tiles_m = (M + p.bm - 1) / p.bm;
+    g.tiles_n = (N + p.bn - 1) / p.bn;
+    g.nblocks = g.tiles_m * g.tiles_n * p.splits;
+    g.per_xcd = (g.nblocks + 7) / 8;
+    if (K == 0) {
+        // C = 0: run the kernel with an empty K range
+        g.kper = 0;
+        g.splits = 1;
+        g.nblocks = g.tiles_m * g.tiles_n;
+        g.per_xcd = (g.nblocks + 7) / 8;
+    }
+    const size_t as = dt_size(a_dt), bs = dt_size(b_dt);
+    const bool va = lda % 4 == 0 && reinterpret_cast<uintptr_t>(A) % (4 * as) == 0;
+    const bool vb = ldb % 4 == 0 && reinterpret_cast<uintptr_t>(B) % (4 * bs) == 0;
+    if (!transA && !transB) return launch_trans<false, false>(g, p, a_dt, b_dt, c_dt, va, vb, st);
+    if (!transA && transB) return launch_trans<false, true>(g, p, a_dt, b_dt, c_dt, va, vb, st);
+    if (transA && !transB) return launch_trans<true, false>(g, p, a_dt, b_dt, c_dt, va, vb, st);
+    return launch_trans<true, true>(g, p, a_dt, b_dt, c_dt, va, vb, st);
+}
+
+}  // namespace gnnmp

@@ -1,0 +1,151 @@
+// internal.h -- shared declarations of the gnnmp library (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/gnnmp.h"
+
+namespace gnnmp {
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+void set_error(const std::string& msg);
+const char* last_error_cstr();
+gnn_status_t fail(gnn_status_t s, const std::string& msg);
+gnn_status_t hip_fail(hipError_t e, const char* what);
+gnn_status_t launch_status(const char* what);  // checks hipGetLastError after launches
+
+#define GNN_REQUIRE(cond, msg)                                                   \
+    do {                                                                         \
+        if (!(cond)) return ::gnnmp::fail(GNN_ERR_INVALID_ARG, (msg));           \
+    } while (0)
+
+#define GNN_HIP(call)                                                            \
+    do {                                                                         \
+        hipError_t e__ = (call);                                                 \
+        if (e__ != hipSuccess) return ::gnnmp::hip_fail(e__, #call);             \
+    } while (0)
+
+#define GNN_TRY(call)                                                            \
+    do {                                                                         \
+        gnn_status_t s__ = (call);                                               \
+        if (s__ != GNN_OK) return s__;                                           \
+    } while (0)
+
+// ---------------------------------------------------------------------------
+// graph
+// ---------------------------------------------------------------------------
+// Rows whose degree exceeds kChunk are cut into chunks of kChunk edges for the
+// aggregation kernels; each chunk is an independent work item and the chunks
+// of one row are summed afterwards in a fixed order.
+constexpr int64_t kChunk = 256;
+// Rows above this degree get a whole workgroup in the per-row edge kernels.
+constexpr int64_t kBlockRow = 2048;
+
+struct RowPlan {               // one per view (CSR by destination, CSC by source)
+    int32_t* order = nullptr;      // [n] rows by degree desc, ties by id
+    int64_t n_heavy = 0;           // rows with degree > kChunk: order[0 .. n_heavy)
+    int64_t n_block = 0;           // rows with degree > kBlockRow: order[0 .. n_block)
+    int64_t n_chunks = 0;          // chunks of the heavy rows
+    int32_t* chunk_row = nullptr;  // [n_chunks] index into order of the chunk's row
+    int32_t* chunk_first = nullptr;// [n_heavy + 1] first chunk of heavy row i
+    int64_t max_degree = 0;
+};
+
+struct Graph {
+    int64_t n = 0, nnz = 0;
+    bool has_csc = false;
+    int64_t* row_ptr = nullptr;   // [n+1]
+    int32_t* col = nullptr;       // [nnz]
+    float* dinv = nullptr;        // [n]
+    int64_t* col_ptr = nullptr;   // [n+1]
+    int32_t* csc_row = nullptr;   // [nnz]
+    int32_t* csc_eid = nullptr;   // [nnz]
+    RowPlan plan[2];              // 0: CSR, 1: CSC
+    std::vector<void*> allocations;
+};
+
+// Host-side construction (graph_build.cpp).
+struct HostGraph {
+    int64_t n = 0;
+    std::vector<int64_t> row_ptr;
+    std::vector<int32_t> col;
+    std::vector<float> dinv;
+    std::vector<int64_t> col_ptr;
+    std::vector<int32_t> csc_row, csc_eid;
+};
+gnn_status_t build_host_graph(int64_t n, int64_t m, const int32_t* src, const int32_t* dst, bool symmetrize,
+                              bool csc, HostGraph& out);
+void degree_order(const std::vector<int64_t>& ptr, std::vector<int32_t>& order);
+
+// ---------------------------------------------------------------------------
+// launchers (one per kernel family); all validate nothing, the API does that
+// ---------------------------------------------------------------------------
+struct AggView {          // what an aggregation walks
+    int64_t n;
+    const int64_t* ptr;   // row_ptr or col_ptr
+    const int32_t* idx;   // col or csc_row (the "other end" of each edge)
+    const int32_t* eid;   // CSR slot of each entry (CSC only) or nullptr
+    const RowPlan* plan;
+};
+
+AggView csr_view(const Graph& g);
+AggView csc_view(const Graph& g);
+
+struct Rank1Epilogue {    // Y[r, k*dh + j] += a[r, k] * va[k, j] + b[r, k] * vb[k, j]
+    const float* a = nullptr;
+    const float* va = nullptr;
+    const float* b = nullptr;
+    const float* vb = nullptr;
+};
+
+gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
+                         const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                         int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st);
+size_t spmm_partial_bytes(const RowPlan& p, int64_t d);
+
+gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, const float* D, int64_t ldd,
+                              int heads, float slope, float* out, float* out_pre, hipStream_t st);
+gnn_status_t launch_sddmm_dot(const AggView& v, const void* src_feat, int64_t ld_src, const void* dst_feat,
+                              int64_t ld_dst, gnn_dtype_t dt, int heads, int64_t d_head, float* out, hipStream_t st);
+gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha, int heads, hipStream_t st);
+gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha,
+                                     const float* pre, float slope, float* dE, int heads, hipStream_t st);
+gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st);
+
+gnn_status_t launch_gat_scores(int64_t n, const float* Hp, int heads, int64_t d_head, const float* a_src,
+                               const float* a_dst, float* S, float* D, hipStream_t st);
+size_t head_colsum_partial_bytes(int64_t n, int heads, int64_t d_head);
+gnn_status_t launch_head_colsum(int64_t n, const float* coefA, const float* coefB, const float* Hp, int heads,
+                                int64_t d_head, float* outA, float* outB, float* partial, hipStream_t st);
+
+size_t gemm_ws_bytes(int transA, int transB, int64_t M, int64_t N, int64_t K);
+gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
+                         int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb, void* C, gnn_dtype_t c_dt,
+                         int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu = 0);
+
+size_t xent_ws_bytes(int64_t n);
+gnn_status_t launch_softmax_xent(const float* logits, int64_t n, int64_t c, int64_t ld, const int32_t* labels,
+                                 float* loss, float* dlogits, int64_t ld_d, float* ws, hipStream_t st);
+gnn_status_t launch_relu_mask(int64_t count, const void* dY, const void* Y, gnn_dtype_t y_dt, void* G,
+                              gnn_dtype_t g_dt, hipStream_t st);
+
+gnn_status_t launch_quantize(const float* H, int64_t ldh, int64_t d, const int32_t* rows, int64_t n_rows, int bits,
+                             uint64_t seed, uint32_t stream_id, uint8_t* packed, float* scale, float* zero,
+                             hipStream_t st);
+gnn_status_t launch_dequantize(const uint8_t* packed, const float* scale, const float* zero, int64_t n_rows,
+                               int64_t d, int bits, const int32_t* rows, float* H, int64_t ldh, hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+inline size_t dt_size(gnn_dtype_t t) { return t == GNN_BF16 ? 2 : 4; }
+
+}  // namespace gnnmp
+
+struct gnn_graph {
+    gnnmp::Graph g;
+};

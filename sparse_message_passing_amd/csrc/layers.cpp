@@ -1,0 +1,276 @@
+// layers.cpp -- GCN and GAT layers composed from the primitives.
+//
+// GCN (AdaQP Eqn. 3; Sancus Sec. 2): Y = sigma(A_hat X W).  The product runs
+// on the narrower side: GEMM first when d_out <= d_in, otherwise the
+// aggregation first.
+// GAT (Tango, GAT running example, Fig. 1a forward / Fig. 1b backward).
+//
+// Workspaces are carved in 256-byte aligned slices; their sizes are returned
+// by the *_workspace_size queries with the same arithmetic.
+
+#include <algorithm>
+
+#include "internal.h"
+
+namespace gnnmp {
+namespace {
+
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* p) : base(static_cast<char*>(p)) {}
+    void* take(size_t bytes) {
+        void* p = base ? base + off : nullptr;
+        off += align_up(bytes);
+        return p;
+    }
+};
+
+// GCN workspace: [G (masked gradient)] [T (aggregation or GEMM intermediate)]
+//                [split-K partials] [SpMM partials]
+struct GcnWs {
+    size_t g, t, gemm, spmm;
+    size_t total() const { return align_up(g) + align_up(t) + align_up(gemm) + align_up(spmm); }
+};
+
+GcnWs gcn_ws(const Graph& g, int64_t d_in, int64_t d_out) {
+    GcnWs w;
+    const int64_t n = g.n;
+    const int64_t dmax = std::max(d_in, d_out);
+    w.g = static_cast<size_t>(n) * d_out * 4;   // worst case f32
+    w.t = static_cast<size_t>(n) * dmax * 4;
+    w.gemm = std::max(gemm_ws_bytes(1, 0, d_in, d_out, n), gemm_ws_bytes(0, 0, n, d_out, d_in));
+    w.gemm = std::max(w.gemm, gemm_ws_bytes(0, 1, n, d_in, d_out));
+    w.spmm = spmm_partial_bytes(g.plan[0], dmax);
+    return w;
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+}  // namespace
+}  // namespace gnnmp
+
+using namespace gnnmp;
+
+extern "C" {
+
+size_t gnn_gcn_workspace_size(gnn_graph_t h, int64_t d_in, int64_t d_out) {
+    if (!h || d_in <= 0 || d_out <= 0) return 0;
+    return gcn_ws(h->g, d_in, d_out).total();
+}
+
+gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t d_in, const float* W,
+                               int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, void* saved, void* ws,
+                               size_t ws_bytes, void* stream) {
+    GNN_REQUIRE(h, "gnn_gcn_layer_fwd: graph handle is NULL");
+    const Graph& g = h->g;
+    GNN_REQUIRE(d_in >= 1 && d_out >= 1, "gnn_gcn_layer_fwd: widths must be >= 1");
+    GNN_REQUIRE((x_dt == GNN_F32 || x_dt == GNN_BF16) && (y_dt == GNN_F32 || y_dt == GNN_BF16),
+                "gnn_gcn_layer_fwd: unknown dtype");
+    GNN_REQUIRE(relu == 0 || relu == 1, "gnn_gcn_layer_fwd: relu must be 0 or 1");
+    GNN_REQUIRE(g.n == 0 || (X && W && Y), "gnn_gcn_layer_fwd: NULL pointer");
+    const bool gemm_first = d_out <= d_in;
+    GNN_REQUIRE(gemm_first || g.n == 0 || saved, "gnn_gcn_layer_fwd: saved is NULL (aggregate-first order)");
+    const GcnWs w = gcn_ws(g, d_in, d_out);
+    if (ws_bytes < w.total() || (!ws && w.total()))
+        return fail(GNN_ERR_WORKSPACE, "gnn_gcn_layer_fwd: workspace smaller than gnn_gcn_workspace_size()");
+    if (g.n == 0) return GNN_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Carver c(ws);
+    c.take(w.g);
+    void* T = c.take(w.t);
+    void* gws = c.take(w.gemm);
+    float* sws = static_cast<float*>(c.take(w.spmm));
+    if (gemm_first) {
+        GNN_TRY(launch_gemm(0, 0, g.n, d_out, d_in, X, x_dt, d_in, W, GNN_F32, d_out, T, x_dt, d_out, gws, w.gemm,
+                            st));
+        return launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, T, x_dt, d_out, Y, y_dt, d_out, d_out, relu,
+                           Rank1Epilogue{}, sws, st);
+    }
+    GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, X, x_dt, d_in, saved, x_dt, d_in, d_in, 0,
+                        Rank1Epilogue{}, sws, st));
+    return launch_gemm(0, 0, g.n, d_out, d_in, saved, x_dt, d_in, W, GNN_F32, d_out, Y, y_dt, d_out, gws, w.gemm, st,
+                       relu);
+}
+
+gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t d_in, const float* W,
+                               int64_t d_out, int relu, const void* Y, const void* dY, gnn_dtype_t y_dt,
+                               const void* saved, void* dX, float* dW, void* ws, size_t ws_bytes, void* stream) {
+    GNN_REQUIRE(h, "gnn_gcn_layer_bwd: graph handle is NULL");
+    const Graph& g = h->g;
+    GNN_REQUIRE(d_in >= 1 && d_out >= 1, "gnn_gcn_layer_bwd: widths must be >= 1");
+    GNN_REQUIRE((x_dt == GNN_F32 || x_dt == GNN_BF16) && (y_dt == GNN_F32 || y_dt == GNN_BF16),
+                "gnn_gcn_layer_bwd: unknown dtype");
+    GNN_REQUIRE(relu == 0 || relu == 1, "gnn_gcn_layer_bwd: relu must be 0 or 1");
+    GNN_REQUIRE(dW && W, "gnn_gcn_layer_bwd: W or dW is NULL");
+    GNN_REQUIRE(g.n == 0 || dY, "gnn_gcn_layer_bwd: dY is NULL");
+    GNN_REQUIRE(!relu || g.n == 0 || Y, "gnn_gcn_layer_bwd: Y is NULL (needed for the ReLU mask)");
+    const bool gemm_first = d_out <= d_in;
+    GNN_REQUIRE(g.n == 0 || (gemm_first ? X != nullptr : saved != nullptr),
+                "gnn_gcn_layer_bwd: X (GEMM-first) or saved (aggregate-first) is NULL");
+    GNN_REQUIRE(!relu || (aligned16(Y) && aligned16(dY)), "gnn_gcn_layer_bwd: Y and dY must be 16-byte aligned");
+    const GcnWs w = gcn_ws(g, d_in, d_out);
+    if (ws_bytes < w.total() || (!ws && w.total()))
+        return fail(GNN_ERR_WORKSPACE, "gnn_gcn_layer_bwd: workspace smaller than gnn_gcn_workspace_size()");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Carver c(ws);
+    void* Gb = c.take(w.g);
+    void* T = c.take(w.t);
+    void* gws = c.take(w.gemm);
+    float* sws = static_cast<float*>(c.take(w.spmm));
+    // G = dY * [Y > 0]: materialised in the storage type when masked
+    const void* G = dY;
+    gnn_dtype_t g_dt = y_dt;
+    if (relu && g.n) {
+        GNN_TRY(launch_relu_mask(g.n * d_out, dY, Y, y_dt, Gb, x_dt, st));
+        G = Gb;
+        g_dt = x_dt;
+    }
+    if (gemm_first) {
+        // dZ = A_hat G;  dW = X^T dZ;  dX = dZ W^T
+        GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, G, g_dt, d_out, T, x_dt, d_out, d_out, 0,
+                            Rank1Epilogue{}, sws, st));
+        GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, X, x_dt, d_in, T, x_dt, d_out, dW, GNN_F32, d_out, gws, w.gemm,
+                            st));
+        if (dX)
+            GNN_TRY(launch_gemm(0, 1, g.n, d_in, d_out, T, x_dt, d_out, W, GNN_F32, d_out, dX, x_dt, d_in, gws,
+                                w.gemm, st));
+        return GNN_OK;
+    }
+    // dW = (A_hat X)^T G;  dX = A_hat (G W^T)
+    GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, saved, x_dt, d_in, G, g_dt, d_out, dW, GNN_F32, d_out, gws, w.gemm,
+                        st));
+    if (dX) {
+        GNN_TRY(launch_gemm(0, 1, g.n, d_in, d_out, G, g_dt, d_out, W, GNN_F32, d_out, T, x_dt, d_in, gws, w.gemm,
+                            st));
+        GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, T, x_dt, d_in, dX, x_dt, d_in, d_in, 0,
+                            Rank1Epilogue{}, sws, st));
+    }
+    return GNN_OK;
+}
+
+// ---------------------------------------------------------------------------
+// GAT
+// ---------------------------------------------------------------------------
+size_t gnn_gat_saved_size(gnn_graph_t h, int heads, int64_t d_head) {
+    if (!h || heads < 1 || d_head < 1) return 0;
+    const Graph& g = h->g;
+    const size_t n = g.n, e = g.nnz, hd = static_cast<size_t>(heads) * d_head;
+    return align_up(n * hd * 4) + 2 * align_up(n * heads * 4) + 2 * align_up(e * heads * 4);
+}
+
+size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_head) {
+    if (!h || heads < 1 || d_head < 1 || d_in < 1) return 0;
+    const Graph& g = h->g;
+    const size_t n = g.n, e = g.nnz;
+    const int64_t hd = heads * d_head;
+    size_t t = align_up(e * heads * 4) + 2 * align_up(n * heads * 4) + align_up(n * hd * 4);
+    t += align_up(head_colsum_partial_bytes(g.n, heads, d_head));
+    size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
+    gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
+    t += align_up(gemm);
+    t += align_up(std::max(spmm_partial_bytes(g.plan[0], hd), g.has_csc ? spmm_partial_bytes(g.plan[1], hd) : 0));
+    return t;
+}
+
+namespace {
+struct GatSaved {
+    float *Hp, *S, *D, *Epre, *alpha;
+};
+GatSaved carve_saved(const Graph& g, void* saved, int heads, int64_t d_head) {
+    Carver c(saved);
+    const size_t n = g.n, e = g.nnz, hd = static_cast<size_t>(heads) * d_head;
+    GatSaved s;
+    s.Hp = static_cast<float*>(c.take(n * hd * 4));
+    s.S = static_cast<float*>(c.take(n * heads * 4));
+    s.D = static_cast<float*>(c.take(n * heads * 4));
+    s.Epre = static_cast<float*>(c.take(e * heads * 4));
+    s.alpha = static_cast<float*>(c.take(e * heads * 4));
+    return s;
+}
+}  // namespace
+
+gnn_status_t gnn_gat_layer_fwd(gnn_graph_t h, const float* X, int64_t d_in, const float* W, const float* a_src,
+                               const float* a_dst, int heads, int64_t d_head, float slope, float* Y, void* saved,
+                               void* ws, size_t ws_bytes, void* stream) {
+    GNN_REQUIRE(h, "gnn_gat_layer_fwd: graph handle is NULL");
+    const Graph& g = h->g;
+    GNN_REQUIRE(d_in >= 1 && heads >= 1 && d_head >= 1, "gnn_gat_layer_fwd: sizes must be >= 1");
+    GNN_REQUIRE(g.n == 0 || (X && W && a_src && a_dst && Y && saved), "gnn_gat_layer_fwd: NULL pointer");
+    const size_t need = gnn_gat_workspace_size(h, d_in, heads, d_head);
+    if (ws_bytes < need || (!ws && need))
+        return fail(GNN_ERR_WORKSPACE, "gnn_gat_layer_fwd: workspace smaller than gnn_gat_workspace_size()");
+    if (g.n == 0) return GNN_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t hd = heads * d_head;
+    GatSaved s = carve_saved(g, saved, heads, d_head);
+    Carver c(ws);
+    c.take(static_cast<size_t>(g.nnz) * heads * 4);
+    c.take(static_cast<size_t>(g.n) * heads * 4);
+    c.take(static_cast<size_t>(g.n) * heads * 4);
+    c.take(static_cast<size_t>(g.n) * hd * 4);
+    c.take(head_colsum_partial_bytes(g.n, heads, d_head));
+    size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
+    gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
+    void* gws = c.take(gemm);
+    float* sws = static_cast<float*>(c.take(1));
+    // H' = X W;  S, D per-head scores;  E = LReLU(S[src] + D[dst]);  alpha = softmax;  Y = (G . alpha) H'
+    GNN_TRY(launch_gemm(0, 0, g.n, hd, d_in, X, GNN_F32, d_in, W, GNN_F32, hd, s.Hp, GNN_F32, hd, gws, gemm, st));
+    GNN_TRY(launch_gat_scores(g.n, s.Hp, heads, d_head, a_src, a_dst, s.S, s.D, st));
+    GNN_TRY(launch_sddmm_add(csr_view(g), s.S, heads, s.D, heads, heads, slope, s.alpha, s.Epre, st));
+    GNN_TRY(launch_edge_softmax(csr_view(g), s.alpha, s.alpha, heads, st));
+    return launch_spmm(csr_view(g), g.dinv, GNN_W_EDGE, s.alpha, heads, s.Hp, GNN_F32, hd, Y, GNN_F32, hd, hd, 0,
+                       Rank1Epilogue{}, sws, st);
+}
+
+gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, const float* W, const float* a_src,
+                               const float* a_dst, int heads, int64_t d_head, float slope, const float* dY,
+                               const void* saved, float* dX, float* dW, float* da_src, float* da_dst, void* ws,
+                               size_t ws_bytes, void* stream) {
+    GNN_REQUIRE(h, "gnn_gat_layer_bwd: graph handle is NULL");
+    const Graph& g = h->g;
+    GNN_REQUIRE(d_in >= 1 && heads >= 1 && d_head >= 1, "gnn_gat_layer_bwd: sizes must be >= 1");
+    GNN_REQUIRE(dW && da_src && da_dst, "gnn_gat_layer_bwd: NULL gradient pointer");
+    GNN_REQUIRE(g.n == 0 || (X && W && a_src && a_dst && dY && saved), "gnn_gat_layer_bwd: NULL pointer");
+    if (!g.has_csc) return fail(GNN_ERR_GRAPH, "gnn_gat_layer_bwd: the graph needs the CSC view");
+    const size_t need = gnn_gat_workspace_size(h, d_in, heads, d_head);
+    if (ws_bytes < need || (!ws && need))
+        return fail(GNN_ERR_WORKSPACE, "gnn_gat_layer_bwd: workspace smaller than gnn_gat_workspace_size()");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t hd = heads * d_head;
+    GatSaved s = carve_saved(g, const_cast<void*>(saved), heads, d_head);
+    Carver c(ws);
+    float* dEb = static_cast<float*>(c.take(static_cast<size_t>(g.nnz) * heads * 4));
+    float* dD = static_cast<float*>(c.take(static_cast<size_t>(g.n) * heads * 4));
+    float* dS = static_cast<float*>(c.take(static_cast<size_t>(g.n) * heads * 4));
+    float* dHp = static_cast<float*>(c.take(static_cast<size_t>(g.n) * hd * 4));
+    float* cps = static_cast<float*>(c.take(head_colsum_partial_bytes(g.n, heads, d_head)));
+    size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
+    gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
+    void* gws = c.take(gemm);
+    float* sws = static_cast<float*>(c.take(1));
+    const AggView csr = csr_view(g), csc = csc_view(g);
+    // dalpha = dY[dst] . H'[src];  dE = alpha (dalpha - P) * LReLU'
+    GNN_TRY(launch_sddmm_dot(csr, s.Hp, hd, dY, hd, GNN_F32, heads, d_head, dEb, st));
+    GNN_TRY(launch_edge_softmax_bwd(csr, s.alpha, dEb, s.Epre, slope, dEb, heads, st));
+    // dD = in-edge sums, dS = out-edge sums
+    GNN_TRY(launch_edge_reduce(csr, dEb, heads, dD, st));
+    GNN_TRY(launch_edge_reduce(csc, dEb, heads, dS, st));
+    // dH' = (G . alpha)^T dY + dS a_src + dD a_dst
+    Rank1Epilogue r1;
+    r1.a = dS;
+    r1.va = a_src;
+    r1.b = dD;
+    r1.vb = a_dst;
+    GNN_TRY(launch_spmm(csc, g.dinv, GNN_W_EDGE, s.alpha, heads, dY, GNN_F32, hd, dHp, GNN_F32, hd, hd, 0, r1, sws,
+                        st));
+    // da_src = sum_v dS[v] H'[v], da_dst = sum_v dD[v] H'[v] per head
+    GNN_TRY(launch_head_colsum(g.n, dS, dD, s.Hp, heads, d_head, da_src, da_dst, cps, st));
+    // dW = X^T dH',  dX = dH' W^T
+    GNN_TRY(launch_gemm(1, 0, d_in, hd, g.n, X, GNN_F32, d_in, dHp, GNN_F32, hd, dW, GNN_F32, hd, gws, gemm, st));
+    if (dX)
+        GNN_TRY(launch_gemm(0, 1, g.n, d_in, hd, dHp, GNN_F32, hd, W, GNN_F32, hd, dX, GNN_F32, d_in, gws, gemm, st));
+    return GNN_OK;
+}
+
+}  // extern "C"

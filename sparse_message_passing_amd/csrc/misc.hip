@@ -1,0 +1,114 @@
+// misc.hip -- the loss and the ReLU gradient mask.
+//
+// Mean softmax cross-entropy over all rows (the loss of a node-classification
+// GCN; the pages train with full-graph gradient descent, AdaQP Eqn. 8):
+//   loss = (1/n) sum_v [logsumexp(z_v) - z_v[y_v]],  dz = (softmax(z_v) - onehot(y_v)) / n.
+// Tango keeps the layer that feeds the softmax in full precision, so the
+// logits, their gradient and the loss are binary32.  One wave per row; the
+// per-row losses are added in a fixed order (per block, then over blocks).
+
+#include "device.h"
+#include "internal.h"
+
+namespace gnnmp {
+
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one wave per row
+
+__global__ __launch_bounds__(256) void xent_rows(const float* z, int64_t n, int64_t c, int64_t ld,
+                                                 const int32_t* labels, float* dz, int64_t ldd, float inv_n,
+                                                 float* block_loss) {
+    __shared__ float sh[kRowsPerBlock];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t v = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + w;
+    float row_loss = 0.0f;
+    if (v < n) {
+        const float* zr = z + v * ld;
+        const int32_t y = labels[v];
+        float m = -INFINITY;
+        for (int64_t j = lane; j < c; j += 64) m = fmaxf(m, zr[j]);
+        m = group_max<64>(m);
+        float s = 0.0f;
+        for (int64_t j = lane; j < c; j += 64) s += __expf(zr[j] - m);
+        s = group_sum<64>(s);
+        const float lse = m + __logf(s);
+        row_loss = lse - zr[y];
+        if (dz) {
+            const float is = 1.0f / s;
+            for (int64_t j = lane; j < c; j += 64) {
+                float p = __expf(zr[j] - m) * is;
+                if (j == y) p -= 1.0f;
+                dz[v * ldd + j] = p * inv_n;
+            }
+        }
+    }
+    if (lane == 0) sh[w] = row_loss;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int i = 0; i < kRowsPerBlock; ++i) t += sh[i];
+        block_loss[blockIdx.x] = t;
+    }
+}
+
+__global__ __launch_bounds__(256) void xent_total(const float* block_loss, int64_t nb, float inv_n, float* loss) {
+    __shared__ float sh[256];
+    float t = 0.0f;
+    for (int64_t i = threadIdx.x; i < nb; i += 256) t += block_loss[i];
+    sh[threadIdx.x] = t;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *loss = sh[0] * inv_n;
+}
+
+template <typename TY, typename TG>
+__global__ __launch_bounds__(256) void relu_mask_kernel(int64_t count, const TY* dY, const TY* Y, TG* G) {
+    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (i + 4 <= count) {
+        float4 d = Elem<TY>::load4(dY + i), y = Elem<TY>::load4(Y + i);
+        d.x = y.x > 0.0f ? d.x : 0.0f;
+        d.y = y.y > 0.0f ? d.y : 0.0f;
+        d.z = y.z > 0.0f ? d.z : 0.0f;
+        d.w = y.w > 0.0f ? d.w : 0.0f;
+        Elem<TG>::store4(G + i, d);
+    } else {
+        for (int64_t j = i; j < count; ++j) Elem<TG>::store(G + j, Elem<TY>::load(Y + j) > 0.0f ? Elem<TY>::load(dY + j) : 0.0f);
+    }
+}
+
+}  // namespace
+
+size_t xent_ws_bytes(int64_t n) {
+    return align_up(static_cast<size_t>((n + kRowsPerBlock - 1) / kRowsPerBlock) * sizeof(float));
+}
+
+gnn_status_t launch_softmax_xent(const float* logits, int64_t n, int64_t c, int64_t ld, const int32_t* labels,
+                                 float* loss, float* dlogits, int64_t ld_d, float* ws, hipStream_t st) {
+    const int64_t nb = (n + kRowsPerBlock - 1) / kRowsPerBlock;
+    const float inv_n = n > 0 ? 1.0f / static_cast<float>(n) : 0.0f;
+    if (nb > 0)
+        hipLaunchKernelGGL(xent_rows, dim3(nb), dim3(256), 0, st, logits, n, c, ld, labels, dlogits, ld_d, inv_n, ws);
+    hipLaunchKernelGGL(xent_total, dim3(1), dim3(256), 0, st, ws, nb, inv_n, loss);
+    return launch_status("gnn_softmax_xent");
+}
+
+gnn_status_t launch_relu_mask(int64_t count, const void* dY, const void* Y, gnn_dtype_t y_dt, void* G,
+                              gnn_dtype_t g_dt, hipStream_t st) {
+    if (count == 0) return GNN_OK;
+    const int64_t blocks = (count + 1023) / 1024;
+#define GNN_RM(TY, TG)                                                                                      \
+    hipLaunchKernelGGL((relu_mask_kernel<TY, TG>), dim3(blocks), dim3(256), 0, st, count,                   \
+                       static_cast<const TY*>(dY), static_cast<const TY*>(Y), static_cast<TG*>(G))
+    if (y_dt == GNN_F32 && g_dt == GNN_F32) GNN_RM(float, float);
+    else if (y_dt == GNN_F32) GNN_RM(float, bf16_t);
+    else if (g_dt == GNN_F32) GNN_RM(bf16_t, float);
+    else GNN_RM(bf16_t, bf16_t);
+#undef GNN_RM
+    return launch_status("ReLU gradient mask");
+}
+
+}  // namespace gnnmp

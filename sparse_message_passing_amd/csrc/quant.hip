@@ -1,0 +1,199 @@
+// quant.hip -- per-row stochastic integer quantisation and dequantisation of
+// exchanged message rows (AdaQP, arXiv 2306.01381, Eqn. 4 and 5).
+//
+// Quantise, row r (node rows[r]) with b bits:
+//   Z = min(h), R = max(h) - min(h), inv = (2^b - 1)/R, S = R/(2^b - 1)
+//   x = (h - Z) * inv,  q = min(floor(x) + [u < x - floor(x)], 2^b - 1)
+// every operation an IEEE binary32 operation with one rounding (no
+// contraction), so the codes agree bit for bit with any other faithful
+// implementation.  u comes from Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC'11): counter
+// (node, f/4, stream, 0), key (seed low, seed high), word f%4, top 24 bits
+// times 2^-24.  Stateless, so a rerun draws the same numbers.
+//
+// One wave per row.  Lane l owns feature quads 4l, 4l+256, ...; one Philox
+// call yields exactly the four uniforms of a quad, and a quad's codes fill
+// b/2 whole bytes (2-bit: 1 byte, 4-bit: 2, 8-bit: 4), so each lane writes
+// its own bytes with one store and the row is written contiguously.
+// Dequantise: h = fma(q, S, Z), one rounding.
+
+#include "device.h"
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace gnnmp {
+
+namespace {
+
+constexpr int kMaxQuads = 4;  // d <= 1024
+
+struct U4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                            uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0, c1 = lo1, c2 = n2, c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return U4{c0, c1, c2, c3};
+}
+
+// minimum / maximum with -0 < +0, so the result is independent of the order
+// in which the row is scanned
+__device__ __forceinline__ float min_z(float a, float b) { return (b < a || (b == a && signbit(b))) ? b : a; }
+__device__ __forceinline__ float max_z(float a, float b) { return (b > a || (b == a && !signbit(b))) ? b : a; }
+
+__device__ __forceinline__ float u24(uint32_t w) { return static_cast<float>(w >> 8) * (1.0f / 16777216.0f); }
+
+__global__ __launch_bounds__(256) void quantize_kernel(const float* H, int64_t ldh, int64_t d, const int32_t* rows,
+                                                       int64_t n_rows, int bits, uint32_t k0, uint32_t k1,
+                                                       uint32_t stream_id, uint8_t* packed, float* scale,
+                                                       float* zero) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const uint32_t node = static_cast<uint32_t>(rows[r]);
+    const float* h = H + static_cast<int64_t>(node) * ldh;
+    const int64_t nq = (d + 3) / 4;
+    float x[kMaxQuads][4];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxQuads; ++i) {
+        const int64_t q = lane + 64 * i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t f = 4 * q + j;
+            x[i][j] = (q < nq && f < d) ? h[f] : 0.0f;
+            if (q < nq && f < d) {
+                mn = min_z(mn, x[i][j]);
+                mx = max_z(mx, x[i][j]);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = min_z(mn, __shfl_xor(mn, o, 64));
+        mx = max_z(mx, __shfl_xor(mx, o, 64));
+    }
+    const float R = __fsub_rn(mx, mn);
+    const uint32_t top = (1u << bits) - 1u;
+    const float levels = static_cast<float>(top);
+    const bool flat = !(R != 0.0f);
+    const float inv = flat ? 0.0f : __fdiv_rn(levels, R);
+    if (lane == 0) {
+        zero[r] = mn;
+        scale[r] = flat ? 0.0f : __fdiv_rn(R, levels);
+    }
+    const int64_t row_bytes = d * bits / 8;
+    uint8_t* out = packed + r * row_bytes;
+    const bool wide = (row_bytes % 4 == 0) && (reinterpret_cast<uintptr_t>(packed) % 4 == 0);
+#pragma unroll
+    for (int i = 0; i < kMaxQuads; ++i) {
+        const int64_t q = lane + 64 * i;
+        if (q >= nq) break;
+        uint32_t code[4] = {0u, 0u, 0u, 0u};
+        if (!flat) {
+            const U4 rnd = philox4x32_10(node, static_cast<uint32_t>(q), stream_id, 0u, k0, k1);
+            const uint32_t w[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = __fsub_rn(x[i][j], mn);
+                const float xs = __fmul_rn(t, inv);
+                const float fl = floorf(xs);
+                const float frac = __fsub_rn(xs, fl);
+                uint32_t c = static_cast<uint32_t>(fl) + (u24(w[j]) < frac ? 1u : 0u);
+                code[j] = c > top ? top : c;
+            }
+        }
+        const int64_t nvalid = min<int64_t>(4, d - 4 * q);
+        if (bits == 8) {
+            if (nvalid == 4 && wide) {
+                *reinterpret_cast<uint32_t*>(out + 4 * q) = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+            } else {
+                for (int j = 0; j < nvalid; ++j) out[4 * q + j] = static_cast<uint8_t>(code[j]);
+            }
+        } else if (bits == 4) {
+            const uint32_t lo = code[0] | (code[1] << 4), hi = code[2] | (code[3] << 4);
+            if (nvalid == 4 && wide) {
+                *reinterpret_cast<uint16_t*>(out + 2 * q) = static_cast<uint16_t>(lo | (hi << 8));
+            } else {
+                out[2 * q] = static_cast<uint8_t>(lo);  // d even: a partial quad holds 2 features
+                if (nvalid == 4) out[2 * q + 1] = static_cast<uint8_t>(hi);
+            }
+        } else {
+            out[q] = static_cast<uint8_t>(code[0] | (code[1] << 2) | (code[2] << 4) | (code[3] << 6));
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* packed, const float* scale, const float* zero,
+                                                         int64_t n_rows, int64_t d, int bits, const int32_t* rows,
+                                                         float* H, int64_t ldh) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const float S = scale[r], Z = zero[r];
+    const int64_t row_bytes = d * bits / 8;
+    const uint8_t* in = packed + r * row_bytes;
+    float* h = H + static_cast<int64_t>(rows[r]) * ldh;
+    const int64_t nq = (d + 3) / 4;
+    const uint32_t mask = (1u << bits) - 1u;
+    const bool vec = (ldh % 4 == 0) && (reinterpret_cast<uintptr_t>(H) % 16 == 0);
+    const bool wide = (row_bytes % 4 == 0) && (reinterpret_cast<uintptr_t>(packed) % 4 == 0);
+    for (int64_t q = lane; q < nq; q += 64) {
+        const int64_t nvalid = min<int64_t>(4, d - 4 * q);
+        uint32_t word;
+        if (bits == 8) {
+            if (nvalid == 4 && wide) word = *reinterpret_cast<const uint32_t*>(in + 4 * q);
+            else {
+                word = 0;
+                for (int j = 0; j < nvalid; ++j) word |= static_cast<uint32_t>(in[4 * q + j]) << (8 * j);
+            }
+        } else if (bits == 4) {
+            if (nvalid == 4 && wide) word = *reinterpret_cast<const uint16_t*>(in + 2 * q);
+            else word = static_cast<uint32_t>(in[2 * q]) | (nvalid == 4 ? static_cast<uint32_t>(in[2 * q + 1]) << 8 : 0u);
+        } else {
+            word = in[q];
+        }
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = __fmaf_rn(static_cast<float>((word >> (j * bits)) & mask), S, Z);
+        if (vec && nvalid == 4) {
+            *reinterpret_cast<float4*>(h + 4 * q) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+            for (int j = 0; j < nvalid; ++j) h[4 * q + j] = o[j];
+        }
+    }
+}
+
+}  // namespace
+
+gnn_status_t launch_quantize(const float* H, int64_t ldh, int64_t d, const int32_t* rows, int64_t n_rows, int bits,
+                             uint64_t seed, uint32_t stream_id, uint8_t* packed, float* scale, float* zero,
+                             hipStream_t st) {
+    if (n_rows == 0) return GNN_OK;
+    if (d > 64 * 4 * kMaxQuads) return fail(GNN_ERR_UNSUPPORTED, "gnn_quantize: d must be at most 1024");
+    const int64_t blocks = (n_rows + 3) / 4;
+    hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(256), 0, st, H, ldh, d, rows, n_rows, bits,
+                       static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), stream_id, packed, scale, zero);
+    return launch_status("gnn_quantize");
+}
+
+gnn_status_t launch_dequantize(const uint8_t* packed, const float* scale, const float* zero, int64_t n_rows,
+                               int64_t d, int bits, const int32_t* rows, float* H, int64_t ldh, hipStream_t st) {
+    if (n_rows == 0) return GNN_OK;
+    const int64_t blocks = (n_rows + 3) / 4;
+    hipLaunchKernelGGL(dequantize_kernel, dim3(blocks), dim3(256), 0, st, packed, scale, zero, n_rows, d, bits, rows,
+                       H, ldh);
+    return launch_status("gnn_dequantize");
+}
+
+}  // namespace gnnmp

@@ -1,0 +1,310 @@
+// spmm.hip -- aggregation Y = (G . w) X over the CSR (in-edges) or CSC
+// (out-edges) view.
+//
+// AdaQP (arXiv 2306.01381) Eqn. 3: the aggregation of node v is the weighted
+// sum of its neighbours' rows; Tango (SC'23), GAT running example:
+// "H(l) = (G . alpha) H'" with one weight per (edge, head), and the
+// backward SpMM over the reversed graph.
+//
+// Work decomposition (gfx950, wave64):
+//  * a "group" of LANES lanes owns one output row; lane l holds features
+//    (c*LANES + l)*VEC .. +VEC-1, so every gathered source row is read with
+//    fully coalesced 16-byte (fp32) or 8-byte (bf16) loads;
+//  * the group first loads LANES edge indices (and weights) in one coalesced
+//    access, then walks them by broadcasting each index from its lane
+//    (v_readlane for whole-wave groups, ds_bpermute otherwise), four source
+//    rows in flight per lane;
+//  * rows are visited in degree-descending order (the graph's `order`), and a
+//    row longer than kChunk edges is cut into kChunk-edge chunks that are
+//    independent work items writing binary32 partial rows; a second kernel
+//    adds each row's partials in chunk order.  No atomics: bitwise
+//    reproducible.
+
+#include "device.h"
+#include "internal.h"
+
+namespace gnnmp {
+
+namespace {
+
+constexpr int kMaxHeads = 8;
+
+struct SpmmArgs {
+    int64_t n;
+    const int64_t* ptr;
+    const int32_t* idx;
+    const int32_t* eid;
+    const int32_t* order;
+    int64_t n_heavy, n_chunks;
+    const int32_t* chunk_row;
+    const int32_t* chunk_first;
+    const float* dinv;
+    const float* edge_w;
+    int wmode;
+    int heads;
+    int64_t dh;
+    const void* X;
+    int64_t ldx;
+    void* Y;
+    int64_t ldy;
+    int64_t d;
+    int relu;
+    Rank1Epilogue r1;
+    float* partial;
+};
+
+template <int VEC>
+struct Acc {
+    float v[VEC];
+};
+
+template <int LANES, int VEC, int NCH, typename TI, typename TO>
+__global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
+    const int lane = threadIdx.x % LANES;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * (256 / LANES) + threadIdx.x / LANES;
+    int64_t row, eb, ee;
+    bool heavy;
+    if (gid < a.n_chunks) {
+        const int oi = a.chunk_row[gid];
+        row = a.order[oi];
+        const int64_t c = gid - a.chunk_first[oi];
+        eb = a.ptr[row] + c * kChunk;
+        ee = min(eb + kChunk, a.ptr[row + 1]);
+        heavy = true;
+    } else {
+        const int64_t li = gid - a.n_chunks + a.n_heavy;
+        if (li >= a.n) return;
+        row = a.order[li];
+        eb = a.ptr[row];
+        ee = a.ptr[row + 1];
+        heavy = false;
+    }
+    const TI* X = static_cast<const TI*>(a.X);
+
+    float acc[NCH][VEC];
+    int hd[NCH];
+    bool act[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int64_t f = static_cast<int64_t>(c * LANES + lane) * VEC;
+        act[c] = f < a.d;
+        hd[c] = act[c] ? static_cast<int>(f / a.dh) : 0;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[c][i] = 0.0f;
+    }
+    const float dv = a.wmode == GNN_W_GCN ? a.dinv[row] : 1.0f;
+    const int heads = a.heads;
+
+    for (int64_t e0 = eb; e0 < ee; e0 += LANES) {
+        const int cnt = static_cast<int>(min(static_cast<int64_t>(LANES), ee - e0));
+        int u_my = static_cast<int>(row);
+        float w_my[kMaxHeads];
+#pragma unroll
+        for (int k = 0; k < kMaxHeads; ++k) w_my[k] = 0.0f;
+        if (lane < cnt) {
+            const int64_t e = e0 + lane;
+            u_my = a.idx[e];
+            if (a.wmode == GNN_W_GCN) {
+                w_my[0] = a.dinv[u_my] * dv;
+            } else if (a.wmode == GNN_W_ONES) {
+                w_my[0] = 1.0f;
+            } else {
+                const int64_t ce = a.eid ? static_cast<int64_t>(a.eid[e]) : e;
+#pragma unroll
+                for (int k = 0; k < kMaxHeads; ++k)
+                    if (k < heads) w_my[k] = a.edge_w[ce * heads + k];
+            }
+        }
+        for (int j = 0; j < cnt; j += 4) {
+            int u[4];
+            float w[4][NCH];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int src = (j + q < cnt) ? j + q : j;
+                u[q] = group_bcast<LANES>(u_my, src);
+                if (heads == 1) {
+                    const float w0 = group_bcast<LANES>(w_my[0], src);
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) w[q][c] = w0;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) w[q][c] = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < kMaxHeads; ++k) {
+                        if (k < heads) {
+                            const float wk = group_bcast<LANES>(w_my[k], src);
+#pragma unroll
+                            for (int c = 0; c < NCH; ++c) w[q][c] = hd[c] == k ? wk : w[q][c];
+                        }
+                    }
+                }
+                if (j + q >= cnt) {
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c) w[q][c] = 0.0f;
+                }
+            }
+            Acc<VEC> xv[4][NCH];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    const int64_t f = static_cast<int64_t>(c * LANES + lane) * VEC;
+                    if (act[c] && j + q < cnt) {
+                        const TI* p = X + static_cast<int64_t>(u[q]) * a.ldx + f;
+                        if constexpr (VEC == 4) {
+                            float4 t = Elem<TI>::load4(p);
+                            xv[q][c].v[0] = t.x;
+                            xv[q][c].v[1] = t.y;
+                            xv[q][c].v[2] = t.z;
+                            xv[q][c].v[3] = t.w;
+                        } else {
+                            xv[q][c].v[0] = Elem<TI>::load(p);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < VEC; ++i) xv[q][c].v[i] = 0.0f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int c = 0; c < NCH; ++c)
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) acc[c][i] = fmaf(w[q][c], xv[q][c].v[i], acc[c][i]);
+        }
+    }
+
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (!act[c]) continue;
+        const int64_t f = static_cast<int64_t>(c * LANES + lane) * VEC;
+        if (heavy) {
+            float* P = a.partial + gid * a.d + f;
+            if constexpr (VEC == 4)
+                *reinterpret_cast<float4*>(P) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+            else
+                P[0] = acc[c][0];
+            continue;
+        }
+        if (a.r1.a) {
+            const float ra = a.r1.a[row * heads + hd[c]];
+            const float rb = a.r1.b[row * heads + hd[c]];
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                acc[c][i] = acc[c][i] + (ra * a.r1.va[f + i] + rb * a.r1.vb[f + i]);
+        }
+        if (a.relu) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[c][i] = fmaxf(acc[c][i], 0.0f);
+        }
+        TO* Y = static_cast<TO*>(a.Y) + row * a.ldy + f;
+        if constexpr (VEC == 4)
+            Elem<TO>::store4(Y, make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]));
+        else
+            Elem<TO>::store(Y, acc[c][0]);
+    }
+}
+
+// Sum the partial rows of each heavy row in chunk order, then the epilogue.
+template <typename TO>
+__global__ __launch_bounds__(256) void spmm_fixup(SpmmArgs a) {
+    const int64_t i = blockIdx.x;
+    const int64_t row = a.order[i];
+    const int64_t c0 = a.chunk_first[i], c1 = a.chunk_first[i + 1];
+    for (int64_t f = threadIdx.x; f < a.d; f += blockDim.x) {
+        float s = 0.0f;
+        for (int64_t c = c0; c < c1; ++c) s += a.partial[c * a.d + f];
+        if (a.r1.a) {
+            const int64_t h = f / a.dh;
+            s = s + (a.r1.a[row * a.heads + h] * a.r1.va[f] + a.r1.b[row * a.heads + h] * a.r1.vb[f]);
+        }
+        if (a.relu) s = fmaxf(s, 0.0f);
+        Elem<TO>::store(static_cast<TO*>(a.Y) + row * a.ldy + f, s);
+    }
+}
+
+template <int LANES, int VEC, int NCH, typename TI, typename TO>
+void launch_t(const SpmmArgs& a, hipStream_t st) {
+    const int64_t groups = a.n_chunks + (a.n - a.n_heavy);
+    const int64_t gpb = 256 / LANES;
+    const int64_t blocks = (groups + gpb - 1) / gpb;
+    if (blocks > 0) hipLaunchKernelGGL((spmm_kernel<LANES, VEC, NCH, TI, TO>), dim3(blocks), dim3(256), 0, st, a);
+    if (a.n_heavy > 0) hipLaunchKernelGGL((spmm_fixup<TO>), dim3(a.n_heavy), dim3(256), 0, st, a);
+}
+
+template <typename TI, typename TO>
+gnn_status_t dispatch(const SpmmArgs& a, int vec, int lanes, int nch, hipStream_t st) {
+    if (vec == 4) {
+        if (nch == 1) {
+            if (lanes == 16) launch_t<16, 4, 1, TI, TO>(a, st);
+            else if (lanes == 32) launch_t<32, 4, 1, TI, TO>(a, st);
+            else launch_t<64, 4, 1, TI, TO>(a, st);
+        } else if (nch == 2) {
+            launch_t<64, 4, 2, TI, TO>(a, st);
+        } else {
+            launch_t<64, 4, 4, TI, TO>(a, st);
+        }
+    } else {
+        if (nch == 1) launch_t<64, 1, 1, TI, TO>(a, st);
+        else if (nch == 2) launch_t<64, 1, 2, TI, TO>(a, st);
+        else launch_t<64, 1, 4, TI, TO>(a, st);
+    }
+    return launch_status("gnn_spmm");
+}
+
+}  // namespace
+
+size_t spmm_partial_bytes(const RowPlan& p, int64_t d) {
+    return p.n_chunks > 0 ? align_up(static_cast<size_t>(p.n_chunks) * d * sizeof(float)) : 0;
+}
+
+gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
+                         const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                         int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st) {
+    if (v.n == 0 || d == 0) return GNN_OK;
+    if (heads > kMaxHeads) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm: at most 8 heads");
+    SpmmArgs a;
+    a.n = v.n;
+    a.ptr = v.ptr;
+    a.idx = v.idx;
+    a.eid = v.eid;
+    a.order = v.plan->order;
+    a.n_heavy = v.plan->n_heavy;
+    a.n_chunks = v.plan->n_chunks;
+    a.chunk_row = v.plan->chunk_row;
+    a.chunk_first = v.plan->chunk_first;
+    a.dinv = dinv;
+    a.edge_w = edge_w;
+    a.wmode = wmode;
+    a.heads = heads;
+    a.dh = d / heads;
+    a.X = X;
+    a.ldx = ldx;
+    a.Y = Y;
+    a.ldy = ldy;
+    a.d = d;
+    a.relu = relu;
+    a.r1 = r1;
+    a.partial = partial;
+    const size_t xs = dt_size(x_dt), ys = dt_size(y_dt);
+    const bool aligned = (reinterpret_cast<uintptr_t>(X) % (4 * xs) == 0) &&
+                         (reinterpret_cast<uintptr_t>(Y) % (4 * ys) == 0);
+    const int vec = (d % 4 == 0 && ldx % 4 == 0 && ldy % 4 == 0 && (a.dh % 4 == 0) && aligned) ? 4 : 1;
+    const int64_t need = (d + vec - 1) / vec;  // lanes for one pass over the features
+    int lanes, nch;
+    if (vec == 4 && need <= 16) lanes = 16, nch = 1;
+    else if (vec == 4 && need <= 32) lanes = 32, nch = 1;
+    else {
+        lanes = 64;
+        nch = need <= 64 ? 1 : need <= 128 ? 2 : need <= 256 ? 4 : 0;
+        if (nch == 4 && need <= 192) nch = 4;
+    }
+    if (nch == 0) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm: d too large (max 1024 for 16-byte rows, 256 otherwise)");
+    if (x_dt == GNN_F32 && y_dt == GNN_F32) return dispatch<float, float>(a, vec, lanes, nch, st);
+    if (x_dt == GNN_F32 && y_dt == GNN_BF16) return dispatch<float, bf16_t>(a, vec, lanes, nch, st);
+    if (x_dt == GNN_BF16 && y_dt == GNN_F32) return dispatch<bf16_t, float>(a, vec, lanes, nch, st);
+    return dispatch<bf16_t, bf16_t>(a, vec, lanes, nch, st);
+}
+
+}  // namespace gnnmp

@@ -1,0 +1,320 @@
+"""Thin Python binding of libgnnmp.so (ctypes).
+
+Each function carries the name of the C entry point it calls and only
+marshals arguments: torch tensors give device pointers, the current torch
+stream gives the HIP stream, and workspaces are torch allocations.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgnnmp.so")
+
+GNN_F32, GNN_BF16 = 0, 1
+GNN_W_GCN, GNN_W_ONES, GNN_W_EDGE = 0, 1, 2
+GNN_GRAPH_SYMMETRIZE, GNN_GRAPH_CSC = 0x1, 0x2
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "out of memory", 4: "HIP error",
+          5: "graph lacks the required view", 6: "workspace too small"}
+
+# exported symbols and their argument types (P = pointer, I = int64, i = int32, U = uint32, Q = uint64, F = float, S = size_t)
+_SIGS = {
+    "gnn_status_string": ("i", "P"),
+    "gnn_last_error": ("", "P"),
+    "gnn_graph_create": ("IIPPUP", "i"),
+    "gnn_graph_destroy": ("P", "i"),
+    "gnn_graph_info": ("PP", "i"),
+    "gnn_graph_export": ("PPPPPPPPPP", "i"),
+    "gnn_spmm_workspace_size": ("PiI", "S"),
+    "gnn_spmm": ("PiiPiPiIPiIIiPSP", "i"),
+    "gnn_edge_reduce": ("PiPiPP", "i"),
+    "gnn_sddmm": ("PiPIPIiiIFPPP", "i"),
+    "gnn_edge_softmax": ("PPPiP", "i"),
+    "gnn_edge_softmax_bwd": ("PPPPFPiP", "i"),
+    "gnn_gemm_workspace_size": ("iiIII", "S"),
+    "gnn_gemm": ("iiIIIPiIPiIPiIPSP", "i"),
+    "gnn_softmax_xent_workspace_size": ("I", "S"),
+    "gnn_softmax_xent": ("PIIIPPPIPSP", "i"),
+    "gnn_quantize": ("PIIPIiQUPPPP", "i"),
+    "gnn_dequantize": ("PPPIIiPPIP", "i"),
+    "gnn_gcn_workspace_size": ("PII", "S"),
+    "gnn_gcn_layer_fwd": ("PPiIPIiPiPPSP", "i"),
+    "gnn_gcn_layer_bwd": ("PPiIPIiPPiPPPPSP", "i"),
+    "gnn_gat_saved_size": ("PiI", "S"),
+    "gnn_gat_workspace_size": ("PIiI", "S"),
+    "gnn_gat_layer_fwd": ("PPIPPPiIFPPPSP", "i"),
+    "gnn_gat_layer_bwd": ("PPIPPPiIFPPPPPPPSP", "i"),
+}
+_CT = {"P": C.c_void_p, "I": C.c_int64, "i": C.c_int, "U": C.c_uint32, "Q": C.c_uint64, "F": C.c_float,
+       "S": C.c_size_t}
+
+EXPORTED = tuple(_SIGS)
+
+
+class GnnError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class _Info(C.Structure):
+    _fields_ = [("n", C.c_int64), ("nnz", C.c_int64), ("max_in_degree", C.c_int64), ("max_out_degree", C.c_int64),
+                ("has_csc", C.c_int), ("row_ptr", C.c_void_p), ("col", C.c_void_p), ("dinv", C.c_void_p),
+                ("perm", C.c_void_p), ("col_ptr", C.c_void_p), ("csc_row", C.c_void_p), ("csc_eid", C.c_void_p),
+                ("perm_t", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_message_passing_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = [_CT[a] for a in args]
+            fn.restype = C.c_char_p if name in ("gnn_status_string", "gnn_last_error") else _CT[res]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise GnnError(status, lib().gnn_last_error().decode())
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    return t.data_ptr()
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return GNN_F32
+    if t.dtype == torch.bfloat16:
+        return GNN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _ld(t):
+    return t.stride(0) if t.dim() == 2 else t.shape[-1]
+
+
+# ---------------------------------------------------------------------------
+# graph
+# ---------------------------------------------------------------------------
+class Graph:
+    """Owns a library graph handle (CSR by destination, optional CSC view)."""
+
+    def __init__(self, handle, device):
+        self.h = handle
+        self.device = device
+        info = _Info()
+        _check(lib().gnn_graph_info(self.h, C.byref(info)))
+        self.n, self.nnz = info.n, info.nnz
+        self.max_in_degree, self.max_out_degree = info.max_in_degree, info.max_out_degree
+        self.has_csc = bool(info.has_csc)
+
+    def __del__(self):
+        if getattr(self, "h", None) and _lib is not None:
+            _lib.gnn_graph_destroy(self.h)
+            self.h = None
+
+
+def gnn_graph_create(n, src, dst, symmetrize=False, csc=False, device="cuda"):
+    src = np.ascontiguousarray(src, dtype=np.int32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst differ in length")
+    torch.cuda.set_device(torch.device(device))
+    h = C.c_void_p()
+    flags = (GNN_GRAPH_SYMMETRIZE if symmetrize else 0) | (GNN_GRAPH_CSC if csc else 0)
+    _check(lib().gnn_graph_create(int(n), src.size, src.ctypes.data_as(C.c_void_p), dst.ctypes.data_as(C.c_void_p),
+                                  flags, C.byref(h)))
+    return Graph(h, torch.device(device))
+
+
+def gnn_graph_export(g: Graph):
+    n, e = g.n, g.nnz
+    out = dict(row_ptr=np.empty(n + 1, np.int64), col=np.empty(e, np.int32), dinv=np.empty(n, np.float32),
+               w=np.empty(e, np.float32), perm=np.empty(n, np.int32))
+    if g.has_csc:
+        out.update(col_ptr=np.empty(n + 1, np.int64), csc_row=np.empty(e, np.int32), csc_eid=np.empty(e, np.int32),
+                   perm_t=np.empty(n, np.int32))
+    P = lambda k: out[k].ctypes.data_as(C.c_void_p) if k in out else None
+    _check(lib().gnn_graph_export(g.h, P("row_ptr"), P("col"), P("dinv"), P("w"), P("perm"), P("col_ptr"),
+                                  P("csc_row"), P("csc_eid"), P("perm_t")))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# primitives
+# ---------------------------------------------------------------------------
+def gnn_spmm(g: Graph, X, Y, weights="gcn", heads=1, transpose=False, relu=False, d=None, ws=None):
+    """Y = (G . w) X (transpose: over the reversed graph), optional ReLU.
+    weights: "gcn", "ones" or an f32 tensor [nnz, heads]."""
+    d = X.shape[1] if d is None else d
+    if isinstance(weights, str):
+        wmode, ew = {"gcn": GNN_W_GCN, "ones": GNN_W_ONES}[weights], None
+    else:
+        wmode, ew = GNN_W_EDGE, weights
+    need = lib().gnn_spmm_workspace_size(g.h, int(transpose), d)
+    if ws is None:
+        ws = _ws(need, X.device)
+    _check(lib().gnn_spmm(g.h, int(transpose), wmode, _p(ew), heads, _p(X), _dt(X), _ld(X), _p(Y), _dt(Y), _ld(Y), d,
+                          int(relu), _p(ws), ws.numel(), _stream()))
+    return Y
+
+
+def gnn_edge_reduce(g: Graph, vals, out, by_src=False):
+    _check(lib().gnn_edge_reduce(g.h, int(by_src), _p(vals), vals.shape[1], _p(out), _stream()))
+    return out
+
+
+def gnn_sddmm(g: Graph, op, src_feat, dst_feat, heads, d_head, out, slope=float("nan"), out_pre=None):
+    """op "add": out = LReLU(src[u,k] + dst[v,k]); op "dot": out = <src[u, head k], dst[v, head k]>."""
+    opc = {"add": 0, "dot": 1}[op]
+    _check(lib().gnn_sddmm(g.h, opc, _p(src_feat), _ld(src_feat), _p(dst_feat), _ld(dst_feat), _dt(src_feat), heads,
+                           d_head, float(slope), _p(out), _p(out_pre), _stream()))
+    return out
+
+
+def gnn_edge_softmax(g: Graph, E, alpha):
+    _check(lib().gnn_edge_softmax(g.h, _p(E), _p(alpha), E.shape[1], _stream()))
+    return alpha
+
+
+def gnn_edge_softmax_bwd(g: Graph, alpha, dalpha, dE, lrelu_pre=None, slope=0.0):
+    _check(lib().gnn_edge_softmax_bwd(g.h, _p(alpha), _p(dalpha), _p(lrelu_pre), float(slope), _p(dE),
+                                      alpha.shape[1], _stream()))
+    return dE
+
+
+def gnn_gemm(A, B, C_, transA=False, transB=False, ws=None):
+    """C = op(A) op(B)."""
+    M = A.shape[1] if transA else A.shape[0]
+    K = A.shape[0] if transA else A.shape[1]
+    N = B.shape[0] if transB else B.shape[1]
+    if (B.shape[1] if transB else B.shape[0]) != K or tuple(C_.shape) != (M, N):
+        raise ValueError("gnn_gemm: shape mismatch")
+    need = lib().gnn_gemm_workspace_size(int(transA), int(transB), M, N, K)
+    if ws is None:
+        ws = _ws(need, A.device)
+    _check(lib().gnn_gemm(int(transA), int(transB), M, N, K, _p(A), _dt(A), _ld(A), _p(B), _dt(B), _ld(B), _p(C_),
+                          _dt(C_), _ld(C_), _p(ws), ws.numel(), _stream()))
+    return C_
+
+
+def gnn_softmax_xent(logits, labels, loss, dlogits=None, ws=None):
+    n, c = logits.shape
+    if ws is None:
+        ws = _ws(lib().gnn_softmax_xent_workspace_size(n), logits.device)
+    _check(lib().gnn_softmax_xent(_p(logits), n, c, _ld(logits), _p(labels), _p(loss), _p(dlogits),
+                                  _ld(dlogits) if dlogits is not None else c, _p(ws), ws.numel(), _stream()))
+    return loss
+
+
+def gnn_quantize(H, rows, bits, seed, packed, scale, zero, stream_id=0, d=None):
+    d = H.shape[1] if d is None else d
+    _check(lib().gnn_quantize(_p(H), _ld(H), d, _p(rows), rows.numel(), bits, int(seed), int(stream_id), _p(packed),
+                              _p(scale), _p(zero), _stream()))
+    return packed, scale, zero
+
+
+def gnn_dequantize(packed, scale, zero, rows, bits, H, d=None):
+    d = H.shape[1] if d is None else d
+    _check(lib().gnn_dequantize(_p(packed), _p(scale), _p(zero), rows.numel(), d, bits, _p(rows), _p(H), _ld(H),
+                                _stream()))
+    return H
+
+
+# ---------------------------------------------------------------------------
+# layers
+# ---------------------------------------------------------------------------
+def gnn_gcn_workspace_size(g: Graph, d_in, d_out):
+    return lib().gnn_gcn_workspace_size(g.h, d_in, d_out)
+
+
+def gnn_gcn_layer_fwd(g: Graph, X, W, Y, relu, saved=None, ws=None):
+    d_in, d_out = W.shape
+    if ws is None:
+        ws = _ws(gnn_gcn_workspace_size(g, d_in, d_out), X.device)
+    _check(lib().gnn_gcn_layer_fwd(g.h, _p(X), _dt(X), d_in, _p(W), d_out, int(relu), _p(Y), _dt(Y), _p(saved),
+                                   _p(ws), ws.numel(), _stream()))
+    return Y
+
+
+def gnn_gcn_layer_bwd(g: Graph, X, W, Y, dY, relu, dW, dX=None, saved=None, ws=None):
+    d_in, d_out = W.shape
+    if ws is None:
+        ws = _ws(gnn_gcn_workspace_size(g, d_in, d_out), dY.device)
+    x_dt = _dt(X) if X is not None else _dt(saved)
+    _check(lib().gnn_gcn_layer_bwd(g.h, _p(X), x_dt, d_in, _p(W), d_out, int(relu), _p(Y), _p(dY), _dt(dY),
+                                   _p(saved), _p(dX), _p(dW), _p(ws), ws.numel(), _stream()))
+    return dX, dW
+
+
+def gnn_gat_saved_size(g: Graph, heads, d_head):
+    return lib().gnn_gat_saved_size(g.h, heads, d_head)
+
+
+def gnn_gat_workspace_size(g: Graph, d_in, heads, d_head):
+    return lib().gnn_gat_workspace_size(g.h, d_in, heads, d_head)
+
+
+def gnn_gat_layer_fwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, Y, saved, ws=None):
+    d_in = X.shape[1]
+    if ws is None:
+        ws = _ws(gnn_gat_workspace_size(g, d_in, heads, d_head), X.device)
+    _check(lib().gnn_gat_layer_fwd(g.h, _p(X), d_in, _p(W), _p(a_src), _p(a_dst), heads, d_head, float(slope), _p(Y),
+                                   _p(saved), _p(ws), ws.numel(), _stream()))
+    return Y
+
+
+def gnn_gat_layer_bwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, dY, saved, dW, da_src, da_dst, dX=None,
+                      ws=None):
+    d_in = X.shape[1]
+    if ws is None:
+        ws = _ws(gnn_gat_workspace_size(g, d_in, heads, d_head), X.device)
+    _check(lib().gnn_gat_layer_bwd(g.h, _p(X), d_in, _p(W), _p(a_src), _p(a_dst), heads, d_head, float(slope), _p(dY),
+                                   _p(saved), _p(dX), _p(dW), _p(da_src), _p(da_dst), _p(ws), ws.numel(), _stream()))
+    return dX, dW, da_src, da_dst
+
+
+def gat_saved_views(g: Graph, saved, heads, d_head):
+    """Views (H', S, D, E_pre, alpha) into a GAT forward's saved buffer (the
+    same 256-byte aligned slices the library carves)."""
+    f = saved.view(torch.float32) if saved.dtype == torch.uint8 else saved
+    al = lambda b: (b + 255) // 256 * 256
+    n, e, hd = g.n, g.nnz, heads * d_head
+    off = 0
+    out = []
+    for count, shape in ((n * hd, (n, hd)), (n * heads, (n, heads)), (n * heads, (n, heads)),
+                         (e * heads, (e, heads)), (e * heads, (e, heads))):
+        out.append(f[off // 4: off // 4 + count].view(*shape))
+        off += al(count * 4)
+    return tuple(out)

@@ -1,0 +1,150 @@
+"""Whole steps of the hot path over the C ABI, with every buffer allocated
+once up front (torch supplies device memory; all arithmetic runs in
+libgnnmp's kernels):
+
+* ``GcnStack``  -- an L-layer GCN (ReLU on hidden layers, none on the
+  logits), mean softmax cross-entropy, and the backward pass down to the
+  first layer's weight gradient.
+* ``GatLayer``  -- one GAT layer forward and backward for a given upstream
+  gradient.
+* ``QuantExchange`` -- one partition's quantised exchange: the marginal rows
+  are quantised (one call per bit-width group) and dequantised into the
+  aggregation input, then aggregated with the GCN operator.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import gnnmp
+
+
+def _dt(name):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+class GcnStack:
+    def __init__(self, g: gnnmp.Graph, X, Ws, labels, dtype="f32"):
+        self.g = g
+        dev = X.device
+        self.dt = _dt(dtype)
+        self.X = X.to(self.dt).contiguous()
+        self.Ws = [w.contiguous() for w in Ws]
+        self.labels = labels
+        n = g.n
+        L = len(Ws)
+        self.widths = [Ws[0].shape[0]] + [w.shape[1] for w in Ws]
+        # activations: hidden layers in the storage type, logits in binary32
+        self.H = [self.X] + [torch.empty((n, self.widths[i + 1]), dtype=self.dt if i < L - 1 else torch.float32,
+                                         device=dev) for i in range(L)]
+        self.saved = [torch.empty((n, self.widths[i]), dtype=self.dt, device=dev)
+                      if self.widths[i + 1] > self.widths[i] else None for i in range(L)]
+        self.dW = [torch.empty_like(w) for w in self.Ws]
+        self.dH = [None] + [torch.empty((n, self.widths[i]), dtype=self.dt, device=dev) for i in range(1, L)]
+        self.dlogits = torch.empty((n, self.widths[-1]), dtype=torch.float32, device=dev)
+        self.loss = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = max(gnnmp.gnn_gcn_workspace_size(g, self.widths[i], self.widths[i + 1]) for i in range(L))
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.xent_ws = torch.empty(max(gnnmp.lib().gnn_softmax_xent_workspace_size(n), 1), dtype=torch.uint8,
+                                   device=dev)
+
+    def forward(self):
+        L = len(self.Ws)
+        for i in range(L):
+            gnnmp.gnn_gcn_layer_fwd(self.g, self.H[i], self.Ws[i], self.H[i + 1], relu=i < L - 1,
+                                    saved=self.saved[i], ws=self.ws)
+        gnnmp.gnn_softmax_xent(self.H[-1], self.labels, self.loss, self.dlogits, ws=self.xent_ws)
+        return self.loss
+
+    def backward(self):
+        L = len(self.Ws)
+        dY = self.dlogits
+        for i in reversed(range(L)):
+            gnnmp.gnn_gcn_layer_bwd(self.g, self.H[i], self.Ws[i], self.H[i + 1], dY, relu=i < L - 1, dW=self.dW[i],
+                                    dX=self.dH[i] if i > 0 else None, saved=self.saved[i], ws=self.ws)
+            dY = self.dH[i]
+        return self.dW
+
+    def step(self):
+        self.forward()
+        return self.backward()
+
+    def spmm_edge_feats(self):
+        """Edge x feature products one step aggregates (forward + backward)."""
+        L = len(self.Ws)
+        tot = 0
+        for i in range(L):
+            din, dout = self.widths[i], self.widths[i + 1]
+            agg = min(din, dout) if dout <= din else din
+            tot += agg                       # forward aggregation
+            if dout <= din:
+                tot += dout                  # backward: A_hat G
+            elif i > 0:
+                tot += din                   # backward: A_hat (G W^T), not formed for layer 0
+        return tot * self.g.nnz
+
+
+class GatLayer:
+    def __init__(self, g: gnnmp.Graph, X, W, a_src, a_dst, heads, d_head, slope, dY):
+        self.g, self.X, self.W = g, X.contiguous(), W.contiguous()
+        self.a_src, self.a_dst = a_src.contiguous(), a_dst.contiguous()
+        self.heads, self.d_head, self.slope = heads, d_head, slope
+        self.dY = dY.contiguous()
+        dev = X.device
+        n, hd = g.n, heads * d_head
+        self.Y = torch.empty((n, hd), device=dev)
+        self.saved = torch.empty(gnnmp.gnn_gat_saved_size(g, heads, d_head), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(gnnmp.gnn_gat_workspace_size(g, X.shape[1], heads, d_head), 1), dtype=torch.uint8,
+                              device=dev)
+        self.dX = torch.empty_like(self.X)
+        self.dW = torch.empty_like(self.W)
+        self.da_src = torch.empty_like(self.a_src)
+        self.da_dst = torch.empty_like(self.a_dst)
+
+    def forward(self):
+        return gnnmp.gnn_gat_layer_fwd(self.g, self.X, self.W, self.a_src, self.a_dst, self.heads, self.d_head,
+                                       self.slope, self.Y, self.saved, ws=self.ws)
+
+    def backward(self, need_dX=True):
+        return gnnmp.gnn_gat_layer_bwd(self.g, self.X, self.W, self.a_src, self.a_dst, self.heads, self.d_head,
+                                       self.slope, self.dY, self.saved, self.dW, self.da_src, self.da_dst,
+                                       dX=self.dX if need_dX else None, ws=self.ws)
+
+    def step(self):
+        self.forward()
+        return self.backward()
+
+
+class QuantExchange:
+    def __init__(self, g: gnnmp.Graph, H, rows, bits, seed, stream_id=0):
+        """bits: 2, 4, 8, or an int array giving each row's width."""
+        self.g, self.H = g, H.contiguous()
+        dev = H.device
+        d = H.shape[1]
+        rows = np.asarray(rows, np.int32)
+        b = np.full(rows.size, bits, np.int32) if np.isscalar(bits) else np.asarray(bits, np.int32)
+        self.groups = []
+        for bb in (2, 4, 8):
+            sel = rows[b == bb]
+            if sel.size == 0:
+                continue
+            self.groups.append((bb, torch.from_numpy(sel).to(dev),
+                                torch.empty((sel.size, d * bb // 8), dtype=torch.uint8, device=dev),
+                                torch.empty(sel.size, device=dev), torch.empty(sel.size, device=dev)))
+        self.seed, self.stream_id = seed, stream_id
+        self.Hmix = self.H.clone()
+        self.Y = torch.empty_like(self.H)
+        self.ws = torch.empty(max(gnnmp.lib().gnn_spmm_workspace_size(g.h, 0, d), 1), dtype=torch.uint8, device=dev)
+
+    def quantize(self):
+        for bb, rows, pk, sc, zr in self.groups:
+            gnnmp.gnn_quantize(self.H, rows, bb, self.seed, pk, sc, zr, stream_id=self.stream_id)
+
+    def dequantize(self):
+        for bb, rows, pk, sc, zr in self.groups:
+            gnnmp.gnn_dequantize(pk, sc, zr, rows, bb, self.Hmix)
+
+    def step(self):
+        self.quantize()
+        self.dequantize()
+        return gnnmp.gnn_spmm(self.g, self.Hmix, self.Y, ws=self.ws)

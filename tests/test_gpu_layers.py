@@ -1,0 +1,199 @@
+"""GPU parity of the layer entry points (GCN and GAT, forward and backward)
+against the oracle's compositions.  Backward tests feed both sides the
+oracle's forward tensors, so ReLU / LeakyReLU decisions are identical and
+every output is checked element by element; the whole multi-layer step is
+checked end to end in norm (there a decision near zero may legitimately
+flip between two correct roundings)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (RTOL16, RTOL32, check_close, from_dev, graph_pair, hub_edges, rmat_graph, to_dev)
+from sparse_message_passing_amd import gnnmp, synth
+from sparse_message_passing_amd.step import GcnStack
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def gcn_mag(og, X, W):
+    """Magnitude |A_hat| |X| |W| of a GCN layer output (either operand order)."""
+    w = og.gcn_norm()[1]
+    return oracle.spmm(og, np.abs(X) @ np.abs(W), np.abs(w))
+
+
+@pytest.fixture(scope="module")
+def c1():
+    inp = synth.config_inputs(1)
+    g, og = graph_pair(inp["src"], inp["dst"], int(inp["n"]), True, csc=False)
+    return g, og, inp
+
+
+def test_c1_gcn_layer_forward(c1):
+    # ReLU(A_hat (H W)): 1000 nodes, G(n, m) + self-loops, 64 -> 64
+    g, og, inp = c1
+    X, W = inp["X"], inp["W0"]
+    ref, _ = oracle.gcn_layer_fwd(og, X, W, relu=True)
+    Y = torch.empty((og.n, 64), device="cuda")
+    gnnmp.gnn_gcn_layer_fwd(g, to_dev(X), to_dev(W), Y, relu=True)
+    check_close(from_dev(Y), ref, gcn_mag(og, X, W), what="C1 forward")
+
+
+@pytest.fixture(scope="module")
+def hubsym():
+    s, t = hub_edges(6000, 40000, 2500, 31)
+    return graph_pair(s, t, 6000, True, csc=False)
+
+
+GCN_CASES = [  # d_in, d_out, relu, storage dtype, output dtype
+    (64, 64, True, "f32", "f32"),
+    (48, 96, True, "f32", "f32"),
+    (256, 41, False, "f32", "f32"),
+    (100, 256, True, "bf16", "bf16"),
+    (256, 47, False, "bf16", "f32"),
+    (256, 256, True, "bf16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", GCN_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_gcn_layer_fwd_bwd(hubsym, case):
+    d_in, d_out, relu, dt, out_dt = case
+    g, og = hubsym
+    r = np.random.default_rng(d_in * d_out)
+    X = oracle.store(r.standard_normal((og.n, d_in)), dt)
+    W = synth.glorot(d_in, d_out, 5)
+    rtol = RTOL16 if dt == "bf16" else RTOL32
+    # forward
+    Y_ref, saved_ref = oracle.gcn_layer_fwd(og, X, W, relu, dt=dt, out_dt=out_dt)
+    Xd = to_dev(X, TDT[dt])
+    Wd = to_dev(W)
+    Y = torch.empty((og.n, d_out), dtype=TDT[out_dt], device="cuda")
+    saved = torch.empty((og.n, d_in), dtype=TDT[dt], device="cuda") if d_out > d_in else None
+    gnnmp.gnn_gcn_layer_fwd(g, Xd, Wd, Y, relu=relu, saved=saved)
+    check_close(from_dev(Y), Y_ref, gcn_mag(og, X, W), rtol=rtol, bf16_out=out_dt == "bf16", what="gcn fwd")
+    # backward from the oracle's forward tensors
+    dY = oracle.store(r.standard_normal((og.n, d_out)), out_dt)
+    dX_ref, dW_ref = oracle.gcn_layer_bwd(og, X, saved_ref, Y_ref, dY, W, relu, need_dX=True, dt=dt)
+    w = og.gcn_norm()[1]
+    G = np.abs(np.where(Y_ref > 0, dY, 0.0)) if relu else np.abs(dY)
+    if d_out <= d_in:
+        MdZ = oracle.spmm(og, G, np.abs(w))
+        mag_dW = np.abs(X).T.astype(np.float64) @ MdZ
+        mag_dX = MdZ @ np.abs(W).T
+    else:
+        mag_dW = oracle.spmm(og, np.abs(X), np.abs(w)).T @ G
+        mag_dX = oracle.spmm(og, G @ np.abs(W).T, np.abs(w))
+    dYd = to_dev(dY, TDT[out_dt])
+    Yd = to_dev(Y_ref, TDT[out_dt])
+    sv = to_dev(saved_ref, TDT[dt]) if saved_ref is not None else None
+    dW = torch.empty((d_in, d_out), device="cuda")
+    dX = torch.empty((og.n, d_in), dtype=TDT[dt], device="cuda")
+    gnnmp.gnn_gcn_layer_bwd(g, Xd, Wd, Yd, dYd, relu, dW, dX=dX, saved=sv)
+    check_close(from_dev(dW), dW_ref, mag_dW, rtol=rtol, what="gcn dW")
+    check_close(from_dev(dX), dX_ref, mag_dX, rtol=rtol, bf16_out=dt == "bf16", what="gcn dX")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gcn_three_layer_step(dt):
+    # the multi-layer forward + backward + loss of the 3-layer workloads, scaled down
+    s, t, n = rmat_graph(13, 16, True, 2001)
+    g, og = graph_pair(s, t, n, True, csc=False)
+    r = np.random.default_rng(1)
+    widths = [128, 256, 256, 41] if dt == "f32" else [100, 256, 256, 47]
+    X = oracle.store(r.standard_normal((n, widths[0])), dt)
+    Ws = [synth.glorot(widths[i], widths[i + 1], 10 + i) for i in range(3)]
+    lab = r.integers(0, widths[-1], n).astype(np.int32)
+    ref = oracle.gcn_forward_backward(og, X, Ws, lab, dt=dt)
+    st = GcnStack(g, to_dev(X, TDT[dt]), [to_dev(w) for w in Ws], to_dev(lab), dtype=dt)
+    st.step()
+    torch.cuda.synchronize()
+    tol = 1e-4 if dt == "f32" else 2e-2
+    assert abs(st.loss.item() - ref["loss"]) <= tol * abs(ref["loss"])
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel(from_dev(st.H[-1]), ref["logits"]) <= tol
+    for i in range(3):
+        assert rel(from_dev(st.dW[i]), ref["dW"][i]) <= tol * (3 if dt == "f32" else 1), i
+    # deterministic: a second step gives the same bits
+    dW0 = [w.clone() for w in st.dW]
+    st.step()
+    assert all(torch.equal(a, b) for a, b in zip(dW0, st.dW))
+
+
+# ---------------------------------------------------------------------------
+# GAT
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def gatg():
+    s, t = hub_edges(3000, 30000, 2300, 41)
+    return graph_pair(s, t, 3000, False, csc=True)
+
+
+@pytest.mark.parametrize("heads,dh,din", [(4, 64, 256), (2, 32, 48), (1, 64, 64)])
+def test_gat_layer_fwd_bwd(gatg, heads, dh, din):
+    g, og = gatg
+    n, hd = og.n, heads * dh
+    r = np.random.default_rng(heads * dh + din)
+    X = r.standard_normal((n, din)).astype(np.float32)
+    W = synth.glorot(din, hd, 3)
+    a_s = synth.glorot(dh, 1, 4, shape=(heads, dh))
+    a_d = synth.glorot(dh, 1, 5, shape=(heads, dh))
+    slope = 0.2
+    fw = oracle.gat_layer_fwd(og, X, W, a_s, a_d, heads, slope)
+    Xd, Wd, asd, add = to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d)
+    Y = torch.empty((n, hd), device="cuda")
+    saved = torch.empty(gnnmp.gnn_gat_saved_size(g, heads, dh), dtype=torch.uint8, device="cuda")
+    gnnmp.gnn_gat_layer_fwd(g, Xd, Wd, asd, add, heads, dh, slope, Y, saved)
+    Hp, S, D, Ep, al = gnnmp.gat_saved_views(g, saved, heads, dh)
+    mHp = np.abs(X) @ np.abs(W)
+    check_close(from_dev(Hp), fw["Hp"], mHp, what="H'")
+    mS = oracle.gat_scores(mHp, np.abs(a_s), heads)
+    mD = oracle.gat_scores(mHp, np.abs(a_d), heads)
+    check_close(from_dev(S), fw["S"], mS, what="S")
+    check_close(from_dev(D), fw["D"], mD, what="D")
+    mE = mS[og.col] + mD[og.dst]
+    check_close(from_dev(Ep), fw["E_pre"], mE, what="E_pre")
+    # alpha moves by at most alpha * 2 max|dE| over the destination's in-edges
+    rowmax = np.maximum.reduceat(mE, og.row_ptr[:-1], axis=0)[og.dst]
+    m_al = fw["alpha"] * (2 * rowmax + 1)
+    check_close(from_dev(al), fw["alpha"], m_al, what="alpha")
+    mY = oracle.spmm(og, mHp, m_al, heads) + oracle.spmm(og, np.abs(fw["Hp"]), fw["alpha"], heads)
+    check_close(from_dev(Y), fw["Y"], mY, what="GAT Y")
+
+    # backward on the oracle's saved tensors
+    for view, key in zip((Hp, S, D, Ep, al), ("Hp", "S", "D", "E_pre", "alpha")):
+        view.copy_(to_dev(fw[key]))
+    dY = r.standard_normal((n, hd)).astype(np.float32)
+    bw = oracle.gat_layer_bwd(og, fw, X, W, a_s, a_d, dY, heads, slope)
+    dX = torch.empty((n, din), device="cuda")
+    dW = torch.empty((din, hd), device="cuda")
+    das = torch.empty((heads, dh), device="cuda")
+    dad = torch.empty((heads, dh), device="cuda")
+    gnnmp.gnn_gat_layer_bwd(g, Xd, Wd, asd, add, heads, dh, slope, to_dev(dY), saved, dW, das, dad, dX=dX)
+    A = np.abs(fw["alpha"])
+    m_dal = oracle.sddmm_dot(og, np.abs(dY), np.abs(fw["Hp"]), heads)
+    m_dE = A * (m_dal + oracle.edge_reduce(og, A * m_dal)[og.dst])
+    fac = np.where(fw["E_pre"] > 0, 1.0, slope)
+    m_dEp = m_dE * fac
+    m_dD = oracle.edge_reduce(og, m_dEp)
+    m_dS = oracle.edge_reduce(og, m_dEp, by_src=True)
+    m_dHp = (oracle.spmm(og, np.abs(dY), A, heads, transpose=True)
+             + (m_dS[:, :, None] * np.abs(a_s)[None] + m_dD[:, :, None] * np.abs(a_d)[None]).reshape(n, hd))
+    H3 = np.abs(fw["Hp"]).reshape(n, heads, dh)
+    check_close(from_dev(das), bw["da_src"], np.einsum("nk,nkj->kj", m_dS, H3), what="da_src")
+    check_close(from_dev(dad), bw["da_dst"], np.einsum("nk,nkj->kj", m_dD, H3), what="da_dst")
+    check_close(from_dev(dW), bw["dW"], np.abs(X).T @ m_dHp, what="GAT dW")
+    check_close(from_dev(dX), bw["dX"], m_dHp @ np.abs(W).T, what="GAT dX")
+
+
+def test_gat_bwd_requires_csc():
+    s, t = hub_edges(100, 300, 10, 1)
+    g = gnnmp.gnn_graph_create(100, s, t, csc=False)
+    X = torch.zeros((100, 64), device="cuda")
+    W = torch.zeros((64, 64), device="cuda")
+    a = torch.zeros((1, 64), device="cuda")
+    saved = torch.zeros(gnnmp.gnn_gat_saved_size(g, 1, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(gnnmp.GnnError, match="CSC"):
+        gnnmp.gnn_gat_layer_bwd(g, X, W, a, a, 1, 64, 0.2, torch.zeros((100, 64), device="cuda"), saved,
+                                torch.empty_like(W), torch.empty_like(a), torch.empty_like(a))

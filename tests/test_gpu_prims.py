@@ -1,0 +1,381 @@
+"""GPU parity of every C-ABI primitive against the CPU oracle, element by
+element, on seeded inputs that span several tiles and a ragged tail, with
+hub rows that take the chunked and whole-workgroup paths."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (RTOL32, bf16_values, check_close, from_dev, graph_pair, hub_edges, rmat_graph, to_dev)
+from sparse_message_passing_amd import gnnmp, synth
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# graph layer: bit-exact
+# ---------------------------------------------------------------------------
+def _graph_cases():
+    r = np.random.default_rng(0)
+    s = r.integers(0, 37, 200).astype(np.int32)
+    t = r.integers(0, 37, 200).astype(np.int32)
+    s[:30] = t[:30]                                  # self-loops
+    s = np.concatenate([s, s[:50]])                  # repeats
+    t = np.concatenate([t, t[:50]])
+    yield "tiny-directed", s, t, 37, False
+    yield "tiny-sym", s, t, 37, True
+    s1, t1 = synth.gnm_pairs(1000, 5000, 1001)
+    yield "gnm1000", s1, t1, 1000, True
+    s2, t2, n2 = rmat_graph(13, 16, True, 5)
+    yield "rmat13-sym", s2, t2, n2, True
+    s3, t3 = hub_edges(6000, 20000, 4500, 3)
+    yield "hub-directed", s3, t3, 6000, False
+    yield "empty", np.zeros(0, np.int32), np.zeros(0, np.int32), 5, True
+
+
+@pytest.mark.parametrize("case", list(_graph_cases()), ids=lambda c: c[0])
+def test_graph_build_bit_exact(case):
+    _, s, t, n, sym = case
+    g, og = graph_pair(s, t, n, sym, csc=True)
+    ex = gnnmp.gnn_graph_export(g)
+    assert g.n == og.n and g.nnz == og.nnz
+    assert np.array_equal(ex["row_ptr"], og.row_ptr)
+    assert np.array_equal(ex["col"], og.col)
+    dinv, w = og.gcn_norm()
+    assert np.array_equal(ex["dinv"].view(np.uint32), dinv.view(np.uint32))
+    assert np.array_equal(ex["w"].view(np.uint32), w.view(np.uint32))
+    assert np.array_equal(ex["perm"], og.degree_perm())
+    colptr, row, eid = og.csc()
+    assert np.array_equal(ex["col_ptr"], colptr)
+    assert np.array_equal(ex["csc_row"], row)
+    assert np.array_equal(ex["csc_eid"], eid)
+    # out-degree order of the transposed view
+    od = np.diff(colptr)
+    ids = np.arange(n)
+    assert np.array_equal(ex["perm_t"], np.lexsort((ids, -od)).astype(np.int32))
+    assert g.max_in_degree == (og.deg.max() if n else 0)
+
+
+# ---------------------------------------------------------------------------
+# SpMM
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def hubg():
+    s, t = hub_edges(5000, 40000, 3000, 11)
+    return graph_pair(s, t, 5000, True, csc=True)
+
+
+SPMM_CASES = [
+    # d, weights, heads, transpose, relu, x_dt, y_dt
+    (256, "gcn", 1, False, False, "f32", "f32"),
+    (256, "gcn", 1, False, True, "f32", "f32"),
+    (128, "gcn", 1, False, False, "f32", "f32"),
+    (64, "ones", 1, False, False, "f32", "f32"),
+    (41, "gcn", 1, False, False, "f32", "f32"),
+    (3, "gcn", 1, False, True, "f32", "f32"),
+    (1, "ones", 1, True, False, "f32", "f32"),
+    (100, "gcn", 1, False, True, "bf16", "bf16"),
+    (256, "gcn", 1, False, False, "bf16", "f32"),
+    (47, "gcn", 1, False, False, "f32", "bf16"),
+    (256, "edge", 4, False, False, "f32", "f32"),
+    (256, "edge", 4, True, False, "f32", "f32"),
+    (64, "edge", 2, True, False, "f32", "f32"),
+    (512, "gcn", 1, False, False, "f32", "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SPMM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_spmm(hubg, case):
+    d, wname, heads, transpose, relu, xdt, ydt = case
+    g, og = hubg
+    r = np.random.default_rng(d + heads)
+    X = r.standard_normal((og.n, d)).astype(np.float32)
+    if xdt == "bf16":
+        X = bf16_values(X)
+    if wname == "gcn":
+        w, wt = og.gcn_norm()[1], "gcn"
+    elif wname == "ones":
+        w, wt = None, "ones"
+    else:
+        w = r.random((og.nnz, heads)).astype(np.float32)
+        wt = to_dev(w)
+    ref = oracle.spmm(og, X, w, heads, transpose=transpose)
+    mag = oracle.spmm_mag(og, X, w, heads, transpose=transpose)
+    if relu:
+        ref = np.maximum(ref, 0)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    Xd = to_dev(X, tdt[xdt])
+    Y = torch.full((og.n, d), float("nan"), dtype=tdt[ydt], device=Xd.device)
+    gnnmp.gnn_spmm(g, Xd, Y, weights=wt, heads=heads, transpose=transpose, relu=relu)
+    torch.cuda.synchronize()
+    check_close(from_dev(Y), ref, mag, bf16_out=ydt == "bf16", what="spmm")
+
+
+def test_spmm_integer_exact(hubg):
+    # unit weights on small-integer features: every fp32 partial sum is exact
+    g, og = hubg
+    r = np.random.default_rng(5)
+    X = r.integers(-4, 5, (og.n, 256)).astype(np.float32)
+    Y = torch.empty((og.n, 256), device="cuda")
+    gnnmp.gnn_spmm(g, to_dev(X), Y, weights="ones")
+    ref = oracle.spmm(og, X)
+    assert np.array_equal(from_dev(Y), ref.astype(np.float32))
+
+
+def test_spmm_leading_dims_and_determinism(hubg):
+    g, og = hubg
+    r = np.random.default_rng(6)
+    Xbig = r.standard_normal((og.n, 72)).astype(np.float32)
+    Xd = to_dev(Xbig)[:, :64]                       # ldx = 72
+    Ybig = torch.zeros((og.n, 68), device="cuda")
+    Y = Ybig[:, :64]                                 # ldy = 68
+    gnnmp.gnn_spmm(g, Xd, Y)
+    w = og.gcn_norm()[1]
+    ref = oracle.spmm(og, Xbig[:, :64], w)
+    check_close(from_dev(Y), ref, oracle.spmm_mag(og, Xbig[:, :64], w), what="spmm-ld")
+    assert torch.all(Ybig[:, 64:] == 0)
+    Y2 = torch.zeros_like(Ybig)
+    gnnmp.gnn_spmm(g, Xd, Y2[:, :64])
+    assert torch.equal(Ybig, Y2)
+
+
+def test_spmm_workspace_too_small(hubg):
+    g, og = hubg
+    X = torch.zeros((og.n, 64), device="cuda")
+    Y = torch.zeros_like(X)
+    with pytest.raises(gnnmp.GnnError):
+        gnnmp.gnn_spmm(g, X, Y, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+GEMM_CASES = [
+    # M, N, K, transA, transB, a_dt, b_dt, c_dt
+    (1000, 64, 64, False, False, "f32", "f32", "f32"),
+    (4099, 256, 128, False, False, "f32", "f32", "f32"),
+    (777, 41, 256, False, False, "f32", "f32", "f32"),
+    (1000, 256, 41, False, True, "f32", "f32", "f32"),
+    (3000, 100, 47, False, True, "f32", "f32", "f32"),
+    (256, 256, 70001, True, False, "f32", "f32", "f32"),
+    (128, 41, 9000, True, False, "f32", "f32", "f32"),
+    (2500, 256, 100, False, False, "bf16", "f32", "bf16"),
+    (100, 256, 30000, True, False, "bf16", "bf16", "f32"),
+    (2500, 47, 256, False, False, "bf16", "f32", "f32"),
+    (33, 7, 5, False, False, "f32", "f32", "f32"),
+]
+
+
+def _mat(r, shape, dt):
+    a = r.standard_normal(shape).astype(np.float32)
+    return bf16_values(a) if dt == "bf16" else a
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_gemm(case):
+    M, N, K, ta, tb, adt, bdt, cdt = case
+    r = np.random.default_rng(M + N + K)
+    A = _mat(r, (K, M) if ta else (M, K), adt)
+    B = _mat(r, (N, K) if tb else (K, N), bdt)
+    ref = oracle.gemm(A, B, ta, tb)
+    mag = oracle.gemm(np.abs(A), np.abs(B), ta, tb)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    C = torch.full((M, N), float("nan"), dtype=tdt[cdt], device="cuda")
+    gnnmp.gnn_gemm(to_dev(A, tdt[adt]), to_dev(B, tdt[bdt]), C, transA=ta, transB=tb)
+    torch.cuda.synchronize()
+    check_close(from_dev(C), ref, mag, bf16_out=cdt == "bf16", what="gemm")
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
+def test_gemm_integer_exact(ta, tb):
+    # integer inputs in [-4, 4]: all partial sums exact in binary32, any order
+    r = np.random.default_rng(3)
+    M, N, K = 1037, 130, 256
+    A = r.integers(-4, 5, (K, M) if ta else (M, K)).astype(np.float32)
+    B = r.integers(-4, 5, (N, K) if tb else (K, N)).astype(np.float32)
+    C = torch.empty((M, N), device="cuda")
+    gnnmp.gnn_gemm(to_dev(A), to_dev(B), C, transA=ta, transB=tb)
+    assert np.array_equal(from_dev(C), oracle.gemm(A, B, ta, tb).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# SDDMM, edge softmax, edge reductions
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def dirg():
+    s, t = hub_edges(4000, 30000, 2600, 21)
+    return graph_pair(s, t, 4000, False, csc=True)
+
+
+@pytest.mark.parametrize("heads", [1, 2, 4, 8])
+def test_sddmm_add_bit_exact(dirg, heads):
+    g, og = dirg
+    r = np.random.default_rng(heads)
+    S = r.standard_normal((og.n, heads)).astype(np.float32)
+    D = r.standard_normal((og.n, heads)).astype(np.float32)
+    Ep, E = oracle.sddmm_add(og, S, D, 0.2)
+    out = torch.empty((og.nnz, heads), device="cuda")
+    pre = torch.empty_like(out)
+    gnnmp.gnn_sddmm(g, "add", to_dev(S), to_dev(D), heads, 1, out, slope=0.2, out_pre=pre)
+    assert np.array_equal(from_dev(out).view(np.uint32), E.view(np.uint32))
+    assert np.array_equal(from_dev(pre).view(np.uint32), Ep.view(np.uint32))
+    # no activation
+    gnnmp.gnn_sddmm(g, "add", to_dev(S), to_dev(D), heads, 1, out)
+    assert np.array_equal(from_dev(out).view(np.uint32), Ep.view(np.uint32))
+
+
+@pytest.mark.parametrize("heads,dh,dt", [(4, 64, "f32"), (2, 32, "f32"), (1, 64, "f32"), (4, 16, "f32"),
+                                         (4, 64, "bf16")])
+def test_sddmm_dot(dirg, heads, dh, dt):
+    g, og = dirg
+    r = np.random.default_rng(heads * dh)
+    A = r.standard_normal((og.n, heads * dh)).astype(np.float32)   # source side (H')
+    B = r.standard_normal((og.n, heads * dh)).astype(np.float32)   # destination side (dY)
+    if dt == "bf16":
+        A, B = bf16_values(A), bf16_values(B)
+    ref = oracle.sddmm_dot(og, B, A, heads)
+    mag = oracle.sddmm_dot(og, np.abs(B), np.abs(A), heads)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    out = torch.empty((og.nnz, heads), device="cuda")
+    gnnmp.gnn_sddmm(g, "dot", to_dev(A, tdt), to_dev(B, tdt), heads, dh, out)
+    check_close(from_dev(out), ref, mag, what="sddmm-dot")
+
+
+@pytest.mark.parametrize("heads", [1, 4, 8])
+def test_edge_softmax(dirg, heads):
+    g, og = dirg
+    r = np.random.default_rng(40 + heads)
+    E = (2 * r.standard_normal((og.nnz, heads))).astype(np.float32)
+    ref = oracle.edge_softmax(og, E)
+    a = torch.empty((og.nnz, heads), device="cuda")
+    gnnmp.gnn_edge_softmax(g, to_dev(E), a)
+    check_close(from_dev(a), ref, np.abs(ref), what="edge-softmax")
+    # in place
+    Ed = to_dev(E)
+    gnnmp.gnn_edge_softmax(g, Ed, Ed)
+    assert torch.equal(Ed, a)
+
+
+@pytest.mark.parametrize("with_pre", [False, True])
+def test_edge_softmax_bwd(dirg, with_pre):
+    g, og = dirg
+    heads = 4
+    r = np.random.default_rng(7)
+    alpha = oracle.to_f32(oracle.edge_softmax(og, r.standard_normal((og.nnz, heads)).astype(np.float32)))
+    dal = r.standard_normal((og.nnz, heads)).astype(np.float32)
+    pre = r.standard_normal((og.nnz, heads)).astype(np.float32)
+    ref = oracle.edge_softmax_bwd(og, alpha, dal)
+    P_mag = oracle.edge_reduce(og, np.abs(alpha) * np.abs(dal))[og.dst]
+    mag = np.abs(alpha) * (np.abs(dal) + P_mag)
+    if with_pre:
+        fac = np.where(pre > 0, 1.0, np.float64(np.float32(0.2)))
+        ref, mag = ref * fac, mag * fac
+    out = torch.empty((og.nnz, heads), device="cuda")
+    gnnmp.gnn_edge_softmax_bwd(g, to_dev(alpha), to_dev(dal), out, lrelu_pre=to_dev(pre) if with_pre else None,
+                               slope=0.2)
+    check_close(from_dev(out), ref, mag, what="edge-softmax-bwd")
+
+
+@pytest.mark.parametrize("by_src,heads", [(False, 4), (True, 4), (False, 1), (True, 2)])
+def test_edge_reduce(dirg, by_src, heads):
+    g, og = dirg
+    r = np.random.default_rng(9 + heads)
+    vals = r.standard_normal((og.nnz, heads)).astype(np.float32)
+    ref = oracle.edge_reduce(og, vals, by_src=by_src)
+    mag = oracle.edge_reduce(og, np.abs(vals), by_src=by_src)
+    out = torch.empty((og.n, heads), device="cuda")
+    gnnmp.gnn_edge_reduce(g, to_dev(vals), out, by_src=by_src)
+    check_close(from_dev(out), ref, mag, what="edge-reduce")
+
+
+# ---------------------------------------------------------------------------
+# loss
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,c", [(10000, 41), (3333, 47), (5, 130), (1, 1)])
+def test_softmax_xent(n, c):
+    r = np.random.default_rng(n + c)
+    z = (3 * r.standard_normal((n, c))).astype(np.float32)
+    lab = r.integers(0, c, n).astype(np.int32)
+    loss_ref, dz_ref = oracle.softmax_xent(z, lab)
+    loss = torch.empty(1, device="cuda")
+    dz = torch.empty((n, c), device="cuda")
+    gnnmp.gnn_softmax_xent(to_dev(z), to_dev(lab), loss, dz)
+    assert abs(float(loss.item()) - loss_ref) <= RTOL32 * (abs(loss_ref) + np.abs(z).max())
+    mag = (np.abs(dz_ref) + 2.0 / n)
+    check_close(from_dev(dz), dz_ref, mag, what="xent-grad")
+
+
+# ---------------------------------------------------------------------------
+# quantisation: bit-exact codes, scales, zeros and dequantised rows
+# ---------------------------------------------------------------------------
+QCASES = [(256, 2), (256, 4), (256, 8), (100, 4), (100, 8), (41, 8), (64, 2), (1024, 4), (6, 4), (4, 2)]
+
+
+@pytest.mark.parametrize("d,bits", QCASES)
+def test_quantize_dequantize_bit_exact(d, bits):
+    r = np.random.default_rng(d * bits)
+    n = 3000
+    H = r.standard_normal((n, d)).astype(np.float32)
+    H[5] = 1.25                    # constant row
+    H[6, : d // 2] = 0.0           # signed zeros as extremes
+    H[6, d // 2:] = -0.0
+    rows = np.sort(r.choice(n, 1111, replace=False)).astype(np.int32)
+    rows[:3] = [5, 6, 7]
+    rows.sort()
+    seed = int(r.integers(0, 2 ** 63)) | (1 << 40)
+    for stream_id in (0, 7):
+        pk, sc, zr = oracle.quantize(H, rows, bits, seed, stream_id)
+        pkd = torch.empty(pk.shape, dtype=torch.uint8, device="cuda")
+        scd = torch.empty(rows.size, device="cuda")
+        zrd = torch.empty(rows.size, device="cuda")
+        Hd = to_dev(H)
+        rd = to_dev(rows)
+        gnnmp.gnn_quantize(Hd, rd, bits, seed, pkd, scd, zrd, stream_id=stream_id)
+        assert np.array_equal(from_dev(pkd), pk)
+        assert np.array_equal(from_dev(scd).view(np.uint32), sc.view(np.uint32))
+        assert np.array_equal(from_dev(zrd).view(np.uint32), zr.view(np.uint32))
+        out_ref = np.full_like(H, 7.0)
+        oracle.dequantize(pk, sc, zr, rows, d, bits, out_ref)
+        out = torch.full((n, d), 7.0, device="cuda")
+        gnnmp.gnn_dequantize(pkd, scd, zrd, rd, bits, out)
+        assert np.array_equal(from_dev(out).view(np.uint32), out_ref.view(np.uint32))
+
+
+def test_quantize_strided_rows():
+    r = np.random.default_rng(1)
+    Hbig = r.standard_normal((500, 80)).astype(np.float32)
+    rows = np.arange(0, 500, 7, dtype=np.int32)
+    pk, sc, zr = oracle.quantize(np.ascontiguousarray(Hbig[:, :64]), rows, 4, 99)
+    Hd = to_dev(Hbig)[:, :64]
+    pkd = torch.empty(pk.shape, dtype=torch.uint8, device="cuda")
+    scd = torch.empty(rows.size, device="cuda")
+    zrd = torch.empty(rows.size, device="cuda")
+    gnnmp.gnn_quantize(Hd, to_dev(rows), 4, 99, pkd, scd, zrd)
+    assert np.array_equal(from_dev(pkd), pk)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8, "mixed"])
+def test_quantized_exchange_then_aggregate(bits):
+    # AdaQP Eqn. 7 on one partition: marginal rows quantised and dequantised,
+    # central rows exact, then the GCN aggregation
+    s, t, n = rmat_graph(12, 24, True, 77)
+    g, og = graph_pair(s, t, n, True, csc=False)
+    r = np.random.default_rng(3)
+    H = r.standard_normal((n, 256)).astype(np.float32)
+    rows = synth.marginal_rows(n, 0.3, 5)
+    b = bits if bits != "mixed" else synth.random_bits(rows.size, (2, 4, 8), 6)
+    Hmix_ref, Y_ref, parts = oracle.quantized_aggregate(og, H, rows, b, seed=1234)
+    Hd = to_dev(H)
+    Hmix = Hd.clone()
+    for bb, (sel, pk, sc, zr) in parts.items():
+        pkd = torch.empty(pk.shape, dtype=torch.uint8, device="cuda")
+        scd = torch.empty(sel.size, device="cuda")
+        zrd = torch.empty(sel.size, device="cuda")
+        sd = to_dev(sel)
+        gnnmp.gnn_quantize(Hd, sd, bb, 1234, pkd, scd, zrd)
+        gnnmp.gnn_dequantize(pkd, scd, zrd, sd, bb, Hmix)
+    assert np.array_equal(from_dev(Hmix).view(np.uint32), Hmix_ref.view(np.uint32))
+    Y = torch.empty_like(Hmix)
+    gnnmp.gnn_spmm(g, Hmix, Y)
+    w = og.gcn_norm()[1]
+    check_close(from_dev(Y), Y_ref, oracle.spmm_mag(og, Hmix_ref, w), what="mixed aggregate")
