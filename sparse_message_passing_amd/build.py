@@ -40,10 +40,16 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# Per-file flags.  The quantiser's codes must match any faithful binary32
+# evaluation bit for bit, so nothing in it may be fused into an FMA (the
+# backend contracts across statements under the default fp-contract=fast).
+PER_FILE = {"quant.hip": ["-ffp-contract=off"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *COMMON, *lang, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *PER_FILE.get(os.path.basename(src), []), *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

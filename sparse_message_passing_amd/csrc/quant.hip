@@ -20,6 +20,8 @@
 #include "device.h"
 #include "internal.h"
 
+// Built with -ffp-contract=off (see build.py): a fused t*inv - floor(x)
+// would change codes.
 #pragma clang fp contract(off)
 
 namespace gnnmp {

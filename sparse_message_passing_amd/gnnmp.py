@@ -145,17 +145,21 @@ class Graph:
             self.h = None
 
 
-def gnn_graph_create(n, src, dst, symmetrize=False, csc=False, device="cuda"):
+def gnn_graph_create(n, src, dst, symmetrize=False, csc=False, device=None):
+    """Build on `device` (default: the current device); the handle's arrays live there."""
     src = np.ascontiguousarray(src, dtype=np.int32)
     dst = np.ascontiguousarray(dst, dtype=np.int32)
     if src.shape != dst.shape:
         raise ValueError("src and dst differ in length")
-    torch.cuda.set_device(torch.device(device))
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    torch.cuda.set_device(dev)
     h = C.c_void_p()
     flags = (GNN_GRAPH_SYMMETRIZE if symmetrize else 0) | (GNN_GRAPH_CSC if csc else 0)
     _check(lib().gnn_graph_create(int(n), src.size, src.ctypes.data_as(C.c_void_p), dst.ctypes.data_as(C.c_void_p),
                                   flags, C.byref(h)))
-    return Graph(h, torch.device(device))
+    return Graph(h, dev)
 
 
 def gnn_graph_export(g: Graph):

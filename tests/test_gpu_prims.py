@@ -331,7 +331,18 @@ def test_quantize_dequantize_bit_exact(d, bits):
         Hd = to_dev(H)
         rd = to_dev(rows)
         gnnmp.gnn_quantize(Hd, rd, bits, seed, pkd, scd, zrd, stream_id=stream_id)
-        assert np.array_equal(from_dev(pkd), pk)
+        got = from_dev(pkd)
+        if not np.array_equal(got, pk):
+            cg, cr = oracle.unpack_codes(got, d, bits), oracle.unpack_codes(pk, d, bits)
+            bad = np.argwhere(cg != cr)
+            i, f = bad[0]
+            v = rows[i]
+            x = (np.float32(H[v, f]) - zr[i]) * (np.float32(2 ** bits - 1) / (H[v].max() - H[v].min()))
+            u = oracle.philox_uniforms(seed, stream_id, np.array([v], np.int32), d)[0, f]
+            raise AssertionError(f"{len(bad)} codes differ (stream {stream_id}); first row {i} (node {v}) "
+                                 f"feature {f}: gpu {cg[i, f]} ref {cr[i, f]}; h={H[v, f]!r} Z={zr[i]!r} "
+                                 f"S={sc[i]!r} gpuS={from_dev(scd)[i]!r} gpuZ={from_dev(zrd)[i]!r} x~{x!r} u={u!r}; "
+                                 f"bad features {np.unique(bad[:, 1])[:16]} rows {np.unique(bad[:, 0])[:8]}")
         assert np.array_equal(from_dev(scd).view(np.uint32), sc.view(np.uint32))
         assert np.array_equal(from_dev(zrd).view(np.uint32), zr.view(np.uint32))
         out_ref = np.full_like(H, 7.0)
