@@ -214,23 +214,27 @@ gnn_status_t gnn_dequantize(const uint8_t* packed, const float* scale, const flo
 
 /* GCN layer Y = sigma(A_hat X W), sigma = ReLU when relu = 1.  The GEMM runs
  * first when d_out <= d_in, i.e. Y = sigma(A_hat (X W)); otherwise
- * Y = sigma((A_hat X) W) and A_hat X is written to `saved` ([n, d_in] of
- * x_dt, contiguous), which the backward needs.  X [n, d_in] of x_dt,
- * W [d_in, d_out] f32, Y [n, d_out] of y_dt (contiguous).  Intermediates are
+ * Y = sigma((A_hat X) W) and A_hat X is written to `saved` (same layout as X:
+ * [n, ldx] of x_dt), which the backward needs.  X [n, ldx] of x_dt,
+ * W [d_in, d_out] f32 contiguous, Y [n, ldy] of y_dt.  Intermediates are
  * stored in x_dt.  Workspace: gnn_gcn_workspace_size() bytes. */
 size_t gnn_gcn_workspace_size(gnn_graph_t g, int64_t d_in, int64_t d_out);
-gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, int64_t d_in, const float* W,
-                               int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, void* saved,
-                               void* ws, size_t ws_bytes, void* stream);
+gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                               const float* W, int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                               void* saved, void* ws, size_t ws_bytes, void* stream);
 
 /* Its backward.  G = dY * [Y > 0] (ReLU'(0) = 0) when relu, else dY.
- *   GEMM-first:     dZ = A_hat G;  dW = X^T dZ;  dX = dZ W^T
+ *   GEMM-first:      dZ = A_hat G;  dW = X^T dZ;  dX = dZ W^T
  *   aggregate-first: dW = (A_hat X)^T G;  dX = A_hat (G W^T)
- * (A_hat is symmetric).  dY, Y of y_dt; dX [n, d_in] of x_dt (NULL: not
- * formed); dW [d_in, d_out] f32. */
-gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, int64_t d_in, const float* W,
-                               int64_t d_out, int relu, const void* Y, const void* dY, gnn_dtype_t y_dt,
-                               const void* saved, void* dX, float* dW, void* ws, size_t ws_bytes, void* stream);
+ * (A_hat is symmetric).  dY, Y [n, ldy] of y_dt; dX [n, ldx] of x_dt (NULL:
+ * not formed); dW [d_in, d_out] f32.  relu_in = 1 says X is itself a ReLU
+ * output: dX is then returned times [X > 0], the gradient with respect to
+ * the previous layer's pre-activation, and that layer's backward is called
+ * with relu = 0 (this fuses the mask into the last kernel of this call). */
+gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                               const float* W, int64_t d_out, int relu, int relu_in, const void* Y, const void* dY,
+                               gnn_dtype_t y_dt, int64_t ldy, const void* saved, void* dX, float* dW, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* GAT layer forward (Tango, Fig. 1a):  H' = X W;  S = H' a_src, D = H' a_dst
  * per head;  E = LReLU(S[src] + D[dst]);  alpha = edge softmax(E);

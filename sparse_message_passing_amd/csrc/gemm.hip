@@ -50,7 +50,14 @@ struct GemmArgs {
     int64_t nblocks; // real work items (tiles * splits)
     int64_t per_xcd; // ceil(nblocks / 8)
     int relu;        // ReLU epilogue (applied after the split-K sum)
+    MaskEpilogue mask;  // C *= [M > 0] (after the split-K sum)
 };
+
+__device__ __forceinline__ bool mask_on(const MaskEpilogue& m, int64_t r, int64_t c) {
+    if (!m.M) return true;
+    if (m.dt == GNN_BF16) return Elem<bf16_t>::load(static_cast<const bf16_t*>(m.M) + r * m.ld + c) > 0.0f;
+    return Elem<float>::load(static_cast<const float*>(m.M) + r * m.ld + c) > 0.0f;
+}
 
 template <typename T, bool VEC>
 __device__ __forceinline__ void load4(const T* base, int64_t off, bool full, int valid, float (&r)[4]) {
@@ -204,21 +211,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                         g.ws[(split * g.M + m) * g.N + n] = acc[i][j][r];
                     else
                         Elem<TC>::store(static_cast<TC*>(g.C) + m * g.ldc + n,
-                                        g.relu ? fmaxf(acc[i][j][r], 0.0f) : acc[i][j][r]);
+                                        !mask_on(g.mask, m, n) ? 0.0f
+                                        : g.relu             ? fmaxf(acc[i][j][r], 0.0f)
+                                                             : acc[i][j][r]);
                 }
             }
         }
     }
 }
 
+// C = sum over splits in a fixed order: four thread groups each add every
+// fourth split (z = g, g+4, ...), then the four sums are added in order.
 template <typename TC>
 __global__ __launch_bounds__(256) void splitk_reduce(const float* ws, int splits, int64_t M, int64_t N, TC* C,
-                                                     int64_t ldc, int relu) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= M * N) return;
+                                                     int64_t ldc, int relu, MaskEpilogue mask) {
+    __shared__ float part[4][64];
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x & 63);
+    const int grp = threadIdx.x >> 6;
     float s = 0.0f;
-    for (int z = 0; z < splits; ++z) s += ws[z * M * N + i];
-    Elem<TC>::store(C + (i / N) * ldc + (i % N), relu ? fmaxf(s, 0.0f) : s);
+    if (i < M * N)
+        for (int z = grp; z < splits; z += 4) s += ws[z * M * N + i];
+    part[grp][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (grp == 0 && i < M * N) {
+        const int t = threadIdx.x;
+        float tot = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+        const int64_t r = i / N, c = i % N;
+        if (relu) tot = fmaxf(tot, 0.0f);
+        if (!mask_on(mask, r, c)) tot = 0.0f;
+        Elem<TC>::store(C + r * ldc + c, tot);
+    }
 }
 
 struct Plan {
@@ -276,8 +298,8 @@ void launch_types(GemmArgs& g, const Plan& p, bool va, bool vb, hipStream_t st) 
         launch_shape<128, 128, 2, 2, TA_, TB_, TA, TB, TC>(g, va, vb, st);
     if (g.splits > 1) {
         const int64_t tot = g.M * g.N;
-        hipLaunchKernelGGL((splitk_reduce<TC>), dim3((tot + 255) / 256), dim3(256), 0, st, g.ws, g.splits, g.M, g.N,
-                           static_cast<TC*>(g.C), g.ldc, g.relu);
+        hipLaunchKernelGGL((splitk_reduce<TC>), dim3((tot + 63) / 64), dim3(256), 0, st, g.ws, g.splits, g.M, g.N,
+                           static_cast<TC*>(g.C), g.ldc, g.relu, g.mask);
     }
 }
 
@@ -310,7 +332,8 @@ size_t gemm_ws_bytes(int transA, int transB, int64_t M, int64_t N, int64_t K) {
 
 gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
                          int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb, void* C, gnn_dtype_t c_dt,
-                         int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu) {
+                         int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu,
+                         const MaskEpilogue& mask) {
     if (M == 0 || N == 0) return GNN_OK;
     Plan p = make_plan(M, N, K);
     if (p.splits > 1 && ws_bytes < static_cast<size_t>(p.splits) * M * N * sizeof(float))
@@ -320,6 +343,7 @@ gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K
     g.A = A, g.lda = lda, g.B = B, g.ldb = ldb, g.C = C, g.ldc = ldc;
     g.ws = static_cast<float*>(ws);
     g.relu = relu;
+    g.mask = mask;
     g.kper = p.kper;
     g.splits = p.splits;
     g.tiles_m = (M + p.bm - 1) / p.bm;

@@ -104,9 +104,16 @@ struct Rank1Epilogue {    // Y[r, k*dh + j] += a[r, k] * va[k, j] + b[r, k] * vb
     const float* vb = nullptr;
 };
 
+struct MaskEpilogue {     // out[r, f] *= [M[r, f] > 0]  (the ReLU derivative of a stored activation)
+    const void* M = nullptr;
+    int64_t ld = 0;
+    gnn_dtype_t dt = GNN_F32;
+};
+
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
-                         int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st);
+                         int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
+                         const MaskEpilogue& mask = MaskEpilogue{});
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d);
 
 gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, const float* D, int64_t ldd,
@@ -127,13 +134,14 @@ gnn_status_t launch_head_colsum(int64_t n, const float* coefA, const float* coef
 size_t gemm_ws_bytes(int transA, int transB, int64_t M, int64_t N, int64_t K);
 gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
                          int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb, void* C, gnn_dtype_t c_dt,
-                         int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu = 0);
+                         int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu = 0,
+                         const MaskEpilogue& mask = MaskEpilogue{});
 
 size_t xent_ws_bytes(int64_t n);
 gnn_status_t launch_softmax_xent(const float* logits, int64_t n, int64_t c, int64_t ld, const int32_t* labels,
                                  float* loss, float* dlogits, int64_t ld_d, float* ws, hipStream_t st);
-gnn_status_t launch_relu_mask(int64_t count, const void* dY, const void* Y, gnn_dtype_t y_dt, void* G,
-                              gnn_dtype_t g_dt, hipStream_t st);
+gnn_status_t launch_relu_mask(int64_t n, int64_t d, const void* dY, int64_t ldd, const void* Y, int64_t ldy,
+                              gnn_dtype_t y_dt, void* G, int64_t ldg, gnn_dtype_t g_dt, hipStream_t st);
 
 gnn_status_t launch_quantize(const float* H, int64_t ldh, int64_t d, const int32_t* rows, int64_t n_rows, int bits,
                              uint64_t seed, uint32_t stream_id, uint8_t* packed, float* scale, float* zero,

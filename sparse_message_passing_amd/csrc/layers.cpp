@@ -27,7 +27,11 @@ struct Carver {
 };
 
 // GCN workspace: [G (masked gradient)] [T (aggregation or GEMM intermediate)]
-//                [split-K partials] [SpMM partials]
+//                [split-K partials] [SpMM partials]; intermediates are
+// binary32-sized with rows padded to a multiple of 4 elements so that the
+// aggregation always takes 16-byte loads.
+inline int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
+
 struct GcnWs {
     size_t g, t, gemm, spmm;
     size_t total() const { return align_up(g) + align_up(t) + align_up(gemm) + align_up(spmm); }
@@ -37,15 +41,13 @@ GcnWs gcn_ws(const Graph& g, int64_t d_in, int64_t d_out) {
     GcnWs w;
     const int64_t n = g.n;
     const int64_t dmax = std::max(d_in, d_out);
-    w.g = static_cast<size_t>(n) * d_out * 4;   // worst case f32
-    w.t = static_cast<size_t>(n) * dmax * 4;
+    w.g = static_cast<size_t>(n) * pad4(d_out) * 4;   // worst case f32
+    w.t = static_cast<size_t>(n) * pad4(dmax) * 4;
     w.gemm = std::max(gemm_ws_bytes(1, 0, d_in, d_out, n), gemm_ws_bytes(0, 0, n, d_out, d_in));
     w.gemm = std::max(w.gemm, gemm_ws_bytes(0, 1, n, d_in, d_out));
     w.spmm = spmm_partial_bytes(g.plan[0], dmax);
     return w;
 }
-
-bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 }  // namespace
 }  // namespace gnnmp
@@ -59,12 +61,13 @@ size_t gnn_gcn_workspace_size(gnn_graph_t h, int64_t d_in, int64_t d_out) {
     return gcn_ws(h->g, d_in, d_out).total();
 }
 
-gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t d_in, const float* W,
-                               int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, void* saved, void* ws,
-                               size_t ws_bytes, void* stream) {
+gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                               const float* W, int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                               void* saved, void* ws, size_t ws_bytes, void* stream) {
     GNN_REQUIRE(h, "gnn_gcn_layer_fwd: graph handle is NULL");
     const Graph& g = h->g;
     GNN_REQUIRE(d_in >= 1 && d_out >= 1, "gnn_gcn_layer_fwd: widths must be >= 1");
+    GNN_REQUIRE(ldx >= d_in && ldy >= d_out, "gnn_gcn_layer_fwd: leading dimensions too small");
     GNN_REQUIRE((x_dt == GNN_F32 || x_dt == GNN_BF16) && (y_dt == GNN_F32 || y_dt == GNN_BF16),
                 "gnn_gcn_layer_fwd: unknown dtype");
     GNN_REQUIRE(relu == 0 || relu == 1, "gnn_gcn_layer_fwd: relu must be 0 or 1");
@@ -82,33 +85,37 @@ gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, i
     void* gws = c.take(w.gemm);
     float* sws = static_cast<float*>(c.take(w.spmm));
     if (gemm_first) {
-        GNN_TRY(launch_gemm(0, 0, g.n, d_out, d_in, X, x_dt, d_in, W, GNN_F32, d_out, T, x_dt, d_out, gws, w.gemm,
-                            st));
-        return launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, T, x_dt, d_out, Y, y_dt, d_out, d_out, relu,
+        // Z = X W (rows padded to 4), then Y = sigma(A_hat Z)
+        const int64_t ldz = pad4(d_out);
+        GNN_TRY(launch_gemm(0, 0, g.n, d_out, d_in, X, x_dt, ldx, W, GNN_F32, d_out, T, x_dt, ldz, gws, w.gemm, st));
+        return launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, T, x_dt, ldz, Y, y_dt, ldy, d_out, relu,
                            Rank1Epilogue{}, sws, st);
     }
-    GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, X, x_dt, d_in, saved, x_dt, d_in, d_in, 0,
+    // saved = A_hat X (same layout as X), then Y = sigma(saved W)
+    GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, X, x_dt, ldx, saved, x_dt, ldx, d_in, 0,
                         Rank1Epilogue{}, sws, st));
-    return launch_gemm(0, 0, g.n, d_out, d_in, saved, x_dt, d_in, W, GNN_F32, d_out, Y, y_dt, d_out, gws, w.gemm, st,
+    return launch_gemm(0, 0, g.n, d_out, d_in, saved, x_dt, ldx, W, GNN_F32, d_out, Y, y_dt, ldy, gws, w.gemm, st,
                        relu);
 }
 
-gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t d_in, const float* W,
-                               int64_t d_out, int relu, const void* Y, const void* dY, gnn_dtype_t y_dt,
-                               const void* saved, void* dX, float* dW, void* ws, size_t ws_bytes, void* stream) {
+gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                               const float* W, int64_t d_out, int relu, int relu_in, const void* Y, const void* dY,
+                               gnn_dtype_t y_dt, int64_t ldy, const void* saved, void* dX, float* dW, void* ws,
+                               size_t ws_bytes, void* stream) {
     GNN_REQUIRE(h, "gnn_gcn_layer_bwd: graph handle is NULL");
     const Graph& g = h->g;
     GNN_REQUIRE(d_in >= 1 && d_out >= 1, "gnn_gcn_layer_bwd: widths must be >= 1");
+    GNN_REQUIRE(ldx >= d_in && ldy >= d_out, "gnn_gcn_layer_bwd: leading dimensions too small");
     GNN_REQUIRE((x_dt == GNN_F32 || x_dt == GNN_BF16) && (y_dt == GNN_F32 || y_dt == GNN_BF16),
                 "gnn_gcn_layer_bwd: unknown dtype");
-    GNN_REQUIRE(relu == 0 || relu == 1, "gnn_gcn_layer_bwd: relu must be 0 or 1");
+    GNN_REQUIRE((relu == 0 || relu == 1) && (relu_in == 0 || relu_in == 1), "gnn_gcn_layer_bwd: flags must be 0/1");
     GNN_REQUIRE(dW && W, "gnn_gcn_layer_bwd: W or dW is NULL");
     GNN_REQUIRE(g.n == 0 || dY, "gnn_gcn_layer_bwd: dY is NULL");
     GNN_REQUIRE(!relu || g.n == 0 || Y, "gnn_gcn_layer_bwd: Y is NULL (needed for the ReLU mask)");
+    GNN_REQUIRE(!relu_in || !dX || X, "gnn_gcn_layer_bwd: X is NULL (needed for the input ReLU mask)");
     const bool gemm_first = d_out <= d_in;
     GNN_REQUIRE(g.n == 0 || (gemm_first ? X != nullptr : saved != nullptr),
                 "gnn_gcn_layer_bwd: X (GEMM-first) or saved (aggregate-first) is NULL");
-    GNN_REQUIRE(!relu || (aligned16(Y) && aligned16(dY)), "gnn_gcn_layer_bwd: Y and dY must be 16-byte aligned");
     const GcnWs w = gcn_ws(g, d_in, d_out);
     if (ws_bytes < w.total() || (!ws && w.total()))
         return fail(GNN_ERR_WORKSPACE, "gnn_gcn_layer_bwd: workspace smaller than gnn_gcn_workspace_size()");
@@ -121,30 +128,38 @@ gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, i
     // G = dY * [Y > 0]: materialised in the storage type when masked
     const void* G = dY;
     gnn_dtype_t g_dt = y_dt;
+    int64_t ldg = ldy;
     if (relu && g.n) {
-        GNN_TRY(launch_relu_mask(g.n * d_out, dY, Y, y_dt, Gb, x_dt, st));
+        ldg = pad4(d_out);
+        GNN_TRY(launch_relu_mask(g.n, d_out, dY, ldy, Y, ldy, y_dt, Gb, ldg, x_dt, st));
         G = Gb;
         g_dt = x_dt;
     }
+    // the input gradient, optionally times the previous layer's ReLU derivative [X > 0]
+    MaskEpilogue mx;
+    if (relu_in) {
+        mx.M = X;
+        mx.ld = ldx;
+        mx.dt = x_dt;
+    }
     if (gemm_first) {
         // dZ = A_hat G;  dW = X^T dZ;  dX = dZ W^T
-        GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, G, g_dt, d_out, T, x_dt, d_out, d_out, 0,
+        const int64_t ldz = pad4(d_out);
+        GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, G, g_dt, ldg, T, x_dt, ldz, d_out, 0,
                             Rank1Epilogue{}, sws, st));
-        GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, X, x_dt, d_in, T, x_dt, d_out, dW, GNN_F32, d_out, gws, w.gemm,
-                            st));
+        GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, X, x_dt, ldx, T, x_dt, ldz, dW, GNN_F32, d_out, gws, w.gemm, st));
         if (dX)
-            GNN_TRY(launch_gemm(0, 1, g.n, d_in, d_out, T, x_dt, d_out, W, GNN_F32, d_out, dX, x_dt, d_in, gws,
-                                w.gemm, st));
+            GNN_TRY(launch_gemm(0, 1, g.n, d_in, d_out, T, x_dt, ldz, W, GNN_F32, d_out, dX, x_dt, ldx, gws, w.gemm,
+                                st, 0, mx));
         return GNN_OK;
     }
     // dW = (A_hat X)^T G;  dX = A_hat (G W^T)
-    GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, saved, x_dt, d_in, G, g_dt, d_out, dW, GNN_F32, d_out, gws, w.gemm,
-                        st));
+    GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, saved, x_dt, ldx, G, g_dt, ldg, dW, GNN_F32, d_out, gws, w.gemm, st));
     if (dX) {
-        GNN_TRY(launch_gemm(0, 1, g.n, d_in, d_out, G, g_dt, d_out, W, GNN_F32, d_out, T, x_dt, d_in, gws, w.gemm,
-                            st));
-        GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, T, x_dt, d_in, dX, x_dt, d_in, d_in, 0,
-                            Rank1Epilogue{}, sws, st));
+        const int64_t ldt = pad4(d_in);
+        GNN_TRY(launch_gemm(0, 1, g.n, d_in, d_out, G, g_dt, ldg, W, GNN_F32, d_out, T, x_dt, ldt, gws, w.gemm, st));
+        GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, T, x_dt, ldt, dX, x_dt, ldx, d_in, 0,
+                            Rank1Epilogue{}, sws, st, mx));
     }
     return GNN_OK;
 }

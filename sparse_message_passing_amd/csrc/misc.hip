@@ -14,16 +14,18 @@ namespace gnnmp {
 
 namespace {
 
-constexpr int kRowsPerBlock = 4;  // one wave per row
+constexpr int kRowsPerWave = 16;
+constexpr int kRowsPerBlock = 4 * kRowsPerWave;  // four waves, one row at a time each
 
 __global__ __launch_bounds__(256) void xent_rows(const float* z, int64_t n, int64_t c, int64_t ld,
                                                  const int32_t* labels, float* dz, int64_t ldd, float inv_n,
                                                  float* block_loss) {
-    __shared__ float sh[kRowsPerBlock];
+    __shared__ float sh[4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t v = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + w;
-    float row_loss = 0.0f;
-    if (v < n) {
+    float wave_loss = 0.0f;
+    for (int k = 0; k < kRowsPerWave; ++k) {
+        const int64_t v = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + w * kRowsPerWave + k;
+        if (v >= n) break;
         const float* zr = z + v * ld;
         const int32_t y = labels[v];
         float m = -INFINITY;
@@ -33,7 +35,7 @@ __global__ __launch_bounds__(256) void xent_rows(const float* z, int64_t n, int6
         for (int64_t j = lane; j < c; j += 64) s += __expf(zr[j] - m);
         s = group_sum<64>(s);
         const float lse = m + __logf(s);
-        row_loss = lse - zr[y];
+        wave_loss += lse - zr[y];
         if (dz) {
             const float is = 1.0f / s;
             for (int64_t j = lane; j < c; j += 64) {
@@ -43,13 +45,9 @@ __global__ __launch_bounds__(256) void xent_rows(const float* z, int64_t n, int6
             }
         }
     }
-    if (lane == 0) sh[w] = row_loss;
+    if (lane == 0) sh[w] = wave_loss;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        float t = 0.0f;
-        for (int i = 0; i < kRowsPerBlock; ++i) t += sh[i];
-        block_loss[blockIdx.x] = t;
-    }
+    if (threadIdx.x == 0) block_loss[blockIdx.x] = ((sh[0] + sh[1]) + sh[2]) + sh[3];
 }
 
 __global__ __launch_bounds__(256) void xent_total(const float* block_loss, int64_t nb, float inv_n, float* loss) {
@@ -65,19 +63,14 @@ __global__ __launch_bounds__(256) void xent_total(const float* block_loss, int64
     if (threadIdx.x == 0) *loss = sh[0] * inv_n;
 }
 
+// G[r, f] = dY[r, f] * [Y[r, f] > 0] over an n x d block with leading dims
 template <typename TY, typename TG>
-__global__ __launch_bounds__(256) void relu_mask_kernel(int64_t count, const TY* dY, const TY* Y, TG* G) {
-    const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (i + 4 <= count) {
-        float4 d = Elem<TY>::load4(dY + i), y = Elem<TY>::load4(Y + i);
-        d.x = y.x > 0.0f ? d.x : 0.0f;
-        d.y = y.y > 0.0f ? d.y : 0.0f;
-        d.z = y.z > 0.0f ? d.z : 0.0f;
-        d.w = y.w > 0.0f ? d.w : 0.0f;
-        Elem<TG>::store4(G + i, d);
-    } else {
-        for (int64_t j = i; j < count; ++j) Elem<TG>::store(G + j, Elem<TY>::load(Y + j) > 0.0f ? Elem<TY>::load(dY + j) : 0.0f);
-    }
+__global__ __launch_bounds__(256) void relu_mask_kernel(int64_t n, int64_t d, const TY* dY, int64_t ldd, const TY* Y,
+                                                        int64_t ldy, TG* G, int64_t ldg) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n * d) return;
+    const int64_t r = i / d, f = i % d;
+    Elem<TG>::store(G + r * ldg + f, Elem<TY>::load(Y + r * ldy + f) > 0.0f ? Elem<TY>::load(dY + r * ldd + f) : 0.0f);
 }
 
 }  // namespace
@@ -96,13 +89,13 @@ gnn_status_t launch_softmax_xent(const float* logits, int64_t n, int64_t c, int6
     return launch_status("gnn_softmax_xent");
 }
 
-gnn_status_t launch_relu_mask(int64_t count, const void* dY, const void* Y, gnn_dtype_t y_dt, void* G,
-                              gnn_dtype_t g_dt, hipStream_t st) {
-    if (count == 0) return GNN_OK;
-    const int64_t blocks = (count + 1023) / 1024;
+gnn_status_t launch_relu_mask(int64_t n, int64_t d, const void* dY, int64_t ldd, const void* Y, int64_t ldy,
+                              gnn_dtype_t y_dt, void* G, int64_t ldg, gnn_dtype_t g_dt, hipStream_t st) {
+    if (n == 0 || d == 0) return GNN_OK;
+    const int64_t blocks = (n * d + 255) / 256;
 #define GNN_RM(TY, TG)                                                                                      \
-    hipLaunchKernelGGL((relu_mask_kernel<TY, TG>), dim3(blocks), dim3(256), 0, st, count,                   \
-                       static_cast<const TY*>(dY), static_cast<const TY*>(Y), static_cast<TG*>(G))
+    hipLaunchKernelGGL((relu_mask_kernel<TY, TG>), dim3(blocks), dim3(256), 0, st, n, d,                    \
+                       static_cast<const TY*>(dY), ldd, static_cast<const TY*>(Y), ldy, static_cast<TG*>(G), ldg)
     if (y_dt == GNN_F32 && g_dt == GNN_F32) GNN_RM(float, float);
     else if (y_dt == GNN_F32) GNN_RM(float, bf16_t);
     else if (g_dt == GNN_F32) GNN_RM(bf16_t, float);

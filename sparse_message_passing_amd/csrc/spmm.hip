@@ -48,10 +48,19 @@ struct SpmmArgs {
     void* Y;
     int64_t ldy;
     int64_t d;
+    int64_t pd;          // row stride of the partial buffer (d rounded up to 4)
     int relu;
+    int vec_store;       // Y rows take 16-byte (8-byte for bf16) stores
     Rank1Epilogue r1;
+    MaskEpilogue mask;   // Y *= [M > 0]
     float* partial;
 };
+
+template <typename TO>
+__device__ __forceinline__ float mask_of(const MaskEpilogue& m, int64_t row, int64_t f) {
+    if (m.dt == GNN_BF16) return Elem<bf16_t>::load(static_cast<const bf16_t*>(m.M) + row * m.ld + f) > 0.0f ? 1.0f : 0.0f;
+    return Elem<float>::load(static_cast<const float*>(m.M) + row * m.ld + f) > 0.0f ? 1.0f : 0.0f;
+}
 
 template <int VEC>
 struct Acc {
@@ -179,8 +188,9 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
     for (int c = 0; c < NCH; ++c) {
         if (!act[c]) continue;
         const int64_t f = static_cast<int64_t>(c * LANES + lane) * VEC;
+        const int nv = static_cast<int>(min(static_cast<int64_t>(VEC), a.d - f));  // valid features of this lane
         if (heavy) {
-            float* P = a.partial + gid * a.d + f;
+            float* P = a.partial + gid * a.pd + f;
             if constexpr (VEC == 4)
                 *reinterpret_cast<float4*>(P) = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
             else
@@ -192,17 +202,29 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
             const float rb = a.r1.b[row * heads + hd[c]];
 #pragma unroll
             for (int i = 0; i < VEC; ++i)
-                acc[c][i] = acc[c][i] + (ra * a.r1.va[f + i] + rb * a.r1.vb[f + i]);
+                if (i < nv) acc[c][i] = acc[c][i] + (ra * a.r1.va[f + i] + rb * a.r1.vb[f + i]);
         }
         if (a.relu) {
 #pragma unroll
             for (int i = 0; i < VEC; ++i) acc[c][i] = fmaxf(acc[c][i], 0.0f);
         }
+        if (a.mask.M) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                if (i < nv) acc[c][i] = mask_of<TO>(a.mask, row, f + i) > 0.0f ? acc[c][i] : 0.0f;
+        }
         TO* Y = static_cast<TO*>(a.Y) + row * a.ldy + f;
-        if constexpr (VEC == 4)
-            Elem<TO>::store4(Y, make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]));
-        else
+        if constexpr (VEC == 4) {
+            if (nv == 4 && a.vec_store) {
+                Elem<TO>::store4(Y, make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i)
+                    if (i < nv) Elem<TO>::store(Y + i, acc[c][i]);
+            }
+        } else {
             Elem<TO>::store(Y, acc[c][0]);
+        }
     }
 }
 
@@ -214,12 +236,13 @@ __global__ __launch_bounds__(256) void spmm_fixup(SpmmArgs a) {
     const int64_t c0 = a.chunk_first[i], c1 = a.chunk_first[i + 1];
     for (int64_t f = threadIdx.x; f < a.d; f += blockDim.x) {
         float s = 0.0f;
-        for (int64_t c = c0; c < c1; ++c) s += a.partial[c * a.d + f];
+        for (int64_t c = c0; c < c1; ++c) s += a.partial[c * a.pd + f];
         if (a.r1.a) {
             const int64_t h = f / a.dh;
             s = s + (a.r1.a[row * a.heads + h] * a.r1.va[f] + a.r1.b[row * a.heads + h] * a.r1.vb[f]);
         }
         if (a.relu) s = fmaxf(s, 0.0f);
+        if (a.mask.M && !(mask_of<TO>(a.mask, row, f) > 0.0f)) s = 0.0f;
         Elem<TO>::store(static_cast<TO*>(a.Y) + row * a.ldy + f, s);
     }
 }
@@ -256,12 +279,14 @@ gnn_status_t dispatch(const SpmmArgs& a, int vec, int lanes, int nch, hipStream_
 }  // namespace
 
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d) {
-    return p.n_chunks > 0 ? align_up(static_cast<size_t>(p.n_chunks) * d * sizeof(float)) : 0;
+    const int64_t pd = (d + 3) / 4 * 4;
+    return p.n_chunks > 0 ? align_up(static_cast<size_t>(p.n_chunks) * pd * sizeof(float)) : 0;
 }
 
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
-                         int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st) {
+                         int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
+                         const MaskEpilogue& mask) {
     if (v.n == 0 || d == 0) return GNN_OK;
     if (heads > kMaxHeads) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm: at most 8 heads");
     SpmmArgs a;
@@ -286,25 +311,29 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     a.d = d;
     a.relu = relu;
     a.r1 = r1;
+    a.mask = mask;
     a.partial = partial;
+    a.pd = (d + 3) / 4 * 4;
     const size_t xs = dt_size(x_dt), ys = dt_size(y_dt);
-    const bool aligned = (reinterpret_cast<uintptr_t>(X) % (4 * xs) == 0) &&
-                         (reinterpret_cast<uintptr_t>(Y) % (4 * ys) == 0);
-    const int vec = (d % 4 == 0 && ldx % 4 == 0 && ldy % 4 == 0 && (a.dh % 4 == 0) && aligned) ? 4 : 1;
-    const int64_t need = (d + vec - 1) / vec;  // lanes for one pass over the features
+    // 4-wide loads need 4-element aligned rows with room for the last quad;
+    // 4-wide stores additionally need the same of Y (else stores go one by one)
+    const bool vec = ldx % 4 == 0 && ldx >= a.pd && reinterpret_cast<uintptr_t>(X) % (4 * xs) == 0 &&
+                     (heads == 1 || a.dh % 4 == 0);
+    a.vec_store = ldy % 4 == 0 && reinterpret_cast<uintptr_t>(Y) % (4 * ys) == 0;
+    const int64_t need = vec ? a.pd / 4 : d;  // lanes for one pass over the features
     int lanes, nch;
-    if (vec == 4 && need <= 16) lanes = 16, nch = 1;
-    else if (vec == 4 && need <= 32) lanes = 32, nch = 1;
+    if (vec && need <= 16) lanes = 16, nch = 1;
+    else if (vec && need <= 32) lanes = 32, nch = 1;
     else {
         lanes = 64;
         nch = need <= 64 ? 1 : need <= 128 ? 2 : need <= 256 ? 4 : 0;
-        if (nch == 4 && need <= 192) nch = 4;
     }
+    const int vw = vec ? 4 : 1;
     if (nch == 0) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm: d too large (max 1024 for 16-byte rows, 256 otherwise)");
-    if (x_dt == GNN_F32 && y_dt == GNN_F32) return dispatch<float, float>(a, vec, lanes, nch, st);
-    if (x_dt == GNN_F32 && y_dt == GNN_BF16) return dispatch<float, bf16_t>(a, vec, lanes, nch, st);
-    if (x_dt == GNN_BF16 && y_dt == GNN_F32) return dispatch<bf16_t, float>(a, vec, lanes, nch, st);
-    return dispatch<bf16_t, bf16_t>(a, vec, lanes, nch, st);
+    if (x_dt == GNN_F32 && y_dt == GNN_F32) return dispatch<float, float>(a, vw, lanes, nch, st);
+    if (x_dt == GNN_F32 && y_dt == GNN_BF16) return dispatch<float, bf16_t>(a, vw, lanes, nch, st);
+    if (x_dt == GNN_BF16 && y_dt == GNN_F32) return dispatch<bf16_t, float>(a, vw, lanes, nch, st);
+    return dispatch<bf16_t, bf16_t>(a, vw, lanes, nch, st);
 }
 
 }  // namespace gnnmp

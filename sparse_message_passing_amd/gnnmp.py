@@ -45,8 +45,8 @@ _SIGS = {
     "gnn_quantize": ("PIIPIiQUPPPP", "i"),
     "gnn_dequantize": ("PPPIIiPPIP", "i"),
     "gnn_gcn_workspace_size": ("PII", "S"),
-    "gnn_gcn_layer_fwd": ("PPiIPIiPiPPSP", "i"),
-    "gnn_gcn_layer_bwd": ("PPiIPIiPPiPPPPSP", "i"),
+    "gnn_gcn_layer_fwd": ("PPiIIPIiPiIPPSP", "i"),
+    "gnn_gcn_layer_bwd": ("PPiIIPIiiPPiIPPPPSP", "i"),
     "gnn_gat_saved_size": ("PiI", "S"),
     "gnn_gat_workspace_size": ("PIiI", "S"),
     "gnn_gat_layer_fwd": ("PPIPPPiIFPPPSP", "i"),
@@ -264,21 +264,30 @@ def gnn_gcn_workspace_size(g: Graph, d_in, d_out):
 
 
 def gnn_gcn_layer_fwd(g: Graph, X, W, Y, relu, saved=None, ws=None):
+    """Y = sigma(A_hat X W); X, Y may be row-strided views (leading dims from their strides)."""
     d_in, d_out = W.shape
     if ws is None:
         ws = _ws(gnn_gcn_workspace_size(g, d_in, d_out), X.device)
-    _check(lib().gnn_gcn_layer_fwd(g.h, _p(X), _dt(X), d_in, _p(W), d_out, int(relu), _p(Y), _dt(Y), _p(saved),
-                                   _p(ws), ws.numel(), _stream()))
+    if saved is not None and _ld(saved) != _ld(X):
+        raise ValueError("saved must have X's row stride")
+    _check(lib().gnn_gcn_layer_fwd(g.h, _p(X), _dt(X), _ld(X), d_in, _p(W), d_out, int(relu), _p(Y), _dt(Y), _ld(Y),
+                                   _p(saved), _p(ws), ws.numel(), _stream()))
     return Y
 
 
-def gnn_gcn_layer_bwd(g: Graph, X, W, Y, dY, relu, dW, dX=None, saved=None, ws=None):
+def gnn_gcn_layer_bwd(g: Graph, X, W, Y, dY, relu, dW, dX=None, saved=None, ws=None, relu_in=False):
     d_in, d_out = W.shape
     if ws is None:
         ws = _ws(gnn_gcn_workspace_size(g, d_in, d_out), dY.device)
-    x_dt = _dt(X) if X is not None else _dt(saved)
-    _check(lib().gnn_gcn_layer_bwd(g.h, _p(X), x_dt, d_in, _p(W), d_out, int(relu), _p(Y), _p(dY), _dt(dY),
-                                   _p(saved), _p(dX), _p(dW), _p(ws), ws.numel(), _stream()))
+    ref = X if X is not None else saved
+    for t in (dX, saved):
+        if t is not None and _ld(t) != _ld(ref):
+            raise ValueError("dX / saved must have X's row stride")
+    if Y is not None and _ld(Y) != _ld(dY):
+        raise ValueError("Y and dY must share a row stride")
+    _check(lib().gnn_gcn_layer_bwd(g.h, _p(X), _dt(ref), _ld(ref), d_in, _p(W), d_out, int(relu), int(relu_in),
+                                   _p(Y), _p(dY), _dt(dY), _ld(dY), _p(saved), _p(dX), _p(dW), _p(ws), ws.numel(),
+                                   _stream()))
     return dX, dW
 
 

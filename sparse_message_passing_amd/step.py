@@ -23,6 +23,12 @@ def _dt(name):
     return torch.bfloat16 if name == "bf16" else torch.float32
 
 
+def _padded(n, d, dtype, dev):
+    """[n, d] view of an [n, round_up(d, 4)] buffer: 16-byte aligned rows for the kernels."""
+    ld = (d + 3) // 4 * 4
+    return torch.empty((n, ld), dtype=dtype, device=dev)[:, :d]
+
+
 class GcnStack:
     def __init__(self, g: gnnmp.Graph, X, Ws, labels, dtype="f32"):
         self.g = g
@@ -35,13 +41,16 @@ class GcnStack:
         L = len(Ws)
         self.widths = [Ws[0].shape[0]] + [w.shape[1] for w in Ws]
         # activations: hidden layers in the storage type, logits in binary32
-        self.H = [self.X] + [torch.empty((n, self.widths[i + 1]), dtype=self.dt if i < L - 1 else torch.float32,
-                                         device=dev) for i in range(L)]
-        self.saved = [torch.empty((n, self.widths[i]), dtype=self.dt, device=dev)
-                      if self.widths[i + 1] > self.widths[i] else None for i in range(L)]
+        self.H = [self.X] + [_padded(n, self.widths[i + 1], self.dt if i < L - 1 else torch.float32, dev)
+                             for i in range(L)]
+        self.saved = [_padded(n, self.widths[i], self.dt, dev) if self.widths[i + 1] > self.widths[i] else None
+                      for i in range(L)]
+        if self.saved[0] is not None and self.X.stride(0) != self.saved[0].stride(0):
+            self.X = torch.nn.functional.pad(self.X, (0, self.saved[0].stride(0) - self.widths[0]))[:, :self.widths[0]]
+            self.H[0] = self.X
         self.dW = [torch.empty_like(w) for w in self.Ws]
-        self.dH = [None] + [torch.empty((n, self.widths[i]), dtype=self.dt, device=dev) for i in range(1, L)]
-        self.dlogits = torch.empty((n, self.widths[-1]), dtype=torch.float32, device=dev)
+        self.dH = [None] + [_padded(n, self.widths[i], self.dt, dev) for i in range(1, L)]
+        self.dlogits = _padded(n, self.widths[-1], torch.float32, dev)
         self.loss = torch.empty(1, dtype=torch.float32, device=dev)
         ws = max(gnnmp.gnn_gcn_workspace_size(g, self.widths[i], self.widths[i + 1]) for i in range(L))
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
@@ -57,11 +66,14 @@ class GcnStack:
         return self.loss
 
     def backward(self):
+        """Layer i's backward returns its input gradient already multiplied by
+        the ReLU derivative of layer i-1 (relu_in), so no layer re-masks."""
         L = len(self.Ws)
         dY = self.dlogits
         for i in reversed(range(L)):
-            gnnmp.gnn_gcn_layer_bwd(self.g, self.H[i], self.Ws[i], self.H[i + 1], dY, relu=i < L - 1, dW=self.dW[i],
-                                    dX=self.dH[i] if i > 0 else None, saved=self.saved[i], ws=self.ws)
+            gnnmp.gnn_gcn_layer_bwd(self.g, self.H[i], self.Ws[i], None, dY, relu=False, dW=self.dW[i],
+                                    dX=self.dH[i] if i > 0 else None, saved=self.saved[i], ws=self.ws,
+                                    relu_in=i > 0)
             dY = self.dH[i]
         return self.dW
 

@@ -93,6 +93,44 @@ def test_gcn_layer_fwd_bwd(hubsym, case):
     gnnmp.gnn_gcn_layer_bwd(g, Xd, Wd, Yd, dYd, relu, dW, dX=dX, saved=sv)
     check_close(from_dev(dW), dW_ref, mag_dW, rtol=rtol, what="gcn dW")
     check_close(from_dev(dX), dX_ref, mag_dX, rtol=rtol, bf16_out=dt == "bf16", what="gcn dX")
+    # the input gradient times the previous layer's ReLU derivative, fused
+    dX2 = torch.empty_like(dX)
+    gnnmp.gnn_gcn_layer_bwd(g, Xd, Wd, Yd, dYd, relu, dW, dX=dX2, saved=sv, relu_in=True)
+    keep = X > 0
+    check_close(from_dev(dX2), np.where(keep, dX_ref, 0.0), np.where(keep, mag_dX, 0.0) + 1e-30, rtol=rtol,
+                bf16_out=dt == "bf16", what="gcn dX (relu_in)")
+
+
+def test_gcn_layer_row_strided(hubsym):
+    # X, Y, saved and the gradients as row-strided views (widths 41 and 47 padded to 44 / 48)
+    g, og = hubsym
+    r = np.random.default_rng(9)
+    for d_in, d_out in ((41, 47), (47, 41)):
+        X = r.standard_normal((og.n, d_in)).astype(np.float32)
+        W = synth.glorot(d_in, d_out, 2)
+        Y_ref, saved_ref = oracle.gcn_layer_fwd(og, X, W, relu=True)
+        pad = lambda d: torch.zeros((og.n, (d + 3) // 4 * 4 + 4), device="cuda")[:, :d]
+        Xd = pad(d_in)
+        Xd.copy_(to_dev(X))
+        Y = pad(d_out)
+        saved = pad(d_in) if d_out > d_in else None
+        gnnmp.gnn_gcn_layer_fwd(g, Xd, to_dev(W), Y, relu=True, saved=saved)
+        check_close(from_dev(Y), Y_ref, gcn_mag(og, X, W), what=f"strided fwd {d_in}->{d_out}")
+        dY = r.standard_normal((og.n, d_out)).astype(np.float32)
+        dYd = pad(d_out)
+        dYd.copy_(to_dev(dY))
+        Yd = pad(d_out)
+        Yd.copy_(to_dev(Y_ref))
+        sv = None
+        if saved_ref is not None:
+            sv = pad(d_in)
+            sv.copy_(to_dev(saved_ref))
+        dX_ref, dW_ref = oracle.gcn_layer_bwd(og, X, saved_ref, Y_ref, dY, W, True)
+        dX = pad(d_in)
+        dW = torch.empty((d_in, d_out), device="cuda")
+        gnnmp.gnn_gcn_layer_bwd(g, Xd, to_dev(W), Yd, dYd, True, dW, dX=dX, saved=sv)
+        rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+        assert rel(from_dev(dW), dW_ref) < 1e-5 and rel(from_dev(dX), dX_ref) < 1e-5
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
