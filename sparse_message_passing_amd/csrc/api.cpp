@@ -34,8 +34,8 @@ gnn_status_t launch_status(const char* what) {
     return GNN_OK;
 }
 
-AggView csr_view(const Graph& g) { return AggView{g.n, g.row_ptr, g.col, nullptr, &g.plan[0]}; }
-AggView csc_view(const Graph& g) { return AggView{g.n, g.col_ptr, g.csc_row, g.csc_eid, &g.plan[1]}; }
+AggView csr_view(const Graph& g) { return AggView{g.n, g.row_ptr, g.col, nullptr, &g.plan[0], g.wgcn}; }
+AggView csc_view(const Graph& g) { return AggView{g.n, g.col_ptr, g.csc_row, g.csc_eid, &g.plan[1], nullptr}; }
 
 namespace {
 
@@ -134,6 +134,13 @@ gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const in
             s = upload(g, hg.row_ptr, &g.row_ptr);
             if (s == GNN_OK) s = upload(g, hg.col, &g.col);
             if (s == GNN_OK) s = upload(g, hg.dinv, &g.dinv);
+            if (s == GNN_OK) {
+                // GCN edge weights dinv[src] * dinv[dst] (binary32 product), CSR order
+                std::vector<float> w(static_cast<size_t>(g.nnz));
+                for (int64_t v = 0; v < n; ++v)
+                    for (int64_t e = hg.row_ptr[v]; e < hg.row_ptr[v + 1]; ++e) w[e] = hg.dinv[hg.col[e]] * hg.dinv[v];
+                s = upload(g, w, &g.wgcn);
+            }
             if (s == GNN_OK) s = make_plan(g, hg.row_ptr, g.plan[0], nullptr);
             if (s == GNN_OK && g.has_csc) {
                 s = upload(g, hg.col_ptr, &g.col_ptr);

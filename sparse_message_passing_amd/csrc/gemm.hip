@@ -7,11 +7,11 @@
 //  * a 256-thread workgroup computes a BM x BN tile of C; its four waves
 //    split the tile WM x WN ways and each wave owns (BM/WM) x (BN/WN) as a
 //    grid of 16x16 MFMA blocks held in accumulation registers;
-//  * K advances in slabs of 16: the A and B slabs are staged through LDS in
-//    k-major layout (As[k][m], Bs[k][n]); an operand that is contiguous along
-//    k in global memory is transposed on the way in, one that is contiguous
-//    along m / n is stored with 16-byte writes;  the next slab's global loads
-//    are issued before the current slab's MFMAs;
+//  * K advances in slabs of 16 through double-buffered LDS; each operand
+//    keeps its global contiguity in LDS (k-contiguous rows, or k-major
+//    planes), so every global->LDS store is a 16-byte write; the next slab's
+//    global loads are issued before the current slab's MFMAs and its LDS
+//    stores after them, one barrier per slab;
 //  * operand fragments: lane l supplies A[m0 + l%16][k0 + l/16] and
 //    B[k0 + l/16][n0 + l%16]; the result block leaves lane l holding rows
 //    m0 + 4*(l/16) + r, r = 0..3, of column n0 + l%16;
@@ -33,7 +33,8 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 16;
-constexpr int PAD = 4;
+constexpr int PAD = 4;     // row padding of k-contiguous LDS tiles (rows stay 16-byte aligned)
+constexpr int PADM = 16;   // padding of k-major LDS planes: the four k rows a fragment read spans start 16 banks apart
 
 struct GemmArgs {
     int64_t M, N, K;
@@ -80,8 +81,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     constexpr int A_LOADS = BM * BK / 4 / 256;  // float4-sized pieces per thread
     constexpr int B_LOADS = BN * BK / 4 / 256;
     static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
-    __shared__ float As[BK][BM + PAD];
-    __shared__ float Bs[BK][BN + PAD];
+    // An operand contiguous along k is kept k-contiguous in LDS ([rows][BK+PAD]),
+    // one contiguous along m / n is kept k-major ([BK][rows+PAD]): either way the
+    // global->LDS store is one 16-byte write per thread and piece, and the
+    // fragment reads of 16 consecutive rows hit distinct banks.  Two buffers:
+    // the next slab is written while the current one is read.
+    constexpr bool A_KC = !TRANS_A, B_KC = TRANS_B;
+    constexpr int A_SZ = A_KC ? BM * (BK + PAD) : BK * (BM + PADM);
+    constexpr int B_SZ = B_KC ? BN * (BK + PAD) : BK * (BN + PADM);
+    __shared__ float As[2][A_SZ];
+    __shared__ float Bs[2][B_SZ];
 
     // XCD-aware tile map: the blocks dealt to one XCD take a contiguous range
     const int64_t bid = blockIdx.x;
@@ -141,60 +150,70 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
             }
         }
     };
-    auto store_slab = [&]() {
+    auto store_slab = [&](int buf) {
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
             const int q = tid + p * 256;
-            if constexpr (!TRANS_A) {
+            if constexpr (A_KC) {
                 const int mm = q / (BK / 4), kk = (q % (BK / 4)) * 4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) As[kk + i][mm] = ra[p][i];
+                *reinterpret_cast<float4*>(&As[buf][mm * (BK + PAD) + kk]) =
+                    make_float4(ra[p][0], ra[p][1], ra[p][2], ra[p][3]);
             } else {
                 const int kk = q / (BM / 4), mm = (q % (BM / 4)) * 4;
-                *reinterpret_cast<float4*>(&As[kk][mm]) = make_float4(ra[p][0], ra[p][1], ra[p][2], ra[p][3]);
+                *reinterpret_cast<float4*>(&As[buf][kk * (BM + PADM) + mm]) =
+                    make_float4(ra[p][0], ra[p][1], ra[p][2], ra[p][3]);
             }
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
             const int q = tid + p * 256;
-            if constexpr (!TRANS_B) {
-                const int kk = q / (BN / 4), nn = (q % (BN / 4)) * 4;
-                *reinterpret_cast<float4*>(&Bs[kk][nn]) = make_float4(rb[p][0], rb[p][1], rb[p][2], rb[p][3]);
-            } else {
+            if constexpr (B_KC) {
                 const int nn = q / (BK / 4), kk = (q % (BK / 4)) * 4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Bs[kk + i][nn] = rb[p][i];
+                *reinterpret_cast<float4*>(&Bs[buf][nn * (BK + PAD) + kk]) =
+                    make_float4(rb[p][0], rb[p][1], rb[p][2], rb[p][3]);
+            } else {
+                const int kk = q / (BN / 4), nn = (q % (BN / 4)) * 4;
+                *reinterpret_cast<float4*>(&Bs[buf][kk * (BN + PADM) + nn]) =
+                    make_float4(rb[p][0], rb[p][1], rb[p][2], rb[p][3]);
             }
         }
+    };
+    auto a_at = [&](int buf, int row, int k) -> float {
+        if constexpr (A_KC) return As[buf][row * (BK + PAD) + k];
+        else return As[buf][k * (BM + PADM) + row];
+    };
+    auto b_at = [&](int buf, int col, int k) -> float {
+        if constexpr (B_KC) return Bs[buf][col * (BK + PAD) + k];
+        else return Bs[buf][k * (BN + PADM) + col];
     };
 
     const int64_t nslab = (kend - kbeg + BK - 1) / BK;
     if (nslab > 0) {
         load_slab(kbeg);
-        store_slab();
+        store_slab(0);
     }
     __syncthreads();
     for (int64_t s = 0; s < nslab; ++s) {
+        const int buf = static_cast<int>(s & 1);
         if (s + 1 < nslab) load_slab(kbeg + (s + 1) * BK);
 #pragma unroll
         for (int kq = 0; kq < BK / 4; ++kq) {
             const int kr = kq * 4 + (lane >> 4);
             float af[FM], bf[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = As[kr][wm * TM + i * 16 + (lane & 15)];
+            for (int i = 0; i < FM; ++i) af[i] = a_at(buf, wm * TM + i * 16 + (lane & 15), kr);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = Bs[kr][wn * TN + j * 16 + (lane & 15)];
+            for (int j = 0; j < FN; ++j) bf[j] = b_at(buf, wn * TN + j * 16 + (lane & 15), kr);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
+        // the other buffer was last read in iteration s-1, which every wave has
+        // left (barrier below), so it can be refilled now
+        if (s + 1 < nslab) store_slab(buf ^ 1);
         __syncthreads();
-        if (s + 1 < nslab) {
-            store_slab();
-            __syncthreads();
-        }
     }
 
     // epilogue

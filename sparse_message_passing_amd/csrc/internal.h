@@ -63,6 +63,7 @@ struct Graph {
     int64_t* row_ptr = nullptr;   // [n+1]
     int32_t* col = nullptr;       // [nnz]
     float* dinv = nullptr;        // [n]
+    float* wgcn = nullptr;        // [nnz] dinv[src] * dinv[dst] in CSR order
     int64_t* col_ptr = nullptr;   // [n+1]
     int32_t* csc_row = nullptr;   // [nnz]
     int32_t* csc_eid = nullptr;   // [nnz]
@@ -92,6 +93,7 @@ struct AggView {          // what an aggregation walks
     const int32_t* idx;   // col or csc_row (the "other end" of each edge)
     const int32_t* eid;   // CSR slot of each entry (CSC only) or nullptr
     const RowPlan* plan;
+    const float* wgcn;    // GCN weight per edge in this view's order (CSR only) or nullptr
 };
 
 AggView csr_view(const Graph& g);

@@ -54,6 +54,7 @@ struct SpmmArgs {
     Rank1Epilogue r1;
     MaskEpilogue mask;   // Y *= [M > 0]
     float* partial;
+    const float* wgcn;   // GCN edge weights in this view's edge order (NULL: dinv[u]*dinv[v] on the fly)
 };
 
 template <typename TO>
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
             const int64_t e = e0 + lane;
             u_my = a.idx[e];
             if (a.wmode == GNN_W_GCN) {
-                w_my[0] = a.dinv[u_my] * dv;
+                w_my[0] = a.wgcn ? a.wgcn[e] : a.dinv[u_my] * dv;
             } else if (a.wmode == GNN_W_ONES) {
                 w_my[0] = 1.0f;
             } else {
@@ -313,6 +314,7 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     a.r1 = r1;
     a.mask = mask;
     a.partial = partial;
+    a.wgcn = v.wgcn;
     a.pd = (d + 3) / 4 * 4;
     const size_t xs = dt_size(x_dt), ys = dt_size(y_dt);
     // 4-wide loads need 4-element aligned rows with room for the last quad;

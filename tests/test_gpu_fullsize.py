@@ -1,0 +1,279 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times, on outputs the oracle computes one by one (sampled rows,
+columns or edges), plus bit-exact checks where the whole output is cheap for
+the oracle (graph arrays, SDDMM add, quantisation codes)."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.graph import build_graph
+from parity import RTOL16, RTOL32, bf16_values, check_close, from_dev, sub_rows, to_dev
+from sparse_message_passing_amd import gnnmp, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(f"[fullsize] {msg}", flush=True)
+
+
+def sample_rows(og, k, seed):
+    """The k/4 highest in-degree rows (chunked, workgroup paths) and 3k/4 random rows."""
+    r = np.random.default_rng(seed)
+    top = og.degree_perm()[: k // 4]
+    rnd = r.choice(og.n, k - k // 4, replace=False)
+    return np.unique(np.concatenate([top, rnd])).astype(np.int64)
+
+
+@pytest.fixture(scope="module")
+def c2():
+    t = time.time()
+    inp = synth.config_inputs(2)
+    n = int(inp["n"])
+    g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
+    og = build_graph(inp["src"], inp["dst"], n, True)
+    log(f"C2 graph n={n} nnz={og.nnz} ({time.time() - t:.1f} s)")
+    return g, og, inp
+
+
+def test_c2_graph_bit_exact(c2):
+    g, og, _ = c2
+    ex = gnnmp.gnn_graph_export(g)
+    assert np.array_equal(ex["row_ptr"], og.row_ptr) and np.array_equal(ex["col"], og.col)
+    dinv, w = og.gcn_norm()
+    assert np.array_equal(ex["dinv"].view(np.uint32), dinv.view(np.uint32))
+    assert np.array_equal(ex["w"].view(np.uint32), w.view(np.uint32))
+    assert np.array_equal(ex["perm"], og.degree_perm())
+
+
+@pytest.mark.parametrize("d", [256, 128, 41])
+def test_c2_aggregation_sampled_rows(c2, d):
+    g, og, _ = c2
+    X = synth.normal((og.n, d), 77 + d)
+    ld = (d + 3) // 4 * 4
+    Xb = torch.zeros((og.n, ld), device="cuda")
+    Xb[:, :d] = to_dev(X)
+    Yb = torch.empty((og.n, ld), device="cuda")
+    gnnmp.gnn_spmm(g, Xb[:, :d], Yb[:, :d])
+    rows = sample_rows(og, 4096, d)
+    sg, eids = sub_rows(og, rows)
+    w = og.gcn_norm()[1][eids]
+    ref = oracle.spmm(sg, X, w)
+    mag = oracle.spmm(sg, np.abs(X), np.abs(w))
+    check_close(from_dev(Yb[:, :d])[rows], ref, mag, what=f"C2 aggregation d={d}")
+
+
+def test_c2_first_layer_forward_sampled_rows(c2):
+    # ReLU((A_hat X) W1) at 2^20 nodes, 128 -> 256 (aggregate first)
+    g, og, inp = c2
+    X, W = inp["X"], inp["W0"]
+    Y = torch.empty((og.n, 256), device="cuda")
+    saved = torch.empty((og.n, 128), device="cuda")
+    gnnmp.gnn_gcn_layer_fwd(g, to_dev(X), to_dev(W), Y, relu=True, saved=saved)
+    rows = sample_rows(og, 2048, 5)
+    sg, eids = sub_rows(og, rows)
+    w = og.gcn_norm()[1][eids]
+    AX = oracle.to_f32(oracle.spmm(sg, X, w))
+    ref = np.maximum(AX.astype(np.float64) @ W, 0)
+    mag = oracle.spmm(sg, np.abs(X), np.abs(w)) @ np.abs(W)
+    check_close(from_dev(Y)[rows], ref, mag, what="C2 layer-1 forward")
+
+
+@pytest.mark.parametrize("shape", [("nn", 256, 256), ("nn", 128, 256), ("nn", 256, 41), ("nt", 256, 256),
+                                   ("nt", 41, 256), ("tn", 256, 256)])
+def test_c2_gemm_sampled(shape):
+    kind, a, b = shape
+    n = 1 << 20
+    r = np.random.default_rng(a * b)
+    if kind == "nn":      # [n, a] @ [a, b]
+        A = synth.normal((n, a), 11)
+        B = synth.glorot(a, b, 12)
+        C = torch.empty((n, b), device="cuda")
+        gnnmp.gnn_gemm(to_dev(A), to_dev(B), C)
+        rows = r.choice(n, 4096, replace=False)
+        ref = A[rows].astype(np.float64) @ B
+        mag = np.abs(A[rows]).astype(np.float64) @ np.abs(B)
+        check_close(from_dev(C)[rows], ref, mag, what=f"gemm nn {a}x{b}")
+    elif kind == "nt":    # [n, a] @ [b, a]^T
+        A = synth.normal((n, a), 13)
+        B = synth.glorot(b, a, 14)
+        C = torch.empty((n, b), device="cuda")
+        gnnmp.gnn_gemm(to_dev(A), to_dev(B), C, transB=True)
+        rows = r.choice(n, 4096, replace=False)
+        ref = A[rows].astype(np.float64) @ B.T.astype(np.float64)
+        mag = np.abs(A[rows]).astype(np.float64) @ np.abs(B).T
+        check_close(from_dev(C)[rows], ref, mag, what=f"gemm nt {a}x{b}")
+    else:                 # [n, a]^T @ [n, b], K = n (split over K)
+        A = synth.normal((n, a), 15)
+        B = synth.normal((n, b), 16)
+        C = torch.empty((a, b), device="cuda")
+        gnnmp.gnn_gemm(to_dev(A), to_dev(B), C, transA=True)
+        cols = r.choice(b, 8, replace=False)
+        ref = A.T.astype(np.float64) @ B[:, cols].astype(np.float64)
+        mag = np.abs(A).T.astype(np.float64) @ np.abs(B[:, cols]).astype(np.float64)
+        check_close(from_dev(C)[:, cols], ref, mag, what="gemm tn (weight gradient)")
+
+
+# ---------------------------------------------------------------------------
+# GAT layer at 2^21 nodes, 4 heads x 64, input 256
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def c3():
+    t = time.time()
+    inp = synth.config_inputs(3)
+    n = int(inp["n"])
+    g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=False, csc=True)
+    og = build_graph(inp["src"], inp["dst"], n, False)
+    log(f"C3 graph n={n} nnz={og.nnz} ({time.time() - t:.1f} s)")
+    return g, og, inp
+
+
+def test_c3_gat_forward_sampled(c3):
+    g, og, inp = c3
+    cfg = synth.CONFIGS[3]
+    h, dh, slope = cfg["heads"], cfg["d_head"], cfg["slope"]
+    X, W, a_s, a_d = inp["X"], inp["W"], inp["a_src"], inp["a_dst"]
+    Y = torch.empty((og.n, h * dh), device="cuda")
+    saved = torch.empty(gnnmp.gnn_gat_saved_size(g, h, dh), dtype=torch.uint8, device="cuda")
+    gnnmp.gnn_gat_layer_fwd(g, to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d), h, dh, slope, Y, saved)
+    Hp_d, S_d, D_d, Ep_d, al_d = gnnmp.gat_saved_views(g, saved, h, dh)
+    rows = sample_rows(og, 1024, 3)
+    sg, eids = sub_rows(og, rows)
+    # every node the sampled rows touch, and the sub-graph in that local numbering
+    need = np.unique(np.concatenate([sg.col, rows])).astype(np.int64)
+    loc = oracle.OracleGraph(sg.n, sg.row_ptr, np.searchsorted(need, sg.col).astype(np.int32),
+                             np.searchsorted(need, sg.dst).astype(np.int32))
+    Hp = oracle.to_f32(X[need].astype(np.float64) @ W)
+    S = oracle.to_f32(oracle.gat_scores(Hp, a_s, h))
+    D = oracle.to_f32(oracle.gat_scores(Hp, a_d, h))
+    mHp = np.abs(X[need]).astype(np.float64) @ np.abs(W)
+    nd = torch.from_numpy(need).cuda()
+    check_close(from_dev(Hp_d[nd]), Hp, mHp, what="C3 H'")
+    mS = oracle.gat_scores(mHp, np.abs(a_s), h)
+    mD = oracle.gat_scores(mHp, np.abs(a_d), h)
+    check_close(from_dev(S_d[nd]), S, mS, what="C3 S")
+    check_close(from_dev(D_d[nd]), D, mD, what="C3 D")
+    Ep, E = oracle.sddmm_add(loc, S, D, slope)
+    mE = mS[loc.col] + mD[loc.dst]
+    ed = torch.from_numpy(eids).cuda()
+    check_close(from_dev(Ep_d[ed]), Ep, mE, what="C3 E_pre")
+    alpha = oracle.to_f32(oracle.edge_softmax(loc, E))
+    rowmax = np.maximum.reduceat(mE, loc.row_ptr[:-1], axis=0)[np.repeat(np.arange(loc.n), np.diff(loc.row_ptr))]
+    m_al = alpha * (2 * rowmax + 1)
+    check_close(from_dev(al_d[ed]), alpha, m_al, what="C3 alpha")
+    ref = oracle.spmm(loc, Hp, alpha, h)
+    mY = oracle.spmm(loc, mHp, m_al, h) + oracle.spmm(loc, np.abs(Hp), alpha, h)
+    check_close(from_dev(Y)[rows], ref, mY, what="C3 GAT output")
+
+
+def test_c3_sddmm_add_full_bit_exact(c3):
+    # every edge of the 42M-edge graph, scores drawn at random
+    g, og, _ = c3
+    S = synth.normal((og.n, 4), 31)
+    D = synth.normal((og.n, 4), 32)
+    out = torch.empty((og.nnz, 4), device="cuda")
+    pre = torch.empty_like(out)
+    gnnmp.gnn_sddmm(g, "add", to_dev(S), to_dev(D), 4, 1, out, slope=0.2, out_pre=pre)
+    Ep, E = oracle.sddmm_add(og, S, D, 0.2)
+    assert np.array_equal(from_dev(pre).view(np.uint32), Ep.view(np.uint32))
+    assert np.array_equal(from_dev(out).view(np.uint32), E.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# quantised exchange of one partition (2^20 nodes, 314,573 marginal rows)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", [2, 4, 8, "mixed"])
+def test_c5_quantise_full_bit_exact(bits):
+    inp = synth.config_inputs(5)
+    H, rows, seed = inp["H"], inp["rows"], int(inp["philox_seed"])
+    b = inp["mixed_bits"] if bits == "mixed" else np.full(rows.size, bits, np.int32)
+    Hd = to_dev(H)
+    Hmix = Hd.clone()
+    Hmix_ref = H.copy()
+    for bb in (2, 4, 8):
+        sel = rows[b == bb]
+        if sel.size == 0:
+            continue
+        pk, sc, zr = oracle.quantize(H, sel, bb, seed)
+        pkd = torch.empty(pk.shape, dtype=torch.uint8, device="cuda")
+        scd = torch.empty(sel.size, device="cuda")
+        zrd = torch.empty(sel.size, device="cuda")
+        sd = to_dev(sel)
+        gnnmp.gnn_quantize(Hd, sd, bb, seed, pkd, scd, zrd)
+        assert np.array_equal(from_dev(pkd), pk)
+        assert np.array_equal(from_dev(scd).view(np.uint32), sc.view(np.uint32))
+        assert np.array_equal(from_dev(zrd).view(np.uint32), zr.view(np.uint32))
+        gnnmp.gnn_dequantize(pkd, scd, zrd, sd, bb, Hmix)
+        oracle.dequantize(pk, sc, zr, sel, H.shape[1], bb, Hmix_ref)
+    assert np.array_equal(from_dev(Hmix).view(np.uint32), Hmix_ref.view(np.uint32))
+
+
+def test_c5_mixed_aggregate_sampled_rows():
+    inp = synth.config_inputs(5)
+    n = int(inp["n"])
+    g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
+    og = build_graph(inp["src"], inp["dst"], n, True)
+    H, rows, seed = inp["H"], inp["rows"], int(inp["philox_seed"])
+    Hmix_ref = H.copy()
+    for bb in (2, 4, 8):
+        sel = rows[inp["mixed_bits"] == bb]
+        pk, sc, zr = oracle.quantize(H, sel, bb, seed)
+        oracle.dequantize(pk, sc, zr, sel, H.shape[1], bb, Hmix_ref)
+    Y = torch.empty((n, 256), device="cuda")
+    gnnmp.gnn_spmm(g, to_dev(Hmix_ref), Y)
+    sr = sample_rows(og, 4096, 9)
+    sg, eids = sub_rows(og, sr)
+    w = og.gcn_norm()[1][eids]
+    check_close(from_dev(Y)[sr], oracle.spmm(sg, Hmix_ref, w), oracle.spmm(sg, np.abs(Hmix_ref), np.abs(w)),
+                what="C5 aggregation of the mixed matrix")
+
+
+# ---------------------------------------------------------------------------
+# bf16 storage at 2.45M nodes (heavy-tailed, max degree ~17K)
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def c4():
+    t = time.time()
+    inp = synth.config_inputs(4)
+    n = int(inp["n"])
+    g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
+    og = build_graph(inp["src"], inp["dst"], n, True)
+    log(f"C4 graph n={n} nnz={og.nnz} max degree {og.deg.max()} ({time.time() - t:.1f} s)")
+    return g, og, inp
+
+
+def test_c4_graph_bit_exact(c4):
+    g, og, _ = c4
+    ex = gnnmp.gnn_graph_export(g)
+    assert np.array_equal(ex["row_ptr"], og.row_ptr) and np.array_equal(ex["col"], og.col)
+    assert np.array_equal(ex["dinv"].view(np.uint32), og.gcn_norm()[0].view(np.uint32))
+
+
+def test_c4_bf16_first_layer_and_aggregation_sampled(c4):
+    g, og, inp = c4
+    X = bf16_values(inp["X"])
+    W = inp["W0"]
+    Xd = to_dev(X, torch.bfloat16)
+    # layer 1, 100 -> 256, aggregate first, bf16 storage
+    Y = torch.empty((og.n, 256), dtype=torch.bfloat16, device="cuda")
+    saved = torch.empty((og.n, 100), dtype=torch.bfloat16, device="cuda")
+    gnnmp.gnn_gcn_layer_fwd(g, Xd, to_dev(W), Y, relu=True, saved=saved)
+    rows = sample_rows(og, 2048, 4)
+    sg, eids = sub_rows(og, rows)
+    w = og.gcn_norm()[1][eids]
+    AX = oracle.to_bf16(oracle.spmm(sg, X, w))
+    check_close(from_dev(saved)[rows], AX, oracle.spmm(sg, np.abs(X), np.abs(w)), rtol=RTOL16, bf16_out=True,
+                what="C4 A_hat X (bf16)")
+    ref = np.maximum(AX.astype(np.float64) @ W, 0)
+    mag = oracle.spmm(sg, np.abs(X), np.abs(w)) @ np.abs(W)
+    check_close(from_dev(Y)[rows], ref, mag, rtol=RTOL16, bf16_out=True, what="C4 layer-1 forward (bf16)")
+    # 256-wide bf16 aggregation (the hidden layers' SpMM)
+    H = bf16_values(synth.normal((og.n, 256), 41))
+    Hd = to_dev(H, torch.bfloat16)
+    Z = torch.empty_like(Hd)
+    gnnmp.gnn_spmm(g, Hd, Z)
+    check_close(from_dev(Z)[rows], oracle.spmm(sg, H, w), oracle.spmm(sg, np.abs(H), np.abs(w)), rtol=RTOL16,
+                bf16_out=True, what="C4 aggregation d=256 (bf16)")
