@@ -220,9 +220,9 @@ __device__ __forceinline__ void hv_block_reduce(HV<H>& a, float (*sh)[H]) {
 }
 
 template <int H>
-__global__ __launch_bounds__(256) void softmax_fwd_rows(Sched s, const float* E, float* alpha) {
+__device__ __forceinline__ void softmax_fwd_rows(const Sched& s, const float* E, float* alpha, int64_t blk) {
     const int lane = threadIdx.x % G;
-    const int64_t li = s.n_block + static_cast<int64_t>(blockIdx.x) * (256 / G) + threadIdx.x / G;
+    const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
     const int64_t v = s.order[li];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
@@ -253,9 +253,8 @@ __global__ __launch_bounds__(256) void softmax_fwd_rows(Sched s, const float* E,
 }
 
 template <int H>
-__global__ __launch_bounds__(256) void softmax_fwd_block(Sched s, const float* E, float* alpha) {
-    __shared__ float sh[4][H];
-    const int64_t v = s.order[blockIdx.x];
+__device__ __forceinline__ void softmax_fwd_block(const Sched& s, const float* E, float* alpha, int64_t blk, float (*sh)[H]) {
+    const int64_t v = s.order[blk];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
     HV<H> m;
     hv_fill<H>(m, -INFINITY);
@@ -298,10 +297,10 @@ __device__ __forceinline__ HV<H> dE_of(const HV<H>& a, const HV<H>& da, const HV
 }
 
 template <int H>
-__global__ __launch_bounds__(256) void softmax_bwd_rows(Sched s, const float* alpha, const float* dalpha,
-                                                        const float* pre, float slope, float* dE) {
+__device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* alpha, const float* dalpha,
+                                                        const float* pre, float slope, float* dE, int64_t blk) {
     const int lane = threadIdx.x % G;
-    const int64_t li = s.n_block + static_cast<int64_t>(blockIdx.x) * (256 / G) + threadIdx.x / G;
+    const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
     const int64_t v = s.order[li];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
@@ -320,10 +319,9 @@ __global__ __launch_bounds__(256) void softmax_bwd_rows(Sched s, const float* al
 }
 
 template <int H>
-__global__ __launch_bounds__(256) void softmax_bwd_block(Sched s, const float* alpha, const float* dalpha,
-                                                         const float* pre, float slope, float* dE) {
-    __shared__ float sh[4][H];
-    const int64_t v = s.order[blockIdx.x];
+__device__ __forceinline__ void softmax_bwd_block(const Sched& s, const float* alpha, const float* dalpha,
+                                                        const float* pre, float slope, float* dE, int64_t blk, float (*sh)[H]) {
+    const int64_t v = s.order[blk];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
     HV<H> P;
     hv_fill<H>(P, 0.0f);
@@ -343,9 +341,9 @@ __global__ __launch_bounds__(256) void softmax_bwd_block(Sched s, const float* a
 // edge -> node sums; over the CSC view the values are gathered through eid
 // ---------------------------------------------------------------------------
 template <int H>
-__global__ __launch_bounds__(256) void reduce_rows(Sched s, const float* vals, float* out) {
+__device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, float* out, int64_t blk) {
     const int lane = threadIdx.x % G;
-    const int64_t li = s.n_block + static_cast<int64_t>(blockIdx.x) * (256 / G) + threadIdx.x / G;
+    const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
     const int64_t v = s.order[li];
     HV<H> acc;
@@ -361,9 +359,8 @@ __global__ __launch_bounds__(256) void reduce_rows(Sched s, const float* vals, f
 }
 
 template <int H>
-__global__ __launch_bounds__(256) void reduce_block(Sched s, const float* vals, float* out) {
-    __shared__ float sh[4][H];
-    const int64_t v = s.order[blockIdx.x];
+__device__ __forceinline__ void reduce_block(const Sched& s, const float* vals, float* out, int64_t blk, float (*sh)[H]) {
+    const int64_t v = s.order[blk];
     HV<H> acc;
     hv_fill<H>(acc, 0.0f);
     for (int64_t e = s.ptr[v] + threadIdx.x; e < s.ptr[v + 1]; e += 256) {
@@ -374,6 +371,31 @@ __global__ __launch_bounds__(256) void reduce_block(Sched s, const float* vals, 
     }
     hv_block_reduce<H, false>(acc, sh);
     if (threadIdx.x == 0) st<H>(out + v * H, acc);
+}
+
+// One launch per op: the first n_block workgroups each take one long row (the
+// longest first), the rest take 16 short rows each, so the long rows run
+// alongside the short ones instead of in a launch of their own.
+template <int H>
+__global__ __launch_bounds__(256) void softmax_fwd_kernel(Sched s, const float* E, float* alpha) {
+    __shared__ float sh[4][H];
+    if (blockIdx.x < s.n_block) softmax_fwd_block<H>(s, E, alpha, blockIdx.x, sh);
+    else softmax_fwd_rows<H>(s, E, alpha, blockIdx.x - s.n_block);
+}
+
+template <int H>
+__global__ __launch_bounds__(256) void softmax_bwd_kernel(Sched s, const float* alpha, const float* dalpha,
+                                                          const float* pre, float slope, float* dE) {
+    __shared__ float sh[4][H];
+    if (blockIdx.x < s.n_block) softmax_bwd_block<H>(s, alpha, dalpha, pre, slope, dE, blockIdx.x, sh);
+    else softmax_bwd_rows<H>(s, alpha, dalpha, pre, slope, dE, blockIdx.x - s.n_block);
+}
+
+template <int H>
+__global__ __launch_bounds__(256) void reduce_kernel(Sched s, const float* vals, float* out) {
+    __shared__ float sh[4][H];
+    if (blockIdx.x < s.n_block) reduce_block<H>(s, vals, out, blockIdx.x, sh);
+    else reduce_rows<H>(s, vals, out, blockIdx.x - s.n_block);
 }
 
 // ---------------------------------------------------------------------------
@@ -424,6 +446,7 @@ __global__ __launch_bounds__(256) void colsum_stage1(int64_t n, const float* cA,
     for (int64_t f = threadIdx.x; f < d; f += 256) {
         const int64_t k = f / dh;
         float sa = 0.0f, sb = 0.0f;
+#pragma unroll 8
         for (int64_t v = r0; v < r1; ++v) {
             const float x = Hp[v * d + f];
             sa = fmaf(cA[v * heads + k], x, sa);
@@ -434,16 +457,24 @@ __global__ __launch_bounds__(256) void colsum_stage1(int64_t n, const float* cA,
     }
 }
 
+// out[f] (f < 2d: A then B) = sum over blocks b of partial[b][f], in a fixed
+// order: four thread groups take every fourth block, then their sums are added
+// in order.  One workgroup per 64 outputs.
 __global__ __launch_bounds__(256) void colsum_stage2(int64_t nblk, int64_t d, const float* partial, float* outA,
                                                      float* outB) {
-    for (int64_t f = threadIdx.x; f < d; f += 256) {
-        float sa = 0.0f, sb = 0.0f;
-        for (int64_t b = 0; b < nblk; ++b) {
-            sa += partial[(b * 2 + 0) * d + f];
-            sb += partial[(b * 2 + 1) * d + f];
-        }
-        outA[f] = sa;
-        outB[f] = sb;
+    __shared__ float sh[4][64];
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x & 63);  // in [0, 2d)
+    const int grp = threadIdx.x >> 6;
+    float s = 0.0f;
+    if (o < 2 * d)
+        for (int64_t b = grp; b < nblk; b += 4) s += partial[b * 2 * d + o];
+    sh[grp][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (grp == 0 && o < 2 * d) {
+        const int t = threadIdx.x;
+        const float tot = ((sh[0][t] + sh[1][t]) + sh[2][t]) + sh[3][t];
+        if (o < d) outA[o] = tot;
+        else outB[o - d] = tot;
     }
 }
 
@@ -518,8 +549,7 @@ gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha,
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
     GNN_HEADS_SWITCH(heads, {
-        if (s.n_block) hipLaunchKernelGGL((softmax_fwd_block<H>), dim3(s.n_block), dim3(256), 0, st, s, E, alpha);
-        if (blocks) hipLaunchKernelGGL((softmax_fwd_rows<H>), dim3(blocks), dim3(256), 0, st, s, E, alpha);
+        hipLaunchKernelGGL((softmax_fwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, E, alpha);
     });
     return launch_status("gnn_edge_softmax");
 }
@@ -531,12 +561,8 @@ gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
     GNN_HEADS_SWITCH(heads, {
-        if (s.n_block)
-            hipLaunchKernelGGL((softmax_bwd_block<H>), dim3(s.n_block), dim3(256), 0, st, s, alpha, dalpha, pre,
-                               slope, dE);
-        if (blocks)
-            hipLaunchKernelGGL((softmax_bwd_rows<H>), dim3(blocks), dim3(256), 0, st, s, alpha, dalpha, pre, slope,
-                               dE);
+        hipLaunchKernelGGL((softmax_bwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, alpha, dalpha,
+                           pre, slope, dE);
     });
     return launch_status("gnn_edge_softmax_bwd");
 }
@@ -547,8 +573,7 @@ gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, 
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
     GNN_HEADS_SWITCH(heads, {
-        if (s.n_block) hipLaunchKernelGGL((reduce_block<H>), dim3(s.n_block), dim3(256), 0, st, s, vals, out);
-        if (blocks) hipLaunchKernelGGL((reduce_rows<H>), dim3(blocks), dim3(256), 0, st, s, vals, out);
+        hipLaunchKernelGGL((reduce_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, vals, out);
     });
     return launch_status("gnn_edge_reduce");
 }
@@ -588,7 +613,7 @@ gnn_status_t launch_head_colsum(int64_t n, const float* coefA, const float* coef
     if (nblk > 0)
         hipLaunchKernelGGL(colsum_stage1, dim3(nblk), dim3(256), 0, st, n, coefA, coefB, Hp, d, heads, d_head,
                            partial);
-    hipLaunchKernelGGL(colsum_stage2, dim3(1), dim3(256), 0, st, nblk, d, partial, outA, outB);
+    hipLaunchKernelGGL(colsum_stage2, dim3((2 * d + 63) / 64), dim3(256), 0, st, nblk, d, partial, outA, outB);
     return launch_status("GAT attention-vector gradient");
 }
 
