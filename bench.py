@@ -35,6 +35,28 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gcn3_rmat20_hbm_counters.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the 256-wide aggregation, read from the
+    committed rocprofv3 counter summary; None when spmm.hip has changed
+    since the counters were taken (the summary records the source's sha1)."""
+    import hashlib
+    import re
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+        nbytes = re.search(r"^- traffic bytes per launch: (\d+)$", text, re.M)
+        sha = re.search(r"^- spmm\.hip sha1: ([0-9a-f]{40})$", text, re.M)
+        src = os.path.join(ROOT, "sparse_message_passing_amd", "csrc", "spmm.hip")
+        with open(src, "rb") as f:
+            cur = hashlib.sha1(f.read()).hexdigest()
+    except OSError:
+        return None
+    if nbytes is None or sha is None or sha.group(1) != cur:
+        return None
+    return int(nbytes.group(1))
 
 
 def parse():
@@ -63,28 +85,36 @@ def event_time(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
-def spmm_compulsory_bytes(n, nnz, d, s_in=4, s_out=4):
-    """row_ptr (int64) + col (int32) + dinv (4 n) + each input row once + each output row once."""
-    return 8 * (n + 1) + 4 * nnz + 4 * n + s_in * n * d + s_out * n * d
+def spmm_compulsory_bytes(n, nnz, d, s_in=4, s_out=4, edge_weights=True):
+    """row_ptr (int64) + col (int32) + the GCN weights (one f32 per edge as
+    stored, else dinv, one f32 per node) + each input row once + each output
+    row once."""
+    w = 4 * nnz if edge_weights else 4 * n
+    return 8 * (n + 1) + 4 * nnz + w + s_in * n * d + s_out * n * d
 
 
-def cpu_baseline_gcn(scale_down):
+def cpu_baseline_gcn(min_seconds=10.0, max_passes=3):
+    """The oracle's 3-layer forward+backward on the full workload, repeated
+    until at least `min_seconds` of CPU work (at most `max_passes` passes)."""
     import oracle
     from oracle.graph import build_graph
     from sparse_message_passing_amd import synth
-    inp = synth.config_inputs(2, scale_down=scale_down)
+    inp = synth.config_inputs(2)
     n = int(inp["n"])
     og = build_graph(inp["src"], inp["dst"], n, True)
     Ws = [inp["W0"], inp["W1"], inp["W2"]]
-    t0 = time.perf_counter()
-    oracle.gcn_forward_backward(og, inp["X"], Ws, inp["labels"])
-    dt = time.perf_counter() - t0
+    passes, dt = 0, 0.0
+    while passes < max_passes and (passes == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        oracle.gcn_forward_backward(og, inp["X"], Ws, inp["labels"])
+        dt += time.perf_counter() - t0
+        passes += 1
     # same aggregation count as the GPU step: 128 + 256 + 41 forward, 256 + 41 backward
-    work = og.nnz * (128 + 256 + 41 + 256 + 41)
+    work = passes * og.nnz * (128 + 256 + 41 + 256 + 41)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return dict(value=work / dt / 1e9, unit="GEdge*feat/s", cores=threads, kind="oracle",
-                sample=f"full 3-layer forward+backward of the same generator at 2^{20 - scale_down} nodes "
-                       f"(nnz {og.nnz}), {dt:.2f} s")
+                sample=f"{passes} full 3-layer forward+backward pass(es) of the same workload "
+                       f"(2^20 nodes, nnz {og.nnz}), {dt:.2f} s")
 
 
 def main():
@@ -164,11 +194,17 @@ def main():
         spmm_ms = event_time(lambda: gnnmp.gnn_spmm(g, X, Y, ws=ws), a.kernel_reps, stream)
         byts = spmm_compulsory_bytes(g.n, g.nnz, d)
         ach = byts / (spmm_ms * 1e-3) / 1e9
+        traffic = measured_traffic()
         roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(ach / HBM_PEAK_GBS, 4), traffic=None)
+                        frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic)
         extra["spmm_d256_ms"] = round(spmm_ms, 4)
         extra["spmm_d256_gedge_feat_s"] = round(g.nnz * d / (spmm_ms * 1e-3) / 1e9, 2)
         extra["spmm_d256_compulsory_bytes"] = byts
+        extra["spmm_d256_compulsory_bytes_dinv"] = spmm_compulsory_bytes(g.n, g.nnz, d, edge_weights=False)
+        extra["spmm_d256_gather_model_bytes"] = 8 * (g.n + 1) + 8 * g.nnz + 4 * g.nnz * d + 4 * g.n * d
+        if traffic:
+            extra["spmm_d256_counter_GBs"] = round(traffic / (spmm_ms * 1e-3) / 1e9, 1)
+            extra["spmm_d256_traffic_amplification"] = round(traffic / byts, 2)
         # the update GEMM of the 256 -> 256 layer on the matrix cores
         Wt = runner.Ws[1]
         Z = torch.empty_like(X)
@@ -188,7 +224,7 @@ def main():
     cpu = None
     if not a.no_cpu_baseline and cfg["kind"] == "gcn":
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_gcn(scale_down=2)
+        cpu = cpu_baseline_gcn()
     out = {
         "metric": "GNN layer fwd+bwd GEdge*feat/s; SpMM/SDDMM HBM GB/s as % of peak",
         "value": round(value, 3),

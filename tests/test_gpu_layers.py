@@ -101,6 +101,34 @@ def test_gcn_layer_fwd_bwd(hubsym, case):
                 bf16_out=dt == "bf16", what="gcn dX (relu_in)")
 
 
+def test_gcn_layer_bwd_column_slabs():
+    # Source matrices over 256 MB are aggregated in 64-column slabs (300K rows
+    # x 256 f32 = 307 MB): the aggregate-first backward at that size, with the
+    # output-ReLU gradient mask and the fused input-ReLU mask on the slabbed
+    # aggregation, and a 2000-in-neighbour hub (chunked partial rows).
+    n, d_in, d_out = 300_000, 256, 288
+    s, t = hub_edges(n, 1_500_000, 2000, 41)
+    g, og = graph_pair(s, t, n, True, csc=False)
+    r = np.random.default_rng(17)
+    X = r.standard_normal((n, d_in)).astype(np.float32)
+    W = synth.glorot(d_in, d_out, 6)
+    Y_ref, saved_ref = oracle.gcn_layer_fwd(og, X, W, True)
+    dY = r.standard_normal((n, d_out)).astype(np.float32)
+    dX_ref, dW_ref = oracle.gcn_layer_bwd(og, X, saved_ref, Y_ref, dY, W, True)
+    w = og.gcn_norm()[1]
+    G = np.abs(np.where(Y_ref > 0, dY, 0.0))
+    mag_dW = oracle.spmm(og, np.abs(X), np.abs(w)).T @ G
+    mag_dX = oracle.spmm(og, G @ np.abs(W).T, np.abs(w))
+    dW = torch.empty((d_in, d_out), device="cuda")
+    dX = torch.empty((n, d_in), device="cuda")
+    gnnmp.gnn_gcn_layer_bwd(g, to_dev(X), to_dev(W), to_dev(Y_ref), to_dev(dY), True, dW, dX=dX,
+                            saved=to_dev(saved_ref), relu_in=True)
+    check_close(from_dev(dW), dW_ref, mag_dW, what="slabbed dW")
+    keep = X > 0
+    check_close(from_dev(dX), np.where(keep, dX_ref, 0.0), np.where(keep, mag_dX, 0.0) + 1e-30,
+                what="slabbed dX (relu_in)")
+
+
 def test_gcn_layer_row_strided(hubsym):
     # X, Y, saved and the gradients as row-strided views (widths 41 and 47 padded to 44 / 48)
     g, og = hubsym
