@@ -12,9 +12,15 @@
 //    planes), so every global->LDS store is a 16-byte write; the next slab's
 //    global loads are issued before the current slab's MFMAs and its LDS
 //    stores after them, one barrier per slab;
-//  * operand fragments: lane l supplies A[m0 + l%16][k0 + l/16] and
-//    B[k0 + l/16][n0 + l%16]; the result block leaves lane l holding rows
-//    m0 + 4*(l/16) + r, r = 0..3, of column n0 + l%16;
+//  * operand fragments: in MFMA j of a slab, lane l supplies
+//    B[k0 + 4(l/16) + j][n0 + l%16] as the instruction's first operand and
+//    A[m0 + l%16][k0 + 4(l/16) + j] as its second, so a k-contiguous
+//    operand's four values come from one 16-byte LDS read, and the block
+//    computed is the transposed tile: lane l ends holding C[m0 + l%16][n0 +
+//    4(l/16) + r], r = 0..3, four consecutive columns of one row, stored with
+//    one 16-byte write;
+//  * interior tiles load full slabs from running offsets with no per-element
+//    checks; only edge tiles and the last partial slab take the checked path;
 //  * the workgroup -> tile map keeps the tiles that share rows of A on one XCD
 //    (workgroups are dealt round-robin over the 8 XCDs, each with its own L2);
 //  * tall reductions (K = number of nodes, for dW) are split over K; each
@@ -33,8 +39,13 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 16;
-constexpr int PAD = 4;     // row padding of k-contiguous LDS tiles (rows stay 16-byte aligned)
-constexpr int PADM = 16;   // padding of k-major LDS planes: the four k rows a fragment read spans start 16 banks apart
+// LDS padding.  k-contiguous tiles: rows of BK + 4 = 20 floats, so the
+// 16-byte fragment reads of 8 consecutive lanes (rows r..r+7) cover the 32
+// banks once.  k-major planes: rows of (BM or BN) + 4 floats, so the k rows
+// 4g + j that lane groups g = 0, 1 (and 2, 3) read at the same time start
+// 16 banks apart.
+constexpr int PAD = 4;
+constexpr int PADM = 4;
 
 struct GemmArgs {
     int64_t M, N, K;
@@ -51,6 +62,9 @@ struct GemmArgs {
     int64_t nblocks; // real work items (tiles * splits)
     int64_t per_xcd; // ceil(nblocks / 8)
     int relu;        // ReLU epilogue (applied after the split-K sum)
+    int vec_c;       // C rows take 16-byte (bf16: 8-byte) stores
+    int vec_mask;    // mask rows take 16-byte (bf16: 8-byte) loads
+    int vec_ws;      // split-K partial rows (stride N) take 16-byte stores
     MaskEpilogue mask;  // C *= [M > 0] (after the split-K sum)
 };
 
@@ -59,6 +73,14 @@ __device__ __forceinline__ bool mask_on(const MaskEpilogue& m, int64_t r, int64_
     if (m.dt == GNN_BF16) return Elem<bf16_t>::load(static_cast<const bf16_t*>(m.M) + r * m.ld + c) > 0.0f;
     return Elem<float>::load(static_cast<const float*>(m.M) + r * m.ld + c) > 0.0f;
 }
+
+// Piece q of a k-contiguous slab (rows x BK): 16 consecutive lanes take 16
+// rows at the same k quad, the four lane groups of a wave the four quads, so
+// the 16-byte LDS stores hit the same conflict-free bank pattern as the
+// fragment reads (in global memory each row still gets 64 contiguous bytes
+// per instruction).
+__device__ __forceinline__ int kc_row(int q) { return (q >> 6) * 16 + (q & 15); }
+__device__ __forceinline__ int kc_k(int q) { return ((q >> 4) & 3) * 4; }
 
 template <typename T, bool VEC>
 __device__ __forceinline__ void load4(const T* base, int64_t off, bool full, int valid, float (&r)[4]) {
@@ -118,12 +140,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
     float ra[A_LOADS][4], rb[B_LOADS][4];
 
+    // Interior tiles (every row / column of the tile in range, 16-byte
+    // aligned operands) load full slabs without per-element checks, from
+    // per-thread offsets that advance by one slab per call.
+    const bool a_full = VA && m0 + BM <= g.M;
+    const bool b_full = VB && n0 + BN <= g.N;
+    int64_t a_off[A_LOADS], b_off[B_LOADS];
+#pragma unroll
+    for (int p = 0; p < A_LOADS; ++p) {
+        const int q = tid + p * 256;
+        if constexpr (!TRANS_A) a_off[p] = (m0 + kc_row(q)) * g.lda + kbeg + kc_k(q);
+        else a_off[p] = (kbeg + q / (BM / 4)) * g.lda + m0 + (q % (BM / 4)) * 4;
+    }
+#pragma unroll
+    for (int p = 0; p < B_LOADS; ++p) {
+        const int q = tid + p * 256;
+        if constexpr (!TRANS_B) b_off[p] = (kbeg + q / (BN / 4)) * g.ldb + n0 + (q % (BN / 4)) * 4;
+        else b_off[p] = (n0 + kc_row(q)) * g.ldb + kbeg + kc_k(q);
+    }
+    const int64_t a_step = TRANS_A ? BK * g.lda : BK;
+    const int64_t b_step = TRANS_B ? BK : BK * g.ldb;
+
     auto load_slab = [&](int64_t k0) {
+        const bool full_k = k0 + BK <= kend;
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
             const int q = tid + p * 256;
-            if constexpr (!TRANS_A) {  // contiguous along k: q -> (m, k4)
-                const int mm = q / (BK / 4), kk = (q % (BK / 4)) * 4;
+            if (a_full && full_k) {
+                load4<TA, true>(A, a_off[p], true, 4, ra[p]);
+            } else if constexpr (!TRANS_A) {  // contiguous along k: q -> (m, k4)
+                const int mm = kc_row(q), kk = kc_k(q);
                 const int64_t m = m0 + mm, k = k0 + kk;
                 const int valid = (m < g.M) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, kend - k))) : 0;
                 load4<TA, VA>(A, m * g.lda + k, valid == 4, valid, ra[p]);
@@ -133,21 +179,25 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                 const int valid = (k < kend) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, g.M - m))) : 0;
                 load4<TA, VA>(A, k * g.lda + m, valid == 4, valid, ra[p]);
             }
+            a_off[p] += a_step;
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
             const int q = tid + p * 256;
-            if constexpr (!TRANS_B) {  // contiguous along n: q -> (k, n4)
+            if (b_full && full_k) {
+                load4<TB, true>(B, b_off[p], true, 4, rb[p]);
+            } else if constexpr (!TRANS_B) {  // contiguous along n: q -> (k, n4)
                 const int kk = q / (BN / 4), nn = (q % (BN / 4)) * 4;
                 const int64_t n = n0 + nn, k = k0 + kk;
                 const int valid = (k < kend) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, g.N - n))) : 0;
                 load4<TB, VB>(B, k * g.ldb + n, valid == 4, valid, rb[p]);
             } else {                   // contiguous along k: q -> (n, k4)
-                const int nn = q / (BK / 4), kk = (q % (BK / 4)) * 4;
+                const int nn = kc_row(q), kk = kc_k(q);
                 const int64_t n = n0 + nn, k = k0 + kk;
                 const int valid = (n < g.N) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, kend - k))) : 0;
                 load4<TB, VB>(B, n * g.ldb + k, valid == 4, valid, rb[p]);
             }
+            b_off[p] += b_step;
         }
     };
     auto store_slab = [&](int buf) {
@@ -155,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int p = 0; p < A_LOADS; ++p) {
             const int q = tid + p * 256;
             if constexpr (A_KC) {
-                const int mm = q / (BK / 4), kk = (q % (BK / 4)) * 4;
+                const int mm = kc_row(q), kk = kc_k(q);
                 *reinterpret_cast<float4*>(&As[buf][mm * (BK + PAD) + kk]) =
                     make_float4(ra[p][0], ra[p][1], ra[p][2], ra[p][3]);
             } else {
@@ -168,7 +218,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int p = 0; p < B_LOADS; ++p) {
             const int q = tid + p * 256;
             if constexpr (B_KC) {
-                const int nn = q / (BK / 4), kk = (q % (BK / 4)) * 4;
+                const int nn = kc_row(q), kk = kc_k(q);
                 *reinterpret_cast<float4*>(&Bs[buf][nn * (BK + PAD) + kk]) =
                     make_float4(rb[p][0], rb[p][1], rb[p][2], rb[p][3]);
             } else {
@@ -177,14 +227,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                     make_float4(rb[p][0], rb[p][1], rb[p][2], rb[p][3]);
             }
         }
-    };
-    auto a_at = [&](int buf, int row, int k) -> float {
-        if constexpr (A_KC) return As[buf][row * (BK + PAD) + k];
-        else return As[buf][k * (BM + PADM) + row];
-    };
-    auto b_at = [&](int buf, int col, int k) -> float {
-        if constexpr (B_KC) return Bs[buf][col * (BK + PAD) + k];
-        else return Bs[buf][k * (BN + PADM) + col];
     };
 
     const int64_t nslab = (kend - kbeg + BK - 1) / BK;
@@ -196,44 +238,96 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     for (int64_t s = 0; s < nslab; ++s) {
         const int buf = static_cast<int>(s & 1);
         if (s + 1 < nslab) load_slab(kbeg + (s + 1) * BK);
+        // Fragments of the whole slab.  MFMA j of the slab takes k = 4g + j from
+        // lane group g = lane / 16 (any assignment of the slab's 16 k values to
+        // (j, g) pairs gives the same products, as long as A and B agree), so a
+        // k-contiguous operand is read with one 16-byte LDS load per row and
+        // slab, and a k-major one with four 4-byte loads.
+        const int g4 = 4 * (lane >> 4);
+        float af[FM][4], bfr[FN][4];
 #pragma unroll
-        for (int kq = 0; kq < BK / 4; ++kq) {
-            const int kr = kq * 4 + (lane >> 4);
-            float af[FM], bf[FN];
+        for (int i = 0; i < FM; ++i) {
+            const int row = wm * TM + i * 16 + (lane & 15);
+            if constexpr (A_KC) {
+                const float4 t = *reinterpret_cast<const float4*>(&As[buf][row * (BK + PAD) + g4]);
+                af[i][0] = t.x, af[i][1] = t.y, af[i][2] = t.z, af[i][3] = t.w;
+            } else {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = a_at(buf, wm * TM + i * 16 + (lane & 15), kr);
+                for (int j = 0; j < 4; ++j) af[i][j] = As[buf][(g4 + j) * (BM + PADM) + row];
+            }
+        }
 #pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = b_at(buf, wn * TN + j * 16 + (lane & 15), kr);
+        for (int jj = 0; jj < FN; ++jj) {
+            const int col = wn * TN + jj * 16 + (lane & 15);
+            if constexpr (B_KC) {
+                const float4 t = *reinterpret_cast<const float4*>(&Bs[buf][col * (BK + PAD) + g4]);
+                bfr[jj][0] = t.x, bfr[jj][1] = t.y, bfr[jj][2] = t.z, bfr[jj][3] = t.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bfr[jj][j] = Bs[buf][(g4 + j) * (BN + PADM) + col];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+                for (int jj = 0; jj < FN; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(bfr[jj][j], af[i][j], acc[i][jj], 0, 0, 0);
         // the other buffer was last read in iteration s-1, which every wave has
         // left (barrier below), so it can be refilled now
         if (s + 1 < nslab) store_slab(buf ^ 1);
         __syncthreads();
     }
 
-    // epilogue
+    // epilogue: the block (i, jj) leaves lane l holding C[m][nb + r], r = 0..3
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + wm * TM + i * 16 + (lane & 15);
+        if (m >= g.M) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * TN + j * 16 + (lane & 15);
+        for (int jj = 0; jj < FN; ++jj) {
+            const int64_t nb = n0 + wn * TN + jj * 16 + 4 * (lane >> 4);
+            float v[4] = {acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
+            const bool full = nb + 4 <= g.N;
+            if (g.splits > 1) {
+                float* w = g.ws + (split * g.M + m) * g.N + nb;
+                if (full && g.vec_ws) {
+                    *reinterpret_cast<float4*>(w) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm * TM + i * 16 + 4 * (lane >> 4) + r;
-                if (m < g.M && n < g.N) {
-                    if (g.splits > 1)
-                        g.ws[(split * g.M + m) * g.N + n] = acc[i][j][r];
-                    else
-                        Elem<TC>::store(static_cast<TC*>(g.C) + m * g.ldc + n,
-                                        !mask_on(g.mask, m, n) ? 0.0f
-                                        : g.relu             ? fmaxf(acc[i][j][r], 0.0f)
-                                                             : acc[i][j][r]);
+                    for (int r = 0; r < 4; ++r)
+                        if (nb + r < g.N) w[r] = v[r];
                 }
+                continue;
+            }
+            if (g.relu) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = fmaxf(v[r], 0.0f);
+            }
+            if (g.mask.M) {
+                float mk[4];
+                if (full && g.vec_mask) {
+                    float4 t;
+                    if (g.mask.dt == GNN_BF16)
+                        t = Elem<bf16_t>::load4(static_cast<const bf16_t*>(g.mask.M) + m * g.mask.ld + nb);
+                    else
+                        t = Elem<float>::load4(static_cast<const float*>(g.mask.M) + m * g.mask.ld + nb);
+                    mk[0] = t.x, mk[1] = t.y, mk[2] = t.z, mk[3] = t.w;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mk[r] = (nb + r < g.N && mask_on(g.mask, m, nb + r)) ? 1.0f : 0.0f;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = mk[r] > 0.0f ? v[r] : 0.0f;
+            }
+            TC* c = static_cast<TC*>(g.C) + m * g.ldc + nb;
+            if (full && g.vec_c) {
+                Elem<TC>::store4(c, make_float4(v[0], v[1], v[2], v[3]));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (nb + r < g.N) Elem<TC>::store(c + r, v[r]);
             }
         }
     }
@@ -376,7 +470,10 @@ gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K
         g.nblocks = g.tiles_m * g.tiles_n;
         g.per_xcd = (g.nblocks + 7) / 8;
     }
-    const size_t as = dt_size(a_dt), bs = dt_size(b_dt);
+    const size_t as = dt_size(a_dt), bs = dt_size(b_dt), cs = dt_size(c_dt);
+    g.vec_c = ldc % 4 == 0 && reinterpret_cast<uintptr_t>(C) % (4 * cs) == 0;
+    g.vec_mask = mask.M && mask.ld % 4 == 0 && reinterpret_cast<uintptr_t>(mask.M) % (4 * dt_size(mask.dt)) == 0;
+    g.vec_ws = N % 4 == 0;
     const bool va = lda % 4 == 0 && reinterpret_cast<uintptr_t>(A) % (4 * as) == 0;
     const bool vb = ldb % 4 == 0 && reinterpret_cast<uintptr_t>(B) % (4 * bs) == 0;
     if (!transA && !transB) return launch_trans<false, false>(g, p, a_dt, b_dt, c_dt, va, vb, st);
