@@ -16,9 +16,10 @@ on its own stream, and the CPU oracle timed on a bounded sample of the same
 workload.
 
 Other configs (timed the same way, for the record): 3 = one GAT layer
-(4 heads x 64, R-MAT 2^21, directed) forward + backward; 5 = one
-partition's quantised exchange (30% marginal rows of a 2^20-node R-MAT
-graph, 256 wide) followed by the aggregation.
+(4 heads x 64, R-MAT 2^21, directed) forward + backward; 4 = the 3-layer
+GCN with bf16 feature storage on a 2.45M-node Chung-Lu graph (100 -> 256 ->
+256 -> 47); 5 = one partition's quantised exchange (30% marginal rows of a
+2^20-node R-MAT graph, 256 wide) followed by the aggregation.
 """
 from __future__ import annotations
 
@@ -64,7 +65,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     return ap.parse_args()
@@ -147,7 +148,7 @@ def main():
     with torch.cuda.stream(stream):
         if cfg["kind"] == "gcn":
             Ws = [T(inp[f"W{i}"]) for i in range(3)]
-            runner = GcnStack(g, T(inp["X"]), Ws, T(inp["labels"]))
+            runner = GcnStack(g, T(inp["X"]), Ws, T(inp["labels"]), dtype=cfg.get("dtype", "f32"))
             work = runner.spmm_edge_feats()
             metric_work = work
         elif cfg["kind"] == "gat":
@@ -192,16 +193,18 @@ def main():
         Y = torch.empty_like(X)
         ws = torch.empty(max(gnnmp.lib().gnn_spmm_workspace_size(g.h, 0, d), 1), dtype=torch.uint8, device=dev)
         spmm_ms = event_time(lambda: gnnmp.gnn_spmm(g, X, Y, ws=ws), a.kernel_reps, stream)
-        byts = spmm_compulsory_bytes(g.n, g.nnz, d)
+        es = X.element_size()
+        byts = spmm_compulsory_bytes(g.n, g.nnz, d, s_in=es, s_out=es)
         ach = byts / (spmm_ms * 1e-3) / 1e9
-        traffic = measured_traffic()
+        traffic = measured_traffic() if a.config == 2 else None
         roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic)
         extra["spmm_d256_ms"] = round(spmm_ms, 4)
         extra["spmm_d256_gedge_feat_s"] = round(g.nnz * d / (spmm_ms * 1e-3) / 1e9, 2)
         extra["spmm_d256_compulsory_bytes"] = byts
-        extra["spmm_d256_compulsory_bytes_dinv"] = spmm_compulsory_bytes(g.n, g.nnz, d, edge_weights=False)
-        extra["spmm_d256_gather_model_bytes"] = 8 * (g.n + 1) + 8 * g.nnz + 4 * g.nnz * d + 4 * g.n * d
+        extra["spmm_d256_compulsory_bytes_dinv"] = spmm_compulsory_bytes(g.n, g.nnz, d, s_in=es, s_out=es,
+                                                                         edge_weights=False)
+        extra["spmm_d256_gather_model_bytes"] = 8 * (g.n + 1) + 8 * g.nnz + es * g.nnz * d + es * g.n * d
         if traffic:
             extra["spmm_d256_counter_GBs"] = round(traffic / (spmm_ms * 1e-3) / 1e9, 1)
             extra["spmm_d256_traffic_amplification"] = round(traffic / byts, 2)
@@ -236,7 +239,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16-storage/f32-accumulate" if cfg.get("dtype") == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": cfg["name"], "nodes": g.n, "nnz": g.nnz, "max_in_degree": g.max_in_degree,
                    "widths": cfg.get("widths"), "edge_feat_per_step": metric_work},

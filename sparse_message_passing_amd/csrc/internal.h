@@ -115,17 +115,29 @@ struct MaskEpilogue {     // out[r, f] *= [M[r, f] > 0]  (the ReLU derivative of
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
-                         const MaskEpilogue& mask = MaskEpilogue{});
+                         const MaskEpilogue& mask = MaskEpilogue{}, int64_t w_head_stride = 0);
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d);
+// whether gathers from a rows x row_bytes matrix are worth cutting into column slabs
+bool column_slabs_pay(int64_t rows, int64_t row_bytes);
 
 gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, const float* D, int64_t ldd,
                               int heads, float slope, float* out, float* out_pre, hipStream_t st);
 gnn_status_t launch_sddmm_dot(const AggView& v, const void* src_feat, int64_t ld_src, const void* dst_feat,
                               int64_t ld_dst, gnn_dtype_t dt, int heads, int64_t d_head, float* out, hipStream_t st);
 gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha, int heads, hipStream_t st);
+// dalpha_head_stride > 0: dalpha is head-major, dalpha(e, k) = dalpha[k*stride + e]
 gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha,
-                                     const float* pre, float slope, float* dE, int heads, hipStream_t st);
-gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st);
+                                     const float* pre, float slope, float* dE, int heads, hipStream_t st,
+                                     int64_t dalpha_head_stride = 0);
+// perm_dst != NULL: also writes perm_dst[k*perm_stride + j] = perm_src[eid(j)*heads + k] for every
+// position j of the view (CSR-order edge values re-laid head-major in this view's order)
+gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st,
+                                const float* perm_src = nullptr, float* perm_dst = nullptr, int64_t perm_stride = 0);
+// SDDMM dot in one column slab per head, out head-major: out[k*stride + e]
+bool sddmm_dot_heads_supported(int heads, int64_t d_head);
+gnn_status_t launch_sddmm_dot_heads(const AggView& v, const float* src_feat, int64_t ld_src, const float* dst_feat,
+                                    int64_t ld_dst, int heads, int64_t d_head, float* out, int64_t stride,
+                                    hipStream_t st);
 
 gnn_status_t launch_gat_scores(int64_t n, const float* Hp, int heads, int64_t d_head, const float* a_src,
                                const float* a_dst, float* S, float* D, hipStream_t st);

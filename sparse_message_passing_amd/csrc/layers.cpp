@@ -181,6 +181,7 @@ size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_
     const int64_t hd = heads * d_head;
     size_t t = align_up(e * heads * 4) + 2 * align_up(n * heads * 4) + align_up(n * hd * 4);
     t += align_up(head_colsum_partial_bytes(g.n, heads, d_head));
+    t += align_up(e * heads * 4);  // backward: head-major dalpha, then head-major alpha in CSC order
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
     gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
     t += align_up(gemm);
@@ -260,25 +261,41 @@ gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     float* dS = static_cast<float*>(c.take(static_cast<size_t>(g.n) * heads * 4));
     float* dHp = static_cast<float*>(c.take(static_cast<size_t>(g.n) * hd * 4));
     float* cps = static_cast<float*>(c.take(head_colsum_partial_bytes(g.n, heads, d_head)));
+    float* hm = static_cast<float*>(c.take(static_cast<size_t>(g.nnz) * heads * 4));
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
     gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
     void* gws = c.take(gemm);
     float* sws = static_cast<float*>(c.take(1));
     const AggView csr = csr_view(g), csc = csc_view(g);
-    // dalpha = dY[dst] . H'[src];  dE = alpha (dalpha - P) * LReLU'
-    GNN_TRY(launch_sddmm_dot(csr, s.Hp, hd, dY, hd, GNN_F32, heads, d_head, dEb, st));
-    GNN_TRY(launch_edge_softmax_bwd(csr, s.alpha, dEb, s.Epre, slope, dEb, heads, st));
-    // dD = in-edge sums, dS = out-edge sums
-    GNN_TRY(launch_edge_reduce(csr, dEb, heads, dD, st));
-    GNN_TRY(launch_edge_reduce(csc, dEb, heads, dS, st));
-    // dH' = (G . alpha)^T dY + dS a_src + dD a_dst
     Rank1Epilogue r1;
     r1.a = dS;
     r1.va = a_src;
     r1.b = dD;
     r1.vb = a_dst;
-    GNN_TRY(launch_spmm(csc, g.dinv, GNN_W_EDGE, s.alpha, heads, dY, GNN_F32, hd, dHp, GNN_F32, hd, hd, 0, r1, sws,
-                        st));
+    // Per-head column slabs when H' and dY outgrow the memory-side cache: the
+    // SDDMM dot runs one head at a time into a head-major dalpha plane set,
+    // and alpha is re-laid head-major in CSC order (inside the out-edge sum,
+    // which walks the CSC view anyway) so the transposed SpMM reads one
+    // contiguous weight stream per head instead of gathering through eid.
+    const bool by_head = sddmm_dot_heads_supported(heads, d_head) && column_slabs_pay(g.n, hd * 4);
+    if (by_head) {
+        // dalpha = dY[dst] . H'[src];  dE = alpha (dalpha - P) * LReLU'
+        GNN_TRY(launch_sddmm_dot_heads(csr, s.Hp, hd, dY, hd, heads, d_head, hm, g.nnz, st));
+        GNN_TRY(launch_edge_softmax_bwd(csr, s.alpha, hm, s.Epre, slope, dEb, heads, st, g.nnz));
+        // dD = in-edge sums, dS = out-edge sums (+ alpha re-laid, overwriting dalpha)
+        GNN_TRY(launch_edge_reduce(csr, dEb, heads, dD, st));
+        GNN_TRY(launch_edge_reduce(csc, dEb, heads, dS, st, s.alpha, hm, g.nnz));
+        // dH' = (G . alpha)^T dY + dS a_src + dD a_dst
+        GNN_TRY(launch_spmm(csc, g.dinv, GNN_W_EDGE, hm, heads, dY, GNN_F32, hd, dHp, GNN_F32, hd, hd, 0, r1, sws,
+                            st, MaskEpilogue{}, g.nnz));
+    } else {
+        GNN_TRY(launch_sddmm_dot(csr, s.Hp, hd, dY, hd, GNN_F32, heads, d_head, dEb, st));
+        GNN_TRY(launch_edge_softmax_bwd(csr, s.alpha, dEb, s.Epre, slope, dEb, heads, st));
+        GNN_TRY(launch_edge_reduce(csr, dEb, heads, dD, st));
+        GNN_TRY(launch_edge_reduce(csc, dEb, heads, dS, st));
+        GNN_TRY(launch_spmm(csc, g.dinv, GNN_W_EDGE, s.alpha, heads, dY, GNN_F32, hd, dHp, GNN_F32, hd, hd, 0, r1,
+                            sws, st));
+    }
     // da_src = sum_v dS[v] H'[v], da_dst = sum_v dD[v] H'[v] per head
     GNN_TRY(launch_head_colsum(g.n, dS, dD, s.Hp, heads, d_head, da_src, da_dst, cps, st));
     // dW = X^T dH',  dX = dH' W^T

@@ -78,6 +78,7 @@ struct SpmmArgs {
     MaskEpilogue mask;   // Y *= [M > 0]
     float* partial;
     const float* wgcn;   // GCN edge weights in this view's edge order (NULL: dinv[u]*dinv[v] on the fly)
+    int64_t w_hstride;   // > 0: edge weights head-major in this view's order, weight(e, k) = edge_w[k*w_hstride + e]
 };
 
 template <typename TO>
@@ -129,6 +130,10 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
     }
     const float dv = a.wmode == GNN_W_GCN ? a.dinv[row] : 1.0f;
     const int heads = a.heads;
+    // heads this slab's columns belong to (all heads when one pass covers the row)
+    const int64_t slab_f0 = slab * (LANES * VEC * NCH);
+    const int klo = static_cast<int>(slab_f0 / a.dh);
+    const int khi = static_cast<int>(min(a.d, slab_f0 + LANES * VEC * NCH) - 1) / static_cast<int>(a.dh);
 
     for (int64_t e0 = eb; e0 < ee; e0 += LANES) {
         const int cnt = static_cast<int>(min(static_cast<int64_t>(LANES), ee - e0));
@@ -143,11 +148,15 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
                 w_my[0] = a.wgcn ? a.wgcn[e] : a.dinv[u_my] * dv;
             } else if (a.wmode == GNN_W_ONES) {
                 w_my[0] = 1.0f;
+            } else if (a.w_hstride) {
+#pragma unroll
+                for (int k = 0; k < kMaxHeads; ++k)
+                    if (k >= klo && k <= khi) w_my[k] = a.edge_w[k * a.w_hstride + e];
             } else {
                 const int64_t ce = a.eid ? static_cast<int64_t>(a.eid[e]) : e;
 #pragma unroll
                 for (int k = 0; k < kMaxHeads; ++k)
-                    if (k < heads) w_my[k] = a.edge_w[ce * heads + k];
+                    if (k >= klo && k <= khi) w_my[k] = a.edge_w[ce * heads + k];
             }
         }
         for (int j = 0; j < cnt; j += 4) {
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
                     for (int c = 0; c < NCH; ++c) w[q][c] = 0.0f;
 #pragma unroll
                     for (int k = 0; k < kMaxHeads; ++k) {
-                        if (k < heads) {
+                        if (k >= klo && k <= khi) {
                             const float wk = group_bcast<LANES>(w_my[k], src);
 #pragma unroll
                             for (int c = 0; c < NCH; ++c) w[q][c] = hd[c] == k ? wk : w[q][c];
@@ -308,6 +317,8 @@ gnn_status_t dispatch(const SpmmArgs& a, int vec, int lanes, int nch, hipStream_
 
 }  // namespace
 
+bool column_slabs_pay(int64_t rows, int64_t row_bytes) { return rows * row_bytes > kSlabBytes; }
+
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d) {
     const int64_t pd = (d + 3) / 4 * 4;
     return p.n_chunks > 0 ? align_up(static_cast<size_t>(p.n_chunks) * pd * sizeof(float)) : 0;
@@ -316,7 +327,7 @@ size_t spmm_partial_bytes(const RowPlan& p, int64_t d) {
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
-                         const MaskEpilogue& mask) {
+                         const MaskEpilogue& mask, int64_t w_head_stride) {
     if (v.n == 0 || d == 0) return GNN_OK;
     if (heads > kMaxHeads) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm: at most 8 heads");
     SpmmArgs a;
@@ -344,6 +355,7 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     a.mask = mask;
     a.partial = partial;
     a.wgcn = v.wgcn;
+    a.w_hstride = wmode == GNN_W_EDGE ? w_head_stride : 0;
     a.pd = (d + 3) / 4 * 4;
     const size_t xs = dt_size(x_dt), ys = dt_size(y_dt);
     // 4-wide loads need 4-element aligned rows with room for the last quad;
@@ -355,7 +367,9 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     // Column slabs, except where each edge's weights are reached through the
     // CSC-to-CSR edge map: those scattered weight reads would repeat in every
     // slab (measured: slabs slow the transposed 4-head GAT aggregation down).
-    if (vec && !(wmode == GNN_W_EDGE && v.eid)) {
+    // Head-major weights in the view's own order are read contiguously, one
+    // head per slab.
+    if (vec && !(wmode == GNN_W_EDGE && v.eid && a.w_hstride == 0)) {
         // halve the pass width while the source rows' slab (rows x width)
         // exceeds the cache budget, down to the minimum slab row
         const int64_t rows = v.n;

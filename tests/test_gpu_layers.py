@@ -227,7 +227,15 @@ def test_gat_layer_fwd_bwd(gatg, heads, dh, din):
     mY = oracle.spmm(og, mHp, m_al, heads) + oracle.spmm(og, np.abs(fw["Hp"]), fw["alpha"], heads)
     check_close(from_dev(Y), fw["Y"], mY, what="GAT Y")
 
-    # backward on the oracle's saved tensors
+    _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r)
+
+
+def _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r):
+    """Backward from the oracle's forward tensors (copied into `saved`), every
+    gradient checked element by element."""
+    n, hd, din = og.n, heads * dh, X.shape[1]
+    Xd, Wd, asd, add = to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d)
+    Hp, S, D, Ep, al = gnnmp.gat_saved_views(g, saved, heads, dh)
     for view, key in zip((Hp, S, D, Ep, al), ("Hp", "S", "D", "E_pre", "alpha")):
         view.copy_(to_dev(fw[key]))
     dY = r.standard_normal((n, hd)).astype(np.float32)
@@ -251,6 +259,27 @@ def test_gat_layer_fwd_bwd(gatg, heads, dh, din):
     check_close(from_dev(dad), bw["da_dst"], np.einsum("nk,nkj->kj", m_dD, H3), what="da_dst")
     check_close(from_dev(dW), bw["dW"], np.abs(X).T @ m_dHp, what="GAT dW")
     check_close(from_dev(dX), bw["dX"], m_dHp @ np.abs(W).T, what="GAT dX")
+
+
+def test_gat_layer_bwd_by_head_slabs():
+    # H' and dY over 256 MB (300K rows x 4 heads x 64): the backward takes the
+    # per-head slab path (head-major dalpha, alpha re-laid in CSC order inside
+    # the out-edge sum, head-major weights in the transposed SpMM).  A hub
+    # with 5000 in-neighbours and ~5000 out-neighbours exercises the chunked
+    # and whole-workgroup rows of both views.
+    n, heads, dh, din, slope = 300_000, 4, 64, 32, 0.2
+    s, t = hub_edges(n, 2_000_000, 5000, 43)
+    s = np.concatenate([s, np.full(5000, 7, np.int32)])
+    t = np.concatenate([t, np.random.default_rng(44).choice(n, 5000, replace=False).astype(np.int32)])
+    g, og = graph_pair(s, t, n, False, csc=True)
+    r = np.random.default_rng(45)
+    X = r.standard_normal((n, din)).astype(np.float32)
+    W = synth.glorot(din, heads * dh, 3)
+    a_s = synth.glorot(dh, 1, 4, shape=(heads, dh))
+    a_d = synth.glorot(dh, 1, 5, shape=(heads, dh))
+    fw = oracle.gat_layer_fwd(og, X, W, a_s, a_d, heads, slope)
+    saved = torch.empty(gnnmp.gnn_gat_saved_size(g, heads, dh), dtype=torch.uint8, device="cuda")
+    _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r)
 
 
 def test_gat_bwd_requires_csc():
