@@ -224,6 +224,17 @@ def main():
         dw_ms = event_time(lambda: gnnmp.gnn_gemm(X, Z, dW, transA=True, ws=gws2), a.kernel_reps, stream)
         extra["gemm_dW_256x256_ms"] = round(dw_ms, 4)
         extra["gemm_dW_256x256_tflops"] = round(2.0 * g.n * d * d / (dw_ms * 1e-3) / 1e12, 2)
+    if cfg["kind"] == "quant":
+        # the same exchange with the dequantisation inside the gather, and the
+        # backward exchange of the embedding gradients (also fused)
+        with torch.cuda.stream(stream):
+            fused = QuantExchange(g, T(inp["H"]), inp["rows"], inp["mixed_bits"], int(inp["philox_seed"]), fused=True)
+            dY = torch.randn_like(fused.H)
+        fused_ms = event_time(fused.step, a.kernel_reps, stream)
+        bwd_ms = event_time(lambda: fused.backward(dY), a.kernel_reps, stream)
+        extra["fused_step_ms"] = round(fused_ms, 4)
+        extra["fused_step_gedge_feat_s"] = round(metric_work / (fused_ms * 1e-3) / 1e9, 2)
+        extra["backward_exchange_ms"] = round(bwd_ms, 4)
     cpu = None
     if not a.no_cpu_baseline and cfg["kind"] == "gcn":
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -208,6 +208,45 @@ gnn_status_t gnn_quantize(const float* H, int64_t ldh, int64_t d, const int32_t*
 gnn_status_t gnn_dequantize(const uint8_t* packed, const float* scale, const float* zero, int64_t n_rows,
                             int64_t d, int bits, const int32_t* rows, float* H, int64_t ldh, void* stream);
 
+/* Dequantise-in-gather aggregation.  AdaQP (Sec. 3, Eqn. 4, 5 and 7): the
+ * marginal rows a partition receives arrive as per-row codes with their scale
+ * and zero point, and are aggregated with the central rows; Tango's
+ * quantisation-aware aggregation reads the small quantised copy directly.
+ * Here the gather dequantises in registers, so the binary32 copy of the
+ * marginal rows is never written or re-read.
+ *
+ * A group is one bit-width buffer exactly as gnn_quantize writes it. */
+typedef struct {
+    const uint8_t* packed;  /* [n_rows, d*bits/8] device bytes, 4-byte aligned */
+    const float* scale;     /* [n_rows] device */
+    const float* zero;      /* [n_rows] device */
+    int64_t n_rows;         /* < 2^27 */
+    int bits;               /* 2, 4 or 8 */
+} gnn_qgroup_t;
+
+/* Slot map for gnn_spmm_dequant: qslot[v] = -1 for every v in [0, n), then
+ * qslot[rows_g[r]] = (g << 27) | r for each group g in order (a node listed
+ * twice keeps its last entry).  rows: host array of n_groups device pointers
+ * (int32 node ids in [0, n)); counts: host array of n_groups row counts;
+ * n_groups <= 8.  qslot: int32[n] device, written on `stream`. */
+gnn_status_t gnn_quant_slots(int64_t n, int n_groups, const int32_t* const* rows, const int64_t* counts,
+                             int32_t* qslot, void* stream);
+
+/* Y = A_hat X~ (GCN weights, CSR view) with X~[u] = X[u] when qslot[u] < 0,
+ * else the row of slot qslot[u] dequantised as gnn_dequantize does
+ * (fma(q, S, Z), one rounding).  The result is bitwise that of
+ * gnn_dequantize into a copy of X followed by gnn_spmm(GNN_W_GCN): the same
+ * values summed in the same order.  X [n, ldx] f32 (rows with qslot >= 0 are
+ * not read), Y [n, ldy] f32, d % 4 == 0, ldx % 4 == 0, X 16-byte aligned;
+ * groups: host array of n_groups (<= 8) descriptors whose codes have row
+ * length d*bits/8.  relu as in gnn_spmm.  Workspace:
+ * gnn_spmm_dequant_workspace_size(g, d) bytes (hub-row partials plus one
+ * 16-byte record per node, rebuilt from qslot and the groups on every call). */
+size_t gnn_spmm_dequant_workspace_size(gnn_graph_t g, int64_t d);
+gnn_status_t gnn_spmm_dequant(gnn_graph_t g, const float* X, int64_t ldx, const int32_t* qslot,
+                              const gnn_qgroup_t* groups, int n_groups, float* Y, int64_t ldy, int64_t d, int relu,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Layers (GCN: AdaQP Eqn. 3 / Sancus Sec. 2; GAT: Tango Fig. 1a/1b)
  * ------------------------------------------------------------------------ */

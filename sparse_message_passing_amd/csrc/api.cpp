@@ -354,4 +354,56 @@ gnn_status_t gnn_dequantize(const uint8_t* packed, const float* scale, const flo
     return launch_dequantize(packed, scale, zero, n_rows, d, bits, rows, H, ldh, static_cast<hipStream_t>(stream));
 }
 
+gnn_status_t gnn_quant_slots(int64_t n, int n_groups, const int32_t* const* rows, const int64_t* counts,
+                             int32_t* qslot, void* stream) {
+    GNN_REQUIRE(n >= 0 && n < (int64_t(1) << 31), "gnn_quant_slots: n out of range");
+    GNN_REQUIRE(n_groups >= 0 && n_groups <= 8, "gnn_quant_slots: at most 8 groups");
+    GNN_REQUIRE(n == 0 || qslot, "gnn_quant_slots: qslot is NULL");
+    GNN_REQUIRE(n_groups == 0 || (rows && counts), "gnn_quant_slots: rows or counts is NULL");
+    for (int g = 0; g < n_groups; ++g) {
+        GNN_REQUIRE(counts[g] >= 0 && counts[g] < (int64_t(1) << 27), "gnn_quant_slots: group row count out of range");
+        GNN_REQUIRE(counts[g] == 0 || rows[g], "gnn_quant_slots: NULL row list");
+    }
+    return launch_quant_slots(n, n_groups, rows, counts, qslot, static_cast<hipStream_t>(stream));
+}
+
+size_t gnn_spmm_dequant_workspace_size(gnn_graph_t h, int64_t d) {
+    if (!h || d < 1) return 0;
+    const Graph& g = h->g;
+    return align_up(spmm_partial_bytes(g.plan[0], d)) + align_up(quantised_source_record_bytes(g.n));
+}
+
+gnn_status_t gnn_spmm_dequant(gnn_graph_t h, const float* X, int64_t ldx, const int32_t* qslot,
+                              const gnn_qgroup_t* groups, int n_groups, float* Y, int64_t ldy, int64_t d, int relu,
+                              void* ws, size_t ws_bytes, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_spmm_dequant"));
+    const Graph& g = h->g;
+    GNN_REQUIRE(d >= 4 && d % 4 == 0, "gnn_spmm_dequant: d must be a positive multiple of 4");
+    GNN_REQUIRE(ldx >= d && ldy >= d && ldx % 4 == 0, "gnn_spmm_dequant: ldx, ldy must be >= d, ldx a multiple of 4");
+    GNN_REQUIRE(reinterpret_cast<uintptr_t>(X) % 16 == 0, "gnn_spmm_dequant: X must be 16-byte aligned");
+    GNN_REQUIRE(relu == 0 || relu == 1, "gnn_spmm_dequant: relu must be 0 or 1");
+    GNN_REQUIRE(n_groups >= 0 && n_groups <= 8, "gnn_spmm_dequant: at most 8 groups");
+    GNN_REQUIRE(n_groups == 0 || groups, "gnn_spmm_dequant: groups is NULL");
+    GNN_REQUIRE(g.n == 0 || (X && Y && qslot), "gnn_spmm_dequant: X, Y or qslot is NULL");
+    GNN_REQUIRE(static_cast<const void*>(X) != static_cast<const void*>(Y), "gnn_spmm_dequant: X and Y must not overlap");
+    for (int i = 0; i < n_groups; ++i) {
+        const gnn_qgroup_t& q = groups[i];
+        GNN_REQUIRE(q.bits == 2 || q.bits == 4 || q.bits == 8, "gnn_spmm_dequant: group bits must be 2, 4 or 8");
+        GNN_REQUIRE(q.n_rows >= 0 && q.n_rows < (int64_t(1) << 27), "gnn_spmm_dequant: group row count out of range");
+        GNN_REQUIRE(q.n_rows == 0 || (q.packed && q.scale && q.zero), "gnn_spmm_dequant: NULL group buffer");
+        GNN_REQUIRE(reinterpret_cast<uintptr_t>(q.packed) % 4 == 0, "gnn_spmm_dequant: codes must be 4-byte aligned");
+    }
+    const size_t part = align_up(spmm_partial_bytes(g.plan[0], d));
+    const size_t need = part + align_up(quantised_source_record_bytes(g.n));
+    if (!ws || ws_bytes < need) return fail(GNN_ERR_WORKSPACE, "gnn_spmm_dequant: workspace too small");
+    QuantSources qs;
+    qs.qslot = qslot;
+    qs.groups = groups;
+    qs.n_groups = n_groups;
+    qs.records = static_cast<char*>(ws) + part;
+    return launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, X, GNN_F32, ldx, Y, GNN_F32, ldy, d, relu,
+                       Rank1Epilogue{}, static_cast<float*>(ws), static_cast<hipStream_t>(stream), MaskEpilogue{}, 0,
+                       qs);
+}
+
 }  // extern "C"

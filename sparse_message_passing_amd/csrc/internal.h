@@ -112,10 +112,21 @@ struct MaskEpilogue {     // out[r, f] *= [M[r, f] > 0]  (the ReLU derivative of
     gnn_dtype_t dt = GNN_F32;
 };
 
+struct QuantSources {      // dequantise-in-gather: source rows with qslot[u] >= 0 come from quantised groups
+    const int32_t* qslot = nullptr;
+    const gnn_qgroup_t* groups = nullptr;  // host array of n_groups descriptors
+    int n_groups = 0;
+    void* records = nullptr;               // device scratch of 16 bytes per node (quantised_source_record_bytes)
+};
+inline size_t quantised_source_record_bytes(int64_t n) { return static_cast<size_t>(n) * 16; }
+
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
-                         const MaskEpilogue& mask = MaskEpilogue{}, int64_t w_head_stride = 0);
+                         const MaskEpilogue& mask = MaskEpilogue{}, int64_t w_head_stride = 0,
+                         const QuantSources& qs = QuantSources{});
+gnn_status_t launch_quant_slots(int64_t n, int n_groups, const int32_t* const* rows, const int64_t* counts,
+                                int32_t* qslot, hipStream_t st);
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d);
 // whether gathers from a rows x row_bytes matrix are worth cutting into column slabs
 bool column_slabs_pay(int64_t rows, int64_t row_bytes);

@@ -176,7 +176,31 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* packed, 
     }
 }
 
+__global__ __launch_bounds__(256) void slots_fill_kernel(int64_t n, int32_t* qslot) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) qslot[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void slots_scatter_kernel(const int32_t* rows, int64_t count, int32_t tag,
+                                                            int32_t* qslot) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (r < count) qslot[rows[r]] = tag | static_cast<int32_t>(r);
+}
+
 }  // namespace
+
+// Slot map of the dequantise-in-gather aggregation: -1 everywhere, then
+// (group << 27) | r at rows_g[r].  Groups are scattered one launch after the
+// other on the same stream, so a node listed in two groups keeps the later.
+gnn_status_t launch_quant_slots(int64_t n, int n_groups, const int32_t* const* rows, const int64_t* counts,
+                                int32_t* qslot, hipStream_t st) {
+    if (n > 0) hipLaunchKernelGGL(slots_fill_kernel, dim3((n + 255) / 256), dim3(256), 0, st, n, qslot);
+    for (int g = 0; g < n_groups; ++g)
+        if (counts[g] > 0)
+            hipLaunchKernelGGL(slots_scatter_kernel, dim3((counts[g] + 255) / 256), dim3(256), 0, st, rows[g],
+                               counts[g], static_cast<int32_t>(g) << 27, qslot);
+    return launch_status("gnn_quant_slots");
+}
 
 gnn_status_t launch_quantize(const float* H, int64_t ldh, int64_t d, const int32_t* rows, int64_t n_rows, int bits,
                              uint64_t seed, uint32_t stream_id, uint8_t* packed, float* scale, float* zero,

@@ -51,6 +51,16 @@ constexpr int kMaxHeads = 8;
 constexpr int64_t kSlabBytes = GNN_SPMM_SLAB_BYTES;
 constexpr int64_t kSlabMinBytes = GNN_SPMM_SLAB_MIN_BYTES;
 
+constexpr int kMaxQGroups = 8;
+
+struct QGroupDev {        // one bit-width buffer of quantised rows
+    const uint8_t* packed;
+    const float* scale;
+    const float* zero;
+    int64_t row_bytes;
+    int bits;
+};
+
 struct SpmmArgs {
     int64_t n;
     const int64_t* ptr;
@@ -79,7 +89,51 @@ struct SpmmArgs {
     float* partial;
     const float* wgcn;   // GCN edge weights in this view's edge order (NULL: dinv[u]*dinv[v] on the fly)
     int64_t w_hstride;   // > 0: edge weights head-major in this view's order, weight(e, k) = edge_w[k*w_hstride + e]
+    const int32_t* qslot;           // dequantise-in-gather: slot of each source node, -1 = row of X
+    QGroupDev qg[kMaxQGroups];
+    int q_words;                    // every group's code rows are whole 4-byte words
+    const uint4* qrec;              // per-node records (QRec), zero for rows of X
 };
+
+// Dequantise-in-gather.  A per-node record, built once per call, holds for
+// every quantised source its code-row address (bits in the top byte, which
+// device addresses leave free), its scale S and zero point Z, so the gather
+// needs no per-edge group lookup: the lane that owns an edge loads the record
+// with the edge's index and broadcasts it.  dq_load fetches the lane's code
+// bits for features f..f+3 (one aligned 4-byte load when every group's code
+// rows are whole words) and returns them raw, so the loads of the four edges
+// in flight are all issued before any of them is waited on; dq_decode turns
+// them into fma(q, S, Z), one correctly rounded operation each, exactly as the
+// dequantisation kernel does.
+struct QRec {
+    uint32_t lo, hi;  // code-row address, bits << 24 in hi
+    float S, Z;
+};
+
+__device__ __forceinline__ float4 dq_load(const SpmmArgs& a, uint32_t lo, uint32_t hi, float S, float Z, int64_t f) {
+    const int b = static_cast<int>(hi >> 24);
+    const uint8_t* row = reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi & 0xFFFFFFu) << 32) | lo);
+    const int64_t o = (f * b) >> 3;
+    uint32_t w;
+    if (a.q_words) {
+        w = *reinterpret_cast<const uint32_t*>(row + (o & ~int64_t(3))) >> (8 * (o & 3));
+    } else {
+        const uint8_t* cp = row + o;
+        if (b == 8) w = *reinterpret_cast<const uint32_t*>(cp);
+        else if (b == 4) w = *reinterpret_cast<const uint16_t*>(cp);
+        else w = *cp;
+    }
+    return make_float4(S, Z, __uint_as_float(w), __int_as_float(b));
+}
+
+__device__ __forceinline__ void dq_decode(float (&v)[4]) {
+    const float S = v[0], Z = v[1];
+    const uint32_t w = __float_as_uint(v[2]);
+    const int b = __float_as_int(v[3]);
+    const uint32_t m = (1u << b) - 1u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __fmaf_rn(static_cast<float>((w >> (i * b)) & m), S, Z);
+}
 
 template <typename TO>
 __device__ __forceinline__ float mask_of(const MaskEpilogue& m, int64_t row, int64_t f) {
@@ -92,7 +146,7 @@ struct Acc {
     float v[VEC];
 };
 
-template <int LANES, int VEC, int NCH, typename TI, typename TO>
+template <int LANES, int VEC, int NCH, typename TI, typename TO, bool QS>
 __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
     const int lane = threadIdx.x % LANES;
     const int64_t slab = blockIdx.x / a.slab_blocks;
@@ -138,12 +192,14 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
     for (int64_t e0 = eb; e0 < ee; e0 += LANES) {
         const int cnt = static_cast<int>(min(static_cast<int64_t>(LANES), ee - e0));
         int u_my = static_cast<int>(row);
+        uint4 r_my = make_uint4(0u, 0u, 0u, 0u);  // quantised-source record (QS)
         float w_my[kMaxHeads];
 #pragma unroll
         for (int k = 0; k < kMaxHeads; ++k) w_my[k] = 0.0f;
         if (lane < cnt) {
             const int64_t e = e0 + lane;
             u_my = a.idx[e];
+            if constexpr (QS) r_my = a.qrec[u_my];
             if (a.wmode == GNN_W_GCN) {
                 w_my[0] = a.wgcn ? a.wgcn[e] : a.dinv[u_my] * dv;
             } else if (a.wmode == GNN_W_ONES) {
@@ -161,11 +217,22 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
         }
         for (int j = 0; j < cnt; j += 4) {
             int u[4];
+            uint32_t qlo[4], qhi[4];
+            float qS[4], qZ[4];
             float w[4][NCH];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int src = (j + q < cnt) ? j + q : j;
                 u[q] = group_bcast<LANES>(u_my, src);
+                if constexpr (QS) {
+                    qlo[q] = static_cast<uint32_t>(group_bcast<LANES>(static_cast<int>(r_my.x), src));
+                    qhi[q] = static_cast<uint32_t>(group_bcast<LANES>(static_cast<int>(r_my.y), src));
+                    qS[q] = group_bcast<LANES>(__uint_as_float(r_my.z), src);
+                    qZ[q] = group_bcast<LANES>(__uint_as_float(r_my.w), src);
+                } else {
+                    qlo[q] = qhi[q] = 0u;
+                    qS[q] = qZ[q] = 0.0f;
+                }
                 if (heads == 1) {
                     const float w0 = group_bcast<LANES>(w_my[0], src);
 #pragma unroll
@@ -196,7 +263,9 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
                     if (act[c] && j + q < cnt) {
                         const TI* p = X + static_cast<int64_t>(u[q]) * a.ldx + f;
                         if constexpr (VEC == 4) {
-                            float4 t = Elem<TI>::load4(p);
+                            float4 t;
+                            if (QS && qhi[q] != 0u) t = dq_load(a, qlo[q], qhi[q], qS[q], qZ[q], f);  // raw
+                            else t = Elem<TI>::load4(p);
                             xv[q][c].v[0] = t.x;
                             xv[q][c].v[1] = t.y;
                             xv[q][c].v[2] = t.z;
@@ -209,6 +278,13 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
                         for (int i = 0; i < VEC; ++i) xv[q][c].v[i] = 0.0f;
                     }
                 }
+            }
+            if constexpr (QS && VEC == 4) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int c = 0; c < NCH; ++c)
+                        if (qhi[q] != 0u && j + q < cnt) dq_decode(xv[q][c].v);
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -263,6 +339,26 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
     }
 }
 
+// Per-node records of the dequantise-in-gather sources: zero for rows of X,
+// else (code-row address | bits << 56, S, Z) of the node's slot.
+__global__ __launch_bounds__(256) void qrec_kernel(SpmmArgs a, QRec* rec) {
+    const int64_t v = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (v >= a.n) return;
+    const int slot = a.qslot[v];
+    QRec r{0u, 0u, 0.0f, 0.0f};
+    if (slot >= 0) {
+        const int g = slot >> 27;
+        const int64_t i = slot & ((1 << 27) - 1);
+        const QGroupDev& G = a.qg[g];
+        const uint64_t addr = reinterpret_cast<uint64_t>(G.packed + i * G.row_bytes);
+        r.lo = static_cast<uint32_t>(addr);
+        r.hi = static_cast<uint32_t>(addr >> 32) | (static_cast<uint32_t>(G.bits) << 24);
+        r.S = G.scale[i];
+        r.Z = G.zero[i];
+    }
+    *reinterpret_cast<uint4*>(rec + v) = make_uint4(r.lo, r.hi, __float_as_uint(r.S), __float_as_uint(r.Z));
+}
+
 // Sum the partial rows of each heavy row in chunk order, then the epilogue.
 template <typename TO>
 __global__ __launch_bounds__(256) void spmm_fixup(SpmmArgs a) {
@@ -282,7 +378,7 @@ __global__ __launch_bounds__(256) void spmm_fixup(SpmmArgs a) {
     }
 }
 
-template <int LANES, int VEC, int NCH, typename TI, typename TO>
+template <int LANES, int VEC, int NCH, typename TI, typename TO, bool QS = false>
 void launch_t(SpmmArgs a, hipStream_t st) {
     const int64_t groups = a.n_chunks + (a.n - a.n_heavy);
     const int64_t gpb = 256 / LANES;
@@ -290,29 +386,45 @@ void launch_t(SpmmArgs a, hipStream_t st) {
     const int64_t slabs = (a.d + width - 1) / width;
     a.slab_blocks = (groups + gpb - 1) / gpb;
     if (a.slab_blocks > 0)
-        hipLaunchKernelGGL((spmm_kernel<LANES, VEC, NCH, TI, TO>), dim3(a.slab_blocks * slabs), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((spmm_kernel<LANES, VEC, NCH, TI, TO, QS>), dim3(a.slab_blocks * slabs), dim3(256), 0, st,
+                           a);
     if (a.n_heavy > 0) hipLaunchKernelGGL((spmm_fixup<TO>), dim3(a.n_heavy), dim3(256), 0, st, a);
 }
 
-template <typename TI, typename TO>
+template <typename TI, typename TO, bool QS = false>
 gnn_status_t dispatch(const SpmmArgs& a, int vec, int lanes, int nch, hipStream_t st) {
+    if constexpr (QS) {
+        // Whole-wave groups over the whole row: every edge's record, and so
+        // its decode branch, is wave uniform (broadcast with v_readlane).
+        // Measured on the quantised-exchange workload (2^20 nodes, 30%
+        // marginal rows, 256 wide): 3.47 ms, against 3.40 ms for the
+        // slabbed binary32 aggregation plus 0.10 ms of dequantisation (the
+        // smaller code rows make up for the lost column slabs); 16-lane
+        // groups in 64-column slabs took 4.2 ms (per-edge record broadcasts
+        // and divergent decodes), one feature per lane in 64-column slabs
+        // 8.9 ms (four times the instructions).
+        if (nch == 1) launch_t<64, 4, 1, TI, TO, true>(a, st);
+        else if (nch == 2) launch_t<64, 4, 2, TI, TO, true>(a, st);
+        else launch_t<64, 4, 4, TI, TO, true>(a, st);
+        return launch_status("gnn_spmm_dequant");
+    }
     if (vec == 4) {
         if (nch == 1) {
-            if (lanes == 8) launch_t<8, 4, 1, TI, TO>(a, st);
-            else if (lanes == 16) launch_t<16, 4, 1, TI, TO>(a, st);
-            else if (lanes == 32) launch_t<32, 4, 1, TI, TO>(a, st);
-            else launch_t<64, 4, 1, TI, TO>(a, st);
+            if (lanes == 8) launch_t<8, 4, 1, TI, TO, QS>(a, st);
+            else if (lanes == 16) launch_t<16, 4, 1, TI, TO, QS>(a, st);
+            else if (lanes == 32) launch_t<32, 4, 1, TI, TO, QS>(a, st);
+            else launch_t<64, 4, 1, TI, TO, QS>(a, st);
         } else if (nch == 2) {
-            launch_t<64, 4, 2, TI, TO>(a, st);
+            launch_t<64, 4, 2, TI, TO, QS>(a, st);
         } else {
-            launch_t<64, 4, 4, TI, TO>(a, st);
+            launch_t<64, 4, 4, TI, TO, QS>(a, st);
         }
-    } else {
+    } else if constexpr (!QS) {
         if (nch == 1) launch_t<64, 1, 1, TI, TO>(a, st);
         else if (nch == 2) launch_t<64, 1, 2, TI, TO>(a, st);
         else launch_t<64, 1, 4, TI, TO>(a, st);
     }
-    return launch_status("gnn_spmm");
+    return launch_status(QS ? "gnn_spmm_dequant" : "gnn_spmm");
 }
 
 }  // namespace
@@ -327,7 +439,7 @@ size_t spmm_partial_bytes(const RowPlan& p, int64_t d) {
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
-                         const MaskEpilogue& mask, int64_t w_head_stride) {
+                         const MaskEpilogue& mask, int64_t w_head_stride, const QuantSources& qs) {
     if (v.n == 0 || d == 0) return GNN_OK;
     if (heads > kMaxHeads) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm: at most 8 heads");
     SpmmArgs a;
@@ -356,6 +468,15 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     a.partial = partial;
     a.wgcn = v.wgcn;
     a.w_hstride = wmode == GNN_W_EDGE ? w_head_stride : 0;
+    a.qslot = qs.qslot;
+    a.qrec = nullptr;
+    a.q_words = 1;
+    for (int i = 0; i < qs.n_groups; ++i)
+        if ((d * qs.groups[i].bits / 8) % 4 || reinterpret_cast<uintptr_t>(qs.groups[i].packed) % 4) a.q_words = 0;
+    for (int i = 0; i < kMaxQGroups; ++i) a.qg[i] = QGroupDev{nullptr, nullptr, nullptr, 0, 0};
+    for (int i = 0; i < qs.n_groups && i < kMaxQGroups; ++i)
+        a.qg[i] = QGroupDev{qs.groups[i].packed, qs.groups[i].scale, qs.groups[i].zero, d * qs.groups[i].bits / 8,
+                            qs.groups[i].bits};
     a.pd = (d + 3) / 4 * 4;
     const size_t xs = dt_size(x_dt), ys = dt_size(y_dt);
     // 4-wide loads need 4-element aligned rows with room for the last quad;
@@ -389,6 +510,16 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     }
     const int vw = vec ? 4 : 1;
     if (nch == 0) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm: d too large (max 1024 for 16-byte rows, 256 otherwise)");
+    if (qs.qslot) {
+        if (!vec || heads != 1 || x_dt != GNN_F32 || y_dt != GNN_F32 || qs.n_groups > kMaxQGroups || !qs.records)
+            return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm_dequant: needs f32 rows in 16-byte vectors, one head, <= 8 groups");
+        const int64_t full = a.pd / 4;  // lanes for the whole row, no slabs
+        nch = full <= 64 ? 1 : full <= 128 ? 2 : full <= 256 ? 4 : 0;
+        if (nch == 0) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm_dequant: d must be at most 1024");
+        a.qrec = static_cast<const uint4*>(qs.records);
+        hipLaunchKernelGGL(qrec_kernel, dim3((v.n + 255) / 256), dim3(256), 0, st, a, static_cast<QRec*>(qs.records));
+        return dispatch<float, float, true>(a, vw, lanes, nch, st);
+    }
     if (x_dt == GNN_F32 && y_dt == GNN_F32) return dispatch<float, float>(a, vw, lanes, nch, st);
     if (x_dt == GNN_F32 && y_dt == GNN_BF16) return dispatch<float, bf16_t>(a, vw, lanes, nch, st);
     if (x_dt == GNN_BF16 && y_dt == GNN_F32) return dispatch<bf16_t, float>(a, vw, lanes, nch, st);

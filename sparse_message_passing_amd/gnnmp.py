@@ -44,6 +44,9 @@ _SIGS = {
     "gnn_softmax_xent": ("PIIIPPPIPSP", "i"),
     "gnn_quantize": ("PIIPIiQUPPPP", "i"),
     "gnn_dequantize": ("PPPIIiPPIP", "i"),
+    "gnn_quant_slots": ("IiPPPP", "i"),
+    "gnn_spmm_dequant_workspace_size": ("PI", "S"),
+    "gnn_spmm_dequant": ("PPIPPiPIIiPSP", "i"),
     "gnn_gcn_workspace_size": ("PII", "S"),
     "gnn_gcn_layer_fwd": ("PPiIIPIiPiIPPSP", "i"),
     "gnn_gcn_layer_bwd": ("PPiIIPIiiPPiIPPPPSP", "i"),
@@ -254,6 +257,34 @@ def gnn_dequantize(packed, scale, zero, rows, bits, H, d=None):
     _check(lib().gnn_dequantize(_p(packed), _p(scale), _p(zero), rows.numel(), d, bits, _p(rows), _p(H), _ld(H),
                                 _stream()))
     return H
+
+
+class QGroup(C.Structure):
+    """One bit-width buffer of quantised rows (gnn_qgroup_t)."""
+    _fields_ = [("packed", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p), ("n_rows", C.c_int64),
+                ("bits", C.c_int)]
+
+
+def gnn_quant_slots(n, rows_list, qslot):
+    """qslot[v] = -1, then (g << 27) | r at rows_list[g][r]."""
+    k = len(rows_list)
+    rows = (C.c_void_p * max(k, 1))(*[_p(r) for r in rows_list])
+    counts = (C.c_int64 * max(k, 1))(*[r.numel() for r in rows_list])
+    _check(lib().gnn_quant_slots(n, k, rows, counts, _p(qslot), _stream()))
+    return qslot
+
+
+def gnn_spmm_dequant(g: Graph, X, qslot, groups, Y, relu=False, d=None, ws=None):
+    """Y = A_hat X~, X~ = X with the slotted rows dequantised in the gather.
+    groups: list of (packed, scale, zero, bits)."""
+    d = X.shape[1] if d is None else d
+    arr = (QGroup * max(len(groups), 1))(*[QGroup(_p(pk), _p(sc), _p(zr), sc.numel(), b)
+                                           for pk, sc, zr, b in groups])
+    if ws is None:
+        ws = _ws(lib().gnn_spmm_dequant_workspace_size(g.h, d), X.device)
+    _check(lib().gnn_spmm_dequant(g.h, _p(X), _ld(X), _p(qslot), arr, len(groups), _p(Y), _ld(Y), d, int(relu),
+                                  _p(ws), ws.numel(), _stream()))
+    return Y
 
 
 # ---------------------------------------------------------------------------

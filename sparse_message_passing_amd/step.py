@@ -128,7 +128,16 @@ class GatLayer:
 
 
 class QuantExchange:
-    def __init__(self, g: gnnmp.Graph, H, rows, bits, seed, stream_id=0):
+    """One partition's quantised message exchange (AdaQP Sec. 3): the marginal
+    rows are quantised per row (one group per bit-width), "sent", and the
+    receiver aggregates them with the central rows.  The plain path
+    dequantises into a binary32 copy of the matrix and aggregates it; the
+    fused path aggregates straight from the codes (gnn_spmm_dequant), with
+    bitwise the same result.  backward() exchanges the embedding gradients of
+    the same rows the same way (Philox stream stream_id + 1) and aggregates
+    them over the transposed graph (A_hat is symmetric)."""
+
+    def __init__(self, g: gnnmp.Graph, H, rows, bits, seed, stream_id=0, fused=False):
         """bits: 2, 4, 8, or an int array giving each row's width."""
         self.g, self.H = g, H.contiguous()
         dev = H.device
@@ -143,20 +152,34 @@ class QuantExchange:
             self.groups.append((bb, torch.from_numpy(sel).to(dev),
                                 torch.empty((sel.size, d * bb // 8), dtype=torch.uint8, device=dev),
                                 torch.empty(sel.size, device=dev), torch.empty(sel.size, device=dev)))
-        self.seed, self.stream_id = seed, stream_id
-        self.Hmix = self.H.clone()
+        self.seed, self.stream_id, self.fused = seed, stream_id, fused
+        self.Hmix = None if fused else self.H.clone()
         self.Y = torch.empty_like(self.H)
-        self.ws = torch.empty(max(gnnmp.lib().gnn_spmm_workspace_size(g.h, 0, d), 1), dtype=torch.uint8, device=dev)
+        self.dH = torch.empty_like(self.H)
+        self.qslot = torch.empty(g.n, dtype=torch.int32, device=dev)
+        gnnmp.gnn_quant_slots(g.n, [gr[1] for gr in self.groups], self.qslot)
+        self.qgroups = [(pk, sc, zr, bb) for bb, _, pk, sc, zr in self.groups]
+        self.ws = torch.empty(max(gnnmp.lib().gnn_spmm_dequant_workspace_size(g.h, d), 1), dtype=torch.uint8,
+                              device=dev)
 
-    def quantize(self):
+    def quantize(self, M=None, stream_id=None):
+        M = self.H if M is None else M
+        sid = self.stream_id if stream_id is None else stream_id
         for bb, rows, pk, sc, zr in self.groups:
-            gnnmp.gnn_quantize(self.H, rows, bb, self.seed, pk, sc, zr, stream_id=self.stream_id)
+            gnnmp.gnn_quantize(M, rows, bb, self.seed, pk, sc, zr, stream_id=sid)
 
-    def dequantize(self):
+    def dequantize(self, out):
         for bb, rows, pk, sc, zr in self.groups:
-            gnnmp.gnn_dequantize(pk, sc, zr, rows, bb, self.Hmix)
+            gnnmp.gnn_dequantize(pk, sc, zr, rows, bb, out)
 
     def step(self):
         self.quantize()
-        self.dequantize()
+        if self.fused:
+            return gnnmp.gnn_spmm_dequant(self.g, self.H, self.qslot, self.qgroups, self.Y, ws=self.ws)
+        self.dequantize(self.Hmix)
         return gnnmp.gnn_spmm(self.g, self.Hmix, self.Y, ws=self.ws)
+
+    def backward(self, dY):
+        """dH = A_hat^T dY~, the marginal rows of dY exchanged quantised."""
+        self.quantize(dY, self.stream_id + 1)
+        return gnnmp.gnn_spmm_dequant(self.g, dY, self.qslot, self.qgroups, self.dH, ws=self.ws)

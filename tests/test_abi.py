@@ -21,7 +21,8 @@ def test_header_declares_the_boundary():
     names = declared()
     for must in ("gnn_graph_create", "gnn_spmm", "gnn_sddmm", "gnn_edge_softmax", "gnn_edge_softmax_bwd",
                  "gnn_edge_reduce", "gnn_gemm", "gnn_quantize", "gnn_dequantize", "gnn_softmax_xent",
-                 "gnn_gcn_layer_fwd", "gnn_gcn_layer_bwd", "gnn_gat_layer_fwd", "gnn_gat_layer_bwd"):
+                 "gnn_gcn_layer_fwd", "gnn_gcn_layer_bwd", "gnn_gat_layer_fwd", "gnn_gat_layer_bwd",
+                 "gnn_quant_slots", "gnn_spmm_dequant"):
         assert must in names
 
 
@@ -74,3 +75,9 @@ def test_status_strings_and_host_side_validation():
     t = np.array([1, 1], np.int32)
     st = L.gnn_graph_create(4, 2, s.ctypes.data, t.ctypes.data, 0, ctypes.byref(h))
     assert st == 1 and b"out of range" in L.gnn_last_error()
+    # slot map: more than 8 groups; negative n
+    assert L.gnn_quant_slots(4, 9, None, None, None, None) == 1
+    assert L.gnn_quant_slots(-1, 0, None, None, None, None) == 1
+    # dequantising aggregation: NULL graph; then d not a multiple of 4 is checked after the graph
+    st = L.gnn_spmm_dequant(None, None, 4, None, None, 0, None, 4, 4, 0, None, 0, None)
+    assert st == 1 and b"NULL" in L.gnn_last_error()

@@ -231,6 +231,45 @@ def test_c5_mixed_aggregate_sampled_rows():
                 what="C5 aggregation of the mixed matrix")
 
 
+def test_c5_dequant_in_gather_forward_and_backward():
+    # the exchange at full size with the dequantisation in the gather: the
+    # whole output bitwise equal to the two-kernel path, sampled rows against
+    # the oracle; then the backward exchange of the embedding gradients
+    from sparse_message_passing_amd.step import QuantExchange
+    inp = synth.config_inputs(5)
+    n = int(inp["n"])
+    g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
+    og = build_graph(inp["src"], inp["dst"], n, True)
+    H, rows, seed, bits = inp["H"], inp["rows"], int(inp["philox_seed"]), inp["mixed_bits"]
+    Hd = to_dev(H)
+    plain = QuantExchange(g, Hd, rows, bits, seed)
+    fused = QuantExchange(g, Hd, rows, bits, seed, fused=True)
+    Y1 = plain.step().clone()
+    Y2 = fused.step().clone()
+    assert torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
+    sr = sample_rows(og, 4096, 10)
+    sg, eids = sub_rows(og, sr)
+    w = og.gcn_norm()[1][eids]
+
+    def mixed(M, stream):
+        out = M.copy()
+        for bb in (2, 4, 8):
+            sel = rows[bits == bb]
+            pk, sc, zr = oracle.quantize(M, sel, bb, seed, stream)
+            oracle.dequantize(pk, sc, zr, sel, M.shape[1], bb, out)
+        return out
+
+    Hmix_ref = mixed(H, 0)
+    check_close(from_dev(Y2)[sr], oracle.spmm(sg, Hmix_ref, w), oracle.spmm(sg, np.abs(Hmix_ref), np.abs(w)),
+                what="C5 dequant-in-gather forward")
+    del Hmix_ref, Y1, Y2
+    dY = synth.normal((n, 256), 5077)
+    dH = fused.backward(to_dev(dY))
+    dmix_ref = mixed(dY, 1)
+    check_close(from_dev(dH)[sr], oracle.spmm(sg, dmix_ref, w), oracle.spmm(sg, np.abs(dmix_ref), np.abs(w)),
+                what="C5 backward gradient exchange")
+
+
 # ---------------------------------------------------------------------------
 # bf16 storage at 2.45M nodes (heavy-tailed, max degree ~17K)
 # ---------------------------------------------------------------------------

@@ -390,3 +390,113 @@ def test_quantized_exchange_then_aggregate(bits):
     gnnmp.gnn_spmm(g, Hmix, Y)
     w = og.gcn_norm()[1]
     check_close(from_dev(Y), Y_ref, oracle.spmm_mag(og, Hmix_ref, w), what="mixed aggregate")
+
+
+# ---------------------------------------------------------------------------
+# dequantise-in-gather aggregation (marginal rows read straight from codes)
+# ---------------------------------------------------------------------------
+def _gpu_groups(Hd, parts, seed, stream_id):
+    """Quantise each bit-width group on the GPU (codes checked against the
+    oracle's) and return the group descriptors and row lists."""
+    groups, rows_list = [], []
+    for bb, (sel, pk, sc, zr) in parts.items():
+        sd = to_dev(sel)
+        pkd = torch.empty(pk.shape, dtype=torch.uint8, device="cuda")
+        scd = torch.empty(sel.size, device="cuda")
+        zrd = torch.empty(sel.size, device="cuda")
+        gnnmp.gnn_quantize(Hd, sd, bb, seed, pkd, scd, zrd, stream_id=stream_id)
+        assert np.array_equal(from_dev(pkd), pk)
+        groups.append((pkd, scd, zrd, bb))
+        rows_list.append(sd)
+    return groups, rows_list
+
+
+@pytest.mark.parametrize("bits,d", [(2, 256), (4, 64), (8, 256), ("mixed", 256), ("mixed", 4)])
+def test_spmm_dequant_in_gather(bits, d):
+    # AdaQP Eqn. 5 and 7 with the dequantisation moved into the gather: against
+    # the oracle's dequantise-then-aggregate composition element by element,
+    # and bitwise against the GPU's two-kernel path (same values, same order).
+    s, t, n = rmat_graph(12, 24, True, 78)
+    g, og = graph_pair(s, t, n, True, csc=False)
+    r = np.random.default_rng(d)
+    H = r.standard_normal((n, d)).astype(np.float32)
+    rows = synth.marginal_rows(n, 0.3, 7)
+    H[rows[:5]] = 1.5                      # constant rows: scale 0, every value the zero point
+    b = bits if bits != "mixed" else synth.random_bits(rows.size, (2, 4, 8), 8)
+    seed, sid = 4321, 1
+    Hmix_ref, Y_ref, parts = oracle.quantized_aggregate(og, H, rows, b, seed=seed, stream=sid)
+    Hd = to_dev(H)
+    groups, rows_list = _gpu_groups(Hd, parts, seed, sid)
+    qslot = torch.empty(n, dtype=torch.int32, device="cuda")
+    gnnmp.gnn_quant_slots(n, rows_list, qslot)
+    want = np.full(n, -1, np.int64)
+    for gi, (bb, (sel, *_)) in enumerate(parts.items()):
+        want[sel] = (gi << 27) | np.arange(sel.size)
+    assert np.array_equal(from_dev(qslot).astype(np.int64), want)
+    Y = torch.empty((n, d), device="cuda")
+    gnnmp.gnn_spmm_dequant(g, Hd, qslot, groups, Y)
+    w = og.gcn_norm()[1]
+    check_close(from_dev(Y), Y_ref, oracle.spmm_mag(og, Hmix_ref, w), what=f"dequant-in-gather b={bits} d={d}")
+    Hmix = Hd.clone()
+    for (pkd, scd, zrd, bb), sd in zip(groups, rows_list):
+        gnnmp.gnn_dequantize(pkd, scd, zrd, sd, bb, Hmix)
+    Y2 = torch.empty_like(Y)
+    gnnmp.gnn_spmm(g, Hmix, Y2)
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+    # fused ReLU
+    gnnmp.gnn_spmm_dequant(g, Hd, qslot, groups, Y, relu=True)
+    gnnmp.gnn_spmm(g, Hmix, Y2, relu=True)
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+
+
+def test_spmm_dequant_without_quantised_rows():
+    # no groups, every slot -1: the plain aggregation, bitwise
+    s, t = hub_edges(2000, 12000, 700, 5)
+    g, og = graph_pair(s, t, 2000, True, csc=False)
+    X = to_dev(np.random.default_rng(2).standard_normal((2000, 128)).astype(np.float32))
+    qslot = torch.empty(2000, dtype=torch.int32, device="cuda")
+    gnnmp.gnn_quant_slots(2000, [], qslot)
+    assert bool((qslot == -1).all())
+    Y = torch.empty_like(X)
+    Y2 = torch.empty_like(X)
+    gnnmp.gnn_spmm_dequant(g, X, qslot, [], Y)
+    gnnmp.gnn_spmm(g, X, Y2)
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+
+
+def test_spmm_dequant_rejects_bad_shapes():
+    s, t = hub_edges(100, 400, 10, 6)
+    g, _ = graph_pair(s, t, 100, True, csc=False)
+    qslot = torch.full((100,), -1, dtype=torch.int32, device="cuda")
+    X = torch.zeros((100, 42), device="cuda")
+    with pytest.raises(gnnmp.GnnError, match="multiple of 4"):
+        gnnmp.gnn_spmm_dequant(g, X, qslot, [], torch.empty_like(X))
+    X = torch.zeros((100, 64), device="cuda")
+    pk = torch.zeros((1, 16), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros(1, device="cuda")
+    with pytest.raises(gnnmp.GnnError, match="bits"):
+        gnnmp.gnn_spmm_dequant(g, X, qslot, [(pk, sc, sc, 3)], torch.empty_like(X))
+
+
+def test_quantized_exchange_step_fused_and_backward():
+    # the step object: the fused forward equals the two-kernel forward bitwise;
+    # the backward exchanges the gradient rows quantised (Philox stream + 1)
+    from sparse_message_passing_amd.step import QuantExchange
+    s, t, n = rmat_graph(11, 24, True, 79)
+    g, og = graph_pair(s, t, n, True, csc=False)
+    r = np.random.default_rng(11)
+    H = r.standard_normal((n, 128)).astype(np.float32)
+    dY = r.standard_normal((n, 128)).astype(np.float32)
+    rows = synth.marginal_rows(n, 0.3, 12)
+    b = synth.random_bits(rows.size, (2, 4, 8), 13)
+    plain = QuantExchange(g, to_dev(H), rows, b, 77, stream_id=2)
+    fused = QuantExchange(g, to_dev(H), rows, b, 77, stream_id=2, fused=True)
+    Y1 = plain.step().clone()
+    Y2 = fused.step().clone()
+    assert torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
+    mix_ref, Y_ref, _ = oracle.quantized_aggregate(og, H, rows, b, seed=77, stream=2)
+    w = og.gcn_norm()[1]
+    check_close(from_dev(Y2), Y_ref, oracle.spmm_mag(og, mix_ref, w), what="exchange forward")
+    dH = fused.backward(to_dev(dY))
+    dmix_ref, dH_ref, _ = oracle.quantized_aggregate(og, dY, rows, b, seed=77, stream=3)
+    check_close(from_dev(dH), dH_ref, oracle.spmm_mag(og, dmix_ref, w), what="exchange backward")
