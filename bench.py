@@ -126,7 +126,7 @@ def main():
         sys.exit(2)
     import torch
     from sparse_message_passing_amd import gnnmp, synth
-    from sparse_message_passing_amd.step import GatLayer, GcnStack, QuantExchange
+    from sparse_message_passing_amd.step import GatLayer, GcnStack, OverlapExchange, QuantExchange
 
     if not os.path.exists(gnnmp.LIB_PATH):
         from sparse_message_passing_amd import build as hb
@@ -235,6 +235,14 @@ def main():
         extra["fused_step_ms"] = round(fused_ms, 4)
         extra["fused_step_gedge_feat_s"] = round(metric_work / (fused_ms * 1e-3) / 1e9, 2)
         extra["backward_exchange_ms"] = round(bwd_ms, 4)
+        # the exchange split by message origin (local / remote in-edges) under
+        # three schedules of the same kernels, and the stage timeline of each
+        with torch.cuda.stream(stream):
+            ov = OverlapExchange(g, T(inp["H"]), inp["rows"], inp["mixed_bits"], int(inp["philox_seed"]))
+        for name, fn in (("sequential", ov.step_sequential), ("free", ov.step_free), ("staged", ov.step_staged)):
+            extra[f"split_{name}_ms"] = round(event_time(fn, a.kernel_reps, stream), 4)
+            torch.cuda.synchronize()
+            extra[f"split_{name}_timeline_ms"] = ov.timeline()
     cpu = None
     if not a.no_cpu_baseline and cfg["kind"] == "gcn":
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

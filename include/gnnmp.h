@@ -88,6 +88,18 @@ const char* gnn_last_error(void);
  * GNN_ERR_OUT_OF_MEMORY, GNN_ERR_HIP. */
 gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const int32_t* dst,
                               uint32_t flags, gnn_graph_t* out);
+
+/* Split of the aggregation by message origin (AdaQP Eqn. 7: the sum over a
+ * node's local in-neighbours plus the sum over its remote ones).  marginal:
+ * host uint8[n], nonzero for the source rows that arrive over the exchange.
+ * Builds two graphs over the same n nodes: *local holds the in-edges whose
+ * source is not marginal, *remote those whose source is; every edge keeps its
+ * position order within its row and its GCN weight in g, so
+ * A_hat = A_local + A_remote entry by entry (use GNN_W_GCN with them; their
+ * dinv is g's).  Neither has a CSC view.  Both are destroyed with
+ * gnn_graph_destroy; on error neither is created. */
+gnn_status_t gnn_graph_split(gnn_graph_t g, const uint8_t* marginal, gnn_graph_t* local, gnn_graph_t* remote);
+
 gnn_status_t gnn_graph_destroy(gnn_graph_t g);
 
 typedef struct {
@@ -236,7 +248,10 @@ gnn_status_t gnn_quant_slots(int64_t n, int n_groups, const int32_t* const* rows
  * else the row of slot qslot[u] dequantised as gnn_dequantize does
  * (fma(q, S, Z), one rounding).  The result is bitwise that of
  * gnn_dequantize into a copy of X followed by gnn_spmm(GNN_W_GCN): the same
- * values summed in the same order.  X [n, ldx] f32 (rows with qslot >= 0 are
+ * values summed in the same order.  Z (nullable) is added to each sum before
+ * the ReLU, Y = A_hat X~ + Z, one rounding (AdaQP Eqn. 7: the remote part
+ * added to the local part); Z may be Y itself (ldz == ldy).
+ * X [n, ldx] f32 (rows with qslot >= 0 are
  * not read), Y [n, ldy] f32, d % 4 == 0, ldx % 4 == 0, X 16-byte aligned;
  * groups: host array of n_groups (<= 8) descriptors whose codes have row
  * length d*bits/8.  relu as in gnn_spmm.  Workspace:
@@ -244,8 +259,8 @@ gnn_status_t gnn_quant_slots(int64_t n, int n_groups, const int32_t* const* rows
  * 16-byte record per node, rebuilt from qslot and the groups on every call). */
 size_t gnn_spmm_dequant_workspace_size(gnn_graph_t g, int64_t d);
 gnn_status_t gnn_spmm_dequant(gnn_graph_t g, const float* X, int64_t ldx, const int32_t* qslot,
-                              const gnn_qgroup_t* groups, int n_groups, float* Y, int64_t ldy, int64_t d, int relu,
-                              void* ws, size_t ws_bytes, void* stream);
+                              const gnn_qgroup_t* groups, int n_groups, const float* Z, int64_t ldz, float* Y,
+                              int64_t ldy, int64_t d, int relu, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Layers (GCN: AdaQP Eqn. 3 / Sancus Sec. 2; GAT: Tango Fig. 1a/1b)

@@ -383,6 +383,21 @@ def gat_layer_bwd(g, fw, X, W, a_src, a_dst, dY, heads, slope, dt="f32"):
 # rows of H are quantised, dequantised into a copy of H (central rows stay
 # binary32) and the mixed matrix is aggregated with A_hat.
 # ---------------------------------------------------------------------------
+def split_aggregate(g, H, rows, bits, seed, stream=0):
+    """AdaQP Eqn. 7: the aggregation as the sum over local in-neighbours (rows
+    of H as they are) plus the sum over remote ones (the marginal rows after
+    quantisation and dequantisation), each with its weight in A_hat.
+    Returns (local part in f64, remote part in f64, their sum rounded to f32,
+    the mixed matrix the remote part read)."""
+    Hmix, _, _ = quantized_aggregate(g, H, rows, bits, seed, stream)
+    marginal = np.zeros(g.n, dtype=bool)
+    marginal[rows] = True
+    lg, rg, lw, rw = g.split_by_source(marginal)
+    yl = spmm(lg, _c(H, np.float32), lw)
+    yr = spmm(rg, Hmix, rw)
+    return yl, yr, to_f32(yl + yr), Hmix
+
+
 def quantized_aggregate(g, H, rows, bits, seed, stream=0):
     """bits: int (uniform) or int array per row (grouped into one call per width)."""
     H = _c(H, np.float32)

@@ -60,6 +60,24 @@ class OracleGraph:
             self._csc = (colptr, row, eid)
         return self._csc
 
+    # -- AdaQP Eqn. 7: local and remote in-neighbour sums ------------------
+    def split_by_source(self, marginal):
+        """(local, remote, w_local, w_remote): the in-edges of every row whose
+        source is not / is marginal, each in its CSR order, with the GCN weight
+        it has in this graph (the sub-graphs' own degrees play no part)."""
+        marginal = np.asarray(marginal, dtype=bool)
+        _, w = self.gcn_norm()
+        parts = []
+        for want in (False, True):
+            keep = marginal[self.col] == want
+            counts = np.bincount(self.dst[keep], minlength=self.n)
+            row_ptr = np.zeros(self.n + 1, dtype=np.int64)
+            row_ptr[1:] = np.cumsum(counts)
+            parts.append((OracleGraph(self.n, row_ptr, self.col[keep].astype(np.int32),
+                                      self.dst[keep].astype(np.int32)), w[keep]))
+        (lg, lw), (rg, rw) = parts
+        return lg, rg, lw, rw
+
     # -- degree ordering -----------------------------------------------------
     def degree_perm(self):
         """Rows by in-degree descending, ties by id ascending."""

@@ -161,6 +161,73 @@ gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const in
     return GNN_OK;
 }
 
+gnn_status_t gnn_graph_split(gnn_graph_t h, const uint8_t* marginal, gnn_graph_t* local, gnn_graph_t* remote) {
+    GNN_TRY(check_graph(h, "gnn_graph_split"));
+    GNN_REQUIRE(local && remote, "gnn_graph_split: local or remote is NULL");
+    *local = *remote = nullptr;
+    const Graph& g = h->g;
+    GNN_REQUIRE(g.n == 0 || marginal, "gnn_graph_split: marginal is NULL");
+    const size_t n = static_cast<size_t>(g.n), e = static_cast<size_t>(g.nnz);
+    gnn_graph* parts[2] = {nullptr, nullptr};
+    gnn_status_t s = GNN_OK;
+    try {
+        std::vector<int64_t> rp(n + 1, 0);
+        std::vector<int32_t> col(e);
+        std::vector<float> dinv(n), w(e);
+        if (n) GNN_HIP(hipMemcpy(rp.data(), g.row_ptr, (n + 1) * 8, hipMemcpyDeviceToHost));
+        if (e) {
+            GNN_HIP(hipMemcpy(col.data(), g.col, e * 4, hipMemcpyDeviceToHost));
+            GNN_HIP(hipMemcpy(w.data(), g.wgcn, e * 4, hipMemcpyDeviceToHost));
+        }
+        if (n) GNN_HIP(hipMemcpy(dinv.data(), g.dinv, n * 4, hipMemcpyDeviceToHost));
+        for (int k = 0; k < 2 && s == GNN_OK; ++k) {
+            // k = 0: in-edges from sources that are not marginal; k = 1: from marginal ones.
+            // Each row keeps its edges in CSR order and each edge its weight in g.
+            std::vector<int64_t> prp(n + 1, 0);
+            std::vector<int32_t> pcol;
+            std::vector<float> pw;
+            for (size_t v = 0; v < n; ++v) {
+                for (int64_t i = rp[v]; i < rp[v + 1]; ++i) {
+                    const bool m = marginal[col[i]] != 0;
+                    if (m == (k == 1)) {
+                        pcol.push_back(col[i]);
+                        pw.push_back(w[i]);
+                    }
+                }
+                prp[v + 1] = static_cast<int64_t>(pcol.size());
+            }
+            gnn_graph* ph = new (std::nothrow) gnn_graph();
+            if (!ph) {
+                s = fail(GNN_ERR_OUT_OF_MEMORY, "gnn_graph_split: host allocation failed");
+                break;
+            }
+            parts[k] = ph;
+            Graph& pg = ph->g;
+            pg.n = g.n;
+            pg.nnz = static_cast<int64_t>(pcol.size());
+            pg.has_csc = false;
+            s = upload(pg, prp, &pg.row_ptr);
+            if (s == GNN_OK) s = upload(pg, pcol, &pg.col);
+            if (s == GNN_OK) s = upload(pg, dinv, &pg.dinv);
+            if (s == GNN_OK) s = upload(pg, pw, &pg.wgcn);
+            if (s == GNN_OK) s = make_plan(pg, prp, pg.plan[0], nullptr);
+        }
+    } catch (const std::bad_alloc&) {
+        s = fail(GNN_ERR_OUT_OF_MEMORY, "gnn_graph_split: host allocation failed");
+    }
+    if (s != GNN_OK) {
+        for (gnn_graph* ph : parts)
+            if (ph) {
+                free_graph(ph->g);
+                delete ph;
+            }
+        return s;
+    }
+    *local = parts[0];
+    *remote = parts[1];
+    return GNN_OK;
+}
+
 gnn_status_t gnn_graph_destroy(gnn_graph_t h) {
     if (!h) return GNN_OK;
     free_graph(h->g);
@@ -374,8 +441,8 @@ size_t gnn_spmm_dequant_workspace_size(gnn_graph_t h, int64_t d) {
 }
 
 gnn_status_t gnn_spmm_dequant(gnn_graph_t h, const float* X, int64_t ldx, const int32_t* qslot,
-                              const gnn_qgroup_t* groups, int n_groups, float* Y, int64_t ldy, int64_t d, int relu,
-                              void* ws, size_t ws_bytes, void* stream) {
+                              const gnn_qgroup_t* groups, int n_groups, const float* Z, int64_t ldz, float* Y,
+                              int64_t ldy, int64_t d, int relu, void* ws, size_t ws_bytes, void* stream) {
     GNN_TRY(check_graph(h, "gnn_spmm_dequant"));
     const Graph& g = h->g;
     GNN_REQUIRE(d >= 4 && d % 4 == 0, "gnn_spmm_dequant: d must be a positive multiple of 4");
@@ -401,6 +468,10 @@ gnn_status_t gnn_spmm_dequant(gnn_graph_t h, const float* X, int64_t ldx, const 
     qs.groups = groups;
     qs.n_groups = n_groups;
     qs.records = static_cast<char*>(ws) + part;
+    GNN_REQUIRE(!Z || ldz >= d, "gnn_spmm_dequant: ldz must be >= d");
+    GNN_REQUIRE(!Z || Z != Y || ldz == ldy, "gnn_spmm_dequant: Z may alias Y only with ldz == ldy");
+    qs.addend = Z;
+    qs.ld_add = ldz;
     return launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, X, GNN_F32, ldx, Y, GNN_F32, ldy, d, relu,
                        Rank1Epilogue{}, static_cast<float*>(ws), static_cast<hipStream_t>(stream), MaskEpilogue{}, 0,
                        qs);

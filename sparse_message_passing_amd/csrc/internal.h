@@ -117,6 +117,8 @@ struct QuantSources {      // dequantise-in-gather: source rows with qslot[u] >=
     const gnn_qgroup_t* groups = nullptr;  // host array of n_groups descriptors
     int n_groups = 0;
     void* records = nullptr;               // device scratch of 16 bytes per node (quantised_source_record_bytes)
+    const float* addend = nullptr;         // Y = A X~ + addend (may alias Y), before the ReLU
+    int64_t ld_add = 0;
 };
 inline size_t quantised_source_record_bytes(int64_t n) { return static_cast<size_t>(n) * 16; }
 

@@ -93,6 +93,8 @@ struct SpmmArgs {
     QGroupDev qg[kMaxQGroups];
     int q_words;                    // every group's code rows are whole 4-byte words
     const uint4* qrec;              // per-node records (QRec), zero for rows of X
+    const float* addend;            // Y = (G . w) X + addend (may be Y itself), before the ReLU
+    int64_t ld_add;
 };
 
 // Dequantise-in-gather.  A per-node record, built once per call, holds for
@@ -308,6 +310,11 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
                 P[0] = acc[c][0];
             continue;
         }
+        if (a.addend) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                if (i < nv) acc[c][i] = acc[c][i] + a.addend[row * a.ld_add + f + i];
+        }
         if (a.r1.a) {
             const float ra = a.r1.a[row * heads + hd[c]];
             const float rb = a.r1.b[row * heads + hd[c]];
@@ -368,6 +375,7 @@ __global__ __launch_bounds__(256) void spmm_fixup(SpmmArgs a) {
     for (int64_t f = threadIdx.x; f < a.d; f += blockDim.x) {
         float s = 0.0f;
         for (int64_t c = c0; c < c1; ++c) s += a.partial[c * a.pd + f];
+        if (a.addend) s = s + a.addend[row * a.ld_add + f];
         if (a.r1.a) {
             const int64_t h = f / a.dh;
             s = s + (a.r1.a[row * a.heads + h] * a.r1.va[f] + a.r1.b[row * a.heads + h] * a.r1.vb[f]);
@@ -470,6 +478,8 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     a.w_hstride = wmode == GNN_W_EDGE ? w_head_stride : 0;
     a.qslot = qs.qslot;
     a.qrec = nullptr;
+    a.addend = qs.addend;
+    a.ld_add = qs.ld_add;
     a.q_words = 1;
     for (int i = 0; i < qs.n_groups; ++i)
         if ((d * qs.groups[i].bits / 8) % 4 || reinterpret_cast<uintptr_t>(qs.groups[i].packed) % 4) a.q_words = 0;

@@ -30,6 +30,7 @@ _SIGS = {
     "gnn_last_error": ("", "P"),
     "gnn_graph_create": ("IIPPUP", "i"),
     "gnn_graph_destroy": ("P", "i"),
+    "gnn_graph_split": ("PPPP", "i"),
     "gnn_graph_info": ("PP", "i"),
     "gnn_graph_export": ("PPPPPPPPPP", "i"),
     "gnn_spmm_workspace_size": ("PiI", "S"),
@@ -46,7 +47,7 @@ _SIGS = {
     "gnn_dequantize": ("PPPIIiPPIP", "i"),
     "gnn_quant_slots": ("IiPPPP", "i"),
     "gnn_spmm_dequant_workspace_size": ("PI", "S"),
-    "gnn_spmm_dequant": ("PPIPPiPIIiPSP", "i"),
+    "gnn_spmm_dequant": ("PPIPPiPIPIIiPSP", "i"),
     "gnn_gcn_workspace_size": ("PII", "S"),
     "gnn_gcn_layer_fwd": ("PPiIIPIiPiIPPSP", "i"),
     "gnn_gcn_layer_bwd": ("PPiIIPIiiPPiIPPPPSP", "i"),
@@ -165,6 +166,18 @@ def gnn_graph_create(n, src, dst, symmetrize=False, csc=False, device=None):
     return Graph(h, dev)
 
 
+def gnn_graph_split(g: Graph, marginal):
+    """(local, remote): the in-edges from non-marginal / marginal sources
+    (marginal: bool or uint8 array over the n nodes), weights kept from g."""
+    m = np.ascontiguousarray(np.asarray(marginal) != 0, dtype=np.uint8)
+    if m.size != g.n:
+        raise ValueError("marginal must have one entry per node")
+    torch.cuda.set_device(g.device)
+    lo, hi = C.c_void_p(), C.c_void_p()
+    _check(lib().gnn_graph_split(g.h, m.ctypes.data_as(C.c_void_p), C.byref(lo), C.byref(hi)))
+    return Graph(lo, g.device), Graph(hi, g.device)
+
+
 def gnn_graph_export(g: Graph):
     n, e = g.n, g.nnz
     out = dict(row_ptr=np.empty(n + 1, np.int64), col=np.empty(e, np.int32), dinv=np.empty(n, np.float32),
@@ -274,16 +287,17 @@ def gnn_quant_slots(n, rows_list, qslot):
     return qslot
 
 
-def gnn_spmm_dequant(g: Graph, X, qslot, groups, Y, relu=False, d=None, ws=None):
-    """Y = A_hat X~, X~ = X with the slotted rows dequantised in the gather.
+def gnn_spmm_dequant(g: Graph, X, qslot, groups, Y, relu=False, d=None, ws=None, Z=None):
+    """Y = A_hat X~ (+ Z), X~ = X with the slotted rows dequantised in the gather.
     groups: list of (packed, scale, zero, bits)."""
     d = X.shape[1] if d is None else d
     arr = (QGroup * max(len(groups), 1))(*[QGroup(_p(pk), _p(sc), _p(zr), sc.numel(), b)
                                            for pk, sc, zr, b in groups])
     if ws is None:
         ws = _ws(lib().gnn_spmm_dequant_workspace_size(g.h, d), X.device)
-    _check(lib().gnn_spmm_dequant(g.h, _p(X), _ld(X), _p(qslot), arr, len(groups), _p(Y), _ld(Y), d, int(relu),
-                                  _p(ws), ws.numel(), _stream()))
+    _check(lib().gnn_spmm_dequant(g.h, _p(X), _ld(X), _p(qslot), arr, len(groups), _p(Z),
+                                  _ld(Z) if Z is not None else 0, _p(Y), _ld(Y), d, int(relu), _p(ws), ws.numel(),
+                                  _stream()))
     return Y
 
 

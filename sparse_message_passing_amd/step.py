@@ -183,3 +183,133 @@ class QuantExchange:
         """dH = A_hat^T dY~, the marginal rows of dY exchanged quantised."""
         self.quantize(dY, self.stream_id + 1)
         return gnnmp.gnn_spmm_dequant(self.g, dY, self.qslot, self.qgroups, self.dH, ws=self.ws)
+
+
+class OverlapExchange:
+    """The exchange split as AdaQP does (Eqn. 7; Sec. 3, computation-
+    communication parallelisation and its three isolated stages, Fig. 7) on
+    one GPU: the aggregation over in-edges from central sources runs on the
+    binary32 rows at once, while the marginal rows are quantised, "sent" (a
+    device-to-device copy stands in for the transfer) and aggregated from
+    their codes over the in-edges from marginal sources, added to the central
+    part.  Three schedules of the same kernels, with bitwise the same result:
+
+    * sequential: everything on the caller's stream;
+    * free: central aggregation on one stream, quantise + transfer on
+      another, the marginal aggregation after both;
+    * staged (AdaQP Fig. 7): quantise alone, then the central aggregation
+      alongside the transfer, then the marginal aggregation.
+    """
+
+    def __init__(self, g: gnnmp.Graph, H, rows, bits, seed, stream_id=0):
+        self.g, self.H = g, H.contiguous()
+        dev = H.device
+        n, d = g.n, H.shape[1]
+        rows = np.asarray(rows, np.int32)
+        b = np.full(rows.size, bits, np.int32) if np.isscalar(bits) else np.asarray(bits, np.int32)
+        marginal = np.zeros(n, dtype=bool)
+        marginal[rows] = True
+        self.g_local, self.g_remote = gnnmp.gnn_graph_split(g, marginal)
+        self.send, self.recv = [], []
+        for bb in (2, 4, 8):
+            sel = rows[b == bb]
+            if sel.size == 0:
+                continue
+            mk = lambda: (torch.empty((sel.size, d * bb // 8), dtype=torch.uint8, device=dev),
+                          torch.empty(sel.size, device=dev), torch.empty(sel.size, device=dev))
+            self.send.append((bb, torch.from_numpy(sel).to(dev), *mk()))
+            self.recv.append((bb, *mk()))
+        self.seed, self.stream_id = seed, stream_id
+        self.qslot = torch.empty(n, dtype=torch.int32, device=dev)
+        gnnmp.gnn_quant_slots(n, [s[1] for s in self.send], self.qslot)
+        self.recv_groups = [(pk, sc, zr, bb) for bb, pk, sc, zr in self.recv]
+        self.Y = torch.empty_like(self.H)
+        self.ws_l = torch.empty(max(gnnmp.lib().gnn_spmm_workspace_size(self.g_local.h, 0, d), 1),
+                                dtype=torch.uint8, device=dev)
+        self.ws_r = torch.empty(max(gnnmp.lib().gnn_spmm_dequant_workspace_size(self.g_remote.h, d), 1),
+                                dtype=torch.uint8, device=dev)
+        self.s_central = torch.cuda.Stream(device=dev)
+        self.s_marginal = torch.cuda.Stream(device=dev)
+        self.marks = {}
+
+    # -- the four pieces ---------------------------------------------------
+    def quantize(self):
+        for bb, r, pk, sc, zr in self.send:
+            gnnmp.gnn_quantize(self.H, r, bb, self.seed, pk, sc, zr, stream_id=self.stream_id)
+
+    def transfer(self):
+        for (_, _, pk, sc, zr), (_, rpk, rsc, rzr) in zip(self.send, self.recv):
+            rpk.copy_(pk)
+            rsc.copy_(sc)
+            rzr.copy_(zr)
+
+    def central(self):
+        return gnnmp.gnn_spmm(self.g_local, self.H, self.Y, ws=self.ws_l)
+
+    def marginal(self):
+        return gnnmp.gnn_spmm_dequant(self.g_remote, self.H, self.qslot, self.recv_groups, self.Y, ws=self.ws_r,
+                                      Z=self.Y)
+
+    # -- schedules -----------------------------------------------------------
+    def _mark(self, name, stream):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        self.marks[name] = ev
+
+    def step_sequential(self):
+        cur = torch.cuda.current_stream()
+        self._mark("start", cur)
+        self.quantize()
+        self._mark("quantized", cur)
+        self.transfer()
+        self._mark("transferred", cur)
+        self.central()
+        self._mark("central", cur)
+        self.marginal()
+        self._mark("end", cur)
+        return self.Y
+
+    def step_free(self):
+        cur = torch.cuda.current_stream()
+        self._mark("start", cur)
+        self.s_central.wait_event(self.marks["start"])
+        self.s_marginal.wait_event(self.marks["start"])
+        with torch.cuda.stream(self.s_central):
+            self.central()
+            self._mark("central", self.s_central)
+        with torch.cuda.stream(self.s_marginal):
+            self.quantize()
+            self._mark("quantized", self.s_marginal)
+            self.transfer()
+            self._mark("transferred", self.s_marginal)
+            self.s_marginal.wait_event(self.marks["central"])
+            self.marginal()
+            self._mark("end", self.s_marginal)
+        cur.wait_event(self.marks["end"])
+        return self.Y
+
+    def step_staged(self):
+        cur = torch.cuda.current_stream()
+        self._mark("start", cur)
+        self.s_marginal.wait_event(self.marks["start"])
+        with torch.cuda.stream(self.s_marginal):          # stage 1: quantise alone
+            self.quantize()
+            self._mark("quantized", self.s_marginal)
+        self.s_central.wait_event(self.marks["quantized"])
+        with torch.cuda.stream(self.s_central):           # stage 2: central aggregation ...
+            self.central()
+            self._mark("central", self.s_central)
+        with torch.cuda.stream(self.s_marginal):          # ... alongside the transfer
+            self.transfer()
+            self._mark("transferred", self.s_marginal)
+            self.s_marginal.wait_event(self.marks["central"])
+            self.marginal()                               # stage 3: marginal aggregation
+            self._mark("end", self.s_marginal)
+        cur.wait_event(self.marks["end"])
+        return self.Y
+
+    def timeline(self):
+        """ms from the start mark to each recorded mark of the last step
+        (call after synchronising)."""
+        t0 = self.marks["start"]
+        return {k: round(t0.elapsed_time(ev), 4) for k, ev in self.marks.items() if k != "start"}

@@ -79,5 +79,5 @@ def test_status_strings_and_host_side_validation():
     assert L.gnn_quant_slots(4, 9, None, None, None, None) == 1
     assert L.gnn_quant_slots(-1, 0, None, None, None, None) == 1
     # dequantising aggregation: NULL graph; then d not a multiple of 4 is checked after the graph
-    st = L.gnn_spmm_dequant(None, None, 4, None, None, 0, None, 4, 4, 0, None, 0, None)
+    st = L.gnn_spmm_dequant(None, None, 4, None, None, 0, None, 0, None, 4, 4, 0, None, 0, None)
     assert st == 1 and b"NULL" in L.gnn_last_error()

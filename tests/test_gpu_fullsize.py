@@ -270,6 +270,24 @@ def test_c5_dequant_in_gather_forward_and_backward():
                 what="C5 backward gradient exchange")
 
 
+def test_c5_overlapped_exchange_schedules():
+    # the split exchange at full size: three schedules bitwise equal, the
+    # whole output against the oracle's local + remote sums
+    from sparse_message_passing_amd.step import OverlapExchange
+    inp = synth.config_inputs(5)
+    n = int(inp["n"])
+    g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
+    og = build_graph(inp["src"], inp["dst"], n, True)
+    H, rows, seed, bits = inp["H"], inp["rows"], int(inp["philox_seed"]), inp["mixed_bits"]
+    ex = OverlapExchange(g, to_dev(H), rows, bits, seed)
+    outs = [step().clone() for step in (ex.step_sequential, ex.step_free, ex.step_staged)]
+    assert all(torch.equal(outs[0].view(torch.int32), o.view(torch.int32)) for o in outs[1:])
+    yl, yr, ref, Hmix = oracle.split_aggregate(og, H, rows, bits, seed)
+    sr = sample_rows(og, 8192, 11)
+    mag = oracle.spmm_mag(og, Hmix, og.gcn_norm()[1])[sr]
+    check_close(from_dev(outs[0])[sr], ref[sr], mag, what="C5 overlapped exchange")
+
+
 # ---------------------------------------------------------------------------
 # bf16 storage at 2.45M nodes (heavy-tailed, max degree ~17K)
 # ---------------------------------------------------------------------------

@@ -500,3 +500,45 @@ def test_quantized_exchange_step_fused_and_backward():
     dH = fused.backward(to_dev(dY))
     dmix_ref, dH_ref, _ = oracle.quantized_aggregate(og, dY, rows, b, seed=77, stream=3)
     check_close(from_dev(dH), dH_ref, oracle.spmm_mag(og, dmix_ref, w), what="exchange backward")
+
+
+# ---------------------------------------------------------------------------
+# AdaQP Eqn. 7 split and the overlapped exchange
+# ---------------------------------------------------------------------------
+def test_graph_split_matches_oracle():
+    s, t = hub_edges(3000, 20000, 800, 21)
+    g, og = graph_pair(s, t, 3000, True, csc=False)
+    marginal = np.random.default_rng(22).random(3000) < 0.3
+    lo, hi = gnnmp.gnn_graph_split(g, marginal)
+    lg, rg, lw, rw = og.split_by_source(marginal)
+    for gg, ref, wref in ((lo, lg, lw), (hi, rg, rw)):
+        ex = gnnmp.gnn_graph_export(gg)
+        assert np.array_equal(ex["row_ptr"], ref.row_ptr) and np.array_equal(ex["col"], ref.col)
+        assert np.array_equal(ex["w"].view(np.uint32), wref.view(np.uint32))
+        assert np.array_equal(ex["perm"], ref.degree_perm())
+
+
+@pytest.mark.parametrize("bits", [4, "mixed"])
+def test_overlap_exchange_schedules(bits):
+    # the central/marginal split on two streams: the three schedules run the
+    # same kernels in the same order per element, so agree bitwise; the result
+    # is Eqn. 7's local sum plus remote sum
+    from sparse_message_passing_amd.step import OverlapExchange
+    s, t, n = rmat_graph(12, 24, True, 80)
+    g, og = graph_pair(s, t, n, True, csc=False)
+    r = np.random.default_rng(23)
+    H = r.standard_normal((n, 256)).astype(np.float32)
+    rows = synth.marginal_rows(n, 0.3, 24)
+    b = bits if bits != "mixed" else synth.random_bits(rows.size, (2, 4, 8), 25)
+    ex = OverlapExchange(g, to_dev(H), rows, b, 555)
+    outs = []
+    for step in (ex.step_sequential, ex.step_free, ex.step_staged):
+        ex.Y.fill_(float("nan"))
+        outs.append(step().clone())
+        torch.cuda.synchronize()
+        tl = ex.timeline()
+        assert tl["end"] >= max(tl["central"], tl["transferred"]) >= 0.0
+    assert all(torch.equal(outs[0].view(torch.int32), o.view(torch.int32)) for o in outs[1:])
+    yl, yr, ref, Hmix = oracle.split_aggregate(og, H, rows, b, 555)
+    check_close(from_dev(outs[0]), ref, oracle.spmm_mag(og, Hmix, og.gcn_norm()[1]) + 1e-30,
+                what=f"overlapped exchange b={bits}")

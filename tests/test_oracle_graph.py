@@ -143,3 +143,32 @@ def test_gcn_norm_dense_matches_definition():
     Ahat = Dm @ Abar @ Dm
     _, w = g.gcn_norm()
     assert np.allclose(g.dense(w), Ahat, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.3, 1.0])
+def test_split_by_source_partitions_the_edges(frac):
+    # AdaQP Eqn. 7: every in-edge is local or remote by its source, each keeps
+    # its weight in A_hat, and the two sums add up to the whole aggregation
+    r = np.random.default_rng(31)
+    n = 400
+    src, dst = r.integers(0, n, 3000), r.integers(0, n, 3000)
+    g = build_graph(src, dst, n, True)
+    marginal = r.random(n) < frac
+    lg, rg, lw, rw = g.split_by_source(marginal)
+    assert lg.nnz + rg.nnz == g.nnz
+    assert not marginal[lg.col].any() and marginal[rg.col].all()
+    # the parent's edges, regrouped: same (dst, src, weight) triples per row, order kept
+    _, w = g.gcn_norm()
+    for v in range(0, n, 7):
+        row = g.col[g.row_ptr[v]:g.row_ptr[v + 1]]
+        wv = w[g.row_ptr[v]:g.row_ptr[v + 1]]
+        m = marginal[row]
+        assert np.array_equal(lg.col[lg.row_ptr[v]:lg.row_ptr[v + 1]], row[~m])
+        assert np.array_equal(rg.col[rg.row_ptr[v]:rg.row_ptr[v + 1]], row[m])
+        assert np.array_equal(lw[lg.row_ptr[v]:lg.row_ptr[v + 1]], wv[~m])
+        assert np.array_equal(rw[rg.row_ptr[v]:rg.row_ptr[v + 1]], wv[m])
+    # linearity against the dense operator
+    X = r.standard_normal((n, 5))
+    A = g.dense(w).astype(np.float64)
+    Y = oracle.spmm(lg, X, lw) + oracle.spmm(rg, X, rw)
+    assert np.allclose(Y, A @ X, rtol=1e-12, atol=1e-12)
