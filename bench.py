@@ -235,6 +235,21 @@ def main():
         extra["fused_step_ms"] = round(fused_ms, 4)
         extra["fused_step_gedge_feat_s"] = round(metric_work / (fused_ms * 1e-3) / 1e9, 2)
         extra["backward_exchange_ms"] = round(bwd_ms, 4)
+        # adaptive bit-widths: statistics on the GPU, greedy assignment on the
+        # host, at the average width of the uniform {2, 4, 8} draw
+        from sparse_message_passing_amd.step import adaptive_bits
+        rows_d = T(inp["rows"].astype(np.int32))
+        beta_d = torch.empty(rows_d.numel(), device=dev)
+        rng_d = torch.empty_like(beta_d)
+        extra["quant_stats_ms"] = round(event_time(lambda: gnnmp.gnn_quant_stats(g, runner.H, rows_d, beta_d, rng_d),
+                                                   a.kernel_reps, stream), 4)
+        avg = float(inp["mixed_bits"].mean())
+        t0 = time.perf_counter()
+        bits_a, beta_h = adaptive_bits(g, runner.H, inp["rows"], avg)
+        extra["assign_total_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+        var = lambda b: float(np.sum(beta_h.astype(np.float64) / (2.0 ** b - 1.0) ** 2))
+        extra["variance_adaptive_over_uniform"] = round(var(bits_a) / var(inp["mixed_bits"]), 4)
+        extra["adaptive_bits_histogram"] = {int(b): int((bits_a == b).sum()) for b in (2, 4, 8)}
         # the exchange split by message origin (local / remote in-edges) under
         # three schedules of the same kernels, and the stage timeline of each
         with torch.cuda.stream(stream):

@@ -220,6 +220,29 @@ gnn_status_t gnn_quantize(const float* H, int64_t ldh, int64_t d, const int32_t*
 gnn_status_t gnn_dequantize(const uint8_t* packed, const float* scale, const float* zero, int64_t n_rows,
                             int64_t d, int bits, const int32_t* rows, float* H, int64_t ldh, void* stream);
 
+/* Bit-width statistics (AdaQP Sec. 3.2, the beta_k of Problem 11).  For each
+ * listed row r (node k = rows[r]) of H [n, ldh] f32:
+ *   range[r] = max(h_k) - min(h_k)   (binary32, the R gnn_quantize uses)
+ *   beta[r]  = (S2 * d) * range^2 / 6,  S2 = sum of alpha^2 over the edges
+ * from k to the nodes that aggregate it, alpha = edge_w[e] (f32 [nnz], CSR
+ * order) or the GCN weight when edge_w is NULL.  The edges from k are its
+ * out-edges (CSC view) when the graph has one, else its CSR row, which holds
+ * the same edges and weights on a symmetrised GCN graph.  The stochastic
+ * rounding variance a row adds is beta / (2^b - 1)^2.  beta, range: f32
+ * [n_rows] device; every operation binary32 with one rounding. */
+gnn_status_t gnn_quant_stats(gnn_graph_t g, const float* edge_w, const float* H, int64_t ldh, int64_t d,
+                             const int32_t* rows, int64_t n_rows, float* beta, float* range, void* stream);
+
+/* Greedy bit-width assignment, a stand-in for AdaQP's assignment MILP
+ * (Problem 12, solved there with a third-party solver): with candidate widths
+ * {2, 4, 8} and a byte budget of avg_bits * m * d / 8, minimise
+ * sum_k beta_k / (2^b_k - 1)^2.  Every row starts at 2 bits; upgrades
+ * (2 -> 4 costs d/4 bytes, 4 -> 8 costs d/2) are taken in decreasing order
+ * of variance removed per byte, ties by smaller row index, each only if it
+ * still fits; a row's 4 -> 8 is considered once its 2 -> 4 is taken.
+ * Host arrays: beta [m] (>= 0, finite), bits [m] out.  2 <= avg_bits <= 8. */
+gnn_status_t gnn_assign_bits(int64_t m, const float* beta, int64_t d, double avg_bits, int32_t* bits);
+
 /* Dequantise-in-gather aggregation.  AdaQP (Sec. 3, Eqn. 4, 5 and 7): the
  * marginal rows a partition receives arrive as per-row codes with their scale
  * and zero point, and are aggregated with the central rows; Tango's

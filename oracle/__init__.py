@@ -383,6 +383,51 @@ def gat_layer_bwd(g, fw, X, W, a_src, a_dst, dY, heads, slope, dt="f32"):
 # rows of H are quantised, dequantised into a copy of H (central rows stay
 # binary32) and the mixed matrix is aggregated with A_hat.
 # ---------------------------------------------------------------------------
+def quant_stats(g, H, rows, w=None):
+    """AdaQP Sec. 3.2, the beta_k of Problem 11, by definition: for node
+    k = rows[r], range = max(h_k) - min(h_k) (binary32 subtraction) and
+    beta = sum over k's out-edges of alpha^2, times D * range^2 / 6 (f64).
+    alpha: w (CSR order) or the GCN weights."""
+    H = _c(H, np.float32)
+    rows = np.asarray(rows, dtype=np.int64)
+    if w is None:
+        _, w = g.gcn_norm()
+    w = np.asarray(w, dtype=np.float64)
+    colptr, _, eid = g.csc()
+    rng = (H[rows].max(axis=1) - H[rows].min(axis=1)).astype(np.float32)
+    s2 = np.array([np.sum(w[eid[colptr[k]:colptr[k + 1]]] ** 2) for k in rows], dtype=np.float64)
+    beta = s2 * H.shape[1] * rng.astype(np.float64) ** 2 / 6.0
+    return beta, rng
+
+
+def quant_variance(beta, bits):
+    """Total stochastic-rounding variance sum_k beta_k / (2^b_k - 1)^2."""
+    b = np.asarray(bits, dtype=np.float64)
+    return float(np.sum(np.asarray(beta, dtype=np.float64) / (2.0 ** b - 1.0) ** 2))
+
+
+def assign_bits_greedy(beta, d, avg_bits):
+    """The greedy stand-in for AdaQP's assignment problem, as a sorted sweep:
+    every upgrade (2 -> 4 of each row: one budget unit of d/4 bytes; 4 -> 8:
+    two units) is visited in decreasing order of variance removed per unit,
+    ties by row index; an upgrade is taken when it fits in what is left and,
+    for 4 -> 8, when the row already has 4 bits."""
+    beta = np.asarray(beta, dtype=np.float64)
+    m = beta.size
+    units = int(np.floor((avg_bits - 2.0) * m * d / 8.0 / (d / 4.0) + 1e-9))
+    per_unit = [(1 / 9 - 1 / 225) / 1.0, (1 / 225 - 1 / 65025) / 2.0]
+    cands = [(-beta[k] * per_unit[st], k, st) for st in (0, 1) for k in range(m)]
+    cands.sort()
+    bits = np.full(m, 2, dtype=np.int32)
+    for _, k, st in cands:
+        cost = 1 if st == 0 else 2
+        if cost > units or (st == 1 and bits[k] != 4):
+            continue
+        units -= cost
+        bits[k] = 4 if st == 0 else 8
+    return bits
+
+
 def split_aggregate(g, H, rows, bits, seed, stream=0):
     """AdaQP Eqn. 7: the aggregation as the sum over local in-neighbours (rows
     of H as they are) plus the sum over remote ones (the marginal rows after

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "internal.h"
 
@@ -419,6 +420,61 @@ gnn_status_t gnn_dequantize(const uint8_t* packed, const float* scale, const flo
     GNN_REQUIRE(n_rows >= 0, "gnn_dequantize: n_rows must be >= 0");
     GNN_REQUIRE(n_rows == 0 || (H && rows && packed && scale && zero), "gnn_dequantize: NULL pointer");
     return launch_dequantize(packed, scale, zero, n_rows, d, bits, rows, H, ldh, static_cast<hipStream_t>(stream));
+}
+
+gnn_status_t gnn_quant_stats(gnn_graph_t h, const float* edge_w, const float* H, int64_t ldh, int64_t d,
+                             const int32_t* rows, int64_t n_rows, float* beta, float* range, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_quant_stats"));
+    const Graph& g = h->g;
+    GNN_REQUIRE(d >= 1 && ldh >= d, "gnn_quant_stats: need d >= 1 and ldh >= d");
+    GNN_REQUIRE(n_rows >= 0, "gnn_quant_stats: n_rows must be >= 0");
+    GNN_REQUIRE(n_rows == 0 || (H && rows && beta && range), "gnn_quant_stats: NULL pointer");
+    const float* w = edge_w ? edge_w : g.wgcn;
+    if (g.has_csc) return launch_quant_stats(csc_view(g), w, H, ldh, d, rows, n_rows, beta, range,
+                                             static_cast<hipStream_t>(stream));
+    return launch_quant_stats(csr_view(g), w, H, ldh, d, rows, n_rows, beta, range, static_cast<hipStream_t>(stream));
+}
+
+gnn_status_t gnn_assign_bits(int64_t m, const float* beta, int64_t d, double avg_bits, int32_t* bits) {
+    GNN_REQUIRE(m >= 0 && d >= 1, "gnn_assign_bits: need m >= 0 and d >= 1");
+    GNN_REQUIRE(m == 0 || (beta && bits), "gnn_assign_bits: NULL pointer");
+    GNN_REQUIRE(avg_bits >= 2.0 && avg_bits <= 8.0, "gnn_assign_bits: avg_bits must be in [2, 8]");
+    for (int64_t k = 0; k < m; ++k)
+        GNN_REQUIRE(std::isfinite(beta[k]) && beta[k] >= 0.0f, "gnn_assign_bits: beta must be finite and >= 0");
+    // budget in quarter-row units: a 2 -> 4 upgrade costs one (d/4 bytes), 4 -> 8 costs two
+    const double extra_bytes = (avg_bits - 2.0) * static_cast<double>(m) * static_cast<double>(d) / 8.0;
+    int64_t units = static_cast<int64_t>(std::floor(extra_bytes / (static_cast<double>(d) / 4.0) + 1e-9));
+    // variance removed per quarter-row unit: beta (1/9 - 1/225) for 2 -> 4, beta (1/225 - 1/65025) / 2 for 4 -> 8
+    const double g24 = 1.0 / 9.0 - 1.0 / 225.0, g48 = (1.0 / 225.0 - 1.0 / 65025.0) / 2.0;
+    struct Cand {
+        double gain;
+        int64_t k;
+        int stage;  // 0: 2 -> 4, 1: 4 -> 8
+    };
+    auto worse = [](const Cand& a, const Cand& b) { return a.gain < b.gain || (a.gain == b.gain && a.k > b.k); };
+    std::vector<Cand> heap;
+    heap.reserve(static_cast<size_t>(m));
+    for (int64_t k = 0; k < m; ++k) {
+        bits[k] = 2;
+        heap.push_back(Cand{static_cast<double>(beta[k]) * g24, k, 0});
+    }
+    std::make_heap(heap.begin(), heap.end(), worse);
+    while (!heap.empty() && units > 0) {
+        std::pop_heap(heap.begin(), heap.end(), worse);
+        const Cand c = heap.back();
+        heap.pop_back();
+        const int64_t cost = c.stage == 0 ? 1 : 2;
+        if (cost > units) continue;
+        units -= cost;
+        if (c.stage == 0) {
+            bits[c.k] = 4;
+            heap.push_back(Cand{static_cast<double>(beta[c.k]) * g48, c.k, 1});
+            std::push_heap(heap.begin(), heap.end(), worse);
+        } else {
+            bits[c.k] = 8;
+        }
+    }
+    return GNN_OK;
 }
 
 gnn_status_t gnn_quant_slots(int64_t n, int n_groups, const int32_t* const* rows, const int64_t* counts,

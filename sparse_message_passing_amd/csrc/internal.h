@@ -127,6 +127,8 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
                          const MaskEpilogue& mask = MaskEpilogue{}, int64_t w_head_stride = 0,
                          const QuantSources& qs = QuantSources{});
+gnn_status_t launch_quant_stats(const AggView& v, const float* w, const float* H, int64_t ldh, int64_t d,
+                                const int32_t* rows, int64_t n_rows, float* beta, float* range, hipStream_t st);
 gnn_status_t launch_quant_slots(int64_t n, int n_groups, const int32_t* const* rows, const int64_t* counts,
                                 int32_t* qslot, hipStream_t st);
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d);

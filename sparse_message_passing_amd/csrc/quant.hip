@@ -176,6 +176,45 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* packed, 
     }
 }
 
+// Bit-width statistics of AdaQP Sec. 3.2 (the beta_k of Problem 11): for
+// listed row r (node k = rows[r]) the range R = max(h_k) - min(h_k) and
+//   beta = (sum over k's edges of alpha^2) * D * R^2 / 6,
+// alpha the edge's GCN weight.  One wave per row: the row's features for
+// the range (minimum and maximum as the quantiser takes them, so R is the
+// quantiser's R bit for bit), then the squared weights of the node's edges.
+__global__ __launch_bounds__(256) void quant_stats_kernel(const float* H, int64_t ldh, int64_t d,
+                                                          const int32_t* rows, int64_t n_rows, const int64_t* ptr,
+                                                          const int32_t* eid, const float* w, float* beta,
+                                                          float* range) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const int64_t k = rows[r];
+    const float* h = H + k * ldh;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int64_t f = lane; f < d; f += 64) {
+        const float x = h[f];
+        mn = min_z(mn, x);
+        mx = max_z(mx, x);
+    }
+    float s2 = 0.0f;
+    for (int64_t e = ptr[k] + lane; e < ptr[k + 1]; e += 64) {
+        const float a = w[eid ? static_cast<int64_t>(eid[e]) : e];
+        s2 = __fmaf_rn(a, a, s2);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = min_z(mn, __shfl_xor(mn, o, 64));
+        mx = max_z(mx, __shfl_xor(mx, o, 64));
+        s2 = __fadd_rn(s2, __shfl_xor(s2, o, 64));
+    }
+    if (lane == 0) {
+        const float R = __fsub_rn(mx, mn);
+        range[r] = R;
+        beta[r] = __fdiv_rn(__fmul_rn(__fmul_rn(s2, static_cast<float>(d)), __fmul_rn(R, R)), 6.0f);
+    }
+}
+
 __global__ __launch_bounds__(256) void slots_fill_kernel(int64_t n, int32_t* qslot) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i < n) qslot[i] = -1;
@@ -188,6 +227,14 @@ __global__ __launch_bounds__(256) void slots_scatter_kernel(const int32_t* rows,
 }
 
 }  // namespace
+
+gnn_status_t launch_quant_stats(const AggView& v, const float* w, const float* H, int64_t ldh, int64_t d,
+                                const int32_t* rows, int64_t n_rows, float* beta, float* range, hipStream_t st) {
+    if (n_rows == 0) return GNN_OK;
+    hipLaunchKernelGGL(quant_stats_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, st, H, ldh, d, rows, n_rows, v.ptr,
+                       v.eid, w, beta, range);
+    return launch_status("gnn_quant_stats");
+}
 
 // Slot map of the dequantise-in-gather aggregation: -1 everywhere, then
 // (group << 27) | r at rows_g[r].  Groups are scattered one launch after the

@@ -24,7 +24,8 @@ GNN_GRAPH_SYMMETRIZE, GNN_GRAPH_CSC = 0x1, 0x2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "out of memory", 4: "HIP error",
           5: "graph lacks the required view", 6: "workspace too small"}
 
-# exported symbols and their argument types (P = pointer, I = int64, i = int32, U = uint32, Q = uint64, F = float, S = size_t)
+# exported symbols and their argument types (P = pointer, I = int64, i = int32, U = uint32, Q = uint64, F = float,
+# D = double, S = size_t)
 _SIGS = {
     "gnn_status_string": ("i", "P"),
     "gnn_last_error": ("", "P"),
@@ -46,6 +47,8 @@ _SIGS = {
     "gnn_quantize": ("PIIPIiQUPPPP", "i"),
     "gnn_dequantize": ("PPPIIiPPIP", "i"),
     "gnn_quant_slots": ("IiPPPP", "i"),
+    "gnn_quant_stats": ("PPPIIPIPPP", "i"),
+    "gnn_assign_bits": ("IPIDP", "i"),
     "gnn_spmm_dequant_workspace_size": ("PI", "S"),
     "gnn_spmm_dequant": ("PPIPPiPIPIIiPSP", "i"),
     "gnn_gcn_workspace_size": ("PII", "S"),
@@ -57,7 +60,7 @@ _SIGS = {
     "gnn_gat_layer_bwd": ("PPIPPPiIFPPPPPPPSP", "i"),
 }
 _CT = {"P": C.c_void_p, "I": C.c_int64, "i": C.c_int, "U": C.c_uint32, "Q": C.c_uint64, "F": C.c_float,
-       "S": C.c_size_t}
+       "D": C.c_double, "S": C.c_size_t}
 
 EXPORTED = tuple(_SIGS)
 
@@ -270,6 +273,23 @@ def gnn_dequantize(packed, scale, zero, rows, bits, H, d=None):
     _check(lib().gnn_dequantize(_p(packed), _p(scale), _p(zero), rows.numel(), d, bits, _p(rows), _p(H), _ld(H),
                                 _stream()))
     return H
+
+
+def gnn_quant_stats(g: Graph, H, rows, beta, rng, edge_w=None, d=None):
+    """beta[r], range[r] of the listed rows (AdaQP's bit-width statistics)."""
+    d = H.shape[1] if d is None else d
+    _check(lib().gnn_quant_stats(g.h, _p(edge_w), _p(H), _ld(H), d, _p(rows), rows.numel(), _p(beta), _p(rng),
+                                 _stream()))
+    return beta, rng
+
+
+def gnn_assign_bits(beta, d, avg_bits):
+    """Greedy {2, 4, 8} assignment under an average-bits budget (host arrays)."""
+    b = np.ascontiguousarray(np.asarray(beta, dtype=np.float32))
+    out = np.empty(b.size, dtype=np.int32)
+    _check(lib().gnn_assign_bits(b.size, b.ctypes.data_as(C.c_void_p), int(d), float(avg_bits),
+                                 out.ctypes.data_as(C.c_void_p)))
+    return out
 
 
 class QGroup(C.Structure):

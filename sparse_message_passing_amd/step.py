@@ -313,3 +313,15 @@ class OverlapExchange:
         (call after synchronising)."""
         t0 = self.marks["start"]
         return {k: round(t0.elapsed_time(ev), 4) for k, ev in self.marks.items() if k != "start"}
+
+
+def adaptive_bits(g: gnnmp.Graph, H, rows, avg_bits, edge_w=None):
+    """AdaQP's adaptive bit-width assignment with the greedy stand-in for its
+    solver: per-row statistics on the GPU (gnn_quant_stats), then the
+    assignment on the host (gnn_assign_bits).  Returns (bits, beta) as numpy."""
+    rows_d = torch.from_numpy(np.asarray(rows, np.int32)).to(H.device)
+    beta = torch.empty(rows_d.numel(), device=H.device)
+    rng = torch.empty_like(beta)
+    gnnmp.gnn_quant_stats(g, H, rows_d, beta, rng, edge_w=edge_w)
+    b = beta.cpu().numpy()
+    return gnnmp.gnn_assign_bits(b, H.shape[1], avg_bits), b

@@ -288,6 +288,21 @@ def test_c5_overlapped_exchange_schedules():
     check_close(from_dev(outs[0])[sr], ref[sr], mag, what="C5 overlapped exchange")
 
 
+def test_c5_bit_width_statistics():
+    # per-row range (bit-exact) and beta of every marginal row at full size
+    inp = synth.config_inputs(5)
+    n = int(inp["n"])
+    g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
+    og = build_graph(inp["src"], inp["dst"], n, True)
+    H, rows = inp["H"], inp["rows"]
+    beta = torch.empty(rows.size, device="cuda")
+    rng = torch.empty(rows.size, device="cuda")
+    gnnmp.gnn_quant_stats(g, to_dev(H), to_dev(rows.astype(np.int32)), beta, rng)
+    beta_ref, rng_ref = oracle.quant_stats(og, H, rows)
+    assert np.array_equal(from_dev(rng).view(np.uint32), rng_ref.view(np.uint32))
+    np.testing.assert_allclose(from_dev(beta), beta_ref, rtol=2e-6, atol=0)
+
+
 # ---------------------------------------------------------------------------
 # bf16 storage at 2.45M nodes (heavy-tailed, max degree ~17K)
 # ---------------------------------------------------------------------------

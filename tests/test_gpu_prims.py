@@ -542,3 +542,44 @@ def test_overlap_exchange_schedules(bits):
     yl, yr, ref, Hmix = oracle.split_aggregate(og, H, rows, b, 555)
     check_close(from_dev(outs[0]), ref, oracle.spmm_mag(og, Hmix, og.gcn_norm()[1]) + 1e-30,
                 what=f"overlapped exchange b={bits}")
+
+
+# ---------------------------------------------------------------------------
+# bit-width statistics (AdaQP Sec. 3.2) and the adaptive assignment
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("directed", [False, True])
+def test_quant_stats_matches_oracle(directed):
+    s, t = hub_edges(5000, 30000, 1500, 26)
+    g, og = graph_pair(s, t, 5000, not directed, csc=directed)
+    r = np.random.default_rng(27)
+    H = (r.standard_normal((5000, 96)) * r.uniform(0.1, 4, (5000, 1))).astype(np.float32)
+    rows = synth.marginal_rows(5000, 0.3, 28)
+    rows = np.concatenate([rows, [0]]).astype(np.int32)   # the hub (node 0 has hub_in in-edges)
+    H[rows[3]] = -2.5                                      # a constant row: range 0, beta 0
+    w = None if not directed else r.random(og.nnz).astype(np.float32)
+    beta_ref, rng_ref = oracle.quant_stats(og, H, rows, w)
+    beta = torch.empty(rows.size, device="cuda")
+    rngd = torch.empty(rows.size, device="cuda")
+    gnnmp.gnn_quant_stats(g, to_dev(H), to_dev(rows), beta, rngd, edge_w=None if w is None else to_dev(w))
+    assert np.array_equal(from_dev(rngd).view(np.uint32), rng_ref.view(np.uint32))
+    np.testing.assert_allclose(from_dev(beta), beta_ref, rtol=2e-6, atol=0)
+
+
+def test_adaptive_assignment_lowers_variance():
+    # statistics on the GPU, greedy assignment on the host, at the average
+    # width of uniform sampling from {2, 4, 8}: lower variance than the
+    # uniform draw (AdaQP Table 6's comparison, in variance terms)
+    from sparse_message_passing_amd.step import adaptive_bits
+    s, t, n = rmat_graph(12, 24, True, 81)
+    g, og = graph_pair(s, t, n, True, csc=False)
+    r = np.random.default_rng(29)
+    H = (r.standard_normal((n, 128)) * r.lognormal(0, 1, (n, 1))).astype(np.float32)
+    rows = synth.marginal_rows(n, 0.3, 30)
+    uniform = synth.random_bits(rows.size, (2, 4, 8), 31)
+    avg = float(uniform.mean())
+    bits, beta = adaptive_bits(g, to_dev(H), rows, avg)
+    beta_ref, _ = oracle.quant_stats(og, H, rows)
+    np.testing.assert_allclose(beta, beta_ref, rtol=2e-6)
+    assert np.array_equal(bits, oracle.assign_bits_greedy(beta.astype(np.float64), 128, avg))
+    assert bits.sum() <= uniform.sum()                          # no more bytes than the uniform draw
+    assert oracle.quant_variance(beta, bits) < oracle.quant_variance(beta, uniform)

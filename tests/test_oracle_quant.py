@@ -137,3 +137,73 @@ def test_signed_zero_extremes():
                                  np.array([0, 1, 2], np.int32), 8, seed=1)
     assert np.signbit(zr[0]) and np.signbit(zr[1]) and sc[0] == 0 and sc[1] == 0
     assert zr[2] == 0.0 and np.signbit(zr[2])
+
+
+# ---------------------------------------------------------------------------
+# bit-width statistics and the greedy assignment (AdaQP Sec. 3.2, Problem 11)
+# ---------------------------------------------------------------------------
+def test_quant_stats_closed_form_on_a_star():
+    # star: hub 0 joined to 1..4, symmetrised with self-loops; the hub's row
+    # degree is 5, a leaf's 2.  The hub's out-edges carry 1/sqrt(5*2) to each
+    # leaf and 1/5 to itself: S2 = 4/10 + 1/25.  A leaf's carry 1/sqrt(10) to
+    # the hub and 1/2 to itself: S2 = 1/10 + 1/4.
+    from oracle.graph import build_graph
+    g = build_graph(np.zeros(4, np.int64), np.arange(1, 5), 5, True)
+    H = np.array([[0, 1, 3, -1], [2, 2, 2, 2], [0, 0, 0, 4], [1, 2, 3, 4], [5, -5, 0, 0]], np.float32)
+    beta, rng = oracle.quant_stats(g, H, np.array([0, 1, 2]))
+    assert np.array_equal(rng, np.array([4, 0, 4], np.float32))
+    assert np.allclose(beta, [(0.4 + 0.04) * 4 * 16 / 6, 0.0, (0.1 + 0.25) * 4 * 16 / 6], rtol=1e-6)
+
+
+def test_quant_variance_matches_measured_error():
+    # beta / (2^b - 1)^2 with unit weights (S2 = 1) is D R^2 / (6 (2^b-1)^2),
+    # the squared error stochastic rounding leaves in a row whose values are
+    # spread evenly: compare with the oracle quantiser's measured error
+    K, d = 200, 512
+    r = np.random.default_rng(8)
+    H = (r.uniform(-1, 1, (K, d)) * r.uniform(0.1, 3, (K, 1))).astype(np.float32)
+    rows = np.arange(K, dtype=np.int32)
+    rng = (H.max(1) - H.min(1)).astype(np.float64)
+    beta = d * rng ** 2 / 6
+    for b in (2, 4, 8):
+        pk, sc, zr = oracle.quantize(H, rows, b, seed=9)
+        out = np.zeros_like(H)
+        oracle.dequantize(pk, sc, zr, rows, d, b, out)
+        err = float(((out.astype(np.float64) - H) ** 2).sum())
+        assert abs(err / oracle.quant_variance(beta, np.full(K, b)) - 1.0) < 0.03, b
+
+
+def test_greedy_worked_example():
+    # d = 4, budget avg 4 bits over 3 rows = 3 units of d/4 bytes:
+    # upgrades by variance removed per unit: row 0 2->4 (9*0.1067), row 1
+    # 2->4 (0.1067), row 0 4->8 (0.0199, needs 2 units: no longer fits), row 2
+    # 2->4 (0, fits)
+    assert list(oracle.assign_bits_greedy([9.0, 1.0, 0.0], 4, 4.0)) == [4, 4, 4]
+    assert list(oracle.assign_bits_greedy([9.0, 1.0, 0.0], 4, 2.0)) == [2, 2, 2]
+    assert list(oracle.assign_bits_greedy([9.0, 1.0, 0.0], 4, 8.0)) == [8, 8, 8]
+    # 3 units over two rows: row 1's 2->4 (0.107 per unit) beats row 0's 4->8
+    # (0.020 per unit), which then no longer fits; with beta 1000 it is the
+    # other way round (2.21 per unit)
+    assert list(oracle.assign_bits_greedy([9.0, 1.0], 4, 5.0)) == [4, 4]
+    assert list(oracle.assign_bits_greedy([1000.0, 1.0], 4, 5.0)) == [8, 2]
+
+
+def test_greedy_against_brute_force():
+    # on tiny instances: within budget, monotone in the budget, and never worse
+    # than the best assignment that leaves out one 4->8 upgrade's worth
+    import itertools
+    r = np.random.default_rng(5)
+    cost = {2: 0, 4: 1, 8: 3}
+    for _ in range(300):
+        m = int(r.integers(1, 6))
+        d = 8
+        beta = r.exponential(1.0, m) * (r.random(m) < 0.9)
+        avg = 2 + 6 * r.random()
+        units = int(np.floor((avg - 2) * m / 2 + 1e-9))
+        b = oracle.assign_bits_greedy(beta, d, avg)
+        assert sum(cost[int(x)] for x in b) <= units
+        more = oracle.assign_bits_greedy(beta, d, min(8.0, avg + 2.0 / m))
+        assert oracle.quant_variance(beta, more) <= oracle.quant_variance(beta, b) + 1e-15
+        best = min(oracle.quant_variance(beta, c) for c in itertools.product((2, 4, 8), repeat=m)
+                   if sum(cost[x] for x in c) <= max(units - 2, 0))
+        assert oracle.quant_variance(beta, b) <= best * (1 + 1e-12) + 1e-15
