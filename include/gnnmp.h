@@ -55,7 +55,10 @@ typedef enum { GNN_F32 = 0, GNN_BF16 = 1 } gnn_dtype_t;
 typedef enum {
     GNN_W_GCN = 0,   /* A_hat entries dinv[u]*dinv[v] (Sancus Sec. 2), heads must be 1 */
     GNN_W_ONES = 1,  /* every weight 1 (Tango's "ones" SpMM)                          */
-    GNN_W_EDGE = 2   /* caller's edge_w[nnz, heads] in CSR order (GAT attention)       */
+    GNN_W_EDGE = 2,  /* caller's edge_w[nnz, heads] in CSR order (GAT attention)       */
+    GNN_W_MEAN = 3   /* 1 / (row length) of the destination: the mean over {v} u N(v)
+                        (GraphSAGE's mean aggregator in AdaQP's weighted-sum form,
+                        Eqn. 1); heads must be 1                                      */
 } gnn_weights_t;
 
 typedef struct gnn_graph* gnn_graph_t;

@@ -47,6 +47,13 @@ class OracleGraph:
             self._norm = (dinv, w)
         return self._norm
 
+    # -- mean aggregation (GraphSAGE in AdaQP's weighted-sum form, Eqn. 1) ---
+    def mean_weights(self):
+        """w[e] = 1 / (row length of the edge's destination), binary32: the
+        aggregation of v is the mean over {v} u N(v)."""
+        inv = (np.float32(1.0) / self.deg.astype(np.float32)).astype(np.float32)
+        return inv[self.dst]
+
     # -- transposed view -----------------------------------------------------
     def csc(self):
         """(colptr int64[n+1], row int32[nnz], eid int32[nnz]): column u lists the

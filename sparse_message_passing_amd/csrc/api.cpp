@@ -35,8 +35,10 @@ gnn_status_t launch_status(const char* what) {
     return GNN_OK;
 }
 
-AggView csr_view(const Graph& g) { return AggView{g.n, g.row_ptr, g.col, nullptr, &g.plan[0], g.wgcn}; }
-AggView csc_view(const Graph& g) { return AggView{g.n, g.col_ptr, g.csc_row, g.csc_eid, &g.plan[1], nullptr}; }
+AggView csr_view(const Graph& g) { return AggView{g.n, g.row_ptr, g.col, nullptr, &g.plan[0], g.wgcn, g.dmean}; }
+AggView csc_view(const Graph& g) {
+    return AggView{g.n, g.col_ptr, g.csc_row, g.csc_eid, &g.plan[1], nullptr, g.dmean};
+}
 
 namespace {
 
@@ -142,6 +144,12 @@ gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const in
                     for (int64_t e = hg.row_ptr[v]; e < hg.row_ptr[v + 1]; ++e) w[e] = hg.dinv[hg.col[e]] * hg.dinv[v];
                 s = upload(g, w, &g.wgcn);
             }
+            if (s == GNN_OK) {
+                std::vector<float> dm(static_cast<size_t>(n));
+                for (int64_t v = 0; v < n; ++v)
+                    dm[v] = 1.0f / static_cast<float>(hg.row_ptr[v + 1] - hg.row_ptr[v]);
+                s = upload(g, dm, &g.dmean);
+            }
             if (s == GNN_OK) s = make_plan(g, hg.row_ptr, g.plan[0], nullptr);
             if (s == GNN_OK && g.has_csc) {
                 s = upload(g, hg.col_ptr, &g.col_ptr);
@@ -174,13 +182,14 @@ gnn_status_t gnn_graph_split(gnn_graph_t h, const uint8_t* marginal, gnn_graph_t
     try {
         std::vector<int64_t> rp(n + 1, 0);
         std::vector<int32_t> col(e);
-        std::vector<float> dinv(n), w(e);
+        std::vector<float> dinv(n), dmean(n), w(e);
         if (n) GNN_HIP(hipMemcpy(rp.data(), g.row_ptr, (n + 1) * 8, hipMemcpyDeviceToHost));
         if (e) {
             GNN_HIP(hipMemcpy(col.data(), g.col, e * 4, hipMemcpyDeviceToHost));
             GNN_HIP(hipMemcpy(w.data(), g.wgcn, e * 4, hipMemcpyDeviceToHost));
         }
         if (n) GNN_HIP(hipMemcpy(dinv.data(), g.dinv, n * 4, hipMemcpyDeviceToHost));
+        if (n) GNN_HIP(hipMemcpy(dmean.data(), g.dmean, n * 4, hipMemcpyDeviceToHost));
         for (int k = 0; k < 2 && s == GNN_OK; ++k) {
             // k = 0: in-edges from sources that are not marginal; k = 1: from marginal ones.
             // Each row keeps its edges in CSR order and each edge its weight in g.
@@ -211,6 +220,7 @@ gnn_status_t gnn_graph_split(gnn_graph_t h, const uint8_t* marginal, gnn_graph_t
             if (s == GNN_OK) s = upload(pg, pcol, &pg.col);
             if (s == GNN_OK) s = upload(pg, dinv, &pg.dinv);
             if (s == GNN_OK) s = upload(pg, pw, &pg.wgcn);
+            if (s == GNN_OK) s = upload(pg, dmean, &pg.dmean);
             if (s == GNN_OK) s = make_plan(pg, prp, pg.plan[0], nullptr);
         }
     } catch (const std::bad_alloc&) {
@@ -304,8 +314,10 @@ gnn_status_t gnn_spmm(gnn_graph_t h, int transpose, gnn_weights_t wmode, const f
     GNN_REQUIRE(ldx >= d && ldy >= d, "gnn_spmm: leading dimensions must be >= d");
     GNN_REQUIRE(heads >= 1 && d % heads == 0, "gnn_spmm: heads must divide d");
     GNN_REQUIRE(!bad_dt(x_dt) && !bad_dt(y_dt), "gnn_spmm: unknown dtype");
-    GNN_REQUIRE(wmode == GNN_W_GCN || wmode == GNN_W_ONES || wmode == GNN_W_EDGE, "gnn_spmm: unknown weight mode");
-    GNN_REQUIRE(wmode != GNN_W_GCN || heads == 1, "gnn_spmm: GCN weights need heads == 1");
+    GNN_REQUIRE(wmode == GNN_W_GCN || wmode == GNN_W_ONES || wmode == GNN_W_EDGE || wmode == GNN_W_MEAN,
+                "gnn_spmm: unknown weight mode");
+    GNN_REQUIRE((wmode != GNN_W_GCN && wmode != GNN_W_MEAN) || heads == 1,
+                "gnn_spmm: GCN and mean weights need heads == 1");
     GNN_REQUIRE(wmode != GNN_W_EDGE || edge_w, "gnn_spmm: edge_w is NULL");
     GNN_REQUIRE(relu == 0 || relu == 1, "gnn_spmm: relu must be 0 or 1");
     GNN_REQUIRE(g.n == 0 || (X && Y), "gnn_spmm: X or Y is NULL");

@@ -64,6 +64,7 @@ struct Graph {
     int32_t* col = nullptr;       // [nnz]
     float* dinv = nullptr;        // [n]
     float* wgcn = nullptr;        // [nnz] dinv[src] * dinv[dst] in CSR order
+    float* dmean = nullptr;       // [n] 1 / row length (binary32 division), the mean-aggregation weight
     int64_t* col_ptr = nullptr;   // [n+1]
     int32_t* csc_row = nullptr;   // [nnz]
     int32_t* csc_eid = nullptr;   // [nnz]
@@ -94,6 +95,7 @@ struct AggView {          // what an aggregation walks
     const int32_t* eid;   // CSR slot of each entry (CSC only) or nullptr
     const RowPlan* plan;
     const float* wgcn;    // GCN weight per edge in this view's order (CSR only) or nullptr
+    const float* dmean;   // [n] 1 / CSR row length: the mean weight of every in-edge of a row
 };
 
 AggView csr_view(const Graph& g);

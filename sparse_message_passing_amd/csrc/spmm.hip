@@ -88,6 +88,7 @@ struct SpmmArgs {
     MaskEpilogue mask;   // Y *= [M > 0]
     float* partial;
     const float* wgcn;   // GCN edge weights in this view's edge order (NULL: dinv[u]*dinv[v] on the fly)
+    const float* dmean;  // [n] 1 / CSR row length (mean weights)
     int64_t w_hstride;   // > 0: edge weights head-major in this view's order, weight(e, k) = edge_w[k*w_hstride + e]
     const int32_t* qslot;           // dequantise-in-gather: slot of each source node, -1 = row of X
     QGroupDev qg[kMaxQGroups];
@@ -184,7 +185,10 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc[c][i] = 0.0f;
     }
-    const float dv = a.wmode == GNN_W_GCN ? a.dinv[row] : 1.0f;
+    // per-row factor: dinv of the row (GCN), or the row's mean weight (CSR view)
+    const float dv = a.wmode == GNN_W_GCN                ? a.dinv[row]
+                     : (a.wmode == GNN_W_MEAN && !a.eid) ? a.dmean[row]
+                                                         : 1.0f;
     const int heads = a.heads;
     // heads this slab's columns belong to (all heads when one pass covers the row)
     const int64_t slab_f0 = slab * (LANES * VEC * NCH);
@@ -206,6 +210,10 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
                 w_my[0] = a.wgcn ? a.wgcn[e] : a.dinv[u_my] * dv;
             } else if (a.wmode == GNN_W_ONES) {
                 w_my[0] = 1.0f;
+            } else if (a.wmode == GNN_W_MEAN) {
+                // an in-edge of row v weighs 1/len(v); over the CSC view the
+                // edge's destination is the other end
+                w_my[0] = a.eid ? a.dmean[u_my] : dv;
             } else if (a.w_hstride) {
 #pragma unroll
                 for (int k = 0; k < kMaxHeads; ++k)
@@ -475,6 +483,7 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     a.mask = mask;
     a.partial = partial;
     a.wgcn = v.wgcn;
+    a.dmean = v.dmean;
     a.w_hstride = wmode == GNN_W_EDGE ? w_head_stride : 0;
     a.qslot = qs.qslot;
     a.qrec = nullptr;

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgnnmp.so")
 
 GNN_F32, GNN_BF16 = 0, 1
-GNN_W_GCN, GNN_W_ONES, GNN_W_EDGE = 0, 1, 2
+GNN_W_GCN, GNN_W_ONES, GNN_W_EDGE, GNN_W_MEAN = 0, 1, 2, 3
 GNN_GRAPH_SYMMETRIZE, GNN_GRAPH_CSC = 0x1, 0x2
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "out of memory", 4: "HIP error",
@@ -199,10 +199,10 @@ def gnn_graph_export(g: Graph):
 # ---------------------------------------------------------------------------
 def gnn_spmm(g: Graph, X, Y, weights="gcn", heads=1, transpose=False, relu=False, d=None, ws=None):
     """Y = (G . w) X (transpose: over the reversed graph), optional ReLU.
-    weights: "gcn", "ones" or an f32 tensor [nnz, heads]."""
+    weights: "gcn", "ones", "mean" or an f32 tensor [nnz, heads]."""
     d = X.shape[1] if d is None else d
     if isinstance(weights, str):
-        wmode, ew = {"gcn": GNN_W_GCN, "ones": GNN_W_ONES}[weights], None
+        wmode, ew = {"gcn": GNN_W_GCN, "ones": GNN_W_ONES, "mean": GNN_W_MEAN}[weights], None
     else:
         wmode, ew = GNN_W_EDGE, weights
     need = lib().gnn_spmm_workspace_size(g.h, int(transpose), d)

@@ -81,6 +81,9 @@ SPMM_CASES = [
     (256, "edge", 4, True, False, "f32", "f32"),
     (64, "edge", 2, True, False, "f32", "f32"),
     (512, "gcn", 1, False, False, "f32", "f32"),
+    (256, "mean", 1, False, False, "f32", "f32"),
+    (128, "mean", 1, True, False, "f32", "f32"),
+    (100, "mean", 1, False, True, "bf16", "bf16"),
 ]
 
 
@@ -96,6 +99,8 @@ def test_spmm(hubg, case):
         w, wt = og.gcn_norm()[1], "gcn"
     elif wname == "ones":
         w, wt = None, "ones"
+    elif wname == "mean":
+        w, wt = og.mean_weights(), "mean"
     else:
         w = r.random((og.nnz, heads)).astype(np.float32)
         wt = to_dev(w)

@@ -172,3 +172,21 @@ def test_split_by_source_partitions_the_edges(frac):
     A = g.dense(w).astype(np.float64)
     Y = oracle.spmm(lg, X, lw) + oracle.spmm(rg, X, rw)
     assert np.allclose(Y, A @ X, rtol=1e-12, atol=1e-12)
+
+
+def test_mean_weights_against_brute_force():
+    # GraphSAGE mean: row v of the aggregation is the average of the rows of
+    # {v} u N(v), by Python sets on a tiny directed graph
+    r = np.random.default_rng(41)
+    n = 60
+    src, dst = r.integers(0, n, 400), r.integers(0, n, 400)
+    g = build_graph(src, dst, n, False)
+    ins = brute_in_sets(src, dst, n, False)
+    X = r.standard_normal((n, 3))
+    Y = oracle.spmm(g, X, g.mean_weights())
+    for v in range(n):
+        nb = sorted(ins[v])
+        assert np.allclose(Y[v], X[nb].mean(axis=0), rtol=1e-6, atol=1e-7)
+    # every row's weights sum to 1 within the rounding of 1/len
+    sums = np.add.reduceat(g.mean_weights().astype(np.float64), g.row_ptr[:-1])
+    assert np.all(np.abs(sums - 1.0) <= g.deg * 2.0 ** -24)
