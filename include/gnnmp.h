@@ -316,6 +316,20 @@ gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, i
                                gnn_dtype_t y_dt, int64_t ldy, const void* saved, void* dX, float* dW, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* GraphSAGE layer with the mean aggregator in AdaQP's weighted-sum form
+ * (Eqn. 1 with alpha_{u,v} = 1/|{v} u N(v)|): Y = sigma(M X W), M = the mean
+ * operator (GNN_W_MEAN weights).  Same arguments, operand-order rule, saved
+ * tensor and workspace as the GCN layer; the backward applies M^T and needs
+ * the CSC view (M is not symmetric). */
+size_t gnn_sage_workspace_size(gnn_graph_t g, int64_t d_in, int64_t d_out);
+gnn_status_t gnn_sage_layer_fwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                                const float* W, int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                                void* saved, void* ws, size_t ws_bytes, void* stream);
+gnn_status_t gnn_sage_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                                const float* W, int64_t d_out, int relu, int relu_in, const void* Y, const void* dY,
+                                gnn_dtype_t y_dt, int64_t ldy, const void* saved, void* dX, float* dW, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* GAT layer forward (Tango, Fig. 1a):  H' = X W;  S = H' a_src, D = H' a_dst
  * per head;  E = LReLU(S[src] + D[dst]);  alpha = edge softmax(E);
  * Y[v, head k] = sum_in alpha[e,k] H'[u, head k] (heads concatenated, no bias,

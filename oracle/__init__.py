@@ -305,6 +305,38 @@ def gcn_layer_bwd(g, X, saved, Y, dY, W, relu, need_dX=True, dt="f32"):
     return dX, dW
 
 
+def sage_layer_fwd(g, X, W, relu, dt="f32", out_dt=None):
+    """GraphSAGE with the mean aggregator in AdaQP's weighted-sum form (Eqn. 1,
+    alpha = 1/|{v} u N(v)|): Y = sigma(M X W), operand order as the GCN layer.
+    Returns (Y, saved) with saved = M X for the aggregate-first order."""
+    out_dt = dt if out_dt is None else out_dt
+    w = g.mean_weights()
+    d_in, d_out = W.shape
+    if d_out <= d_in:
+        A = spmm(g, store(gemm(X, W), dt), w)
+        return store(np.maximum(A, 0.0) if relu else A, out_dt), None
+    MX = store(spmm(g, X, w), dt)
+    P = gemm(MX, W)
+    return store(np.maximum(P, 0.0) if relu else P, out_dt), MX
+
+
+def sage_layer_bwd(g, X, saved, Y, dY, W, relu, need_dX=True, dt="f32"):
+    """Its backward: the aggregation gradient goes through M^T (the transposed
+    product over the same weights), since M is not symmetric."""
+    w = g.mean_weights()
+    d_in, d_out = W.shape
+    G = store(np.where(Y > 0, dY, 0.0), dt) if relu else np.asarray(dY)
+    if d_out <= d_in:
+        dZ = store(spmm(g, G, w, transpose=True), dt)
+        dW = store(gemm(X, dZ, transA=True), _wdt(dt))
+        dX = store(gemm(dZ, W, transB=True), dt) if need_dX else None
+        return dX, dW
+    dW = store(gemm(saved, G, transA=True), _wdt(dt))
+    if not need_dX:
+        return None, dW
+    return store(spmm(g, store(gemm(G, W, transB=True), dt), w, transpose=True), dt), dW
+
+
 def gcn_forward_backward(g, X, Ws, labels, dt="f32"):
     """Multi-layer GCN: ReLU on hidden layers, none on the logits, mean softmax
     cross-entropy; the first layer's input gradient is not formed.

@@ -9,6 +9,7 @@
 // by the *_workspace_size queries with the same arithmetic.
 
 #include <algorithm>
+#include <string>
 
 #include "internal.h"
 
@@ -46,37 +47,30 @@ GcnWs gcn_ws(const Graph& g, int64_t d_in, int64_t d_out) {
     w.gemm = std::max(gemm_ws_bytes(1, 0, d_in, d_out, n), gemm_ws_bytes(0, 0, n, d_out, d_in));
     w.gemm = std::max(w.gemm, gemm_ws_bytes(0, 1, n, d_in, d_out));
     w.spmm = spmm_partial_bytes(g.plan[0], dmax);
+    if (g.has_csc) w.spmm = std::max(w.spmm, spmm_partial_bytes(g.plan[1], dmax));
     return w;
 }
 
-}  // namespace
-}  // namespace gnnmp
-
-using namespace gnnmp;
-
-extern "C" {
-
-size_t gnn_gcn_workspace_size(gnn_graph_t h, int64_t d_in, int64_t d_out) {
-    if (!h || d_in <= 0 || d_out <= 0) return 0;
-    return gcn_ws(h->g, d_in, d_out).total();
-}
-
-gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+// One graph-convolution layer, Y = sigma(A X W), with A the GCN operator
+// (A_hat, symmetric) or the mean operator (not symmetric: the backward walks
+// its transpose over the CSC view).
+gnn_status_t conv_fwd(const char* api, gnn_weights_t wmode, gnn_graph_t h, const void* X, gnn_dtype_t x_dt,
+                      int64_t ldx, int64_t d_in,
                                const float* W, int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                                void* saved, void* ws, size_t ws_bytes, void* stream) {
-    GNN_REQUIRE(h, "gnn_gcn_layer_fwd: graph handle is NULL");
+    GNN_REQUIRE(h, std::string(api) + ": graph handle is NULL");
     const Graph& g = h->g;
-    GNN_REQUIRE(d_in >= 1 && d_out >= 1, "gnn_gcn_layer_fwd: widths must be >= 1");
-    GNN_REQUIRE(ldx >= d_in && ldy >= d_out, "gnn_gcn_layer_fwd: leading dimensions too small");
+    GNN_REQUIRE(d_in >= 1 && d_out >= 1, std::string(api) + ": widths must be >= 1");
+    GNN_REQUIRE(ldx >= d_in && ldy >= d_out, std::string(api) + ": leading dimensions too small");
     GNN_REQUIRE((x_dt == GNN_F32 || x_dt == GNN_BF16) && (y_dt == GNN_F32 || y_dt == GNN_BF16),
-                "gnn_gcn_layer_fwd: unknown dtype");
-    GNN_REQUIRE(relu == 0 || relu == 1, "gnn_gcn_layer_fwd: relu must be 0 or 1");
-    GNN_REQUIRE(g.n == 0 || (X && W && Y), "gnn_gcn_layer_fwd: NULL pointer");
+                std::string(api) + ": unknown dtype");
+    GNN_REQUIRE(relu == 0 || relu == 1, std::string(api) + ": relu must be 0 or 1");
+    GNN_REQUIRE(g.n == 0 || (X && W && Y), std::string(api) + ": NULL pointer");
     const bool gemm_first = d_out <= d_in;
-    GNN_REQUIRE(gemm_first || g.n == 0 || saved, "gnn_gcn_layer_fwd: saved is NULL (aggregate-first order)");
+    GNN_REQUIRE(gemm_first || g.n == 0 || saved, std::string(api) + ": saved is NULL (aggregate-first order)");
     const GcnWs w = gcn_ws(g, d_in, d_out);
     if (ws_bytes < w.total() || (!ws && w.total()))
-        return fail(GNN_ERR_WORKSPACE, "gnn_gcn_layer_fwd: workspace smaller than gnn_gcn_workspace_size()");
+        return fail(GNN_ERR_WORKSPACE, std::string(api) + ": workspace smaller than gnn_gcn_workspace_size()");
     if (g.n == 0) return GNN_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     Carver c(ws);
@@ -88,37 +82,43 @@ gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, i
         // Z = X W (rows padded to 4), then Y = sigma(A_hat Z)
         const int64_t ldz = pad4(d_out);
         GNN_TRY(launch_gemm(0, 0, g.n, d_out, d_in, X, x_dt, ldx, W, GNN_F32, d_out, T, x_dt, ldz, gws, w.gemm, st));
-        return launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, T, x_dt, ldz, Y, y_dt, ldy, d_out, relu,
+        return launch_spmm(csr_view(g), g.dinv, wmode, nullptr, 1, T, x_dt, ldz, Y, y_dt, ldy, d_out, relu,
                            Rank1Epilogue{}, sws, st);
     }
     // saved = A_hat X (same layout as X), then Y = sigma(saved W)
-    GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, X, x_dt, ldx, saved, x_dt, ldx, d_in, 0,
+    GNN_TRY(launch_spmm(csr_view(g), g.dinv, wmode, nullptr, 1, X, x_dt, ldx, saved, x_dt, ldx, d_in, 0,
                         Rank1Epilogue{}, sws, st));
     return launch_gemm(0, 0, g.n, d_out, d_in, saved, x_dt, ldx, W, GNN_F32, d_out, Y, y_dt, ldy, gws, w.gemm, st,
                        relu);
 }
 
-gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+gnn_status_t conv_bwd(const char* api, gnn_weights_t wmode, gnn_graph_t h, const void* X, gnn_dtype_t x_dt,
+                      int64_t ldx, int64_t d_in,
                                const float* W, int64_t d_out, int relu, int relu_in, const void* Y, const void* dY,
                                gnn_dtype_t y_dt, int64_t ldy, const void* saved, void* dX, float* dW, void* ws,
                                size_t ws_bytes, void* stream) {
-    GNN_REQUIRE(h, "gnn_gcn_layer_bwd: graph handle is NULL");
+    GNN_REQUIRE(h, std::string(api) + ": graph handle is NULL");
     const Graph& g = h->g;
-    GNN_REQUIRE(d_in >= 1 && d_out >= 1, "gnn_gcn_layer_bwd: widths must be >= 1");
-    GNN_REQUIRE(ldx >= d_in && ldy >= d_out, "gnn_gcn_layer_bwd: leading dimensions too small");
+    // the backward aggregates over the transposed operator: A_hat is
+    // symmetric (its CSR view serves), the mean operator is not (CSC view)
+    if (wmode == GNN_W_MEAN && !g.has_csc) return fail(GNN_ERR_GRAPH, std::string(api) + ": needs the CSC view");
+    const AggView bview = wmode == GNN_W_MEAN ? csc_view(g) : csr_view(g);
+    GNN_REQUIRE(d_in >= 1 && d_out >= 1, std::string(api) + ": widths must be >= 1");
+    GNN_REQUIRE(ldx >= d_in && ldy >= d_out, std::string(api) + ": leading dimensions too small");
     GNN_REQUIRE((x_dt == GNN_F32 || x_dt == GNN_BF16) && (y_dt == GNN_F32 || y_dt == GNN_BF16),
-                "gnn_gcn_layer_bwd: unknown dtype");
-    GNN_REQUIRE((relu == 0 || relu == 1) && (relu_in == 0 || relu_in == 1), "gnn_gcn_layer_bwd: flags must be 0/1");
-    GNN_REQUIRE(dW && W, "gnn_gcn_layer_bwd: W or dW is NULL");
-    GNN_REQUIRE(g.n == 0 || dY, "gnn_gcn_layer_bwd: dY is NULL");
-    GNN_REQUIRE(!relu || g.n == 0 || Y, "gnn_gcn_layer_bwd: Y is NULL (needed for the ReLU mask)");
-    GNN_REQUIRE(!relu_in || !dX || X, "gnn_gcn_layer_bwd: X is NULL (needed for the input ReLU mask)");
+                std::string(api) + ": unknown dtype");
+    GNN_REQUIRE((relu == 0 || relu == 1) && (relu_in == 0 || relu_in == 1),
+                std::string(api) + ": flags must be 0/1");
+    GNN_REQUIRE(dW && W, std::string(api) + ": W or dW is NULL");
+    GNN_REQUIRE(g.n == 0 || dY, std::string(api) + ": dY is NULL");
+    GNN_REQUIRE(!relu || g.n == 0 || Y, std::string(api) + ": Y is NULL (needed for the ReLU mask)");
+    GNN_REQUIRE(!relu_in || !dX || X, std::string(api) + ": X is NULL (needed for the input ReLU mask)");
     const bool gemm_first = d_out <= d_in;
     GNN_REQUIRE(g.n == 0 || (gemm_first ? X != nullptr : saved != nullptr),
-                "gnn_gcn_layer_bwd: X (GEMM-first) or saved (aggregate-first) is NULL");
+                std::string(api) + ": X (GEMM-first) or saved (aggregate-first) is NULL");
     const GcnWs w = gcn_ws(g, d_in, d_out);
     if (ws_bytes < w.total() || (!ws && w.total()))
-        return fail(GNN_ERR_WORKSPACE, "gnn_gcn_layer_bwd: workspace smaller than gnn_gcn_workspace_size()");
+        return fail(GNN_ERR_WORKSPACE, std::string(api) + ": workspace smaller than gnn_gcn_workspace_size()");
     hipStream_t st = static_cast<hipStream_t>(stream);
     Carver c(ws);
     void* Gb = c.take(w.g);
@@ -145,7 +145,7 @@ gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, i
     if (gemm_first) {
         // dZ = A_hat G;  dW = X^T dZ;  dX = dZ W^T
         const int64_t ldz = pad4(d_out);
-        GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, G, g_dt, ldg, T, x_dt, ldz, d_out, 0,
+        GNN_TRY(launch_spmm(bview, g.dinv, wmode, nullptr, 1, G, g_dt, ldg, T, x_dt, ldz, d_out, 0,
                             Rank1Epilogue{}, sws, st));
         GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, X, x_dt, ldx, T, x_dt, ldz, dW, GNN_F32, d_out, gws, w.gemm, st));
         if (dX)
@@ -158,10 +158,56 @@ gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, i
     if (dX) {
         const int64_t ldt = pad4(d_in);
         GNN_TRY(launch_gemm(0, 1, g.n, d_in, d_out, G, g_dt, ldg, W, GNN_F32, d_out, T, x_dt, ldt, gws, w.gemm, st));
-        GNN_TRY(launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, T, x_dt, ldt, dX, x_dt, ldx, d_in, 0,
+        GNN_TRY(launch_spmm(bview, g.dinv, wmode, nullptr, 1, T, x_dt, ldt, dX, x_dt, ldx, d_in, 0,
                             Rank1Epilogue{}, sws, st, mx));
     }
     return GNN_OK;
+}
+
+}  // namespace
+}  // namespace gnnmp
+
+using namespace gnnmp;
+
+extern "C" {
+
+size_t gnn_gcn_workspace_size(gnn_graph_t h, int64_t d_in, int64_t d_out) {
+    if (!h || d_in <= 0 || d_out <= 0) return 0;
+    return gcn_ws(h->g, d_in, d_out).total();
+}
+
+gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                               const float* W, int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                               void* saved, void* ws, size_t ws_bytes, void* stream) {
+    return conv_fwd("gnn_gcn_layer_fwd", GNN_W_GCN, h, X, x_dt, ldx, d_in, W, d_out, relu, Y, y_dt, ldy, saved, ws,
+                    ws_bytes, stream);
+}
+
+gnn_status_t gnn_gcn_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                               const float* W, int64_t d_out, int relu, int relu_in, const void* Y, const void* dY,
+                               gnn_dtype_t y_dt, int64_t ldy, const void* saved, void* dX, float* dW, void* ws,
+                               size_t ws_bytes, void* stream) {
+    return conv_bwd("gnn_gcn_layer_bwd", GNN_W_GCN, h, X, x_dt, ldx, d_in, W, d_out, relu, relu_in, Y, dY, y_dt, ldy,
+                    saved, dX, dW, ws, ws_bytes, stream);
+}
+
+size_t gnn_sage_workspace_size(gnn_graph_t h, int64_t d_in, int64_t d_out) {
+    return gnn_gcn_workspace_size(h, d_in, d_out);
+}
+
+gnn_status_t gnn_sage_layer_fwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                                const float* W, int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                                void* saved, void* ws, size_t ws_bytes, void* stream) {
+    return conv_fwd("gnn_sage_layer_fwd", GNN_W_MEAN, h, X, x_dt, ldx, d_in, W, d_out, relu, Y, y_dt, ldy, saved, ws,
+                    ws_bytes, stream);
+}
+
+gnn_status_t gnn_sage_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, int64_t ldx, int64_t d_in,
+                                const float* W, int64_t d_out, int relu, int relu_in, const void* Y, const void* dY,
+                                gnn_dtype_t y_dt, int64_t ldy, const void* saved, void* dX, float* dW, void* ws,
+                                size_t ws_bytes, void* stream) {
+    return conv_bwd("gnn_sage_layer_bwd", GNN_W_MEAN, h, X, x_dt, ldx, d_in, W, d_out, relu, relu_in, Y, dY, y_dt,
+                    ldy, saved, dX, dW, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -54,6 +54,9 @@ _SIGS = {
     "gnn_gcn_workspace_size": ("PII", "S"),
     "gnn_gcn_layer_fwd": ("PPiIIPIiPiIPPSP", "i"),
     "gnn_gcn_layer_bwd": ("PPiIIPIiiPPiIPPPPSP", "i"),
+    "gnn_sage_workspace_size": ("PII", "S"),
+    "gnn_sage_layer_fwd": ("PPiIIPIiPiIPPSP", "i"),
+    "gnn_sage_layer_bwd": ("PPiIIPIiiPPiIPPPPSP", "i"),
     "gnn_gat_saved_size": ("PiI", "S"),
     "gnn_gat_workspace_size": ("PIiI", "S"),
     "gnn_gat_layer_fwd": ("PPIPPPiIFPPPSP", "i"),
@@ -328,19 +331,20 @@ def gnn_gcn_workspace_size(g: Graph, d_in, d_out):
     return lib().gnn_gcn_workspace_size(g.h, d_in, d_out)
 
 
-def gnn_gcn_layer_fwd(g: Graph, X, W, Y, relu, saved=None, ws=None):
+def gnn_gcn_layer_fwd(g: Graph, X, W, Y, relu, saved=None, ws=None, _fn="gnn_gcn_layer_fwd"):
     """Y = sigma(A_hat X W); X, Y may be row-strided views (leading dims from their strides)."""
     d_in, d_out = W.shape
     if ws is None:
         ws = _ws(gnn_gcn_workspace_size(g, d_in, d_out), X.device)
     if saved is not None and _ld(saved) != _ld(X):
         raise ValueError("saved must have X's row stride")
-    _check(lib().gnn_gcn_layer_fwd(g.h, _p(X), _dt(X), _ld(X), d_in, _p(W), d_out, int(relu), _p(Y), _dt(Y), _ld(Y),
+    _check(getattr(lib(), _fn)(g.h, _p(X), _dt(X), _ld(X), d_in, _p(W), d_out, int(relu), _p(Y), _dt(Y), _ld(Y),
                                    _p(saved), _p(ws), ws.numel(), _stream()))
     return Y
 
 
-def gnn_gcn_layer_bwd(g: Graph, X, W, Y, dY, relu, dW, dX=None, saved=None, ws=None, relu_in=False):
+def gnn_gcn_layer_bwd(g: Graph, X, W, Y, dY, relu, dW, dX=None, saved=None, ws=None, relu_in=False,
+                      _fn="gnn_gcn_layer_bwd"):
     d_in, d_out = W.shape
     if ws is None:
         ws = _ws(gnn_gcn_workspace_size(g, d_in, d_out), dY.device)
@@ -350,10 +354,20 @@ def gnn_gcn_layer_bwd(g: Graph, X, W, Y, dY, relu, dW, dX=None, saved=None, ws=N
             raise ValueError("dX / saved must have X's row stride")
     if Y is not None and _ld(Y) != _ld(dY):
         raise ValueError("Y and dY must share a row stride")
-    _check(lib().gnn_gcn_layer_bwd(g.h, _p(X), _dt(ref), _ld(ref), d_in, _p(W), d_out, int(relu), int(relu_in),
+    _check(getattr(lib(), _fn)(g.h, _p(X), _dt(ref), _ld(ref), d_in, _p(W), d_out, int(relu), int(relu_in),
                                    _p(Y), _p(dY), _dt(dY), _ld(dY), _p(saved), _p(dX), _p(dW), _p(ws), ws.numel(),
                                    _stream()))
     return dX, dW
+
+
+def gnn_sage_layer_fwd(g: Graph, X, W, Y, relu, saved=None, ws=None):
+    """Y = sigma(M X W), M the mean aggregation (GraphSAGE)."""
+    return gnn_gcn_layer_fwd(g, X, W, Y, relu, saved=saved, ws=ws, _fn="gnn_sage_layer_fwd")
+
+
+def gnn_sage_layer_bwd(g: Graph, X, W, Y, dY, relu, dW, dX=None, saved=None, ws=None, relu_in=False):
+    return gnn_gcn_layer_bwd(g, X, W, Y, dY, relu, dW, dX=dX, saved=saved, ws=ws, relu_in=relu_in,
+                             _fn="gnn_sage_layer_bwd")
 
 
 def gnn_gat_saved_size(g: Graph, heads, d_head):

@@ -101,6 +101,63 @@ def test_gcn_layer_fwd_bwd(hubsym, case):
                 bf16_out=dt == "bf16", what="gcn dX (relu_in)")
 
 
+SAGE_CASES = [  # d_in, d_out, relu, storage dtype
+    (64, 64, True, "f32"),
+    (48, 96, True, "f32"),
+    (256, 41, False, "f32"),
+    (100, 256, True, "bf16"),
+]
+
+
+@pytest.fixture(scope="module")
+def hubdir():
+    s, t = hub_edges(6000, 40000, 2500, 33)
+    return graph_pair(s, t, 6000, False, csc=True)
+
+
+@pytest.mark.parametrize("case", SAGE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_sage_layer_fwd_bwd(hubdir, case):
+    # GraphSAGE mean aggregation on a directed graph: the backward must use
+    # the transposed mean operator (over the CSC view)
+    d_in, d_out, relu, dt = case
+    g, og = hubdir
+    r = np.random.default_rng(d_in + 7 * d_out)
+    X = oracle.store(r.standard_normal((og.n, d_in)), dt)
+    W = synth.glorot(d_in, d_out, 8)
+    rtol = RTOL16 if dt == "bf16" else RTOL32
+    w = og.mean_weights()
+    Y_ref, saved_ref = oracle.sage_layer_fwd(og, X, W, relu, dt=dt)
+    Xd, Wd = to_dev(X, TDT[dt]), to_dev(W)
+    Y = torch.empty((og.n, d_out), dtype=TDT[dt], device="cuda")
+    saved = torch.empty((og.n, d_in), dtype=TDT[dt], device="cuda") if d_out > d_in else None
+    gnnmp.gnn_sage_layer_fwd(g, Xd, Wd, Y, relu=relu, saved=saved)
+    check_close(from_dev(Y), Y_ref, oracle.spmm(og, np.abs(X) @ np.abs(W), w), rtol=rtol, bf16_out=dt == "bf16",
+                what="sage fwd")
+    dY = oracle.store(r.standard_normal((og.n, d_out)), dt)
+    dX_ref, dW_ref = oracle.sage_layer_bwd(og, X, saved_ref, Y_ref, dY, W, relu, dt=dt)
+    G = np.abs(np.where(Y_ref > 0, dY, 0.0)) if relu else np.abs(dY)
+    if d_out <= d_in:
+        MdZ = oracle.spmm(og, G, w, transpose=True)
+        mag_dW, mag_dX = np.abs(X).T.astype(np.float64) @ MdZ, MdZ @ np.abs(W).T
+    else:
+        mag_dW = oracle.spmm(og, np.abs(X), w).T @ G
+        mag_dX = oracle.spmm(og, G @ np.abs(W).T, w, transpose=True)
+    dW = torch.empty((d_in, d_out), device="cuda")
+    dX = torch.empty((og.n, d_in), dtype=TDT[dt], device="cuda")
+    gnnmp.gnn_sage_layer_bwd(g, Xd, Wd, to_dev(Y_ref, TDT[dt]), to_dev(dY, TDT[dt]), relu, dW, dX=dX,
+                             saved=to_dev(saved_ref, TDT[dt]) if saved_ref is not None else None)
+    check_close(from_dev(dW), dW_ref, mag_dW, rtol=rtol, what="sage dW")
+    check_close(from_dev(dX), dX_ref, mag_dX, rtol=rtol, bf16_out=dt == "bf16", what="sage dX")
+
+
+def test_sage_bwd_requires_csc(hubsym):
+    g, og = hubsym
+    X = torch.zeros((og.n, 8), device="cuda")
+    W = torch.zeros((8, 8), device="cuda")
+    with pytest.raises(gnnmp.GnnError, match="CSC"):
+        gnnmp.gnn_sage_layer_bwd(g, X, W, X, X, True, torch.empty_like(W), dX=torch.empty_like(X))
+
+
 def test_gcn_layer_bwd_column_slabs():
     # Source matrices over 256 MB are aggregated in 64-column slabs (300K rows
     # x 256 f32 = 307 MB): the aggregate-first backward at that size, with the

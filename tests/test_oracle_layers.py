@@ -124,3 +124,27 @@ def test_bf16_rounding_rne():
     y = oracle.to_bf16(x)
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1.0); 1 + 3*2^-9 rounds up
     assert y.tolist() == [1.0, 1.0, 1.0 + 2 ** -7, 1.0, -2.5, 0.0]
+
+
+@pytest.mark.parametrize("d_in,d_out,relu", [(8, 8, True), (6, 10, True), (10, 3, False)])
+def test_sage_fwd_dense_and_bwd_finite_difference(d_in, d_out, relu):
+    # forward against D^-1 A dense on a directed graph (M is not symmetric),
+    # backward against finite differences
+    g = graph(12, sym=False)
+    r = np.random.default_rng(13)
+    X = r.standard_normal((g.n, d_in))
+    W = r.standard_normal((d_in, d_out))
+    R = r.standard_normal((g.n, d_out))
+    M = g.dense(g.mean_weights())
+    Y, saved = oracle.sage_layer_fwd(g, X, W, relu, dt="f64")
+    P = M @ X @ W
+    assert np.allclose(Y, np.maximum(P, 0) if relu else P, rtol=1e-6, atol=1e-6)
+
+    def fX(Xv):
+        return float(np.sum(oracle.sage_layer_fwd(g, Xv, W, relu, dt="f64")[0] * R))
+
+    def fW(Wv):
+        return float(np.sum(oracle.sage_layer_fwd(g, X, Wv, relu, dt="f64")[0] * R))
+    dX, dW = oracle.sage_layer_bwd(g, X, saved, Y, R, W, relu, dt="f64")
+    fd_check(fX, X, dX, 14)
+    fd_check(fW, W, dW, 15)
