@@ -28,6 +28,7 @@
 //    in order.  No atomics: bitwise reproducible.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -37,6 +38,15 @@ namespace gnnmp {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+
+// four widened bf16 values back to bf16 (exact: their low 16 bits are zero)
+__device__ __forceinline__ bf16x4 to_bf16x4(const float (&v)[4]) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = static_cast<short>(__float_as_uint(v[i]) >> 16);
+    return r;
+}
 
 constexpr int BK = 16;
 // LDS padding.  k-contiguous tiles: rows of BK + 4 = 20 floats, so the
@@ -109,6 +119,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     // fragment reads of 16 consecutive rows hit distinct banks.  Two buffers:
     // the next slab is written while the current one is read.
     constexpr bool A_KC = !TRANS_A, B_KC = TRANS_B;
+    constexpr bool kBf16Pair = std::is_same<TA, bf16_t>::value && std::is_same<TB, bf16_t>::value;
     constexpr int A_SZ = A_KC ? BM * (BK + PAD) : BK * (BM + PADM);
     constexpr int B_SZ = B_KC ? BN * (BK + PAD) : BK * (BN + PADM);
     __shared__ float As[2][A_SZ];
@@ -267,13 +278,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                 for (int j = 0; j < 4; ++j) bfr[jj][j] = Bs[buf][(g4 + j) * (BN + PADM) + col];
             }
         }
+        if constexpr (kBf16Pair) {
+            // Both operands stored as bf16: the slab's 16 k values go through
+            // one bf16 MFMA per block (lane group g supplies k = 4g..4g+3, the
+            // instruction's own layout).  bf16 x bf16 products are exact in
+            // binary32 and accumulate in binary32, so only the summation order
+            // differs from the f32 path.  The LDS holds the widened values; the
+            // top 16 bits of each are the bf16 it came from.
+            bf16x4 ab[FM], bb[FN];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < FM; ++i) ab[i] = to_bf16x4(af[i]);
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) bb[jj] = to_bf16x4(bfr[jj]);
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int jj = 0; jj < FN; ++jj)
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(bfr[jj][j], af[i][j], acc[i][jj], 0, 0, 0);
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bb[jj], ab[i], acc[i][jj], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < FN; ++jj)
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(bfr[jj][j], af[i][j], acc[i][jj], 0, 0, 0);
+        }
         // the other buffer was last read in iteration s-1, which every wave has
         // left (barrier below), so it can be refilled now
         if (s + 1 < nslab) store_slab(buf ^ 1);

@@ -168,6 +168,11 @@ GEMM_CASES = [
     (100, 256, 30000, True, False, "bf16", "bf16", "f32"),
     (2500, 47, 256, False, False, "bf16", "f32", "f32"),
     (33, 7, 5, False, False, "f32", "f32", "f32"),
+    # both operands bf16: the bf16 matrix-core path
+    (1037, 130, 256, False, False, "bf16", "bf16", "f32"),
+    (999, 256, 100, False, True, "bf16", "bf16", "bf16"),
+    (256, 47, 70003, True, False, "bf16", "bf16", "f32"),
+    (70, 50, 30, True, True, "bf16", "bf16", "f32"),
 ]
 
 
@@ -189,6 +194,19 @@ def test_gemm(case):
     gnnmp.gnn_gemm(to_dev(A, tdt[adt]), to_dev(B, tdt[bdt]), C, transA=ta, transB=tb)
     torch.cuda.synchronize()
     check_close(from_dev(C), ref, mag, bf16_out=cdt == "bf16", what="gemm")
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
+def test_gemm_bf16_pair_integer_exact(ta, tb):
+    # bf16 x bf16 on the bf16 matrix cores with small integers: every product
+    # and partial sum is exact in binary32, so the result is exact
+    r = np.random.default_rng(4)
+    M, N, K = 515, 260, 4100
+    A = r.integers(-3, 4, (K, M) if ta else (M, K)).astype(np.float32)
+    B = r.integers(-3, 4, (N, K) if tb else (K, N)).astype(np.float32)
+    C = torch.empty((M, N), device="cuda")
+    gnnmp.gnn_gemm(to_dev(A, torch.bfloat16), to_dev(B, torch.bfloat16), C, transA=ta, transB=tb)
+    assert np.array_equal(from_dev(C), oracle.gemm(A, B, ta, tb).astype(np.float32))
 
 
 @pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
