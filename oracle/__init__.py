@@ -76,6 +76,7 @@ def lib():
             "orc_philox_uniforms": [U64, U32, P, I64, I64, P],
             "orc_quantize": [P, I64, I64, P, I64, I32, U64, U32, P, P, P],
             "orc_dequantize": [P, P, P, I64, I64, I32, P, P, I64],
+            "orc_quantize_sym8": [P, I64, I64, I64, U64, U32, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -237,6 +238,28 @@ def quantize(H, rows, bits, seed, stream=0):
     lib().orc_quantize(_p(H), d, d, _p(rows), n_rows, bits, int(seed), int(stream),
                        _p(packed), _p(scale), _p(zero))
     return packed, scale, zero
+
+
+def quantize_sym8(X, seed, stream=0):
+    """Tango's symmetric, tensor-level, dynamic 8-bit quantisation with
+    stochastic rounding: (q int8 [rows, cols], s float32) with X ~ q * s."""
+    X = _c(X, np.float32)
+    rows, cols = X.shape
+    q = np.empty((rows, cols), dtype=np.int8)
+    s = np.empty(1, dtype=np.float32)
+    lib().orc_quantize_sym8(_p(X), cols, rows, cols, int(seed), int(stream), _p(q), _p(s))
+    return q, s[0]
+
+
+def gemm_q8(A, B, seed, stream=0):
+    """Tango's quantisation-aware GEMM: A (stream) and B (stream + 1) quantised
+    as quantize_sym8, int8 x int8 products summed exactly (int64 here, int32 on
+    the device), dequantised in binary32: C = f32(acc) * (s_A * s_B)."""
+    qa, sa = quantize_sym8(A, seed, stream)
+    qb, sb = quantize_sym8(B, seed, stream + 1)
+    acc = qa.astype(np.int64) @ qb.astype(np.int64)
+    scale = np.float32(sa) * np.float32(sb)
+    return (acc.astype(np.float32) * scale).astype(np.float32), qa, qb, sa, sb
 
 
 def dequantize(packed, scale, zero, rows, d, bits, H_out):

@@ -290,3 +290,43 @@ void orc_dequantize(const uint8_t* packed, const float* scale, const float* zero
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Tango (SC'23), quantisation background and the quantisation-aware GEMM:
+ * symmetric, tensor-level, dynamic 8-bit quantisation with stochastic
+ * rounding.  m = max |X| over the whole tensor, s = m / 127; a value maps to
+ * x = X * (127 / m) in [-127, 127] and rounds stochastically,
+ * q = floor(x) + [u < x - floor(x)], clamped to [-127, 127]; X ~ q * s.
+ * In binary32 with one rounding per operation.  The uniform of element
+ * (r, c) is the Philox draw of counter (r, c/4, stream, 0), word c mod 4.
+ * m == 0 gives q = 0 and s = 0.  q is [rows, cols] row-major.
+ * ------------------------------------------------------------------------- */
+void orc_quantize_sym8(const float* X, int64_t ldx, int64_t rows, int64_t cols,
+                       uint64_t seed, uint32_t stream, int8_t* q, float* s)
+{
+    float m = 0.0f;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            float a = fabsf(X[r * ldx + c]);
+            if (a > m) m = a;
+        }
+    *s = m / 127.0f;
+    if (m == 0.0f) {
+        memset(q, 0, (size_t)(rows * cols));
+        *s = 0.0f;
+        return;
+    }
+    const float inv = 127.0f / m;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            float x = X[r * ldx + c] * inv;
+            float fl = floorf(x);
+            float frac = x - fl;
+            float u = philox_uniform(seed, stream, (uint32_t)r, (uint32_t)c);
+            int32_t v = (int32_t)fl + (u < frac ? 1 : 0);
+            if (v > 127) v = 127;
+            if (v < -127) v = -127;
+            q[r * cols + c] = (int8_t)v;
+        }
+}

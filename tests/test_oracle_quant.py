@@ -207,3 +207,53 @@ def test_greedy_against_brute_force():
         best = min(oracle.quant_variance(beta, c) for c in itertools.product((2, 4, 8), repeat=m)
                    if sum(cost[x] for x in c) <= max(units - 2, 0))
         assert oracle.quant_variance(beta, b) <= best * (1 + 1e-12) + 1e-15
+
+
+# ---------------------------------------------------------------------------
+# Tango's symmetric tensor-level 8-bit quantisation and quantisation-aware GEMM
+# ---------------------------------------------------------------------------
+def test_sym8_integer_grid_is_exact():
+    # max |X| = 127 makes the scale 1 (127/127) and every integer in range its
+    # own code: no randomness left, and the GEMM is the exact integer product
+    r = np.random.default_rng(50)
+    A = r.integers(-127, 128, (33, 70)).astype(np.float32)
+    A[0, 0] = 127
+    B = r.integers(-127, 128, (70, 19)).astype(np.float32)
+    B[3, 2] = -127
+    C, qa, qb, sa, sb = oracle.gemm_q8(A, B, seed=1)
+    assert sa == 1.0 and sb == 1.0
+    assert np.array_equal(qa, A.astype(np.int8)) and np.array_equal(qb, B.astype(np.int8))
+    assert np.array_equal(C, (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float32))
+
+
+def test_sym8_zero_tensor():
+    C, qa, qb, sa, sb = oracle.gemm_q8(np.zeros((5, 8), np.float32), np.ones((8, 3), np.float32), seed=2)
+    assert sa == 0.0 and not qa.any() and not C.any()
+
+
+def test_sym8_unbiased_and_within_one_step():
+    # stochastic rounding: every dequantised value within one step of the
+    # input, and the mean over independent draws converges to it
+    r = np.random.default_rng(51)
+    X = r.standard_normal((16, 64)).astype(np.float32)
+    acc = np.zeros(X.shape)
+    K = 400
+    for seed in range(K):
+        q, s = oracle.quantize_sym8(X, seed)
+        deq = q.astype(np.float64) * s
+        assert np.all(np.abs(deq - X) <= s * (1 + 1e-6))
+        acc += deq
+    s = np.abs(X).max() / 127
+    assert np.all(np.abs(acc / K - X) <= 5 * s * 0.5 / np.sqrt(K))
+    assert q.min() >= -127 and q.max() <= 127
+
+
+def test_q8_gemm_error_bound():
+    # |C - A B| <= sum_k (|a| s_B + |b| s_A + s_A s_B) plus the final rounding
+    r = np.random.default_rng(52)
+    A = r.standard_normal((40, 128)).astype(np.float32)
+    B = r.standard_normal((128, 30)).astype(np.float32)
+    C, qa, qb, sa, sb = oracle.gemm_q8(A, B, seed=3)
+    bound = (np.abs(A) @ np.ones_like(B)) * sb + (np.ones_like(A) @ np.abs(B)) * sa + A.shape[1] * sa * sb
+    ref = A.astype(np.float64) @ B
+    assert np.all(np.abs(C - ref) <= bound + 1e-6 * np.abs(ref))
