@@ -194,6 +194,24 @@ gnn_status_t gnn_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K,
                       const void* A, gnn_dtype_t a_dt, int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb,
                       void* C, gnn_dtype_t c_dt, int64_t ldc, void* ws, size_t ws_bytes, void* stream);
 
+/* Quantisation-aware GEMM (Tango, SC'23: symmetric, tensor-level, dynamic
+ * 8-bit quantisation with stochastic rounding; int8 x int8 products summed in
+ * int32; the result dequantised in the epilogue).  For X in {A, B}:
+ * m = max|X|, x = X * (127/m), q = floor(x) + [u < x - floor(x)] clamped to
+ * [-127, 127], s = m/127 (binary32, one rounding per operation; m == 0 gives
+ * q = 0, s = 0); u is the Philox4x32-10 draw of key (seed low, seed high),
+ * counter (row, col/4, stream, 0), word col mod 4 of X's own element, with
+ * stream = stream_id for A and stream_id + 1 for B.  C = f32(sum_k qA qB) *
+ * (s_A * s_B) (the int32 sum converted with round-to-nearest-even): bit-exact
+ * against any faithful implementation.  K <= 133,000 keeps the int32 sums
+ * from overflowing (|q| <= 127).  A [M, lda] f32,
+ * B [K, ldb] f32 (no transposes), C [M, ldc] f32.  Workspace (the quantised
+ * copies, K padded to 64, and the scales): gnn_gemm_q8_workspace_size(). */
+size_t gnn_gemm_q8_workspace_size(int64_t M, int64_t N, int64_t K);
+gnn_status_t gnn_gemm_q8(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                         float* C, int64_t ldc, uint64_t seed, uint32_t stream_id, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Mean softmax cross-entropy over n rows of c logits and its gradient:
  *   loss = (1/n) sum_v [logsumexp(z_v) - z_v[y_v]],  dz = (softmax(z_v) - onehot(y_v)) / n.
  * logits [n, ld] f32, labels int32[n] in [0, c), loss: one device float,

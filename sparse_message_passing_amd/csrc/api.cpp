@@ -434,6 +434,25 @@ gnn_status_t gnn_dequantize(const uint8_t* packed, const float* scale, const flo
     return launch_dequantize(packed, scale, zero, n_rows, d, bits, rows, H, ldh, static_cast<hipStream_t>(stream));
 }
 
+size_t gnn_gemm_q8_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return gemm_q8_ws_bytes(M, N, K);
+}
+
+gnn_status_t gnn_gemm_q8(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                         float* C, int64_t ldc, uint64_t seed, uint32_t stream_id, void* ws, size_t ws_bytes,
+                         void* stream) {
+    GNN_REQUIRE(M >= 0 && N >= 0 && K >= 0, "gnn_gemm_q8: sizes must be >= 0");
+    GNN_REQUIRE(K <= 133000, "gnn_gemm_q8: K above 133,000 could overflow the int32 sums");
+    GNN_REQUIRE(lda >= std::max<int64_t>(K, 1) && ldb >= std::max<int64_t>(N, 1) && ldc >= std::max<int64_t>(N, 1),
+                "gnn_gemm_q8: leading dimensions too small");
+    GNN_REQUIRE(M == 0 || N == 0 || (C && (K == 0 || (A && B))), "gnn_gemm_q8: NULL pointer");
+    if (M == 0 || N == 0) return GNN_OK;
+    const size_t need = gemm_q8_ws_bytes(M, N, K);
+    if (!ws || ws_bytes < need) return fail(GNN_ERR_WORKSPACE, "gnn_gemm_q8: workspace too small");
+    return launch_gemm_q8(M, N, K, A, lda, B, ldb, C, ldc, seed, stream_id, ws, static_cast<hipStream_t>(stream));
+}
+
 gnn_status_t gnn_quant_stats(gnn_graph_t h, const float* edge_w, const float* H, int64_t ldh, int64_t d,
                              const int32_t* rows, int64_t n_rows, float* beta, float* range, void* stream) {
     GNN_TRY(check_graph(h, "gnn_quant_stats"));

@@ -129,6 +129,12 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
                          const MaskEpilogue& mask = MaskEpilogue{}, int64_t w_head_stride = 0,
                          const QuantSources& qs = QuantSources{});
+gnn_status_t launch_quantize_sym8(const float* X, int64_t ldx, int64_t rows, int64_t cols, const float* mptr,
+                                  uint64_t seed, uint32_t stream_id, int8_t* out, int64_t out_ld, int transpose,
+                                  float* s_out, hipStream_t st);
+size_t gemm_q8_ws_bytes(int64_t M, int64_t N, int64_t K);
+gnn_status_t launch_gemm_q8(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                            float* C, int64_t ldc, uint64_t seed, uint32_t stream_id, void* ws, hipStream_t st);
 gnn_status_t launch_quant_stats(const AggView& v, const float* w, const float* H, int64_t ldh, int64_t d,
                                 const int32_t* rows, int64_t n_rows, float* beta, float* range, hipStream_t st);
 gnn_status_t launch_quant_slots(int64_t n, int n_groups, const int32_t* const* rows, const int64_t* counts,

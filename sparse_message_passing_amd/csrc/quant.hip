@@ -215,6 +215,54 @@ __global__ __launch_bounds__(256) void quant_stats_kernel(const float* H, int64_
     }
 }
 
+// Tango's symmetric, tensor-level, dynamic 8-bit quantisation (quantisation
+// background section) with stochastic rounding: m = max|X| (computed before,
+// read from device memory), x = X * (127 / m), q = floor(x) + [u < x -
+// floor(x)] clamped to [-127, 127], s = m / 127 (m == 0: q = 0, s = 0).
+// u is the Philox draw of counter (r, c/4, stream, 0), word c mod 4 -- one
+// call per thread covers four consecutive columns.  The output is
+// k-contiguous with out_ld >= the k extent, the padding filled with zero
+// codes: transpose = 0 writes out[r][c] (k = c), transpose = 1 writes
+// out[c][r] (k = r).
+__global__ __launch_bounds__(256) void quantize_sym8_kernel(const float* X, int64_t ldx, int64_t rows, int64_t cols,
+                                                            const float* mptr, uint32_t k0, uint32_t k1,
+                                                            uint32_t stream_id, int8_t* out, int64_t out_ld,
+                                                            int transpose, int64_t rows_ext, int64_t cq,
+                                                            float* s_out) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (t >= rows_ext * cq) return;
+    const int64_t r = t / cq, c4 = (t % cq) * 4;
+    const float m = *mptr;
+    if (t == 0) s_out[0] = m == 0.0f ? 0.0f : __fdiv_rn(m, 127.0f);
+    int q[4] = {0, 0, 0, 0};
+    if (r < rows && c4 < cols && m != 0.0f) {
+        const float inv = __fdiv_rn(127.0f, m);
+        const U4 rnd = philox4x32_10(static_cast<uint32_t>(r), static_cast<uint32_t>(c4 >> 2), stream_id, 0u, k0, k1);
+        const uint32_t w[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (c4 + j >= cols) break;
+            const float x = __fmul_rn(X[r * ldx + c4 + j], inv);
+            const float fl = floorf(x);
+            const float frac = __fsub_rn(x, fl);
+            int v = static_cast<int>(fl) + (u24(w[j]) < frac ? 1 : 0);
+            q[j] = v > 127 ? 127 : (v < -127 ? -127 : v);
+        }
+    }
+    if (!transpose) {
+        if (r < rows) {
+            const uint32_t packed = (static_cast<uint32_t>(q[0]) & 0xFFu) | ((static_cast<uint32_t>(q[1]) & 0xFFu) << 8) |
+                                    ((static_cast<uint32_t>(q[2]) & 0xFFu) << 16) |
+                                    ((static_cast<uint32_t>(q[3]) & 0xFFu) << 24);
+            *reinterpret_cast<uint32_t*>(out + r * out_ld + c4) = packed;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (c4 + j < cols) out[(c4 + j) * out_ld + r] = static_cast<int8_t>(q[j]);
+    }
+}
+
 __global__ __launch_bounds__(256) void slots_fill_kernel(int64_t n, int32_t* qslot) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i < n) qslot[i] = -1;
@@ -234,6 +282,22 @@ gnn_status_t launch_quant_stats(const AggView& v, const float* w, const float* H
     hipLaunchKernelGGL(quant_stats_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, st, H, ldh, d, rows, n_rows, v.ptr,
                        v.eid, w, beta, range);
     return launch_status("gnn_quant_stats");
+}
+
+// rows x cols f32 -> int8 codes, k-contiguous; k extent padded to out_ld
+gnn_status_t launch_quantize_sym8(const float* X, int64_t ldx, int64_t rows, int64_t cols, const float* mptr,
+                                  uint64_t seed, uint32_t stream_id, int8_t* out, int64_t out_ld, int transpose,
+                                  float* s_out, hipStream_t st) {
+    // non-transposed: every row, columns up to out_ld (zero padding);
+    // transposed: rows (k) up to out_ld, columns in quads
+    const int64_t rows_ext = transpose ? out_ld : rows;
+    const int64_t cq = transpose ? (cols + 3) / 4 : out_ld / 4;
+    const int64_t total = rows_ext * cq;
+    if (total > 0)
+        hipLaunchKernelGGL(quantize_sym8_kernel, dim3((total + 255) / 256), dim3(256), 0, st, X, ldx, rows, cols, mptr,
+                           static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), stream_id, out, out_ld,
+                           transpose, rows_ext, cq, s_out);
+    return launch_status("8-bit symmetric quantisation");
 }
 
 // Slot map of the dequantise-in-gather aggregation: -1 everywhere, then

@@ -42,6 +42,8 @@ _SIGS = {
     "gnn_edge_softmax_bwd": ("PPPPFPiP", "i"),
     "gnn_gemm_workspace_size": ("iiIII", "S"),
     "gnn_gemm": ("iiIIIPiIPiIPiIPSP", "i"),
+    "gnn_gemm_q8_workspace_size": ("III", "S"),
+    "gnn_gemm_q8": ("IIIPIPIPIQUPSP", "i"),
     "gnn_softmax_xent_workspace_size": ("I", "S"),
     "gnn_softmax_xent": ("PIIIPPPIPSP", "i"),
     "gnn_quantize": ("PIIPIiQUPPPP", "i"),
@@ -276,6 +278,17 @@ def gnn_dequantize(packed, scale, zero, rows, bits, H, d=None):
     _check(lib().gnn_dequantize(_p(packed), _p(scale), _p(zero), rows.numel(), d, bits, _p(rows), _p(H), _ld(H),
                                 _stream()))
     return H
+
+
+def gnn_gemm_q8(A, B, C, seed, stream_id=0, ws=None):
+    """C = dequant(q8(A) q8(B)): Tango's quantisation-aware GEMM (f32 in and out)."""
+    M, K = A.shape
+    N = B.shape[1]
+    if ws is None:
+        ws = _ws(lib().gnn_gemm_q8_workspace_size(M, N, K), A.device)
+    _check(lib().gnn_gemm_q8(M, N, K, _p(A), _ld(A), _p(B), _ld(B), _p(C), _ld(C), int(seed), int(stream_id), _p(ws),
+                             ws.numel(), _stream()))
+    return C
 
 
 def gnn_quant_stats(g: Graph, H, rows, beta, rng, edge_w=None, d=None):

@@ -117,6 +117,23 @@ def test_c2_gemm_sampled(shape):
         check_close(from_dev(C)[:, cols], ref, mag, what="gemm tn (weight gradient)")
 
 
+def test_c2_gemm_q8_sampled_rows_bit_exact():
+    # the quantisation-aware GEMM at the 256 -> 256 update's full shape: the
+    # tensor-wide scales and the codes of the sampled rows from the oracle,
+    # the sampled output rows bit for bit
+    n = 1 << 20
+    A = synth.normal((n, 256), 17)
+    B = synth.glorot(256, 256, 18)
+    qa, sa = oracle.quantize_sym8(A, 99, 0)
+    qb, sb = oracle.quantize_sym8(B, 99, 1)
+    C = torch.empty((n, 256), device="cuda")
+    gnnmp.gnn_gemm_q8(to_dev(A), to_dev(B), C, seed=99, stream_id=0)
+    rows = np.random.default_rng(19).choice(n, 4096, replace=False)
+    acc = qa[rows].astype(np.int64) @ qb.astype(np.int64)
+    ref = acc.astype(np.float32) * (np.float32(sa) * np.float32(sb))
+    assert np.array_equal(from_dev(C)[rows].view(np.uint32), ref.view(np.uint32))
+
+
 # ---------------------------------------------------------------------------
 # GAT layer at 2^21 nodes, 4 heads x 64, input 256
 # ---------------------------------------------------------------------------

@@ -606,3 +606,38 @@ def test_adaptive_assignment_lowers_variance():
     assert np.array_equal(bits, oracle.assign_bits_greedy(beta.astype(np.float64), 128, avg))
     assert bits.sum() <= uniform.sum()                          # no more bytes than the uniform draw
     assert oracle.quant_variance(beta, bits) < oracle.quant_variance(beta, uniform)
+
+
+# ---------------------------------------------------------------------------
+# Tango's quantisation-aware GEMM on the int8 matrix cores
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(1000, 256, 128), (777, 41, 256), (4099, 100, 70), (33, 7, 5), (300, 130, 3000)])
+def test_gemm_q8_bit_exact(M, N, K):
+    # codes, int32 sums and the binary32 dequantisation are all fixed by the
+    # definition: the result matches the oracle bit for bit
+    r = np.random.default_rng(M + N + K)
+    A = (r.standard_normal((M, K)) * r.uniform(0.5, 2, (M, 1))).astype(np.float32)
+    B = r.standard_normal((K, N)).astype(np.float32)
+    ref, *_ = oracle.gemm_q8(A, B, seed=606, stream=3)
+    C = torch.full((M, N), float("nan"), device="cuda")
+    gnnmp.gnn_gemm_q8(to_dev(A), to_dev(B), C, seed=606, stream_id=3)
+    assert np.array_equal(from_dev(C).view(np.uint32), ref.view(np.uint32))
+
+
+def test_gemm_q8_zero_and_strided():
+    r = np.random.default_rng(7)
+    A = np.zeros((50, 64), np.float32)
+    B = r.standard_normal((64, 20)).astype(np.float32)
+    C = torch.full((50, 20), float("nan"), device="cuda")
+    gnnmp.gnn_gemm_q8(to_dev(A), to_dev(B), C, seed=1)
+    assert not from_dev(C).any()
+    # row-strided operands and output
+    A = r.standard_normal((90, 40)).astype(np.float32)
+    Ab = torch.zeros((90, 48), device="cuda")
+    Ab[:, :40] = to_dev(A)
+    Bb = torch.zeros((40, 24), device="cuda")
+    Bb[:, :20] = to_dev(B[:40])
+    Cb = torch.zeros((90, 28), device="cuda")
+    gnnmp.gnn_gemm_q8(Ab[:, :40], Bb[:, :20], Cb[:, :20], seed=2)
+    ref, *_ = oracle.gemm_q8(A, B[:40], seed=2)
+    assert np.array_equal(from_dev(Cb[:, :20]).view(np.uint32), ref.view(np.uint32))
