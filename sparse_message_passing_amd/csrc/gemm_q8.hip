@@ -34,10 +34,11 @@ __global__ __launch_bounds__(256) void absmax_stage1(const float* X, int64_t ld,
                                                      float* partial) {
     __shared__ float sh[4];
     float m = 0.0f;
-    const int64_t total = rows * cols;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * 256)
-        m = fmaxf(m, fabsf(X[(i / cols) * ld + i % cols]));
+    // rows dealt round-robin to the workgroups, columns across the threads
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const float* x = X + r * ld;
+        for (int64_t c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(x[c]));
+    }
     m = group_max<64>(m);
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
     __syncthreads();

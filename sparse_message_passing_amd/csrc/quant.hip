@@ -239,10 +239,18 @@ __global__ __launch_bounds__(256) void quantize_sym8_kernel(const float* X, int6
         const float inv = __fdiv_rn(127.0f, m);
         const U4 rnd = philox4x32_10(static_cast<uint32_t>(r), static_cast<uint32_t>(c4 >> 2), stream_id, 0u, k0, k1);
         const uint32_t w[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+        float xin[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float* xr = X + r * ldx + c4;
+        if (c4 + 4 <= cols && (reinterpret_cast<uintptr_t>(xr) & 15) == 0) {
+            const float4 v = *reinterpret_cast<const float4*>(xr);
+            xin[0] = v.x, xin[1] = v.y, xin[2] = v.z, xin[3] = v.w;
+        } else {
+            for (int j = 0; j < 4 && c4 + j < cols; ++j) xin[j] = xr[j];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (c4 + j >= cols) break;
-            const float x = __fmul_rn(X[r * ldx + c4 + j], inv);
+            const float x = __fmul_rn(xin[j], inv);
             const float fl = floorf(x);
             const float frac = __fsub_rn(x, fl);
             int v = static_cast<int>(fl) + (u24(w[j]) < frac ? 1 : 0);
