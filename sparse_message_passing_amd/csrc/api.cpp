@@ -321,7 +321,7 @@ gnn_status_t gnn_spmm(gnn_graph_t h, int transpose, gnn_weights_t wmode, const f
     GNN_REQUIRE(wmode != GNN_W_EDGE || edge_w, "gnn_spmm: edge_w is NULL");
     GNN_REQUIRE(relu == 0 || relu == 1, "gnn_spmm: relu must be 0 or 1");
     GNN_REQUIRE(g.n == 0 || (X && Y), "gnn_spmm: X or Y is NULL");
-    GNN_REQUIRE(X != Y, "gnn_spmm: X and Y must not overlap");
+    GNN_REQUIRE(g.n == 0 || X != Y, "gnn_spmm: X and Y must not overlap");
     if (transpose && !g.has_csc) return fail(GNN_ERR_GRAPH, "gnn_spmm: transpose needs the CSC view");
     const RowPlan& p = g.plan[transpose ? 1 : 0];
     const size_t need = spmm_partial_bytes(p, d);
