@@ -23,6 +23,7 @@ namespace gnnmp {
 namespace {
 
 constexpr int G = 16;  // lanes per row in the per-row edge kernels
+constexpr int kCache = 4;  // edges per lane kept in registers by the softmax kernels (rows up to 64 edges)
 
 template <int H>
 struct HV {
@@ -272,6 +273,42 @@ __device__ __forceinline__ void softmax_fwd_rows(const Sched& s, const float* E,
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
     HV<H> m;
     hv_fill<H>(m, -INFINITY);
+    if (ee - eb <= G * kCache) {
+        // short row: each lane keeps its (up to kCache) edges in registers, so
+        // E is read once; the same per-lane orders as the general path below
+        HV<H> x[kCache];
+#pragma unroll
+        for (int c = 0; c < kCache; ++c) {
+            const int64_t e = eb + lane + c * G;
+            if (e < ee) {
+                x[c] = ld<H>(E + e * H);
+#pragma unroll
+                for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x[c].v[k]);
+            }
+        }
+        hv_group_max<H, G>(m);
+        HV<H> z;
+        hv_fill<H>(z, 0.0f);
+#pragma unroll
+        for (int c = 0; c < kCache; ++c)
+            if (eb + lane + c * G < ee) {
+#pragma unroll
+                for (int k = 0; k < H; ++k) z.v[k] += __expf(x[c].v[k] - m.v[k]);
+            }
+        hv_group_sum<H, G>(z);
+#pragma unroll
+        for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];
+#pragma unroll
+        for (int c = 0; c < kCache; ++c) {
+            const int64_t e = eb + lane + c * G;
+            if (e < ee) {
+#pragma unroll
+                for (int k = 0; k < H; ++k) x[c].v[k] = __expf(x[c].v[k] - m.v[k]) * z.v[k];
+                st<H>(alpha + e * H, x[c]);
+            }
+        }
+        return;
+    }
     for (int64_t e = eb + lane; e < ee; e += G) {
         HV<H> x = ld<H>(E + e * H);
 #pragma unroll
@@ -360,6 +397,27 @@ __device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* al
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
     HV<H> P;
     hv_fill<H>(P, 0.0f);
+    if (ee - eb <= G * kCache) {
+        // short row: alpha and dalpha of the lane's edges stay in registers
+        HV<H> a[kCache], da[kCache];
+#pragma unroll
+        for (int c = 0; c < kCache; ++c) {
+            const int64_t e = eb + lane + c * G;
+            if (e < ee) {
+                a[c] = ld<H>(alpha + e * H);
+                da[c] = ld_da<H>(dalpha, e, hs);
+#pragma unroll
+                for (int k = 0; k < H; ++k) P.v[k] = fmaf(a[c].v[k], da[c].v[k], P.v[k]);
+            }
+        }
+        hv_group_sum<H, G>(P);
+#pragma unroll
+        for (int c = 0; c < kCache; ++c) {
+            const int64_t e = eb + lane + c * G;
+            if (e < ee) st<H>(dE + e * H, dE_of<H>(a[c], da[c], P, pre, e, slope));
+        }
+        return;
+    }
     for (int64_t e = eb + lane; e < ee; e += G) {
         HV<H> a = ld<H>(alpha + e * H), da = ld_da<H>(dalpha, e, hs);
 #pragma unroll
