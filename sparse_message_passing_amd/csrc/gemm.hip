@@ -386,6 +386,15 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* ws, int splits
     }
 }
 
+// out[k][n] = B[n][k]  (B: N rows of K, leading dimension ldb; out: K rows of N)
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* B, int64_t ldb, int64_t N, int64_t K, T* out) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= N * K) return;
+    const int64_t k = i / N, n = i % N;
+    out[i] = B[n * ldb + k];
+}
+
 struct Plan {
     int bm, bn, wm, wn;
     int splits;
@@ -465,12 +474,25 @@ gnn_status_t launch_trans(GemmArgs& g, const Plan& p, gnn_dtype_t a, gnn_dtype_t
 
 }  // namespace
 
+// A small B given transposed (a weight matrix in dX = dZ W^T) is transposed
+// once into the workspace and the product runs in the NN form, whose
+// k-major B tile loads and fragment reads are the faster of the two.
+constexpr int64_t kSmallB = int64_t(1) << 22;
+
+bool transpose_b_first(int transA, int transB, int64_t N, int64_t K) {
+    return !transA && transB && N >= 1 && K >= 1 && N * K <= kSmallB;
+}
+
+size_t split_bytes(const Plan& p, int64_t M, int64_t N) {
+    return p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * M * N * sizeof(float)) : 0;
+}
+
 size_t gemm_ws_bytes(int transA, int transB, int64_t M, int64_t N, int64_t K) {
-    (void)transA;
-    (void)transB;
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     Plan p = make_plan(M, N, K);
-    return p.splits > 1 ? align_up(static_cast<size_t>(p.splits) * M * N * sizeof(float)) : 0;
+    size_t b = split_bytes(p, M, N);
+    if (transpose_b_first(transA, transB, N, K)) b += align_up(static_cast<size_t>(N) * K * sizeof(float));
+    return b;
 }
 
 gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
@@ -479,8 +501,22 @@ gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K
                          const MaskEpilogue& mask) {
     if (M == 0 || N == 0) return GNN_OK;
     Plan p = make_plan(M, N, K);
-    if (p.splits > 1 && ws_bytes < static_cast<size_t>(p.splits) * M * N * sizeof(float))
+    if (ws_bytes < gemm_ws_bytes(transA, transB, M, N, K))
         return fail(GNN_ERR_WORKSPACE, "gnn_gemm: workspace smaller than gnn_gemm_workspace_size()");
+    if (transpose_b_first(transA, transB, N, K)) {
+        void* Bt = static_cast<char*>(ws) + split_bytes(p, M, N);
+        const int64_t total = N * K;
+        if (b_dt == GNN_BF16)
+            hipLaunchKernelGGL((transpose_kernel<bf16_t>), dim3((total + 255) / 256), dim3(256), 0, st,
+                               static_cast<const bf16_t*>(B), ldb, N, K, static_cast<bf16_t*>(Bt));
+        else
+            hipLaunchKernelGGL((transpose_kernel<float>), dim3((total + 255) / 256), dim3(256), 0, st,
+                               static_cast<const float*>(B), ldb, N, K, static_cast<float*>(Bt));
+        GNN_TRY(launch_status("gnn_gemm (B transpose)"));
+        B = Bt;
+        ldb = N;
+        transB = 0;
+    }
     GemmArgs g;
     g.M = M, g.N = N, g.K = K;
     g.A = A, g.lda = lda, g.B = B, g.ldb = ldb, g.C = C, g.ldc = ldc;
