@@ -4,8 +4,8 @@
 // GCN; the pages train with full-graph gradient descent, AdaQP Eqn. 8):
 //   loss = (1/n) sum_v [logsumexp(z_v) - z_v[y_v]],  dz = (softmax(z_v) - onehot(y_v)) / n.
 // Tango keeps the layer that feeds the softmax in full precision, so the
-// logits, their gradient and the loss are binary32.  One wave per row; the
-// per-row losses are added in a fixed order (per block, then over blocks).
+// logits, their gradient and the loss are binary32.  The per-row losses are
+// added in a fixed order (per group, per block, then over blocks).
 
 #include "device.h"
 #include "internal.h"
@@ -14,40 +14,49 @@ namespace gnnmp {
 
 namespace {
 
-constexpr int kRowsPerWave = 16;
-constexpr int kRowsPerBlock = 4 * kRowsPerWave;  // four waves, one row at a time each
+constexpr int kRowsPerBlock = 64;
 
+// A group of LG lanes per row (LG = 16 when the row has at most 64 classes,
+// else a whole wave), 256/LG groups per workgroup, each taking the block's
+// rows g, g + 256/LG, ...; the block's loss is the sum over its groups in
+// group order, each group's rows added in row order.
+template <int LG>
 __global__ __launch_bounds__(256) void xent_rows(const float* z, int64_t n, int64_t c, int64_t ld,
                                                  const int32_t* labels, float* dz, int64_t ldd, float inv_n,
                                                  float* block_loss) {
-    __shared__ float sh[4];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    float wave_loss = 0.0f;
-    for (int k = 0; k < kRowsPerWave; ++k) {
-        const int64_t v = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + w * kRowsPerWave + k;
+    constexpr int NG = 256 / LG;
+    __shared__ float sh[NG];
+    const int lane = threadIdx.x % LG, grp = threadIdx.x / LG;
+    float grp_loss = 0.0f;
+    for (int k = grp; k < kRowsPerBlock; k += NG) {
+        const int64_t v = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + k;
         if (v >= n) break;
         const float* zr = z + v * ld;
         const int32_t y = labels[v];
         float m = -INFINITY;
-        for (int64_t j = lane; j < c; j += 64) m = fmaxf(m, zr[j]);
-        m = group_max<64>(m);
+        for (int64_t j = lane; j < c; j += LG) m = fmaxf(m, zr[j]);
+        m = group_max<LG>(m);
         float s = 0.0f;
-        for (int64_t j = lane; j < c; j += 64) s += __expf(zr[j] - m);
-        s = group_sum<64>(s);
+        for (int64_t j = lane; j < c; j += LG) s += __expf(zr[j] - m);
+        s = group_sum<LG>(s);
         const float lse = m + __logf(s);
-        wave_loss += lse - zr[y];
+        grp_loss += lse - zr[y];
         if (dz) {
             const float is = 1.0f / s;
-            for (int64_t j = lane; j < c; j += 64) {
+            for (int64_t j = lane; j < c; j += LG) {
                 float p = __expf(zr[j] - m) * is;
                 if (j == y) p -= 1.0f;
                 dz[v * ldd + j] = p * inv_n;
             }
         }
     }
-    if (lane == 0) sh[w] = wave_loss;
+    if (lane == 0) sh[grp] = grp_loss;
     __syncthreads();
-    if (threadIdx.x == 0) block_loss[blockIdx.x] = ((sh[0] + sh[1]) + sh[2]) + sh[3];
+    if (threadIdx.x == 0) {
+        float t = sh[0];
+        for (int g = 1; g < NG; ++g) t += sh[g];
+        block_loss[blockIdx.x] = t;
+    }
 }
 
 __global__ __launch_bounds__(256) void xent_total(const float* block_loss, int64_t nb, float inv_n, float* loss) {
@@ -83,8 +92,12 @@ gnn_status_t launch_softmax_xent(const float* logits, int64_t n, int64_t c, int6
                                  float* loss, float* dlogits, int64_t ld_d, float* ws, hipStream_t st) {
     const int64_t nb = (n + kRowsPerBlock - 1) / kRowsPerBlock;
     const float inv_n = n > 0 ? 1.0f / static_cast<float>(n) : 0.0f;
-    if (nb > 0)
-        hipLaunchKernelGGL(xent_rows, dim3(nb), dim3(256), 0, st, logits, n, c, ld, labels, dlogits, ld_d, inv_n, ws);
+    if (nb > 0 && c <= 64)
+        hipLaunchKernelGGL((xent_rows<16>), dim3(nb), dim3(256), 0, st, logits, n, c, ld, labels, dlogits, ld_d,
+                           inv_n, ws);
+    else if (nb > 0)
+        hipLaunchKernelGGL((xent_rows<64>), dim3(nb), dim3(256), 0, st, logits, n, c, ld, labels, dlogits, ld_d,
+                           inv_n, ws);
     hipLaunchKernelGGL(xent_total, dim3(1), dim3(256), 0, st, ws, nb, inv_n, loss);
     return launch_status("gnn_softmax_xent");
 }
