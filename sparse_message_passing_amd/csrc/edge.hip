@@ -373,6 +373,15 @@ __device__ __forceinline__ HV<H> ld_da(const float* da, int64_t e, int64_t hs) {
     return r;
 }
 
+// the dE record of edge e: os == H holds dE alone; os == 2H holds dE then
+// alpha, so a later gather through the CSC edge map fetches both in one
+// 32-byte record (4 heads) instead of two 16-byte reads from two arrays
+template <int H>
+__device__ __forceinline__ void put_dE(float* dE, int64_t os, int64_t e, const HV<H>& d, const HV<H>& a) {
+    st<H>(dE + e * os, d);
+    if (os != H) st<H>(dE + e * os + H, a);
+}
+
 template <int H>
 __device__ __forceinline__ HV<H> dE_of(const HV<H>& a, const HV<H>& da, const HV<H>& P, const float* pre,
                                        int64_t e, float slope) {
@@ -389,7 +398,8 @@ __device__ __forceinline__ HV<H> dE_of(const HV<H>& a, const HV<H>& da, const HV
 
 template <int H>
 __device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* alpha, const float* dalpha, int64_t hs,
-                                                        const float* pre, float slope, float* dE, int64_t blk) {
+                                                        const float* pre, float slope, float* dE, int64_t os,
+                                                        int64_t blk) {
     const int lane = threadIdx.x % G;
     const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
@@ -414,7 +424,7 @@ __device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* al
 #pragma unroll
         for (int c = 0; c < kCache; ++c) {
             const int64_t e = eb + lane + c * G;
-            if (e < ee) st<H>(dE + e * H, dE_of<H>(a[c], da[c], P, pre, e, slope));
+            if (e < ee) put_dE<H>(dE, os, e, dE_of<H>(a[c], da[c], P, pre, e, slope), a[c]);
         }
         return;
     }
@@ -426,13 +436,14 @@ __device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* al
     hv_group_sum<H, G>(P);
     for (int64_t e = eb + lane; e < ee; e += G) {
         HV<H> a = ld<H>(alpha + e * H), da = ld_da<H>(dalpha, e, hs);
-        st<H>(dE + e * H, dE_of<H>(a, da, P, pre, e, slope));
+        put_dE<H>(dE, os, e, dE_of<H>(a, da, P, pre, e, slope), a);
     }
 }
 
 template <int H>
 __device__ __forceinline__ void softmax_bwd_block(const Sched& s, const float* alpha, const float* dalpha, int64_t hs,
-                                                        const float* pre, float slope, float* dE, int64_t blk, float (*sh)[H]) {
+                                                        const float* pre, float slope, float* dE, int64_t os, int64_t blk,
+                                                        float (*sh)[H]) {
     const int64_t v = s.order[blk];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
     HV<H> P;
@@ -445,7 +456,7 @@ __device__ __forceinline__ void softmax_bwd_block(const Sched& s, const float* a
     hv_block_reduce<H, false>(P, sh);
     for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
         HV<H> a = ld<H>(alpha + e * H), da = ld_da<H>(dalpha, e, hs);
-        st<H>(dE + e * H, dE_of<H>(a, da, P, pre, e, slope));
+        put_dE<H>(dE, os, e, dE_of<H>(a, da, P, pre, e, slope), a);
     }
 }
 
@@ -454,6 +465,7 @@ __device__ __forceinline__ void softmax_bwd_block(const Sched& s, const float* a
 // ---------------------------------------------------------------------------
 struct Perm {              // optional re-layout of CSR-order edge values into this view's order, head-major
     const float* src = nullptr;
+    int64_t src_stride = 0;   // elements per edge record of src
     float* dst = nullptr;
     int64_t stride = 0;
 };
@@ -461,13 +473,14 @@ struct Perm {              // optional re-layout of CSR-order edge values into t
 template <int H>
 __device__ __forceinline__ void perm_put(const Perm& p, int64_t e, int64_t ce) {
     if (!p.dst) return;
-    const HV<H> a = ld<H>(p.src + ce * H);
+    const HV<H> a = ld<H>(p.src + ce * p.src_stride);
 #pragma unroll
     for (int k = 0; k < H; ++k) p.dst[k * p.stride + e] = a.v[k];
 }
 
 template <int H>
-__device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, float* out, int64_t blk, Perm pm) {
+__device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, int64_t vs, float* out, int64_t blk,
+                                            Perm pm) {
     const int lane = threadIdx.x % G;
     const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
@@ -476,7 +489,7 @@ __device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, f
     hv_fill<H>(acc, 0.0f);
     for (int64_t e = s.ptr[v] + lane; e < s.ptr[v + 1]; e += G) {
         const int64_t ce = s.eid ? static_cast<int64_t>(s.eid[e]) : e;
-        HV<H> x = ld<H>(vals + ce * H);
+        HV<H> x = ld<H>(vals + ce * vs);
         perm_put<H>(pm, e, ce);
 #pragma unroll
         for (int k = 0; k < H; ++k) acc.v[k] += x.v[k];
@@ -486,14 +499,14 @@ __device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, f
 }
 
 template <int H>
-__device__ __forceinline__ void reduce_block(const Sched& s, const float* vals, float* out, int64_t blk, float (*sh)[H],
-                                             Perm pm) {
+__device__ __forceinline__ void reduce_block(const Sched& s, const float* vals, int64_t vs, float* out, int64_t blk,
+                                             float (*sh)[H], Perm pm) {
     const int64_t v = s.order[blk];
     HV<H> acc;
     hv_fill<H>(acc, 0.0f);
     for (int64_t e = s.ptr[v] + threadIdx.x; e < s.ptr[v + 1]; e += 256) {
         const int64_t ce = s.eid ? static_cast<int64_t>(s.eid[e]) : e;
-        HV<H> x = ld<H>(vals + ce * H);
+        HV<H> x = ld<H>(vals + ce * vs);
         perm_put<H>(pm, e, ce);
 #pragma unroll
         for (int k = 0; k < H; ++k) acc.v[k] += x.v[k];
@@ -514,17 +527,18 @@ __global__ __launch_bounds__(256) void softmax_fwd_kernel(Sched s, const float* 
 
 template <int H>
 __global__ __launch_bounds__(256) void softmax_bwd_kernel(Sched s, const float* alpha, const float* dalpha,
-                                                          int64_t hs, const float* pre, float slope, float* dE) {
+                                                          int64_t hs, const float* pre, float slope, float* dE,
+                                                          int64_t os) {
     __shared__ float sh[4][H];
-    if (blockIdx.x < s.n_block) softmax_bwd_block<H>(s, alpha, dalpha, hs, pre, slope, dE, blockIdx.x, sh);
-    else softmax_bwd_rows<H>(s, alpha, dalpha, hs, pre, slope, dE, blockIdx.x - s.n_block);
+    if (blockIdx.x < s.n_block) softmax_bwd_block<H>(s, alpha, dalpha, hs, pre, slope, dE, os, blockIdx.x, sh);
+    else softmax_bwd_rows<H>(s, alpha, dalpha, hs, pre, slope, dE, os, blockIdx.x - s.n_block);
 }
 
 template <int H>
-__global__ __launch_bounds__(256) void reduce_kernel(Sched s, const float* vals, float* out, Perm pm) {
+__global__ __launch_bounds__(256) void reduce_kernel(Sched s, const float* vals, int64_t vs, float* out, Perm pm) {
     __shared__ float sh[4][H];
-    if (blockIdx.x < s.n_block) reduce_block<H>(s, vals, out, blockIdx.x, sh, pm);
-    else reduce_rows<H>(s, vals, out, blockIdx.x - s.n_block, pm);
+    if (blockIdx.x < s.n_block) reduce_block<H>(s, vals, vs, out, blockIdx.x, sh, pm);
+    else reduce_rows<H>(s, vals, vs, out, blockIdx.x - s.n_block, pm);
 }
 
 // ---------------------------------------------------------------------------
@@ -684,20 +698,22 @@ gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha,
 }
 
 gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha, const float* pre,
-                                     float slope, float* dE, int heads, hipStream_t st, int64_t dalpha_head_stride) {
+                                     float slope, float* dE, int heads, hipStream_t st, int64_t dalpha_head_stride,
+                                     int64_t out_stride) {
     if (v.n == 0) return GNN_OK;
     Sched s = make_sched(v);
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
     GNN_HEADS_SWITCH(heads, {
         hipLaunchKernelGGL((softmax_bwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, alpha, dalpha,
-                           dalpha_head_stride, pre, slope, dE);
+                           dalpha_head_stride, pre, slope, dE, out_stride ? out_stride : int64_t(H));
     });
     return launch_status("gnn_edge_softmax_bwd");
 }
 
 gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st,
-                                const float* perm_src, float* perm_dst, int64_t perm_stride) {
+                                const float* perm_src, float* perm_dst, int64_t perm_stride, int64_t vals_stride,
+                                int64_t perm_src_stride) {
     if (v.n == 0) return GNN_OK;
     Sched s = make_sched(v);
     const int64_t light = s.n - s.n_block;
@@ -705,11 +721,13 @@ gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, 
     Perm pm;
     if (perm_dst) {
         pm.src = perm_src;
+        pm.src_stride = perm_src_stride ? perm_src_stride : heads;
         pm.dst = perm_dst;
         pm.stride = perm_stride;
     }
+    const int64_t vs = vals_stride ? vals_stride : heads;
     GNN_HEADS_SWITCH(heads, {
-        hipLaunchKernelGGL((reduce_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, vals, out, pm);
+        hipLaunchKernelGGL((reduce_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, vals, vs, out, pm);
     });
     return launch_status("gnn_edge_reduce");
 }

@@ -149,13 +149,16 @@ gnn_status_t launch_sddmm_dot(const AggView& v, const void* src_feat, int64_t ld
                               int64_t ld_dst, gnn_dtype_t dt, int heads, int64_t d_head, float* out, hipStream_t st);
 gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha, int heads, hipStream_t st);
 // dalpha_head_stride > 0: dalpha is head-major, dalpha(e, k) = dalpha[k*stride + e]
+// out_stride: elements per dE record (0: heads); 2*heads also copies alpha after dE in each record
 gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha,
                                      const float* pre, float slope, float* dE, int heads, hipStream_t st,
-                                     int64_t dalpha_head_stride = 0);
+                                     int64_t dalpha_head_stride = 0, int64_t out_stride = 0);
 // perm_dst != NULL: also writes perm_dst[k*perm_stride + j] = perm_src[eid(j)*heads + k] for every
 // position j of the view (CSR-order edge values re-laid head-major in this view's order)
+// vals_stride / perm_src_stride: elements per edge record of vals / perm_src (0: heads)
 gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st,
-                                const float* perm_src = nullptr, float* perm_dst = nullptr, int64_t perm_stride = 0);
+                                const float* perm_src = nullptr, float* perm_dst = nullptr, int64_t perm_stride = 0,
+                                int64_t vals_stride = 0, int64_t perm_src_stride = 0);
 // SDDMM dot in one column slab per head, out head-major: out[k*stride + e]
 bool sddmm_dot_heads_supported(int heads, int64_t d_head);
 gnn_status_t launch_sddmm_dot_heads(const AggView& v, const float* src_feat, int64_t ld_src, const float* dst_feat,

@@ -225,7 +225,7 @@ size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_
     const Graph& g = h->g;
     const size_t n = g.n, e = g.nnz;
     const int64_t hd = heads * d_head;
-    size_t t = align_up(e * heads * 4) + 2 * align_up(n * heads * 4) + align_up(n * hd * 4);
+    size_t t = align_up(2 * e * heads * 4) + 2 * align_up(n * heads * 4) + align_up(n * hd * 4);
     t += align_up(head_colsum_partial_bytes(g.n, heads, d_head));
     t += align_up(e * heads * 4);  // backward: head-major dalpha, then head-major alpha in CSC order
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
@@ -302,7 +302,7 @@ gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     const int64_t hd = heads * d_head;
     GatSaved s = carve_saved(g, const_cast<void*>(saved), heads, d_head);
     Carver c(ws);
-    float* dEb = static_cast<float*>(c.take(static_cast<size_t>(g.nnz) * heads * 4));
+    float* dEb = static_cast<float*>(c.take(2 * static_cast<size_t>(g.nnz) * heads * 4));  // [nnz][dE | alpha]
     float* dD = static_cast<float*>(c.take(static_cast<size_t>(g.n) * heads * 4));
     float* dS = static_cast<float*>(c.take(static_cast<size_t>(g.n) * heads * 4));
     float* dHp = static_cast<float*>(c.take(static_cast<size_t>(g.n) * hd * 4));
@@ -327,10 +327,11 @@ gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     if (by_head) {
         // dalpha = dY[dst] . H'[src];  dE = alpha (dalpha - P) * LReLU'
         GNN_TRY(launch_sddmm_dot_heads(csr, s.Hp, hd, dY, hd, heads, d_head, hm, g.nnz, st));
-        GNN_TRY(launch_edge_softmax_bwd(csr, s.alpha, hm, s.Epre, slope, dEb, heads, st, g.nnz));
+        // records [dE | alpha] per edge: the out-edge sum below gathers both in one read
+        GNN_TRY(launch_edge_softmax_bwd(csr, s.alpha, hm, s.Epre, slope, dEb, heads, st, g.nnz, 2 * heads));
         // dD = in-edge sums, dS = out-edge sums (+ alpha re-laid, overwriting dalpha)
-        GNN_TRY(launch_edge_reduce(csr, dEb, heads, dD, st));
-        GNN_TRY(launch_edge_reduce(csc, dEb, heads, dS, st, s.alpha, hm, g.nnz));
+        GNN_TRY(launch_edge_reduce(csr, dEb, heads, dD, st, nullptr, nullptr, 0, 2 * heads));
+        GNN_TRY(launch_edge_reduce(csc, dEb, heads, dS, st, dEb + heads, hm, g.nnz, 2 * heads, 2 * heads));
         // dH' = (G . alpha)^T dY + dS a_src + dD a_dst
         GNN_TRY(launch_spmm(csc, g.dinv, GNN_W_EDGE, hm, heads, dY, GNN_F32, hd, dHp, GNN_F32, hd, hd, 0, r1, sws,
                             st, MaskEpilogue{}, g.nnz));
