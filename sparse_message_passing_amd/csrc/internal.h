@@ -148,6 +148,9 @@ gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, con
 gnn_status_t launch_sddmm_dot(const AggView& v, const void* src_feat, int64_t ld_src, const void* dst_feat,
                               int64_t ld_dst, gnn_dtype_t dt, int heads, int64_t d_head, float* out, hipStream_t st);
 gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha, int heads, hipStream_t st);
+// SDDMM-add + LeakyReLU + edge softmax in one pass (S, D: [n, heads]); E_pre and alpha [nnz, heads]
+gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float* D, int heads, float slope,
+                                  float* alpha, float* out_pre, hipStream_t st);
 // dalpha_head_stride > 0: dalpha is head-major, dalpha(e, k) = dalpha[k*stride + e]
 // out_stride: elements per dE record (0: heads); 2*heads also copies alpha after dE in each record
 gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha,

@@ -279,8 +279,7 @@ gnn_status_t gnn_gat_layer_fwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     // H' = X W;  S, D per-head scores;  E = LReLU(S[src] + D[dst]);  alpha = softmax;  Y = (G . alpha) H'
     GNN_TRY(launch_gemm(0, 0, g.n, hd, d_in, X, GNN_F32, d_in, W, GNN_F32, hd, s.Hp, GNN_F32, hd, gws, gemm, st));
     GNN_TRY(launch_gat_scores(g.n, s.Hp, heads, d_head, a_src, a_dst, s.S, s.D, st));
-    GNN_TRY(launch_sddmm_add(csr_view(g), s.S, heads, s.D, heads, heads, slope, s.alpha, s.Epre, st));
-    GNN_TRY(launch_edge_softmax(csr_view(g), s.alpha, s.alpha, heads, st));
+    GNN_TRY(launch_gat_attention(csr_view(g), s.S, s.D, heads, slope, s.alpha, s.Epre, st));
     return launch_spmm(csr_view(g), g.dinv, GNN_W_EDGE, s.alpha, heads, s.Hp, GNN_F32, hd, Y, GNN_F32, hd, hd, 0,
                        Rank1Epilogue{}, sws, st);
 }
