@@ -353,8 +353,9 @@ gnn_status_t gnn_sage_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, 
  * Y[v, head k] = sum_in alpha[e,k] H'[u, head k] (heads concatenated, no bias,
  * no output activation).  X [n, d_in] f32, W [d_in, heads*d_head] f32,
  * a_src, a_dst [heads, d_head] f32, Y [n, heads*d_head] f32.
- * saved: gnn_gat_saved_size() bytes holding H', S, D, E_pre, alpha for the
- * backward.  Needs the CSC view only for the backward. */
+ * saved: gnn_gat_saved_size() bytes holding H', S, D, each destination's
+ * softmax maximum M and 1 / sum of exponentials Z per head ([n, heads] each),
+ * and alpha, for the backward.  Needs the CSC view only for the backward. */
 size_t gnn_gat_saved_size(gnn_graph_t g, int heads, int64_t d_head);
 size_t gnn_gat_workspace_size(gnn_graph_t g, int64_t d_in, int heads, int64_t d_head);
 gnn_status_t gnn_gat_layer_fwd(gnn_graph_t g, const float* X, int64_t d_in, const float* W, const float* a_src,
@@ -368,11 +369,16 @@ gnn_status_t gnn_gat_layer_fwd(gnn_graph_t g, const float* X, int64_t d_in, cons
  *   dH' = (G . alpha)^T dY + dS a_src + dD a_dst        (SpMM on the CSC view)
  *   da_src[k] = sum_v dS[v,k] H'[v, head k], likewise da_dst
  *   dW = X^T dH',  dX = dH' W^T  (dX nullable).
- * Requires the CSC view. */
+ * Y is the forward's output [n, heads*d_head]: since Y[v] = sum_in alpha H'[u],
+ * P[v, k] = <dY[v, head k], Y[v, head k]>, a row product taken before any
+ * dE, which lets the SDDMM dot, dE, dS and the transposed SpMM run as one
+ * pass over the out-edges (alpha formed again from S, D, M, Z).  Requires the
+ * CSC view, 1, 2, 4 or 8 heads and d_head a power of two from 4 to 256
+ * (GNN_ERR_UNSUPPORTED otherwise). */
 gnn_status_t gnn_gat_layer_bwd(gnn_graph_t g, const float* X, int64_t d_in, const float* W, const float* a_src,
-                               const float* a_dst, int heads, int64_t d_head, float slope, const float* dY,
-                               const void* saved, float* dX, float* dW, float* da_src, float* da_dst,
-                               void* ws, size_t ws_bytes, void* stream);
+                               const float* a_dst, int heads, int64_t d_head, float slope, const float* Y,
+                               const float* dY, const void* saved, float* dX, float* dW, float* da_src,
+                               float* da_dst, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -155,6 +155,11 @@ gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const in
                 s = upload(g, hg.col_ptr, &g.col_ptr);
                 if (s == GNN_OK) s = upload(g, hg.csc_row, &g.csc_row);
                 if (s == GNN_OK) s = upload(g, hg.csc_eid, &g.csc_eid);
+                if (s == GNN_OK) {
+                    std::vector<int32_t> cpos(hg.csc_eid.size());
+                    for (size_t j = 0; j < cpos.size(); ++j) cpos[hg.csc_eid[j]] = static_cast<int32_t>(j);
+                    s = upload(g, cpos, &g.csr_cpos);
+                }
                 if (s == GNN_OK) s = make_plan(g, hg.col_ptr, g.plan[1], nullptr);
             }
         }

@@ -180,50 +180,6 @@ __global__ __launch_bounds__(256) void sddmm_dot_kernel(Sched s, const T* src, i
 }
 
 // ---------------------------------------------------------------------------
-// SDDMM dot in column slabs, one head per slab (grid = slab_blocks x heads,
-// slab-major), so the gathered rows of one head stay cache resident while that
-// head's dot products run.  A group of HL = d_head/4 lanes per row; the dot
-// of edge j+q lands in lane j+q, and each batch of HL edges is written with
-// one coalesced store into the head's contiguous output plane.
-// ---------------------------------------------------------------------------
-template <int HL, typename T>
-__global__ __launch_bounds__(256) void sddmm_dot_heads_kernel(Sched s, int64_t slab_blocks, const T* src,
-                                                              int64_t ld_src, const T* dst, int64_t ld_dst,
-                                                              int64_t d_head, int64_t stride, float* out) {
-    const int lane = threadIdx.x % HL;
-    const int64_t k = blockIdx.x / slab_blocks;
-    const int64_t gid = static_cast<int64_t>(blockIdx.x - k * slab_blocks) * (256 / HL) + threadIdx.x / HL;
-    int64_t v, eb, ee;
-    if (!work_item(s, gid, v, eb, ee)) return;
-    const int64_t f = k * d_head + lane * 4;
-    const float4 dvec = Elem<T>::load4(dst + v * ld_dst + f);
-    float* o = out + k * stride;
-    for (int64_t e0 = eb; e0 < ee; e0 += HL) {
-        const int cnt = static_cast<int>(min(static_cast<int64_t>(HL), ee - e0));
-        const int u_my = lane < cnt ? s.idx[e0 + lane] : 0;
-        float res = 0.0f;
-        for (int j = 0; j < cnt; j += 4) {
-            float4 x[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int u = group_bcast<HL>(u_my, j + q < cnt ? j + q : j);
-                x[q] = Elem<T>::load4(src + static_cast<int64_t>(u) * ld_src + f);
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float p = x[q].x * dvec.x;
-                p = fmaf(x[q].y, dvec.y, p);
-                p = fmaf(x[q].z, dvec.z, p);
-                p = fmaf(x[q].w, dvec.w, p);
-                p = group_sum<HL>(p);
-                if (lane == j + q) res = p;
-            }
-        }
-        if (lane < cnt) o[e0 + lane] = res;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // edge softmax and its backward: per-row groups for rows of degree <=
 // kBlockRow, one workgroup per longer row
 // ---------------------------------------------------------------------------
@@ -356,7 +312,7 @@ __device__ __forceinline__ HV<H> attn_score(const float* S, const HV<H>& dv, int
 
 template <int H>
 __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const float* D, float slope, int act,
-                                          float* alpha, float* out_pre, int64_t blk) {
+                                          float* alpha, float* out_pre, float* mo, float* zo, int64_t blk) {
     const int lane = threadIdx.x % G;
     const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
@@ -374,7 +330,7 @@ __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const 
             const int64_t e = eb + lane + c * G;
             if (e < ee) {
                 x[c] = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-                st<H>(out_pre + e * H, pre);
+                if (out_pre) st<H>(out_pre + e * H, pre);
 #pragma unroll
                 for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x[c].v[k]);
             }
@@ -389,6 +345,7 @@ __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const 
         hv_group_sum<H, G>(z);
 #pragma unroll
         for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];
+        if (mo && lane == 0) st<H>(mo + v * H, m), st<H>(zo + v * H, z);
 #pragma unroll
         for (int c = 0; c < kCache; ++c) {
             const int64_t e = eb + lane + c * G;
@@ -402,7 +359,7 @@ __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const 
     }
     for (int64_t e = eb + lane; e < ee; e += G) {
         const HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-        st<H>(out_pre + e * H, pre);
+        if (out_pre) st<H>(out_pre + e * H, pre);
 #pragma unroll
         for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x.v[k]);
     }
@@ -415,6 +372,7 @@ __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const 
     hv_group_sum<H, G>(z);
 #pragma unroll
     for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];
+    if (mo && lane == 0) st<H>(mo + v * H, m), st<H>(zo + v * H, z);
     for (int64_t e = eb + lane; e < ee; e += G) {
         HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
 #pragma unroll
@@ -425,7 +383,8 @@ __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const 
 
 template <int H>
 __device__ __forceinline__ void attn_block(const Sched& s, const float* S, const float* D, float slope, int act,
-                                           float* alpha, float* out_pre, int64_t blk, float (*sh)[H]) {
+                                           float* alpha, float* out_pre, float* mo, float* zo, int64_t blk,
+                                           float (*sh)[H]) {
     const int64_t v = s.order[blk];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
     HV<H> dv, pre, m, z;
@@ -434,7 +393,7 @@ __device__ __forceinline__ void attn_block(const Sched& s, const float* S, const
     hv_fill<H>(m, -INFINITY);
     for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
         const HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-        st<H>(out_pre + e * H, pre);
+        if (out_pre) st<H>(out_pre + e * H, pre);
 #pragma unroll
         for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x.v[k]);
     }
@@ -448,6 +407,7 @@ __device__ __forceinline__ void attn_block(const Sched& s, const float* S, const
     hv_block_reduce<H, false>(z, sh);
 #pragma unroll
     for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];
+    if (mo && threadIdx.x == 0) st<H>(mo + v * H, m), st<H>(zo + v * H, z);
     for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
         HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
 #pragma unroll
@@ -458,10 +418,10 @@ __device__ __forceinline__ void attn_block(const Sched& s, const float* S, const
 
 template <int H>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(Sched s, const float* S, const float* D, float slope, int act,
-                                                       float* alpha, float* out_pre) {
+                                                       float* alpha, float* out_pre, float* mo, float* zo) {
     __shared__ float sh[4][H];
-    if (blockIdx.x < s.n_block) attn_block<H>(s, S, D, slope, act, alpha, out_pre, blockIdx.x, sh);
-    else attn_rows<H>(s, S, D, slope, act, alpha, out_pre, blockIdx.x - s.n_block);
+    if (blockIdx.x < s.n_block) attn_block<H>(s, S, D, slope, act, alpha, out_pre, mo, zo, blockIdx.x, sh);
+    else attn_rows<H>(s, S, D, slope, act, alpha, out_pre, mo, zo, blockIdx.x - s.n_block);
 }
 
 template <int H>
@@ -494,25 +454,6 @@ __device__ __forceinline__ void softmax_fwd_block(const Sched& s, const float* E
     }
 }
 
-// dalpha of edge e: edge-major ([e*H + k]) when hs == 0, else head-major ([k*hs + e])
-template <int H>
-__device__ __forceinline__ HV<H> ld_da(const float* da, int64_t e, int64_t hs) {
-    if (hs == 0) return ld<H>(da + e * H);
-    HV<H> r;
-#pragma unroll
-    for (int k = 0; k < H; ++k) r.v[k] = da[k * hs + e];
-    return r;
-}
-
-// the dE record of edge e: os == H holds dE alone; os == 2H holds dE then
-// alpha, so a later gather through the CSC edge map fetches both in one
-// 32-byte record (4 heads) instead of two 16-byte reads from two arrays
-template <int H>
-__device__ __forceinline__ void put_dE(float* dE, int64_t os, int64_t e, const HV<H>& d, const HV<H>& a) {
-    st<H>(dE + e * os, d);
-    if (os != H) st<H>(dE + e * os + H, a);
-}
-
 template <int H>
 __device__ __forceinline__ HV<H> dE_of(const HV<H>& a, const HV<H>& da, const HV<H>& P, const float* pre,
                                        int64_t e, float slope) {
@@ -528,9 +469,8 @@ __device__ __forceinline__ HV<H> dE_of(const HV<H>& a, const HV<H>& da, const HV
 }
 
 template <int H>
-__device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* alpha, const float* dalpha, int64_t hs,
-                                                        const float* pre, float slope, float* dE, int64_t os,
-                                                        int64_t blk) {
+__device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* alpha, const float* dalpha,
+                                                 const float* pre, float slope, float* dE, int64_t blk) {
     const int lane = threadIdx.x % G;
     const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
@@ -546,7 +486,7 @@ __device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* al
             const int64_t e = eb + lane + c * G;
             if (e < ee) {
                 a[c] = ld<H>(alpha + e * H);
-                da[c] = ld_da<H>(dalpha, e, hs);
+                da[c] = ld<H>(dalpha + e * H);
 #pragma unroll
                 for (int k = 0; k < H; ++k) P.v[k] = fmaf(a[c].v[k], da[c].v[k], P.v[k]);
             }
@@ -555,63 +495,47 @@ __device__ __forceinline__ void softmax_bwd_rows(const Sched& s, const float* al
 #pragma unroll
         for (int c = 0; c < kCache; ++c) {
             const int64_t e = eb + lane + c * G;
-            if (e < ee) put_dE<H>(dE, os, e, dE_of<H>(a[c], da[c], P, pre, e, slope), a[c]);
+            if (e < ee) st<H>(dE + e * H, dE_of<H>(a[c], da[c], P, pre, e, slope));
         }
         return;
     }
     for (int64_t e = eb + lane; e < ee; e += G) {
-        HV<H> a = ld<H>(alpha + e * H), da = ld_da<H>(dalpha, e, hs);
+        HV<H> a = ld<H>(alpha + e * H), da = ld<H>(dalpha + e * H);
 #pragma unroll
         for (int k = 0; k < H; ++k) P.v[k] = fmaf(a.v[k], da.v[k], P.v[k]);
     }
     hv_group_sum<H, G>(P);
     for (int64_t e = eb + lane; e < ee; e += G) {
-        HV<H> a = ld<H>(alpha + e * H), da = ld_da<H>(dalpha, e, hs);
-        put_dE<H>(dE, os, e, dE_of<H>(a, da, P, pre, e, slope), a);
+        HV<H> a = ld<H>(alpha + e * H), da = ld<H>(dalpha + e * H);
+        st<H>(dE + e * H, dE_of<H>(a, da, P, pre, e, slope));
     }
 }
 
 template <int H>
-__device__ __forceinline__ void softmax_bwd_block(const Sched& s, const float* alpha, const float* dalpha, int64_t hs,
-                                                        const float* pre, float slope, float* dE, int64_t os, int64_t blk,
-                                                        float (*sh)[H]) {
+__device__ __forceinline__ void softmax_bwd_block(const Sched& s, const float* alpha, const float* dalpha,
+                                                  const float* pre, float slope, float* dE, int64_t blk,
+                                                  float (*sh)[H]) {
     const int64_t v = s.order[blk];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
     HV<H> P;
     hv_fill<H>(P, 0.0f);
     for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
-        HV<H> a = ld<H>(alpha + e * H), da = ld_da<H>(dalpha, e, hs);
+        HV<H> a = ld<H>(alpha + e * H), da = ld<H>(dalpha + e * H);
 #pragma unroll
         for (int k = 0; k < H; ++k) P.v[k] = fmaf(a.v[k], da.v[k], P.v[k]);
     }
     hv_block_reduce<H, false>(P, sh);
     for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
-        HV<H> a = ld<H>(alpha + e * H), da = ld_da<H>(dalpha, e, hs);
-        put_dE<H>(dE, os, e, dE_of<H>(a, da, P, pre, e, slope), a);
+        HV<H> a = ld<H>(alpha + e * H), da = ld<H>(dalpha + e * H);
+        st<H>(dE + e * H, dE_of<H>(a, da, P, pre, e, slope));
     }
 }
 
 // ---------------------------------------------------------------------------
 // edge -> node sums; over the CSC view the values are gathered through eid
 // ---------------------------------------------------------------------------
-struct Perm {              // optional re-layout of CSR-order edge values into this view's order, head-major
-    const float* src = nullptr;
-    int64_t src_stride = 0;   // elements per edge record of src
-    float* dst = nullptr;
-    int64_t stride = 0;
-};
-
 template <int H>
-__device__ __forceinline__ void perm_put(const Perm& p, int64_t e, int64_t ce) {
-    if (!p.dst) return;
-    const HV<H> a = ld<H>(p.src + ce * p.src_stride);
-#pragma unroll
-    for (int k = 0; k < H; ++k) p.dst[k * p.stride + e] = a.v[k];
-}
-
-template <int H>
-__device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, int64_t vs, float* out, int64_t blk,
-                                            Perm pm) {
+__device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, float* out, int64_t blk) {
     const int lane = threadIdx.x % G;
     const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
@@ -620,8 +544,7 @@ __device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, i
     hv_fill<H>(acc, 0.0f);
     for (int64_t e = s.ptr[v] + lane; e < s.ptr[v + 1]; e += G) {
         const int64_t ce = s.eid ? static_cast<int64_t>(s.eid[e]) : e;
-        HV<H> x = ld<H>(vals + ce * vs);
-        perm_put<H>(pm, e, ce);
+        HV<H> x = ld<H>(vals + ce * H);
 #pragma unroll
         for (int k = 0; k < H; ++k) acc.v[k] += x.v[k];
     }
@@ -630,15 +553,14 @@ __device__ __forceinline__ void reduce_rows(const Sched& s, const float* vals, i
 }
 
 template <int H>
-__device__ __forceinline__ void reduce_block(const Sched& s, const float* vals, int64_t vs, float* out, int64_t blk,
-                                             float (*sh)[H], Perm pm) {
+__device__ __forceinline__ void reduce_block(const Sched& s, const float* vals, float* out, int64_t blk,
+                                             float (*sh)[H]) {
     const int64_t v = s.order[blk];
     HV<H> acc;
     hv_fill<H>(acc, 0.0f);
     for (int64_t e = s.ptr[v] + threadIdx.x; e < s.ptr[v + 1]; e += 256) {
         const int64_t ce = s.eid ? static_cast<int64_t>(s.eid[e]) : e;
-        HV<H> x = ld<H>(vals + ce * vs);
-        perm_put<H>(pm, e, ce);
+        HV<H> x = ld<H>(vals + ce * H);
 #pragma unroll
         for (int k = 0; k < H; ++k) acc.v[k] += x.v[k];
     }
@@ -658,18 +580,17 @@ __global__ __launch_bounds__(256) void softmax_fwd_kernel(Sched s, const float* 
 
 template <int H>
 __global__ __launch_bounds__(256) void softmax_bwd_kernel(Sched s, const float* alpha, const float* dalpha,
-                                                          int64_t hs, const float* pre, float slope, float* dE,
-                                                          int64_t os) {
+                                                          const float* pre, float slope, float* dE) {
     __shared__ float sh[4][H];
-    if (blockIdx.x < s.n_block) softmax_bwd_block<H>(s, alpha, dalpha, hs, pre, slope, dE, os, blockIdx.x, sh);
-    else softmax_bwd_rows<H>(s, alpha, dalpha, hs, pre, slope, dE, os, blockIdx.x - s.n_block);
+    if (blockIdx.x < s.n_block) softmax_bwd_block<H>(s, alpha, dalpha, pre, slope, dE, blockIdx.x, sh);
+    else softmax_bwd_rows<H>(s, alpha, dalpha, pre, slope, dE, blockIdx.x - s.n_block);
 }
 
 template <int H>
-__global__ __launch_bounds__(256) void reduce_kernel(Sched s, const float* vals, int64_t vs, float* out, Perm pm) {
+__global__ __launch_bounds__(256) void reduce_kernel(Sched s, const float* vals, float* out) {
     __shared__ float sh[4][H];
-    if (blockIdx.x < s.n_block) reduce_block<H>(s, vals, vs, out, blockIdx.x, sh, pm);
-    else reduce_rows<H>(s, vals, vs, out, blockIdx.x - s.n_block, pm);
+    if (blockIdx.x < s.n_block) reduce_block<H>(s, vals, out, blockIdx.x, sh);
+    else reduce_rows<H>(s, vals, out, blockIdx.x - s.n_block);
 }
 
 // ---------------------------------------------------------------------------
@@ -829,7 +750,7 @@ gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha,
 }
 
 gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float* D, int heads, float slope,
-                                  float* alpha, float* out_pre, hipStream_t st) {
+                                  float* alpha, float* out_pre, float* row_max, float* row_rsum, hipStream_t st) {
     if (v.n == 0) return GNN_OK;
     Sched s = make_sched(v);
     const int64_t light = s.n - s.n_block;
@@ -837,71 +758,33 @@ gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float*
     const int act = slope == slope;  // NaN: no activation
     GNN_HEADS_SWITCH(heads, {
         hipLaunchKernelGGL((attn_fwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, S, D,
-                           act ? slope : 0.0f, act, alpha, out_pre);
+                           act ? slope : 0.0f, act, alpha, out_pre, row_max, row_rsum);
     });
     return launch_status("GAT attention");
 }
 
 gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha, const float* pre,
-                                     float slope, float* dE, int heads, hipStream_t st, int64_t dalpha_head_stride,
-                                     int64_t out_stride) {
+                                     float slope, float* dE, int heads, hipStream_t st) {
     if (v.n == 0) return GNN_OK;
     Sched s = make_sched(v);
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
     GNN_HEADS_SWITCH(heads, {
         hipLaunchKernelGGL((softmax_bwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, alpha, dalpha,
-                           dalpha_head_stride, pre, slope, dE, out_stride ? out_stride : int64_t(H));
+                           pre, slope, dE);
     });
     return launch_status("gnn_edge_softmax_bwd");
 }
 
-gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st,
-                                const float* perm_src, float* perm_dst, int64_t perm_stride, int64_t vals_stride,
-                                int64_t perm_src_stride) {
+gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st) {
     if (v.n == 0) return GNN_OK;
     Sched s = make_sched(v);
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
-    Perm pm;
-    if (perm_dst) {
-        pm.src = perm_src;
-        pm.src_stride = perm_src_stride ? perm_src_stride : heads;
-        pm.dst = perm_dst;
-        pm.stride = perm_stride;
-    }
-    const int64_t vs = vals_stride ? vals_stride : heads;
     GNN_HEADS_SWITCH(heads, {
-        hipLaunchKernelGGL((reduce_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, vals, vs, out, pm);
+        hipLaunchKernelGGL((reduce_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, vals, out);
     });
     return launch_status("gnn_edge_reduce");
-}
-
-bool sddmm_dot_heads_supported(int heads, int64_t d_head) {
-    return heads >= 2 && heads <= 8 && (d_head == 32 || d_head == 64 || d_head == 128 || d_head == 256);
-}
-
-gnn_status_t launch_sddmm_dot_heads(const AggView& v, const float* src_feat, int64_t ld_src, const float* dst_feat,
-                                    int64_t ld_dst, int heads, int64_t d_head, float* out, int64_t stride,
-                                    hipStream_t st) {
-    if (v.n == 0) return GNN_OK;
-    if (!sddmm_dot_heads_supported(heads, d_head) || ld_src % 4 || ld_dst % 4)
-        return fail(GNN_ERR_UNSUPPORTED, "SDDMM dot by head: d_head must be 32, 64, 128 or 256");
-    Sched s = make_sched(v);
-    const int hl = static_cast<int>(d_head / 4);
-    const int64_t slab_blocks = (sched_items(s) + (256 / hl) - 1) / (256 / hl);
-    const dim3 grid(static_cast<unsigned>(slab_blocks * heads));
-#define GNN_DOTH(HLv)                                                                                     \
-    hipLaunchKernelGGL((sddmm_dot_heads_kernel<HLv, float>), grid, dim3(256), 0, st, s, slab_blocks, src_feat, \
-                       ld_src, dst_feat, ld_dst, d_head, stride, out)
-    switch (hl) {
-        case 8: GNN_DOTH(8); break;
-        case 16: GNN_DOTH(16); break;
-        case 32: GNN_DOTH(32); break;
-        default: GNN_DOTH(64); break;
-    }
-#undef GNN_DOTH
-    return launch_status("SDDMM dot by head");
 }
 
 gnn_status_t launch_gat_scores(int64_t n, const float* Hp, int heads, int64_t d_head, const float* a_src,

@@ -68,6 +68,7 @@ struct Graph {
     int64_t* col_ptr = nullptr;   // [n+1]
     int32_t* csc_row = nullptr;   // [nnz]
     int32_t* csc_eid = nullptr;   // [nnz]
+    int32_t* csr_cpos = nullptr;  // [nnz] CSC slot of each CSR edge (the inverse of csc_eid)
     RowPlan plan[2];              // 0: CSR, 1: CSC
     std::vector<void*> allocations;
 };
@@ -148,25 +149,22 @@ gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, con
 gnn_status_t launch_sddmm_dot(const AggView& v, const void* src_feat, int64_t ld_src, const void* dst_feat,
                               int64_t ld_dst, gnn_dtype_t dt, int heads, int64_t d_head, float* out, hipStream_t st);
 gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha, int heads, hipStream_t st);
-// SDDMM-add + LeakyReLU + edge softmax in one pass (S, D: [n, heads]); E_pre and alpha [nnz, heads]
+// GAT backward edge pass: records, the fused out-edge pass (dalpha, dE, dS, transposed aggregation + dS a_src),
+// hub fixups, and the in-edge sum dD with dD a_dst added to dH'
+bool gat_fused_bwd_supported(int heads, int64_t d_head);
+size_t gat_fused_bwd_partial_bytes(const RowPlan& csc_plan, int heads, int64_t d_head);
+gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const int32_t* cpos, int64_t nnz,
+                                  int heads, int64_t d_head, float slope, const float* Hp, const float* S,
+                                  const float* D, const float* M, const float* Z, const float* Y, const float* dY,
+                                  const float* a_src, const float* a_dst, float4* rec, float* dEh, float* dEc,
+                                  float* part, float* dS, float* dD, float* dHp, hipStream_t st);
+// SDDMM-add + LeakyReLU + edge softmax in one pass (S, D: [n, heads]); alpha and (optional) E_pre
+// [nnz, heads]; optional row_max, row_rsum [n, heads]: each row's score maximum and 1 / sum of exponentials
 gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float* D, int heads, float slope,
-                                  float* alpha, float* out_pre, hipStream_t st);
-// dalpha_head_stride > 0: dalpha is head-major, dalpha(e, k) = dalpha[k*stride + e]
-// out_stride: elements per dE record (0: heads); 2*heads also copies alpha after dE in each record
+                                  float* alpha, float* out_pre, float* row_max, float* row_rsum, hipStream_t st);
 gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha,
-                                     const float* pre, float slope, float* dE, int heads, hipStream_t st,
-                                     int64_t dalpha_head_stride = 0, int64_t out_stride = 0);
-// perm_dst != NULL: also writes perm_dst[k*perm_stride + j] = perm_src[eid(j)*heads + k] for every
-// position j of the view (CSR-order edge values re-laid head-major in this view's order)
-// vals_stride / perm_src_stride: elements per edge record of vals / perm_src (0: heads)
-gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st,
-                                const float* perm_src = nullptr, float* perm_dst = nullptr, int64_t perm_stride = 0,
-                                int64_t vals_stride = 0, int64_t perm_src_stride = 0);
-// SDDMM dot in one column slab per head, out head-major: out[k*stride + e]
-bool sddmm_dot_heads_supported(int heads, int64_t d_head);
-gnn_status_t launch_sddmm_dot_heads(const AggView& v, const float* src_feat, int64_t ld_src, const float* dst_feat,
-                                    int64_t ld_dst, int heads, int64_t d_head, float* out, int64_t stride,
-                                    hipStream_t st);
+                                     const float* pre, float slope, float* dE, int heads, hipStream_t st);
+gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st);
 
 gnn_status_t launch_gat_scores(int64_t n, const float* Hp, int heads, int64_t d_head, const float* a_src,
                                const float* a_dst, float* S, float* D, hipStream_t st);

@@ -217,7 +217,7 @@ size_t gnn_gat_saved_size(gnn_graph_t h, int heads, int64_t d_head) {
     if (!h || heads < 1 || d_head < 1) return 0;
     const Graph& g = h->g;
     const size_t n = g.n, e = g.nnz, hd = static_cast<size_t>(heads) * d_head;
-    return align_up(n * hd * 4) + 2 * align_up(n * heads * 4) + 2 * align_up(e * heads * 4);
+    return align_up(n * hd * 4) + 4 * align_up(n * heads * 4) + align_up(e * heads * 4);
 }
 
 size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_head) {
@@ -225,19 +225,22 @@ size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_
     const Graph& g = h->g;
     const size_t n = g.n, e = g.nnz;
     const int64_t hd = heads * d_head;
-    size_t t = align_up(2 * e * heads * 4) + 2 * align_up(n * heads * 4) + align_up(n * hd * 4);
-    t += align_up(head_colsum_partial_bytes(g.n, heads, d_head));
-    t += align_up(e * heads * 4);  // backward: head-major dalpha, then head-major alpha in CSC order
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
     gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
-    t += align_up(gemm);
-    t += align_up(std::max(spmm_partial_bytes(g.plan[0], hd), g.has_csc ? spmm_partial_bytes(g.plan[1], hd) : 0));
-    return t;
+    // forward: GEMM workspace, then the aggregation's hub-row partials
+    const size_t fwd = align_up(gemm) + align_up(spmm_partial_bytes(g.plan[0], hd));
+    // backward: dE (CSC order: per-head planes, then per-edge records), the
+    // per-destination records, dD, dS, dH', the CSC pass's chunk partials,
+    // the column-sum partials, the GEMM workspace
+    size_t bwd = 2 * align_up(e * heads * 4) + align_up(n * heads * 16) + 2 * align_up(n * heads * 4) +
+                 align_up(n * hd * 4) + align_up(head_colsum_partial_bytes(g.n, heads, d_head)) + align_up(gemm);
+    if (g.has_csc) bwd += align_up(gat_fused_bwd_partial_bytes(g.plan[1], heads, d_head));
+    return std::max(fwd, bwd);
 }
 
 namespace {
 struct GatSaved {
-    float *Hp, *S, *D, *Epre, *alpha;
+    float *Hp, *S, *D, *M, *Z, *alpha;
 };
 GatSaved carve_saved(const Graph& g, void* saved, int heads, int64_t d_head) {
     Carver c(saved);
@@ -246,7 +249,8 @@ GatSaved carve_saved(const Graph& g, void* saved, int heads, int64_t d_head) {
     s.Hp = static_cast<float*>(c.take(n * hd * 4));
     s.S = static_cast<float*>(c.take(n * heads * 4));
     s.D = static_cast<float*>(c.take(n * heads * 4));
-    s.Epre = static_cast<float*>(c.take(e * heads * 4));
+    s.M = static_cast<float*>(c.take(n * heads * 4));
+    s.Z = static_cast<float*>(c.take(n * heads * 4));
     s.alpha = static_cast<float*>(c.take(e * heads * 4));
     return s;
 }
@@ -267,81 +271,55 @@ gnn_status_t gnn_gat_layer_fwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     const int64_t hd = heads * d_head;
     GatSaved s = carve_saved(g, saved, heads, d_head);
     Carver c(ws);
-    c.take(static_cast<size_t>(g.nnz) * heads * 4);
-    c.take(static_cast<size_t>(g.n) * heads * 4);
-    c.take(static_cast<size_t>(g.n) * heads * 4);
-    c.take(static_cast<size_t>(g.n) * hd * 4);
-    c.take(head_colsum_partial_bytes(g.n, heads, d_head));
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
     gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
     void* gws = c.take(gemm);
     float* sws = static_cast<float*>(c.take(1));
-    // H' = X W;  S, D per-head scores;  E = LReLU(S[src] + D[dst]);  alpha = softmax;  Y = (G . alpha) H'
+    // H' = X W;  S, D per-head scores;  E = LReLU(S[src] + D[dst]);  alpha = softmax
+    // (keeping each row's maximum and 1/sum);  Y = (G . alpha) H'
     GNN_TRY(launch_gemm(0, 0, g.n, hd, d_in, X, GNN_F32, d_in, W, GNN_F32, hd, s.Hp, GNN_F32, hd, gws, gemm, st));
     GNN_TRY(launch_gat_scores(g.n, s.Hp, heads, d_head, a_src, a_dst, s.S, s.D, st));
-    GNN_TRY(launch_gat_attention(csr_view(g), s.S, s.D, heads, slope, s.alpha, s.Epre, st));
+    GNN_TRY(launch_gat_attention(csr_view(g), s.S, s.D, heads, slope, s.alpha, nullptr, s.M, s.Z, st));
     return launch_spmm(csr_view(g), g.dinv, GNN_W_EDGE, s.alpha, heads, s.Hp, GNN_F32, hd, Y, GNN_F32, hd, hd, 0,
                        Rank1Epilogue{}, sws, st);
 }
 
 gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, const float* W, const float* a_src,
-                               const float* a_dst, int heads, int64_t d_head, float slope, const float* dY,
-                               const void* saved, float* dX, float* dW, float* da_src, float* da_dst, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               const float* a_dst, int heads, int64_t d_head, float slope, const float* Y,
+                               const float* dY, const void* saved, float* dX, float* dW, float* da_src,
+                               float* da_dst, void* ws, size_t ws_bytes, void* stream) {
     GNN_REQUIRE(h, "gnn_gat_layer_bwd: graph handle is NULL");
     const Graph& g = h->g;
     GNN_REQUIRE(d_in >= 1 && heads >= 1 && d_head >= 1, "gnn_gat_layer_bwd: sizes must be >= 1");
     GNN_REQUIRE(dW && da_src && da_dst, "gnn_gat_layer_bwd: NULL gradient pointer");
-    GNN_REQUIRE(g.n == 0 || (X && W && a_src && a_dst && dY && saved), "gnn_gat_layer_bwd: NULL pointer");
+    GNN_REQUIRE(g.n == 0 || (X && W && a_src && a_dst && Y && dY && saved), "gnn_gat_layer_bwd: NULL pointer");
     if (!g.has_csc) return fail(GNN_ERR_GRAPH, "gnn_gat_layer_bwd: the graph needs the CSC view");
+    if (!gat_fused_bwd_supported(heads, d_head))
+        return fail(GNN_ERR_UNSUPPORTED, "gnn_gat_layer_bwd: needs 1, 2, 4 or 8 heads and d_head a power of two "
+                                         "from 4 to 256");
     const size_t need = gnn_gat_workspace_size(h, d_in, heads, d_head);
     if (ws_bytes < need || (!ws && need))
         return fail(GNN_ERR_WORKSPACE, "gnn_gat_layer_bwd: workspace smaller than gnn_gat_workspace_size()");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t hd = heads * d_head;
+    const size_t n = g.n, e = g.nnz;
     GatSaved s = carve_saved(g, const_cast<void*>(saved), heads, d_head);
     Carver c(ws);
-    float* dEb = static_cast<float*>(c.take(2 * static_cast<size_t>(g.nnz) * heads * 4));  // [nnz][dE | alpha]
-    float* dD = static_cast<float*>(c.take(static_cast<size_t>(g.n) * heads * 4));
-    float* dS = static_cast<float*>(c.take(static_cast<size_t>(g.n) * heads * 4));
-    float* dHp = static_cast<float*>(c.take(static_cast<size_t>(g.n) * hd * 4));
+    float* dEh = static_cast<float*>(c.take(e * heads * 4));
+    float* dEc = static_cast<float*>(c.take(e * heads * 4));
+    float4* rec = static_cast<float4*>(c.take(n * heads * 16));
+    float* dD = static_cast<float*>(c.take(n * heads * 4));
+    float* dS = static_cast<float*>(c.take(n * heads * 4));
+    float* dHp = static_cast<float*>(c.take(n * hd * 4));
     float* cps = static_cast<float*>(c.take(head_colsum_partial_bytes(g.n, heads, d_head)));
-    float* hm = static_cast<float*>(c.take(static_cast<size_t>(g.nnz) * heads * 4));
+    float* part = static_cast<float*>(c.take(gat_fused_bwd_partial_bytes(g.plan[1], heads, d_head)));
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
     gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
     void* gws = c.take(gemm);
-    float* sws = static_cast<float*>(c.take(1));
-    const AggView csr = csr_view(g), csc = csc_view(g);
-    Rank1Epilogue r1;
-    r1.a = dS;
-    r1.va = a_src;
-    r1.b = dD;
-    r1.vb = a_dst;
-    // Per-head column slabs when H' and dY outgrow the memory-side cache: the
-    // SDDMM dot runs one head at a time into a head-major dalpha plane set,
-    // and alpha is re-laid head-major in CSC order (inside the out-edge sum,
-    // which walks the CSC view anyway) so the transposed SpMM reads one
-    // contiguous weight stream per head instead of gathering through eid.
-    const bool by_head = sddmm_dot_heads_supported(heads, d_head) && column_slabs_pay(g.n, hd * 4);
-    if (by_head) {
-        // dalpha = dY[dst] . H'[src];  dE = alpha (dalpha - P) * LReLU'
-        GNN_TRY(launch_sddmm_dot_heads(csr, s.Hp, hd, dY, hd, heads, d_head, hm, g.nnz, st));
-        // records [dE | alpha] per edge: the out-edge sum below gathers both in one read
-        GNN_TRY(launch_edge_softmax_bwd(csr, s.alpha, hm, s.Epre, slope, dEb, heads, st, g.nnz, 2 * heads));
-        // dD = in-edge sums, dS = out-edge sums (+ alpha re-laid, overwriting dalpha)
-        GNN_TRY(launch_edge_reduce(csr, dEb, heads, dD, st, nullptr, nullptr, 0, 2 * heads));
-        GNN_TRY(launch_edge_reduce(csc, dEb, heads, dS, st, dEb + heads, hm, g.nnz, 2 * heads, 2 * heads));
-        // dH' = (G . alpha)^T dY + dS a_src + dD a_dst
-        GNN_TRY(launch_spmm(csc, g.dinv, GNN_W_EDGE, hm, heads, dY, GNN_F32, hd, dHp, GNN_F32, hd, hd, 0, r1, sws,
-                            st, MaskEpilogue{}, g.nnz));
-    } else {
-        GNN_TRY(launch_sddmm_dot(csr, s.Hp, hd, dY, hd, GNN_F32, heads, d_head, dEb, st));
-        GNN_TRY(launch_edge_softmax_bwd(csr, s.alpha, dEb, s.Epre, slope, dEb, heads, st));
-        GNN_TRY(launch_edge_reduce(csr, dEb, heads, dD, st));
-        GNN_TRY(launch_edge_reduce(csc, dEb, heads, dS, st));
-        GNN_TRY(launch_spmm(csc, g.dinv, GNN_W_EDGE, s.alpha, heads, dY, GNN_F32, hd, dHp, GNN_F32, hd, hd, 0, r1,
-                            sws, st));
-    }
+    // dalpha, dE, dS and (G . alpha)^T dY + dS a_src in one pass over the
+    // out-edges; dD and its dD a_dst term in one pass over the in-edges
+    GNN_TRY(launch_gat_bwd_fused(csr_view(g), csc_view(g), g.csr_cpos, g.nnz, heads, d_head, slope, s.Hp, s.S, s.D,
+                                 s.M, s.Z, Y, dY, a_src, a_dst, rec, dEh, dEc, part, dS, dD, dHp, st));
     // da_src = sum_v dS[v] H'[v], da_dst = sum_v dD[v] H'[v] per head
     GNN_TRY(launch_head_colsum(g.n, dS, dD, s.Hp, heads, d_head, da_src, da_dst, cps, st));
     // dW = X^T dH',  dX = dH' W^T

@@ -62,7 +62,7 @@ _SIGS = {
     "gnn_gat_saved_size": ("PiI", "S"),
     "gnn_gat_workspace_size": ("PIiI", "S"),
     "gnn_gat_layer_fwd": ("PPIPPPiIFPPPSP", "i"),
-    "gnn_gat_layer_bwd": ("PPIPPPiIFPPPPPPPSP", "i"),
+    "gnn_gat_layer_bwd": ("PPIPPPiIFPPPPPPPPSP", "i"),
 }
 _CT = {"P": C.c_void_p, "I": C.c_int64, "i": C.c_int, "U": C.c_uint32, "Q": C.c_uint64, "F": C.c_float,
        "D": C.c_double, "S": C.c_size_t}
@@ -400,26 +400,28 @@ def gnn_gat_layer_fwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, Y, sav
     return Y
 
 
-def gnn_gat_layer_bwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, dY, saved, dW, da_src, da_dst, dX=None,
-                      ws=None):
+def gnn_gat_layer_bwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, Y, dY, saved, dW, da_src, da_dst,
+                      dX=None, ws=None):
     d_in = X.shape[1]
     if ws is None:
         ws = _ws(gnn_gat_workspace_size(g, d_in, heads, d_head), X.device)
-    _check(lib().gnn_gat_layer_bwd(g.h, _p(X), d_in, _p(W), _p(a_src), _p(a_dst), heads, d_head, float(slope), _p(dY),
-                                   _p(saved), _p(dX), _p(dW), _p(da_src), _p(da_dst), _p(ws), ws.numel(), _stream()))
+    _check(lib().gnn_gat_layer_bwd(g.h, _p(X), d_in, _p(W), _p(a_src), _p(a_dst), heads, d_head, float(slope), _p(Y),
+                                   _p(dY), _p(saved), _p(dX), _p(dW), _p(da_src), _p(da_dst), _p(ws), ws.numel(),
+                                   _stream()))
     return dX, dW, da_src, da_dst
 
 
 def gat_saved_views(g: Graph, saved, heads, d_head):
-    """Views (H', S, D, E_pre, alpha) into a GAT forward's saved buffer (the
-    same 256-byte aligned slices the library carves)."""
+    """Views (H', S, D, M, Z, alpha) into a GAT forward's saved buffer (the
+    same 256-byte aligned slices the library carves): M and Z are each
+    destination's softmax maximum and 1 / sum of exponentials per head."""
     f = saved.view(torch.float32) if saved.dtype == torch.uint8 else saved
     al = lambda b: (b + 255) // 256 * 256
     n, e, hd = g.n, g.nnz, heads * d_head
     off = 0
     out = []
     for count, shape in ((n * hd, (n, hd)), (n * heads, (n, heads)), (n * heads, (n, heads)),
-                         (e * heads, (e, heads)), (e * heads, (e, heads))):
+                         (n * heads, (n, heads)), (n * heads, (n, heads)), (e * heads, (e, heads))):
         out.append(f[off // 4: off // 4 + count].view(*shape))
         off += al(count * 4)
     return tuple(out)

@@ -119,7 +119,7 @@ class GatLayer:
 
     def backward(self, need_dX=True):
         return gnnmp.gnn_gat_layer_bwd(self.g, self.X, self.W, self.a_src, self.a_dst, self.heads, self.d_head,
-                                       self.slope, self.dY, self.saved, self.dW, self.da_src, self.da_dst,
+                                       self.slope, self.Y, self.dY, self.saved, self.dW, self.da_src, self.da_dst,
                                        dX=self.dX if need_dX else None, ws=self.ws)
 
     def step(self):

@@ -90,3 +90,23 @@ def sub_rows(og, rows):
     eids = np.concatenate([np.arange(og.row_ptr[v], og.row_ptr[v + 1]) for v in rows]) if rows.size else np.zeros(0, np.int64)
     dst = np.repeat(rows.astype(np.int32), lens)
     return oracle.OracleGraph(rows.size, rp, og.col[eids].astype(np.int32), dst), eids
+
+
+def softmax_row_stats(og, E):
+    """Per destination row and head, the maximum M of the scores E over the
+    row's in-edges and Z = 1 / sum exp(E - M) (float64; rows without in-edges
+    get M = -inf, Z = inf), so that alpha = exp(E - M[dst]) * Z[dst]."""
+    E = np.asarray(E, np.float64)
+    n, h = og.n, E.shape[1]
+    deg = np.diff(og.row_ptr)
+    M = np.full((n, h), -np.inf)
+    has = deg > 0
+    if og.nnz:
+        M[has] = np.maximum.reduceat(E, og.row_ptr[:-1][has], axis=0)
+    row = np.repeat(np.arange(n), deg)  # CSR row of each edge slot
+    ex = np.exp(E - M[row])
+    s = np.zeros((n, h))
+    np.add.at(s, row, ex)
+    with np.errstate(divide="ignore"):
+        Z = 1.0 / s
+    return M, Z

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from oracle.graph import build_graph
-from parity import RTOL16, RTOL32, bf16_values, check_close, from_dev, sub_rows, to_dev
+from parity import RTOL16, RTOL32, bf16_values, check_close, from_dev, softmax_row_stats, sub_rows, to_dev
 from sparse_message_passing_amd import gnnmp, synth
 
 pytestmark = pytest.mark.gpu
@@ -156,7 +156,7 @@ def test_c3_gat_forward_sampled(c3):
     Y = torch.empty((og.n, h * dh), device="cuda")
     saved = torch.empty(gnnmp.gnn_gat_saved_size(g, h, dh), dtype=torch.uint8, device="cuda")
     gnnmp.gnn_gat_layer_fwd(g, to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d), h, dh, slope, Y, saved)
-    Hp_d, S_d, D_d, Ep_d, al_d = gnnmp.gat_saved_views(g, saved, h, dh)
+    Hp_d, S_d, D_d, M_d, Z_d, al_d = gnnmp.gat_saved_views(g, saved, h, dh)
     rows = sample_rows(og, 1024, 3)
     sg, eids = sub_rows(og, rows)
     # every node the sampled rows touch, and the sub-graph in that local numbering
@@ -176,9 +176,13 @@ def test_c3_gat_forward_sampled(c3):
     Ep, E = oracle.sddmm_add(loc, S, D, slope)
     mE = mS[loc.col] + mD[loc.dst]
     ed = torch.from_numpy(eids).cuda()
-    check_close(from_dev(Ep_d[ed]), Ep, mE, what="C3 E_pre")
+    rowmax_v = np.maximum.reduceat(mE, loc.row_ptr[:-1], axis=0)
+    M_ref, Z_ref = softmax_row_stats(loc, E)
+    rd = torch.from_numpy(rows.astype(np.int64)).cuda()
+    check_close(from_dev(M_d[rd]), M_ref, rowmax_v, what="C3 softmax row maximum")
+    check_close(from_dev(Z_d[rd]), Z_ref, Z_ref * (2 * rowmax_v + 1), what="C3 softmax 1/sum")
     alpha = oracle.to_f32(oracle.edge_softmax(loc, E))
-    rowmax = np.maximum.reduceat(mE, loc.row_ptr[:-1], axis=0)[np.repeat(np.arange(loc.n), np.diff(loc.row_ptr))]
+    rowmax = rowmax_v[np.repeat(np.arange(loc.n), np.diff(loc.row_ptr))]
     m_al = alpha * (2 * rowmax + 1)
     check_close(from_dev(al_d[ed]), alpha, m_al, what="C3 alpha")
     ref = oracle.spmm(loc, Hp, alpha, h)

@@ -9,7 +9,8 @@ import pytest
 import torch
 
 import oracle
-from parity import (RTOL16, RTOL32, check_close, from_dev, graph_pair, hub_edges, rmat_graph, to_dev)
+from parity import (RTOL16, RTOL32, check_close, from_dev, graph_pair, hub_edges, rmat_graph, softmax_row_stats,
+                    to_dev)
 from sparse_message_passing_amd import gnnmp, synth
 from sparse_message_passing_amd.step import GcnStack
 
@@ -268,7 +269,7 @@ def test_gat_layer_fwd_bwd(gatg, heads, dh, din):
     Y = torch.empty((n, hd), device="cuda")
     saved = torch.empty(gnnmp.gnn_gat_saved_size(g, heads, dh), dtype=torch.uint8, device="cuda")
     gnnmp.gnn_gat_layer_fwd(g, Xd, Wd, asd, add, heads, dh, slope, Y, saved)
-    Hp, S, D, Ep, al = gnnmp.gat_saved_views(g, saved, heads, dh)
+    Hp, S, D, M, Z, al = gnnmp.gat_saved_views(g, saved, heads, dh)
     mHp = np.abs(X) @ np.abs(W)
     check_close(from_dev(Hp), fw["Hp"], mHp, what="H'")
     mS = oracle.gat_scores(mHp, np.abs(a_s), heads)
@@ -276,9 +277,15 @@ def test_gat_layer_fwd_bwd(gatg, heads, dh, din):
     check_close(from_dev(S), fw["S"], mS, what="S")
     check_close(from_dev(D), fw["D"], mD, what="D")
     mE = mS[og.col] + mD[og.dst]
-    check_close(from_dev(Ep), fw["E_pre"], mE, what="E_pre")
+    # each row's softmax maximum moves with the scores; 1 / sum by at most
+    # (1 / sum) * 2 max|dE| over the row, like alpha
+    M_ref, Z_ref = softmax_row_stats(og, fw["E"])
+    has = np.diff(og.row_ptr) > 0
+    rowmax_v = np.maximum.reduceat(mE, og.row_ptr[:-1], axis=0)
+    check_close(from_dev(M)[has], M_ref[has], rowmax_v[has], what="softmax row maximum")
+    check_close(from_dev(Z)[has], Z_ref[has], Z_ref[has] * (2 * rowmax_v[has] + 1), what="softmax 1/sum")
     # alpha moves by at most alpha * 2 max|dE| over the destination's in-edges
-    rowmax = np.maximum.reduceat(mE, og.row_ptr[:-1], axis=0)[og.dst]
+    rowmax = rowmax_v[og.dst]
     m_al = fw["alpha"] * (2 * rowmax + 1)
     check_close(from_dev(al), fw["alpha"], m_al, what="alpha")
     mY = oracle.spmm(og, mHp, m_al, heads) + oracle.spmm(og, np.abs(fw["Hp"]), fw["alpha"], heads)
@@ -292,16 +299,18 @@ def _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r):
     gradient checked element by element."""
     n, hd, din = og.n, heads * dh, X.shape[1]
     Xd, Wd, asd, add = to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d)
-    Hp, S, D, Ep, al = gnnmp.gat_saved_views(g, saved, heads, dh)
-    for view, key in zip((Hp, S, D, Ep, al), ("Hp", "S", "D", "E_pre", "alpha")):
-        view.copy_(to_dev(fw[key]))
+    Hp, S, D, M, Z, al = gnnmp.gat_saved_views(g, saved, heads, dh)
+    M_ref, Z_ref = softmax_row_stats(og, fw["E"])
+    for view, val in zip((Hp, S, D, M, Z, al), (fw["Hp"], fw["S"], fw["D"], M_ref, Z_ref, fw["alpha"])):
+        view.copy_(to_dev(val))
     dY = r.standard_normal((n, hd)).astype(np.float32)
     bw = oracle.gat_layer_bwd(og, fw, X, W, a_s, a_d, dY, heads, slope)
     dX = torch.empty((n, din), device="cuda")
     dW = torch.empty((din, hd), device="cuda")
     das = torch.empty((heads, dh), device="cuda")
     dad = torch.empty((heads, dh), device="cuda")
-    gnnmp.gnn_gat_layer_bwd(g, Xd, Wd, asd, add, heads, dh, slope, to_dev(dY), saved, dW, das, dad, dX=dX)
+    gnnmp.gnn_gat_layer_bwd(g, Xd, Wd, asd, add, heads, dh, slope, to_dev(fw["Y"]), to_dev(dY), saved, dW, das, dad,
+                            dX=dX)
     A = np.abs(fw["alpha"])
     m_dal = oracle.sddmm_dot(og, np.abs(dY), np.abs(fw["Hp"]), heads)
     m_dE = A * (m_dal + oracle.edge_reduce(og, A * m_dal)[og.dst])
@@ -319,11 +328,10 @@ def _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r):
 
 
 def test_gat_layer_bwd_by_head_slabs():
-    # H' and dY over 256 MB (300K rows x 4 heads x 64): the backward takes the
-    # per-head slab path (head-major dalpha, alpha re-laid in CSC order inside
-    # the out-edge sum, head-major weights in the transposed SpMM).  A hub
-    # with 5000 in-neighbours and ~5000 out-neighbours exercises the chunked
-    # and whole-workgroup rows of both views.
+    # H' and dY over 256 MB (300K rows x 4 heads x 64), the out-edge pass one
+    # head at a time.  A hub with 5000 in-neighbours and ~5000 out-neighbours
+    # exercises the chunked out-edge rows (partial rows summed afterwards) and
+    # the whole-workgroup rows of the in-edge sum.
     n, heads, dh, din, slope = 300_000, 4, 64, 32, 0.2
     s, t = hub_edges(n, 2_000_000, 5000, 43)
     s = np.concatenate([s, np.full(5000, 7, np.int32)])
@@ -347,5 +355,6 @@ def test_gat_bwd_requires_csc():
     a = torch.zeros((1, 64), device="cuda")
     saved = torch.zeros(gnnmp.gnn_gat_saved_size(g, 1, 64), dtype=torch.uint8, device="cuda")
     with pytest.raises(gnnmp.GnnError, match="CSC"):
-        gnnmp.gnn_gat_layer_bwd(g, X, W, a, a, 1, 64, 0.2, torch.zeros((100, 64), device="cuda"), saved,
+        gnnmp.gnn_gat_layer_bwd(g, X, W, a, a, 1, 64, 0.2, torch.zeros((100, 64), device="cuda"),
+                                torch.zeros((100, 64), device="cuda"), saved,
                                 torch.empty_like(W), torch.empty_like(a), torch.empty_like(a))
