@@ -254,7 +254,10 @@ def gatg():
     return graph_pair(s, t, 3000, False, csc=True)
 
 
-@pytest.mark.parametrize("heads,dh,din", [(4, 64, 256), (2, 32, 48), (1, 64, 64)])
+# every group width of the backward's out-edge pass (d_head/4 = 1 ... 64 lanes)
+# and every head count it instantiates
+@pytest.mark.parametrize("heads,dh,din", [(4, 64, 256), (2, 32, 48), (1, 64, 64), (8, 8, 32), (1, 4, 16),
+                                          (8, 16, 24), (2, 128, 64), (1, 256, 40)])
 def test_gat_layer_fwd_bwd(gatg, heads, dh, din):
     g, og = gatg
     n, hd = og.n, heads * dh

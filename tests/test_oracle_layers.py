@@ -119,6 +119,30 @@ def test_gat_bwd_finite_difference():
     assert np.allclose(oracle.edge_reduce(g, bw["dE"]), 0.0, atol=1e-12)
 
 
+def test_gat_softmax_term_is_row_product_and_row_stats_rebuild_alpha():
+    # The GPU backward takes the softmax backward's per-destination term
+    # P[v] = sum_in alpha dalpha as <dY[v], Y[v]> per head (Y[v] = sum_in
+    # alpha H'[u]) and forms alpha again from each row's maximum and 1/sum;
+    # both against the oracle's edge-sum order, in float64.
+    from parity import softmax_row_stats
+    g = graph(12, n=30, m=120, sym=False)
+    r = np.random.default_rng(13)
+    h, dh, din = 4, 3, 5
+    X = r.standard_normal((g.n, din))
+    W = r.standard_normal((din, h * dh))
+    a_s = r.standard_normal((h, dh))
+    a_d = r.standard_normal((h, dh))
+    dY = r.standard_normal((g.n, h * dh))
+    fw = oracle.gat_layer_fwd(g, X, W, a_s, a_d, h, 0.2, dt="f64")
+    bw = oracle.gat_layer_bwd(g, fw, X, W, a_s, a_d, dY, h, 0.2, dt="f64")
+    P_edges = oracle.edge_reduce(g, fw["alpha"] * bw["dalpha"])
+    P_rows = np.einsum("nkj,nkj->nk", dY.reshape(g.n, h, dh), fw["Y"].reshape(g.n, h, dh))
+    assert np.allclose(P_rows, P_edges, rtol=1e-12, atol=1e-12)
+    M, Z = softmax_row_stats(g, fw["E"])
+    assert np.array_equal(M[g.dst], np.maximum(M[g.dst], fw["E"]))  # M bounds every in-edge score
+    assert np.allclose(np.exp(fw["E"] - M[g.dst]) * Z[g.dst], fw["alpha"], rtol=1e-12, atol=0)
+
+
 def test_bf16_rounding_rne():
     x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -9, 1.0 + 2 ** -9, -2.5, 0.0], np.float32)
     y = oracle.to_bf16(x)
