@@ -230,6 +230,19 @@ def main():
         extra["gemm_q8_256x256_ms"] = round(q8_ms, 4)
         extra["gemm_q8_256x256_tops_incl_quantise"] = round(2.0 * g.n * d * d / (q8_ms * 1e-3) / 1e12, 2)
         extra["gemm_dW_256x256_tflops"] = round(2.0 * g.n * d * d / (dw_ms * 1e-3) / 1e12, 2)
+    if cfg["kind"] == "gat":
+        # the attention-gradient SDDMM dot as a primitive (f32), and Tango's
+        # variant on 8-bit codes (maxima + quantisation of both operands +
+        # the gather of 1-byte codes), on the layer's own H' and a dY
+        h, dh = cfg["heads"], cfg["d_head"]
+        Hp = runner.saved[:g.n * h * dh * 4].view(torch.float32).view(g.n, h * dh)
+        dYs = runner.dY
+        dal = torch.empty((g.nnz, h), device=dev)
+        extra["sddmm_dot_f32_ms"] = round(event_time(
+            lambda: gnnmp.gnn_sddmm(g, "dot", Hp, dYs, h, dh, dal), a.kernel_reps, stream), 4)
+        sws = torch.empty(gnnmp.lib().gnn_sddmm_q8_workspace_size(g.h, h * dh), dtype=torch.uint8, device=dev)
+        extra["sddmm_q8_ms"] = round(event_time(
+            lambda: gnnmp.gnn_sddmm_q8(g, Hp, dYs, h, dh, dal, seed=5, ws=sws), a.kernel_reps, stream), 4)
     if cfg["kind"] == "quant":
         # the same exchange with the dequantisation inside the gather, and the
         # backward exchange of the embedding gradients (also fused)

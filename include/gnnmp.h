@@ -212,6 +212,25 @@ gnn_status_t gnn_gemm_q8(int64_t M, int64_t N, int64_t K, const float* A, int64_
                          float* C, int64_t ldc, uint64_t seed, uint32_t stream_id, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* SDDMM dot on quantised inputs (Tango, SC'23, "SDDMM with on-the-fly
+ * dequantization": a product of two quantised values is the product of their
+ * codes times the product of their scales, so the dot runs on the 8-bit
+ * codes, which a random gather reads at a quarter of the bytes).  Both
+ * operands are quantised over the whole tensor exactly as gnn_gemm_q8
+ * quantises its operands: src_feat ([n, ld_src] f32) with stream_id,
+ * dst_feat ([n, ld_dst] f32) with stream_id + 1, counters (node, feature/4).
+ * out[e, k] = f32(sum_j q_src[u, k*d_head + j] * q_dst[v, k*d_head + j]) *
+ * (s_src * s_dst) for CSR edge e = u -> v (int32 sums, exact; bit-exact
+ * against any faithful implementation); out [nnz, heads] f32 in CSR order.
+ * d_head must be 16 times a power of two (16 ... 256) and heads * d_head
+ * <= 1024 (GNN_ERR_INVALID_ARG otherwise).  Workspace (both quantised
+ * copies, n x heads*d_head bytes each, and the scales):
+ * gnn_sddmm_q8_workspace_size(g, heads*d_head). */
+size_t gnn_sddmm_q8_workspace_size(gnn_graph_t g, int64_t d);
+gnn_status_t gnn_sddmm_q8(gnn_graph_t g, const float* src_feat, int64_t ld_src, const float* dst_feat,
+                          int64_t ld_dst, int heads, int64_t d_head, uint64_t seed, uint32_t stream_id, float* out,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Mean softmax cross-entropy over n rows of c logits and its gradient:
  *   loss = (1/n) sum_v [logsumexp(z_v) - z_v[y_v]],  dz = (softmax(z_v) - onehot(y_v)) / n.
  * logits [n, ld] f32, labels int32[n] in [0, c), loss: one device float,

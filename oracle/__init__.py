@@ -262,6 +262,25 @@ def gemm_q8(A, B, seed, stream=0):
     return (acc.astype(np.float32) * scale).astype(np.float32), qa, qb, sa, sb
 
 
+def sddmm_q8(g, src_feat, dst_feat, heads, seed, stream=0):
+    """Tango's SDDMM dot on quantised inputs ("SDDMM with on-the-fly
+    dequantization": a product of two quantised values is the product of the
+    codes times the product of the scales, so the dot runs on the codes):
+    src_feat quantised on `stream`, dst_feat on `stream + 1`, both as
+    quantize_sym8 over the whole tensor; for edge u -> v and head k the int8
+    products over the head's features summed exactly (int64 here),
+    out[e, k] = f32(acc) * (s_src * s_dst) in binary32."""
+    qs, ss = quantize_sym8(src_feat, seed, stream)
+    qd, sd = quantize_sym8(dst_feat, seed, stream + 1)
+    n, d = qs.shape
+    dh = d // heads
+    A = qs.astype(np.int64).reshape(n, heads, dh)
+    B = qd.astype(np.int64).reshape(qd.shape[0], heads, dh)
+    acc = np.einsum("ekj,ekj->ek", A[g.col], B[g.dst])
+    scale = np.float32(ss) * np.float32(sd)
+    return (acc.astype(np.float32) * scale).astype(np.float32), qs, qd, ss, sd
+
+
 def dequantize(packed, scale, zero, rows, d, bits, H_out):
     """Writes the dequantised rows into H_out (float32 [n, d]) in place."""
     packed = _c(packed, np.uint8)

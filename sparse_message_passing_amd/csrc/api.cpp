@@ -458,6 +458,29 @@ gnn_status_t gnn_gemm_q8(int64_t M, int64_t N, int64_t K, const float* A, int64_
     return launch_gemm_q8(M, N, K, A, lda, B, ldb, C, ldc, seed, stream_id, ws, static_cast<hipStream_t>(stream));
 }
 
+size_t gnn_sddmm_q8_workspace_size(gnn_graph_t h, int64_t d) {
+    if (!h || d < 0) return 0;
+    return sddmm_q8_ws_bytes(h->g.n, d);
+}
+
+gnn_status_t gnn_sddmm_q8(gnn_graph_t h, const float* src_feat, int64_t ld_src, const float* dst_feat,
+                          int64_t ld_dst, int heads, int64_t d_head, uint64_t seed, uint32_t stream_id, float* out,
+                          void* ws, size_t ws_bytes, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_sddmm_q8"));
+    const Graph& g = h->g;
+    GNN_REQUIRE(heads >= 1 && d_head >= 1, "gnn_sddmm_q8: heads and d_head must be >= 1");
+    GNN_REQUIRE(sddmm_q8_supported(heads, d_head),
+                "gnn_sddmm_q8: d_head must be 16 times a power of two (16 ... 256) and heads * d_head <= 1024");
+    const int64_t d = heads * d_head;
+    GNN_REQUIRE(ld_src >= d && ld_dst >= d, "gnn_sddmm_q8: leading dimension too small");
+    GNN_REQUIRE(g.n == 0 || (src_feat && dst_feat && out), "gnn_sddmm_q8: NULL pointer");
+    if (g.n == 0) return GNN_OK;
+    const size_t need = sddmm_q8_ws_bytes(g.n, d);
+    if (!ws || ws_bytes < need) return fail(GNN_ERR_WORKSPACE, "gnn_sddmm_q8: workspace too small");
+    return launch_sddmm_q8(csr_view(g), src_feat, ld_src, dst_feat, ld_dst, heads, d_head, seed, stream_id, out, ws,
+                           static_cast<hipStream_t>(stream));
+}
+
 gnn_status_t gnn_quant_stats(gnn_graph_t h, const float* edge_w, const float* H, int64_t ldh, int64_t d,
                              const int32_t* rows, int64_t n_rows, float* beta, float* range, void* stream) {
     GNN_TRY(check_graph(h, "gnn_quant_stats"));

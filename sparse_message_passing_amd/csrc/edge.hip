@@ -180,6 +180,58 @@ __global__ __launch_bounds__(256) void sddmm_dot_kernel(Sched s, const T* src, i
 }
 
 // ---------------------------------------------------------------------------
+// SDDMM dot on 8-bit codes (Tango: the dot of two quantised rows is the dot
+// of their codes times the product of the scales).  A group of LQ lanes per
+// row, each lane 16 code bytes of the row (four v_dot4 steps, int32 sums,
+// exact); the HQ = d_head/16 lanes of a head are summed with a butterfly and
+// the head's first lane writes f32(sum) * (s_src * s_dst).  A gathered row is
+// d bytes instead of 4d.
+// ---------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ int group_isum(int v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+    return v;
+}
+
+template <int LQ, int HQ>
+__global__ __launch_bounds__(256) void sddmm_q8_kernel(Sched s, const int8_t* src, const int8_t* dst, int64_t d,
+                                                       int heads, const float* sc, float* out) {
+    const int lane = threadIdx.x % LQ;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * (256 / LQ) + threadIdx.x / LQ;
+    int64_t v, eb, ee;
+    if (!work_item(s, gid, v, eb, ee)) return;
+    const bool act = static_cast<int64_t>(lane) * 16 < d;  // lanes past the row's d/16 contribute zeros
+    const int64_t f = static_cast<int64_t>(lane) * 16;
+    const int4 zero4 = make_int4(0, 0, 0, 0);
+    const int4 dv = act ? *reinterpret_cast<const int4*>(dst + v * d + f) : zero4;
+    const int head = lane / HQ;
+    const float scale = __fmul_rn(sc[0], sc[1]);
+    for (int64_t e0 = eb; e0 < ee; e0 += LQ) {
+        const int cnt = static_cast<int>(min(static_cast<int64_t>(LQ), ee - e0));
+        const int u_my = lane < cnt ? s.idx[e0 + lane] : 0;
+        for (int j = 0; j < cnt; j += 4) {
+            int4 x[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int u = group_bcast<LQ>(u_my, j + q < cnt ? j + q : j);
+                x[q] = act ? *reinterpret_cast<const int4*>(src + static_cast<int64_t>(u) * d + f) : zero4;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int p = __builtin_amdgcn_sdot4(x[q].x, dv.x, 0, false);
+                p = __builtin_amdgcn_sdot4(x[q].y, dv.y, p, false);
+                p = __builtin_amdgcn_sdot4(x[q].z, dv.z, p, false);
+                p = __builtin_amdgcn_sdot4(x[q].w, dv.w, p, false);
+                p = group_isum<HQ>(p);
+                if (act && j + q < cnt && (lane % HQ) == 0)
+                    out[(e0 + j + q) * heads + head] = __fmul_rn(static_cast<float>(p), scale);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // edge softmax and its backward: per-row groups for rows of degree <=
 // kBlockRow, one workgroup per longer row
 // ---------------------------------------------------------------------------
@@ -696,6 +748,60 @@ gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, con
     GNN_HEADS_SWITCH(heads, hipLaunchKernelGGL((sddmm_add_kernel<H>), dim3(blocks), dim3(256), 0, st, s, S, lds, D,
                                                ldd, act ? slope : 0.0f, act, out, out_pre));
     return launch_status("gnn_sddmm(add)");
+}
+
+bool sddmm_q8_supported(int heads, int64_t d_head) {
+    const int64_t hq = d_head / 16;
+    return heads >= 1 && d_head % 16 == 0 && hq >= 1 && hq <= 16 && (hq & (hq - 1)) == 0 && heads * d_head <= 1024;
+}
+
+size_t sddmm_q8_ws_bytes(int64_t n, int64_t d) {
+    return 2 * align_up(static_cast<size_t>(n) * d) + align_up(1024 * 4) + align_up(4 * 4);
+}
+
+gnn_status_t launch_sddmm_q8(const AggView& v, const float* src, int64_t ld_src, const float* dst, int64_t ld_dst,
+                             int heads, int64_t d_head, uint64_t seed, uint32_t stream_id, float* out, void* ws,
+                             hipStream_t st) {
+    const int64_t n = v.n, d = heads * d_head;
+    if (n == 0) return GNN_OK;
+    char* w = static_cast<char*>(ws);
+    int8_t* qs = reinterpret_cast<int8_t*>(w);
+    w += align_up(static_cast<size_t>(n) * d);
+    int8_t* qd = reinterpret_cast<int8_t*>(w);
+    w += align_up(static_cast<size_t>(n) * d);
+    float* partial = reinterpret_cast<float*>(w);
+    w += align_up(1024 * 4);
+    float* stat = reinterpret_cast<float*>(w);  // [max|src|, max|dst|, s_src, s_dst]
+    // tensor-level scales and the sequential quantisation pass over each operand
+    GNN_TRY(launch_absmax(src, ld_src, n, d, partial, stat + 0, st));
+    GNN_TRY(launch_absmax(dst, ld_dst, n, d, partial + 512, stat + 1, st));
+    GNN_TRY(launch_quantize_sym8(src, ld_src, n, d, stat + 0, seed, stream_id, qs, d, 0, stat + 2, st));
+    GNN_TRY(launch_quantize_sym8(dst, ld_dst, n, d, stat + 1, seed, stream_id + 1, qd, d, 0, stat + 3, st));
+    Sched s = make_sched(v);
+    const int64_t need = (d + 15) / 16;
+    const int lq = need <= 4 ? 4 : need <= 8 ? 8 : need <= 16 ? 16 : need <= 32 ? 32 : 64;
+    const int hq = static_cast<int>(d_head / 16);
+    const int64_t blocks = (sched_items(s) + (256 / lq) - 1) / (256 / lq);
+#define GNN_Q8(L, HQv) \
+    hipLaunchKernelGGL((sddmm_q8_kernel<L, HQv>), dim3(blocks), dim3(256), 0, st, s, qs, qd, d, heads, stat + 2, out)
+#define GNN_Q8_H(L)                                           \
+    switch (hq) {                                             \
+        case 1: GNN_Q8(L, 1); break;                          \
+        case 2: GNN_Q8(L, 2); break;                          \
+        case 4: GNN_Q8(L, 4); break;                          \
+        case 8: if (L >= 8) { GNN_Q8(L, 8); } break;          \
+        default: if (L >= 16) { GNN_Q8(L, 16); } break;       \
+    }
+    switch (lq) {
+        case 4: GNN_Q8_H(4) break;
+        case 8: GNN_Q8_H(8) break;
+        case 16: GNN_Q8_H(16) break;
+        case 32: GNN_Q8_H(32) break;
+        default: GNN_Q8_H(64) break;
+    }
+#undef GNN_Q8_H
+#undef GNN_Q8
+    return launch_status("gnn_sddmm_q8");
 }
 
 gnn_status_t launch_sddmm_dot(const AggView& v, const void* src_feat, int64_t ld_src, const void* dst_feat,

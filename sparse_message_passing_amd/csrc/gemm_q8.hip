@@ -7,7 +7,8 @@
 // v_mfma_i32_16x16x64_i8 here (64 k values per instruction).
 //
 //  * the tensor-wide maxima |A|, |B| come from a two-stage max reduction
-//    (order free, so the result is exact and deterministic);
+//    (order free, so the result is exact and deterministic; a contiguous
+//    operand is read as one run of 16-byte loads);
 //  * the quantised copies are k-contiguous, rows padded with zero codes to a
 //    multiple of 64 k, so the GEMM needs no k bounds;
 //  * a 256-thread workgroup computes a 128 x 128 tile of C, its four waves
@@ -30,14 +31,38 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int QBM = 128, QBN = 128, QBK = 64, QPAD = 16;
 
+__device__ __forceinline__ float absmax4(float m, float4 v) {
+    return fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+}
+
 __global__ __launch_bounds__(256) void absmax_stage1(const float* X, int64_t ld, int64_t rows, int64_t cols,
                                                      float* partial) {
     __shared__ float sh[4];
     float m = 0.0f;
-    // rows dealt round-robin to the workgroups, columns across the threads
-    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-        const float* x = X + r * ld;
-        for (int64_t c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(x[c]));
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t nthr = static_cast<int64_t>(gridDim.x) * 256;
+    if (ld == cols && (reinterpret_cast<uintptr_t>(X) & 15) == 0) {
+        // one contiguous run of rows * cols floats: 16-byte loads, eight in
+        // flight per thread, then the tail
+        const int64_t total = rows * cols, n4 = total / 4;
+        const float4* X4 = reinterpret_cast<const float4*>(X);
+        int64_t i = tid;
+        for (; i + 7 * nthr < n4; i += 8 * nthr) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = X4[i + u * nthr];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) m = absmax4(m, v[u]);
+        }
+        for (; i < n4; i += nthr) m = absmax4(m, X4[i]);
+        for (int64_t j = n4 * 4 + tid; j < total; j += nthr) m = fmaxf(m, fabsf(X[j]));
+    } else {
+        // strided rows: dealt round-robin to the waves, columns across the lanes
+        const int lane = threadIdx.x & 63;
+        for (int64_t r = tid >> 6; r < rows; r += nthr >> 6) {
+            const float* x = X + r * ld;
+            for (int64_t c = lane; c < cols; c += 64) m = fmaxf(m, fabsf(x[c]));
+        }
     }
     m = group_max<64>(m);
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
@@ -157,6 +182,13 @@ __global__ __launch_bounds__(256) void gemm_q8_kernel(Q8Args g) {
 
 int64_t q8_padded_k(int64_t K) { return (K + QBK - 1) / QBK * QBK; }
 
+gnn_status_t launch_absmax(const float* X, int64_t ld, int64_t rows, int64_t cols, float* partial, float* out,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(absmax_stage1, dim3(512), dim3(256), 0, st, X, ld, rows, cols, partial);
+    hipLaunchKernelGGL(absmax_stage2, dim3(1), dim3(256), 0, st, partial, 512, out);
+    return launch_status("8-bit quantisation (maxima)");
+}
+
 size_t gemm_q8_ws_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t Kp = q8_padded_k(K);
     return align_up(static_cast<size_t>(M) * Kp) + align_up(static_cast<size_t>(N) * Kp) + align_up(1024 * 4) +
@@ -175,11 +207,8 @@ gnn_status_t launch_gemm_q8(int64_t M, int64_t N, int64_t K, const float* A, int
     w += align_up(1024 * 4);
     float* stat = reinterpret_cast<float*>(w);  // [max|A|, max|B|, s_A, s_B]
     // tensor-wide maxima (512 partial blocks per operand)
-    hipLaunchKernelGGL(absmax_stage1, dim3(512), dim3(256), 0, st, A, lda, M, K, partial);
-    hipLaunchKernelGGL(absmax_stage2, dim3(1), dim3(256), 0, st, partial, 512, stat + 0);
-    hipLaunchKernelGGL(absmax_stage1, dim3(512), dim3(256), 0, st, B, ldb, K, N, partial + 512);
-    hipLaunchKernelGGL(absmax_stage2, dim3(1), dim3(256), 0, st, partial + 512, 512, stat + 1);
-    GNN_TRY(launch_status("gnn_gemm_q8 (maxima)"));
+    GNN_TRY(launch_absmax(A, lda, M, K, partial, stat + 0, st));
+    GNN_TRY(launch_absmax(B, ldb, K, N, partial + 512, stat + 1, st));
     // quantised copies: A as is, B transposed, both k-contiguous with zero padding
     GNN_TRY(launch_quantize_sym8(A, lda, M, K, stat + 0, seed, stream_id, Aq, Kp, 0, stat + 2, st));
     GNN_TRY(launch_quantize_sym8(B, ldb, K, N, stat + 1, seed, stream_id + 1, Bq, Kp, 1, stat + 3, st));

@@ -133,7 +133,16 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
 gnn_status_t launch_quantize_sym8(const float* X, int64_t ldx, int64_t rows, int64_t cols, const float* mptr,
                                   uint64_t seed, uint32_t stream_id, int8_t* out, int64_t out_ld, int transpose,
                                   float* s_out, hipStream_t st);
+// max |X| over a rows x cols block: 512 partial maxima (partial[0..511]), then one
+gnn_status_t launch_absmax(const float* X, int64_t ld, int64_t rows, int64_t cols, float* partial, float* out,
+                           hipStream_t st);
 size_t gemm_q8_ws_bytes(int64_t M, int64_t N, int64_t K);
+// SDDMM dot on 8-bit codes (both operands quantised like the 8-bit GEMM's)
+bool sddmm_q8_supported(int heads, int64_t d_head);
+size_t sddmm_q8_ws_bytes(int64_t n, int64_t d);
+gnn_status_t launch_sddmm_q8(const AggView& v, const float* src, int64_t ld_src, const float* dst, int64_t ld_dst,
+                             int heads, int64_t d_head, uint64_t seed, uint32_t stream_id, float* out, void* ws,
+                             hipStream_t st);
 gnn_status_t launch_gemm_q8(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
                             float* C, int64_t ldc, uint64_t seed, uint32_t stream_id, void* ws, hipStream_t st);
 gnn_status_t launch_quant_stats(const AggView& v, const float* w, const float* H, int64_t ldh, int64_t d,

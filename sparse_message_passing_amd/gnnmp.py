@@ -44,6 +44,8 @@ _SIGS = {
     "gnn_gemm": ("iiIIIPiIPiIPiIPSP", "i"),
     "gnn_gemm_q8_workspace_size": ("III", "S"),
     "gnn_gemm_q8": ("IIIPIPIPIQUPSP", "i"),
+    "gnn_sddmm_q8_workspace_size": ("PI", "S"),
+    "gnn_sddmm_q8": ("PPIPIiIQUPPSP", "i"),
     "gnn_softmax_xent_workspace_size": ("I", "S"),
     "gnn_softmax_xent": ("PIIIPPPIPSP", "i"),
     "gnn_quantize": ("PIIPIiQUPPPP", "i"),
@@ -289,6 +291,16 @@ def gnn_gemm_q8(A, B, C, seed, stream_id=0, ws=None):
     _check(lib().gnn_gemm_q8(M, N, K, _p(A), _ld(A), _p(B), _ld(B), _p(C), _ld(C), int(seed), int(stream_id), _p(ws),
                              ws.numel(), _stream()))
     return C
+
+
+def gnn_sddmm_q8(g: Graph, src_feat, dst_feat, heads, d_head, out, seed, stream_id=0, ws=None):
+    """out[e, k] = dequant(q8(src_feat)[u, head k] . q8(dst_feat)[v, head k]):
+    Tango's SDDMM dot on 8-bit codes (f32 in and out)."""
+    if ws is None:
+        ws = _ws(lib().gnn_sddmm_q8_workspace_size(g.h, heads * d_head), src_feat.device)
+    _check(lib().gnn_sddmm_q8(g.h, _p(src_feat), _ld(src_feat), _p(dst_feat), _ld(dst_feat), heads, d_head,
+                              int(seed), int(stream_id), _p(out), _p(ws), ws.numel(), _stream()))
+    return out
 
 
 def gnn_quant_stats(g: Graph, H, rows, beta, rng, edge_w=None, d=None):

@@ -370,3 +370,20 @@ def test_c4_bf16_first_layer_and_aggregation_sampled(c4):
     gnnmp.gnn_spmm(g, Hd, Z)
     check_close(from_dev(Z)[rows], oracle.spmm(sg, H, w), oracle.spmm(sg, np.abs(H), np.abs(w)), rtol=RTOL16,
                 bf16_out=True, what="C4 aggregation d=256 (bf16)")
+
+
+def test_c3_sddmm_q8_sampled_bit_exact(c3):
+    # Tango's quantised SDDMM dot at the full 2^21-node size: both 2 GB
+    # operands quantised over the whole tensor, sampled rows bit-exact
+    g, og, inp = c3
+    cfg = synth.CONFIGS[3]
+    h, dh = cfg["heads"], cfg["d_head"]
+    S = synth.normal((og.n, h * dh), 3101)
+    D = synth.normal((og.n, h * dh), 3102)
+    out = torch.empty((og.nnz, h), device="cuda")
+    gnnmp.gnn_sddmm_q8(g, to_dev(S), to_dev(D), h, dh, out, seed=31, stream_id=1)
+    rows = sample_rows(og, 512, 5)
+    sg, eids = sub_rows(og, rows)
+    ref, *_ = oracle.sddmm_q8(sg, S, D, h, seed=31, stream=1)
+    got = from_dev(out[torch.from_numpy(eids).cuda()])
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))

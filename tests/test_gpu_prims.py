@@ -641,3 +641,42 @@ def test_gemm_q8_zero_and_strided():
     gnnmp.gnn_gemm_q8(Ab[:, :40], Bb[:, :20], Cb[:, :20], seed=2)
     ref, *_ = oracle.gemm_q8(A, B[:40], seed=2)
     assert np.array_equal(from_dev(Cb[:, :20]).view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# Tango's SDDMM dot on 8-bit codes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("heads,dh", [(4, 64), (1, 16), (3, 16), (2, 128), (8, 32), (1, 256), (4, 256)])
+def test_sddmm_q8_bit_exact(heads, dh):
+    # codes, int32 sums and the binary32 dequantisation are fixed by the
+    # definition: every edge matches the oracle bit for bit (a hub with 2300
+    # in-edges exercises the chunked rows)
+    s, t = hub_edges(3000, 30000, 2300, heads * dh)
+    g, og = graph_pair(s, t, 3000, False, csc=False)
+    r = np.random.default_rng(heads + dh)
+    S = (r.standard_normal((og.n, heads * dh)) * r.uniform(0.5, 2, (og.n, 1))).astype(np.float32)
+    D = r.standard_normal((og.n, heads * dh)).astype(np.float32)
+    ref, *_ = oracle.sddmm_q8(og, S, D, heads, seed=77, stream=2)
+    out = torch.full((og.nnz, heads), float("nan"), device="cuda")
+    gnnmp.gnn_sddmm_q8(g, to_dev(S), to_dev(D), heads, dh, out, seed=77, stream_id=2)
+    assert np.array_equal(from_dev(out).view(np.uint32), ref.view(np.uint32))
+
+
+def test_sddmm_q8_strided_zero_and_unsupported():
+    s, t = hub_edges(500, 4000, 300, 5)
+    g, og = graph_pair(s, t, 500, False, csc=False)
+    r = np.random.default_rng(8)
+    S = r.standard_normal((og.n, 64)).astype(np.float32)
+    D = r.standard_normal((og.n, 64)).astype(np.float32)
+    Sb = torch.zeros((og.n, 80), device="cuda")
+    Sb[:, :64] = to_dev(S)
+    Db = torch.zeros((og.n, 72), device="cuda")
+    Db[:, :64] = to_dev(D)
+    out = torch.empty((og.nnz, 2), device="cuda")
+    gnnmp.gnn_sddmm_q8(g, Sb[:, :64], Db[:, :64], 2, 32, out, seed=3)
+    ref, *_ = oracle.sddmm_q8(og, S, D, 2, seed=3)
+    assert np.array_equal(from_dev(out).view(np.uint32), ref.view(np.uint32))
+    gnnmp.gnn_sddmm_q8(g, torch.zeros((og.n, 64), device="cuda"), Db[:, :64], 2, 32, out, seed=3)
+    assert not from_dev(out).any()
+    with pytest.raises(gnnmp.GnnError, match="d_head"):
+        gnnmp.gnn_sddmm_q8(g, Sb[:, :48], Db[:, :48], 2, 24, out, seed=3)

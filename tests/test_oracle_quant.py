@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle.graph import build_graph
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
@@ -257,3 +258,57 @@ def test_q8_gemm_error_bound():
     bound = (np.abs(A) @ np.ones_like(B)) * sb + (np.ones_like(A) @ np.abs(B)) * sa + A.shape[1] * sa * sb
     ref = A.astype(np.float64) @ B
     assert np.all(np.abs(C - ref) <= bound + 1e-6 * np.abs(ref))
+
+
+# ---------------------------------------------------------------------------
+# Tango's SDDMM dot on quantised inputs
+# ---------------------------------------------------------------------------
+def _small_graph(seed, n=40, m=300):
+    r = np.random.default_rng(seed)
+    return build_graph(r.integers(0, n, m).astype(np.int32), r.integers(0, n, m).astype(np.int32), n, False)
+
+
+def test_sddmm_q8_integer_grid_is_exact_dot():
+    # integer features with max |x| = 127: scale 1, codes = values, and the
+    # quantised SDDMM is the exact SDDMM dot, per head, on every edge
+    g = _small_graph(60)
+    r = np.random.default_rng(61)
+    heads, dh = 3, 16
+    S = r.integers(-127, 128, (g.n, heads * dh)).astype(np.float32)
+    D = r.integers(-127, 128, (g.n, heads * dh)).astype(np.float32)
+    S[1, 2], D[4, 5] = 127, -127
+    out, qs, qd, ss, sd = oracle.sddmm_q8(g, S, D, heads, seed=7)
+    assert ss == 1.0 and sd == 1.0
+    ref = oracle.sddmm_dot(g, D, S, heads)  # out[e] = <S[src], D[dst]>
+    assert np.array_equal(out, ref.astype(np.float32))
+    # brute force over the edge list
+    for e in range(0, g.nnz, 37):
+        u, v = g.col[e], g.dst[e]
+        for k in range(heads):
+            sl = slice(k * dh, (k + 1) * dh)
+            assert out[e, k] == float(np.dot(S[u, sl].astype(np.int64), D[v, sl].astype(np.int64)))
+
+
+def test_sddmm_q8_streams_and_error_bound():
+    g = _small_graph(62)
+    r = np.random.default_rng(63)
+    heads, dh = 2, 32
+    S = r.standard_normal((g.n, heads * dh)).astype(np.float32)
+    D = r.standard_normal((g.n, heads * dh)).astype(np.float32)
+    out, qs, qd, ss, sd = oracle.sddmm_q8(g, S, D, heads, seed=9, stream=4)
+    # the operands' codes are quantize_sym8 on streams s and s + 1
+    q1, s1 = oracle.quantize_sym8(S, 9, 4)
+    q2, s2 = oracle.quantize_sym8(D, 9, 5)
+    assert np.array_equal(qs, q1) and np.array_equal(qd, q2) and ss == s1 and sd == s2
+    # |out - exact| <= sum_j (|a| s_D + |b| s_S + s_S s_D) per head, plus the final rounding
+    ref = oracle.sddmm_dot(g, D, S, heads)
+    aS = np.abs(S).reshape(g.n, heads, dh).sum(-1)
+    aD = np.abs(D).reshape(g.n, heads, dh).sum(-1)
+    bound = aS[g.col] * sd + aD[g.dst] * ss + dh * ss * sd
+    assert np.all(np.abs(out - ref) <= bound + 1e-6 * np.abs(ref))
+
+
+def test_sddmm_q8_zero_operand():
+    g = _small_graph(64)
+    out, qs, qd, ss, sd = oracle.sddmm_q8(g, np.zeros((g.n, 16), np.float32), np.ones((g.n, 16), np.float32), 1, 3)
+    assert ss == 0.0 and not out.any()
