@@ -224,11 +224,13 @@ def main():
         dw_ms = event_time(lambda: gnnmp.gnn_gemm(X, Z, dW, transA=True, ws=gws2), a.kernel_reps, stream)
         extra["gemm_dW_256x256_ms"] = round(dw_ms, 4)
         # Tango's quantisation-aware variant of the same update (maxima,
-        # stochastic 8-bit quantisation of both operands, int8 matrix cores)
-        qws = torch.empty(gnnmp.lib().gnn_gemm_q8_workspace_size(g.n, d, d), dtype=torch.uint8, device=dev)
-        q8_ms = event_time(lambda: gnnmp.gnn_gemm_q8(X, Wt, Z, seed=5, ws=qws), a.kernel_reps, stream)
-        extra["gemm_q8_256x256_ms"] = round(q8_ms, 4)
-        extra["gemm_q8_256x256_tops_incl_quantise"] = round(2.0 * g.n * d * d / (q8_ms * 1e-3) / 1e12, 2)
+        # stochastic 8-bit quantisation of both operands, int8 matrix cores):
+        # f32 in and out, so only on the f32 workload
+        if X.dtype == torch.float32:
+            qws = torch.empty(gnnmp.lib().gnn_gemm_q8_workspace_size(g.n, d, d), dtype=torch.uint8, device=dev)
+            q8_ms = event_time(lambda: gnnmp.gnn_gemm_q8(X, Wt, Z, seed=5, ws=qws), a.kernel_reps, stream)
+            extra["gemm_q8_256x256_ms"] = round(q8_ms, 4)
+            extra["gemm_q8_256x256_tops_incl_quantise"] = round(2.0 * g.n * d * d / (q8_ms * 1e-3) / 1e12, 2)
         extra["gemm_dW_256x256_tflops"] = round(2.0 * g.n * d * d / (dw_ms * 1e-3) / 1e12, 2)
     if cfg["kind"] == "gat":
         # the attention-gradient SDDMM dot as a primitive (f32), and Tango's

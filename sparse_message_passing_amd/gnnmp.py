@@ -126,6 +126,26 @@ def _dt(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _f32(*ts):
+    """Entry points whose C signature takes float*: refuse other dtypes before
+    any pointer reaches the library (a bf16 buffer read as float would run
+    past its end)."""
+    for t in ts:
+        if t is not None and not isinstance(t, int) and t.dtype != torch.float32:
+            raise TypeError(f"expected a float32 tensor, got {t.dtype}")
+
+
+def _i32(*ts):
+    for t in ts:
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError(f"expected an int32 tensor, got {t.dtype}")
+
+
+def _shape_at_least(t, rows, cols, what):
+    if t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{what}: expected at least [{rows}, {cols}], got {list(t.shape)}")
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -212,6 +232,7 @@ def gnn_spmm(g: Graph, X, Y, weights="gcn", heads=1, transpose=False, relu=False
         wmode, ew = {"gcn": GNN_W_GCN, "ones": GNN_W_ONES, "mean": GNN_W_MEAN}[weights], None
     else:
         wmode, ew = GNN_W_EDGE, weights
+        _f32(ew)
     need = lib().gnn_spmm_workspace_size(g.h, int(transpose), d)
     if ws is None:
         ws = _ws(need, X.device)
@@ -221,6 +242,7 @@ def gnn_spmm(g: Graph, X, Y, weights="gcn", heads=1, transpose=False, relu=False
 
 
 def gnn_edge_reduce(g: Graph, vals, out, by_src=False):
+    _f32(vals, out)
     _check(lib().gnn_edge_reduce(g.h, int(by_src), _p(vals), vals.shape[1], _p(out), _stream()))
     return out
 
@@ -228,17 +250,22 @@ def gnn_edge_reduce(g: Graph, vals, out, by_src=False):
 def gnn_sddmm(g: Graph, op, src_feat, dst_feat, heads, d_head, out, slope=float("nan"), out_pre=None):
     """op "add": out = LReLU(src[u,k] + dst[v,k]); op "dot": out = <src[u, head k], dst[v, head k]>."""
     opc = {"add": 0, "dot": 1}[op]
+    _f32(out, out_pre)
+    if op == "add":
+        _f32(src_feat, dst_feat)
     _check(lib().gnn_sddmm(g.h, opc, _p(src_feat), _ld(src_feat), _p(dst_feat), _ld(dst_feat), _dt(src_feat), heads,
                            d_head, float(slope), _p(out), _p(out_pre), _stream()))
     return out
 
 
 def gnn_edge_softmax(g: Graph, E, alpha):
+    _f32(E, alpha)
     _check(lib().gnn_edge_softmax(g.h, _p(E), _p(alpha), E.shape[1], _stream()))
     return alpha
 
 
 def gnn_edge_softmax_bwd(g: Graph, alpha, dalpha, dE, lrelu_pre=None, slope=0.0):
+    _f32(alpha, dalpha, dE, lrelu_pre)
     _check(lib().gnn_edge_softmax_bwd(g.h, _p(alpha), _p(dalpha), _p(lrelu_pre), float(slope), _p(dE),
                                       alpha.shape[1], _stream()))
     return dE
@@ -261,6 +288,8 @@ def gnn_gemm(A, B, C_, transA=False, transB=False, ws=None):
 
 def gnn_softmax_xent(logits, labels, loss, dlogits=None, ws=None):
     n, c = logits.shape
+    _f32(logits, loss, dlogits)
+    _i32(labels)
     if ws is None:
         ws = _ws(lib().gnn_softmax_xent_workspace_size(n), logits.device)
     _check(lib().gnn_softmax_xent(_p(logits), n, c, _ld(logits), _p(labels), _p(loss), _p(dlogits),
@@ -269,6 +298,8 @@ def gnn_softmax_xent(logits, labels, loss, dlogits=None, ws=None):
 
 
 def gnn_quantize(H, rows, bits, seed, packed, scale, zero, stream_id=0, d=None):
+    _f32(H, scale, zero)
+    _i32(rows)
     d = H.shape[1] if d is None else d
     _check(lib().gnn_quantize(_p(H), _ld(H), d, _p(rows), rows.numel(), bits, int(seed), int(stream_id), _p(packed),
                               _p(scale), _p(zero), _stream()))
@@ -276,6 +307,8 @@ def gnn_quantize(H, rows, bits, seed, packed, scale, zero, stream_id=0, d=None):
 
 
 def gnn_dequantize(packed, scale, zero, rows, bits, H, d=None):
+    _f32(H, scale, zero)
+    _i32(rows)
     d = H.shape[1] if d is None else d
     _check(lib().gnn_dequantize(_p(packed), _p(scale), _p(zero), rows.numel(), d, bits, _p(rows), _p(H), _ld(H),
                                 _stream()))
@@ -284,8 +317,11 @@ def gnn_dequantize(packed, scale, zero, rows, bits, H, d=None):
 
 def gnn_gemm_q8(A, B, C, seed, stream_id=0, ws=None):
     """C = dequant(q8(A) q8(B)): Tango's quantisation-aware GEMM (f32 in and out)."""
+    _f32(A, B, C)
     M, K = A.shape
     N = B.shape[1]
+    if B.shape[0] != K or tuple(C.shape) != (M, N):
+        raise ValueError("gnn_gemm_q8: shape mismatch")
     if ws is None:
         ws = _ws(lib().gnn_gemm_q8_workspace_size(M, N, K), A.device)
     _check(lib().gnn_gemm_q8(M, N, K, _p(A), _ld(A), _p(B), _ld(B), _p(C), _ld(C), int(seed), int(stream_id), _p(ws),
@@ -296,6 +332,10 @@ def gnn_gemm_q8(A, B, C, seed, stream_id=0, ws=None):
 def gnn_sddmm_q8(g: Graph, src_feat, dst_feat, heads, d_head, out, seed, stream_id=0, ws=None):
     """out[e, k] = dequant(q8(src_feat)[u, head k] . q8(dst_feat)[v, head k]):
     Tango's SDDMM dot on 8-bit codes (f32 in and out)."""
+    _f32(src_feat, dst_feat, out)
+    _shape_at_least(src_feat, g.n, heads * d_head, "gnn_sddmm_q8 src_feat")
+    _shape_at_least(dst_feat, g.n, heads * d_head, "gnn_sddmm_q8 dst_feat")
+    _shape_at_least(out, g.nnz, heads, "gnn_sddmm_q8 out")
     if ws is None:
         ws = _ws(lib().gnn_sddmm_q8_workspace_size(g.h, heads * d_head), src_feat.device)
     _check(lib().gnn_sddmm_q8(g.h, _p(src_feat), _ld(src_feat), _p(dst_feat), _ld(dst_feat), heads, d_head,
@@ -305,6 +345,8 @@ def gnn_sddmm_q8(g: Graph, src_feat, dst_feat, heads, d_head, out, seed, stream_
 
 def gnn_quant_stats(g: Graph, H, rows, beta, rng, edge_w=None, d=None):
     """beta[r], range[r] of the listed rows (AdaQP's bit-width statistics)."""
+    _f32(H, beta, rng, edge_w)
+    _i32(rows)
     d = H.shape[1] if d is None else d
     _check(lib().gnn_quant_stats(g.h, _p(edge_w), _p(H), _ld(H), d, _p(rows), rows.numel(), _p(beta), _p(rng),
                                  _stream()))
@@ -338,6 +380,8 @@ def gnn_quant_slots(n, rows_list, qslot):
 def gnn_spmm_dequant(g: Graph, X, qslot, groups, Y, relu=False, d=None, ws=None, Z=None):
     """Y = A_hat X~ (+ Z), X~ = X with the slotted rows dequantised in the gather.
     groups: list of (packed, scale, zero, bits)."""
+    _f32(X, Y, Z, *[sc for _, sc, _, _ in groups], *[zr for _, _, zr, _ in groups])
+    _i32(qslot)
     d = X.shape[1] if d is None else d
     arr = (QGroup * max(len(groups), 1))(*[QGroup(_p(pk), _p(sc), _p(zr), sc.numel(), b)
                                            for pk, sc, zr, b in groups])
@@ -359,6 +403,7 @@ def gnn_gcn_workspace_size(g: Graph, d_in, d_out):
 def gnn_gcn_layer_fwd(g: Graph, X, W, Y, relu, saved=None, ws=None, _fn="gnn_gcn_layer_fwd"):
     """Y = sigma(A_hat X W); X, Y may be row-strided views (leading dims from their strides)."""
     d_in, d_out = W.shape
+    _f32(W)
     if ws is None:
         ws = _ws(gnn_gcn_workspace_size(g, d_in, d_out), X.device)
     if saved is not None and _ld(saved) != _ld(X):
@@ -371,6 +416,7 @@ def gnn_gcn_layer_fwd(g: Graph, X, W, Y, relu, saved=None, ws=None, _fn="gnn_gcn
 def gnn_gcn_layer_bwd(g: Graph, X, W, Y, dY, relu, dW, dX=None, saved=None, ws=None, relu_in=False,
                       _fn="gnn_gcn_layer_bwd"):
     d_in, d_out = W.shape
+    _f32(W, dW)
     if ws is None:
         ws = _ws(gnn_gcn_workspace_size(g, d_in, d_out), dY.device)
     ref = X if X is not None else saved
@@ -403,8 +449,24 @@ def gnn_gat_workspace_size(g: Graph, d_in, heads, d_head):
     return lib().gnn_gat_workspace_size(g.h, d_in, heads, d_head)
 
 
-def gnn_gat_layer_fwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, Y, saved, ws=None):
+def _gat_check(g, X, W, a_src, a_dst, heads, d_head, saved, Y, dY=None, dX=None):
+    """The GAT entry points take contiguous f32 node matrices with n rows."""
+    _f32(X, W, a_src, a_dst, Y, dY, dX)
+    hd = heads * d_head
     d_in = X.shape[1]
+    for t, cols, what in ((X, d_in, "X"), (Y, hd, "Y"), (dY, hd, "dY"), (dX, d_in, "dX")):
+        if t is not None and (t.dim() != 2 or tuple(t.shape) != (g.n, cols) or not t.is_contiguous()):
+            raise ValueError(f"GAT {what}: expected a contiguous [{g.n}, {cols}] tensor, got {list(t.shape)}")
+    for t, shape, what in ((W, (d_in, hd), "W"), (a_src, (heads, d_head), "a_src"), (a_dst, (heads, d_head), "a_dst")):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"GAT {what}: expected a contiguous {list(shape)} tensor, got {list(t.shape)}")
+    if saved.numel() * saved.element_size() < gnn_gat_saved_size(g, heads, d_head):
+        raise ValueError("GAT: saved is smaller than gnn_gat_saved_size()")
+    return d_in
+
+
+def gnn_gat_layer_fwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, Y, saved, ws=None):
+    d_in = _gat_check(g, X, W, a_src, a_dst, heads, d_head, saved, Y)
     if ws is None:
         ws = _ws(gnn_gat_workspace_size(g, d_in, heads, d_head), X.device)
     _check(lib().gnn_gat_layer_fwd(g.h, _p(X), d_in, _p(W), _p(a_src), _p(a_dst), heads, d_head, float(slope), _p(Y),
@@ -414,7 +476,11 @@ def gnn_gat_layer_fwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, Y, sav
 
 def gnn_gat_layer_bwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, Y, dY, saved, dW, da_src, da_dst,
                       dX=None, ws=None):
-    d_in = X.shape[1]
+    d_in = _gat_check(g, X, W, a_src, a_dst, heads, d_head, saved, Y, dY, dX)
+    _f32(dW, da_src, da_dst)
+    if tuple(dW.shape) != tuple(W.shape) or tuple(da_src.shape) != (heads, d_head) or \
+            tuple(da_dst.shape) != (heads, d_head):
+        raise ValueError("GAT: dW, da_src, da_dst must have the shapes of W, a_src, a_dst")
     if ws is None:
         ws = _ws(gnn_gat_workspace_size(g, d_in, heads, d_head), X.device)
     _check(lib().gnn_gat_layer_bwd(g.h, _p(X), d_in, _p(W), _p(a_src), _p(a_dst), heads, d_head, float(slope), _p(Y),

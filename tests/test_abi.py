@@ -81,3 +81,28 @@ def test_status_strings_and_host_side_validation():
     # dequantising aggregation: NULL graph; then d not a multiple of 4 is checked after the graph
     st = L.gnn_spmm_dequant(None, None, 4, None, None, 0, None, 0, None, 4, 4, 0, None, 0, None)
     assert st == 1 and b"NULL" in L.gnn_last_error()
+
+
+def test_binding_refuses_wrong_dtypes_before_the_library():
+    # float* entry points must never receive a bf16 (or integer) buffer: the
+    # kernels would read and write past its end.  The binding checks first,
+    # so this runs without a GPU (the tensors never reach the library).
+    import torch
+    from sparse_message_passing_amd import gnnmp
+    bf = torch.zeros((4, 16), dtype=torch.bfloat16)
+    f = torch.zeros((4, 16))
+    rows = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        gnnmp.gnn_gemm_q8(bf, f.T, f[:, :4], seed=0)
+    with pytest.raises(TypeError):
+        gnnmp.gnn_gemm_q8(f, f.T, bf[:, :4], seed=0)
+    with pytest.raises(TypeError):
+        gnnmp.gnn_sddmm_q8(None, bf, f, 1, 16, f, seed=0)
+    with pytest.raises(TypeError):
+        gnnmp.gnn_quantize(bf, rows, 8, 0, None, f, f)
+    with pytest.raises(TypeError):
+        gnnmp.gnn_quantize(f, rows.long(), 8, 0, None, f, f)
+    with pytest.raises(TypeError):
+        gnnmp.gnn_edge_softmax(None, bf, f)
+    with pytest.raises(TypeError):
+        gnnmp.gnn_gcn_layer_fwd(None, f, bf, f, True)

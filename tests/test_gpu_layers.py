@@ -350,6 +350,23 @@ def test_gat_layer_bwd_by_head_slabs():
     _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r)
 
 
+@pytest.mark.parametrize("heads,dh", [(3, 16), (2, 12), (1, 512)])
+def test_gat_bwd_rejects_unsupported_shapes(heads, dh):
+    # the backward's out-edge pass needs 1, 2, 4 or 8 heads and d_head a power
+    # of two from 4 to 256: anything else is refused before any launch
+    s, t = hub_edges(64, 200, 10, 2)
+    g = gnnmp.gnn_graph_create(64, s, t, csc=True)
+    hd = heads * dh
+    X = torch.zeros((64, 8), device="cuda")
+    W = torch.zeros((8, hd), device="cuda")
+    a = torch.zeros((heads, dh), device="cuda")
+    Y = torch.zeros((64, hd), device="cuda")
+    saved = torch.zeros(gnnmp.gnn_gat_saved_size(g, heads, dh), dtype=torch.uint8, device="cuda")
+    with pytest.raises(gnnmp.GnnError, match="power of two"):
+        gnnmp.gnn_gat_layer_bwd(g, X, W, a, a, heads, dh, 0.2, Y, Y, saved, torch.empty_like(W), torch.empty_like(a),
+                                torch.empty_like(a))
+
+
 def test_gat_bwd_requires_csc():
     s, t = hub_edges(100, 300, 10, 1)
     g = gnnmp.gnn_graph_create(100, s, t, csc=False)
