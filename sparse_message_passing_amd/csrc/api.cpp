@@ -588,8 +588,7 @@ gnn_status_t gnn_spmm_dequant(gnn_graph_t h, const float* X, int64_t ldx, const 
     qs.addend = Z;
     qs.ld_add = ldz;
     return launch_spmm(csr_view(g), g.dinv, GNN_W_GCN, nullptr, 1, X, GNN_F32, ldx, Y, GNN_F32, ldy, d, relu,
-                       Rank1Epilogue{}, static_cast<float*>(ws), static_cast<hipStream_t>(stream), MaskEpilogue{}, 0,
-                       qs);
+                       Rank1Epilogue{}, static_cast<float*>(ws), static_cast<hipStream_t>(stream), MaskEpilogue{}, qs);
 }
 
 }  // extern "C"

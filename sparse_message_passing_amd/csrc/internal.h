@@ -128,8 +128,7 @@ inline size_t quantised_source_record_bytes(int64_t n) { return static_cast<size
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
-                         const MaskEpilogue& mask = MaskEpilogue{}, int64_t w_head_stride = 0,
-                         const QuantSources& qs = QuantSources{});
+                         const MaskEpilogue& mask = MaskEpilogue{}, const QuantSources& qs = QuantSources{});
 gnn_status_t launch_quantize_sym8(const float* X, int64_t ldx, int64_t rows, int64_t cols, const float* mptr,
                                   uint64_t seed, uint32_t stream_id, int8_t* out, int64_t out_ld, int transpose,
                                   float* s_out, hipStream_t st);
@@ -151,7 +150,6 @@ gnn_status_t launch_quant_slots(int64_t n, int n_groups, const int32_t* const* r
                                 int32_t* qslot, hipStream_t st);
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d);
 // whether gathers from a rows x row_bytes matrix are worth cutting into column slabs
-bool column_slabs_pay(int64_t rows, int64_t row_bytes);
 
 gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, const float* D, int64_t ldd,
                               int heads, float slope, float* out, float* out_pre, hipStream_t st);
