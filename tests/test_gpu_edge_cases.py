@@ -89,3 +89,63 @@ def test_gemm_empty_reduction_is_zero():
     C = torch.full((70, 33), float("nan"), device="cuda")
     gnnmp.gnn_gemm(A, B, C)
     assert not torch.isnan(C).any() and not C.any()
+
+
+def test_zero_node_graph_attention_and_quantised_calls():
+    # GAT forward/backward and the 8-bit SDDMM on an empty node set: nothing
+    # to gather, and the parameter gradients are empty sums (zero)
+    g = gnnmp.gnn_graph_create(0, np.zeros(0, np.int32), np.zeros(0, np.int32), csc=True)
+    heads, dh, din = 4, 16, 8
+    X = torch.zeros((0, din), device="cuda")
+    W = torch.ones((din, heads * dh), device="cuda")
+    a = torch.ones((heads, dh), device="cuda")
+    Y = torch.zeros((0, heads * dh), device="cuda")
+    saved = torch.zeros(max(gnnmp.gnn_gat_saved_size(g, heads, dh), 1), dtype=torch.uint8, device="cuda")
+    gnnmp.gnn_gat_layer_fwd(g, X, W, a, a, heads, dh, 0.2, Y, saved)
+    dW = torch.full_like(W, float("nan"))
+    das = torch.full_like(a, float("nan"))
+    dad = torch.full_like(a, float("nan"))
+    gnnmp.gnn_gat_layer_bwd(g, X, W, a, a, heads, dh, 0.2, Y, Y, saved, dW, das, dad, dX=torch.zeros_like(X))
+    assert not dW.any() and not das.any() and not dad.any()
+    out = torch.zeros((0, heads), device="cuda")
+    gnnmp.gnn_sddmm_q8(g, Y, Y, heads, dh, out, seed=1)
+    torch.cuda.synchronize()
+
+
+def test_gat_on_self_loops_only():
+    # one in-edge per node (its self-loop): alpha = 1 exactly, so the layer
+    # output is H' = X W bit for bit; in the backward the softmax term equals
+    # the node's own attention gradient, dE = 0, dS = dD = 0, da_src = da_dst
+    # = 0, and dH' = dY, so dW = X^T dY and dX = dY W^T
+    n, heads, dh, din = 2000, 4, 64, 48
+    g, og = graph_pair(np.zeros(0, np.int32), np.zeros(0, np.int32), n, False, csc=True)
+    r = np.random.default_rng(70)
+    X = to_dev(r.standard_normal((n, din)).astype(np.float32))
+    W = to_dev((r.standard_normal((din, heads * dh)) * 0.1).astype(np.float32))
+    a_s = to_dev(r.standard_normal((heads, dh)).astype(np.float32))
+    a_d = to_dev(r.standard_normal((heads, dh)).astype(np.float32))
+    Y = torch.empty((n, heads * dh), device="cuda")
+    saved = torch.empty(gnnmp.gnn_gat_saved_size(g, heads, dh), dtype=torch.uint8, device="cuda")
+    gnnmp.gnn_gat_layer_fwd(g, X, W, a_s, a_d, heads, dh, 0.2, Y, saved)
+    Hp = gnnmp.gat_saved_views(g, saved, heads, dh)[0]
+    al = gnnmp.gat_saved_views(g, saved, heads, dh)[5]
+    assert torch.equal(al, torch.ones_like(al))
+    assert torch.equal(Y, Hp)
+    dY = torch.randn((n, heads * dh), device="cuda")
+    dW = torch.empty_like(W)
+    dX = torch.empty_like(X)
+    das = torch.empty_like(a_s)
+    dad = torch.empty_like(a_d)
+    gnnmp.gnn_gat_layer_bwd(g, X, W, a_s, a_d, heads, dh, 0.2, Y, dY, saved, dW, das, dad, dX=dX)
+    # |P| and |dalpha| are at most scale per row; dE = alpha (dalpha - P) is
+    # zero up to a few roundings of that, and da sums n such terms times H'
+    scale = float((dY.abs().sum(1) * Hp.abs().sum(1)).max())
+    tol = 1e-6 * n * scale * float(Hp.abs().max())
+    assert float(das.abs().max()) <= tol and float(dad.abs().max()) <= tol
+    dW_ref = torch.empty_like(W)
+    gnnmp.gnn_gemm(X, dY, dW_ref, transA=True)
+    dX_ref = torch.empty_like(X)
+    gnnmp.gnn_gemm(dY, W, dX_ref, transB=True)
+    for got, ref, what in ((dW, dW_ref, "dW"), (dX, dX_ref, "dX")):
+        err = float((got - ref).abs().max())
+        assert err <= 1e-5 * float(ref.abs().max()) + tol, (what, err)
