@@ -24,8 +24,11 @@ def _dt(name):
 
 
 def _padded(n, d, dtype, dev):
-    """[n, d] view of an [n, round_up(d, 4)] buffer: 16-byte aligned rows for the kernels."""
-    ld = (d + 3) // 4 * 4
+    """[n, d] view of a buffer whose rows are a whole number of 16 bytes
+    (d rounded up to 4 f32 or 8 bf16 elements), so every row gather is made of
+    16-byte loads."""
+    q = 8 if dtype == torch.bfloat16 else 4
+    ld = (d + q - 1) // q * q
     return torch.empty((n, ld), dtype=dtype, device=dev)[:, :d]
 
 

@@ -116,6 +116,46 @@ def test_spmm(hubg, case):
     check_close(from_dev(Y), ref, mag, bf16_out=ydt == "bf16", what="spmm")
 
 
+# bf16 sources whose rows are a whole number of 16 bytes take eight features
+# per lane: ragged widths inside padded rows, several heads, the transposed
+# view (weights through the edge map), epilogues, and hub rows split in chunks
+@pytest.mark.parametrize("d,ld,wname,heads,transpose,relu,ydt", [
+    (256, 256, "gcn", 1, False, False, "bf16"),
+    (100, 104, "gcn", 1, False, True, "bf16"),
+    (200, 208, "mean", 1, False, False, "f32"),
+    (256, 256, "edge", 4, False, False, "f32"),
+    (256, 256, "edge", 4, True, False, "bf16"),
+    (512, 512, "gcn", 1, True, True, "f32"),
+    (64, 64, "ones", 1, False, False, "bf16"),
+])
+def test_spmm_bf16_sixteen_byte_rows(hubg, d, ld, wname, heads, transpose, relu, ydt):
+    g, og = hubg
+    r = np.random.default_rng(d + ld + heads)
+    X = bf16_values(r.standard_normal((og.n, d)).astype(np.float32))
+    if wname == "gcn":
+        w, wt = og.gcn_norm()[1], "gcn"
+    elif wname == "ones":
+        w, wt = None, "ones"
+    elif wname == "mean":
+        w, wt = og.mean_weights(), "mean"
+    else:
+        w = r.random((og.nnz, heads)).astype(np.float32)
+        wt = to_dev(w)
+    ref = oracle.spmm(og, X, w, heads, transpose=transpose)
+    mag = oracle.spmm_mag(og, X, w, heads, transpose=transpose)
+    if relu:
+        ref = np.maximum(ref, 0)
+    Xb = torch.zeros((og.n, ld), dtype=torch.bfloat16, device="cuda")
+    Xb[:, :d] = to_dev(X, torch.bfloat16)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    Y = torch.full((og.n, ld), float("nan"), dtype=tdt[ydt], device="cuda")
+    gnnmp.gnn_spmm(g, Xb[:, :d], Y[:, :d], weights=wt, heads=heads, transpose=transpose, relu=relu)
+    torch.cuda.synchronize()
+    check_close(from_dev(Y[:, :d]), ref, mag, bf16_out=ydt == "bf16", what="spmm bf16 16-byte rows")
+    if ld > d:  # the padding columns of Y are never written
+        assert torch.isnan(Y[:, d:].float()).all()
+
+
 def test_spmm_integer_exact(hubg):
     # unit weights on small-integer features: every fp32 partial sum is exact
     g, og = hubg
