@@ -372,9 +372,11 @@ gnn_status_t gnn_sage_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, 
  * Y[v, head k] = sum_in alpha[e,k] H'[u, head k] (heads concatenated, no bias,
  * no output activation).  X [n, d_in] f32, W [d_in, heads*d_head] f32,
  * a_src, a_dst [heads, d_head] f32, Y [n, heads*d_head] f32.
- * saved: gnn_gat_saved_size() bytes holding H', S, D, each destination's
- * softmax maximum M and 1 / sum of exponentials Z per head ([n, heads] each),
- * and alpha, for the backward.  Needs the CSC view only for the backward. */
+ * saved: gnn_gat_saved_size() bytes holding H' [n, heads*d_head], S, D,
+ * each destination's softmax maximum M and 1 / sum of exponentials Z per head
+ * ([n, heads] each), and alpha as one plane of nnz values per head (CSR
+ * order), in that order, each slice starting on a 256-byte boundary.  Needs
+ * the CSC view only for the backward. */
 size_t gnn_gat_saved_size(gnn_graph_t g, int heads, int64_t d_head);
 size_t gnn_gat_workspace_size(gnn_graph_t g, int64_t d_in, int heads, int64_t d_head);
 gnn_status_t gnn_gat_layer_fwd(gnn_graph_t g, const float* X, int64_t d_in, const float* W, const float* a_src,

@@ -350,6 +350,18 @@ __device__ __forceinline__ void softmax_fwd_rows(const Sched& s, const float* E,
 // rows keep their scores in registers; longer ones form them again in each
 // of the softmax's three sweeps (S is small and stays cached).
 // ---------------------------------------------------------------------------
+// alpha of edge e: edge-major (alpha[e*H + k]) when as == 0, else one plane
+// per head (alpha[k*as + e]), which the aggregation reads one head per slab
+template <int H>
+__device__ __forceinline__ void st_alpha(float* alpha, int64_t as, int64_t e, const HV<H>& x) {
+    if (as == 0) {
+        st<H>(alpha + e * H, x);
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < H; ++k) alpha[k * as + e] = x.v[k];
+}
+
 template <int H>
 __device__ __forceinline__ HV<H> attn_score(const float* S, const HV<H>& dv, int64_t u, float slope, int act,
                                             HV<H>& pre) {
@@ -364,7 +376,7 @@ __device__ __forceinline__ HV<H> attn_score(const float* S, const HV<H>& dv, int
 
 template <int H>
 __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const float* D, float slope, int act,
-                                          float* alpha, float* out_pre, float* mo, float* zo, int64_t blk) {
+                                          float* alpha, int64_t as, float* out_pre, float* mo, float* zo, int64_t blk) {
     const int lane = threadIdx.x % G;
     const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
     if (li >= s.n) return;
@@ -404,7 +416,7 @@ __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const 
             if (e < ee) {
 #pragma unroll
                 for (int k = 0; k < H; ++k) x[c].v[k] = __expf(x[c].v[k] - m.v[k]) * z.v[k];
-                st<H>(alpha + e * H, x[c]);
+                st_alpha<H>(alpha, as, e, x[c]);
             }
         }
         return;
@@ -429,13 +441,13 @@ __device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const 
         HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
 #pragma unroll
         for (int k = 0; k < H; ++k) x.v[k] = __expf(x.v[k] - m.v[k]) * z.v[k];
-        st<H>(alpha + e * H, x);
+        st_alpha<H>(alpha, as, e, x);
     }
 }
 
 template <int H>
 __device__ __forceinline__ void attn_block(const Sched& s, const float* S, const float* D, float slope, int act,
-                                           float* alpha, float* out_pre, float* mo, float* zo, int64_t blk,
+                                           float* alpha, int64_t as, float* out_pre, float* mo, float* zo, int64_t blk,
                                            float (*sh)[H]) {
     const int64_t v = s.order[blk];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
@@ -464,16 +476,16 @@ __device__ __forceinline__ void attn_block(const Sched& s, const float* S, const
         HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
 #pragma unroll
         for (int k = 0; k < H; ++k) x.v[k] = __expf(x.v[k] - m.v[k]) * z.v[k];
-        st<H>(alpha + e * H, x);
+        st_alpha<H>(alpha, as, e, x);
     }
 }
 
 template <int H>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(Sched s, const float* S, const float* D, float slope, int act,
-                                                       float* alpha, float* out_pre, float* mo, float* zo) {
+                                                       float* alpha, int64_t as, float* out_pre, float* mo, float* zo) {
     __shared__ float sh[4][H];
-    if (blockIdx.x < s.n_block) attn_block<H>(s, S, D, slope, act, alpha, out_pre, mo, zo, blockIdx.x, sh);
-    else attn_rows<H>(s, S, D, slope, act, alpha, out_pre, mo, zo, blockIdx.x - s.n_block);
+    if (blockIdx.x < s.n_block) attn_block<H>(s, S, D, slope, act, alpha, as, out_pre, mo, zo, blockIdx.x, sh);
+    else attn_rows<H>(s, S, D, slope, act, alpha, as, out_pre, mo, zo, blockIdx.x - s.n_block);
 }
 
 template <int H>
@@ -856,7 +868,8 @@ gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha,
 }
 
 gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float* D, int heads, float slope,
-                                  float* alpha, float* out_pre, float* row_max, float* row_rsum, hipStream_t st) {
+                                  float* alpha, int64_t alpha_head_stride, float* out_pre, float* row_max,
+                                  float* row_rsum, hipStream_t st) {
     if (v.n == 0) return GNN_OK;
     Sched s = make_sched(v);
     const int64_t light = s.n - s.n_block;
@@ -864,7 +877,7 @@ gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float*
     const int act = slope == slope;  // NaN: no activation
     GNN_HEADS_SWITCH(heads, {
         hipLaunchKernelGGL((attn_fwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, S, D,
-                           act ? slope : 0.0f, act, alpha, out_pre, row_max, row_rsum);
+                           act ? slope : 0.0f, act, alpha, alpha_head_stride, out_pre, row_max, row_rsum);
     });
     return launch_status("GAT attention");
 }

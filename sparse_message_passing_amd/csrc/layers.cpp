@@ -279,9 +279,11 @@ gnn_status_t gnn_gat_layer_fwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     // (keeping each row's maximum and 1/sum);  Y = (G . alpha) H'
     GNN_TRY(launch_gemm(0, 0, g.n, hd, d_in, X, GNN_F32, d_in, W, GNN_F32, hd, s.Hp, GNN_F32, hd, gws, gemm, st));
     GNN_TRY(launch_gat_scores(g.n, s.Hp, heads, d_head, a_src, a_dst, s.S, s.D, st));
-    GNN_TRY(launch_gat_attention(csr_view(g), s.S, s.D, heads, slope, s.alpha, nullptr, s.M, s.Z, st));
+    // alpha is kept one plane per head, so the aggregation's head slabs read
+    // their weights contiguously
+    GNN_TRY(launch_gat_attention(csr_view(g), s.S, s.D, heads, slope, s.alpha, g.nnz, nullptr, s.M, s.Z, st));
     return launch_spmm(csr_view(g), g.dinv, GNN_W_EDGE, s.alpha, heads, s.Hp, GNN_F32, hd, Y, GNN_F32, hd, hd, 0,
-                       Rank1Epilogue{}, sws, st);
+                       Rank1Epilogue{}, sws, st, MaskEpilogue{}, QuantSources{}, g.nnz);
 }
 
 gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, const float* W, const float* a_src,
