@@ -182,8 +182,9 @@ __global__ __launch_bounds__(256) void gat_bwd_csc_kernel(GatBwdArgs a) {
         make_float4(fmaf(ds, as.x, acc.x), fmaf(ds, as.y, acc.y), fmaf(ds, as.z, acc.z), fmaf(ds, as.w, acc.w));
 }
 
-// hub sources: sum the chunks' partial rows and dS in chunk order, then the
-// dS a_src term.  One wave per (hub row, head).
+// hub sources: sum the chunks' partial rows and dS, then the dS a_src term.
+// One wave per (hub row, head).  Chunk c goes to accumulator (c - c0) mod 4,
+// the four added pairwise at the end: a fixed order with four loads in flight.
 __global__ __launch_bounds__(256) void gat_bwd_fixup_kernel(GatBwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -193,18 +194,49 @@ __global__ __launch_bounds__(256) void gat_bwd_fixup_kernel(GatBwdArgs a) {
     const int k = static_cast<int>(w - i * H);
     const int64_t u = a.order[i];
     const int64_t c0 = a.chunk_first[i], c1 = a.chunk_first[i + 1];
-    float ds = 0.0f;
-    for (int64_t c = c0; c < c1; ++c) ds += a.pds[c * H + k];
+    float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    {
+        int64_t c = c0;
+        for (; c + 4 <= c1; c += 4) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) d4[q] += a.pds[(c + q) * H + k];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (c + q < c1) d4[q] += a.pds[(c + q) * H + k];
+    }
+    const float ds = (d4[0] + d4[1]) + (d4[2] + d4[3]);
     const int64_t hd = H * a.dh;
     for (int64_t f = lane * 4; f < a.dh; f += 256) {
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int64_t c = c0; c < c1; ++c) {
-            const float4 p = *reinterpret_cast<const float4*>(a.part + (c * H + k) * a.dh + f);
-            acc.x += p.x;
-            acc.y += p.y;
-            acc.z += p.z;
-            acc.w += p.w;
+        float4 p4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p4[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        int64_t c = c0;
+        for (; c + 4 <= c1; c += 4) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 p = *reinterpret_cast<const float4*>(a.part + ((c + q) * H + k) * a.dh + f);
+                p4[q].x += p.x;
+                p4[q].y += p.y;
+                p4[q].z += p.z;
+                p4[q].w += p.w;
+            }
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (c + q < c1) {
+                const float4 p = *reinterpret_cast<const float4*>(a.part + ((c + q) * H + k) * a.dh + f);
+                p4[q].x += p.x;
+                p4[q].y += p.y;
+                p4[q].z += p.z;
+                p4[q].w += p.w;
+            }
+        }
+        float4 acc;
+        acc.x = (p4[0].x + p4[1].x) + (p4[2].x + p4[3].x);
+        acc.y = (p4[0].y + p4[1].y) + (p4[2].y + p4[3].y);
+        acc.z = (p4[0].z + p4[1].z) + (p4[2].z + p4[3].z);
+        acc.w = (p4[0].w + p4[1].w) + (p4[2].w + p4[3].w);
         const float4 as = *reinterpret_cast<const float4*>(a.a_src + k * a.dh + f);
         *reinterpret_cast<float4*>(a.dHp + u * hd + k * a.dh + f) =
             make_float4(fmaf(ds, as.x, acc.x), fmaf(ds, as.y, acc.y), fmaf(ds, as.z, acc.z), fmaf(ds, as.w, acc.w));

@@ -396,15 +396,26 @@ __global__ __launch_bounds__(256) void qrec_kernel(SpmmArgs a, QRec* rec) {
     *reinterpret_cast<uint4*>(rec + v) = make_uint4(r.lo, r.hi, __float_as_uint(r.S), __float_as_uint(r.Z));
 }
 
-// Sum the partial rows of each heavy row in chunk order, then the epilogue.
+// Sum the partial rows of each heavy row, then the epilogue.  Chunk c goes to
+// accumulator (c - c0) mod 8 and the eight are added pairwise at the end: a
+// fixed order (deterministic) with eight loads in flight, so the longest hub
+// row (over a hundred chunks) does not wait on one load per chunk.
 template <typename TO>
 __global__ __launch_bounds__(256) void spmm_fixup(SpmmArgs a) {
     const int64_t i = blockIdx.x;
     const int64_t row = a.order[i];
     const int64_t c0 = a.chunk_first[i], c1 = a.chunk_first[i + 1];
     for (int64_t f = threadIdx.x; f < a.d; f += blockDim.x) {
-        float s = 0.0f;
-        for (int64_t c = c0; c < c1; ++c) s += a.partial[c * a.pd + f];
+        float p8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        int64_t c = c0;
+        for (; c + 8 <= c1; c += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) p8[u] += a.partial[(c + u) * a.pd + f];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (c + u < c1) p8[u] += a.partial[(c + u) * a.pd + f];
+        float s = ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
         if (a.addend) s = s + a.addend[row * a.ld_add + f];
         if (a.r1.a) {
             const int64_t h = f / a.dh;
