@@ -724,9 +724,20 @@ __global__ __launch_bounds__(256) void colsum_stage2(int64_t nblk, int64_t d, co
     __shared__ float sh[4][64];
     const int64_t o = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x & 63);  // in [0, 2d)
     const int grp = threadIdx.x >> 6;
-    float s = 0.0f;
-    if (o < 2 * d)
-        for (int64_t b = grp; b < nblk; b += 4) s += partial[b * 2 * d + o];
+    // block b goes to group b mod 4, and within the group to accumulator
+    // (b / 4) mod 4: a fixed order with four loads in flight per thread
+    float p4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (o < 2 * d) {
+        int64_t b = grp;
+        for (; b + 12 < nblk; b += 16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p4[q] += partial[(b + 4 * q) * 2 * d + o];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (b + 4 * q < nblk) p4[q] += partial[(b + 4 * q) * 2 * d + o];
+    }
+    const float s = (p4[0] + p4[1]) + (p4[2] + p4[3]);
     sh[grp][threadIdx.x & 63] = s;
     __syncthreads();
     if (grp == 0 && o < 2 * d) {

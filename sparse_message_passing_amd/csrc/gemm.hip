@@ -371,9 +371,20 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* ws, int splits
     __shared__ float part[4][64];
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x & 63);
     const int grp = threadIdx.x >> 6;
-    float s = 0.0f;
-    if (i < M * N)
-        for (int z = grp; z < splits; z += 4) s += ws[z * M * N + i];
+    // split z goes to group z mod 4, and within the group to accumulator
+    // (z / 4) mod 4: a fixed order with four loads in flight per thread
+    float p4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (i < M * N) {
+        int z = grp;
+        for (; z + 12 < splits; z += 16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p4[q] += ws[(z + 4 * q) * M * N + i];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (z + 4 * q < splits) p4[q] += ws[(z + 4 * q) * M * N + i];
+    }
+    const float s = (p4[0] + p4[1]) + (p4[2] + p4[3]);
     part[grp][threadIdx.x & 63] = s;
     __syncthreads();
     if (grp == 0 && i < M * N) {

@@ -61,9 +61,18 @@ __global__ __launch_bounds__(256) void xent_rows(const float* z, int64_t n, int6
 
 __global__ __launch_bounds__(256) void xent_total(const float* block_loss, int64_t nb, float inv_n, float* loss) {
     __shared__ float sh[256];
-    float t = 0.0f;
-    for (int64_t i = threadIdx.x; i < nb; i += 256) t += block_loss[i];
-    sh[threadIdx.x] = t;
+    // entry i goes to accumulator (i / 256) mod 4: a fixed order with four
+    // loads in flight per thread
+    float p4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int64_t i = threadIdx.x;
+    for (; i + 768 < nb; i += 1024) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p4[q] += block_loss[i + 256 * q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (i + 256 * q < nb) p4[q] += block_loss[i + 256 * q];
+    sh[threadIdx.x] = (p4[0] + p4[1]) + (p4[2] + p4[3]);
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
         if (threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
