@@ -94,15 +94,77 @@ def spmm_compulsory_bytes(n, nnz, d, s_in=4, s_out=4, edge_weights=True):
     return 8 * (n + 1) + 4 * nnz + w + s_in * n * d + s_out * n * d
 
 
-def cpu_baseline_gcn(min_seconds=10.0, max_passes=3):
-    """The oracle's 3-layer forward+backward on the full workload, repeated
-    until at least `min_seconds` of CPU work (at most `max_passes` passes)."""
-    import oracle
+def oracle_graph(k):
     from oracle.graph import build_graph
     from sparse_message_passing_amd import synth
-    inp = synth.config_inputs(2)
-    n = int(inp["n"])
-    og = build_graph(inp["src"], inp["dst"], n, True)
+    inp = synth.config_inputs(k)
+    return build_graph(inp["src"], inp["dst"], int(inp["n"]), synth.CONFIGS[k]["symmetric"]), inp
+
+
+def row_sample(og, edges):
+    """Consecutive rows from inside the id range (R-MAT makes ids with few
+    one bits its hubs, so the start 0.7071 n has a typical mix) holding about
+    `edges` edges, as an oracle graph of their own (column ids stay global).
+    Returns it and its first edge slot."""
+    import oracle
+    r0 = int(og.n * 0.7071)
+    e0 = int(og.row_ptr[r0])
+    r1 = int(np.searchsorted(og.row_ptr, e0 + edges))
+    r1 = max(r0 + 1, min(r1, og.n))
+    e1 = int(og.row_ptr[r1])
+    rp = og.row_ptr[r0:r1 + 1] - e0
+    return oracle.OracleGraph(r1 - r0, rp, og.col[e0:e1].copy(), (og.dst[e0:e1] - r0).astype(np.int32)), e0
+
+
+def cpu_oracle_kernels(k, og, inp, edges=1_000_000):
+    """The oracle's own steps timed on one host thread and on all of them, on
+    a bounded sample of the workload: the 256-wide aggregation (GCN
+    workloads), the SDDMM dot and the edge softmax (GAT), the quantiser over
+    the marginal rows (quantised exchange).  Rates in the bench's units."""
+    import oracle
+    from sparse_message_passing_amd import synth
+    allt = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cfg = synth.CONFIGS[k]
+    out = {"threads_all": allt}
+    jobs = []
+    # inputs already in the oracle's float64, so the timed calls convert nothing
+    if cfg["kind"] == "gcn" or cfg["kind"] == "quant":
+        sub, e0 = row_sample(og, edges)
+        X = np.random.default_rng(77).standard_normal((og.n, 256))
+        w = og.gcn_norm()[1][e0:e0 + sub.nnz].astype(np.float64)
+        jobs.append(("spmm_d256_gedge_feat_s", lambda: oracle.spmm(sub, X, w), sub.nnz * 256, f"{sub.n} rows, {sub.nnz} edges"))
+    if cfg["kind"] == "gat":
+        sub, e0 = row_sample(og, edges)
+        A = np.random.default_rng(78).standard_normal((sub.n, 256))   # destination rows of the sample
+        B = np.random.default_rng(79).standard_normal((og.n, 256))
+        E = np.random.default_rng(80).standard_normal((sub.nnz, 4))
+        jobs.append(("sddmm_dot_gedge_feat_s", lambda: oracle.sddmm_dot(sub, A, B, 4), sub.nnz * 256,
+                     f"{sub.n} rows, {sub.nnz} edges, 4 heads x 64"))
+        jobs.append(("edge_softmax_gedge_s", lambda: oracle.edge_softmax(sub, E), sub.nnz, f"{sub.nnz} edges, 4 heads"))
+    if cfg["kind"] == "quant":
+        H = inp["H"]
+        rows = inp["rows"].astype(np.int32)
+        jobs.append(("quantize_8bit_rows_per_s", lambda: oracle.quantize(H, rows, 8, 1), rows.size,
+                     f"{rows.size} rows x 256 at 8 bits"))
+    for name, fn, work, what in jobs:
+        rec = {"sample": what}
+        for label, th in (("one_thread", 1), ("all_threads", allt)):
+            prev = oracle.set_threads(th)
+            t0 = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t0
+            oracle.set_threads(prev)
+            rec[label] = round(work / dt / 1e9, 4) if "gedge" in name else round(work / dt, 1)
+        out[name] = rec
+    return out
+
+
+def cpu_baseline_gcn(min_seconds=10.0, max_passes=3):
+    """The oracle's 3-layer forward+backward on the full workload, repeated
+    until at least `min_seconds` of CPU work (at most `max_passes` passes);
+    also returns the oracle graph and inputs for the per-step timings."""
+    import oracle
+    og, inp = oracle_graph(2)
     Ws = [inp["W0"], inp["W1"], inp["W2"]]
     passes, dt = 0, 0.0
     while passes < max_passes and (passes == 0 or dt < min_seconds):
@@ -115,7 +177,7 @@ def cpu_baseline_gcn(min_seconds=10.0, max_passes=3):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return dict(value=work / dt / 1e9, unit="GEdge*feat/s", cores=threads, kind="oracle",
                 sample=f"{passes} full 3-layer forward+backward pass(es) of the same workload "
-                       f"(2^20 nodes, nnz {og.nnz}), {dt:.2f} s")
+                       f"(2^20 nodes, nnz {og.nnz}), {dt:.2f} s"), og, inp
 
 
 def main():
@@ -280,9 +342,14 @@ def main():
             torch.cuda.synchronize()
             extra[f"split_{name}_timeline_ms"] = ov.timeline()
     cpu = None
-    if not a.no_cpu_baseline and cfg["kind"] == "gcn":
+    if not a.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline_gcn()
+        if a.config == 2:
+            cpu, og, oinp = cpu_baseline_gcn()
+        else:
+            og, oinp = oracle_graph(a.config)
+        extra["cpu_oracle"] = cpu_oracle_kernels(a.config, og, oinp)
+        print("# CPU oracle timed", file=sys.stderr, flush=True)
     out = {
         "metric": "GNN layer fwd+bwd GEdge*feat/s; SpMM/SDDMM HBM GB/s as % of peak",
         "value": round(value, 3),

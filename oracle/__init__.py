@@ -65,6 +65,8 @@ def lib():
         L = C.CDLL(_SO)
         P, I64, I32, F32, U64, U32 = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_uint64, C.c_uint32
         sigs = {
+            "orc_set_threads": [I32],
+            "orc_threads": [],
             "orc_spmm": [I64, P, P, P, I32, P, I64, I64, P],
             "orc_spmm_t": [I64, P, P, P, I32, P, I64, I64, P],
             "orc_sddmm_dot": [I64, P, P, P, I64, P, I64, I32, I64, P],
@@ -82,8 +84,17 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = None
+        L.orc_threads.restype = I32
         _lib = L
     return _lib
+
+
+def set_threads(n):
+    """Thread count of the oracle's row-parallel loops (results are the same
+    at any count); returns the previous count."""
+    prev = lib().orc_threads()
+    lib().orc_set_threads(int(n))
+    return prev
 
 
 def _p(a):

@@ -22,8 +22,13 @@
  *     same at any thread count.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <string.h>
+
+/* Thread count of the row-parallel loops (results do not depend on it). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------------------
  * Aggregation as a sparse-dense product (SpMM).
