@@ -22,8 +22,8 @@
 // cache; per-destination records {D, m, 1/z, c} of the head are packed into
 // one 16-byte read, and dE goes to the head's own plane (coalesced stores),
 // re-laid afterwards as one record of all heads per edge for the in-edge sum.
-// Out-edge hubs are cut into chunks whose partial rows are summed in chunk
-// order afterwards: deterministic, no atomics.
+// Out-edge hubs are cut into chunks whose partial rows are summed afterwards
+// in a fixed order: deterministic, no atomics.
 
 #include "device.h"
 #include "internal.h"
