@@ -28,10 +28,16 @@ struct Carver {
 };
 
 // GCN workspace: [G (masked gradient)] [T (aggregation or GEMM intermediate)]
-//                [split-K partials] [SpMM partials]; intermediates are
-// binary32-sized with rows padded to a multiple of 4 elements so that the
-// aggregation always takes 16-byte loads.
-inline int64_t pad4(int64_t d) { return (d + 3) / 4 * 4; }
+//                [split-K partials] [SpMM partials].  Intermediate rows are
+// padded so a gathered row touches as few cache lines as its size allows:
+// f32 rows to a multiple of 64 bytes (the 41-wide aggregation: 0.535 ms in
+// 176-byte rows, 0.513 ms in 192-byte rows), bf16 rows to whole 128-byte lines.
+inline int64_t pad_row(int64_t d, gnn_dtype_t dt) {
+    return dt == GNN_BF16 ? (d + 63) / 64 * 64 : (d + 15) / 16 * 16;
+}
+inline size_t row_bytes_max(int64_t d) {
+    return static_cast<size_t>(std::max(pad_row(d, GNN_F32) * 4, pad_row(d, GNN_BF16) * 2));
+}
 
 struct GcnWs {
     size_t g, t, gemm, spmm;
@@ -42,8 +48,8 @@ GcnWs gcn_ws(const Graph& g, int64_t d_in, int64_t d_out) {
     GcnWs w;
     const int64_t n = g.n;
     const int64_t dmax = std::max(d_in, d_out);
-    w.g = static_cast<size_t>(n) * pad4(d_out) * 4;   // worst case f32
-    w.t = static_cast<size_t>(n) * pad4(dmax) * 4;
+    w.g = static_cast<size_t>(n) * row_bytes_max(d_out);
+    w.t = static_cast<size_t>(n) * row_bytes_max(dmax);
     w.gemm = std::max(gemm_ws_bytes(1, 0, d_in, d_out, n), gemm_ws_bytes(0, 0, n, d_out, d_in));
     w.gemm = std::max(w.gemm, gemm_ws_bytes(0, 1, n, d_in, d_out));
     w.spmm = spmm_partial_bytes(g.plan[0], dmax);
@@ -79,8 +85,8 @@ gnn_status_t conv_fwd(const char* api, gnn_weights_t wmode, gnn_graph_t h, const
     void* gws = c.take(w.gemm);
     float* sws = static_cast<float*>(c.take(w.spmm));
     if (gemm_first) {
-        // Z = X W (rows padded to 4), then Y = sigma(A_hat Z)
-        const int64_t ldz = pad4(d_out);
+        // Z = X W (padded rows), then Y = sigma(A_hat Z)
+        const int64_t ldz = pad_row(d_out, x_dt);
         GNN_TRY(launch_gemm(0, 0, g.n, d_out, d_in, X, x_dt, ldx, W, GNN_F32, d_out, T, x_dt, ldz, gws, w.gemm, st));
         return launch_spmm(csr_view(g), g.dinv, wmode, nullptr, 1, T, x_dt, ldz, Y, y_dt, ldy, d_out, relu,
                            Rank1Epilogue{}, sws, st);
@@ -130,7 +136,7 @@ gnn_status_t conv_bwd(const char* api, gnn_weights_t wmode, gnn_graph_t h, const
     gnn_dtype_t g_dt = y_dt;
     int64_t ldg = ldy;
     if (relu && g.n) {
-        ldg = pad4(d_out);
+        ldg = pad_row(d_out, x_dt);
         GNN_TRY(launch_relu_mask(g.n, d_out, dY, ldy, Y, ldy, y_dt, Gb, ldg, x_dt, st));
         G = Gb;
         g_dt = x_dt;
@@ -144,7 +150,7 @@ gnn_status_t conv_bwd(const char* api, gnn_weights_t wmode, gnn_graph_t h, const
     }
     if (gemm_first) {
         // dZ = A_hat G;  dW = X^T dZ;  dX = dZ W^T
-        const int64_t ldz = pad4(d_out);
+        const int64_t ldz = pad_row(d_out, x_dt);
         GNN_TRY(launch_spmm(bview, g.dinv, wmode, nullptr, 1, G, g_dt, ldg, T, x_dt, ldz, d_out, 0,
                             Rank1Epilogue{}, sws, st));
         GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, X, x_dt, ldx, T, x_dt, ldz, dW, GNN_F32, d_out, gws, w.gemm, st));
@@ -156,7 +162,7 @@ gnn_status_t conv_bwd(const char* api, gnn_weights_t wmode, gnn_graph_t h, const
     // dW = (A_hat X)^T G;  dX = A_hat (G W^T)
     GNN_TRY(launch_gemm(1, 0, d_in, d_out, g.n, saved, x_dt, ldx, G, g_dt, ldg, dW, GNN_F32, d_out, gws, w.gemm, st));
     if (dX) {
-        const int64_t ldt = pad4(d_in);
+        const int64_t ldt = pad_row(d_in, x_dt);
         GNN_TRY(launch_gemm(0, 1, g.n, d_in, d_out, G, g_dt, ldg, W, GNN_F32, d_out, T, x_dt, ldt, gws, w.gemm, st));
         GNN_TRY(launch_spmm(bview, g.dinv, wmode, nullptr, 1, T, x_dt, ldt, dX, x_dt, ldx, d_in, 0,
                             Rank1Epilogue{}, sws, st, mx));
