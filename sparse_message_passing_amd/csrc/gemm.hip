@@ -12,6 +12,11 @@
 //    planes), so every global->LDS store is a 16-byte write; the next slab's
 //    global loads are issued before the current slab's MFMAs and its LDS
 //    stores after them, one barrier per slab;
+//  * the weight-gradient products (A transposed, K = number of nodes) use a
+//    second instantiation whose interior tiles keep two slabs of loads in
+//    flight (registers for slab s + 1 and s + 2), so a load has two slabs of
+//    MFMAs to arrive instead of one; it holds more registers (two waves per
+//    SIMD instead of three), which loses on the other shapes;
 //  * operand fragments: in MFMA j of a slab, lane l supplies
 //    B[k0 + 4(l/16) + j][n0 + l%16] as the instruction's first operand and
 //    A[m0 + l%16][k0 + 4(l/16) + j] as its second, so a k-contiguous
@@ -105,8 +110,8 @@ __device__ __forceinline__ void load4(const T* base, int64_t off, bool full, int
 
 // TRANS_A: A given as [K][lda] (element (m,k) at A[k*lda+m]); else [M][lda].
 // TRANS_B: B given as [N][ldb] (element (k,n) at B[n*ldb+k]); else [K][ldb].
-template <int BM, int BN, int WM, int WN, bool TRANS_A, bool TRANS_B, bool VA, bool VB, typename TA, typename TB,
-          typename TC>
+template <int BM, int BN, int WM, int WN, bool TRANS_A, bool TRANS_B, bool VA, bool VB, bool PF, typename TA,
+          typename TB, typename TC>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
@@ -150,6 +155,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     float ra[A_LOADS][4], rb[B_LOADS][4];
+    float ra1[A_LOADS][4], rb1[B_LOADS][4];  // slab s + 1 while s + 2 loads (PF)
 
     // Interior tiles (every row / column of the tile in range, 16-byte
     // aligned operands) load full slabs without per-element checks, from
@@ -241,14 +247,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     };
 
     const int64_t nslab = (kend - kbeg + BK - 1) / BK;
-    if (nslab > 0) {
-        load_slab(kbeg);
-        store_slab(0);
-    }
-    __syncthreads();
-    for (int64_t s = 0; s < nslab; ++s) {
-        const int buf = static_cast<int>(s & 1);
-        if (s + 1 < nslab) load_slab(kbeg + (s + 1) * BK);
+    // the MFMAs of the slab held in LDS buffer buf
+    auto compute = [&](const int buf) {
         // Fragments of the whole slab.  MFMA j of the slab takes k = 4g + j from
         // lane group g = lane / 16 (any assignment of the slab's 16 k values to
         // (j, g) pairs gives the same products, as long as A and B agree), so a
@@ -304,10 +304,98 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                     for (int jj = 0; jj < FN; ++jj)
                         acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x4f32(bfr[jj][j], af[i][j], acc[i][jj], 0, 0, 0);
         }
-        // the other buffer was last read in iteration s-1, which every wave has
-        // left (barrier below), so it can be refilled now
-        if (s + 1 < nslab) store_slab(buf ^ 1);
+    };
+    // interior tile, whole slabs (PF): unchecked loads from the running
+    // offsets into register set x, and that set's LDS stores
+    auto load_full = [&](float (&xa)[A_LOADS][4], float (&xb)[B_LOADS][4]) {
+#pragma unroll
+        for (int p = 0; p < A_LOADS; ++p) {
+            load4<TA, true>(A, a_off[p], true, 4, xa[p]);
+            a_off[p] += a_step;
+        }
+#pragma unroll
+        for (int p = 0; p < B_LOADS; ++p) {
+            load4<TB, true>(B, b_off[p], true, 4, xb[p]);
+            b_off[p] += b_step;
+        }
+    };
+    auto store_full = [&](int buf, const float (&xa)[A_LOADS][4], const float (&xb)[B_LOADS][4]) {
+#pragma unroll
+        for (int p = 0; p < A_LOADS; ++p) {
+            const int q = tid + p * 256;
+            if constexpr (A_KC) {
+                *reinterpret_cast<float4*>(&As[buf][kc_row(q) * (BK + PAD) + kc_k(q)]) =
+                    make_float4(xa[p][0], xa[p][1], xa[p][2], xa[p][3]);
+            } else {
+                *reinterpret_cast<float4*>(&As[buf][(q / (BM / 4)) * (BM + PADM) + (q % (BM / 4)) * 4]) =
+                    make_float4(xa[p][0], xa[p][1], xa[p][2], xa[p][3]);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < B_LOADS; ++p) {
+            const int q = tid + p * 256;
+            if constexpr (B_KC) {
+                *reinterpret_cast<float4*>(&Bs[buf][kc_row(q) * (BK + PAD) + kc_k(q)]) =
+                    make_float4(xb[p][0], xb[p][1], xb[p][2], xb[p][3]);
+            } else {
+                *reinterpret_cast<float4*>(&Bs[buf][(q / (BN / 4)) * (BN + PADM) + (q % (BN / 4)) * 4]) =
+                    make_float4(xb[p][0], xb[p][1], xb[p][2], xb[p][3]);
+            }
+        }
+    };
+    if (PF && a_full && b_full && (kend - kbeg) % BK == 0 && nslab >= 2) {
+        // Two slabs of loads in flight.  Straight-line code (the loop handles
+        // two slabs per trip, each register set with a fixed role) lets the
+        // compiler wait for exactly the older slab's loads; the scheduling
+        // barriers keep the loads ahead of the MFMAs they overlap.
+        load_full(ra, rb);
+        store_full(0, ra, rb);
+        load_full(ra1, rb1);
         __syncthreads();
+        int64_t s = 0;
+        // here LDS buffer 0 holds slab s and (ra1, rb1) slab s + 1
+        for (; s + 3 < nslab; s += 2) {
+            load_full(ra, rb);  // slab s + 2
+            __builtin_amdgcn_sched_barrier(0);
+            compute(0);
+            store_full(1, ra1, rb1);
+            __syncthreads();
+            load_full(ra1, rb1);  // slab s + 3
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            store_full(0, ra, rb);
+            __syncthreads();
+        }
+        if (s + 3 == nslab) {  // three slabs left
+            load_full(ra, rb);
+            compute(0);
+            store_full(1, ra1, rb1);
+            __syncthreads();
+            compute(1);
+            store_full(0, ra, rb);
+            __syncthreads();
+            compute(0);
+        } else {  // two slabs left
+            compute(0);
+            store_full(1, ra1, rb1);
+            __syncthreads();
+            compute(1);
+        }
+    } else {
+        if (nslab > 0) {
+            load_slab(kbeg);
+            store_slab(0);
+        }
+        __syncthreads();
+        for (int64_t s = 0; s < nslab; ++s) {
+            const int buf = static_cast<int>(s & 1);
+            if (s + 1 < nslab) load_slab(kbeg + (s + 1) * BK);
+            compute(buf);
+            // the other buffer was last read in iteration s-1, which every wave
+            // has left (barrier below), so it can be refilled now
+            if (s + 1 < nslab) store_slab(buf ^ 1);
+            __syncthreads();
+        }
     }
 
     // epilogue: the block (i, jj) leaves lane l holding C[m][nb + r], r = 0..3
@@ -439,17 +527,29 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
 template <int BM, int BN, int WM, int WN, bool TA_, bool TB_, typename TA, typename TB, typename TC>
 void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
     const int64_t grid = 8 * g.per_xcd;
+    // Two slabs of loads in flight for the transposed-A products (weight
+    // gradients, K = nodes) in 128 x 128 tiles.  Measured per launch: f32
+    // over 2^20 rows 1.00 -> 0.95 ms, bf16 over 2.45M rows 2.31 -> 1.45 ms;
+    // the same variant lost on 128 x 64 tiles (0.43 -> 0.72 ms) and on the NN
+    // updates in a whole step (1.25 -> 1.30 ms).
+    if constexpr (TA_ && BN == 128) {
+        if (va && vb && (g.splits > 1 ? g.kper : g.K) >= 256) {
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, true, TA, TB, TC>), dim3(grid),
+                               dim3(256), 0, st, g);
+            return;
+        }
+    }
     if (va && vb)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, TA, TB, TC>), dim3(grid), dim3(256), 0,
-                           st, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, false, TA, TB, TC>), dim3(grid),
+                           dim3(256), 0, st, g);
     else if (va)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, false, TA, TB, TC>), dim3(grid), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, false, false, TA, TB, TC>), dim3(grid), dim3(256), 0,
                            st, g);
     else if (vb)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, true, TA, TB, TC>), dim3(grid), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, true, false, TA, TB, TC>), dim3(grid), dim3(256), 0,
                            st, g);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, false, TA, TB, TC>), dim3(grid), dim3(256),
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, false, false, TA, TB, TC>), dim3(grid), dim3(256),
                            0, st, g);
 }
 
