@@ -46,9 +46,11 @@ template <typename T>
 gnn_status_t upload(Graph& g, const std::vector<T>& h, T** out) {
     *out = nullptr;
     if (h.empty()) return GNN_OK;
-    void* p = nullptr;
+    // the slot exists before the allocation, so a failed push_back cannot
+    // leak device memory (free_graph frees every recorded slot; null is fine)
+    g.allocations.push_back(nullptr);
+    void*& p = g.allocations.back();
     GNN_HIP(hipMalloc(&p, h.size() * sizeof(T)));
-    g.allocations.push_back(p);
     GNN_HIP(hipMemcpy(p, h.data(), h.size() * sizeof(T), hipMemcpyHostToDevice));
     *out = static_cast<T*>(p);
     return GNN_OK;
