@@ -12,11 +12,12 @@
 //    planes), so every global->LDS store is a 16-byte write; the next slab's
 //    global loads are issued before the current slab's MFMAs and its LDS
 //    stores after them, one barrier per slab;
-//  * the weight-gradient products (A transposed, K = number of nodes) use a
-//    second instantiation whose interior tiles keep two slabs of loads in
-//    flight (registers for slab s + 1 and s + 2), so a load has two slabs of
-//    MFMAs to arrive instead of one; it holds more registers (two waves per
-//    SIMD instead of three), which loses on the other shapes;
+//  * the weight-gradient products (A transposed, K = number of nodes) and
+//    the products with a bf16 A use a second instantiation whose interior
+//    tiles keep two slabs of loads in flight (registers for slab s + 1 and
+//    s + 2), so a load has two slabs of MFMAs to arrive instead of one; it
+//    holds more registers (two waves per SIMD instead of three), which loses
+//    on the f32 NN updates;
 //  * operand fragments: in MFMA j of a slab, lane l supplies
 //    B[k0 + 4(l/16) + j][n0 + l%16] as the instruction's first operand and
 //    A[m0 + l%16][k0 + 4(l/16) + j] as its second, so a k-contiguous
@@ -89,13 +90,13 @@ __device__ __forceinline__ bool mask_on(const MaskEpilogue& m, int64_t r, int64_
     return Elem<float>::load(static_cast<const float*>(m.M) + r * m.ld + c) > 0.0f;
 }
 
-// Piece q of a k-contiguous slab (rows x BK): 16 consecutive lanes take 16
-// rows at the same k quad, the four lane groups of a wave the four quads, so
-// the 16-byte LDS stores hit the same conflict-free bank pattern as the
-// fragment reads (in global memory each row still gets 64 contiguous bytes
-// per instruction).
-__device__ __forceinline__ int kc_row(int q) { return (q >> 6) * 16 + (q & 15); }
-__device__ __forceinline__ int kc_k(int q) { return ((q >> 4) & 3) * 4; }
+// Piece q of a k-contiguous slab (rows x BK): four consecutive lanes take the
+// four k quads of one row, so each 16-lane quarter of a load instruction
+// reads four whole 64-byte row pieces (a quarter of sixteen rows at one quad
+// each, the earlier mapping, touched four times as many cache lines per
+// instruction: 1-3% slower across the products measured).
+__device__ __forceinline__ int kc_row(int q) { return q >> 2; }
+__device__ __forceinline__ int kc_k(int q) { return (q & 3) * 4; }
 
 template <typename T, bool VEC>
 __device__ __forceinline__ void load4(const T* base, int64_t off, bool full, int valid, float (&r)[4]) {
@@ -528,11 +529,13 @@ template <int BM, int BN, int WM, int WN, bool TA_, bool TB_, typename TA, typen
 void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
     const int64_t grid = 8 * g.per_xcd;
     // Two slabs of loads in flight for the transposed-A products (weight
-    // gradients, K = nodes) in 128 x 128 tiles.  Measured per launch: f32
-    // over 2^20 rows 1.00 -> 0.95 ms, bf16 over 2.45M rows 2.31 -> 1.45 ms;
-    // the same variant lost on 128 x 64 tiles (0.43 -> 0.72 ms) and on the NN
-    // updates in a whole step (1.25 -> 1.30 ms).
-    if constexpr (TA_ && BN == 128) {
+    // gradients, K = nodes) and the products with a bf16 A, in 128 x 128
+    // tiles.  Measured per launch: f32 weight gradient over 2^20 rows 1.00 ->
+    // 0.95 ms, bf16 over 2.45M rows 2.31 -> 1.45 ms, bf16 x f32 update over
+    // 2.45M rows 3.09 -> 2.92 ms; the same variant lost on 128 x 64 tiles
+    // (0.43 -> 0.72 ms) and on the f32 NN updates in a whole step (1.25 ->
+    // 1.30 ms).
+    if constexpr ((TA_ || std::is_same<TA, bf16_t>::value) && BN == 128) {
         if (va && vb && (g.splits > 1 ? g.kper : g.K) >= 256) {
             hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, true, TA, TB, TC>), dim3(grid),
                                dim3(256), 0, st, g);
