@@ -213,6 +213,16 @@ GEMM_CASES = [
     (999, 256, 100, False, True, "bf16", "bf16", "bf16"),
     (256, 47, 70003, True, False, "bf16", "bf16", "f32"),
     (70, 50, 30, True, True, "bf16", "bf16", "f32"),
+    # interior 128 x 128 tiles with a K span of 256 or more: the loads go two
+    # slabs ahead (weight gradients and bf16-A products); odd and even slab
+    # counts end the pipelined loop differently, and a ragged M mixes in edge
+    # tiles that take the checked one-slab loop
+    (256, 128, 4096, True, False, "f32", "f32", "f32"),
+    (128, 256, 272, True, False, "f32", "f32", "f32"),
+    (256, 256, 288, True, False, "bf16", "bf16", "f32"),
+    (2048, 256, 272, False, False, "bf16", "f32", "bf16"),
+    (2100, 256, 288, False, False, "bf16", "f32", "f32"),
+    (1024, 128, 256, False, False, "bf16", "bf16", "f32"),
 ]
 
 
