@@ -97,8 +97,8 @@ def spmm_compulsory_bytes(n, nnz, d, s_in=4, s_out=4, edge_weights=True):
 def oracle_graph(k):
     from oracle.graph import build_graph
     from sparse_message_passing_amd import synth
-    inp = synth.config_inputs(k)
-    return build_graph(inp["src"], inp["dst"], int(inp["n"]), synth.CONFIGS[k]["symmetric"]), inp
+    inp = synth.workload_inputs(k)
+    return build_graph(inp["src"], inp["dst"], int(inp["n"]), synth.WORKLOADS[k]["symmetric"]), inp
 
 
 def row_sample(og, edges):
@@ -124,7 +124,7 @@ def cpu_oracle_kernels(k, og, inp, edges=1_000_000):
     import oracle
     from sparse_message_passing_amd import synth
     allt = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    cfg = synth.CONFIGS[k]
+    cfg = synth.WORKLOADS[k]
     out = {"threads_all": allt}
     jobs = []
     # inputs already in the oracle's float64, so the timed calls convert nothing
@@ -196,9 +196,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream()
-    cfg = synth.CONFIGS[a.config]
+    cfg = synth.WORKLOADS[a.config]
     t0 = time.time()
-    inp = synth.config_inputs(a.config)
+    inp = synth.workload_inputs(a.config)
     n = int(inp["n"])
     print(f"# inputs ready ({time.time() - t0:.1f} s)", file=sys.stderr, flush=True)
     t0 = time.time()

@@ -18,7 +18,7 @@ Recipes (all numpy ``Generator(PCG64(seed))``):
   (a heavy-tailed graph with a single ~17K hub, like ogbn-products).
 * features ~ N(0, 1) (float32), Glorot-uniform weights, uniform labels.
 
-Config k uses seed 1000*k + {1 graph, 2 features, 3 weights, 4 labels or
+Workload k uses seed 1000*k + {1 graph, 2 features, 3 weights, 4 labels or
 upstream gradient, 5 marginal rows}; the Philox seed of the quantiser is
 1000*k + 6.
 """
@@ -29,7 +29,7 @@ import numpy as np
 
 __all__ = [
     "rng", "gnm_pairs", "rmat_edges", "chung_lu_pairs", "normal", "glorot",
-    "labels", "marginal_rows", "random_bits", "CONFIGS", "config_inputs",
+    "labels", "marginal_rows", "random_bits", "WORKLOADS", "workload_inputs",
 ]
 
 
@@ -139,7 +139,7 @@ def random_bits(m: int, choices, seed: int) -> np.ndarray:
 # The five workloads.  ``scale_down`` shrinks node and edge counts (same
 # generator, same degree) for parity tests the oracle finishes in seconds.
 # ---------------------------------------------------------------------------
-CONFIGS = {
+WORKLOADS = {
     1: dict(name="gcn1-gnm1k", kind="gcn", graph="gnm", n=1000, pairs=5000,
             symmetric=True, widths=[64, 64], relu_last=True, dtype="f32"),
     2: dict(name="gcn3-rmat20", kind="gcn", graph="rmat", scale=20, avg_deg=16,
@@ -154,10 +154,10 @@ CONFIGS = {
 }
 
 
-def config_graph(k: int, scale_down: int = 0):
-    """Raw edge list (src, dst, n) of config k.  ``scale_down`` halves the node
+def workload_graph(k: int, scale_down: int = 0):
+    """Raw edge list (src, dst, n) of workload k.  ``scale_down`` halves the node
     count that many times, keeping the average degree."""
-    cfg = CONFIGS[k]
+    cfg = WORKLOADS[k]
     seed = 1000 * k + 1
     if cfg["graph"] == "gnm":
         n = cfg["n"] >> scale_down
@@ -178,15 +178,15 @@ def config_graph(k: int, scale_down: int = 0):
     return s, d, n
 
 
-def config_inputs(k: int, scale_down: int = 0, cache: bool = True):
-    """All seeded inputs of config k as a dict of numpy arrays (cached on disk)."""
-    cfg = CONFIGS[k]
+def workload_inputs(k: int, scale_down: int = 0, cache: bool = True):
+    """All seeded inputs of workload k as a dict of numpy arrays (cached on disk)."""
+    cfg = WORKLOADS[k]
     cdir = os.environ.get("GNNMP_INPUT_CACHE", os.path.join(os.environ.get("TMPDIR", "/tmp"), "gnnmp_inputs"))
     path = os.path.join(cdir, f"cfg{k}_sd{scale_down}.npz")
     if cache and os.path.exists(path):
         with np.load(path, allow_pickle=False) as z:
             return {key: z[key] for key in z.files}
-    src, dst, n = config_graph(k, scale_down)
+    src, dst, n = workload_graph(k, scale_down)
     out = dict(src=src, dst=dst, n=np.int64(n))
     base = 1000 * k
     if cfg["kind"] == "gcn":

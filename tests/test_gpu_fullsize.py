@@ -31,7 +31,7 @@ def sample_rows(og, k, seed):
 @pytest.fixture(scope="module")
 def c2():
     t = time.time()
-    inp = synth.config_inputs(2)
+    inp = synth.workload_inputs(2)
     n = int(inp["n"])
     g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
     og = build_graph(inp["src"], inp["dst"], n, True)
@@ -140,7 +140,7 @@ def test_c2_gemm_q8_sampled_rows_bit_exact():
 @pytest.fixture(scope="module")
 def c3():
     t = time.time()
-    inp = synth.config_inputs(3)
+    inp = synth.workload_inputs(3)
     n = int(inp["n"])
     g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=False, csc=True)
     og = build_graph(inp["src"], inp["dst"], n, False)
@@ -150,7 +150,7 @@ def c3():
 
 def test_c3_gat_forward_sampled(c3):
     g, og, inp = c3
-    cfg = synth.CONFIGS[3]
+    cfg = synth.WORKLOADS[3]
     h, dh, slope = cfg["heads"], cfg["d_head"], cfg["slope"]
     X, W, a_s, a_d = inp["X"], inp["W"], inp["a_src"], inp["a_dst"]
     Y = torch.empty((og.n, h * dh), device="cuda")
@@ -208,7 +208,7 @@ def test_c3_sddmm_add_full_bit_exact(c3):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("bits", [2, 4, 8, "mixed"])
 def test_c5_quantise_full_bit_exact(bits):
-    inp = synth.config_inputs(5)
+    inp = synth.workload_inputs(5)
     H, rows, seed = inp["H"], inp["rows"], int(inp["philox_seed"])
     b = inp["mixed_bits"] if bits == "mixed" else np.full(rows.size, bits, np.int32)
     Hd = to_dev(H)
@@ -233,7 +233,7 @@ def test_c5_quantise_full_bit_exact(bits):
 
 
 def test_c5_mixed_aggregate_sampled_rows():
-    inp = synth.config_inputs(5)
+    inp = synth.workload_inputs(5)
     n = int(inp["n"])
     g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
     og = build_graph(inp["src"], inp["dst"], n, True)
@@ -257,7 +257,7 @@ def test_c5_dequant_in_gather_forward_and_backward():
     # whole output bitwise equal to the two-kernel path, sampled rows against
     # the oracle; then the backward exchange of the embedding gradients
     from sparse_message_passing_amd.step import QuantExchange
-    inp = synth.config_inputs(5)
+    inp = synth.workload_inputs(5)
     n = int(inp["n"])
     g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
     og = build_graph(inp["src"], inp["dst"], n, True)
@@ -295,7 +295,7 @@ def test_c5_overlapped_exchange_schedules():
     # the split exchange at full size: three schedules bitwise equal, the
     # whole output against the oracle's local + remote sums
     from sparse_message_passing_amd.step import OverlapExchange
-    inp = synth.config_inputs(5)
+    inp = synth.workload_inputs(5)
     n = int(inp["n"])
     g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
     og = build_graph(inp["src"], inp["dst"], n, True)
@@ -311,7 +311,7 @@ def test_c5_overlapped_exchange_schedules():
 
 def test_c5_bit_width_statistics():
     # per-row range (bit-exact) and beta of every marginal row at full size
-    inp = synth.config_inputs(5)
+    inp = synth.workload_inputs(5)
     n = int(inp["n"])
     g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
     og = build_graph(inp["src"], inp["dst"], n, True)
@@ -330,7 +330,7 @@ def test_c5_bit_width_statistics():
 @pytest.fixture(scope="module")
 def c4():
     t = time.time()
-    inp = synth.config_inputs(4)
+    inp = synth.workload_inputs(4)
     n = int(inp["n"])
     g = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True)
     og = build_graph(inp["src"], inp["dst"], n, True)
@@ -376,7 +376,7 @@ def test_c3_sddmm_q8_sampled_bit_exact(c3):
     # Tango's quantised SDDMM dot at the full 2^21-node size: both 2 GB
     # operands quantised over the whole tensor, sampled rows bit-exact
     g, og, inp = c3
-    cfg = synth.CONFIGS[3]
+    cfg = synth.WORKLOADS[3]
     h, dh = cfg["heads"], cfg["d_head"]
     S = synth.normal((og.n, h * dh), 3101)
     D = synth.normal((og.n, h * dh), 3102)

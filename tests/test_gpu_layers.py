@@ -27,7 +27,7 @@ def gcn_mag(og, X, W):
 
 @pytest.fixture(scope="module")
 def c1():
-    inp = synth.config_inputs(1)
+    inp = synth.workload_inputs(1)
     g, og = graph_pair(inp["src"], inp["dst"], int(inp["n"]), True, csc=False)
     return g, og, inp
 
