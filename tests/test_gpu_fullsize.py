@@ -117,6 +117,37 @@ def test_c2_gemm_sampled(shape):
         check_close(from_dev(C)[:, cols], ref, mag, what="gemm tn (weight gradient)")
 
 
+@pytest.mark.parametrize("kind", ["nn", "tn"])
+def test_c4_bf16_gemm_sampled(kind):
+    # the bf16 workload's 256-wide products over 2.45M rows (a ragged last
+    # tile): the bf16 x f32 update into bf16 and the bf16 x bf16 weight
+    # gradient (split over K), both on the two-slabs-ahead load pipeline
+    n = synth.WORKLOADS[4]["n"]
+    r = np.random.default_rng(44)
+    A = bf16_values(synth.normal((n, 256), 41))
+    if kind == "nn":
+        W = synth.glorot(256, 256, 42)
+        C = torch.empty((n, 256), dtype=torch.bfloat16, device="cuda")
+        gnnmp.gnn_gemm(to_dev(A, torch.bfloat16), to_dev(W), C)
+        rows = np.unique(np.concatenate([r.choice(n, 4096, replace=False), np.arange(n - 64, n)]))
+        ref = A[rows].astype(np.float64) @ W
+        mag = np.abs(A[rows]).astype(np.float64) @ np.abs(W)
+        check_close(from_dev(C)[rows], ref, mag, bf16_out=True, what="bf16 update nn 256x256")
+    else:
+        B = bf16_values(synth.normal((n, 256), 43))
+        C = torch.empty((256, 256), device="cuda")
+        gnnmp.gnn_gemm(to_dev(A, torch.bfloat16), to_dev(B, torch.bfloat16), C, transA=True)
+        cols = r.choice(256, 6, replace=False)
+        ref = np.zeros((256, cols.size))
+        mag = np.zeros((256, cols.size))
+        for i in range(0, n, 1 << 18):  # float64 in row chunks
+            a = A[i:i + (1 << 18)].astype(np.float64)
+            bc = B[i:i + (1 << 18), cols].astype(np.float64)
+            ref += a.T @ bc
+            mag += np.abs(a).T @ np.abs(bc)
+        check_close(from_dev(C)[:, cols], ref, mag, what="bf16 weight gradient tn 256x256")
+
+
 def test_c2_gemm_q8_sampled_rows_bit_exact():
     # the quantisation-aware GEMM at the 256 -> 256 update's full shape: the
     # tensor-wide scales and the codes of the sampled rows from the oracle,
