@@ -294,6 +294,23 @@ def main():
             extra["gemm_q8_256x256_ms"] = round(q8_ms, 4)
             extra["gemm_q8_256x256_tops_incl_quantise"] = round(2.0 * g.n * d * d / (q8_ms * 1e-3) / 1e12, 2)
         extra["gemm_dW_256x256_tflops"] = round(2.0 * g.n * d * d / (dw_ms * 1e-3) / 1e12, 2)
+        if a.config == 2:
+            # GraphSAGE's mean aggregator on the same edges: the aggregation
+            # alone and a 256 -> 256 layer forward + backward (the backward
+            # runs the transposed mean operator over the CSC view)
+            gs = gnnmp.gnn_graph_create(n, inp["src"], inp["dst"], symmetrize=True, csc=True)
+            extra["sage_mean_spmm_d256_ms"] = round(event_time(
+                lambda: gnnmp.gnn_spmm(gs, X, Y, weights="mean", ws=ws), a.kernel_reps, stream), 4)
+            Ys = torch.empty_like(X)
+            with torch.cuda.stream(stream):
+                dYs = torch.randn_like(X)
+            dXs = torch.empty_like(X)
+            dWs = torch.empty((d, d), device=dev)
+            extra["sage_layer_fwd_ms"] = round(event_time(
+                lambda: gnnmp.gnn_sage_layer_fwd(gs, X, Wt, Ys, True), a.kernel_reps, stream), 4)
+            extra["sage_layer_bwd_ms"] = round(event_time(
+                lambda: gnnmp.gnn_sage_layer_bwd(gs, X, Wt, Ys, dYs, True, dWs, dX=dXs), a.kernel_reps, stream), 4)
+            del Ys, dYs, dXs, gs
     if cfg["kind"] == "gat":
         # the attention-gradient SDDMM dot as a primitive (f32), and Tango's
         # variant on 8-bit codes (maxima + quantisation of both operands +
