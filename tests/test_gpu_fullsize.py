@@ -66,6 +66,35 @@ def test_c2_aggregation_sampled_rows(c2, d):
     check_close(from_dev(Yb[:, :d])[rows], ref, mag, what=f"C2 aggregation d={d}")
 
 
+def test_c2_mean_aggregation_sampled(c2):
+    # GraphSAGE's mean aggregator at 2^20 nodes, 256 wide (weight 1/row
+    # length), and its transpose over the CSC view (the layer backward)
+    _, og, inp = c2
+    gs = gnnmp.gnn_graph_create(og.n, inp["src"], inp["dst"], symmetrize=True, csc=True)
+    d = 256
+    X = synth.normal((og.n, d), 91)
+    Xd = to_dev(X)
+    Y = torch.empty_like(Xd)
+    w = og.mean_weights()
+    gnnmp.gnn_spmm(gs, Xd, Y, weights="mean")
+    rows = sample_rows(og, 4096, 91)
+    sg, eids = sub_rows(og, rows)
+    check_close(from_dev(Y)[rows], oracle.spmm(sg, X, w[eids]), oracle.spmm(sg, np.abs(X), w[eids]),
+                what="C2 mean aggregation")
+    gnnmp.gnn_spmm(gs, Xd, Y, weights="mean", transpose=True)
+    # output row u of the transpose sums w[e] X[v] over u's out-edges (u -> v)
+    colptr, crow, ceid = og.csc()
+    cols = sample_rows(og, 4096, 92)
+    lens = colptr[cols + 1] - colptr[cols]
+    idx = np.concatenate([np.arange(colptr[u], colptr[u + 1]) for u in cols])
+    rp = np.zeros(cols.size + 1, np.int64)
+    rp[1:] = np.cumsum(lens)
+    tg = oracle.OracleGraph(cols.size, rp, crow[idx].astype(np.int32), np.repeat(cols.astype(np.int32), lens))
+    wt = w[ceid[idx]]
+    check_close(from_dev(Y)[cols], oracle.spmm(tg, X, wt), oracle.spmm(tg, np.abs(X), wt),
+                what="C2 transposed mean aggregation")
+
+
 def test_c2_first_layer_forward_sampled_rows(c2):
     # ReLU((A_hat X) W1) at 2^20 nodes, 128 -> 256 (aggregate first)
     g, og, inp = c2
