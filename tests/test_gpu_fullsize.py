@@ -250,6 +250,81 @@ def test_c3_gat_forward_sampled(c3):
     check_close(from_dev(Y)[rows], ref, mY, what="C3 GAT output")
 
 
+def test_c3_gat_backward_sampled(c3):
+    # the layer backward at 2^21 nodes in the launch configuration the bench
+    # times, dX on sampled nodes u: every step between dY and dX (SDDMM dot,
+    # softmax backward, LeakyReLU', in- and out-edge sums, the transposed
+    # SpMM, the rank-1 terms, the GEMM) recomputed by the oracle from X, W,
+    # a and dY for those nodes only.  u needs the full in-edge rows of u and
+    # of every destination of u's out-edges.
+    g, og, inp = c3
+    cfg = synth.WORKLOADS[3]
+    h, dh, slope = cfg["heads"], cfg["d_head"], cfg["slope"]
+    hd = h * dh
+    X, W, a_s, a_d, dY = inp["X"], inp["W"], inp["a_src"], inp["a_dst"], inp["dY"]
+    Xd, Wd, asd, add = to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d)
+    Y = torch.empty((og.n, hd), device="cuda")
+    saved = torch.empty(gnnmp.gnn_gat_saved_size(g, h, dh), dtype=torch.uint8, device="cuda")
+    gnnmp.gnn_gat_layer_fwd(g, Xd, Wd, asd, add, h, dh, slope, Y, saved)
+    dX = torch.empty((og.n, X.shape[1]), device="cuda")
+    dW = torch.empty((X.shape[1], hd), device="cuda")
+    das = torch.empty((h, dh), device="cuda")
+    dad = torch.empty((h, dh), device="cuda")
+    gnnmp.gnn_gat_layer_bwd(g, Xd, Wd, asd, add, h, dh, slope, Y, to_dev(dY), saved, dW, das, dad, dX=dX)
+    colptr, crow, _ = og.csc()
+    outdeg = np.diff(colptr)
+    r = np.random.default_rng(7)
+    U = np.unique(np.concatenate([np.argsort(-outdeg, kind="stable")[:2],
+                                  r.choice(og.n, 126, replace=False)])).astype(np.int64)
+    dX_gpu = from_dev(dX[torch.from_numpy(U).cuda()])
+    del dX, dW, Y, saved
+    log("C3 backward on the GPU done")
+    V = np.unique(np.concatenate([U] + [crow[colptr[u]:colptr[u + 1]].astype(np.int64) for u in U]))
+    sg, _ = sub_rows(og, V)
+    need = np.unique(np.concatenate([sg.col.astype(np.int64), V]))
+    loc = oracle.OracleGraph(sg.n, sg.row_ptr, np.searchsorted(need, sg.col).astype(np.int32),
+                             np.searchsorted(need, sg.dst).astype(np.int32))
+    row_e = np.repeat(np.arange(loc.n), np.diff(loc.row_ptr))
+    log(f"C3 backward oracle: {U.size} nodes, {V.size} rows, {loc.nnz} edges, {need.size} rows of H'")
+    Hp = oracle.to_f32(X[need].astype(np.float64) @ W)
+    S = oracle.to_f32(oracle.gat_scores(Hp, a_s, h))
+    D = oracle.to_f32(oracle.gat_scores(Hp, a_d, h))
+    Ep, E = oracle.sddmm_add(loc, S, D, slope)
+    alpha = oracle.to_f32(oracle.edge_softmax(loc, E))
+    dYV = dY[V]
+    dal = oracle.to_f32(oracle.sddmm_dot(loc, dYV, Hp, h))
+    dE = oracle.to_f32(oracle.edge_softmax_bwd(loc, alpha, dal))
+    fac = np.where(Ep > 0, 1.0, float(np.float32(slope)))
+    dEp = oracle.to_f32(dE * fac)
+    ru = np.searchsorted(V, U)
+    dD = oracle.to_f32(oracle.edge_reduce(loc, dEp))[ru]
+    # the out-edges of u are the edges whose source is u
+    nu = np.searchsorted(need, U)
+    out_e = np.nonzero(np.isin(loc.col, nu))[0]
+    pos = np.searchsorted(nu, loc.col[out_e])
+    dS = np.zeros((U.size, h))
+    np.add.at(dS, pos, dEp[out_e].astype(np.float64))
+    dS = oracle.to_f32(dS)
+    agg = np.zeros((U.size, hd))
+    contrib = alpha[out_e].astype(np.float64)[:, :, None] * dYV[row_e[out_e]].astype(np.float64).reshape(-1, h, dh)
+    np.add.at(agg, pos, contrib.reshape(-1, hd))
+    rank1 = (dS.astype(np.float64)[:, :, None] * a_s[None] + dD.astype(np.float64)[:, :, None] * a_d[None])
+    dHp = oracle.to_f32(agg + rank1.reshape(-1, hd))
+    ref = dHp.astype(np.float64) @ W.T.astype(np.float64)
+    # magnitudes: each term's absolute value carried through the same steps
+    A = np.abs(alpha).astype(np.float64)
+    m_dal = oracle.sddmm_dot(loc, np.abs(dYV), np.abs(Hp), h)
+    m_dEp = A * (m_dal + oracle.edge_reduce(loc, A * m_dal)[row_e]) * fac
+    m_dD = oracle.edge_reduce(loc, m_dEp)[ru]
+    m_dS = np.zeros((U.size, h))
+    np.add.at(m_dS, pos, m_dEp[out_e])
+    m_agg = np.zeros((U.size, hd))
+    m_c = A[out_e][:, :, None] * np.abs(dYV[row_e[out_e]]).astype(np.float64).reshape(-1, h, dh)
+    np.add.at(m_agg, pos, m_c.reshape(-1, hd))
+    m_dHp = m_agg + (m_dS[:, :, None] * np.abs(a_s)[None] + m_dD[:, :, None] * np.abs(a_d)[None]).reshape(-1, hd)
+    check_close(dX_gpu, ref, m_dHp @ np.abs(W).T, what="C3 GAT dX")
+
+
 def test_c3_sddmm_add_full_bit_exact(c3):
     # every edge of the 42M-edge graph, scores drawn at random
     g, og, _ = c3
