@@ -111,6 +111,37 @@ def test_c2_first_layer_forward_sampled_rows(c2):
     check_close(from_dev(Y)[rows], ref, mag, what="C2 layer-1 forward")
 
 
+def test_c2_gcn_layer_256_fwd_bwd(c2):
+    # the 256 -> 256 ReLU layer at 2^20 nodes (GEMM, then aggregation):
+    # Y on sampled rows; the backward from the oracle's Y (so the ReLU mask is
+    # the same decision on both sides): dW in full, dX on sampled rows
+    g, og, inp = c2
+    n = og.n
+    X = synth.normal((n, 256), 81)
+    W = inp["W1"]
+    dY = synth.normal((n, 256), 82)
+    Xd, Wd = to_dev(X), to_dev(W)
+    Y = torch.empty((n, 256), device="cuda")
+    gnnmp.gnn_gcn_layer_fwd(g, Xd, Wd, Y, relu=True)
+    dW = torch.empty((256, 256), device="cuda")
+    dX = torch.empty((n, 256), device="cuda")
+    Y_ref, _ = oracle.gcn_layer_fwd(og, X, W, True)
+    log("C2 256-wide layer: oracle forward done")
+    gnnmp.gnn_gcn_layer_bwd(g, Xd, Wd, to_dev(Y_ref), to_dev(dY), True, dW, dX=dX)
+    rows = sample_rows(og, 4096, 83)
+    sg, eids = sub_rows(og, rows)
+    w = og.gcn_norm()[1]
+    need = np.unique(sg.col)
+    mZ = np.zeros((n, 256))
+    mZ[need] = np.abs(X[need]).astype(np.float64) @ np.abs(W)
+    check_close(from_dev(Y)[rows], Y_ref[rows], oracle.spmm(sg, mZ, w[eids]), what="C2 256-wide layer Y")
+    dX_ref, dW_ref = oracle.gcn_layer_bwd(og, X, None, Y_ref, dY, W, True)
+    log("C2 256-wide layer: oracle backward done")
+    m_dZ = oracle.spmm(og, np.abs(np.where(Y_ref > 0, dY, 0.0)), w)
+    check_close(from_dev(dW), dW_ref, np.abs(X).T.astype(np.float64) @ m_dZ, what="C2 256-wide layer dW")
+    check_close(from_dev(dX)[rows], dX_ref[rows], m_dZ[rows] @ np.abs(W).T, what="C2 256-wide layer dX")
+
+
 @pytest.mark.parametrize("shape", [("nn", 256, 256), ("nn", 128, 256), ("nn", 256, 41), ("nt", 256, 256),
                                    ("nt", 41, 256), ("tn", 256, 256)])
 def test_c2_gemm_sampled(shape):
