@@ -95,6 +95,22 @@ def test_c2_mean_aggregation_sampled(c2):
                 what="C2 transposed mean aggregation")
 
 
+@pytest.mark.parametrize("c", [41, 47])
+def test_full_softmax_xent(c2, c):
+    # the loss at the GCN workloads' logit shapes (2^20 x 41; 47 classes as
+    # the bf16 workload's, on the same rows): loss and every gradient entry
+    _, og, _ = c2
+    n = og.n
+    z = 3 * synth.normal((n, c), 60 + c)
+    lab = synth.labels(n, c, 70 + c).astype(np.int32)
+    loss_ref, dz_ref = oracle.softmax_xent(z, lab)
+    loss = torch.empty(1, device="cuda")
+    dz = torch.empty((n, c), device="cuda")
+    gnnmp.gnn_softmax_xent(to_dev(z), to_dev(lab), loss, dz)
+    assert abs(float(loss.item()) - loss_ref) <= RTOL32 * (abs(loss_ref) + np.abs(z).max())
+    check_close(from_dev(dz), dz_ref, np.abs(dz_ref) + 2.0 / n, what=f"loss gradient {n}x{c}")
+
+
 def test_c2_first_layer_forward_sampled_rows(c2):
     # ReLU((A_hat X) W1) at 2^20 nodes, 128 -> 256 (aggregate first)
     g, og, inp = c2
