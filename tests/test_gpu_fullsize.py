@@ -255,6 +255,20 @@ def c3():
     return g, og, inp
 
 
+def test_c3_graph_bit_exact(c3):
+    # the directed 2^21-node graph: CSR, the CSC view with its CSR slots, and
+    # both degree orders
+    g, og, _ = c3
+    ex = gnnmp.gnn_graph_export(g)
+    assert np.array_equal(ex["row_ptr"], og.row_ptr) and np.array_equal(ex["col"], og.col)
+    colptr, crow, ceid = og.csc()
+    assert np.array_equal(ex["col_ptr"], colptr) and np.array_equal(ex["csc_row"], crow)
+    assert np.array_equal(ex["csc_eid"], ceid)
+    assert np.array_equal(ex["perm"], og.degree_perm())
+    outdeg = np.diff(colptr)
+    assert np.array_equal(ex["perm_t"], np.lexsort((np.arange(og.n), -outdeg)).astype(np.int32))
+
+
 def test_c3_gat_forward_sampled(c3):
     g, og, inp = c3
     cfg = synth.WORKLOADS[3]
@@ -552,6 +566,43 @@ def test_c4_bf16_first_layer_and_aggregation_sampled(c4):
     gnnmp.gnn_spmm(g, Hd, Z)
     check_close(from_dev(Z)[rows], oracle.spmm(sg, H, w), oracle.spmm(sg, np.abs(H), np.abs(w)), rtol=RTOL16,
                 bf16_out=True, what="C4 aggregation d=256 (bf16)")
+
+
+def test_c4_bf16_layer_256_fwd_bwd(c4):
+    # the bf16 workload's 256 -> 256 ReLU layer at 2.45M nodes (bf16 features
+    # and gradients, binary32 weights and accumulators): Y on sampled rows;
+    # the backward from the oracle's Y: dW in full, dX on sampled rows
+    g, og, inp = c4
+    n = og.n
+    X = bf16_values(synth.normal((n, 256), 85))
+    W = inp["W1"]
+    dY = bf16_values(synth.normal((n, 256), 86))
+    Xd, Wd = to_dev(X, torch.bfloat16), to_dev(W)
+    Y = torch.empty((n, 256), dtype=torch.bfloat16, device="cuda")
+    gnnmp.gnn_gcn_layer_fwd(g, Xd, Wd, Y, relu=True)
+    rows = sample_rows(og, 4096, 87)
+    Y_gpu_rows = from_dev(Y)[rows]
+    del Y
+    Y_ref, _ = oracle.gcn_layer_fwd(og, X, W, True, dt="bf16")
+    log("C4 256-wide bf16 layer: oracle forward done")
+    sg, eids = sub_rows(og, rows)
+    w = og.gcn_norm()[1]
+    need = np.unique(sg.col)
+    mZ = np.zeros((n, 256))
+    mZ[need] = np.abs(X[need]).astype(np.float64) @ np.abs(W)
+    check_close(Y_gpu_rows, Y_ref[rows], oracle.spmm(sg, mZ, w[eids]), rtol=RTOL16, bf16_out=True,
+                what="C4 256-wide layer Y (bf16)")
+    dW = torch.empty((256, 256), device="cuda")
+    dX = torch.empty((n, 256), dtype=torch.bfloat16, device="cuda")
+    gnnmp.gnn_gcn_layer_bwd(g, Xd, Wd, to_dev(Y_ref, torch.bfloat16), to_dev(dY, torch.bfloat16), True, dW, dX=dX)
+    dX_rows = from_dev(dX)[rows]
+    dX_ref, dW_ref = oracle.gcn_layer_bwd(og, X, None, Y_ref, dY, W, True, dt="bf16")
+    log("C4 256-wide bf16 layer: oracle backward done")
+    m_dZ = oracle.spmm(og, np.abs(np.where(Y_ref > 0, dY, 0.0)), w)
+    check_close(from_dev(dW), dW_ref, np.abs(X).T.astype(np.float64) @ m_dZ, rtol=RTOL16,
+                what="C4 256-wide layer dW")
+    check_close(dX_rows, dX_ref[rows], m_dZ[rows] @ np.abs(W).T, rtol=RTOL16, bf16_out=True,
+                what="C4 256-wide layer dX (bf16)")
 
 
 def test_c3_sddmm_q8_sampled_bit_exact(c3):
