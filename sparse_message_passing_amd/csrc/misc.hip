@@ -15,6 +15,7 @@ namespace gnnmp {
 namespace {
 
 constexpr int kRowsPerBlock = 64;
+constexpr int kRowCache = 4;  // row entries a lane keeps in registers (rows of up to 4 LG classes)
 
 // A group of LG lanes per row (LG = 16 when the row has at most 64 classes,
 // else a whole wave), 256/LG groups per workgroup, each taking the block's
@@ -33,6 +34,41 @@ __global__ __launch_bounds__(256) void xent_rows(const float* z, int64_t n, int6
         if (v >= n) break;
         const float* zr = z + v * ld;
         const int32_t y = labels[v];
+        if (c <= LG * kRowCache) {
+            // the row read once into registers (lane holds j = lane + LG i);
+            // the same operations in the same order as the general path
+            float zv[kRowCache];
+#pragma unroll
+            for (int i = 0; i < kRowCache; ++i) {
+                const int64_t j = lane + LG * i;
+                zv[i] = j < c ? zr[j] : -INFINITY;
+            }
+            float m = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < kRowCache; ++i)
+                if (lane + LG * i < c) m = fmaxf(m, zv[i]);
+            m = group_max<LG>(m);
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kRowCache; ++i)
+                if (lane + LG * i < c) s += __expf(zv[i] - m);
+            s = group_sum<LG>(s);
+            const float lse = m + __logf(s);
+            grp_loss += lse - zr[y];
+            if (dz) {
+                const float is = 1.0f / s;
+#pragma unroll
+                for (int i = 0; i < kRowCache; ++i) {
+                    const int64_t j = lane + LG * i;
+                    if (j < c) {
+                        float p = __expf(zv[i] - m) * is;
+                        if (j == y) p -= 1.0f;
+                        dz[v * ldd + j] = p * inv_n;
+                    }
+                }
+            }
+            continue;
+        }
         float m = -INFINITY;
         for (int64_t j = lane; j < c; j += LG) m = fmaxf(m, zr[j]);
         m = group_max<LG>(m);
