@@ -350,6 +350,22 @@ def test_gat_layer_bwd_by_head_slabs():
     _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r)
 
 
+def test_gat_layer_deterministic(gatg):
+    # no atomics anywhere in the layer: two forward + backward passes give the
+    # same bits (hub rows chunked, partial rows summed in a fixed order)
+    g, og = gatg
+    from sparse_message_passing_amd.step import GatLayer
+    r = np.random.default_rng(91)
+    heads, dh, din = 4, 64, 256
+    L = GatLayer(g, to_dev(r.standard_normal((og.n, din)).astype(np.float32)), to_dev(synth.glorot(din, heads * dh, 3)),
+                 to_dev(synth.glorot(dh, 1, 4, shape=(heads, dh))), to_dev(synth.glorot(dh, 1, 5, shape=(heads, dh))),
+                 heads, dh, 0.2, to_dev(r.standard_normal((og.n, heads * dh)).astype(np.float32)))
+    L.step()
+    first = [t.clone() for t in (L.Y, L.dX, L.dW, L.da_src, L.da_dst)]
+    L.step()
+    assert all(torch.equal(a, b) for a, b in zip(first, (L.Y, L.dX, L.dW, L.da_src, L.da_dst)))
+
+
 @pytest.mark.parametrize("heads,dh", [(3, 16), (2, 12), (1, 512)])
 def test_gat_bwd_rejects_unsupported_shapes(heads, dh):
     # the backward's out-edge pass needs 1, 2, 4 or 8 heads and d_head a power
