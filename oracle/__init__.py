@@ -36,11 +36,10 @@ from .graph import OracleGraph, build_graph  # noqa: F401
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "_build", "liboracle.so")
 
-# Functions without an independent pin (the oracle's own definition is the only reference).
-UNPINNED = {
-    "philox4x32_10": "exact output stream not pinned to published known-answer vectors "
-                     "(none available offline); pinned only statistically and by bijectivity",
-}
+# Functions without an independent pin (the oracle's own definition is the only
+# reference).  Empty: the Philox4x32-10 stream is compared word for word with
+# rocRAND's engine (tests/test_oracle_philox_pin.py).
+UNPINNED = {}
 
 
 def build(force: bool = False) -> str:
