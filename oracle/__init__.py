@@ -113,10 +113,14 @@ def to_f32(x):
 
 def to_bf16(x):
     """Round to bfloat16 (round-to-nearest-even) through binary32; returns
-    float32 values that are exactly representable in bfloat16."""
+    float32 values that are exactly representable in bfloat16.  A NaN stays a
+    NaN of the same sign with the quiet bit set (rounding its bits would carry
+    a payload held only in the low half into the exponent: an infinity)."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
     u = f.view(np.uint32).astype(np.uint64)
     r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = np.where(nan, ((u >> 16) | 0x40) << 16, r)
     return r.astype(np.uint32).view(np.float32)
 
 

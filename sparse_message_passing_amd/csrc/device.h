@@ -11,9 +11,12 @@ typedef uint16_t bf16_t;  // bfloat16 storage
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// round-to-nearest-even; NaN stays NaN, infinities stay infinite
+// round-to-nearest-even; infinities stay infinite, and a NaN stays a NaN of
+// the same sign (quiet bit set: a payload only in the low 16 bits would
+// otherwise round into the exponent and read as an infinity)
 __device__ __forceinline__ bf16_t f2bf(float f) {
     uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return static_cast<bf16_t>(u >> 16);
 }

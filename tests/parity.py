@@ -5,8 +5,10 @@ Tolerance (floating point): a reduction output r (a sum of terms t_i) is
 accepted when |gpu - r| <= rtol * M with M = sum |t_i| computed by the
 oracle on absolute values; binary32 accumulation gives rtol = 1e-4 (an
 error of that size needs ~1000 ulps of cancellation-free drift).  A
-bfloat16 store adds half an ulp of bf16, 2^-9 |r|, which the check allows
-on top (2e-2 * M is the bf16 bar; the accumulation is still binary32).
+bfloat16 store adds at most half an ulp of bf16: with 8 significant bits
+that is at most 2^-8 |r| (the bound at r just above a power of two), which
+the check allows on top (2e-2 * M is the bf16 bar; the accumulation is still
+binary32).
 Integer, index and code outputs are compared for equality.
 """
 from __future__ import annotations

@@ -150,6 +150,30 @@ def test_bf16_rounding_rne():
     assert y.tolist() == [1.0, 1.0, 1.0 + 2 ** -7, 1.0, -2.5, 0.0]
 
 
+def test_bf16_rounding_against_torch_and_nan():
+    """The store rounding against torch's CPU conversion to bfloat16 (a
+    library round-to-nearest-even) on random bit patterns of every exponent,
+    ties, the largest finite values and infinities; NaNs (which torch turns
+    into one canonical NaN) must stay NaNs of their sign, also those whose
+    payload lies only in the low 16 bits."""
+    import torch
+    r = np.random.default_rng(31)
+    bits = r.integers(0, 2**32, 200_000, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0x00000000, 0x80000000, 0x00000001, 0x00008000, 0x00018000, 0x3F808000, 0x3F818000,
+                        0x3F80FFFF, 0x7F7FFFFF, 0x7F7F7FFF, 0x7F7F8000, 0xFF7FFFFF, 0x7F800000, 0xFF800000,
+                        0x7F800001, 0xFF800001, 0x7F80FFFF, 0x7FC00000, 0xFFFFFFFF, 0x7F807FFF], np.uint32)
+    bits = np.concatenate([special, bits])
+    x = bits.view(np.float32)
+    got = oracle.to_bf16(x)
+    nan = np.isnan(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    assert np.all(np.isnan(got[nan]))
+    assert np.array_equal(np.signbit(got[nan]), np.signbit(x[nan]))
+    assert np.all(got.view(np.uint32) & 0xFFFF == 0)
+    assert oracle.to_bf16(np.array([0x7F800001], np.uint32).view(np.float32)).view(np.uint32)[0] == 0x7FC00000
+
+
 @pytest.mark.parametrize("d_in,d_out,relu", [(8, 8, True), (6, 10, True), (10, 3, False)])
 def test_sage_fwd_dense_and_bwd_finite_difference(d_in, d_out, relu):
     # forward against D^-1 A dense on a directed graph (M is not symmetric),
