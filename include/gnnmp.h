@@ -118,16 +118,31 @@ typedef struct {
     const int32_t* csc_row;   /* [nnz]  destination of each CSC slot        */
     const int32_t* csc_eid;   /* [nnz]  CSR slot of each CSC slot           */
     const int32_t* perm_t;    /* [n]    columns by out-degree desc, ties by id */
+    int symmetric;            /* 1: built with GNN_GRAPH_SYMMETRIZE (A_hat^T = A_hat) */
+    /* Degree buckets of the degree-ordered lists perm (in-degree) and perm_t
+     * (out-degree; all zero without CSC): bucket i holds positions
+     * [bucket_off[i], bucket_off[i+1]) -- degree > bucket_threshold[0], then
+     * degree > bucket_threshold[1], then the rest -- so bucket_off =
+     * {0, #rows with degree > 2048, #rows with degree > 256, n}.  The
+     * aggregation kernels give rows of the first bucket a whole workgroup in
+     * the per-row edge kernels and cut rows of the first two into 256-edge
+     * chunks; the thresholds are tuning choices of this library. */
+    int64_t bucket_threshold[2];   /* {2048, 256} */
+    int64_t bucket_off[4];
+    int64_t bucket_off_t[4];
 } gnn_graph_info_t;
 
 gnn_status_t gnn_graph_info(gnn_graph_t g, gnn_graph_info_t* out /* host */);
 
 /* Copy views back to host buffers (any pointer may be NULL to skip it).
  * w receives the GCN edge weights dinv[src]*dinv[dst] in CSR order
- * (binary32 product of the two binary32 factors).  Synchronous. */
+ * (binary32 product of the two binary32 factors); bucket_off and
+ * bucket_off_t receive int64[4] each, the bucket offsets of gnn_graph_info.
+ * The CSC outputs (col_ptr, csc_row, csc_eid, perm_t, bucket_off_t) need the
+ * CSC view (GNN_ERR_GRAPH otherwise).  Synchronous. */
 gnn_status_t gnn_graph_export(gnn_graph_t g, int64_t* row_ptr, int32_t* col, float* dinv, float* w,
-                              int32_t* perm, int64_t* col_ptr, int32_t* csc_row, int32_t* csc_eid,
-                              int32_t* perm_t /* all host */);
+                              int32_t* perm, int64_t* bucket_off, int64_t* col_ptr, int32_t* csc_row,
+                              int32_t* csc_eid, int32_t* perm_t, int64_t* bucket_off_t /* all host */);
 
 /* ------------------------------------------------------------------------
  * Primitives
@@ -341,9 +356,13 @@ gnn_status_t gnn_gcn_layer_fwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, i
                                void* saved, void* ws, size_t ws_bytes, void* stream);
 
 /* Its backward.  G = dY * [Y > 0] (ReLU'(0) = 0) when relu, else dY.
- *   GEMM-first:      dZ = A_hat G;  dW = X^T dZ;  dX = dZ W^T
- *   aggregate-first: dW = (A_hat X)^T G;  dX = A_hat (G W^T)
- * (A_hat is symmetric).  dY, Y [n, ldy] of y_dt; dX [n, ldx] of x_dt (NULL:
+ *   GEMM-first:      dZ = A_hat^T G;  dW = X^T dZ;  dX = dZ W^T
+ *   aggregate-first: dW = (A_hat X)^T G;  dX = A_hat^T (G W^T)
+ * A_hat^T is applied over the CSR view when the graph was built with
+ * GNN_GRAPH_SYMMETRIZE (A_hat^T = A_hat), otherwise over the CSC view
+ * (GNN_ERR_GRAPH without one: a graph that is not symmetrised, such as the
+ * parts gnn_graph_split returns, needs GNN_GRAPH_CSC for the backward).
+ * dY, Y [n, ldy] of y_dt; dX [n, ldx] of x_dt (NULL:
  * not formed); dW [d_in, d_out] f32.  relu_in = 1 says X is itself a ReLU
  * output: dX is then returned times [X > 0], the gradient with respect to
  * the previous layer's pre-activation, and that layer's backward is called
@@ -376,7 +395,9 @@ gnn_status_t gnn_sage_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, 
  * each destination's softmax maximum M and 1 / sum of exponentials Z per head
  * ([n, heads] each), and alpha as one plane of nnz values per head (CSR
  * order), in that order, each slice starting on a 256-byte boundary.  Needs
- * the CSC view only for the backward. */
+ * the CSC view only for the backward.  Shapes: 1, 2, 4 or 8 heads, d_head a
+ * power of two from 4 to 256 and heads * d_head <= 1024 (GNN_ERR_UNSUPPORTED
+ * otherwise, before anything is launched). */
 size_t gnn_gat_saved_size(gnn_graph_t g, int heads, int64_t d_head);
 size_t gnn_gat_workspace_size(gnn_graph_t g, int64_t d_in, int heads, int64_t d_head);
 gnn_status_t gnn_gat_layer_fwd(gnn_graph_t g, const float* X, int64_t d_in, const float* W, const float* a_src,

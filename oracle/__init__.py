@@ -349,7 +349,7 @@ def gcn_layer_bwd(g, X, saved, Y, dY, W, relu, need_dX=True, dt="f32"):
     # it the upstream gradient is consumed as it is
     G = store(np.where(Y > 0, dY, 0.0), dt) if relu else np.asarray(dY)
     if d_out <= d_in:
-        dZ = store(spmm(g, G, w), dt)          # A_hat symmetric: A_hat^T G = A_hat G
+        dZ = store(spmm(g, G, w, transpose=True), dt)      # A_hat^T G
         dW = store(gemm(X, dZ, transA=True), _wdt(dt))
         dX = store(gemm(dZ, W, transB=True), dt) if need_dX else None
         return dX, dW
@@ -357,7 +357,7 @@ def gcn_layer_bwd(g, X, saved, Y, dY, W, relu, need_dX=True, dt="f32"):
     if not need_dX:
         return None, dW
     T = store(gemm(G, W, transB=True), dt)
-    dX = store(spmm(g, T, w), dt)
+    dX = store(spmm(g, T, w, transpose=True), dt)      # A_hat^T (G W^T)
     return dX, dW
 
 

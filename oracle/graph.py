@@ -91,10 +91,16 @@ class OracleGraph:
         ids = np.arange(self.n, dtype=np.int64)
         return np.lexsort((ids, -self.deg)).astype(np.int32)
 
-    def bucket_offsets(self, thresholds):
+    def bucket_offsets(self, thresholds, by_out=False):
         """Given descending degree thresholds t_0 > t_1 > ..., offsets into the
-        degree-ordered row list where the degree first drops to <= t_i."""
-        d_sorted = self.deg[self.degree_perm()]
+        degree-ordered row list where the degree first drops to <= t_i (by_out:
+        the columns of the transposed view ordered by out-degree)."""
+        if by_out:
+            deg = np.bincount(self.col, minlength=self.n).astype(np.int64)
+            ids = np.arange(self.n, dtype=np.int64)
+            d_sorted = deg[np.lexsort((ids, -deg))]
+        else:
+            d_sorted = self.deg[self.degree_perm()]
         # d_sorted is non-increasing; count rows with degree > t
         off = [0]
         for t in thresholds:

@@ -80,6 +80,15 @@ gnn_status_t make_plan(Graph& g, const std::vector<int64_t>& ptr, RowPlan& p, st
     return GNN_OK;
 }
 
+// Offsets of the degree buckets in the degree-ordered row list: rows of
+// degree > kBlockRow, then > kChunk, then the rest: {0, n_block, n_heavy, n}.
+void bucket_offsets(const RowPlan& p, int64_t n, int64_t* off) {
+    off[0] = 0;
+    off[1] = p.n_block;
+    off[2] = p.n_heavy;
+    off[3] = n;
+}
+
 void free_graph(Graph& g) {
     for (void* p : g.allocations) (void)hipFree(p);
     g.allocations.clear();
@@ -136,6 +145,7 @@ gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const in
             g.n = n;
             g.nnz = n ? hg.row_ptr[n] : 0;
             g.has_csc = (flags & GNN_GRAPH_CSC) != 0;
+            g.symmetric = (flags & GNN_GRAPH_SYMMETRIZE) != 0;
             s = upload(g, hg.row_ptr, &g.row_ptr);
             if (s == GNN_OK) s = upload(g, hg.col, &g.col);
             if (s == GNN_OK) s = upload(g, hg.dinv, &g.dinv);
@@ -271,15 +281,23 @@ gnn_status_t gnn_graph_info(gnn_graph_t h, gnn_graph_info_t* out) {
     out->csc_row = g.csc_row;
     out->csc_eid = g.csc_eid;
     out->perm_t = g.plan[1].order;
+    out->symmetric = g.symmetric;
+    out->bucket_threshold[0] = kBlockRow;
+    out->bucket_threshold[1] = kChunk;
+    bucket_offsets(g.plan[0], g.n, out->bucket_off);
+    if (g.has_csc) bucket_offsets(g.plan[1], g.n, out->bucket_off_t);
     return GNN_OK;
 }
 
 gnn_status_t gnn_graph_export(gnn_graph_t h, int64_t* row_ptr, int32_t* col, float* dinv, float* w, int32_t* perm,
-                              int64_t* col_ptr, int32_t* csc_row, int32_t* csc_eid, int32_t* perm_t) {
+                              int64_t* bucket_off, int64_t* col_ptr, int32_t* csc_row, int32_t* csc_eid,
+                              int32_t* perm_t, int64_t* bucket_off_t) {
     GNN_TRY(check_graph(h, "gnn_graph_export"));
     const Graph& g = h->g;
-    if (!g.has_csc && (col_ptr || csc_row || csc_eid || perm_t))
+    if (!g.has_csc && (col_ptr || csc_row || csc_eid || perm_t || bucket_off_t))
         return fail(GNN_ERR_GRAPH, "gnn_graph_export: the graph has no CSC view");
+    if (bucket_off) bucket_offsets(g.plan[0], g.n, bucket_off);
+    if (bucket_off_t) bucket_offsets(g.plan[1], g.n, bucket_off_t);
     const size_t n1 = static_cast<size_t>(g.n + 1), n = static_cast<size_t>(g.n), e = static_cast<size_t>(g.nnz);
     if (row_ptr && g.row_ptr) GNN_HIP(hipMemcpy(row_ptr, g.row_ptr, n1 * 8, hipMemcpyDeviceToHost));
     if (col && e) GNN_HIP(hipMemcpy(col, g.col, e * 4, hipMemcpyDeviceToHost));

@@ -60,6 +60,7 @@ struct RowPlan {               // one per view (CSR by destination, CSC by sourc
 struct Graph {
     int64_t n = 0, nnz = 0;
     bool has_csc = false;
+    bool symmetric = false;       // built with GNN_GRAPH_SYMMETRIZE: A_hat^T = A_hat
     int64_t* row_ptr = nullptr;   // [n+1]
     int32_t* col = nullptr;       // [nnz]
     float* dinv = nullptr;        // [n]

@@ -58,8 +58,8 @@ GcnWs gcn_ws(const Graph& g, int64_t d_in, int64_t d_out) {
 }
 
 // One graph-convolution layer, Y = sigma(A X W), with A the GCN operator
-// (A_hat, symmetric) or the mean operator (not symmetric: the backward walks
-// its transpose over the CSC view).
+// A_hat or the mean operator; the backward applies A^T (the CSR view when A is
+// a symmetrised graph's A_hat, else the CSC view).
 gnn_status_t conv_fwd(const char* api, gnn_weights_t wmode, gnn_graph_t h, const void* X, gnn_dtype_t x_dt,
                       int64_t ldx, int64_t d_in,
                                const float* W, int64_t d_out, int relu, void* Y, gnn_dtype_t y_dt, int64_t ldy,
@@ -105,10 +105,15 @@ gnn_status_t conv_bwd(const char* api, gnn_weights_t wmode, gnn_graph_t h, const
                                size_t ws_bytes, void* stream) {
     GNN_REQUIRE(h, std::string(api) + ": graph handle is NULL");
     const Graph& g = h->g;
-    // the backward aggregates over the transposed operator: A_hat is
-    // symmetric (its CSR view serves), the mean operator is not (CSC view)
-    if (wmode == GNN_W_MEAN && !g.has_csc) return fail(GNN_ERR_GRAPH, std::string(api) + ": needs the CSC view");
-    const AggView bview = wmode == GNN_W_MEAN ? csc_view(g) : csr_view(g);
+    // the backward aggregates over the transposed operator: A_hat of a
+    // symmetrised graph is symmetric (its CSR view serves); A_hat of any
+    // other graph and the mean operator are not (CSC view: the GCN weight
+    // dinv[u] * dinv[v] is formed there from the same two factors)
+    const bool use_csr = wmode == GNN_W_GCN && g.symmetric;
+    if (!use_csr && !g.has_csc)
+        return fail(GNN_ERR_GRAPH, std::string(api) + ": the transposed aggregation needs the CSC view (graph not "
+                                                      "symmetrised)");
+    const AggView bview = use_csr ? csr_view(g) : csc_view(g);
     GNN_REQUIRE(d_in >= 1 && d_out >= 1, std::string(api) + ": widths must be >= 1");
     GNN_REQUIRE(ldx >= d_in && ldy >= d_out, std::string(api) + ": leading dimensions too small");
     GNN_REQUIRE((x_dt == GNN_F32 || x_dt == GNN_BF16) && (y_dt == GNN_F32 || y_dt == GNN_BF16),
@@ -269,6 +274,11 @@ gnn_status_t gnn_gat_layer_fwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     const Graph& g = h->g;
     GNN_REQUIRE(d_in >= 1 && heads >= 1 && d_head >= 1, "gnn_gat_layer_fwd: sizes must be >= 1");
     GNN_REQUIRE(g.n == 0 || (X && W && a_src && a_dst && Y && saved), "gnn_gat_layer_fwd: NULL pointer");
+    // the shapes the score, attention and aggregation kernels take, checked
+    // before the first launch (the same heads and d_head as the backward)
+    if (!gat_fused_bwd_supported(heads, d_head) || heads * d_head > 1024)
+        return fail(GNN_ERR_UNSUPPORTED, "gnn_gat_layer_fwd: needs 1, 2, 4 or 8 heads, d_head a power of two from 4 "
+                                         "to 256 and heads * d_head <= 1024");
     const size_t need = gnn_gat_workspace_size(h, d_in, heads, d_head);
     if (ws_bytes < need || (!ws && need))
         return fail(GNN_ERR_WORKSPACE, "gnn_gat_layer_fwd: workspace smaller than gnn_gat_workspace_size()");

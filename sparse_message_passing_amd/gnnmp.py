@@ -33,7 +33,7 @@ _SIGS = {
     "gnn_graph_destroy": ("P", "i"),
     "gnn_graph_split": ("PPPP", "i"),
     "gnn_graph_info": ("PP", "i"),
-    "gnn_graph_export": ("PPPPPPPPPP", "i"),
+    "gnn_graph_export": ("PPPPPPPPPPPP", "i"),
     "gnn_spmm_workspace_size": ("PiI", "S"),
     "gnn_spmm": ("PiiPiPiIPiIIiPSP", "i"),
     "gnn_edge_reduce": ("PiPiPP", "i"),
@@ -82,7 +82,8 @@ class _Info(C.Structure):
     _fields_ = [("n", C.c_int64), ("nnz", C.c_int64), ("max_in_degree", C.c_int64), ("max_out_degree", C.c_int64),
                 ("has_csc", C.c_int), ("row_ptr", C.c_void_p), ("col", C.c_void_p), ("dinv", C.c_void_p),
                 ("perm", C.c_void_p), ("col_ptr", C.c_void_p), ("csc_row", C.c_void_p), ("csc_eid", C.c_void_p),
-                ("perm_t", C.c_void_p)]
+                ("perm_t", C.c_void_p), ("symmetric", C.c_int), ("bucket_threshold", C.c_int64 * 2),
+                ("bucket_off", C.c_int64 * 4), ("bucket_off_t", C.c_int64 * 4)]
 
 
 _lib = None
@@ -172,6 +173,10 @@ class Graph:
         self.n, self.nnz = info.n, info.nnz
         self.max_in_degree, self.max_out_degree = info.max_in_degree, info.max_out_degree
         self.has_csc = bool(info.has_csc)
+        self.symmetric = bool(info.symmetric)
+        self.bucket_threshold = list(info.bucket_threshold)
+        self.bucket_off = list(info.bucket_off)
+        self.bucket_off_t = list(info.bucket_off_t)
 
     def __del__(self):
         if getattr(self, "h", None) and _lib is not None:
@@ -211,13 +216,13 @@ def gnn_graph_split(g: Graph, marginal):
 def gnn_graph_export(g: Graph):
     n, e = g.n, g.nnz
     out = dict(row_ptr=np.empty(n + 1, np.int64), col=np.empty(e, np.int32), dinv=np.empty(n, np.float32),
-               w=np.empty(e, np.float32), perm=np.empty(n, np.int32))
+               w=np.empty(e, np.float32), perm=np.empty(n, np.int32), bucket_off=np.empty(4, np.int64))
     if g.has_csc:
         out.update(col_ptr=np.empty(n + 1, np.int64), csc_row=np.empty(e, np.int32), csc_eid=np.empty(e, np.int32),
-                   perm_t=np.empty(n, np.int32))
+                   perm_t=np.empty(n, np.int32), bucket_off_t=np.empty(4, np.int64))
     P = lambda k: out[k].ctypes.data_as(C.c_void_p) if k in out else None
-    _check(lib().gnn_graph_export(g.h, P("row_ptr"), P("col"), P("dinv"), P("w"), P("perm"), P("col_ptr"),
-                                  P("csc_row"), P("csc_eid"), P("perm_t")))
+    _check(lib().gnn_graph_export(g.h, P("row_ptr"), P("col"), P("dinv"), P("w"), P("perm"), P("bucket_off"),
+                                  P("col_ptr"), P("csc_row"), P("csc_eid"), P("perm_t"), P("bucket_off_t")))
     return out
 
 

@@ -58,10 +58,22 @@ GCN_CASES = [  # d_in, d_out, relu, storage dtype, output dtype
 ]
 
 
-@pytest.mark.parametrize("case", GCN_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_gcn_layer_fwd_bwd(hubsym, case):
+@pytest.fixture(scope="module")
+def hubdir():
+    s, t = hub_edges(6000, 40000, 2500, 33)
+    return graph_pair(s, t, 6000, False, csc=True)
+
+
+GCN_DIRECTED_CASES = [GCN_CASES[0], GCN_CASES[1], GCN_CASES[3]]
+
+
+@pytest.mark.parametrize("which,case", [("hubsym", c) for c in GCN_CASES] + [("hubdir", c) for c in GCN_DIRECTED_CASES],
+                         ids=lambda c: c if isinstance(c, str) else "-".join(map(str, c)))
+def test_gcn_layer_fwd_bwd(request, which, case):
+    # on the directed graph A_hat is not symmetric, so the backward runs over
+    # the CSC view (A_hat^T); on the symmetrised one over the CSR view
     d_in, d_out, relu, dt, out_dt = case
-    g, og = hubsym
+    g, og = request.getfixturevalue(which)
     r = np.random.default_rng(d_in * d_out)
     X = oracle.store(r.standard_normal((og.n, d_in)), dt)
     W = synth.glorot(d_in, d_out, 5)
@@ -80,12 +92,12 @@ def test_gcn_layer_fwd_bwd(hubsym, case):
     w = og.gcn_norm()[1]
     G = np.abs(np.where(Y_ref > 0, dY, 0.0)) if relu else np.abs(dY)
     if d_out <= d_in:
-        MdZ = oracle.spmm(og, G, np.abs(w))
+        MdZ = oracle.spmm(og, G, np.abs(w), transpose=True)
         mag_dW = np.abs(X).T.astype(np.float64) @ MdZ
         mag_dX = MdZ @ np.abs(W).T
     else:
         mag_dW = oracle.spmm(og, np.abs(X), np.abs(w)).T @ G
-        mag_dX = oracle.spmm(og, G @ np.abs(W).T, np.abs(w))
+        mag_dX = oracle.spmm(og, G @ np.abs(W).T, np.abs(w), transpose=True)
     dYd = to_dev(dY, TDT[out_dt])
     Yd = to_dev(Y_ref, TDT[out_dt])
     sv = to_dev(saved_ref, TDT[dt]) if saved_ref is not None else None
@@ -108,12 +120,6 @@ SAGE_CASES = [  # d_in, d_out, relu, storage dtype
     (256, 41, False, "f32"),
     (100, 256, True, "bf16"),
 ]
-
-
-@pytest.fixture(scope="module")
-def hubdir():
-    s, t = hub_edges(6000, 40000, 2500, 33)
-    return graph_pair(s, t, 6000, False, csc=True)
 
 
 @pytest.mark.parametrize("case", SAGE_CASES, ids=lambda c: "-".join(map(str, c)))
@@ -149,6 +155,16 @@ def test_sage_layer_fwd_bwd(hubdir, case):
                              saved=to_dev(saved_ref, TDT[dt]) if saved_ref is not None else None)
     check_close(from_dev(dW), dW_ref, mag_dW, rtol=rtol, what="sage dW")
     check_close(from_dev(dX), dX_ref, mag_dX, rtol=rtol, bf16_out=dt == "bf16", what="sage dX")
+
+
+def test_gcn_bwd_directed_requires_csc():
+    # A_hat of a graph that is not symmetrised has no symmetric CSR shortcut
+    s, t = hub_edges(500, 2000, 100, 35)
+    g, og = graph_pair(s, t, 500, False, csc=False)
+    X = torch.zeros((og.n, 8), device="cuda")
+    W = torch.zeros((8, 8), device="cuda")
+    with pytest.raises(gnnmp.GnnError, match="CSC"):
+        gnnmp.gnn_gcn_layer_bwd(g, X, W, X, X, True, torch.empty_like(W), dX=torch.empty_like(X))
 
 
 def test_sage_bwd_requires_csc(hubsym):
@@ -381,6 +397,23 @@ def test_gat_bwd_rejects_unsupported_shapes(heads, dh):
     with pytest.raises(gnnmp.GnnError, match="power of two"):
         gnnmp.gnn_gat_layer_bwd(g, X, W, a, a, heads, dh, 0.2, Y, Y, saved, torch.empty_like(W), torch.empty_like(a),
                                 torch.empty_like(a))
+
+
+@pytest.mark.parametrize("heads,dh", [(3, 16), (2, 12), (1, 512), (8, 256)])
+def test_gat_fwd_rejects_unsupported_shapes(heads, dh):
+    # refused before the first launch: Y and the saved tensors stay untouched
+    s, t = hub_edges(64, 200, 10, 2)
+    g = gnnmp.gnn_graph_create(64, s, t, csc=True)
+    hd = heads * dh
+    X = torch.ones((64, 8), device="cuda")
+    W = torch.ones((8, hd), device="cuda")
+    a = torch.ones((heads, dh), device="cuda")
+    Y = torch.full((64, hd), 7.0, device="cuda")
+    saved = torch.full((gnnmp.gnn_gat_saved_size(g, heads, dh),), 5, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gnnmp.GnnError, match="power of two"):
+        gnnmp.gnn_gat_layer_fwd(g, X, W, a, a, heads, dh, 0.2, Y, saved)
+    torch.cuda.synchronize()
+    assert bool(torch.all(Y == 7.0)) and bool(torch.all(saved == 5))
 
 
 def test_gat_bwd_requires_csc():

@@ -92,6 +92,22 @@ def test_degree_perm_and_buckets():
         assert np.all((d[lo:hi] <= upper) & (d[lo:hi] > lower))
 
 
+def test_out_degree_buckets_brute_force():
+    # out-degree buckets of the transposed view, counted edge by edge
+    g0 = np.random.default_rng(8)
+    n = 150
+    src = (g0.integers(0, n, 2000) % 23).astype(np.int32)  # skew out-degrees
+    dst = g0.integers(0, n, 2000).astype(np.int32)
+    g = build_graph(src, dst, n, False)
+    outdeg = [0] * n
+    for u in g.col.tolist():
+        outdeg[u] += 1
+    th = [60, 20, 1]
+    want = [0] + [sum(1 for x in outdeg if x > t) for t in th] + [n]
+    assert g.bucket_offsets(th, by_out=True).tolist() == want
+    assert g.bucket_offsets(th).tolist() == [0] + [int(np.sum(g.deg > t)) for t in th] + [n]
+
+
 def _ring(n):
     s = np.arange(n, dtype=np.int32)
     return s, (s + 1) % n

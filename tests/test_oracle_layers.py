@@ -37,9 +37,11 @@ def test_gcn_fwd_dense(d_in, d_out):
     assert np.allclose(Y, ref, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("sym", [True, False], ids=["symmetrised", "directed"])
 @pytest.mark.parametrize("d_in,d_out,relu", [(8, 8, True), (6, 10, True), (10, 3, False), (5, 9, False)])
-def test_gcn_bwd_finite_difference(d_in, d_out, relu):
-    g = graph(2)
+def test_gcn_bwd_finite_difference(d_in, d_out, relu, sym):
+    # on a directed graph A_hat is not symmetric: the backward must apply A_hat^T
+    g = graph(2, sym=sym)
     r = np.random.default_rng(3)
     X = r.standard_normal((g.n, d_in))
     W = r.standard_normal((d_in, d_out))
