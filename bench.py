@@ -1,31 +1,42 @@
 """Benchmark of the per-layer GNN message-passing hot path on one GPU.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
 
-Default workload (config 2): 3-layer GCN forward + backward, binary32,
-R-MAT (a=0.57, b=c=0.19) with 2^20 nodes and average degree 16,
-symmetrised with self-loops and GCN normalisation; widths 128 -> 256 -> 256
--> 41; mean softmax cross-entropy against random labels.  A step is one
-forward pass, the loss, and the backward pass down to the first layer's
-weight gradient, with every input resident in HBM.
+Default workload (config 3): one GAT layer forward + backward, binary32,
+4 heads x 64, input width 256, on an R-MAT graph (a=0.57, b=c=0.19) with
+2^21 nodes, average degree 20, directed, with self-loops: H' = XW, the
+per-head scores, SDDMM-add + LeakyReLU(0.2) + edge softmax, the weighted
+aggregation, and the backward (SDDMM dot, softmax backward, edge sums, the
+transposed aggregation, dW, dX) for a seeded upstream gradient, with every
+input resident in HBM.
 
-Printed value: GEdge*feat/s = (sum over the step's aggregations of
-nnz * width) / step time.  Beside it: the roofline of the dominant kernel
-(the aggregation of the 256-wide layers, HBM-bound), timed with HIP events
-on its own stream, and the CPU oracle timed on a bounded sample of the same
-workload.
+Printed value: GEdge*feat/s = (edge x feature products of the step's
+aggregation-shaped passes) / step time; for the GAT layer the weighted
+aggregation, the SDDMM dot and the transposed aggregation (3 nnz h d_head).
+Beside it:
+  * roofline: the dominant kernel of the step (GAT: the backward's pass over
+    the out-edges; GCN and the quantised exchange: the 256-wide aggregation),
+    algorithmic bytes per launch / its average duration, timed with HIP events
+    on its own stream over the timed steps; `traffic` from the committed
+    rocprofv3 counter summary of the same kernel, when that summary was taken
+    on the current sources;
+  * kernels_measured: every instrumented kernel of a few further steps, with
+    its byte (or flop) model and fraction of the HBM (or matrix-core) peak;
+  * cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
-Other configs (timed the same way, for the record): 3 = one GAT layer
-(4 heads x 64, R-MAT 2^21, directed) forward + backward; 4 = the 3-layer
-GCN with bf16 feature storage on a 2.45M-node Chung-Lu graph (100 -> 256 ->
-256 -> 47); 5 = one partition's quantised exchange (30% marginal rows of a
-2^20-node R-MAT graph, 256 wide) followed by the aggregation.
+Other configs (--config): 2 = 3-layer GCN, binary32, R-MAT 2^20 (128 -> 256
+-> 256 -> 41, softmax cross-entropy); 4 = the 3-layer GCN with bf16 feature
+storage on a 2.45M-node Chung-Lu graph (100 -> 256 -> 256 -> 47); 5 = one
+partition's quantised exchange (30% marginal rows of a 2^20-node R-MAT graph,
+256 wide) followed by the aggregation.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,28 +47,38 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gcn3_rmat20_hbm_counters.md")
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
-def measured_traffic():
-    """HBM bytes per launch of the 256-wide aggregation, read from the
-    committed rocprofv3 counter summary; None when spmm.hip has changed
-    since the counters were taken (the summary records the source's sha1)."""
-    import hashlib
-    import re
+def source_digest():
+    """sha1 over every library source and the build script (compiler flags):
+    a counter summary taken on other sources no longer describes the kernel."""
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "sparse_message_passing_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
+    files.append(os.path.join(ROOT, "sparse_message_passing_amd", "build.py"))
+    for p in files:
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, key):
+    """HBM bytes per launch of kernel `key` on `workload`, read from the
+    committed rocprofv3 counter summary profiles/<workload>_hbm_counters.md;
+    None when there is none or it was taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             text = f.read()
-        nbytes = re.search(r"^- traffic bytes per launch: (\d+)$", text, re.M)
-        sha = re.search(r"^- spmm\.hip sha1: ([0-9a-f]{40})$", text, re.M)
-        src = os.path.join(ROOT, "sparse_message_passing_amd", "csrc", "spmm.hip")
-        with open(src, "rb") as f:
-            cur = hashlib.sha1(f.read()).hexdigest()
     except OSError:
         return None
-    if nbytes is None or sha is None or sha.group(1) != cur:
+    sha = re.search(r"^- source sha1: ([0-9a-f]{40})$", text, re.M)
+    hit = re.search(r"^- traffic bytes per launch \[" + re.escape(key) + r"\]: (\d+)$", text, re.M)
+    if sha is None or hit is None or sha.group(1) != source_digest():
         return None
-    return int(nbytes.group(1))
+    return int(hit.group(1))
 
 
 def parse():
@@ -65,9 +86,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--cpu-sample-edges", type=int, default=2_000_000)
     return ap.parse_args()
 
 
@@ -86,14 +108,91 @@ def event_time(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
-def spmm_compulsory_bytes(n, nnz, d, s_in=4, s_out=4, edge_weights=True):
-    """row_ptr (int64) + col (int32) + the GCN weights (one f32 per edge as
-    stored, else dinv, one f32 per node) + each input row once + each output
-    row once."""
-    w = 4 * nnz if edge_weights else 4 * n
-    return 8 * (n + 1) + 4 * nnz + w + s_in * n * d + s_out * n * d
+# ---------------------------------------------------------------------------
+# algorithmic work per launch of each instrumented kernel (bytes each array
+# must move at least once, or flops); n nodes, nnz edges incl. self-loops
+# ---------------------------------------------------------------------------
+def spmm_compulsory_bytes(n, nnz, d, s_in=4, s_out=4, edge_weights=True, heads=1):
+    """row_ptr (int64) + col (int32) + the edge weights (one f32 per edge and
+    head as stored, else dinv, one f32 per node) + each input row once + each
+    output row once + the degree order (int32 per row)."""
+    w = 4 * nnz * heads if edge_weights else 4 * n
+    return 8 * (n + 1) + 4 * nnz + w + s_in * n * d + s_out * n * d + 4 * n
 
 
+def gat_bwd_csc_bytes(n, nnz, h, dh):
+    """Per head slab: col_ptr, destination ids, the order, the H' and dY
+    slices read once, dH' slice written once, S and dS, the 16-byte
+    per-destination records, the dE plane written."""
+    return h * (8 * (n + 1) + 8 * nnz + 12 * n * dh + 28 * n)
+
+
+def kernel_model(key, n, nnz, ctx):
+    """(kind, amount) for an instrumented key: ("bytes", B) or ("flops", F, bytes);
+    None when the key has no model here."""
+    kv = dict(re.findall(r"(\w+)=(\S+)", key))
+    name = key.split()[0]
+    size = lambda t: 2 if t == "bf16" else 4
+    if name == "spmm_kernel":
+        m = re.search(r"(\w+)->(\w+)", key)
+        d, h = int(kv["d"]), int(kv["h"])
+        return ("bytes", spmm_compulsory_bytes(n, nnz, d, size(m.group(1)), size(m.group(2)), heads=h))
+    if name == "attn_fwd_kernel":
+        h = int(kv["h"])
+        return ("bytes", 8 * (n + 1) + 4 * nnz + 8 * n * h + 4 * nnz * h + 8 * n * h + 4 * n)
+    if name == "gat_bwd_csc_kernel":
+        return ("bytes", gat_bwd_csc_bytes(n, nnz, int(kv["h"]), int(kv["dh"])))
+    if name == "gat_in_sum_kernel":
+        h, dh = int(kv["h"]), int(kv["dh"])
+        return ("bytes", 8 * (n + 1) + 4 * nnz + 4 * nnz * h + 4 * n * h + 8 * n * h * dh + 4 * n)
+    if name == "sddmm_dot_kernel":
+        h, dh = int(kv["h"]), int(kv["dh"])
+        s = size(key.split()[-1])
+        return ("bytes", 8 * (n + 1) + 4 * nnz + 2 * s * n * h * dh + 4 * nnz * h)
+    if name == "softmax_fwd_kernel":
+        return ("bytes", 8 * (n + 1) + 8 * nnz * int(kv["h"]))
+    if name in ("quantize_kernel", "dequantize_kernel"):
+        b, d = int(kv["b"]), int(kv["d"])
+        m = ctx.get("quant_rows", {}).get(b)
+        if m is None:
+            return None
+        return ("bytes", 4 * m * d + m * d * b // 8 + 8 * m + 4 * m)
+    if name == "gemm":
+        M, N, K = int(kv["M"]), int(kv["N"]), int(kv["K"])
+        ab = re.search(r"(\w+),(\w+)->(\w+)", key)
+        sa, sb, sc = (size(ab.group(i)) for i in (1, 2, 3))
+        return ("flops", 2 * M * N * K, sa * M * K + sb * K * N + sc * M * N, ab.group(1), ab.group(2))
+    return None
+
+
+def kernel_table(gnnmp, keys, n, nnz, ctx):
+    out = {}
+    for key in keys:
+        cnt, tot = gnnmp.gnn_timer_result(key)
+        if cnt == 0:
+            continue
+        ms = tot / cnt
+        rec = {"launches": cnt, "ms_per_launch": round(ms, 4)}
+        m = kernel_model(key, n, nnz, ctx)
+        if m and m[0] == "bytes":
+            gbs = m[1] / (ms * 1e-3) / 1e9
+            rec.update(bound="hbm", bytes_per_launch=m[1], achieved_GBs=round(gbs, 1),
+                       frac=round(gbs / HBM_PEAK_GBS, 4))
+        elif m and m[0] == "flops":
+            flops, byts, ta, tb = m[1], m[2], m[3], m[4]
+            peak = BF16_MFMA_PEAK_TFLOPS if (ta == "bf16" and tb == "bf16") else FP32_MFMA_PEAK_TFLOPS
+            tf = flops / (ms * 1e-3) / 1e12
+            ceiling = min(peak, flops / byts * HBM_PEAK_GBS / 1e3)  # TFLOP/s the HBM roofline allows
+            rec.update(bound="mfma" if ceiling >= peak else "hbm", tflops=round(tf, 2), peak_tflops=peak,
+                       frac_of_peak=round(tf / peak, 4), ceiling_tflops=round(ceiling, 1),
+                       frac_of_ceiling=round(tf / ceiling, 4))
+        out[key] = rec
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baselines
+# ---------------------------------------------------------------------------
 def oracle_graph(k):
     from oracle.graph import build_graph
     from sparse_message_passing_amd import synth
@@ -101,45 +200,133 @@ def oracle_graph(k):
     return build_graph(inp["src"], inp["dst"], int(inp["n"]), synth.WORKLOADS[k]["symmetric"]), inp
 
 
-def row_sample(og, edges):
-    """Consecutive rows from inside the id range (R-MAT makes ids with few
-    one bits its hubs, so the start 0.7071 n has a typical mix) holding about
-    `edges` edges, as an oracle graph of their own (column ids stay global).
-    Returns it and its first edge slot."""
+def oracle_threads():
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_baseline_gcn_full(og, inp, work_per_pass, min_seconds=10.0, max_passes=3):
+    """The oracle's 3-layer forward+backward on the whole workload, repeated
+    until at least `min_seconds` of CPU work (at most `max_passes` passes)."""
+    import oracle
+    Ws = [inp["W0"], inp["W1"], inp["W2"]]
+    passes, dt = 0, 0.0
+    while passes < max_passes and (passes == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        oracle.gcn_forward_backward(og, inp["X"], Ws, inp["labels"])
+        dt += time.perf_counter() - t0
+        passes += 1
+    return dict(value=round(passes * work_per_pass / dt / 1e9, 4), unit="GEdge*feat/s", cores=oracle_threads(),
+                kind="oracle", sample=f"{passes} full 3-layer forward+backward pass(es) of the same workload "
+                                      f"({og.n} nodes, nnz {og.nnz}), {dt:.2f} s")
+
+
+def sample_graph(og, edges):
+    """A bounded sample of the workload's graph: the destination rows from
+    0.7071 n on (R-MAT gives ids with few one bits its hubs, so that start has
+    a typical mix) holding about `edges` in-edges, with every source of those
+    edges, relabelled compactly (ascending ids keep every row's order); the
+    sources outside the rows get their self-loop, so every node has a row.
+    Returns (oracle graph, original ids of its nodes)."""
     import oracle
     r0 = int(og.n * 0.7071)
     e0 = int(og.row_ptr[r0])
     r1 = int(np.searchsorted(og.row_ptr, e0 + edges))
     r1 = max(r0 + 1, min(r1, og.n))
     e1 = int(og.row_ptr[r1])
-    rp = og.row_ptr[r0:r1 + 1] - e0
-    return oracle.OracleGraph(r1 - r0, rp, og.col[e0:e1].copy(), (og.dst[e0:e1] - r0).astype(np.int32)), e0
+    col, dst = og.col[e0:e1].astype(np.int64), og.dst[e0:e1].astype(np.int64)
+    T = np.unique(np.concatenate([np.arange(r0, r1), col]))
+    extra = np.setdiff1d(T, np.arange(r0, r1))
+    col = np.concatenate([col, extra])
+    dst = np.concatenate([dst, extra])
+    key = np.searchsorted(T, dst) * T.size + np.searchsorted(T, col)
+    key.sort()
+    nd, nc = (key // T.size).astype(np.int32), (key % T.size).astype(np.int32)
+    rp = np.zeros(T.size + 1, np.int64)
+    rp[1:] = np.cumsum(np.bincount(nd, minlength=T.size))
+    return oracle.OracleGraph(int(T.size), rp, nc, nd), T
+
+
+EDGE_OPS = ("spmm", "sddmm_add", "sddmm_dot", "edge_softmax", "edge_softmax_bwd", "edge_reduce")
+
+
+def cpu_baseline_sampled(k, og, inp, work, edges):
+    """The oracle's own step (the same functions the parity tests check) run on
+    a bounded sample of the workload (sample_graph), with the time of its
+    per-edge calls (aggregations, SDDMM, edge softmax and its backward, edge
+    sums) and of the rest (dense products, scores, quantisation, loss, store
+    rounding: per-node work) kept apart; each part is scaled to the whole
+    workload (edges: nnz / sample nnz; the rest: n / sample nodes) and the
+    step work is divided by the scaled time."""
+    import oracle
+    from sparse_message_passing_amd import synth
+    cfg = synth.WORKLOADS[k]
+    sg, T = sample_graph(og, edges)
+    spent = {"edge": 0.0}
+    saved = {name: getattr(oracle, name) for name in EDGE_OPS}
+
+    def timed(fn):
+        def w(*a, **kw):
+            t0 = time.perf_counter()
+            try:
+                return fn(*a, **kw)
+            finally:
+                spent["edge"] += time.perf_counter() - t0
+        return w
+
+    for name, fn in saved.items():
+        setattr(oracle, name, timed(fn))
+    try:
+        t0 = time.perf_counter()
+        if cfg["kind"] == "gat":
+            X = inp["X"][T]
+            fw = oracle.gat_layer_fwd(sg, X, inp["W"], inp["a_src"], inp["a_dst"], cfg["heads"], cfg["slope"])
+            oracle.gat_layer_bwd(sg, fw, X, inp["W"], inp["a_src"], inp["a_dst"], inp["dY"][T], cfg["heads"],
+                                 cfg["slope"])
+        elif cfg["kind"] == "gcn":
+            Ws = [inp[f"W{i}"] for i in range(len(cfg["widths"]) - 1)]
+            oracle.gcn_forward_backward(sg, inp["X"][T], Ws, inp["labels"][T], dt=cfg.get("dtype", "f32"))
+        else:
+            sel = np.isin(T, inp["rows"])
+            rows = np.nonzero(sel)[0].astype(np.int32)
+            bits = inp["mixed_bits"][np.searchsorted(inp["rows"], T[sel])]
+            Hmix, _, _ = oracle.quantized_aggregate(sg, inp["H"][T], rows, bits, int(inp["philox_seed"]))
+        total = time.perf_counter() - t0
+    finally:
+        for name, fn in saved.items():
+            setattr(oracle, name, fn)
+    t_edge = spent["edge"]
+    t_node = total - t_edge
+    est = t_edge * og.nnz / sg.nnz + t_node * og.n / sg.n
+    return dict(value=round(work / est / 1e9, 4), unit="GEdge*feat/s", cores=oracle_threads(), kind="oracle",
+                sample=f"the oracle's whole step on {sg.n} of {og.n} nodes and {sg.nnz} of {og.nnz} edges "
+                       f"(the in-edges of destinations {int(og.n * 0.7071)}.. with their sources, relabelled): "
+                       f"{t_edge:.2f} s in per-edge calls scaled by {og.nnz / sg.nnz:.1f}, {t_node:.2f} s in "
+                       f"per-node work scaled by {og.n / sg.n:.2f}: {est:.1f} s estimated for the whole step")
 
 
 def cpu_oracle_kernels(k, og, inp, edges=1_000_000):
     """The oracle's own steps timed on one host thread and on all of them, on
-    a bounded sample of the workload: the 256-wide aggregation (GCN
-    workloads), the SDDMM dot and the edge softmax (GAT), the quantiser over
-    the marginal rows (quantised exchange).  Rates in the bench's units."""
+    a bounded row sample: the 256-wide aggregation (GCN workloads), the SDDMM
+    dot and the edge softmax (GAT), the quantiser over the marginal rows
+    (quantised exchange).  Rates in the bench's units."""
     import oracle
     from sparse_message_passing_amd import synth
-    allt = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    allt = oracle_threads()
     cfg = synth.WORKLOADS[k]
     out = {"threads_all": allt}
     jobs = []
-    # inputs already in the oracle's float64, so the timed calls convert nothing
-    if cfg["kind"] == "gcn" or cfg["kind"] == "quant":
-        sub, e0 = row_sample(og, edges)
-        X = np.random.default_rng(77).standard_normal((og.n, 256))
-        w = og.gcn_norm()[1][e0:e0 + sub.nnz].astype(np.float64)
-        jobs.append(("spmm_d256_gedge_feat_s", lambda: oracle.spmm(sub, X, w), sub.nnz * 256, f"{sub.n} rows, {sub.nnz} edges"))
+    sub, T = sample_graph(og, edges)
+    if cfg["kind"] in ("gcn", "quant"):
+        X = np.random.default_rng(77).standard_normal((sub.n, 256))
+        w = sub.gcn_norm()[1].astype(np.float64)
+        jobs.append(("spmm_d256_gedge_feat_s", lambda: oracle.spmm(sub, X, w), sub.nnz * 256,
+                     f"{sub.n} nodes, {sub.nnz} edges"))
     if cfg["kind"] == "gat":
-        sub, e0 = row_sample(og, edges)
-        A = np.random.default_rng(78).standard_normal((sub.n, 256))   # destination rows of the sample
-        B = np.random.default_rng(79).standard_normal((og.n, 256))
+        A = np.random.default_rng(78).standard_normal((sub.n, 256))
+        B = np.random.default_rng(79).standard_normal((sub.n, 256))
         E = np.random.default_rng(80).standard_normal((sub.nnz, 4))
         jobs.append(("sddmm_dot_gedge_feat_s", lambda: oracle.sddmm_dot(sub, A, B, 4), sub.nnz * 256,
-                     f"{sub.n} rows, {sub.nnz} edges, 4 heads x 64"))
+                     f"{sub.n} nodes, {sub.nnz} edges, 4 heads x 64"))
         jobs.append(("edge_softmax_gedge_s", lambda: oracle.edge_softmax(sub, E), sub.nnz, f"{sub.nnz} edges, 4 heads"))
     if cfg["kind"] == "quant":
         H = inp["H"]
@@ -157,27 +344,6 @@ def cpu_oracle_kernels(k, og, inp, edges=1_000_000):
             rec[label] = round(work / dt / 1e9, 4) if "gedge" in name else round(work / dt, 1)
         out[name] = rec
     return out
-
-
-def cpu_baseline_gcn(min_seconds=10.0, max_passes=3):
-    """The oracle's 3-layer forward+backward on the full workload, repeated
-    until at least `min_seconds` of CPU work (at most `max_passes` passes);
-    also returns the oracle graph and inputs for the per-step timings."""
-    import oracle
-    og, inp = oracle_graph(2)
-    Ws = [inp["W0"], inp["W1"], inp["W2"]]
-    passes, dt = 0, 0.0
-    while passes < max_passes and (passes == 0 or dt < min_seconds):
-        t0 = time.perf_counter()
-        oracle.gcn_forward_backward(og, inp["X"], Ws, inp["labels"])
-        dt += time.perf_counter() - t0
-        passes += 1
-    # same aggregation count as the GPU step: 128 + 256 + 41 forward, 256 + 41 backward
-    work = passes * og.nnz * (128 + 256 + 41 + 256 + 41)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=work / dt / 1e9, unit="GEdge*feat/s", cores=threads, kind="oracle",
-                sample=f"{passes} full 3-layer forward+backward pass(es) of the same workload "
-                       f"(2^20 nodes, nnz {og.nnz}), {dt:.2f} s"), og, inp
 
 
 def main():
@@ -207,20 +373,29 @@ def main():
           file=sys.stderr, flush=True)
     T = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     extra = {}
+    ctx = {}
     with torch.cuda.stream(stream):
         if cfg["kind"] == "gcn":
             Ws = [T(inp[f"W{i}"]) for i in range(3)]
             runner = GcnStack(g, T(inp["X"]), Ws, T(inp["labels"]), dtype=cfg.get("dtype", "f32"))
-            work = runner.spmm_edge_feats()
-            metric_work = work
+            metric_work = runner.spmm_edge_feats()
+            sdt = "bf16" if cfg.get("dtype") == "bf16" else "f32"
+            dom_key = f"spmm_kernel d=256 h=1 {sdt}->{sdt} csr"
+            es = 2 if sdt == "bf16" else 4
+            dom_bytes = spmm_compulsory_bytes(g.n, g.nnz, 256, es, es)
         elif cfg["kind"] == "gat":
-            runner = GatLayer(g, T(inp["X"]), T(inp["W"]), T(inp["a_src"]), T(inp["a_dst"]), cfg["heads"],
-                              cfg["d_head"], cfg["slope"], T(inp["dY"]))
-            hd = cfg["heads"] * cfg["d_head"]
-            metric_work = g.nnz * hd * 3  # weighted SpMM, SDDMM dot, transposed SpMM
+            h, dh = cfg["heads"], cfg["d_head"]
+            runner = GatLayer(g, T(inp["X"]), T(inp["W"]), T(inp["a_src"]), T(inp["a_dst"]), h, dh, cfg["slope"],
+                              T(inp["dY"]))
+            metric_work = g.nnz * h * dh * 3  # weighted SpMM, SDDMM dot, transposed SpMM
+            dom_key = f"gat_bwd_csc_kernel h={h} dh={dh}"
+            dom_bytes = gat_bwd_csc_bytes(g.n, g.nnz, h, dh)
         else:
             runner = QuantExchange(g, T(inp["H"]), inp["rows"], inp["mixed_bits"], int(inp["philox_seed"]))
             metric_work = g.nnz * cfg["d"]
+            dom_key = "spmm_kernel d=256 h=1 f32->f32 csr"
+            dom_bytes = spmm_compulsory_bytes(g.n, g.nnz, 256)
+            ctx["quant_rows"] = {bb: int(r.numel()) for bb, r, _, _, _ in runner.groups}
     # a plain 1 GiB device copy: the reference that scales the HBM byte
     # counters (FETCH_SIZE / WRITE_SIZE) when this command runs under rocprofv3
     with torch.cuda.stream(stream):
@@ -233,6 +408,10 @@ def main():
         with torch.cuda.stream(stream):
             runner.step()
     torch.cuda.synchronize()
+
+    # ---- timed region: the steps, with the dominant kernel's launches
+    # bracketed by HIP events on the stream they run on -------------------
+    gnnmp.gnn_timer_start(dom_key, capacity=max(64, 8 * a.steps))
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
@@ -243,57 +422,56 @@ def main():
         end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    gnnmp.gnn_timer_stop()
     ms = start.elapsed_time(end) / a.steps
     print(f"# timed {a.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
     value = metric_work / (ms * 1e-3) / 1e9
+    launches, dom_total = gnnmp.gnn_timer_result(dom_key)
+    if launches == 0:
+        raise RuntimeError(f"the dominant kernel {dom_key!r} was not launched in the timed steps")
+    dom_ms = dom_total / launches
+    ach = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(cfg["name"], dom_key)
+    roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic)
+    extra["dominant_kernel"] = {"key": dom_key, "launches_timed": launches, "ms_per_launch": round(dom_ms, 4),
+                                "algorithmic_bytes_per_launch": dom_bytes,
+                                "edge_feat_per_s": None}
+    if traffic:
+        extra["dominant_kernel"]["counter_GBs"] = round(traffic / (dom_ms * 1e-3) / 1e9, 1)
+        extra["dominant_kernel"]["traffic_amplification"] = round(traffic / dom_bytes, 2)
+    hd = 256 if cfg["kind"] != "gat" else cfg["heads"] * cfg["d_head"]
+    extra["dominant_kernel"]["edge_feat_per_s"] = round(g.nnz * hd / (dom_ms * 1e-3) / 1e9, 2)
 
-    # --- dominant kernel: the aggregation (SpMM) ---------------------------
-    roofline = None
+    # ---- every instrumented kernel over a few more steps ---------------------
+    gnnmp.gnn_timer_start(None, capacity=4096)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            runner.step()
+    torch.cuda.synchronize()
+    gnnmp.gnn_timer_stop()
+    extra["kernels_measured"] = kernel_table(gnnmp, gnnmp.gnn_timer_keys(), g.n, g.nnz, ctx)
+    gnnmp.gnn_timer_release()
+
+    # ---- primitives of the path timed alone ----------------------------------
     if cfg["kind"] == "gcn":
         d = 256
         X = runner.H[1]                       # a 256-wide activation
         Y = torch.empty_like(X)
         ws = torch.empty(max(gnnmp.lib().gnn_spmm_workspace_size(g.h, 0, d), 1), dtype=torch.uint8, device=dev)
-        spmm_ms = event_time(lambda: gnnmp.gnn_spmm(g, X, Y, ws=ws), a.kernel_reps, stream)
+        extra["spmm_d256_alone_ms"] = round(event_time(lambda: gnnmp.gnn_spmm(g, X, Y, ws=ws), a.kernel_reps,
+                                                       stream), 4)
         es = X.element_size()
-        byts = spmm_compulsory_bytes(g.n, g.nnz, d, s_in=es, s_out=es)
-        ach = byts / (spmm_ms * 1e-3) / 1e9
-        traffic = measured_traffic() if a.config == 2 else None
-        roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic)
-        extra["spmm_d256_ms"] = round(spmm_ms, 4)
-        extra["spmm_d256_gedge_feat_s"] = round(g.nnz * d / (spmm_ms * 1e-3) / 1e9, 2)
-        extra["spmm_d256_compulsory_bytes"] = byts
-        extra["spmm_d256_compulsory_bytes_dinv"] = spmm_compulsory_bytes(g.n, g.nnz, d, s_in=es, s_out=es,
-                                                                         edge_weights=False)
         extra["spmm_d256_gather_model_bytes"] = 8 * (g.n + 1) + 8 * g.nnz + es * g.nnz * d + es * g.n * d
-        if traffic:
-            extra["spmm_d256_counter_GBs"] = round(traffic / (spmm_ms * 1e-3) / 1e9, 1)
-            extra["spmm_d256_traffic_amplification"] = round(traffic / byts, 2)
-        # the update GEMM of the 256 -> 256 layer on the matrix cores
         Wt = runner.Ws[1]
         Z = torch.empty_like(X)
-        gws = torch.empty(max(gnnmp.lib().gnn_gemm_workspace_size(0, 0, g.n, d, d), 1), dtype=torch.uint8, device=dev)
-        gemm_ms = event_time(lambda: gnnmp.gnn_gemm(X, Wt, Z, ws=gws), a.kernel_reps, stream)
-        tf = 2.0 * g.n * d * d / (gemm_ms * 1e-3) / 1e12
-        extra["gemm_256x256_ms"] = round(gemm_ms, 4)
-        extra["gemm_256x256_tflops"] = round(tf, 2)
-        extra["gemm_256x256_frac_fp32_mfma"] = round(tf / FP32_MFMA_PEAK_TFLOPS, 4)
-        # the weight-gradient GEMM (K = number of nodes, split over K)
-        dW = torch.empty((d, d), device=dev)
-        gws2 = torch.empty(max(gnnmp.lib().gnn_gemm_workspace_size(1, 0, d, d, g.n), 1), dtype=torch.uint8,
-                           device=dev)
-        dw_ms = event_time(lambda: gnnmp.gnn_gemm(X, Z, dW, transA=True, ws=gws2), a.kernel_reps, stream)
-        extra["gemm_dW_256x256_ms"] = round(dw_ms, 4)
-        # Tango's quantisation-aware variant of the same update (maxima,
-        # stochastic 8-bit quantisation of both operands, int8 matrix cores):
-        # f32 in and out, so only on the f32 workload
+        # Tango's quantisation-aware variant of the 256 x 256 update (maxima,
+        # stochastic 8-bit quantisation of both operands, int8 matrix cores)
         if X.dtype == torch.float32:
             qws = torch.empty(gnnmp.lib().gnn_gemm_q8_workspace_size(g.n, d, d), dtype=torch.uint8, device=dev)
             q8_ms = event_time(lambda: gnnmp.gnn_gemm_q8(X, Wt, Z, seed=5, ws=qws), a.kernel_reps, stream)
             extra["gemm_q8_256x256_ms"] = round(q8_ms, 4)
             extra["gemm_q8_256x256_tops_incl_quantise"] = round(2.0 * g.n * d * d / (q8_ms * 1e-3) / 1e12, 2)
-        extra["gemm_dW_256x256_tflops"] = round(2.0 * g.n * d * d / (dw_ms * 1e-3) / 1e12, 2)
         if a.config == 2:
             # GraphSAGE's mean aggregator on the same edges: the aggregation
             # alone and a 256 -> 256 layer forward + backward (the backward
@@ -312,18 +490,28 @@ def main():
                 lambda: gnnmp.gnn_sage_layer_bwd(gs, X, Wt, Ys, dYs, True, dWs, dX=dXs), a.kernel_reps, stream), 4)
             del Ys, dYs, dXs, gs
     if cfg["kind"] == "gat":
-        # the attention-gradient SDDMM dot as a primitive (f32), and Tango's
-        # variant on 8-bit codes (maxima + quantisation of both operands +
-        # the gather of 1-byte codes), on the layer's own H' and a dY
+        # the SDDMM dot (f32) as a primitive, Tango's variant on 8-bit codes
+        # (maxima + quantisation of both operands + the gather of 1-byte
+        # codes), and the SDDMM add + edge softmax primitives, on the layer's
+        # own H', S, D and dY
         h, dh = cfg["heads"], cfg["d_head"]
-        Hp = runner.saved[:g.n * h * dh * 4].view(torch.float32).view(g.n, h * dh)
+        Hp, S, D = gnnmp.gat_saved_views(g, runner.saved, h, dh)[:3]
         dYs = runner.dY
         dal = torch.empty((g.nnz, h), device=dev)
+        E = torch.empty((g.nnz, h), device=dev)
         extra["sddmm_dot_f32_ms"] = round(event_time(
             lambda: gnnmp.gnn_sddmm(g, "dot", Hp, dYs, h, dh, dal), a.kernel_reps, stream), 4)
+        extra["sddmm_dot_f32_GBs"] = round(kernel_model(f"sddmm_dot_kernel h={h} dh={dh} f32", g.n, g.nnz, ctx)[1]
+                                           / (extra["sddmm_dot_f32_ms"] * 1e-3) / 1e9, 1)
         sws = torch.empty(gnnmp.lib().gnn_sddmm_q8_workspace_size(g.h, h * dh), dtype=torch.uint8, device=dev)
         extra["sddmm_q8_ms"] = round(event_time(
             lambda: gnnmp.gnn_sddmm_q8(g, Hp, dYs, h, dh, dal, seed=5, ws=sws), a.kernel_reps, stream), 4)
+        extra["sddmm_add_lrelu_ms"] = round(event_time(
+            lambda: gnnmp.gnn_sddmm(g, "add", S, D, h, 1, E, slope=cfg["slope"]), a.kernel_reps, stream), 4)
+        extra["edge_softmax_ms"] = round(event_time(
+            lambda: gnnmp.gnn_edge_softmax(g, E, dal), a.kernel_reps, stream), 4)
+        sm_bytes = kernel_model(f"softmax_fwd_kernel h={h}", g.n, g.nnz, ctx)[1]
+        extra["edge_softmax_GBs"] = round(sm_bytes / (extra["edge_softmax_ms"] * 1e-3) / 1e9, 1)
     if cfg["kind"] == "quant":
         # the same exchange with the dequantisation inside the gather, and the
         # backward exchange of the embedding gradients (also fused)
@@ -361,10 +549,11 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         print("# timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        og, oinp = oracle_graph(a.config)
         if a.config == 2:
-            cpu, og, oinp = cpu_baseline_gcn()
+            cpu = cpu_baseline_gcn_full(og, oinp, metric_work)
         else:
-            og, oinp = oracle_graph(a.config)
+            cpu = cpu_baseline_sampled(a.config, og, oinp, metric_work, a.cpu_sample_edges)
         extra["cpu_oracle"] = cpu_oracle_kernels(a.config, og, oinp)
         print("# CPU oracle timed", file=sys.stderr, flush=True)
     out = {

@@ -422,6 +422,34 @@ gnn_status_t gnn_gat_layer_bwd(gnn_graph_t g, const float* X, int64_t d_in, cons
                                const float* dY, const void* saved, float* dX, float* dW, float* da_src,
                                float* da_dst, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Kernel timers (measurement of this library's own kernels; not an
+ * operation of the pages).  For callers that report the duration of one
+ * kernel inside a larger step, e.g. a roofline fraction: while timing is on,
+ * each instrumented launch whose key equals `key` (every instrumented launch
+ * when key is NULL or "") is bracketed by two HIP events recorded on the
+ * stream it is launched on.  Keys name the kernel and its shape, e.g.
+ * "spmm_kernel d=256 h=1 f32->f32 csr", "gat_bwd_csc_kernel h=4 dh=64",
+ * "attn_fwd_kernel h=4", "gemm M=... N=... K=... ta=0 tb=0 f32,f32->f32".
+ *   gnn_timer_start   creates a pool of 2*capacity events (host call; events
+ *                     are created here, never while launches are timed),
+ *                     clears earlier records and turns timing on.
+ *   gnn_timer_stop    turns timing off (records are kept).
+ *   gnn_timer_result  waits for the recorded events of `key` and returns the
+ *                     number of timed launches and their summed duration in
+ *                     ms; GNN_ERR_WORKSPACE when launches were dropped
+ *                     because the pool was full.
+ *   gnn_timer_keys    every key launched while timing was on, one per line
+ *                     (buf: host, len bytes incl. the terminating NUL).
+ *   gnn_timer_release destroys the pool.
+ * Timing is process-wide (one pool, guarded by a lock); the event records
+ * add a few microseconds per timed launch to the stream. */
+gnn_status_t gnn_timer_start(const char* key, int64_t capacity);
+gnn_status_t gnn_timer_stop(void);
+gnn_status_t gnn_timer_result(const char* key, int64_t* launches, double* total_ms);
+gnn_status_t gnn_timer_keys(char* buf, size_t len);
+gnn_status_t gnn_timer_release(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,8 +46,17 @@ def sources():
 PER_FILE = {"quant.hip": ["-ffp-contract=off"]}
 
 
-def _compile(src: str) -> str:
+def _headers_mtime() -> float:
+    hs = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    hs += [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    return max(os.path.getmtime(h) for h in hs)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj) and \
+            os.path.getmtime(obj) > max(os.path.getmtime(src), _headers_mtime(), os.path.getmtime(__file__)):
+        return obj
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [hipcc(), *COMMON, *PER_FILE.get(os.path.basename(src), []), *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,12 +70,14 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
+def build(jobs: int | None = None, verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every source (incremental: only those whose object is older
+    than the source, a header or this script) and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)), 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, incremental), srcs))
     tmp = LIB + f".tmp{os.getpid()}"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp, "-lpthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -81,4 +92,6 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
-    build(ap.parse_args().jobs)
+    ap.add_argument("--incremental", action="store_true")
+    a = ap.parse_args()
+    build(a.jobs, incremental=a.incremental)

@@ -768,6 +768,7 @@ gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, con
     Sched s = make_sched(v);
     const int64_t blocks = (sched_items(s) + (256 / G) - 1) / (256 / G);
     const int act = slope == slope;  // NaN: no activation
+    ScopedTimer t(st, "sddmm_add_kernel h=%d", heads);
     GNN_HEADS_SWITCH(heads, hipLaunchKernelGGL((sddmm_add_kernel<H>), dim3(blocks), dim3(256), 0, st, s, S, lds, D,
                                                ldd, act ? slope : 0.0f, act, out, out_pre));
     return launch_status("gnn_sddmm(add)");
@@ -840,6 +841,7 @@ gnn_status_t launch_sddmm_dot(const AggView& v, const void* src_feat, int64_t ld
     if (need != lanes) return fail(GNN_ERR_UNSUPPORTED, "gnn_sddmm(dot): heads*d_head must be 64, 128 or 256");
     Sched s = make_sched(v);
     const int64_t blocks = (sched_items(s) + (256 / lanes) - 1) / (256 / lanes);
+    ScopedTimer t(st, "sddmm_dot_kernel h=%d dh=%lld %s", heads, static_cast<long long>(d_head), dt_name(dt));
 #define GNN_DOT(L, HLv, T)                                                                                         \
     hipLaunchKernelGGL((sddmm_dot_kernel<L, HLv, T>), dim3(blocks), dim3(256), 0, st, s,                          \
                        static_cast<const T*>(src_feat), ld_src, static_cast<const T*>(dst_feat), ld_dst, heads, out)
@@ -872,6 +874,7 @@ gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha,
     Sched s = make_sched(v);
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
+    ScopedTimer t(st, "softmax_fwd_kernel h=%d", heads);
     GNN_HEADS_SWITCH(heads, {
         hipLaunchKernelGGL((softmax_fwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, E, alpha);
     });
@@ -886,6 +889,7 @@ gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float*
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
     const int act = slope == slope;  // NaN: no activation
+    ScopedTimer t(st, "attn_fwd_kernel h=%d", heads);
     GNN_HEADS_SWITCH(heads, {
         hipLaunchKernelGGL((attn_fwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, S, D,
                            act ? slope : 0.0f, act, alpha, alpha_head_stride, out_pre, row_max, row_rsum);
@@ -899,6 +903,7 @@ gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const
     Sched s = make_sched(v);
     const int64_t light = s.n - s.n_block;
     const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
+    ScopedTimer t(st, "softmax_bwd_kernel h=%d", heads);
     GNN_HEADS_SWITCH(heads, {
         hipLaunchKernelGGL((softmax_bwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, alpha, dalpha,
                            pre, slope, dE);

@@ -415,6 +415,8 @@ gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const 
     a.slab_blocks = (items + gpb - 1) / gpb;
 #define GNN_CSC(Lv) \
     hipLaunchKernelGGL((gat_bwd_csc_kernel<Lv>), dim3(a.slab_blocks * heads), dim3(256), 0, st, a)
+    {
+    ScopedTimer t(st, "gat_bwd_csc_kernel h=%d dh=%lld", heads, static_cast<long long>(d_head));
     switch (hl) {
         case 1: GNN_CSC(1); break;
         case 2: GNN_CSC(2); break;
@@ -423,6 +425,7 @@ gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const 
         case 16: GNN_CSC(16); break;
         case 32: GNN_CSC(32); break;
         default: GNN_CSC(64); break;
+    }
     }
 #undef GNN_CSC
     if (p.n_heavy > 0)
@@ -448,6 +451,7 @@ gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const 
     b.dHp = dHp;
     const int64_t light = n - b.n_block;
     const int64_t blocks = b.n_block + (light + (256 / kInLanes) - 1) / (256 / kInLanes);
+    ScopedTimer t(st, "gat_in_sum_kernel h=%d dh=%lld", heads, static_cast<long long>(d_head));
     switch (heads) {
         case 1: hipLaunchKernelGGL((gat_in_sum_kernel<1>), dim3(blocks), dim3(256), 0, st, b); break;
         case 2: hipLaunchKernelGGL((gat_in_sum_kernel<2>), dim3(blocks), dim3(256), 0, st, b); break;

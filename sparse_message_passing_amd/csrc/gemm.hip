@@ -659,6 +659,10 @@ gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K
     g.vec_ws = N % 4 == 0;
     const bool va = lda % 4 == 0 && reinterpret_cast<uintptr_t>(A) % (4 * as) == 0;
     const bool vb = ldb % 4 == 0 && reinterpret_cast<uintptr_t>(B) % (4 * bs) == 0;
+    // timed: the product and, when split over K, its fixed-order reduction
+    ScopedTimer t(st, "gemm M=%lld N=%lld K=%lld ta=%d tb=%d %s,%s->%s", static_cast<long long>(M),
+                  static_cast<long long>(N), static_cast<long long>(K), transA, transB, dt_name(a_dt), dt_name(b_dt),
+                  dt_name(c_dt));
     if (!transA && !transB) return launch_trans<false, false>(g, p, a_dt, b_dt, c_dt, va, vb, st);
     if (!transA && transB) return launch_trans<false, true>(g, p, a_dt, b_dt, c_dt, va, vb, st);
     if (transA && !transB) return launch_trans<true, false>(g, p, a_dt, b_dt, c_dt, va, vb, st);

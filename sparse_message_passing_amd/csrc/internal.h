@@ -3,7 +3,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdarg>
 #include <cstdint>
+#include <cstdio>
 #include <string>
 #include <vector>
 
@@ -200,6 +202,25 @@ gnn_status_t launch_quantize(const float* H, int64_t ldh, int64_t d, const int32
                              hipStream_t st);
 gnn_status_t launch_dequantize(const uint8_t* packed, const float* scale, const float* zero, int64_t n_rows,
                                int64_t d, int bits, const int32_t* rows, float* H, int64_t ldh, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// kernel timers (timer.cpp): a launch inside a ScopedTimer's scope is
+// bracketed by HIP events on its stream while timing is on and the timer's
+// key (printf-formatted) matches the key gnn_timer_start asked for
+// ---------------------------------------------------------------------------
+bool timer_on();
+class ScopedTimer {
+public:
+    ScopedTimer(hipStream_t st, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+    ~ScopedTimer();
+    ScopedTimer(const ScopedTimer&) = delete;
+    ScopedTimer& operator=(const ScopedTimer&) = delete;
+
+private:
+    hipStream_t st_;
+    int slot_ = -1;
+};
+inline const char* dt_name(gnn_dtype_t t) { return t == GNN_BF16 ? "bf16" : "f32"; }
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 inline size_t dt_size(gnn_dtype_t t) { return t == GNN_BF16 ? 2 : 4; }

@@ -327,6 +327,7 @@ gnn_status_t launch_quantize(const float* H, int64_t ldh, int64_t d, const int32
     if (n_rows == 0) return GNN_OK;
     if (d > 64 * 4 * kMaxQuads) return fail(GNN_ERR_UNSUPPORTED, "gnn_quantize: d must be at most 1024");
     const int64_t blocks = (n_rows + 3) / 4;
+    ScopedTimer t(st, "quantize_kernel b=%d d=%lld", bits, static_cast<long long>(d));
     hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(256), 0, st, H, ldh, d, rows, n_rows, bits,
                        static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), stream_id, packed, scale, zero);
     return launch_status("gnn_quantize");
@@ -336,6 +337,7 @@ gnn_status_t launch_dequantize(const uint8_t* packed, const float* scale, const 
                                int64_t d, int bits, const int32_t* rows, float* H, int64_t ldh, hipStream_t st) {
     if (n_rows == 0) return GNN_OK;
     const int64_t blocks = (n_rows + 3) / 4;
+    ScopedTimer t(st, "dequantize_kernel b=%d d=%lld", bits, static_cast<long long>(d));
     hipLaunchKernelGGL(dequantize_kernel, dim3(blocks), dim3(256), 0, st, packed, scale, zero, n_rows, d, bits, rows,
                        H, ldh);
     return launch_status("gnn_dequantize");

@@ -434,9 +434,13 @@ void launch_t(SpmmArgs a, hipStream_t st) {
     const int64_t width = LANES * VEC * NCH;  // features one pass covers
     const int64_t slabs = (a.d + width - 1) / width;
     a.slab_blocks = (groups + gpb - 1) / gpb;
-    if (a.slab_blocks > 0)
+    if (a.slab_blocks > 0) {
+        ScopedTimer t(st, "spmm_kernel d=%lld h=%d %s->%s %s%s", static_cast<long long>(a.d), a.heads,
+                      sizeof(TI) == 2 ? "bf16" : "f32", sizeof(TO) == 2 ? "bf16" : "f32", a.eid ? "csc" : "csr",
+                      QS ? " dequant" : "");
         hipLaunchKernelGGL((spmm_kernel<LANES, VEC, NCH, TI, TO, QS>), dim3(a.slab_blocks * slabs), dim3(256), 0, st,
                            a);
+    }
     if (a.n_heavy > 0) hipLaunchKernelGGL((spmm_fixup<TO>), dim3(a.n_heavy), dim3(256), 0, st, a);
 }
 

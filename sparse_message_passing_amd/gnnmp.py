@@ -65,6 +65,11 @@ _SIGS = {
     "gnn_gat_workspace_size": ("PIiI", "S"),
     "gnn_gat_layer_fwd": ("PPIPPPiIFPPPSP", "i"),
     "gnn_gat_layer_bwd": ("PPIPPPiIFPPPPPPPPSP", "i"),
+    "gnn_timer_start": ("PI", "i"),
+    "gnn_timer_stop": ("", "i"),
+    "gnn_timer_result": ("PPP", "i"),
+    "gnn_timer_keys": ("PS", "i"),
+    "gnn_timer_release": ("", "i"),
 }
 _CT = {"P": C.c_void_p, "I": C.c_int64, "i": C.c_int, "U": C.c_uint32, "Q": C.c_uint64, "F": C.c_float,
        "D": C.c_double, "S": C.c_size_t}
@@ -510,3 +515,33 @@ def gat_saved_views(g: Graph, saved, heads, d_head):
         off += al(count * 4)
     out[-1] = out[-1].t()  # alpha is stored one plane per head; the view is [nnz, heads]
     return tuple(out)
+
+
+# ---------------------------------------------------------------------------
+# kernel timers (measurement)
+# ---------------------------------------------------------------------------
+def gnn_timer_start(key=None, capacity=4096):
+    """Time the launches whose key equals `key` (all instrumented launches
+    when None) with HIP events on their streams, until gnn_timer_stop()."""
+    _check(lib().gnn_timer_start(None if key is None else key.encode(), int(capacity)))
+
+
+def gnn_timer_stop():
+    _check(lib().gnn_timer_stop())
+
+
+def gnn_timer_result(key):
+    """(launches, total_ms) of the timed launches of `key`."""
+    n, ms = C.c_int64(), C.c_double()
+    _check(lib().gnn_timer_result(key.encode(), C.byref(n), C.byref(ms)))
+    return n.value, ms.value
+
+
+def gnn_timer_keys():
+    buf = C.create_string_buffer(1 << 16)
+    _check(lib().gnn_timer_keys(buf, len(buf)))
+    return [k for k in buf.value.decode().split("\n") if k]
+
+
+def gnn_timer_release():
+    _check(lib().gnn_timer_release())
