@@ -67,7 +67,6 @@ def lib():
             "orc_set_threads": [I32],
             "orc_threads": [],
             "orc_spmm": [I64, P, P, P, I32, P, I64, I64, P],
-            "orc_spmm_t": [I64, P, P, P, I32, P, I64, I64, P],
             "orc_sddmm_dot": [I64, P, P, P, I64, P, I64, I32, I64, P],
             "orc_edge_softmax": [I64, P, P, I32, P],
             "orc_edge_softmax_bwd": [I64, P, P, P, I32, P],
@@ -136,6 +135,10 @@ def store(x, dt):
 # primitives (float64 results unless the step is fixed in binary32)
 # ---------------------------------------------------------------------------
 def spmm(g: OracleGraph, X, w=None, heads=1, transpose=False):
+    """Y[v] = sum over in-edges u -> v of w(e) X[u] (AdaQP Eqn. 3's weighted
+    sum; per head with heads > 1).  transpose: Y[u] = sum over out-edges
+    u -> v of w(e) X[v], computed as the same sum over the transposed graph
+    (its CSC view), with each edge keeping its weight."""
     X = _c(X, np.float64)
     n, d = g.n, X.shape[1]
     # the transposed product writes n rows from n input rows; the plain one
@@ -144,8 +147,12 @@ def spmm(g: OracleGraph, X, w=None, heads=1, transpose=False):
         raise ValueError("X has too few rows for this graph")
     wa = None if w is None else _c(w, np.float64)
     Y = np.empty((n, d), dtype=np.float64)
-    fn = lib().orc_spmm_t if transpose else lib().orc_spmm
-    fn(n, _p(g.row_ptr), _p(g.col), _p(wa), heads, _p(X), d, d, _p(Y))
+    if transpose:
+        colptr, row, eid = g.csc()
+        wt = None if wa is None else _c(wa.reshape(g.nnz, -1)[eid], np.float64)
+        lib().orc_spmm(n, _p(colptr), _p(_c(row, np.int32)), _p(wt), heads, _p(X), d, d, _p(Y))
+    else:
+        lib().orc_spmm(n, _p(g.row_ptr), _p(g.col), _p(wa), heads, _p(X), d, d, _p(Y))
     return Y
 
 

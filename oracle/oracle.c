@@ -63,28 +63,6 @@ void orc_spmm(int64_t n, const int64_t* row_ptr, const int32_t* col,
     }
 }
 
-/* Transposed aggregation: Y = (G . w)^T X, i.e. every edge u -> v sends
- * w[e] * X[v] back to its source u.  Tango, GAT running example, backward:
- * the gradient flows over the reversed graph.  Written as the plain scatter
- * over all edges (serial, so the order of the double sums is fixed). */
-void orc_spmm_t(int64_t n, const int64_t* row_ptr, const int32_t* col,
-                const double* w, int heads, const double* X, int64_t ldx,
-                int64_t d, double* Y)
-{
-    const int64_t dh = d / heads;
-    memset(Y, 0, sizeof(double) * (size_t)(n * d));
-    for (int64_t v = 0; v < n; ++v) {
-        const double* x = X + v * ldx;
-        for (int64_t e = row_ptr[v]; e < row_ptr[v + 1]; ++e) {
-            double* y = Y + (int64_t)col[e] * d;
-            for (int64_t f = 0; f < d; ++f) {
-                double we = w ? w[e * heads + f / dh] : 1.0;
-                y[f] += we * x[f];
-            }
-        }
-    }
-}
-
 /* SDDMM with the "dot" operator: out[e, k] = <A[v, head k], B[u, head k]>
  * for edge e = (u -> v).  Tango uses it for the attention gradient
  * d(alpha)[e] = dH(l)[dst] . H'[src] (quantised SDDMM paragraph, "dot"). */

@@ -112,3 +112,78 @@ def softmax_row_stats(og, E):
     with np.errstate(divide="ignore"):
         Z = 1.0 / s
     return M, Z
+
+
+
+def check_gcn_stack_step(og, st, Ws, labels, dt, rows=None, log=print):
+    """Element-by-element parity of one GcnStack step (forward, loss, backward)
+    the way the library chains it, layer by layer: each layer's outputs are
+    compared with the oracle's layer applied to the GPU's own inputs of that
+    layer (the activation, the saved aggregate, the upstream gradient), so
+    every ReLU decision is shared and every check covers one layer's
+    rounding.  The backward of layer i > 0 returns its input gradient times
+    [H_i > 0] (the previous layer's ReLU derivative, fused).  rows: check the
+    row-valued outputs on these rows only (None: every row), with the graph
+    symmetrised (A_hat^T restricted to rows is then A_hat's rows); the weight
+    gradients and the loss are always checked in full."""
+    rtol = RTOL16 if dt == "bf16" else RTOL32
+    bf = dt == "bf16"
+    L = len(Ws)
+    H = [from_dev(h) for h in st.H]
+    w = og.gcn_norm()[1]
+    wa = np.abs(w)
+    if rows is None:
+        sel = lambda a: a
+        loc, need, wl = og, np.arange(og.n), w          # the rows' in-edge graph and the sources it reads
+        aggT_mag = lambda M: oracle.spmm(og, M, wa, transpose=True)
+    else:
+        sg, eids = sub_rows(og, rows)
+        need = np.unique(sg.col).astype(np.int64)
+        loc = oracle.OracleGraph(sg.n, sg.row_ptr, np.searchsorted(need, sg.col).astype(np.int32), sg.dst)
+        wl = w[eids]
+        sel = lambda a: a[rows]
+        aggT_mag = lambda M: oracle.spmm(loc, M[need], np.abs(wl))
+    for i in range(L):
+        last = i == L - 1
+        out_dt = "f32" if last else dt
+        W = np.asarray(Ws[i], np.float64)
+        d_in, d_out = W.shape
+        Xn = H[i][need].astype(np.float64)
+        if d_out <= d_in:                            # Z = X W (stored), Y = sigma(A_hat Z)
+            A = oracle.spmm(loc, oracle.store(Xn @ W, dt), wl)
+        else:                                        # saved = A_hat X (stored), Y = sigma(saved W)
+            saved_ref = oracle.store(oracle.spmm(loc, Xn, wl), dt)
+            sv = sel(from_dev(st.saved[i]))
+            check_close(sv, saved_ref, oracle.spmm(loc, np.abs(Xn), np.abs(wl)), rtol=rtol, bf16_out=bf,
+                        what=f"step layer {i} saved A_hat X")
+            A = sv.astype(np.float64) @ W            # the GEMM reads the GPU's own saved aggregate
+        Y_ref = oracle.store(A if last else np.maximum(A, 0.0), out_dt)
+        check_close(sel(H[i + 1]), Y_ref, oracle.spmm(loc, np.abs(Xn) @ np.abs(W), np.abs(wl)), rtol=rtol,
+                    bf16_out=bf and not last, what=f"step layer {i} forward")
+        log(f"step layer {i} forward checked")
+    loss_ref, dz_ref = oracle.softmax_xent(H[L], labels)
+    n = og.n
+    assert abs(float(st.loss.item()) - loss_ref) <= RTOL32 * (abs(loss_ref) + np.abs(H[L]).max()), "step loss"
+    check_close(from_dev(st.dlogits), dz_ref, np.abs(dz_ref) + 2.0 / n, what="step loss gradient")
+    U = from_dev(st.dlogits)
+    for i in reversed(range(L)):
+        W = np.asarray(Ws[i], np.float64)
+        d_in, d_out = W.shape
+        saved = from_dev(st.saved[i]) if st.saved[i] is not None else None
+        dX_ref, dW_ref = oracle.gcn_layer_bwd(og, H[i], saved, H[i + 1], U, Ws[i], relu=False, need_dX=i > 0,
+                                              dt=dt)
+        Ga = np.abs(U).astype(np.float64)
+        if d_out <= d_in:                            # dZ = A_hat^T G, dW = X^T dZ, dX = dZ W^T
+            MdZ = oracle.spmm(og, Ga, wa, transpose=True)
+            m_dW = np.abs(H[i]).T.astype(np.float64) @ MdZ
+            m_dX = lambda: sel(MdZ) @ np.abs(W).T
+        else:                                        # dW = (A_hat X)^T G, dX = A_hat^T (G W^T)
+            m_dW = np.abs(saved).T.astype(np.float64) @ Ga
+            m_dX = lambda: aggT_mag(Ga @ np.abs(W).T)
+        check_close(from_dev(st.dW[i]), dW_ref, m_dW, rtol=rtol, what=f"step layer {i} dW")
+        if i > 0:
+            keep = sel(H[i] > 0)
+            check_close(sel(from_dev(st.dH[i])), np.where(keep, sel(dX_ref), 0.0), np.where(keep, m_dX(), 0.0),
+                        rtol=rtol, bf16_out=bf, what=f"step layer {i} dX (times the ReLU derivative)")
+            U = from_dev(st.dH[i])
+        log(f"step layer {i} backward checked")

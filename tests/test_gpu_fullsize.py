@@ -10,8 +10,10 @@ import torch
 
 import oracle
 from oracle.graph import build_graph
-from parity import RTOL16, RTOL32, bf16_values, check_close, from_dev, softmax_row_stats, sub_rows, to_dev
+from parity import (RTOL16, RTOL32, bf16_values, check_close, check_gcn_stack_step, from_dev, softmax_row_stats,
+                    sub_rows, to_dev)
 from sparse_message_passing_amd import gnnmp, synth
+from sparse_message_passing_amd.step import GatLayer, GcnStack
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +50,20 @@ def test_c2_graph_bit_exact(c2):
     assert np.array_equal(ex["w"].view(np.uint32), w.view(np.uint32))
     assert np.array_equal(ex["perm"], og.degree_perm())
     assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 256]))
+
+
+def test_c2_gcn_step_chain(c2):
+    # the 3-layer step the benchmark times (GcnStack) at 2^20 nodes, every
+    # element of every layer output, saved aggregate, loss gradient, input
+    # gradient and weight gradient, each layer against the oracle's layer on
+    # the GPU's own inputs of that layer (padded strides, the fused input
+    # ReLU masks and the reused buffers included)
+    g, og, inp = c2
+    Ws = [inp[f"W{i}"] for i in range(3)]
+    st = GcnStack(g, to_dev(inp["X"]), [to_dev(w) for w in Ws], to_dev(inp["labels"]), dtype="f32")
+    st.step()
+    torch.cuda.synchronize()
+    check_gcn_stack_step(og, st, Ws, inp["labels"], "f32", log=log)
 
 
 @pytest.mark.parametrize("d", [256, 128, 41])
@@ -272,15 +288,28 @@ def test_c3_graph_bit_exact(c3):
     assert np.array_equal(ex["bucket_off_t"], og.bucket_offsets([2048, 256], by_out=True))
 
 
-def test_c3_gat_forward_sampled(c3):
+@pytest.fixture(scope="module")
+def c3_step(c3):
+    """One GatLayer step (forward, then backward for the seeded upstream
+    gradient) on the 2^21-node workload: the object and the launch
+    configuration the benchmark times."""
+    g, og, inp = c3
+    cfg = synth.WORKLOADS[3]
+    L = GatLayer(g, to_dev(inp["X"]), to_dev(inp["W"]), to_dev(inp["a_src"]), to_dev(inp["a_dst"]), cfg["heads"],
+                 cfg["d_head"], cfg["slope"], to_dev(inp["dY"]))
+    L.step()
+    torch.cuda.synchronize()
+    log("C3 GatLayer step done")
+    return L
+
+
+def test_c3_gat_forward_sampled(c3, c3_step):
     g, og, inp = c3
     cfg = synth.WORKLOADS[3]
     h, dh, slope = cfg["heads"], cfg["d_head"], cfg["slope"]
     X, W, a_s, a_d = inp["X"], inp["W"], inp["a_src"], inp["a_dst"]
-    Y = torch.empty((og.n, h * dh), device="cuda")
-    saved = torch.empty(gnnmp.gnn_gat_saved_size(g, h, dh), dtype=torch.uint8, device="cuda")
-    gnnmp.gnn_gat_layer_fwd(g, to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d), h, dh, slope, Y, saved)
-    Hp_d, S_d, D_d, M_d, Z_d, al_d = gnnmp.gat_saved_views(g, saved, h, dh)
+    Y = c3_step.Y
+    Hp_d, S_d, D_d, M_d, Z_d, al_d = gnnmp.gat_saved_views(g, c3_step.saved, h, dh)
     rows = sample_rows(og, 1024, 3)
     sg, eids = sub_rows(og, rows)
     # every node the sampled rows touch, and the sub-graph in that local numbering
@@ -314,7 +343,7 @@ def test_c3_gat_forward_sampled(c3):
     check_close(from_dev(Y)[rows], ref, mY, what="C3 GAT output")
 
 
-def test_c3_gat_backward_sampled(c3):
+def test_c3_gat_backward_sampled(c3, c3_step):
     # the layer backward at 2^21 nodes in the launch configuration the bench
     # times, dX on sampled nodes u: every step between dY and dX (SDDMM dot,
     # softmax backward, LeakyReLU', in- and out-edge sums, the transposed
@@ -326,23 +355,13 @@ def test_c3_gat_backward_sampled(c3):
     h, dh, slope = cfg["heads"], cfg["d_head"], cfg["slope"]
     hd = h * dh
     X, W, a_s, a_d, dY = inp["X"], inp["W"], inp["a_src"], inp["a_dst"], inp["dY"]
-    Xd, Wd, asd, add = to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d)
-    Y = torch.empty((og.n, hd), device="cuda")
-    saved = torch.empty(gnnmp.gnn_gat_saved_size(g, h, dh), dtype=torch.uint8, device="cuda")
-    gnnmp.gnn_gat_layer_fwd(g, Xd, Wd, asd, add, h, dh, slope, Y, saved)
-    dX = torch.empty((og.n, X.shape[1]), device="cuda")
-    dW = torch.empty((X.shape[1], hd), device="cuda")
-    das = torch.empty((h, dh), device="cuda")
-    dad = torch.empty((h, dh), device="cuda")
-    gnnmp.gnn_gat_layer_bwd(g, Xd, Wd, asd, add, h, dh, slope, Y, to_dev(dY), saved, dW, das, dad, dX=dX)
+    dX = c3_step.dX
     colptr, crow, _ = og.csc()
     outdeg = np.diff(colptr)
     r = np.random.default_rng(7)
     U = np.unique(np.concatenate([np.argsort(-outdeg, kind="stable")[:2],
                                   r.choice(og.n, 126, replace=False)])).astype(np.int64)
     dX_gpu = from_dev(dX[torch.from_numpy(U).cuda()])
-    del dX, dW, Y, saved
-    log("C3 backward on the GPU done")
     V = np.unique(np.concatenate([U] + [crow[colptr[u]:colptr[u + 1]].astype(np.int64) for u in U]))
     sg, _ = sub_rows(og, V)
     need = np.unique(np.concatenate([sg.col.astype(np.int64), V]))
@@ -387,6 +406,53 @@ def test_c3_gat_backward_sampled(c3):
     np.add.at(m_agg, pos, m_c.reshape(-1, hd))
     m_dHp = m_agg + (m_dS[:, :, None] * np.abs(a_s)[None] + m_dD[:, :, None] * np.abs(a_d)[None]).reshape(-1, hd)
     check_close(dX_gpu, ref, m_dHp @ np.abs(W).T, what="C3 GAT dX")
+
+
+def test_c3_gat_step_attention_and_weight_gradients(c3, c3_step):
+    # the step's da_src, da_dst (every entry) and dW (every row of 8 sampled
+    # columns, one or more per head) at 2^21 nodes: the oracle runs the whole
+    # forward and the backward's edge steps (SDDMM dot, softmax backward,
+    # LeakyReLU', in- and out-edge sums) over all 42M edges, and the
+    # transposed aggregation for the sampled columns only
+    g, og, inp = c3
+    cfg = synth.WORKLOADS[3]
+    h, dh, slope = cfg["heads"], cfg["d_head"], cfg["slope"]
+    hd = h * dh
+    X, W, a_s, a_d, dY = inp["X"], inp["W"], inp["a_src"], inp["a_dst"], inp["dY"]
+    fw = oracle.gat_layer_fwd(og, X, W, a_s, a_d, h, slope)
+    log("C3 oracle forward done")
+    Hp, alpha = fw["Hp"], fw["alpha"]
+    fac = np.where(fw["E_pre"] > 0, 1.0, float(np.float32(slope)))
+    dal = oracle.to_f32(oracle.sddmm_dot(og, dY, Hp, h))
+    dEp = oracle.to_f32(oracle.to_f32(oracle.edge_softmax_bwd(og, alpha, dal)) * fac)
+    dD = oracle.to_f32(oracle.edge_reduce(og, dEp))
+    dS = oracle.to_f32(oracle.edge_reduce(og, dEp, by_src=True))
+    log("C3 oracle edge backward done")
+    # magnitudes carried through the same steps
+    A = np.abs(alpha).astype(np.float64)
+    row_e = og.dst
+    m_Hp = np.abs(X).astype(np.float64) @ np.abs(W)
+    m_dal = oracle.sddmm_dot(og, np.abs(dY), np.abs(Hp), h)
+    m_dEp = A * (m_dal + oracle.edge_reduce(og, A * m_dal)[row_e]) * fac
+    m_dD = oracle.edge_reduce(og, m_dEp)
+    m_dS = oracle.edge_reduce(og, m_dEp, by_src=True)
+    H3, mH3 = Hp.astype(np.float64).reshape(-1, h, dh), m_Hp.reshape(-1, h, dh)
+    for name, coef, mcoef, got in (("da_src", dS, m_dS, c3_step.da_src), ("da_dst", dD, m_dD, c3_step.da_dst)):
+        ref = np.einsum("nk,nkj->kj", coef.astype(np.float64), H3)
+        mag = np.einsum("nk,nkj->kj", mcoef, np.abs(H3)) + np.einsum("nk,nkj->kj", np.abs(coef), mH3)
+        check_close(from_dev(got), ref, mag, what=f"C3 step {name}")
+    r = np.random.default_rng(17)
+    cols = np.unique(np.concatenate([np.arange(h) * dh, r.choice(hd, 8 - h, replace=False)]))
+    dW_gpu = from_dev(c3_step.dW)[:, cols]
+    for ci, c in enumerate(cols):
+        k, j = divmod(int(c), dh)
+        agg = oracle.spmm(og, dY[:, c:c + 1], alpha[:, k], transpose=True)[:, 0]
+        m_agg = oracle.spmm(og, np.abs(dY[:, c:c + 1]), A[:, k], transpose=True)[:, 0]
+        dHp_c = oracle.to_f32(agg + dS[:, k].astype(np.float64) * a_s[k, j] + dD[:, k].astype(np.float64) * a_d[k, j])
+        m_dHp_c = m_agg + m_dS[:, k] * abs(a_s[k, j]) + m_dD[:, k] * abs(a_d[k, j])
+        ref = X.T.astype(np.float64) @ dHp_c.astype(np.float64)
+        mag = np.abs(X).T.astype(np.float64) @ m_dHp_c
+        check_close(dW_gpu[:, ci], ref, mag, what=f"C3 step dW column {c}")
 
 
 def test_c3_sddmm_add_full_bit_exact(c3):
@@ -535,6 +601,19 @@ def c4():
     og = build_graph(inp["src"], inp["dst"], n, True)
     log(f"C4 graph n={n} nnz={og.nnz} max degree {og.deg.max()} ({time.time() - t:.1f} s)")
     return g, og, inp
+
+
+def test_c4_gcn_step_chain(c4):
+    # the bf16 3-layer step the benchmark times (GcnStack) at 2.45M nodes:
+    # every layer output, saved aggregate and input gradient on sampled rows,
+    # the loss, its gradient and every weight gradient in full, each layer
+    # against the oracle's layer on the GPU's own inputs of that layer
+    g, og, inp = c4
+    Ws = [inp[f"W{i}"] for i in range(3)]
+    st = GcnStack(g, to_dev(inp["X"]), [to_dev(w) for w in Ws], to_dev(inp["labels"]), dtype="bf16")
+    st.step()
+    torch.cuda.synchronize()
+    check_gcn_stack_step(og, st, Ws, inp["labels"], "bf16", rows=sample_rows(og, 4096, 9), log=log)
 
 
 def test_c4_graph_bit_exact(c4):

@@ -1,16 +1,16 @@
 """GPU parity of the layer entry points (GCN and GAT, forward and backward)
 against the oracle's compositions.  Backward tests feed both sides the
 oracle's forward tensors, so ReLU / LeakyReLU decisions are identical and
-every output is checked element by element; the whole multi-layer step is
-checked end to end in norm (there a decision near zero may legitimately
-flip between two correct roundings)."""
+every output is checked element by element; the multi-layer step is checked
+layer by layer, element by element, each layer against the oracle applied to
+the GPU's own inputs of that layer."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from parity import (RTOL16, RTOL32, check_close, from_dev, graph_pair, hub_edges, rmat_graph, softmax_row_stats,
-                    to_dev)
+from parity import (RTOL16, RTOL32, check_close, check_gcn_stack_step, from_dev, graph_pair, hub_edges, rmat_graph,
+                    softmax_row_stats, to_dev)
 from sparse_message_passing_amd import gnnmp, synth
 from sparse_message_passing_amd.step import GcnStack
 
@@ -23,6 +23,18 @@ def gcn_mag(og, X, W):
     """Magnitude |A_hat| |X| |W| of a GCN layer output (either operand order)."""
     w = og.gcn_norm()[1]
     return oracle.spmm(og, np.abs(X) @ np.abs(W), np.abs(w))
+
+
+def gcn_bwd_mags(og, X, W, G):
+    """Magnitudes of the GCN layer's dW and dX for the (masked) upstream
+    gradient G, in the operand order the layer takes."""
+    w = np.abs(og.gcn_norm()[1])
+    G = np.abs(np.asarray(G, np.float64))
+    d_in, d_out = W.shape
+    if d_out <= d_in:
+        MdZ = oracle.spmm(og, G, w, transpose=True)
+        return np.abs(X).T.astype(np.float64) @ MdZ, MdZ @ np.abs(W).T
+    return oracle.spmm(og, np.abs(X), w).T @ G, oracle.spmm(og, G @ np.abs(W).T, w, transpose=True)
 
 
 @pytest.fixture(scope="module")
@@ -89,15 +101,7 @@ def test_gcn_layer_fwd_bwd(request, which, case):
     # backward from the oracle's forward tensors
     dY = oracle.store(r.standard_normal((og.n, d_out)), out_dt)
     dX_ref, dW_ref = oracle.gcn_layer_bwd(og, X, saved_ref, Y_ref, dY, W, relu, need_dX=True, dt=dt)
-    w = og.gcn_norm()[1]
-    G = np.abs(np.where(Y_ref > 0, dY, 0.0)) if relu else np.abs(dY)
-    if d_out <= d_in:
-        MdZ = oracle.spmm(og, G, np.abs(w), transpose=True)
-        mag_dW = np.abs(X).T.astype(np.float64) @ MdZ
-        mag_dX = MdZ @ np.abs(W).T
-    else:
-        mag_dW = oracle.spmm(og, np.abs(X), np.abs(w)).T @ G
-        mag_dX = oracle.spmm(og, G @ np.abs(W).T, np.abs(w), transpose=True)
+    mag_dW, mag_dX = gcn_bwd_mags(og, X, W, np.where(Y_ref > 0, dY, 0.0) if relu else dY)
     dYd = to_dev(dY, TDT[out_dt])
     Yd = to_dev(Y_ref, TDT[out_dt])
     sv = to_dev(saved_ref, TDT[dt]) if saved_ref is not None else None
@@ -231,13 +235,18 @@ def test_gcn_layer_row_strided(hubsym):
         dX = pad(d_in)
         dW = torch.empty((d_in, d_out), device="cuda")
         gnnmp.gnn_gcn_layer_bwd(g, Xd, to_dev(W), Yd, dYd, True, dW, dX=dX, saved=sv)
-        rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
-        assert rel(from_dev(dW), dW_ref) < 1e-5 and rel(from_dev(dX), dX_ref) < 1e-5
+        m_dW, m_dX = gcn_bwd_mags(og, X, W, np.where(Y_ref > 0, dY, 0.0))
+        check_close(from_dev(dW), dW_ref, m_dW, what=f"strided dW {d_in}->{d_out}")
+        check_close(from_dev(dX), dX_ref, m_dX, what=f"strided dX {d_in}->{d_out}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_gcn_three_layer_step(dt):
-    # the multi-layer forward + backward + loss of the 3-layer workloads, scaled down
+    # the multi-layer forward + backward + loss of the 3-layer workloads,
+    # scaled down, through the same GcnStack the benchmark times: every layer
+    # output, saved aggregate, loss gradient, input gradient and weight
+    # gradient element by element against the oracle's layer on the GPU's own
+    # inputs of that layer
     s, t, n = rmat_graph(13, 16, True, 2001)
     g, og = graph_pair(s, t, n, True, csc=False)
     r = np.random.default_rng(1)
@@ -245,16 +254,15 @@ def test_gcn_three_layer_step(dt):
     X = oracle.store(r.standard_normal((n, widths[0])), dt)
     Ws = [synth.glorot(widths[i], widths[i + 1], 10 + i) for i in range(3)]
     lab = r.integers(0, widths[-1], n).astype(np.int32)
-    ref = oracle.gcn_forward_backward(og, X, Ws, lab, dt=dt)
     st = GcnStack(g, to_dev(X, TDT[dt]), [to_dev(w) for w in Ws], to_dev(lab), dtype=dt)
     st.step()
     torch.cuda.synchronize()
+    check_gcn_stack_step(og, st, Ws, lab, dt, log=lambda m: None)
+    # and the whole step against the oracle's own composition (in norm: a
+    # ReLU decision within rounding of zero may differ between the two)
+    ref = oracle.gcn_forward_backward(og, X, Ws, lab, dt=dt)
     tol = 1e-4 if dt == "f32" else 2e-2
     assert abs(st.loss.item() - ref["loss"]) <= tol * abs(ref["loss"])
-    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
-    assert rel(from_dev(st.H[-1]), ref["logits"]) <= tol
-    for i in range(3):
-        assert rel(from_dev(st.dW[i]), ref["dW"][i]) <= tol * (3 if dt == "f32" else 1), i
     # deterministic: a second step gives the same bits
     dW0 = [w.clone() for w in st.dW]
     st.step()
