@@ -90,7 +90,74 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--cpu-sample-edges", type=int, default=2_000_000)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run only the reference kernels of known traffic and flops and print their rates")
     return ap.parse_args()
+
+
+def calibrate(reps=5):
+    """Achievable peaks of this GPU from reference kernels of known bytes and
+    flops (sparse_message_passing_amd/calib/calib.hip): a streaming read and
+    a copy of 1 GiB, random row gathers from tables that fit the L2 of one
+    XCD (2 MiB), the memory-side cache (32-128 MiB) or neither (1-2 GiB), and
+    matrix-core loops in f32, bf16 and i8.  Under rocprofv3 --pmc the same
+    launches give the counter reading per byte moved."""
+    import ctypes as C
+    import torch
+    from sparse_message_passing_amd import build as hb
+    L = C.CDLL(hb.CALIB_LIB)
+    P, I64 = C.c_void_p, C.c_int64
+    L.gnn_calib_read.argtypes = [P, I64, P, I64, P]
+    L.gnn_calib_copy.argtypes = [P, P, I64, P]
+    L.gnn_calib_gather.argtypes = [P, I64, P, I64, P, I64, P]
+    L.gnn_calib_mfma.argtypes = [C.c_int, I64, C.c_int, P, P, P]
+    for f in (L.gnn_calib_read, L.gnn_calib_copy, L.gnn_calib_gather, L.gnn_calib_mfma):
+        f.restype = C.c_int
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    sp = stream.cuda_stream
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"calibration launch failed ({rc})")
+
+    out = {}
+    GiB = 1 << 30
+    with torch.cuda.stream(stream):
+        src = torch.ones(GiB // 4, device=dev)
+        dst = torch.empty_like(src)
+        red = torch.empty(4096, device=dev)
+        t = event_time(lambda: ok(L.gnn_calib_read(src.data_ptr(), GiB, red.data_ptr(), 4096, sp)), reps, stream)
+        out["read_1GiB"] = {"ms": round(t, 4), "GBs": round(GiB / (t * 1e-3) / 1e9, 1), "bytes_read": GiB}
+        t = event_time(lambda: ok(L.gnn_calib_copy(src.data_ptr(), dst.data_ptr(), GiB, sp)), reps, stream)
+        out["copy_1GiB"] = {"ms": round(t, 4), "GBs": round(2 * GiB / (t * 1e-3) / 1e9, 1), "bytes_read": GiB,
+                            "bytes_written": GiB}
+        del dst
+        blocks = 256 * 16
+        gout = torch.empty(blocks * 256, device=dev)
+        n_idx = 1 << 23
+        r = np.random.default_rng(12345)
+        gath = {}
+        for tab in (2 << 20, 32 << 20, 128 << 20, GiB, 2 * GiB):
+            table = src if tab <= GiB else torch.ones(tab // 4, device=dev)
+            for rb in (128, 256, 1024):
+                rows = tab // rb
+                idx = torch.from_numpy(r.integers(0, rows, n_idx, dtype=np.int32)).to(dev)
+                t = event_time(lambda: ok(L.gnn_calib_gather(table.data_ptr(), rb, idx.data_ptr(), n_idx,
+                                                             gout.data_ptr(), blocks, sp)), reps, stream)
+                gath[f"table{tab >> 20}MiB_row{rb}B"] = {"ms": round(t, 4),
+                                                          "gathered_GBs": round(n_idx * rb / (t * 1e-3) / 1e9, 1)}
+            del table
+        out["gather_uniform_8M_rows"] = gath
+        mf = torch.empty(256 * 8 * 256, device=dev)
+        work = C.c_double()
+        for kind, name, iters in ((0, "mfma_f32_16x16x4", 4000), (1, "mfma_bf16_16x16x32", 2000),
+                                  (2, "mfma_i8_16x16x64", 2000)):
+            t = event_time(lambda: ok(L.gnn_calib_mfma(kind, 256 * 8, iters, mf.data_ptr(), C.byref(work), sp)),
+                           reps, stream)
+            out[name] = {"ms": round(t, 4), "TFLOPs": round(work.value / (t * 1e-3) / 1e12, 1)}
+    torch.cuda.synchronize()
+    return out
 
 
 def event_time(fn, reps, stream):
@@ -355,6 +422,10 @@ def main():
     import torch
     from sparse_message_passing_amd import gnnmp, synth
     from sparse_message_passing_amd.step import GatLayer, GcnStack, OverlapExchange, QuantExchange
+
+    if a.calibrate:
+        print(json.dumps({"calibration": calibrate()}), flush=True)
+        return
 
     if not os.path.exists(gnnmp.LIB_PATH):
         from sparse_message_passing_amd import build as hb

@@ -19,6 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgnnmp.so")
+CALIB_LIB = os.path.join(HERE, "libgnnmp_calib.so")
 ARCH = os.environ.get("GNNMP_ARCH", "gfx950")
 
 COMMON = [
@@ -84,9 +85,23 @@ def build(jobs: int | None = None, verbose: bool = True, incremental: bool = Fal
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_calib()
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
+
+
+def build_calib() -> str:
+    """The reference kernels of known traffic and flops (calib/calib.hip) the
+    bench's --calibrate mode runs; a library of their own."""
+    src = os.path.join(HERE, "calib", "calib.hip")
+    tmp = CALIB_LIB + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *COMMON, "-x", "hip", "-shared", src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
 
 
 if __name__ == "__main__":
