@@ -162,6 +162,24 @@ gnn_status_t gnn_spmm(gnn_graph_t g, int transpose, gnn_weights_t wmode, const f
                       const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                       int64_t d, int relu, void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free variant of gnn_spmm, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments,
+ * results (bitwise: the same kernels) and checks as gnn_spmm without the
+ * workspace: the hub-row partial sums go to a fixed device scratch of
+ * gnn_spmm_noalloc_max_scratch() bytes (64 MiB) that the library holds on
+ * each GPU it runs on until the process ends, found on the first call on a
+ * device (with the graph's device current).  Calls whose partials need more
+ * than that (gnn_spmm_workspace_size(g, transpose, d) bytes) fail with
+ * GNN_ERR_UNSUPPORTED before any launch.  Nothing in the scratch needs to
+ * start at zero.  Every call on one GPU shares the scratch: calls that
+ * overlap on one GPU (on different streams without ordering, or from
+ * different host threads) race and must be serialised by the caller. */
+size_t gnn_spmm_noalloc_max_scratch(void);
+gnn_status_t gnn_spmm_noalloc(gnn_graph_t g, int transpose, gnn_weights_t wmode, const float* edge_w, int heads,
+                              const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                              int64_t d, int relu, void* stream);
+
 /* Edge -> node sums (Tango: dD = (G . dE) 1 over in-edges, dS = (G^T . dE) 1
  * over out-edges; the incidence-matrix SpMM).  by_src = 0 sums the in-edges
  * of every node, by_src = 1 its out-edges (needs CSC).  vals [nnz, heads]

@@ -355,6 +355,27 @@ gnn_status_t gnn_spmm(gnn_graph_t h, int transpose, gnn_weights_t wmode, const f
                        ldy, d, relu, Rank1Epilogue{}, static_cast<float*>(ws), static_cast<hipStream_t>(stream));
 }
 
+size_t gnn_spmm_noalloc_max_scratch(void) { return kSpmmScratchBytes; }
+
+gnn_status_t gnn_spmm_noalloc(gnn_graph_t h, int transpose, gnn_weights_t wmode, const float* edge_w, int heads,
+                              const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
+                              int64_t d, int relu, void* stream) {
+    GNN_TRY(check_graph(h, "gnn_spmm_noalloc"));
+    const Graph& g = h->g;
+    if (transpose && !g.has_csc) return fail(GNN_ERR_GRAPH, "gnn_spmm_noalloc: transpose needs the CSC view");
+    GNN_REQUIRE(d >= 1, "gnn_spmm_noalloc: d must be >= 1");
+    const size_t need = spmm_partial_bytes(g.plan[transpose ? 1 : 0], d);
+    if (need > kSpmmScratchBytes)
+        return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm_noalloc: the hub-row partials need " + std::to_string(need) +
+                                             " bytes, more than its " + std::to_string(kSpmmScratchBytes) +
+                                             "-byte device scratch; use gnn_spmm with a workspace");
+    void* ws = nullptr;
+    GNN_TRY(spmm_noalloc_scratch(&ws));
+    // the same checks and kernels as gnn_spmm, with the scratch as its workspace
+    return gnn_spmm(h, transpose, wmode, edge_w, heads, X, x_dt, ldx, Y, y_dt, ldy, d, relu, ws, kSpmmScratchBytes,
+                    stream);
+}
+
 gnn_status_t gnn_edge_reduce(gnn_graph_t h, int by_src, const float* vals, int heads, float* out, void* stream) {
     GNN_TRY(check_graph(h, "gnn_edge_reduce"));
     const Graph& g = h->g;

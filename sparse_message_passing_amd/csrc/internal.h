@@ -153,6 +153,10 @@ gnn_status_t launch_quant_stats(const AggView& v, const float* w, const float* H
 gnn_status_t launch_quant_slots(int64_t n, int n_groups, const int32_t* const* rows, const int64_t* counts,
                                 int32_t* qslot, hipStream_t st);
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d);
+// the allocation-free aggregation's device scratch: its size and its address
+// on the current device (spmm.hip)
+constexpr size_t kSpmmScratchBytes = size_t(64) << 20;
+gnn_status_t spmm_noalloc_scratch(void** out);
 // whether gathers from a rows x row_bytes matrix are worth cutting into column slabs
 
 gnn_status_t launch_sddmm_add(const AggView& v, const float* S, int64_t lds, const float* D, int64_t ldd,

@@ -27,9 +27,17 @@
 //    reproducible.
 
 #include <algorithm>
+#include <mutex>
 
 #include "device.h"
 #include "internal.h"
+
+// Scratch of the allocation-free aggregation (gnn_spmm_noalloc): the hub-row
+// partial sums live here instead of in a caller workspace.  Each GPU the
+// library runs on holds one copy until the process ends; host code reaches
+// it only through the device address hipGetSymbolAddress returns (see
+// spmm_noalloc_scratch), never through this name.
+static __device__ __align__(256) unsigned char scratch[gnnmp::kSpmmScratchBytes];
 
 namespace gnnmp {
 
@@ -481,6 +489,30 @@ gnn_status_t dispatch(const SpmmArgs& a, int vec, int lanes, int nch, hipStream_
 }
 
 }  // namespace
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; HIP errors are reported.
+gnn_status_t spmm_noalloc_scratch(void** out) {
+    static std::mutex mu;
+    static std::vector<void*> ptrs;
+    int dev = 0;
+    GNN_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs.empty()) {
+        int count = 0;
+        GNN_HIP(hipGetDeviceCount(&count));
+        ptrs.assign(static_cast<size_t>(count), nullptr);
+    }
+    if (dev < 0 || static_cast<size_t>(dev) >= ptrs.size())
+        return fail(GNN_ERR_HIP, "gnn_spmm_noalloc: current device out of range");
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        GNN_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return GNN_OK;
+}
 
 size_t spmm_partial_bytes(const RowPlan& p, int64_t d) {
     const int64_t pd = (d + 7) / 8 * 8;

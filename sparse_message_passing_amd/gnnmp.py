@@ -36,6 +36,8 @@ _SIGS = {
     "gnn_graph_export": ("PPPPPPPPPPPP", "i"),
     "gnn_spmm_workspace_size": ("PiI", "S"),
     "gnn_spmm": ("PiiPiPiIPiIIiPSP", "i"),
+    "gnn_spmm_noalloc_max_scratch": ("", "S"),
+    "gnn_spmm_noalloc": ("PiiPiPiIPiIIiP", "i"),
     "gnn_edge_reduce": ("PiPiPP", "i"),
     "gnn_sddmm": ("PiPIPIiiIFPPP", "i"),
     "gnn_edge_softmax": ("PPPiP", "i"),
@@ -248,6 +250,20 @@ def gnn_spmm(g: Graph, X, Y, weights="gcn", heads=1, transpose=False, relu=False
         ws = _ws(need, X.device)
     _check(lib().gnn_spmm(g.h, int(transpose), wmode, _p(ew), heads, _p(X), _dt(X), _ld(X), _p(Y), _dt(Y), _ld(Y), d,
                           int(relu), _p(ws), ws.numel(), _stream()))
+    return Y
+
+
+def gnn_spmm_noalloc(g: Graph, X, Y, weights="gcn", heads=1, transpose=False, relu=False, d=None):
+    """gnn_spmm with the hub-row partials in the library's fixed device scratch
+    (no workspace): for callers that cannot allocate."""
+    d = X.shape[1] if d is None else d
+    if isinstance(weights, str):
+        wmode, ew = {"gcn": GNN_W_GCN, "ones": GNN_W_ONES, "mean": GNN_W_MEAN}[weights], None
+    else:
+        wmode, ew = GNN_W_EDGE, weights
+        _f32(ew)
+    _check(lib().gnn_spmm_noalloc(g.h, int(transpose), wmode, _p(ew), heads, _p(X), _dt(X), _ld(X), _p(Y), _dt(Y),
+                                  _ld(Y), d, int(relu), _stream()))
     return Y
 
 
