@@ -194,6 +194,12 @@ def gat_bwd_csc_bytes(n, nnz, h, dh):
     return h * (8 * (n + 1) + 8 * nnz + 12 * n * dh + 28 * n)
 
 
+def gat_fwd_bytes(n, nnz, h, dh):
+    """Per head slab: row_ptr, source ids, the order, the H' slice read once,
+    D, the Y slice written once, the softmax maximum and 1/sum written."""
+    return h * (8 * (n + 1) + 4 * nnz + 8 * n * dh + 20 * n)
+
+
 def kernel_model(key, n, nnz, ctx):
     """(kind, amount) for an instrumented key: ("bytes", B) or ("flops", F, bytes);
     None when the key has no model here."""
@@ -204,9 +210,8 @@ def kernel_model(key, n, nnz, ctx):
         m = re.search(r"(\w+)->(\w+)", key)
         d, h = int(kv["d"]), int(kv["h"])
         return ("bytes", spmm_compulsory_bytes(n, nnz, d, size(m.group(1)), size(m.group(2)), heads=h))
-    if name == "attn_fwd_kernel":
-        h = int(kv["h"])
-        return ("bytes", 8 * (n + 1) + 4 * nnz + 8 * n * h + 4 * nnz * h + 8 * n * h + 4 * n)
+    if name == "gat_fwd_kernel":
+        return ("bytes", gat_fwd_bytes(n, nnz, int(kv["h"]), int(kv["dh"])))
     if name == "gat_bwd_csc_kernel":
         return ("bytes", gat_bwd_csc_bytes(n, nnz, int(kv["h"]), int(kv["dh"])))
     if name == "gat_in_sum_kernel":

@@ -409,13 +409,18 @@ gnn_status_t gnn_sage_layer_bwd(gnn_graph_t g, const void* X, gnn_dtype_t x_dt, 
  * Y[v, head k] = sum_in alpha[e,k] H'[u, head k] (heads concatenated, no bias,
  * no output activation).  X [n, d_in] f32, W [d_in, heads*d_head] f32,
  * a_src, a_dst [heads, d_head] f32, Y [n, heads*d_head] f32.
+ * The edge part runs as one pass over each destination's in-edges: S[src] is
+ * formed from the gathered row H'[src] (the same binary32 operations as the
+ * stored S, so the same E), and the softmax is folded into the weighted sum
+ * with a running maximum (the same quotient); alpha itself is not stored.
  * saved: gnn_gat_saved_size() bytes holding H' [n, heads*d_head], S, D,
- * each destination's softmax maximum M and 1 / sum of exponentials Z per head
- * ([n, heads] each), and alpha as one plane of nnz values per head (CSR
- * order), in that order, each slice starting on a 256-byte boundary.  Needs
- * the CSC view only for the backward.  Shapes: 1, 2, 4 or 8 heads, d_head a
- * power of two from 4 to 256 and heads * d_head <= 1024 (GNN_ERR_UNSUPPORTED
- * otherwise, before anything is launched). */
+ * each destination's softmax maximum M and Z = 1 / sum_in exp(E - M) per head
+ * ([n, heads] each), in that order, each slice starting on a 256-byte
+ * boundary; the attention weights are alpha[e,k] = exp(E[e,k] - M[dst,k]) *
+ * Z[dst,k].  Needs the CSC view only for the backward.  Shapes: 1, 2, 4 or 8
+ * heads, d_head a power of two from 4 to 256 and heads * d_head <= 1024
+ * (GNN_ERR_UNSUPPORTED otherwise, before anything is launched); Y, a_src,
+ * a_dst and saved 16-byte aligned (GNN_ERR_INVALID_ARG otherwise). */
 size_t gnn_gat_saved_size(gnn_graph_t g, int heads, int64_t d_head);
 size_t gnn_gat_workspace_size(gnn_graph_t g, int64_t d_in, int heads, int64_t d_head);
 gnn_status_t gnn_gat_layer_fwd(gnn_graph_t g, const float* X, int64_t d_in, const float* W, const float* a_src,
@@ -434,7 +439,8 @@ gnn_status_t gnn_gat_layer_fwd(gnn_graph_t g, const float* X, int64_t d_in, cons
  * dE, which lets the SDDMM dot, dE, dS and the transposed SpMM run as one
  * pass over the out-edges (alpha formed again from S, D, M, Z).  Requires the
  * CSC view, 1, 2, 4 or 8 heads and d_head a power of two from 4 to 256
- * (GNN_ERR_UNSUPPORTED otherwise). */
+ * (GNN_ERR_UNSUPPORTED otherwise); Y, dY, a_src, a_dst and saved 16-byte
+ * aligned (GNN_ERR_INVALID_ARG otherwise). */
 gnn_status_t gnn_gat_layer_bwd(gnn_graph_t g, const float* X, int64_t d_in, const float* W, const float* a_src,
                                const float* a_dst, int heads, int64_t d_head, float slope, const float* Y,
                                const float* dY, const void* saved, float* dX, float* dW, float* da_src,

@@ -341,153 +341,6 @@ __device__ __forceinline__ void softmax_fwd_rows(const Sched& s, const float* E,
     }
 }
 
-// ---------------------------------------------------------------------------
-// GAT attention in one pass over each destination's in-edges: the scores
-// E = LReLU(S[src] + D[dst]) are formed on the fly (the same arithmetic as
-// the SDDMM-add kernel), E_pre is stored for the backward's LeakyReLU
-// derivative, and the edge softmax (the same arithmetic and per-lane orders
-// as the softmax kernels) writes alpha -- E itself is never stored.  Short
-// rows keep their scores in registers; longer ones form them again in each
-// of the softmax's three sweeps (S is small and stays cached).
-// ---------------------------------------------------------------------------
-// alpha of edge e: edge-major (alpha[e*H + k]) when as == 0, else one plane
-// per head (alpha[k*as + e]), which the aggregation reads one head per slab
-template <int H>
-__device__ __forceinline__ void st_alpha(float* alpha, int64_t as, int64_t e, const HV<H>& x) {
-    if (as == 0) {
-        st<H>(alpha + e * H, x);
-        return;
-    }
-#pragma unroll
-    for (int k = 0; k < H; ++k) alpha[k * as + e] = x.v[k];
-}
-
-template <int H>
-__device__ __forceinline__ HV<H> attn_score(const float* S, const HV<H>& dv, int64_t u, float slope, int act,
-                                            HV<H>& pre) {
-    HV<H> r;
-#pragma unroll
-    for (int k = 0; k < H; ++k) {
-        pre.v[k] = S[u * H + k] + dv.v[k];
-        r.v[k] = (act && !(pre.v[k] > 0.0f)) ? slope * pre.v[k] : pre.v[k];
-    }
-    return r;
-}
-
-template <int H>
-__device__ __forceinline__ void attn_rows(const Sched& s, const float* S, const float* D, float slope, int act,
-                                          float* alpha, int64_t as, float* out_pre, float* mo, float* zo, int64_t blk) {
-    const int lane = threadIdx.x % G;
-    const int64_t li = s.n_block + static_cast<int64_t>(blk) * (256 / G) + threadIdx.x / G;
-    if (li >= s.n) return;
-    const int64_t v = s.order[li];
-    const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
-    HV<H> dv, pre, m, z;
-#pragma unroll
-    for (int k = 0; k < H; ++k) dv.v[k] = D[v * H + k];
-    hv_fill<H>(m, -INFINITY);
-    hv_fill<H>(z, 0.0f);
-    if (ee - eb <= G * kCache) {
-        HV<H> x[kCache];
-#pragma unroll
-        for (int c = 0; c < kCache; ++c) {
-            const int64_t e = eb + lane + c * G;
-            if (e < ee) {
-                x[c] = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-                if (out_pre) st<H>(out_pre + e * H, pre);
-#pragma unroll
-                for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x[c].v[k]);
-            }
-        }
-        hv_group_max<H, G>(m);
-#pragma unroll
-        for (int c = 0; c < kCache; ++c)
-            if (eb + lane + c * G < ee) {
-#pragma unroll
-                for (int k = 0; k < H; ++k) z.v[k] += __expf(x[c].v[k] - m.v[k]);
-            }
-        hv_group_sum<H, G>(z);
-#pragma unroll
-        for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];
-        if (mo && lane == 0) st<H>(mo + v * H, m), st<H>(zo + v * H, z);
-#pragma unroll
-        for (int c = 0; c < kCache; ++c) {
-            const int64_t e = eb + lane + c * G;
-            if (e < ee) {
-#pragma unroll
-                for (int k = 0; k < H; ++k) x[c].v[k] = __expf(x[c].v[k] - m.v[k]) * z.v[k];
-                st_alpha<H>(alpha, as, e, x[c]);
-            }
-        }
-        return;
-    }
-    for (int64_t e = eb + lane; e < ee; e += G) {
-        const HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-        if (out_pre) st<H>(out_pre + e * H, pre);
-#pragma unroll
-        for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x.v[k]);
-    }
-    hv_group_max<H, G>(m);
-    for (int64_t e = eb + lane; e < ee; e += G) {
-        const HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-#pragma unroll
-        for (int k = 0; k < H; ++k) z.v[k] += __expf(x.v[k] - m.v[k]);
-    }
-    hv_group_sum<H, G>(z);
-#pragma unroll
-    for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];
-    if (mo && lane == 0) st<H>(mo + v * H, m), st<H>(zo + v * H, z);
-    for (int64_t e = eb + lane; e < ee; e += G) {
-        HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-#pragma unroll
-        for (int k = 0; k < H; ++k) x.v[k] = __expf(x.v[k] - m.v[k]) * z.v[k];
-        st_alpha<H>(alpha, as, e, x);
-    }
-}
-
-template <int H>
-__device__ __forceinline__ void attn_block(const Sched& s, const float* S, const float* D, float slope, int act,
-                                           float* alpha, int64_t as, float* out_pre, float* mo, float* zo, int64_t blk,
-                                           float (*sh)[H]) {
-    const int64_t v = s.order[blk];
-    const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
-    HV<H> dv, pre, m, z;
-#pragma unroll
-    for (int k = 0; k < H; ++k) dv.v[k] = D[v * H + k];
-    hv_fill<H>(m, -INFINITY);
-    for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
-        const HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-        if (out_pre) st<H>(out_pre + e * H, pre);
-#pragma unroll
-        for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x.v[k]);
-    }
-    hv_block_reduce<H, true>(m, sh);
-    hv_fill<H>(z, 0.0f);
-    for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
-        const HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-#pragma unroll
-        for (int k = 0; k < H; ++k) z.v[k] += __expf(x.v[k] - m.v[k]);
-    }
-    hv_block_reduce<H, false>(z, sh);
-#pragma unroll
-    for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];
-    if (mo && threadIdx.x == 0) st<H>(mo + v * H, m), st<H>(zo + v * H, z);
-    for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
-        HV<H> x = attn_score<H>(S, dv, s.idx[e], slope, act, pre);
-#pragma unroll
-        for (int k = 0; k < H; ++k) x.v[k] = __expf(x.v[k] - m.v[k]) * z.v[k];
-        st_alpha<H>(alpha, as, e, x);
-    }
-}
-
-template <int H>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(Sched s, const float* S, const float* D, float slope, int act,
-                                                       float* alpha, int64_t as, float* out_pre, float* mo, float* zo) {
-    __shared__ float sh[4][H];
-    if (blockIdx.x < s.n_block) attn_block<H>(s, S, D, slope, act, alpha, as, out_pre, mo, zo, blockIdx.x, sh);
-    else attn_rows<H>(s, S, D, slope, act, alpha, as, out_pre, mo, zo, blockIdx.x - s.n_block);
-}
-
 template <int H>
 __device__ __forceinline__ void softmax_fwd_block(const Sched& s, const float* E, float* alpha, int64_t blk, float (*sh)[H]) {
     const int64_t v = s.order[blk];
@@ -879,22 +732,6 @@ gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha,
         hipLaunchKernelGGL((softmax_fwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, E, alpha);
     });
     return launch_status("gnn_edge_softmax");
-}
-
-gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float* D, int heads, float slope,
-                                  float* alpha, int64_t alpha_head_stride, float* out_pre, float* row_max,
-                                  float* row_rsum, hipStream_t st) {
-    if (v.n == 0) return GNN_OK;
-    Sched s = make_sched(v);
-    const int64_t light = s.n - s.n_block;
-    const int64_t blocks = (light + (256 / G) - 1) / (256 / G);
-    const int act = slope == slope;  // NaN: no activation
-    ScopedTimer t(st, "attn_fwd_kernel h=%d", heads);
-    GNN_HEADS_SWITCH(heads, {
-        hipLaunchKernelGGL((attn_fwd_kernel<H>), dim3(s.n_block + blocks), dim3(256), 0, st, s, S, D,
-                           act ? slope : 0.0f, act, alpha, alpha_head_stride, out_pre, row_max, row_rsum);
-    });
-    return launch_status("GAT attention");
 }
 
 gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha, const float* pre,

@@ -131,8 +131,7 @@ inline size_t quantised_source_record_bytes(int64_t n) { return static_cast<size
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
-                         const MaskEpilogue& mask = MaskEpilogue{}, const QuantSources& qs = QuantSources{},
-                         int64_t w_head_stride = 0);
+                         const MaskEpilogue& mask = MaskEpilogue{}, const QuantSources& qs = QuantSources{});
 gnn_status_t launch_quantize_sym8(const float* X, int64_t ldx, int64_t rows, int64_t cols, const float* mptr,
                                   uint64_t seed, uint32_t stream_id, int8_t* out, int64_t out_ld, int transpose,
                                   float* s_out, hipStream_t st);
@@ -173,12 +172,13 @@ gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const 
                                   const float* D, const float* M, const float* Z, const float* Y, const float* dY,
                                   const float* a_src, const float* a_dst, float4* rec, float* dEh, float* dEc,
                                   float* part, float* dS, float* dD, float* dHp, hipStream_t st);
-// SDDMM-add + LeakyReLU + edge softmax in one pass (S, D: [n, heads]); alpha [nnz, heads], or one
-// plane per head (alpha[k*alpha_head_stride + e]) when alpha_head_stride > 0; optional E_pre [nnz, heads];
-// optional row_max, row_rsum [n, heads]: each row's score maximum and 1 / sum of exponentials
-gnn_status_t launch_gat_attention(const AggView& v, const float* S, const float* D, int heads, float slope,
-                                  float* alpha, int64_t alpha_head_stride, float* out_pre, float* row_max,
-                                  float* row_rsum, hipStream_t st);
+// GAT forward edge pass (gat_fwd.hip): per destination and head, the scores from the gathered H' rows,
+// LeakyReLU, the softmax folded into the weighted aggregation (running maximum); writes Y and each
+// destination's softmax maximum M and 1 / sum Z ([n, heads]); chunk partials in `part`
+size_t gat_fused_fwd_partial_bytes(const RowPlan& csr_plan, int heads, int64_t d_head);
+gnn_status_t launch_gat_fwd_fused(const AggView& csr, int heads, int64_t d_head, float slope, const float* Hp,
+                                  const float* D, const float* a_src, float* Y, float* M, float* Z, float* part,
+                                  hipStream_t st);
 gnn_status_t launch_edge_softmax_bwd(const AggView& v, const float* alpha, const float* dalpha,
                                      const float* pre, float slope, float* dE, int heads, hipStream_t st);
 gnn_status_t launch_edge_reduce(const AggView& v, const float* vals, int heads, float* out, hipStream_t st);

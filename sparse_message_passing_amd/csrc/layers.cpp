@@ -227,8 +227,8 @@ gnn_status_t gnn_sage_layer_bwd(gnn_graph_t h, const void* X, gnn_dtype_t x_dt, 
 size_t gnn_gat_saved_size(gnn_graph_t h, int heads, int64_t d_head) {
     if (!h || heads < 1 || d_head < 1) return 0;
     const Graph& g = h->g;
-    const size_t n = g.n, e = g.nnz, hd = static_cast<size_t>(heads) * d_head;
-    return align_up(n * hd * 4) + 4 * align_up(n * heads * 4) + align_up(e * heads * 4);
+    const size_t n = g.n, hd = static_cast<size_t>(heads) * d_head;
+    return align_up(n * hd * 4) + 4 * align_up(n * heads * 4);
 }
 
 size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_head) {
@@ -238,8 +238,8 @@ size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_
     const int64_t hd = heads * d_head;
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
     gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
-    // forward: GEMM workspace, then the aggregation's hub-row partials
-    const size_t fwd = align_up(gemm) + align_up(spmm_partial_bytes(g.plan[0], hd));
+    // forward: GEMM workspace, then the edge pass's hub-row partials
+    const size_t fwd = align_up(gemm) + align_up(gat_fused_fwd_partial_bytes(g.plan[0], heads, d_head));
     // backward: dE (CSC order: per-head planes, then per-edge records), the
     // per-destination records, dD, dS, dH', the CSC pass's chunk partials,
     // the column-sum partials, the GEMM workspace
@@ -251,20 +251,20 @@ size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_
 
 namespace {
 struct GatSaved {
-    float *Hp, *S, *D, *M, *Z, *alpha;
+    float *Hp, *S, *D, *M, *Z;
 };
 GatSaved carve_saved(const Graph& g, void* saved, int heads, int64_t d_head) {
     Carver c(saved);
-    const size_t n = g.n, e = g.nnz, hd = static_cast<size_t>(heads) * d_head;
+    const size_t n = g.n, hd = static_cast<size_t>(heads) * d_head;
     GatSaved s;
     s.Hp = static_cast<float*>(c.take(n * hd * 4));
     s.S = static_cast<float*>(c.take(n * heads * 4));
     s.D = static_cast<float*>(c.take(n * heads * 4));
     s.M = static_cast<float*>(c.take(n * heads * 4));
     s.Z = static_cast<float*>(c.take(n * heads * 4));
-    s.alpha = static_cast<float*>(c.take(e * heads * 4));
     return s;
 }
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 }  // namespace
 
 gnn_status_t gnn_gat_layer_fwd(gnn_graph_t h, const float* X, int64_t d_in, const float* W, const float* a_src,
@@ -279,6 +279,8 @@ gnn_status_t gnn_gat_layer_fwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     if (!gat_fused_bwd_supported(heads, d_head) || heads * d_head > 1024)
         return fail(GNN_ERR_UNSUPPORTED, "gnn_gat_layer_fwd: needs 1, 2, 4 or 8 heads, d_head a power of two from 4 "
                                          "to 256 and heads * d_head <= 1024");
+    GNN_REQUIRE(g.n == 0 || (aligned16(Y) && aligned16(a_src) && aligned16(a_dst) && aligned16(saved)),
+                "gnn_gat_layer_fwd: Y, a_src, a_dst and saved must be 16-byte aligned");
     const size_t need = gnn_gat_workspace_size(h, d_in, heads, d_head);
     if (ws_bytes < need || (!ws && need))
         return fail(GNN_ERR_WORKSPACE, "gnn_gat_layer_fwd: workspace smaller than gnn_gat_workspace_size()");
@@ -290,16 +292,14 @@ gnn_status_t gnn_gat_layer_fwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
     gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
     void* gws = c.take(gemm);
-    float* sws = static_cast<float*>(c.take(1));
-    // H' = X W;  S, D per-head scores;  E = LReLU(S[src] + D[dst]);  alpha = softmax
-    // (keeping each row's maximum and 1/sum);  Y = (G . alpha) H'
+    float* part = static_cast<float*>(c.take(gat_fused_fwd_partial_bytes(g.plan[0], heads, d_head)));
+    // H' = X W;  S, D per-head scores (S for the backward, D for both);
+    // then one pass over the in-edges: E = LReLU(S[src] + D[dst]) with S[src]
+    // formed from the gathered row H'[src], the softmax folded into
+    // Y = (G . alpha) H', each row's maximum and 1/sum kept
     GNN_TRY(launch_gemm(0, 0, g.n, hd, d_in, X, GNN_F32, d_in, W, GNN_F32, hd, s.Hp, GNN_F32, hd, gws, gemm, st));
     GNN_TRY(launch_gat_scores(g.n, s.Hp, heads, d_head, a_src, a_dst, s.S, s.D, st));
-    // alpha is kept one plane per head, so the aggregation's head slabs read
-    // their weights contiguously
-    GNN_TRY(launch_gat_attention(csr_view(g), s.S, s.D, heads, slope, s.alpha, g.nnz, nullptr, s.M, s.Z, st));
-    return launch_spmm(csr_view(g), g.dinv, GNN_W_EDGE, s.alpha, heads, s.Hp, GNN_F32, hd, Y, GNN_F32, hd, hd, 0,
-                       Rank1Epilogue{}, sws, st, MaskEpilogue{}, QuantSources{}, g.nnz);
+    return launch_gat_fwd_fused(csr_view(g), heads, d_head, slope, s.Hp, s.D, a_src, Y, s.M, s.Z, part, st);
 }
 
 gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, const float* W, const float* a_src,
@@ -315,6 +315,9 @@ gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     if (!gat_fused_bwd_supported(heads, d_head))
         return fail(GNN_ERR_UNSUPPORTED, "gnn_gat_layer_bwd: needs 1, 2, 4 or 8 heads and d_head a power of two "
                                          "from 4 to 256");
+    GNN_REQUIRE(g.n == 0 || (aligned16(Y) && aligned16(dY) && aligned16(a_src) && aligned16(a_dst) &&
+                             aligned16(saved)),
+                "gnn_gat_layer_bwd: Y, dY, a_src, a_dst and saved must be 16-byte aligned");
     const size_t need = gnn_gat_workspace_size(h, d_in, heads, d_head);
     if (ws_bytes < need || (!ws && need))
         return fail(GNN_ERR_WORKSPACE, "gnn_gat_layer_bwd: workspace smaller than gnn_gat_workspace_size()");

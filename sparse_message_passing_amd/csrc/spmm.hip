@@ -97,7 +97,6 @@ struct SpmmArgs {
     float* partial;
     const float* wgcn;   // GCN edge weights in this view's edge order (NULL: dinv[u]*dinv[v] on the fly)
     const float* dmean;  // [n] 1 / CSR row length (mean weights)
-    int64_t w_hstride;   // > 0: edge weights one plane per head in this view's order, weight(e, k) = edge_w[k*w_hstride + e]
     const int32_t* qslot;           // dequantise-in-gather: slot of each source node, -1 = row of X
     QGroupDev qg[kMaxQGroups];
     int q_words;                    // every group's code rows are whole 4-byte words
@@ -223,10 +222,6 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
                 // an in-edge of row v weighs 1/len(v); over the CSC view the
                 // edge's destination is the other end
                 w_my[0] = a.eid ? a.dmean[u_my] : dv;
-            } else if (a.w_hstride) {
-#pragma unroll
-                for (int k = 0; k < kMaxHeads; ++k)
-                    if (k >= klo && k <= khi) w_my[k] = a.edge_w[k * a.w_hstride + e];
             } else {
                 const int64_t ce = a.eid ? static_cast<int64_t>(a.eid[e]) : e;
 #pragma unroll
@@ -522,7 +517,7 @@ size_t spmm_partial_bytes(const RowPlan& p, int64_t d) {
 gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmode, const float* edge_w, int heads,
                          const void* X, gnn_dtype_t x_dt, int64_t ldx, void* Y, gnn_dtype_t y_dt, int64_t ldy,
                          int64_t d, int relu, const Rank1Epilogue& r1, float* partial, hipStream_t st,
-                         const MaskEpilogue& mask, const QuantSources& qs, int64_t w_head_stride) {
+                         const MaskEpilogue& mask, const QuantSources& qs) {
     if (v.n == 0 || d == 0) return GNN_OK;
     if (heads > kMaxHeads) return fail(GNN_ERR_UNSUPPORTED, "gnn_spmm: at most 8 heads");
     SpmmArgs a;
@@ -551,7 +546,6 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     a.partial = partial;
     a.wgcn = v.wgcn;
     a.dmean = v.dmean;
-    a.w_hstride = wmode == GNN_W_EDGE ? w_head_stride : 0;
     a.qslot = qs.qslot;
     a.qrec = nullptr;
     a.addend = qs.addend;
@@ -575,8 +569,7 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     // Column slabs, except where each edge's weights are reached through the
     // CSC-to-CSR edge map: those scattered weight reads would repeat in every
     // slab (measured: slabs slow the transposed 4-head GAT aggregation down).
-    // Weights in one plane per head are read contiguously, one head per slab.
-    if (vec && !(wmode == GNN_W_EDGE && v.eid && a.w_hstride == 0)) {
+    if (vec && !(wmode == GNN_W_EDGE && v.eid)) {
         // halve the pass width while the source rows' slab (rows x width)
         // exceeds the cache budget, down to the minimum slab row
         const int64_t rows = v.n;
@@ -614,7 +607,7 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     if (x_dt == GNN_BF16 && vec && ldx % 8 == 0 && ldx >= a.pd && reinterpret_cast<uintptr_t>(X) % 16 == 0 &&
         (heads == 1 || a.dh % 8 == 0)) {
         int64_t need8 = a.pd / 8;
-        if (!(wmode == GNN_W_EDGE && v.eid && a.w_hstride == 0)) {
+        if (!(wmode == GNN_W_EDGE && v.eid)) {
             int64_t w = 8;
             while (w < need8) w *= 2;
             const int64_t min_w8 = std::max<int64_t>(8, kSlabMinBytes / (8 * static_cast<int64_t>(xs)));

@@ -516,20 +516,19 @@ def gnn_gat_layer_bwd(g: Graph, X, W, a_src, a_dst, heads, d_head, slope, Y, dY,
 
 
 def gat_saved_views(g: Graph, saved, heads, d_head):
-    """Views (H', S, D, M, Z, alpha) into a GAT forward's saved buffer (the
-    same 256-byte aligned slices the library carves): M and Z are each
-    destination's softmax maximum and 1 / sum of exponentials per head;
-    alpha is [nnz, heads] over storage that holds one plane per head."""
+    """Views (H', S, D, M, Z) into a GAT forward's saved buffer (the same
+    256-byte aligned slices the library carves): M and Z are each
+    destination's softmax maximum and 1 / sum of exponentials per head, so
+    alpha[e, k] = exp(LReLU(S[src, k] + D[dst, k]) - M[dst, k]) * Z[dst, k]."""
     f = saved.view(torch.float32) if saved.dtype == torch.uint8 else saved
     al = lambda b: (b + 255) // 256 * 256
-    n, e, hd = g.n, g.nnz, heads * d_head
+    n, hd = g.n, heads * d_head
     off = 0
     out = []
     for count, shape in ((n * hd, (n, hd)), (n * heads, (n, heads)), (n * heads, (n, heads)),
-                         (n * heads, (n, heads)), (n * heads, (n, heads)), (e * heads, (heads, e))):
+                         (n * heads, (n, heads)), (n * heads, (n, heads))):
         out.append(f[off // 4: off // 4 + count].view(*shape))
         off += al(count * 4)
-    out[-1] = out[-1].t()  # alpha is stored one plane per head; the view is [nnz, heads]
     return tuple(out)
 
 

@@ -94,6 +94,18 @@ def sub_rows(og, rows):
     return oracle.OracleGraph(rows.size, rp, og.col[eids].astype(np.int32), dst), eids
 
 
+def saved_alpha(og, S, D, M, Z, slope, eids=None):
+    """The attention weights a GAT forward leaves implied by its saved per-node
+    S, D and per-destination M, Z (device tensors): alpha[e] =
+    exp(LReLU(S[src] + D[dst]) - M[dst]) * Z[dst] in float64 from the binary32
+    score sum (the edges eids of og, or all of them)."""
+    S, D, M, Z = (from_dev(t) for t in (S, D, M, Z))
+    col, dst = (og.col, og.dst) if eids is None else (og.col[eids], og.dst[eids])
+    E = S[col] + D[dst]                       # one binary32 add, as the kernels
+    E = np.where(E > 0, E, np.float32(slope) * E).astype(np.float64)
+    return np.exp(E - M[dst].astype(np.float64)) * Z[dst].astype(np.float64)
+
+
 def softmax_row_stats(og, E):
     """Per destination row and head, the maximum M of the scores E over the
     row's in-edges and Z = 1 / sum exp(E - M) (float64; rows without in-edges

@@ -127,9 +127,12 @@ def test_gat_on_self_loops_only():
     Y = torch.empty((n, heads * dh), device="cuda")
     saved = torch.empty(gnnmp.gnn_gat_saved_size(g, heads, dh), dtype=torch.uint8, device="cuda")
     gnnmp.gnn_gat_layer_fwd(g, X, W, a_s, a_d, heads, dh, 0.2, Y, saved)
-    Hp = gnnmp.gat_saved_views(g, saved, heads, dh)[0]
-    al = gnnmp.gat_saved_views(g, saved, heads, dh)[5]
-    assert torch.equal(al, torch.ones_like(al))
+    Hp, S, D, M, Z = gnnmp.gat_saved_views(g, saved, heads, dh)
+    # the forward's own score of each self-loop is bitwise S + D (the same
+    # binary32 operations), so its maximum is that score and its sum exp(0) = 1
+    E = S + D
+    E = torch.where(E > 0, E, 0.2 * E)
+    assert torch.equal(M, E) and torch.equal(Z, torch.ones_like(Z))
     assert torch.equal(Y, Hp)
     dY = torch.randn((n, heads * dh), device="cuda")
     dW = torch.empty_like(W)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from parity import (RTOL16, RTOL32, check_close, check_gcn_stack_step, from_dev, graph_pair, hub_edges, rmat_graph,
-                    softmax_row_stats, to_dev)
+                    saved_alpha, softmax_row_stats, to_dev)
 from sparse_message_passing_amd import gnnmp, synth
 from sparse_message_passing_amd.step import GcnStack
 
@@ -296,7 +296,7 @@ def test_gat_layer_fwd_bwd(gatg, heads, dh, din):
     Y = torch.empty((n, hd), device="cuda")
     saved = torch.empty(gnnmp.gnn_gat_saved_size(g, heads, dh), dtype=torch.uint8, device="cuda")
     gnnmp.gnn_gat_layer_fwd(g, Xd, Wd, asd, add, heads, dh, slope, Y, saved)
-    Hp, S, D, M, Z, al = gnnmp.gat_saved_views(g, saved, heads, dh)
+    Hp, S, D, M, Z = gnnmp.gat_saved_views(g, saved, heads, dh)
     mHp = np.abs(X) @ np.abs(W)
     check_close(from_dev(Hp), fw["Hp"], mHp, what="H'")
     mS = oracle.gat_scores(mHp, np.abs(a_s), heads)
@@ -314,7 +314,8 @@ def test_gat_layer_fwd_bwd(gatg, heads, dh, din):
     # alpha moves by at most alpha * 2 max|dE| over the destination's in-edges
     rowmax = rowmax_v[og.dst]
     m_al = fw["alpha"] * (2 * rowmax + 1)
-    check_close(from_dev(al), fw["alpha"], m_al, what="alpha")
+    # the attention weights the backward forms again from the saved S, D, M, Z
+    check_close(saved_alpha(og, S, D, M, Z, slope), fw["alpha"], m_al, what="alpha")
     mY = oracle.spmm(og, mHp, m_al, heads) + oracle.spmm(og, np.abs(fw["Hp"]), fw["alpha"], heads)
     check_close(from_dev(Y), fw["Y"], mY, what="GAT Y")
 
@@ -326,9 +327,9 @@ def _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r):
     gradient checked element by element."""
     n, hd, din = og.n, heads * dh, X.shape[1]
     Xd, Wd, asd, add = to_dev(X), to_dev(W), to_dev(a_s), to_dev(a_d)
-    Hp, S, D, M, Z, al = gnnmp.gat_saved_views(g, saved, heads, dh)
+    Hp, S, D, M, Z = gnnmp.gat_saved_views(g, saved, heads, dh)
     M_ref, Z_ref = softmax_row_stats(og, fw["E"])
-    for view, val in zip((Hp, S, D, M, Z, al), (fw["Hp"], fw["S"], fw["D"], M_ref, Z_ref, fw["alpha"])):
+    for view, val in zip((Hp, S, D, M, Z), (fw["Hp"], fw["S"], fw["D"], M_ref, Z_ref)):
         view.copy_(to_dev(val))
     dY = r.standard_normal((n, hd)).astype(np.float32)
     bw = oracle.gat_layer_bwd(og, fw, X, W, a_s, a_d, dY, heads, slope)
