@@ -190,6 +190,10 @@ gnn_status_t launch_head_colsum(int64_t n, const float* coefA, const float* coef
                                 int64_t d_head, float* outA, float* outB, float* partial, hipStream_t st);
 
 size_t gemm_ws_bytes(int transA, int transB, int64_t M, int64_t N, int64_t K);
+// bf16 x bf16 weight gradient C = A^T B (gemm_bf16.hip): split-K partials [splits][M][N] into `part`
+bool gemm_tn_bf16_supported(int64_t lda, int64_t ldb, const void* A, const void* B);
+gnn_status_t launch_gemm_tn_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                                 int64_t ldb, float* part, int64_t splits, int64_t kper, hipStream_t st);
 gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
                          int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb, void* C, gnn_dtype_t c_dt,
                          int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu = 0,

@@ -219,6 +219,12 @@ GEMM_CASES = [
     (999, 256, 100, False, True, "bf16", "bf16", "bf16"),
     (256, 47, 70003, True, False, "bf16", "bf16", "f32"),
     (70, 50, 30, True, True, "bf16", "bf16", "f32"),
+    # bf16 x bf16 weight gradients with rows of a whole 16 bytes, split over K:
+    # the 16x16x32 bf16 matrix-core kernel (ragged M, N and K, bf16 output)
+    (104, 256, 30000, True, False, "bf16", "bf16", "f32"),
+    (256, 72, 70003, True, False, "bf16", "bf16", "f32"),
+    (256, 256, 9000, True, False, "bf16", "bf16", "bf16"),
+    (136, 120, 4104, True, False, "bf16", "bf16", "f32"),
     # interior 128 x 128 tiles with a K span of 256 or more: the loads go two
     # slabs ahead (weight gradients and bf16-A products); odd and even slab
     # counts end the pipelined loop differently, and a ragged M mixes in edge
@@ -252,12 +258,14 @@ def test_gemm(case):
     check_close(from_dev(C), ref, mag, bf16_out=cdt == "bf16", what="gemm")
 
 
-@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False)])
-def test_gemm_bf16_pair_integer_exact(ta, tb):
+@pytest.mark.parametrize("ta,tb,M,N", [(False, False, 515, 260), (False, True, 515, 260), (True, False, 515, 260),
+                                       (True, False, 520, 264)])
+def test_gemm_bf16_pair_integer_exact(ta, tb, M, N):
     # bf16 x bf16 on the bf16 matrix cores with small integers: every product
-    # and partial sum is exact in binary32, so the result is exact
+    # and partial sum is exact in binary32, so the result is exact (rows of a
+    # whole 16 bytes take the 16x16x32 weight-gradient kernel)
     r = np.random.default_rng(4)
-    M, N, K = 515, 260, 4100
+    K = 4100
     A = r.integers(-3, 4, (K, M) if ta else (M, K)).astype(np.float32)
     B = r.integers(-3, 4, (N, K) if tb else (K, N)).astype(np.float32)
     C = torch.empty((M, N), device="cuda")
