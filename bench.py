@@ -216,7 +216,7 @@ def kernel_model(key, n, nnz, ctx):
         return ("bytes", gat_bwd_csc_bytes(n, nnz, int(kv["h"]), int(kv["dh"])))
     if name == "gat_in_sum_kernel":
         h, dh = int(kv["h"]), int(kv["dh"])
-        return ("bytes", 8 * (n + 1) + 4 * nnz + 4 * nnz * h + 4 * n * h + 8 * n * h * dh + 4 * n)
+        return ("bytes", 8 * (n + 1) + 4 * nnz + 4 * nnz * h + 4 * n * h + 4 * n)
     if name == "sddmm_dot_kernel":
         h, dh = int(kv["h"]), int(kv["dh"])
         s = size(key.split()[-1])

@@ -15,7 +15,10 @@
 // needed before any dE, and since sum_in alpha H'[u] is the forward's output
 // row, c[v] = <dY[v, k], Y[v, k]>: a dense row product, not an edge sum.
 // dD needs the in-edge sum, so dE is also written (CSC order) and summed per
-// destination through the CSR -> CSC slot map, which then adds dD a_dst.
+// destination through the CSR -> CSC slot map.  The dD a_dst term of dH' is
+// not added here: the two products that read dH' (dW = X^T dH' and
+// dX = dH' W^T) add it as they load each element, with the same single
+// fmaf, which saves a read and a write of the whole of dH'.
 //
 // The CSC pass runs one head at a time (a column slab of H' and dY, slab-
 // major over the grid) so each gathered slab of dY stays in the memory-side
@@ -268,10 +271,7 @@ struct InSumArgs {
     int64_t n_block;             // rows that take a whole workgroup: order[0 .. n_block)
     const int32_t* cpos;         // CSC slot of each CSR edge
     const float* dEc;            // [nnz, H] CSC order
-    int64_t dh;
-    const float* a_dst;          // [H, dh]
     float* dD;                   // [n, H]
-    float* dHp;                  // [n, H*dh], dD a_dst added in place
 };
 
 template <int H>
@@ -282,23 +282,6 @@ __device__ __forceinline__ void add_edge(float (&acc)[H], const float* p) {
     } else {
 #pragma unroll
         for (int k = 0; k < H; ++k) acc[k] += p[k];
-    }
-}
-
-// dH'[v, f..f+3] += dD[v, head of f] a_dst[f..f+3] for the lane's features
-template <int H>
-__device__ __forceinline__ void add_rank1(const InSumArgs& a, int64_t v, const float (&dd)[H], int64_t f0,
-                                          int64_t step) {
-    const int64_t hd = H * a.dh;
-    for (int64_t f = f0; f < hd; f += step) {
-        const int k = static_cast<int>(f / a.dh);
-        float w = dd[0];
-#pragma unroll
-        for (int kk = 1; kk < H; ++kk) w = kk == k ? dd[kk] : w;
-        float4* p = reinterpret_cast<float4*>(a.dHp + v * hd + f);
-        const float4 h = *p;
-        const float4 ad = *reinterpret_cast<const float4*>(a.a_dst + f);
-        *p = make_float4(fmaf(w, ad.x, h.x), fmaf(w, ad.y, h.y), fmaf(w, ad.z, h.z), fmaf(w, ad.w, h.w));
     }
 }
 
@@ -329,7 +312,6 @@ __global__ __launch_bounds__(256) void gat_in_sum_kernel(InSumArgs a) {
 #pragma unroll
             for (int k = 0; k < H; ++k) a.dD[v * H + k] = acc[k];
         }
-        add_rank1<H>(a, v, acc, threadIdx.x * 4, 1024);
         return;
     }
     const int lane = threadIdx.x % kInLanes;
@@ -345,7 +327,6 @@ __global__ __launch_bounds__(256) void gat_in_sum_kernel(InSumArgs a) {
 #pragma unroll
         for (int k = 0; k < H; ++k) a.dD[v * H + k] = acc[k];
     }
-    add_rank1<H>(a, v, acc, lane * 4, kInLanes * 4);
 }
 
 }  // namespace
@@ -362,7 +343,7 @@ size_t gat_fused_bwd_partial_bytes(const RowPlan& csc_plan, int heads, int64_t d
 gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const int32_t* cpos, int64_t nnz, int heads,
                                   int64_t d_head, float slope, const float* Hp, const float* S, const float* D,
                                   const float* M, const float* Z, const float* Y, const float* dY,
-                                  const float* a_src, const float* a_dst, float4* rec, float* dEh, float* dEc,
+                                  const float* a_src, float4* rec, float* dEh, float* dEc,
                                   float* part, float* dS, float* dD, float* dHp, hipStream_t st) {
     const int64_t n = csr.n;
     if (n == 0) return GNN_OK;
@@ -445,10 +426,7 @@ gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const 
     b.n_block = csr.plan->n_block;
     b.cpos = cpos;
     b.dEc = dEc;
-    b.dh = d_head;
-    b.a_dst = a_dst;
     b.dD = dD;
-    b.dHp = dHp;
     const int64_t light = n - b.n_block;
     const int64_t blocks = b.n_block + (light + (256 / kInLanes) - 1) / (256 / kInLanes);
     ScopedTimer t(st, "gat_in_sum_kernel h=%d dh=%lld", heads, static_cast<long long>(d_head));

@@ -31,7 +31,13 @@
 //    (workgroups are dealt round-robin over the 8 XCDs, each with its own L2);
 //  * tall reductions (K = number of nodes, for dW) are split over K; each
 //    split writes a binary32 partial tile and a second pass adds the splits
-//    in order.  No atomics: bitwise reproducible.
+//    in order.  No atomics: bitwise reproducible;
+//  * an operand may carry a per-head rank-1 term, X[r][c] + s[r, head of c]
+//    v[c], formed with one fmaf as each piece goes to LDS (a compile-time
+//    variant, so other products keep their registers): the GAT backward's
+//    dD a_dst term of dH', which otherwise costs a read and a write of all of
+//    dH' (2^21 x 256 f32: the in-edge pass 1.92 -> 0.90 ms, the dX product
+//    2.54 -> 2.85 ms, the dW product unchanged; results bitwise the same).
 
 #include <algorithm>
 #include <type_traits>
@@ -82,6 +88,8 @@ struct GemmArgs {
     int vec_mask;    // mask rows take 16-byte (bf16: 8-byte) loads
     int vec_ws;      // split-K partial rows (stride N) take 16-byte stores
     MaskEpilogue mask;  // C *= [M > 0] (after the split-K sum)
+    OperandRank1 r1;    // kernels with R1 = 1: A (stored [M][K]) read as A + s v, s per (row m, head of k);
+                        // R1 = 2: B (stored [K][N]) read as B + s v, s per (row k, head of n)
 };
 
 __device__ __forceinline__ bool mask_on(const MaskEpilogue& m, int64_t r, int64_t c) {
@@ -109,16 +117,45 @@ __device__ __forceinline__ void load4(const T* base, int64_t off, bool full, int
     }
 }
 
+// The rank-1 term of a piece (stored row r, columns c..c+3, c a multiple of
+// 4 and so inside one head): its coefficient s[r, c / dh] and the four v[c + i]
+// are loaded with the piece, and added with one fmaf per element when the
+// piece is written to LDS, so the piece's global load is not waited for any
+// earlier than without the term.  Elements past the operand's edge get w = 0
+// or v = 0 (and are zero themselves): they stay zero.
+template <int NP>
+struct Rank1Regs {
+    float w[NP];
+    float v[NP][4];
+};
+
+__device__ __forceinline__ void rank1_v(const OperandRank1& o, int64_t c, int valid, float (&v)[4]) {
+    if (valid == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(o.v + c);
+        v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = i < valid ? o.v[c + i] : 0.0f;
+    }
+}
+
+__device__ __forceinline__ float rank1_w(const OperandRank1& o, int64_t r, int64_t c, int valid) {
+    return valid > 0 ? o.s[r * o.ld + (c >> o.dh_log2)] : 0.0f;
+}
+
 // TRANS_A: A given as [K][lda] (element (m,k) at A[k*lda+m]); else [M][lda].
 // TRANS_B: B given as [N][ldb] (element (k,n) at B[n*ldb+k]); else [K][ldb].
+// R1: 0, or the operand (1: A, 2: B) that carries the rank-1 term g.r1.
 template <int BM, int BN, int WM, int WN, bool TRANS_A, bool TRANS_B, bool VA, bool VB, bool PF, typename TA,
-          typename TB, typename TC>
+          typename TB, typename TC, int R1 = 0>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
     constexpr int A_LOADS = BM * BK / 4 / 256;  // float4-sized pieces per thread
     constexpr int B_LOADS = BN * BK / 4 / 256;
     static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
+    static_assert(R1 == 0 || (R1 == 1 && !TRANS_A) || (R1 == 2 && !TRANS_B), "rank-1 term on an untransposed operand");
+    constexpr int R1N = R1 == 1 ? A_LOADS : R1 == 2 ? B_LOADS : 1;
     // An operand contiguous along k is kept k-contiguous in LDS ([rows][BK+PAD]),
     // one contiguous along m / n is kept k-major ([BK][rows+PAD]): either way the
     // global->LDS store is one 16-byte write per thread and piece, and the
@@ -157,6 +194,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 
     float ra[A_LOADS][4], rb[B_LOADS][4];
     float ra1[A_LOADS][4], rb1[B_LOADS][4];  // slab s + 1 while s + 2 loads (PF)
+    Rank1Regs<R1N> rr, rr1;                  // the rank-1 terms of those two register sets
+    // With the term on B, a thread's pieces all cover columns n0 + 4 (tid % (BN / 4)) .. + 3 in every slab,
+    // so their v is loaded once (zero past column N).
+    float vb_r1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (R1 == 2) {
+        const int64_t c = n0 + (tid % (BN / 4)) * 4;
+        rank1_v(g.r1, c, static_cast<int>(max<int64_t>(0, min<int64_t>(4, g.N - c))), vb_r1);
+    }
 
     // Interior tiles (every row / column of the tile in range, 16-byte
     // aligned operands) load full slabs without per-element checks, from
@@ -186,11 +231,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
             const int q = tid + p * 256;
             if (a_full && full_k) {
                 load4<TA, true>(A, a_off[p], true, 4, ra[p]);
+                if constexpr (R1 == 1) {  // the pieces of a thread share their columns k0 + kc_k(tid)
+                    rr.w[p] = rank1_w(g.r1, m0 + kc_row(q), k0 + kc_k(q), 4);
+                    if (p == 0) rank1_v(g.r1, k0 + kc_k(q), 4, rr.v[0]);
+                    else
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) rr.v[p][i] = rr.v[0][i];
+                }
             } else if constexpr (!TRANS_A) {  // contiguous along k: q -> (m, k4)
                 const int mm = kc_row(q), kk = kc_k(q);
                 const int64_t m = m0 + mm, k = k0 + kk;
                 const int valid = (m < g.M) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, kend - k))) : 0;
                 load4<TA, VA>(A, m * g.lda + k, valid == 4, valid, ra[p]);
+                if constexpr (R1 == 1) {  // edge tiles and slabs: always reloaded
+                    rr.w[p] = rank1_w(g.r1, m, k, valid);
+                    rank1_v(g.r1, k, valid, rr.v[p]);
+                }
             } else {                   // contiguous along m: q -> (k, m4)
                 const int kk = q / (BM / 4), mm = (q % (BM / 4)) * 4;
                 const int64_t m = m0 + mm, k = k0 + kk;
@@ -204,11 +260,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
             const int q = tid + p * 256;
             if (b_full && full_k) {
                 load4<TB, true>(B, b_off[p], true, 4, rb[p]);
+                if constexpr (R1 == 2) rr.w[p] = rank1_w(g.r1, k0 + q / (BN / 4), n0 + (q % (BN / 4)) * 4, 4);
             } else if constexpr (!TRANS_B) {  // contiguous along n: q -> (k, n4)
                 const int kk = q / (BN / 4), nn = (q % (BN / 4)) * 4;
                 const int64_t n = n0 + nn, k = k0 + kk;
                 const int valid = (k < kend) ? static_cast<int>(max<int64_t>(0, min<int64_t>(4, g.N - n))) : 0;
                 load4<TB, VB>(B, k * g.ldb + n, valid == 4, valid, rb[p]);
+                if constexpr (R1 == 2) rr.w[p] = rank1_w(g.r1, k, n, valid);
             } else {                   // contiguous along k: q -> (n, k4)
                 const int nn = kc_row(q), kk = kc_k(q);
                 const int64_t n = n0 + nn, k = k0 + kk;
@@ -219,6 +277,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         }
     };
     auto store_slab = [&](int buf) {
+        if constexpr (R1 == 1) {
+#pragma unroll
+            for (int p = 0; p < A_LOADS; ++p)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ra[p][i] = fmaf(rr.w[p], rr.v[p][i], ra[p][i]);
+        }
+        if constexpr (R1 == 2) {
+#pragma unroll
+            for (int p = 0; p < B_LOADS; ++p)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rb[p][i] = fmaf(rr.w[p], vb_r1[i], rb[p][i]);
+        }
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
             const int q = tid + p * 256;
@@ -311,39 +381,61 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     // load_slab / store_slab with the register set as a parameter; routing
     // the one-slab loop through these made the compiler copy registers in
     // every instantiation's loop (the NN update 1.25 -> 1.48 ms).
-    auto load_full = [&](float (&xa)[A_LOADS][4], float (&xb)[B_LOADS][4]) {
+    int64_t k_full = kbeg;  // first k of the slab load_full reads next
+    auto load_full = [&](float (&xa)[A_LOADS][4], float (&xb)[B_LOADS][4], Rank1Regs<R1N>& xr) {
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
             load4<TA, true>(A, a_off[p], true, 4, xa[p]);
+            if constexpr (R1 == 1) {
+                xr.w[p] = rank1_w(g.r1, m0 + kc_row(tid + p * 256), k_full + kc_k(tid + p * 256), 4);
+                if (p == 0) rank1_v(g.r1, k_full + kc_k(tid), 4, xr.v[0]);
+                else
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xr.v[p][i] = xr.v[0][i];
+            }
             a_off[p] += a_step;
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
             load4<TB, true>(B, b_off[p], true, 4, xb[p]);
+            if constexpr (R1 == 2)
+                xr.w[p] = rank1_w(g.r1, k_full + (tid + p * 256) / (BN / 4), n0 + ((tid + p * 256) % (BN / 4)) * 4, 4);
             b_off[p] += b_step;
         }
+        k_full += BK;
     };
-    auto store_full = [&](int buf, const float (&xa)[A_LOADS][4], const float (&xb)[B_LOADS][4]) {
+    auto store_full = [&](int buf, const float (&xa)[A_LOADS][4], const float (&xb)[B_LOADS][4],
+                          const Rank1Regs<R1N>& xr) {
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
             const int q = tid + p * 256;
+            float t[4] = {xa[p][0], xa[p][1], xa[p][2], xa[p][3]};
+            if constexpr (R1 == 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[i] = fmaf(xr.w[p], xr.v[p][i], t[i]);
+            }
             if constexpr (A_KC) {
                 *reinterpret_cast<float4*>(&As[buf][kc_row(q) * (BK + PAD) + kc_k(q)]) =
-                    make_float4(xa[p][0], xa[p][1], xa[p][2], xa[p][3]);
+                    make_float4(t[0], t[1], t[2], t[3]);
             } else {
                 *reinterpret_cast<float4*>(&As[buf][(q / (BM / 4)) * (BM + PADM) + (q % (BM / 4)) * 4]) =
-                    make_float4(xa[p][0], xa[p][1], xa[p][2], xa[p][3]);
+                    make_float4(t[0], t[1], t[2], t[3]);
             }
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
             const int q = tid + p * 256;
+            float t[4] = {xb[p][0], xb[p][1], xb[p][2], xb[p][3]};
+            if constexpr (R1 == 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[i] = fmaf(xr.w[p], vb_r1[i], t[i]);
+            }
             if constexpr (B_KC) {
                 *reinterpret_cast<float4*>(&Bs[buf][kc_row(q) * (BK + PAD) + kc_k(q)]) =
-                    make_float4(xb[p][0], xb[p][1], xb[p][2], xb[p][3]);
+                    make_float4(t[0], t[1], t[2], t[3]);
             } else {
                 *reinterpret_cast<float4*>(&Bs[buf][(q / (BN / 4)) * (BN + PADM) + (q % (BN / 4)) * 4]) =
-                    make_float4(xb[p][0], xb[p][1], xb[p][2], xb[p][3]);
+                    make_float4(t[0], t[1], t[2], t[3]);
             }
         }
     };
@@ -352,36 +444,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         // two slabs per trip, each register set with a fixed role) lets the
         // compiler wait for exactly the older slab's loads; the scheduling
         // barriers keep the loads ahead of the MFMAs they overlap.
-        load_full(ra, rb);
-        store_full(0, ra, rb);
-        load_full(ra1, rb1);
+        load_full(ra, rb, rr);
+        store_full(0, ra, rb, rr);
+        load_full(ra1, rb1, rr1);
         __syncthreads();
         int64_t s = 0;
         // here LDS buffer 0 holds slab s and (ra1, rb1) slab s + 1
         for (; s + 3 < nslab; s += 2) {
-            load_full(ra, rb);  // slab s + 2
+            load_full(ra, rb, rr);  // slab s + 2
             __builtin_amdgcn_sched_barrier(0);
             compute(0);
-            store_full(1, ra1, rb1);
+            store_full(1, ra1, rb1, rr1);
             __syncthreads();
-            load_full(ra1, rb1);  // slab s + 3
+            load_full(ra1, rb1, rr1);  // slab s + 3
             __builtin_amdgcn_sched_barrier(0);
             compute(1);
-            store_full(0, ra, rb);
+            store_full(0, ra, rb, rr);
             __syncthreads();
         }
         if (s + 3 == nslab) {  // three slabs left
-            load_full(ra, rb);
+            load_full(ra, rb, rr);
             compute(0);
-            store_full(1, ra1, rb1);
+            store_full(1, ra1, rb1, rr1);
             __syncthreads();
             compute(1);
-            store_full(0, ra, rb);
+            store_full(0, ra, rb, rr);
             __syncthreads();
             compute(0);
         } else {  // two slabs left
             compute(0);
-            store_full(1, ra1, rb1);
+            store_full(1, ra1, rb1, rr1);
             __syncthreads();
             compute(1);
         }
@@ -528,7 +620,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
-template <int BM, int BN, int WM, int WN, bool TA_, bool TB_, typename TA, typename TB, typename TC>
+template <int BM, int BN, int WM, int WN, bool TA_, bool TB_, typename TA, typename TB, typename TC, int R1 = 0>
 void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
     const int64_t grid = 8 * g.per_xcd;
     // Two slabs of loads in flight for the transposed-A products (weight
@@ -540,31 +632,31 @@ void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
     // 1.30 ms).
     if constexpr ((TA_ || std::is_same<TA, bf16_t>::value) && BN == 128) {
         if (va && vb && (g.splits > 1 ? g.kper : g.K) >= 256) {
-            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, true, TA, TB, TC>), dim3(grid),
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, true, TA, TB, TC, R1>), dim3(grid),
                                dim3(256), 0, st, g);
             return;
         }
     }
     if (va && vb)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, false, TA, TB, TC>), dim3(grid),
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, false, TA, TB, TC, R1>), dim3(grid),
                            dim3(256), 0, st, g);
     else if (va)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, false, false, TA, TB, TC>), dim3(grid), dim3(256), 0,
-                           st, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, false, false, TA, TB, TC, R1>), dim3(grid),
+                           dim3(256), 0, st, g);
     else if (vb)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, true, false, TA, TB, TC>), dim3(grid), dim3(256), 0,
-                           st, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, true, false, TA, TB, TC, R1>), dim3(grid),
+                           dim3(256), 0, st, g);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, false, false, TA, TB, TC>), dim3(grid), dim3(256),
-                           0, st, g);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, false, false, TA, TB, TC, R1>), dim3(grid),
+                           dim3(256), 0, st, g);
 }
 
-template <bool TA_, bool TB_, typename TA, typename TB, typename TC>
+template <bool TA_, bool TB_, typename TA, typename TB, typename TC, int R1 = 0>
 void launch_types(GemmArgs& g, const Plan& p, bool va, bool vb, hipStream_t st) {
     if (p.bn == 64)
-        launch_shape<128, 64, 4, 1, TA_, TB_, TA, TB, TC>(g, va, vb, st);
+        launch_shape<128, 64, 4, 1, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
     else
-        launch_shape<128, 128, 2, 2, TA_, TB_, TA, TB, TC>(g, va, vb, st);
+        launch_shape<128, 128, 2, 2, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
     if (g.splits > 1) {
         const int64_t tot = g.M * g.N;
         hipLaunchKernelGGL((splitk_reduce<TC>), dim3((tot + 63) / 64), dim3(256), 0, st, g.ws, g.splits, g.M, g.N,
@@ -574,7 +666,20 @@ void launch_types(GemmArgs& g, const Plan& p, bool va, bool vb, hipStream_t st) 
 
 template <bool TA_, bool TB_>
 gnn_status_t launch_trans(GemmArgs& g, const Plan& p, gnn_dtype_t a, gnn_dtype_t b, gnn_dtype_t c, bool va, bool vb,
-                          hipStream_t st) {
+                          int r1, hipStream_t st) {
+    // binary32 products with a rank-1 operand term (the host checks the types)
+    if constexpr (!TA_ && !TB_) {
+        if (r1 == 1) {
+            launch_types<TA_, TB_, float, float, float, 1>(g, p, va, vb, st);
+            return launch_status("gnn_gemm");
+        }
+    }
+    if constexpr (!TB_) {
+        if (r1 == 2) {
+            launch_types<TA_, TB_, float, float, float, 2>(g, p, va, vb, st);
+            return launch_status("gnn_gemm");
+        }
+    }
 #define GNN_GEMM_CASE(TAt, TBt, TCt)                                                     \
     launch_types<TA_, TB_, TAt, TBt, TCt>(g, p, va, vb, st);                             \
     return launch_status("gnn_gemm");
@@ -615,8 +720,26 @@ size_t gemm_ws_bytes(int transA, int transB, int64_t M, int64_t N, int64_t K) {
 gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
                          int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb, void* C, gnn_dtype_t c_dt,
                          int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu,
-                         const MaskEpilogue& mask) {
+                         const MaskEpilogue& mask, const OperandRank1& ra1, const OperandRank1& rb1) {
     if (M == 0 || N == 0) return GNN_OK;
+    auto r1_ok = [](const OperandRank1& o) {
+        return o.s && o.v && o.ld >= 1 && o.dh >= 4 && reinterpret_cast<uintptr_t>(o.v) % 16 == 0;
+    };
+    if ((ra1.s && (ra1.dh & (ra1.dh - 1))) || (rb1.s && (rb1.dh & (rb1.dh - 1))))
+        return fail(GNN_ERR_UNSUPPORTED, "gnn_gemm: a rank-1 operand term needs a power-of-two head width");
+    if ((ra1.s && rb1.s) || (ra1.s && (transA || a_dt != GNN_F32 || !r1_ok(ra1))) ||
+        (rb1.s && (transB || b_dt != GNN_F32 || !r1_ok(rb1))) ||
+        ((ra1.s || rb1.s) && (a_dt != GNN_F32 || b_dt != GNN_F32 || c_dt != GNN_F32)))
+        return fail(GNN_ERR_UNSUPPORTED, "gnn_gemm: a rank-1 operand term needs binary32 operands, an "
+                                         "untransposed operand, a head width that is a multiple of 4 and a "
+                                         "16-byte aligned vector");
+    const int r1 = ra1.s ? 1 : rb1.s ? 2 : 0;
+    {  // every column's head must have a coefficient: (cols - 1) / dh < ld
+        const OperandRank1& o = r1 == 1 ? ra1 : rb1;
+        const int64_t cols = r1 == 1 ? K : N;
+        if (r1 && cols > 0 && (cols - 1) / o.dh >= o.ld)
+            return fail(GNN_ERR_UNSUPPORTED, "gnn_gemm: a rank-1 operand term needs a coefficient for every head");
+    }
     Plan p = make_plan(M, N, K);
     if (ws_bytes < gemm_ws_bytes(transA, transB, M, N, K))
         return fail(GNN_ERR_WORKSPACE, "gnn_gemm: workspace smaller than gnn_gemm_workspace_size()");
@@ -640,6 +763,9 @@ gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K
     g.ws = static_cast<float*>(ws);
     g.relu = relu;
     g.mask = mask;
+    g.r1 = r1 == 1 ? ra1 : rb1;
+    g.r1.dh_log2 = 0;
+    while ((int64_t(1) << g.r1.dh_log2) < g.r1.dh) ++g.r1.dh_log2;
     g.kper = p.kper;
     g.splits = p.splits;
     g.tiles_m = (M + p.bm - 1) / p.bm;
@@ -686,13 +812,13 @@ gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K
         return launch_status("gnn_gemm (split-K reduction)");
     }
     // timed: the product and, when split over K, its fixed-order reduction
-    ScopedTimer t(st, "gemm M=%lld N=%lld K=%lld ta=%d tb=%d %s,%s->%s", static_cast<long long>(M),
+    ScopedTimer t(st, "gemm M=%lld N=%lld K=%lld ta=%d tb=%d %s,%s->%s%s", static_cast<long long>(M),
                   static_cast<long long>(N), static_cast<long long>(K), transA, transB, dt_name(a_dt), dt_name(b_dt),
-                  dt_name(c_dt));
-    if (!transA && !transB) return launch_trans<false, false>(g, p, a_dt, b_dt, c_dt, va, vb, st);
-    if (!transA && transB) return launch_trans<false, true>(g, p, a_dt, b_dt, c_dt, va, vb, st);
-    if (transA && !transB) return launch_trans<true, false>(g, p, a_dt, b_dt, c_dt, va, vb, st);
-    return launch_trans<true, true>(g, p, a_dt, b_dt, c_dt, va, vb, st);
+                  dt_name(c_dt), r1 == 1 ? " +rank1 A" : r1 == 2 ? " +rank1 B" : "");
+    if (!transA && !transB) return launch_trans<false, false>(g, p, a_dt, b_dt, c_dt, va, vb, r1, st);
+    if (!transA && transB) return launch_trans<false, true>(g, p, a_dt, b_dt, c_dt, va, vb, r1, st);
+    if (transA && !transB) return launch_trans<true, false>(g, p, a_dt, b_dt, c_dt, va, vb, r1, st);
+    return launch_trans<true, true>(g, p, a_dt, b_dt, c_dt, va, vb, r1, st);
 }
 
 }  // namespace gnnmp

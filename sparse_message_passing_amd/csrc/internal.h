@@ -118,6 +118,19 @@ struct MaskEpilogue {     // out[r, f] *= [M[r, f] > 0]  (the ReLU derivative of
     gnn_dtype_t dt = GNN_F32;
 };
 
+// A binary32 operand read as X[r][c] + s[r, c / dh] * v[c] (one fmaf per
+// element), r and c the row and column of the operand as stored: the GAT
+// backward's dD a_dst term, applied where the two products that consume dH'
+// load it instead of in a pass of its own.  dh a power of two >= 4, v
+// 16-byte aligned.
+struct OperandRank1 {
+    const float* s = nullptr;  // [rows][ld]
+    int64_t ld = 0;
+    int64_t dh = 4;
+    const float* v = nullptr;  // [cols]
+    int dh_log2 = 2;           // set by the product from dh
+};
+
 struct QuantSources {      // dequantise-in-gather: source rows with qslot[u] >= 0 come from quantised groups
     const int32_t* qslot = nullptr;
     const gnn_qgroup_t* groups = nullptr;  // host array of n_groups descriptors
@@ -164,13 +177,13 @@ gnn_status_t launch_sddmm_dot(const AggView& v, const void* src_feat, int64_t ld
                               int64_t ld_dst, gnn_dtype_t dt, int heads, int64_t d_head, float* out, hipStream_t st);
 gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha, int heads, hipStream_t st);
 // GAT backward edge pass: records, the fused out-edge pass (dalpha, dE, dS, transposed aggregation + dS a_src),
-// hub fixups, and the in-edge sum dD with dD a_dst added to dH'
+// hub fixups, and the in-edge sum dD (the dD a_dst term of dH' is left to the products that read dH')
 bool gat_fused_bwd_supported(int heads, int64_t d_head);
 size_t gat_fused_bwd_partial_bytes(const RowPlan& csc_plan, int heads, int64_t d_head);
 gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const int32_t* cpos, int64_t nnz,
                                   int heads, int64_t d_head, float slope, const float* Hp, const float* S,
                                   const float* D, const float* M, const float* Z, const float* Y, const float* dY,
-                                  const float* a_src, const float* a_dst, float4* rec, float* dEh, float* dEc,
+                                  const float* a_src, float4* rec, float* dEh, float* dEc,
                                   float* part, float* dS, float* dD, float* dHp, hipStream_t st);
 // GAT forward edge pass (gat_fwd.hip): per destination and head, the scores from the gathered H' rows,
 // LeakyReLU, the softmax folded into the weighted aggregation (running maximum); writes Y and each
@@ -197,7 +210,8 @@ gnn_status_t launch_gemm_tn_bf16(int64_t M, int64_t N, int64_t K, const uint16_t
 gnn_status_t launch_gemm(int transA, int transB, int64_t M, int64_t N, int64_t K, const void* A, gnn_dtype_t a_dt,
                          int64_t lda, const void* B, gnn_dtype_t b_dt, int64_t ldb, void* C, gnn_dtype_t c_dt,
                          int64_t ldc, void* ws, size_t ws_bytes, hipStream_t st, int relu = 0,
-                         const MaskEpilogue& mask = MaskEpilogue{});
+                         const MaskEpilogue& mask = MaskEpilogue{}, const OperandRank1& ra1 = OperandRank1{},
+                         const OperandRank1& rb1 = OperandRank1{});
 
 size_t xent_ws_bytes(int64_t n);
 gnn_status_t launch_softmax_xent(const float* logits, int64_t n, int64_t c, int64_t ld, const int32_t* labels,

@@ -337,16 +337,24 @@ gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     size_t gemm = std::max(gemm_ws_bytes(0, 0, g.n, hd, d_in), gemm_ws_bytes(1, 0, d_in, hd, g.n));
     gemm = std::max(gemm, gemm_ws_bytes(0, 1, g.n, d_in, hd));
     void* gws = c.take(gemm);
-    // dalpha, dE, dS and (G . alpha)^T dY + dS a_src in one pass over the
-    // out-edges; dD and its dD a_dst term in one pass over the in-edges
+    // dalpha, dE, dS and P = (G . alpha)^T dY + dS a_src in one pass over the
+    // out-edges; dD in one pass over the in-edges
     GNN_TRY(launch_gat_bwd_fused(csr_view(g), csc_view(g), g.csr_cpos, g.nnz, heads, d_head, slope, s.Hp, s.S, s.D,
-                                 s.M, s.Z, Y, dY, a_src, a_dst, rec, dEh, dEc, part, dS, dD, dHp, st));
+                                 s.M, s.Z, Y, dY, a_src, rec, dEh, dEc, part, dS, dD, dHp, st));
     // da_src = sum_v dS[v] H'[v], da_dst = sum_v dD[v] H'[v] per head
     GNN_TRY(launch_head_colsum(g.n, dS, dD, s.Hp, heads, d_head, da_src, da_dst, cps, st));
-    // dW = X^T dH',  dX = dH' W^T
-    GNN_TRY(launch_gemm(1, 0, d_in, hd, g.n, X, GNN_F32, d_in, dHp, GNN_F32, hd, dW, GNN_F32, hd, gws, gemm, st));
+    // dW = X^T dH',  dX = dH' W^T, with dH' = P + dD a_dst (per head) formed
+    // element by element as the products load it
+    OperandRank1 r1;
+    r1.s = dD;
+    r1.ld = heads;
+    r1.dh = d_head;
+    r1.v = a_dst;
+    GNN_TRY(launch_gemm(1, 0, d_in, hd, g.n, X, GNN_F32, d_in, dHp, GNN_F32, hd, dW, GNN_F32, hd, gws, gemm, st, 0,
+                        MaskEpilogue{}, OperandRank1{}, r1));
     if (dX)
-        GNN_TRY(launch_gemm(0, 1, g.n, d_in, hd, dHp, GNN_F32, hd, W, GNN_F32, hd, dX, GNN_F32, d_in, gws, gemm, st));
+        GNN_TRY(launch_gemm(0, 1, g.n, d_in, hd, dHp, GNN_F32, hd, W, GNN_F32, hd, dX, GNN_F32, d_in, gws, gemm, st,
+                            0, MaskEpilogue{}, r1));
     return GNN_OK;
 }
 
