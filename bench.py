@@ -400,6 +400,10 @@ def cpu_oracle_kernels(k, og, inp, edges=1_000_000):
         jobs.append(("sddmm_dot_gedge_feat_s", lambda: oracle.sddmm_dot(sub, A, B, 4), sub.nnz * 256,
                      f"{sub.n} nodes, {sub.nnz} edges, 4 heads x 64"))
         jobs.append(("edge_softmax_gedge_s", lambda: oracle.edge_softmax(sub, E), sub.nnz, f"{sub.nnz} edges, 4 heads"))
+        Hq = np.random.default_rng(81).standard_normal((60_000, 256)).astype(np.float32)
+        rq = np.arange(60_000, dtype=np.int32)
+        jobs.append(("quantize_8bit_rows_per_s", lambda: oracle.quantize(Hq, rq, 8, 1), rq.size,
+                     f"{rq.size} rows x 256 at 8 bits"))
     if cfg["kind"] == "quant":
         H = inp["H"]
         rows = inp["rows"].astype(np.int32)
@@ -588,6 +592,20 @@ def main():
             lambda: gnnmp.gnn_edge_softmax(g, E, dal), a.kernel_reps, stream), 4)
         sm_bytes = kernel_model(f"softmax_fwd_kernel h={h}", g.n, g.nnz, ctx)[1]
         extra["edge_softmax_GBs"] = round(sm_bytes / (extra["edge_softmax_ms"] * 1e-3) / 1e9, 1)
+        # the 8-bit stochastic quantiser (the exchange's message compression)
+        # on every third row of the layer's H'
+        qrows = torch.arange(0, g.n, 3, dtype=torch.int32, device=dev)
+        m, dq = qrows.numel(), h * dh
+        qp = torch.empty(m * dq, dtype=torch.uint8, device=dev)
+        qs, qz = torch.empty(m, device=dev), torch.empty(m, device=dev)
+        extra["quantize_8bit_ms"] = round(event_time(
+            lambda: gnnmp.gnn_quantize(Hp, qrows, 8, 5, qp, qs, qz), a.kernel_reps, stream), 4)
+        q_bytes = 4 * m * dq + m * dq + 8 * m + 4 * m
+        extra["quantize_8bit_rows"] = m
+        extra["quantize_8bit_GBs"] = round(q_bytes / (extra["quantize_8bit_ms"] * 1e-3) / 1e9, 1)
+        extra["quantize_8bit_frac"] = round(q_bytes / (extra["quantize_8bit_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        extra["sddmm_dot_f32_frac"] = round(extra["sddmm_dot_f32_GBs"] / HBM_PEAK_GBS, 4)
+        extra["edge_softmax_frac"] = round(extra["edge_softmax_GBs"] / HBM_PEAK_GBS, 4)
     if cfg["kind"] == "quant":
         # the same exchange with the dequantisation inside the gather, and the
         # backward exchange of the embedding gradients (also fused)
