@@ -11,7 +11,8 @@
 // (node, f/4, stream, 0), key (seed low, seed high), word f%4, top 24 bits
 // times 2^-24.  Stateless, so a rerun draws the same numbers.
 //
-// One wave per row.  Lane l owns feature quads 4l, 4l+256, ...; one Philox
+// One wave per row.  Lane l owns feature quads l, l + 64, ... (features
+// 4l..4l+3, 4l+256.., read as 16-byte vectors when the rows allow); one Philox
 // call yields exactly the four uniforms of a quad, and a quad's codes fill
 // b/2 whole bytes (2-bit: 1 byte, 4-bit: 2, 8-bit: 4), so each lane writes
 // its own bytes with one store and the row is written contiguously.
@@ -38,8 +39,12 @@ __device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c
                                             uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        // one 32 x 32 -> 64-bit product per multiplier (a single
+        // v_mad_u64_u32, where separate low and high halves take two
+        // multiplies)
+        const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0, p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+        const uint32_t lo0 = static_cast<uint32_t>(p0), hi0 = static_cast<uint32_t>(p0 >> 32);
+        const uint32_t lo1 = static_cast<uint32_t>(p1), hi1 = static_cast<uint32_t>(p1 >> 32);
         const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
         c0 = n0, c1 = lo1, c2 = n2, c3 = lo0;
         k0 += 0x9E3779B9u;
@@ -55,83 +60,121 @@ __device__ __forceinline__ float max_z(float a, float b) { return (b > a || (b =
 
 __device__ __forceinline__ float u24(uint32_t w) { return static_cast<float>(w >> 8) * (1.0f / 16777216.0f); }
 
+// NQ = feature quads per lane (d <= 256 NQ); RW rows per wave (two for rows
+// of at most 256 features, so two rows' loads are in flight at once).  The
+// rows' loads are issued first and the lane's Philox blocks computed while
+// they are in flight (the uniforms do not depend on the data); a flat row
+// ignores them.
+template <int NQ, int RW>
 __global__ __launch_bounds__(256) void quantize_kernel(const float* H, int64_t ldh, int64_t d, const int32_t* rows,
                                                        int64_t n_rows, int bits, uint32_t k0, uint32_t k1,
                                                        uint32_t stream_id, uint8_t* packed, float* scale,
-                                                       float* zero) {
+                                                       float* zero, int vec) {
     const int lane = threadIdx.x & 63;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (r >= n_rows) return;
-    const uint32_t node = static_cast<uint32_t>(rows[r]);
-    const float* h = H + static_cast<int64_t>(node) * ldh;
+    const int64_t r0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RW;
+    if (r0 >= n_rows) return;
     const int64_t nq = (d + 3) / 4;
-    float x[kMaxQuads][4];
-    float mn = INFINITY, mx = -INFINITY;
+    uint32_t node[RW];
+    float x[RW][NQ][4];
 #pragma unroll
-    for (int i = 0; i < kMaxQuads; ++i) {
-        const int64_t q = lane + 64 * i;
+    for (int k = 0; k < RW; ++k) {
+        const bool on = r0 + k < n_rows;
+        node[k] = on ? static_cast<uint32_t>(rows[r0 + k]) : 0u;
+        const float* h = H + static_cast<int64_t>(node[k]) * ldh;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t f = 4 * q + j;
-            x[i][j] = (q < nq && f < d) ? h[f] : 0.0f;
-            if (q < nq && f < d) {
-                mn = min_z(mn, x[i][j]);
-                mx = max_z(mx, x[i][j]);
+        for (int i = 0; i < NQ; ++i) {
+            const int64_t q = lane + 64 * i;
+            if (on && vec && 4 * q + 4 <= d) {
+                const float4 t = *reinterpret_cast<const float4*>(h + 4 * q);
+                x[k][i][0] = t.x, x[k][i][1] = t.y, x[k][i][2] = t.z, x[k][i][3] = t.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[k][i][j] = (on && q < nq && 4 * q + j < d) ? h[4 * q + j] : 0.0f;
+            }
+        }
+    }
+    U4 rnd[RW][NQ];
+#pragma unroll
+    for (int k = 0; k < RW; ++k)
+#pragma unroll
+        for (int i = 0; i < NQ; ++i)
+            rnd[k][i] = philox4x32_10(node[k], static_cast<uint32_t>(lane + 64 * i), stream_id, 0u, k0, k1);
+    float mn[RW], mx[RW];
+#pragma unroll
+    for (int k = 0; k < RW; ++k) {
+        mn[k] = INFINITY, mx[k] = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int64_t q = lane + 64 * i;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (q < nq && 4 * q + j < d) {
+                    mn[k] = min_z(mn[k], x[k][i][j]);
+                    mx[k] = max_z(mx[k], x[k][i][j]);
+                }
             }
         }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        mn = min_z(mn, __shfl_xor(mn, o, 64));
-        mx = max_z(mx, __shfl_xor(mx, o, 64));
+#pragma unroll
+        for (int k = 0; k < RW; ++k) {
+            mn[k] = min_z(mn[k], __shfl_xor(mn[k], o, 64));
+            mx[k] = max_z(mx[k], __shfl_xor(mx[k], o, 64));
+        }
     }
-    const float R = __fsub_rn(mx, mn);
     const uint32_t top = (1u << bits) - 1u;
     const float levels = static_cast<float>(top);
-    const bool flat = !(R != 0.0f);
-    const float inv = flat ? 0.0f : __fdiv_rn(levels, R);
-    if (lane == 0) {
-        zero[r] = mn;
-        scale[r] = flat ? 0.0f : __fdiv_rn(R, levels);
-    }
     const int64_t row_bytes = d * bits / 8;
-    uint8_t* out = packed + r * row_bytes;
     const bool wide = (row_bytes % 4 == 0) && (reinterpret_cast<uintptr_t>(packed) % 4 == 0);
 #pragma unroll
-    for (int i = 0; i < kMaxQuads; ++i) {
-        const int64_t q = lane + 64 * i;
-        if (q >= nq) break;
-        uint32_t code[4] = {0u, 0u, 0u, 0u};
-        if (!flat) {
-            const U4 rnd = philox4x32_10(node, static_cast<uint32_t>(q), stream_id, 0u, k0, k1);
-            const uint32_t w[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float t = __fsub_rn(x[i][j], mn);
-                const float xs = __fmul_rn(t, inv);
-                const float fl = floorf(xs);
-                const float frac = __fsub_rn(xs, fl);
-                uint32_t c = static_cast<uint32_t>(fl) + (u24(w[j]) < frac ? 1u : 0u);
-                code[j] = c > top ? top : c;
-            }
+    for (int k = 0; k < RW; ++k) {
+        const int64_t r = r0 + k;
+        if (r >= n_rows) break;
+        const float R = __fsub_rn(mx[k], mn[k]);
+        const bool flat = !(R != 0.0f);
+        const float inv = flat ? 0.0f : __fdiv_rn(levels, R);
+        if (lane == 0) {
+            zero[r] = mn[k];
+            scale[r] = flat ? 0.0f : __fdiv_rn(R, levels);
         }
-        const int64_t nvalid = min<int64_t>(4, d - 4 * q);
-        if (bits == 8) {
-            if (nvalid == 4 && wide) {
-                *reinterpret_cast<uint32_t*>(out + 4 * q) = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-            } else {
-                for (int j = 0; j < nvalid; ++j) out[4 * q + j] = static_cast<uint8_t>(code[j]);
+        uint8_t* out = packed + r * row_bytes;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int64_t q = lane + 64 * i;
+            if (q >= nq) break;
+            uint32_t code[4] = {0u, 0u, 0u, 0u};
+            if (!flat) {
+                const uint32_t w[4] = {rnd[k][i].x, rnd[k][i].y, rnd[k][i].z, rnd[k][i].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float t = __fsub_rn(x[k][i][j], mn[k]);
+                    const float xs = __fmul_rn(t, inv);
+                    const float fl = floorf(xs);
+                    const float frac = __fsub_rn(xs, fl);
+                    uint32_t c = static_cast<uint32_t>(fl) + (u24(w[j]) < frac ? 1u : 0u);
+                    code[j] = c > top ? top : c;
+                }
             }
-        } else if (bits == 4) {
-            const uint32_t lo = code[0] | (code[1] << 4), hi = code[2] | (code[3] << 4);
-            if (nvalid == 4 && wide) {
-                *reinterpret_cast<uint16_t*>(out + 2 * q) = static_cast<uint16_t>(lo | (hi << 8));
+            const int64_t nvalid = min<int64_t>(4, d - 4 * q);
+            if (bits == 8) {
+                if (nvalid == 4 && wide) {
+                    *reinterpret_cast<uint32_t*>(out + 4 * q) =
+                        code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+                } else {
+                    for (int j = 0; j < nvalid; ++j) out[4 * q + j] = static_cast<uint8_t>(code[j]);
+                }
+            } else if (bits == 4) {
+                const uint32_t lo = code[0] | (code[1] << 4), hi = code[2] | (code[3] << 4);
+                if (nvalid == 4 && wide) {
+                    *reinterpret_cast<uint16_t*>(out + 2 * q) = static_cast<uint16_t>(lo | (hi << 8));
+                } else {
+                    out[2 * q] = static_cast<uint8_t>(lo);  // d even: a partial quad holds 2 features
+                    if (nvalid == 4) out[2 * q + 1] = static_cast<uint8_t>(hi);
+                }
             } else {
-                out[2 * q] = static_cast<uint8_t>(lo);  // d even: a partial quad holds 2 features
-                if (nvalid == 4) out[2 * q + 1] = static_cast<uint8_t>(hi);
+                out[q] = static_cast<uint8_t>(code[0] | (code[1] << 2) | (code[2] << 4) | (code[3] << 6));
             }
-        } else {
-            out[q] = static_cast<uint8_t>(code[0] | (code[1] << 2) | (code[2] << 4) | (code[3] << 6));
         }
     }
 }
@@ -327,9 +370,20 @@ gnn_status_t launch_quantize(const float* H, int64_t ldh, int64_t d, const int32
     if (n_rows == 0) return GNN_OK;
     if (d > 64 * 4 * kMaxQuads) return fail(GNN_ERR_UNSUPPORTED, "gnn_quantize: d must be at most 1024");
     const int64_t blocks = (n_rows + 3) / 4;
+    const int vec = ldh % 4 == 0 && reinterpret_cast<uintptr_t>(H) % 16 == 0;
+    const int nq4 = static_cast<int>(((d + 3) / 4 + 63) / 64);  // quads per lane
     ScopedTimer t(st, "quantize_kernel b=%d d=%lld", bits, static_cast<long long>(d));
-    hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(256), 0, st, H, ldh, d, rows, n_rows, bits,
-                       static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), stream_id, packed, scale, zero);
+#define GNN_Q(NQv, RWv, BLK)                                                                                         \
+    hipLaunchKernelGGL((quantize_kernel<NQv, RWv>), dim3(BLK), dim3(256), 0, st, H, ldh, d, rows, n_rows, bits,    \
+                       static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), stream_id, packed, scale, zero, \
+                       vec)
+    switch (nq4) {
+        case 1: GNN_Q(1, 2, (n_rows + 7) / 8); break;
+        case 2: GNN_Q(2, 1, blocks); break;
+        case 3: GNN_Q(3, 1, blocks); break;
+        default: GNN_Q(4, 1, blocks); break;
+    }
+#undef GNN_Q
     return launch_status("gnn_quantize");
 }
 
