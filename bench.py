@@ -10,7 +10,7 @@ aggregation, and the backward (SDDMM dot, softmax backward, edge sums, the
 transposed aggregation, dW, dX) for a seeded upstream gradient, with every
 input resident in HBM.
 
-Printed value: GEdge*feat/s = (edge x feature products of the step's
+Printed value: GEdge·feat/s = (edge x feature products of the step's
 aggregation-shaped passes) / step time; for the GAT layer the weighted
 aggregation, the SDDMM dot and the transposed aggregation (3 nnz h d_head).
 Beside it:
@@ -287,7 +287,7 @@ def cpu_baseline_gcn_full(og, inp, work_per_pass, min_seconds=10.0, max_passes=3
         oracle.gcn_forward_backward(og, inp["X"], Ws, inp["labels"])
         dt += time.perf_counter() - t0
         passes += 1
-    return dict(value=round(passes * work_per_pass / dt / 1e9, 4), unit="GEdge*feat/s", cores=oracle_threads(),
+    return dict(value=round(passes * work_per_pass / dt / 1e9, 4), unit="GEdge·feat/s", cores=oracle_threads(),
                 kind="oracle", sample=f"{passes} full 3-layer forward+backward pass(es) of the same workload "
                                       f"({og.n} nodes, nnz {og.nnz}), {dt:.2f} s")
 
@@ -369,7 +369,7 @@ def cpu_baseline_sampled(k, og, inp, work, edges):
     t_edge = spent["edge"]
     t_node = total - t_edge
     est = t_edge * og.nnz / sg.nnz + t_node * og.n / sg.n
-    return dict(value=round(work / est / 1e9, 4), unit="GEdge*feat/s", cores=oracle_threads(), kind="oracle",
+    return dict(value=round(work / est / 1e9, 4), unit="GEdge·feat/s", cores=oracle_threads(), kind="oracle",
                 sample=f"the oracle's whole step on {sg.n} of {og.n} nodes and {sg.nnz} of {og.nnz} edges "
                        f"(the in-edges of destinations {int(og.n * 0.7071)}.. with their sources, relabelled): "
                        f"{t_edge:.2f} s in per-edge calls scaled by {og.nnz / sg.nnz:.1f}, {t_node:.2f} s in "
@@ -651,9 +651,9 @@ def main():
         extra["cpu_oracle"] = cpu_oracle_kernels(a.config, og, oinp)
         print("# CPU oracle timed", file=sys.stderr, flush=True)
     out = {
-        "metric": "GNN layer fwd+bwd GEdge*feat/s; SpMM/SDDMM HBM GB/s as % of peak",
+        "metric": "GNN layer fwd+bwd GEdge·feat/s; SpMM/SDDMM HBM GB/s as % of peak",
         "value": round(value, 3),
-        "unit": "GEdge*feat/s",
+        "unit": "GEdge·feat/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
