@@ -56,19 +56,21 @@ gnn_status_t upload(Graph& g, const std::vector<T>& h, T** out) {
     return GNN_OK;
 }
 
-gnn_status_t make_plan(Graph& g, const std::vector<int64_t>& ptr, RowPlan& p, std::vector<int32_t>* order_out) {
+gnn_status_t make_plan(Graph& g, const std::vector<int64_t>& ptr, RowPlan& p, std::vector<int32_t>* order_out,
+                       int64_t chunk) {
     std::vector<int32_t> order;
     degree_order(ptr, order);
     const int64_t n = static_cast<int64_t>(order.size());
     auto deg = [&](int64_t v) { return ptr[v + 1] - ptr[v]; };
     p.max_degree = n ? deg(order[0]) : 0;
+    p.chunk = chunk;
     p.n_heavy = 0;
-    while (p.n_heavy < n && deg(order[p.n_heavy]) > kChunk) ++p.n_heavy;
+    while (p.n_heavy < n && deg(order[p.n_heavy]) > chunk) ++p.n_heavy;
     p.n_block = 0;
     while (p.n_block < n && deg(order[p.n_block]) > kBlockRow) ++p.n_block;
     std::vector<int32_t> chunk_first(p.n_heavy + 1, 0), chunk_row;
     for (int64_t i = 0; i < p.n_heavy; ++i) {
-        const int64_t c = (deg(order[i]) + kChunk - 1) / kChunk;
+        const int64_t c = (deg(order[i]) + chunk - 1) / chunk;
         chunk_first[i + 1] = chunk_first[i] + static_cast<int32_t>(c);
         for (int64_t j = 0; j < c; ++j) chunk_row.push_back(static_cast<int32_t>(i));
     }
@@ -81,7 +83,8 @@ gnn_status_t make_plan(Graph& g, const std::vector<int64_t>& ptr, RowPlan& p, st
 }
 
 // Offsets of the degree buckets in the degree-ordered row list: rows of
-// degree > kBlockRow, then > kChunk, then the rest: {0, n_block, n_heavy, n}.
+// degree > kBlockRow, then > the view's chunk length, then the rest:
+// {0, n_block, n_heavy, n}.
 void bucket_offsets(const RowPlan& p, int64_t n, int64_t* off) {
     off[0] = 0;
     off[1] = p.n_block;
@@ -162,7 +165,7 @@ gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const in
                     dm[v] = 1.0f / static_cast<float>(hg.row_ptr[v + 1] - hg.row_ptr[v]);
                 s = upload(g, dm, &g.dmean);
             }
-            if (s == GNN_OK) s = make_plan(g, hg.row_ptr, g.plan[0], nullptr);
+            if (s == GNN_OK) s = make_plan(g, hg.row_ptr, g.plan[0], nullptr, kChunkCsr);
             if (s == GNN_OK && g.has_csc) {
                 s = upload(g, hg.col_ptr, &g.col_ptr);
                 if (s == GNN_OK) s = upload(g, hg.csc_row, &g.csc_row);
@@ -172,7 +175,7 @@ gnn_status_t gnn_graph_create(int64_t n, int64_t m, const int32_t* src, const in
                     for (size_t j = 0; j < cpos.size(); ++j) cpos[hg.csc_eid[j]] = static_cast<int32_t>(j);
                     s = upload(g, cpos, &g.csr_cpos);
                 }
-                if (s == GNN_OK) s = make_plan(g, hg.col_ptr, g.plan[1], nullptr);
+                if (s == GNN_OK) s = make_plan(g, hg.col_ptr, g.plan[1], nullptr, kChunkCsc);
             }
         }
     } catch (const std::bad_alloc&) {
@@ -238,7 +241,7 @@ gnn_status_t gnn_graph_split(gnn_graph_t h, const uint8_t* marginal, gnn_graph_t
             if (s == GNN_OK) s = upload(pg, dinv, &pg.dinv);
             if (s == GNN_OK) s = upload(pg, pw, &pg.wgcn);
             if (s == GNN_OK) s = upload(pg, dmean, &pg.dmean);
-            if (s == GNN_OK) s = make_plan(pg, prp, pg.plan[0], nullptr);
+            if (s == GNN_OK) s = make_plan(pg, prp, pg.plan[0], nullptr, kChunkCsr);
         }
     } catch (const std::bad_alloc&) {
         s = fail(GNN_ERR_OUT_OF_MEMORY, "gnn_graph_split: host allocation failed");
@@ -283,7 +286,9 @@ gnn_status_t gnn_graph_info(gnn_graph_t h, gnn_graph_info_t* out) {
     out->perm_t = g.plan[1].order;
     out->symmetric = g.symmetric;
     out->bucket_threshold[0] = kBlockRow;
-    out->bucket_threshold[1] = kChunk;
+    out->bucket_threshold[1] = g.plan[0].chunk;
+    out->bucket_threshold_t[0] = g.has_csc ? kBlockRow : 0;
+    out->bucket_threshold_t[1] = g.has_csc ? g.plan[1].chunk : 0;
     bucket_offsets(g.plan[0], g.n, out->bucket_off);
     if (g.has_csc) bucket_offsets(g.plan[1], g.n, out->bucket_off_t);
     return GNN_OK;

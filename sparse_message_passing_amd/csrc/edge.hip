@@ -76,7 +76,7 @@ struct Sched {
     const int32_t* idx;
     const int32_t* eid;
     const int32_t* order;
-    int64_t n_heavy, n_chunks, n_block;
+    int64_t n_heavy, n_chunks, n_block, chunk;
     const int32_t* chunk_row;
     const int32_t* chunk_first;
 };
@@ -91,6 +91,7 @@ Sched make_sched(const AggView& v) {
     s.n_heavy = v.plan->n_heavy;
     s.n_chunks = v.plan->n_chunks;
     s.n_block = v.plan->n_block;
+    s.chunk = v.plan->chunk;
     s.chunk_row = v.plan->chunk_row;
     s.chunk_first = v.plan->chunk_first;
     return s;
@@ -100,8 +101,8 @@ __device__ __forceinline__ bool work_item(const Sched& s, int64_t gid, int64_t& 
     if (gid < s.n_chunks) {
         const int oi = s.chunk_row[gid];
         row = s.order[oi];
-        eb = s.ptr[row] + (gid - s.chunk_first[oi]) * kChunk;
-        ee = min(eb + kChunk, s.ptr[row + 1]);
+        eb = s.ptr[row] + (gid - s.chunk_first[oi]) * s.chunk;
+        ee = min(eb + s.chunk, s.ptr[row + 1]);
         return true;
     }
     const int64_t li = gid - s.n_chunks + s.n_heavy;

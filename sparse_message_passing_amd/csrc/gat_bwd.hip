@@ -70,7 +70,7 @@ struct GatBwdArgs {
     const int64_t* ptr;          // CSC: out-edges of each source
     const int32_t* idx;          // destination of each CSC entry
     const int32_t* order;        // sources by out-degree, descending
-    int64_t n_heavy, n_chunks;
+    int64_t n_heavy, n_chunks, chunk;
     const int32_t* chunk_row;
     const int32_t* chunk_first;
     int heads;
@@ -108,8 +108,8 @@ __global__ __launch_bounds__(256) void gat_bwd_csc_kernel(GatBwdArgs a) {
     if (gid < a.n_chunks) {
         const int oi = a.chunk_row[gid];
         u = a.order[oi];
-        eb = a.ptr[u] + (gid - a.chunk_first[oi]) * kChunk;
-        ee = min(eb + kChunk, a.ptr[u + 1]);
+        eb = a.ptr[u] + (gid - a.chunk_first[oi]) * a.chunk;
+        ee = min(eb + a.chunk, a.ptr[u + 1]);
         heavy = true;
     } else {
         const int64_t li = gid - a.n_chunks + a.n_heavy;
@@ -374,6 +374,7 @@ gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const 
     a.order = p.order;
     a.n_heavy = p.n_heavy;
     a.n_chunks = p.n_chunks;
+    a.chunk = p.chunk;
     a.chunk_row = p.chunk_row;
     a.chunk_first = p.chunk_first;
     a.heads = heads;

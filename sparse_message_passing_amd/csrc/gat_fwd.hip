@@ -19,7 +19,7 @@
 // Work decomposition: one head per column slab (slab-major over the grid, so
 // a slab's gathered rows share the caches), a group of L = d_head / 4 lanes
 // per destination row (lane i holds features 4i..4i+3 of the head), rows in
-// degree-descending order, rows over kChunk in-edges cut into chunks whose
+// degree-descending order, rows over 256 in-edges cut into chunks whose
 // partial (maximum, sum, weighted row) are merged afterwards in chunk order.
 // No atomics: bitwise reproducible.
 
@@ -35,7 +35,7 @@ struct GatFwdArgs {
     const int64_t* ptr;          // CSR: in-edges of each destination
     const int32_t* idx;          // source of each CSR entry
     const int32_t* order;        // destinations by in-degree, descending
-    int64_t n_heavy, n_chunks;
+    int64_t n_heavy, n_chunks, chunk;
     const int32_t* chunk_row;
     const int32_t* chunk_first;
     int heads;
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void gat_fwd_kernel(GatFwdArgs a) {
     if (gid < a.n_chunks) {
         const int oi = a.chunk_row[gid];
         v = a.order[oi];
-        eb = a.ptr[v] + (gid - a.chunk_first[oi]) * kChunk;
-        ee = min(eb + kChunk, a.ptr[v + 1]);
+        eb = a.ptr[v] + (gid - a.chunk_first[oi]) * a.chunk;
+        ee = min(eb + a.chunk, a.ptr[v + 1]);
         heavy = true;
     } else {
         const int64_t li = gid - a.n_chunks + a.n_heavy;
@@ -197,6 +197,7 @@ gnn_status_t launch_gat_fwd_fused(const AggView& csr, int heads, int64_t d_head,
     a.order = p.order;
     a.n_heavy = p.n_heavy;
     a.n_chunks = p.n_chunks;
+    a.chunk = p.chunk;
     a.chunk_row = p.chunk_row;
     a.chunk_first = p.chunk_first;
     a.heads = heads;

@@ -42,16 +42,32 @@ gnn_status_t launch_status(const char* what);  // checks hipGetLastError after l
 // ---------------------------------------------------------------------------
 // graph
 // ---------------------------------------------------------------------------
-// Rows whose degree exceeds kChunk are cut into chunks of kChunk edges for the
-// aggregation kernels; each chunk is an independent work item and the chunks
-// of one row are summed afterwards in a fixed order.
-constexpr int64_t kChunk = 256;
+// Rows whose degree exceeds the view's chunk length are cut into chunks of
+// that many edges for the aggregation kernels; each chunk is an independent
+// work item and the chunks of one row are summed afterwards in a fixed order.
+// Measured on the 2^21-node directed R-MAT graph (4 heads x 64): the
+// in-edge passes are fastest with 256-edge chunks (the forward GAT pass 6.84
+// ms, 7.01 with 1024; the 2^20-node GCN aggregation 2.39 ms, 2.61 with
+// 1024), the out-edge pass of the GAT backward with 2048 (256: 9.36 ms,
+// 512: 8.96, 1024: 8.75, 2048: 8.54, 4096: 8.88, 16384: 11.2); a hub row
+// kept whole in one group is a straggler (73,549 in-edges: 25-27 ms per
+// pass).
+#ifndef GNN_CHUNK_CSR
+#define GNN_CHUNK_CSR 256
+#endif
+#ifndef GNN_CHUNK_CSC
+#define GNN_CHUNK_CSC 2048
+#endif
+constexpr int64_t kChunkCsr = GNN_CHUNK_CSR;  // CSR view (in-edges of each destination)
+constexpr int64_t kChunkCsc = GNN_CHUNK_CSC;  // CSC view (out-edges of each source)
 // Rows above this degree get a whole workgroup in the per-row edge kernels.
 constexpr int64_t kBlockRow = 2048;
+static_assert(kChunkCsr <= kBlockRow && kChunkCsc <= kBlockRow, "the degree buckets nest");
 
 struct RowPlan {               // one per view (CSR by destination, CSC by source)
     int32_t* order = nullptr;      // [n] rows by degree desc, ties by id
-    int64_t n_heavy = 0;           // rows with degree > kChunk: order[0 .. n_heavy)
+    int64_t chunk = kChunkCsr;     // chunk length of this view's heavy rows
+    int64_t n_heavy = 0;           // rows with degree > chunk: order[0 .. n_heavy)
     int64_t n_block = 0;           // rows with degree > kBlockRow: order[0 .. n_block)
     int64_t n_chunks = 0;          // chunks of the heavy rows
     int32_t* chunk_row = nullptr;  // [n_chunks] index into order of the chunk's row

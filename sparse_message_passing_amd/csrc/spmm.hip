@@ -21,7 +21,8 @@
 //    gathers of that slab run; only the edge indices and weights are read
 //    once per slab;
 //  * rows are visited in degree-descending order (the graph's `order`), and a
-//    row longer than kChunk edges is cut into kChunk-edge chunks that are
+//    row longer than the view's chunk length (256 in-edges, 2048 out-edges)
+//    is cut into chunks of that many edges that are
 //    independent work items writing binary32 partial rows; a second kernel
 //    adds each row's partials in chunk order.  No atomics: bitwise
 //    reproducible.
@@ -75,7 +76,7 @@ struct SpmmArgs {
     const int32_t* idx;
     const int32_t* eid;
     const int32_t* order;
-    int64_t n_heavy, n_chunks;
+    int64_t n_heavy, n_chunks, chunk;
     const int32_t* chunk_row;
     const int32_t* chunk_first;
     const float* dinv;
@@ -169,8 +170,8 @@ __global__ __launch_bounds__(256) void spmm_kernel(SpmmArgs a) {
         const int oi = a.chunk_row[gid];
         row = a.order[oi];
         const int64_t c = gid - a.chunk_first[oi];
-        eb = a.ptr[row] + c * kChunk;
-        ee = min(eb + kChunk, a.ptr[row + 1]);
+        eb = a.ptr[row] + c * a.chunk;
+        ee = min(eb + a.chunk, a.ptr[row + 1]);
         heavy = true;
     } else {
         const int64_t li = gid - a.n_chunks + a.n_heavy;
@@ -528,6 +529,7 @@ gnn_status_t launch_spmm(const AggView& v, const float* dinv, gnn_weights_t wmod
     a.order = v.plan->order;
     a.n_heavy = v.plan->n_heavy;
     a.n_chunks = v.plan->n_chunks;
+    a.chunk = v.plan->chunk;
     a.chunk_row = v.plan->chunk_row;
     a.chunk_first = v.plan->chunk_first;
     a.dinv = dinv;

@@ -90,7 +90,8 @@ class _Info(C.Structure):
                 ("has_csc", C.c_int), ("row_ptr", C.c_void_p), ("col", C.c_void_p), ("dinv", C.c_void_p),
                 ("perm", C.c_void_p), ("col_ptr", C.c_void_p), ("csc_row", C.c_void_p), ("csc_eid", C.c_void_p),
                 ("perm_t", C.c_void_p), ("symmetric", C.c_int), ("bucket_threshold", C.c_int64 * 2),
-                ("bucket_off", C.c_int64 * 4), ("bucket_off_t", C.c_int64 * 4)]
+                ("bucket_off", C.c_int64 * 4), ("bucket_off_t", C.c_int64 * 4),
+                ("bucket_threshold_t", C.c_int64 * 2)]
 
 
 _lib = None
@@ -184,6 +185,7 @@ class Graph:
         self.bucket_threshold = list(info.bucket_threshold)
         self.bucket_off = list(info.bucket_off)
         self.bucket_off_t = list(info.bucket_off_t)
+        self.bucket_threshold_t = list(info.bucket_threshold_t)
 
     def __del__(self):
         if getattr(self, "h", None) and _lib is not None:

@@ -285,7 +285,7 @@ def test_c3_graph_bit_exact(c3):
     outdeg = np.diff(colptr)
     assert np.array_equal(ex["perm_t"], np.lexsort((np.arange(og.n), -outdeg)).astype(np.int32))
     assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 256]))
-    assert np.array_equal(ex["bucket_off_t"], og.bucket_offsets([2048, 256], by_out=True))
+    assert np.array_equal(ex["bucket_off_t"], og.bucket_offsets([2048, 2048], by_out=True))
 
 
 @pytest.fixture(scope="module")
