@@ -123,13 +123,13 @@ typedef struct {
      * (out-degree; all zero without CSC): bucket i holds positions
      * [bucket_off[i], bucket_off[i+1]) -- degree > bucket_threshold[0], then
      * degree > bucket_threshold[1], then the rest -- so bucket_off =
-     * {0, #rows with degree > 2048, #rows with degree > 256, n}; likewise
+     * {0, #rows with degree > 2048, #rows with degree > 512, n}; likewise
      * bucket_off_t with bucket_threshold_t = {2048, 2048}.  The aggregation
      * kernels give rows of the first bucket a whole workgroup in the per-row
      * edge kernels and cut rows of the first two into chunks of
      * bucket_threshold[1] (in-edges) or bucket_threshold_t[1] (out-edges)
      * edges; the thresholds are tuning choices of this library. */
-    int64_t bucket_threshold[2];   /* {2048, 256} */
+    int64_t bucket_threshold[2];   /* {2048, 512} */
     int64_t bucket_off[4];
     int64_t bucket_off_t[4];
     int64_t bucket_threshold_t[2]; /* {2048, 2048}; zero without CSC */

@@ -19,7 +19,7 @@
 // Work decomposition: one head per column slab (slab-major over the grid, so
 // a slab's gathered rows share the caches), a group of L = d_head / 4 lanes
 // per destination row (lane i holds features 4i..4i+3 of the head), rows in
-// degree-descending order, rows over 256 in-edges cut into chunks whose
+// degree-descending order, rows over 512 in-edges cut into chunks whose
 // partial (maximum, sum, weighted row) are merged afterwards in chunk order.
 // No atomics: bitwise reproducible.
 

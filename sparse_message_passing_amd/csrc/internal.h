@@ -45,15 +45,16 @@ gnn_status_t launch_status(const char* what);  // checks hipGetLastError after l
 // Rows whose degree exceeds the view's chunk length are cut into chunks of
 // that many edges for the aggregation kernels; each chunk is an independent
 // work item and the chunks of one row are summed afterwards in a fixed order.
-// Measured on the 2^21-node directed R-MAT graph (4 heads x 64): the
-// in-edge passes are fastest with 256-edge chunks (the forward GAT pass 6.84
-// ms, 7.01 with 1024; the 2^20-node GCN aggregation 2.39 ms, 2.61 with
-// 1024), the out-edge pass of the GAT backward with 2048 (256: 9.36 ms,
-// 512: 8.96, 1024: 8.75, 2048: 8.54, 4096: 8.88, 16384: 11.2); a hub row
-// kept whole in one group is a straggler (73,549 in-edges: 25-27 ms per
-// pass).
+// Measured: in-edge views with 512-edge chunks (the forward GAT pass on the
+// 2^21-node directed R-MAT graph, 4 heads x 64: 128: 7.26 ms, 256: 6.80,
+// 512: 6.49, 1024: 7.01; the 256-wide aggregation of the quantised
+// exchange 3.40 -> 3.31 ms from 256 to 512, the 2.45M-node bf16 one
+// unchanged, the 2^20-node GCN one 2.40 -> 2.43 ms), out-edge views with
+// 2048 (the GAT backward's out-edge pass, 256: 9.36 ms, 512: 8.96, 1024:
+// 8.75, 2048: 8.54, 4096: 8.88, 16384: 11.2); a hub row kept whole in one
+// group is a straggler (73,549 in-edges: 25-27 ms per pass).
 #ifndef GNN_CHUNK_CSR
-#define GNN_CHUNK_CSR 256
+#define GNN_CHUNK_CSR 512
 #endif
 #ifndef GNN_CHUNK_CSC
 #define GNN_CHUNK_CSC 2048

@@ -21,7 +21,7 @@
 //    gathers of that slab run; only the edge indices and weights are read
 //    once per slab;
 //  * rows are visited in degree-descending order (the graph's `order`), and a
-//    row longer than the view's chunk length (256 in-edges, 2048 out-edges)
+//    row longer than the view's chunk length (512 in-edges, 2048 out-edges)
 //    is cut into chunks of that many edges that are
 //    independent work items writing binary32 partial rows; a second kernel
 //    adds each row's partials in chunk order.  No atomics: bitwise

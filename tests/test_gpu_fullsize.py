@@ -49,7 +49,7 @@ def test_c2_graph_bit_exact(c2):
     assert np.array_equal(ex["dinv"].view(np.uint32), dinv.view(np.uint32))
     assert np.array_equal(ex["w"].view(np.uint32), w.view(np.uint32))
     assert np.array_equal(ex["perm"], og.degree_perm())
-    assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 256]))
+    assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 512]))
 
 
 def test_c2_gcn_step_chain(c2):
@@ -284,7 +284,7 @@ def test_c3_graph_bit_exact(c3):
     assert np.array_equal(ex["perm"], og.degree_perm())
     outdeg = np.diff(colptr)
     assert np.array_equal(ex["perm_t"], np.lexsort((np.arange(og.n), -outdeg)).astype(np.int32))
-    assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 256]))
+    assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 512]))
     assert np.array_equal(ex["bucket_off_t"], og.bucket_offsets([2048, 2048], by_out=True))
 
 
@@ -621,7 +621,7 @@ def test_c4_graph_bit_exact(c4):
     ex = gnnmp.gnn_graph_export(g)
     assert np.array_equal(ex["row_ptr"], og.row_ptr) and np.array_equal(ex["col"], og.col)
     assert np.array_equal(ex["dinv"].view(np.uint32), og.gcn_norm()[0].view(np.uint32))
-    assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 256]))
+    assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 512]))
 
 
 def test_c4_bf16_first_layer_and_aggregation_sampled(c4):

@@ -55,8 +55,8 @@ def test_graph_build_bit_exact(case):
     assert np.array_equal(ex["perm_t"], np.lexsort((ids, -od)).astype(np.int32))
     assert g.max_in_degree == (og.deg.max() if n else 0)
     # degree buckets of both orders, from the export and from gnn_graph_info
-    assert g.bucket_threshold == [2048, 256] and g.bucket_threshold_t == [2048, 2048]
-    assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 256]))
+    assert g.bucket_threshold == [2048, 512] and g.bucket_threshold_t == [2048, 2048]
+    assert np.array_equal(ex["bucket_off"], og.bucket_offsets([2048, 512]))
     assert np.array_equal(ex["bucket_off_t"], og.bucket_offsets([2048, 2048], by_out=True))
     assert g.bucket_off == ex["bucket_off"].tolist() and g.bucket_off_t == ex["bucket_off_t"].tolist()
     assert g.symmetric == sym

@@ -46,9 +46,9 @@ def test_noalloc_matches_workspace_path_on_consecutive_calls():
 
 
 def test_noalloc_refuses_partials_beyond_its_scratch():
-    # 80 hubs of 60,000 in-edges: 18,800 chunks x 1024 features x 4 bytes
-    # (77 MB) do not fit the 64 MiB scratch
-    n, hubs, deg = 70000, 80, 60000
+    # 160 hubs of 60,000 in-edges: 18,880 chunks of 512 edges x 1024
+    # features x 4 bytes (77 MB) do not fit the 64 MiB scratch
+    n, hubs, deg = 70000, 160, 60000
     r = np.random.default_rng(53)
     src = np.concatenate([r.choice(np.arange(hubs, n), deg, replace=False) for _ in range(hubs)]).astype(np.int32)
     dst = np.repeat(np.arange(hubs, dtype=np.int32), deg)
