@@ -273,6 +273,34 @@ __device__ __forceinline__ void hv_block_reduce(HV<H>& a, float (*sh)[H]) {
     }
 }
 
+// Running maximum m and sum z of exp(x - m) of one value per head: a value
+// above the maximum rescales the sum by exp(m_old - x) (an empty sum stays 0,
+// so the first value gives z = 1); a -inf while the maximum is still -inf
+// adds nothing (as exp(x - m) does once a finite maximum exists).
+template <int H>
+__device__ __forceinline__ void online_add(HV<H>& m, HV<H>& z, const HV<H>& x) {
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+        if (x.v[k] > m.v[k]) {
+            z.v[k] = fmaf(z.v[k], __expf(m.v[k] - x.v[k]), 1.0f);
+            m.v[k] = x.v[k];
+        } else if (m.v[k] != -INFINITY) {
+            z.v[k] += __expf(x.v[k] - m.v[k]);
+        }
+    }
+}
+
+// the G lanes' (m, z) merged: the row maximum, and each lane's sum brought to
+// it before the group sum
+template <int H>
+__device__ __forceinline__ void group_merge(HV<H>& m, HV<H>& z) {
+    HV<H> mt = m;
+    hv_group_max<H, G>(m);
+#pragma unroll
+    for (int k = 0; k < H; ++k) z.v[k] = mt.v[k] == -INFINITY ? 0.0f : z.v[k] * __expf(mt.v[k] - m.v[k]);
+    hv_group_sum<H, G>(z);
+}
+
 template <int H>
 __device__ __forceinline__ void softmax_fwd_rows(const Sched& s, const float* E, float* alpha, int64_t blk) {
     const int lane = threadIdx.x % G;
@@ -318,20 +346,17 @@ __device__ __forceinline__ void softmax_fwd_rows(const Sched& s, const float* E,
         }
         return;
     }
-    for (int64_t e = eb + lane; e < ee; e += G) {
-        HV<H> x = ld<H>(E + e * H);
-#pragma unroll
-        for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x.v[k]);
-    }
-    hv_group_max<H, G>(m);
+    // long row: the maximum and the sum of exponentials in one pass (each
+    // lane keeps a running maximum and rescales its sum when it grows; the
+    // lanes' sums are brought to the row maximum before they are added), then
+    // one pass that writes alpha: E is read twice instead of three times
     HV<H> z;
     hv_fill<H>(z, 0.0f);
     for (int64_t e = eb + lane; e < ee; e += G) {
         HV<H> x = ld<H>(E + e * H);
-#pragma unroll
-        for (int k = 0; k < H; ++k) z.v[k] += __expf(x.v[k] - m.v[k]);
+        online_add<H>(m, z, x);
     }
-    hv_group_sum<H, G>(z);
+    group_merge<H>(m, z);
 #pragma unroll
     for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];
     for (int64_t e = eb + lane; e < ee; e += G) {
@@ -346,21 +371,20 @@ template <int H>
 __device__ __forceinline__ void softmax_fwd_block(const Sched& s, const float* E, float* alpha, int64_t blk, float (*sh)[H]) {
     const int64_t v = s.order[blk];
     const int64_t eb = s.ptr[v], ee = s.ptr[v + 1];
+    // the maximum and the sum of exponentials in one pass (as for long rows
+    // above), then the pass that writes alpha
     HV<H> m;
     hv_fill<H>(m, -INFINITY);
-    for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
-        HV<H> x = ld<H>(E + e * H);
-#pragma unroll
-        for (int k = 0; k < H; ++k) m.v[k] = fmaxf(m.v[k], x.v[k]);
-    }
-    hv_block_reduce<H, true>(m, sh);
     HV<H> z;
     hv_fill<H>(z, 0.0f);
     for (int64_t e = eb + threadIdx.x; e < ee; e += 256) {
         HV<H> x = ld<H>(E + e * H);
-#pragma unroll
-        for (int k = 0; k < H; ++k) z.v[k] += __expf(x.v[k] - m.v[k]);
+        online_add<H>(m, z, x);
     }
+    HV<H> mt = m;
+    hv_block_reduce<H, true>(m, sh);
+#pragma unroll
+    for (int k = 0; k < H; ++k) z.v[k] = mt.v[k] == -INFINITY ? 0.0f : z.v[k] * __expf(mt.v[k] - m.v[k]);
     hv_block_reduce<H, false>(z, sh);
 #pragma unroll
     for (int k = 0; k < H; ++k) z.v[k] = 1.0f / z.v[k];

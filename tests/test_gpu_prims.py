@@ -343,6 +343,35 @@ def test_edge_softmax(dirg, heads):
     assert torch.equal(Ed, a)
 
 
+@pytest.mark.parametrize("heads", [1, 4])
+def test_edge_softmax_long_rows_and_masked_scores(heads):
+    # rows of every length class: short (kept in registers), 65..2048 edges
+    # (one pass for the maximum and sum, one for alpha), over 2048 (a whole
+    # workgroup); about 10% of the scores are -inf (alpha exactly 0), and one
+    # long row starts with -inf in every lane before its finite scores
+    r = np.random.default_rng(60 + heads)
+    n = 6000
+    src = [r.integers(0, n, 40000).astype(np.int32)]
+    dst = [r.integers(0, n, 40000).astype(np.int32)]
+    for hub, deg in ((1, 100), (2, 700), (3, 2100), (4, 5000)):
+        src.append(r.choice(np.setdiff1d(np.arange(n), [hub]), deg, replace=False).astype(np.int32))
+        dst.append(np.full(deg, hub, np.int32))
+    g, og = graph_pair(np.concatenate(src), np.concatenate(dst), n, False, csc=False)
+    E = (3 * r.standard_normal((og.nnz, heads))).astype(np.float32)
+    mask = r.random((og.nnz, heads)) < 0.1
+    mask[og.row_ptr[:-1]] = False  # every row keeps a finite score
+    E[mask] = -np.inf
+    lo, hi = og.row_ptr[2], og.row_ptr[3]  # the 700-edge row: its first 40 scores -inf
+    E[lo:lo + 40] = -np.inf
+    ref = oracle.edge_softmax(og, E)
+    assert np.isfinite(ref).all() and hi - lo > 64
+    a = torch.empty((og.nnz, heads), device="cuda")
+    gnnmp.gnn_edge_softmax(g, to_dev(E), a)
+    got = from_dev(a)
+    check_close(got, ref, np.abs(ref), what="edge-softmax, long rows and -inf scores")
+    assert np.all(got[np.isneginf(E)] == 0.0)
+
+
 @pytest.mark.parametrize("with_pre", [False, True])
 def test_edge_softmax_bwd(dirg, with_pre):
     g, og = dirg
