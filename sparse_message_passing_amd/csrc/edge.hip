@@ -538,34 +538,43 @@ __global__ __launch_bounds__(256) void reduce_kernel(Sched s, const float* vals,
 // ---------------------------------------------------------------------------
 // GAT scores: S[v,k] = <H'[v, head k], a_src[k]>, D likewise (one wave per row)
 // ---------------------------------------------------------------------------
+// Two rows per wave (both rows' loads in flight before either is reduced).
 template <int HL>
 __global__ __launch_bounds__(256) void gat_scores_kernel(int64_t n, const float* Hp, int64_t d, int heads,
                                                          const float* a_src, const float* a_dst, float* S, float* D) {
     const int lane = threadIdx.x & 63;
-    const int64_t v = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (v >= n) return;
+    const int64_t v0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 2;
+    if (v0 >= n) return;
     for (int64_t f0 = 0; f0 < d; f0 += 256) {
         const int64_t f = f0 + lane * 4;
-        float ps = 0.0f, pd = 0.0f;
+        float4 x[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            x[j] = (f < d && v0 + j < n) ? *reinterpret_cast<const float4*>(Hp + (v0 + j) * d + f)
+                                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float4 as = make_float4(0.0f, 0.0f, 0.0f, 0.0f), ad = as;
         if (f < d) {
-            const float4 x = *reinterpret_cast<const float4*>(Hp + v * d + f);
-            const float4 as = *reinterpret_cast<const float4*>(a_src + f);
-            const float4 ad = *reinterpret_cast<const float4*>(a_dst + f);
-            ps = x.x * as.x;
-            ps = fmaf(x.y, as.y, ps);
-            ps = fmaf(x.z, as.z, ps);
-            ps = fmaf(x.w, as.w, ps);
-            pd = x.x * ad.x;
-            pd = fmaf(x.y, ad.y, pd);
-            pd = fmaf(x.z, ad.z, pd);
-            pd = fmaf(x.w, ad.w, pd);
+            as = *reinterpret_cast<const float4*>(a_src + f);
+            ad = *reinterpret_cast<const float4*>(a_dst + f);
         }
-        ps = group_sum<HL>(ps);
-        pd = group_sum<HL>(pd);
-        if (f < d && (lane % HL) == 0) {
-            const int64_t k = f / (HL * 4);
-            S[v * heads + k] = ps;
-            D[v * heads + k] = pd;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float ps = x[j].x * as.x;
+            ps = fmaf(x[j].y, as.y, ps);
+            ps = fmaf(x[j].z, as.z, ps);
+            ps = fmaf(x[j].w, as.w, ps);
+            float pd = x[j].x * ad.x;
+            pd = fmaf(x[j].y, ad.y, pd);
+            pd = fmaf(x[j].z, ad.z, pd);
+            pd = fmaf(x[j].w, ad.w, pd);
+            ps = group_sum<HL>(ps);
+            pd = group_sum<HL>(pd);
+            const int64_t v = v0 + j;
+            if (f < d && v < n && (lane % HL) == 0) {
+                const int64_t k = f / (HL * 4);
+                S[v * heads + k] = ps;
+                D[v * heads + k] = pd;
+            }
         }
     }
 }
@@ -791,7 +800,7 @@ gnn_status_t launch_gat_scores(int64_t n, const float* Hp, int heads, int64_t d_
     const int64_t hl = d_head / 4;
     if (d_head % 4 || (hl & (hl - 1)) || hl > 64 || (d > 256 && 256 % d_head))
         return fail(GNN_ERR_UNSUPPORTED, "GAT scores: d_head must be 4 * a power of two, at most 256");
-    const int64_t blocks = (n + 3) / 4;
+    const int64_t blocks = (n + 7) / 8;  // four waves of two rows
 #define GNN_SC(HLv) \
     hipLaunchKernelGGL((gat_scores_kernel<HLv>), dim3(blocks), dim3(256), 0, st, n, Hp, d, heads, a_src, a_dst, S, D)
     switch (hl) {
