@@ -4,9 +4,10 @@
 // "H' = H(l-1) W") and its backward dW = H^T dZ, dH = dZ W^T.
 //
 // Design (gfx950, wave64, v_mfma_f32_16x16x4_f32):
-//  * a 256-thread workgroup computes a BM x BN tile of C; its four waves
-//    split the tile WM x WN ways and each wave owns (BM/WM) x (BN/WN) as a
-//    grid of 16x16 MFMA blocks held in accumulation registers;
+//  * a workgroup of WM x WN waves computes a BM x BN tile of C (four waves;
+//    eight for the deep f32 NN products, below); each wave owns
+//    (BM/WM) x (BN/WN) as a grid of 16x16 MFMA blocks held in accumulation
+//    registers;
 //  * K advances in slabs of 16 through double-buffered LDS; each operand
 //    keeps its global contiguity in LDS (k-contiguous rows, or k-major
 //    planes), so every global->LDS store is a 16-byte write; the next slab's
@@ -17,7 +18,12 @@
 //    tiles keep two slabs of loads in flight (registers for slab s + 1 and
 //    s + 2), so a load has two slabs of MFMAs to arrive instead of one; it
 //    holds more registers (two waves per SIMD instead of three), which loses
-//    on the f32 NN updates;
+//    on the f32 NN updates with four waves;
+//  * the f32 NN products with K >= 256 (the GAT layer's H' = XW and dX =
+//    dH' W^T, the GCN's 256-deep updates) split the 128 x 128 tile over
+//    eight waves of 64 x 32 instead, which fits the two-slab pipeline in
+//    four waves per SIMD; shallower products keep four waves (a 128-deep
+//    update lost with eight: 0.75 -> 0.86 ms);
 //  * operand fragments: in MFMA j of a slab, lane l supplies
 //    B[k0 + 4(l/16) + j][n0 + l%16] as the instruction's first operand and
 //    A[m0 + l%16][k0 + 4(l/16) + j] as its second, so a k-contiguous
@@ -148,11 +154,12 @@ __device__ __forceinline__ float rank1_w(const OperandRank1& o, int64_t r, int64
 // R1: 0, or the operand (1: A, 2: B) that carries the rank-1 term g.r1.
 template <int BM, int BN, int WM, int WN, bool TRANS_A, bool TRANS_B, bool VA, bool VB, bool PF, typename TA,
           typename TB, typename TC, int R1 = 0>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
+    constexpr int NT = WM * WN * 64;  // threads
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
-    constexpr int A_LOADS = BM * BK / 4 / 256;  // float4-sized pieces per thread
-    constexpr int B_LOADS = BN * BK / 4 / 256;
+    constexpr int A_LOADS = BM * BK / 4 / NT;  // float4-sized pieces per thread
+    constexpr int B_LOADS = BN * BK / 4 / NT;
     static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
     static_assert(R1 == 0 || (R1 == 1 && !TRANS_A) || (R1 == 2 && !TRANS_B), "rank-1 term on an untransposed operand");
     constexpr int R1N = R1 == 1 ? A_LOADS : R1 == 2 ? B_LOADS : 1;
@@ -211,13 +218,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     int64_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
     for (int p = 0; p < A_LOADS; ++p) {
-        const int q = tid + p * 256;
+        const int q = tid + p * NT;
         if constexpr (!TRANS_A) a_off[p] = (m0 + kc_row(q)) * g.lda + kbeg + kc_k(q);
         else a_off[p] = (kbeg + q / (BM / 4)) * g.lda + m0 + (q % (BM / 4)) * 4;
     }
 #pragma unroll
     for (int p = 0; p < B_LOADS; ++p) {
-        const int q = tid + p * 256;
+        const int q = tid + p * NT;
         if constexpr (!TRANS_B) b_off[p] = (kbeg + q / (BN / 4)) * g.ldb + n0 + (q % (BN / 4)) * 4;
         else b_off[p] = (n0 + kc_row(q)) * g.ldb + kbeg + kc_k(q);
     }
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         const bool full_k = k0 + BK <= kend;
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
-            const int q = tid + p * 256;
+            const int q = tid + p * NT;
             if (a_full && full_k) {
                 load4<TA, true>(A, a_off[p], true, 4, ra[p]);
                 if constexpr (R1 == 1) {  // the pieces of a thread share their columns k0 + kc_k(tid)
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
-            const int q = tid + p * 256;
+            const int q = tid + p * NT;
             if (b_full && full_k) {
                 load4<TB, true>(B, b_off[p], true, 4, rb[p]);
                 if constexpr (R1 == 2) rr.w[p] = rank1_w(g.r1, k0 + q / (BN / 4), n0 + (q % (BN / 4)) * 4, 4);
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
-            const int q = tid + p * 256;
+            const int q = tid + p * NT;
             if constexpr (A_KC) {
                 const int mm = kc_row(q), kk = kc_k(q);
                 *reinterpret_cast<float4*>(&As[buf][mm * (BK + PAD) + kk]) =
@@ -304,7 +311,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
-            const int q = tid + p * 256;
+            const int q = tid + p * NT;
             if constexpr (B_KC) {
                 const int nn = kc_row(q), kk = kc_k(q);
                 *reinterpret_cast<float4*>(&Bs[buf][nn * (BK + PAD) + kk]) =
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int p = 0; p < A_LOADS; ++p) {
             load4<TA, true>(A, a_off[p], true, 4, xa[p]);
             if constexpr (R1 == 1) {
-                xr.w[p] = rank1_w(g.r1, m0 + kc_row(tid + p * 256), k_full + kc_k(tid + p * 256), 4);
+                xr.w[p] = rank1_w(g.r1, m0 + kc_row(tid + p * NT), k_full + kc_k(tid + p * NT), 4);
                 if (p == 0) rank1_v(g.r1, k_full + kc_k(tid), 4, xr.v[0]);
                 else
 #pragma unroll
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int p = 0; p < B_LOADS; ++p) {
             load4<TB, true>(B, b_off[p], true, 4, xb[p]);
             if constexpr (R1 == 2)
-                xr.w[p] = rank1_w(g.r1, k_full + (tid + p * 256) / (BN / 4), n0 + ((tid + p * 256) % (BN / 4)) * 4, 4);
+                xr.w[p] = rank1_w(g.r1, k_full + (tid + p * NT) / (BN / 4), n0 + ((tid + p * NT) % (BN / 4)) * 4, 4);
             b_off[p] += b_step;
         }
         k_full += BK;
@@ -408,7 +415,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
                           const Rank1Regs<R1N>& xr) {
 #pragma unroll
         for (int p = 0; p < A_LOADS; ++p) {
-            const int q = tid + p * 256;
+            const int q = tid + p * NT;
             float t[4] = {xa[p][0], xa[p][1], xa[p][2], xa[p][3]};
             if constexpr (R1 == 1) {
 #pragma unroll
@@ -424,7 +431,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         }
 #pragma unroll
         for (int p = 0; p < B_LOADS; ++p) {
-            const int q = tid + p * 256;
+            const int q = tid + p * NT;
             float t[4] = {xb[p][0], xb[p][1], xb[p][2], xb[p][3]};
             if constexpr (R1 == 2) {
 #pragma unroll
@@ -629,34 +636,47 @@ void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
     // 0.95 ms, bf16 over 2.45M rows 2.31 -> 1.45 ms, bf16 x f32 update over
     // 2.45M rows 3.09 -> 2.92 ms; the same variant lost on 128 x 64 tiles
     // (0.43 -> 0.72 ms) and on the f32 NN updates in a whole step (1.25 ->
-    // 1.30 ms).
-    if constexpr ((TA_ || std::is_same<TA, bf16_t>::value) && BN == 128) {
-        if (va && vb && (g.splits > 1 ? g.kper : g.K) >= 256) {
-            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, true, TA, TB, TC, R1>), dim3(grid),
-                               dim3(256), 0, st, g);
-            return;
+    // 1.30 ms).  The eight-wave f32 NN tiles (chosen only for vectorisable
+    // operands and K >= 256) always take it.
+    if constexpr (WN == 4) {
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, true, TA, TB, TC, R1>), dim3(grid),
+                           dim3(WM * WN * 64), 0, st, g);
+    } else {
+        if constexpr ((TA_ || std::is_same<TA, bf16_t>::value) && BN == 128) {
+            if (va && vb && (g.splits > 1 ? g.kper : g.K) >= 256) {
+                hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, true, TA, TB, TC, R1>),
+                                   dim3(grid), dim3(WM * WN * 64), 0, st, g);
+                return;
+            }
         }
+        if (va && vb)
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, false, TA, TB, TC, R1>), dim3(grid),
+                               dim3(WM * WN * 64), 0, st, g);
+        else if (va)
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, false, false, TA, TB, TC, R1>),
+                               dim3(grid), dim3(WM * WN * 64), 0, st, g);
+        else if (vb)
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, true, false, TA, TB, TC, R1>),
+                               dim3(grid), dim3(WM * WN * 64), 0, st, g);
+        else
+            hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, false, false, TA, TB, TC, R1>),
+                               dim3(grid), dim3(WM * WN * 64), 0, st, g);
     }
-    if (va && vb)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, false, TA, TB, TC, R1>), dim3(grid),
-                           dim3(256), 0, st, g);
-    else if (va)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, false, false, TA, TB, TC, R1>), dim3(grid),
-                           dim3(256), 0, st, g);
-    else if (vb)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, true, false, TA, TB, TC, R1>), dim3(grid),
-                           dim3(256), 0, st, g);
-    else
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, false, false, false, TA, TB, TC, R1>), dim3(grid),
-                           dim3(256), 0, st, g);
 }
 
 template <bool TA_, bool TB_, typename TA, typename TB, typename TC, int R1 = 0>
 void launch_types(GemmArgs& g, const Plan& p, bool va, bool vb, hipStream_t st) {
-    if (p.bn == 64)
+    constexpr bool f32_nn = !TA_ && !TB_ && std::is_same<TA, float>::value && std::is_same<TB, float>::value;
+    if (p.bn == 64) {
         launch_shape<128, 64, 4, 1, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
-    else
-        launch_shape<128, 128, 2, 2, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
+    } else {
+        bool eight = false;
+        if constexpr (f32_nn) {
+            eight = g.splits == 1 && va && vb && g.K >= 256;
+            if (eight) launch_shape<128, 128, 2, 4, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
+        }
+        if (!eight) launch_shape<128, 128, 2, 2, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
+    }
     if (g.splits > 1) {
         const int64_t tot = g.M * g.N;
         hipLaunchKernelGGL((splitk_reduce<TC>), dim3((tot + 63) / 64), dim3(256), 0, st, g.ws, g.splits, g.M, g.N,

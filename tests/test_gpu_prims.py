@@ -235,6 +235,13 @@ GEMM_CASES = [
     (2048, 256, 272, False, False, "bf16", "f32", "bf16"),
     (2100, 256, 288, False, False, "bf16", "f32", "f32"),
     (1024, 128, 256, False, False, "bf16", "bf16", "f32"),
+    # f32 NN products with K >= 256 run the 128 x 128 tile over eight waves
+    # (two slabs ahead); odd and even slab counts, a K that ends inside a slab,
+    # ragged M and N, a bf16 output, and a transposed B made NN in the workspace
+    (2048, 256, 272, False, False, "f32", "f32", "f32"),
+    (2100, 200, 288, False, False, "f32", "f32", "f32"),
+    (1040, 130, 300, False, False, "f32", "f32", "bf16"),
+    (1000, 256, 300, False, True, "f32", "f32", "f32"),
 ]
 
 
