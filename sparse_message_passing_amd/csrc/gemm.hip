@@ -20,10 +20,12 @@
 //    holds more registers (two waves per SIMD instead of three), which loses
 //    on the f32 NN updates with four waves;
 //  * the f32 NN products with K >= 256 (the GAT layer's H' = XW and dX =
-//    dH' W^T, the GCN's 256-deep updates) split the 128 x 128 tile over
-//    eight waves of 64 x 32 instead, which fits the two-slab pipeline in
-//    four waves per SIMD; shallower products keep four waves (a 128-deep
-//    update lost with eight: 0.75 -> 0.86 ms);
+//    dH' W^T, the GCN's 256-deep updates) and the f32 weight gradients split
+//    the 128 x 128 tile over eight waves of 64 x 32 instead, which fits the
+//    two-slab pipeline in four waves per SIMD (2^21 x 256 x 256: 2.54 ->
+//    2.44-2.50 ms, with the rank-1 term 2.83 -> 2.66-2.70 ms; the 256 x 256
+//    weight gradient over 2^20 rows 1.12 -> 1.07 ms); shallower NN products
+//    keep four waves (a 128-deep update lost with eight: 0.75 -> 0.86 ms);
 //  * operand fragments: in MFMA j of a slab, lane l supplies
 //    B[k0 + 4(l/16) + j][n0 + l%16] as the instruction's first operand and
 //    A[m0 + l%16][k0 + 4(l/16) + j] as its second, so a k-contiguous
@@ -636,8 +638,8 @@ void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
     // 0.95 ms, bf16 over 2.45M rows 2.31 -> 1.45 ms, bf16 x f32 update over
     // 2.45M rows 3.09 -> 2.92 ms; the same variant lost on 128 x 64 tiles
     // (0.43 -> 0.72 ms) and on the f32 NN updates in a whole step (1.25 ->
-    // 1.30 ms).  The eight-wave f32 NN tiles (chosen only for vectorisable
-    // operands and K >= 256) always take it.
+    // 1.30 ms).  The eight-wave f32 tiles (chosen only for vectorisable
+    // operands and a K span of 256 or more) always take it.
     if constexpr (WN == 4) {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, TA_, TB_, true, true, true, TA, TB, TC, R1>), dim3(grid),
                            dim3(WM * WN * 64), 0, st, g);
@@ -666,13 +668,13 @@ void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
 
 template <bool TA_, bool TB_, typename TA, typename TB, typename TC, int R1 = 0>
 void launch_types(GemmArgs& g, const Plan& p, bool va, bool vb, hipStream_t st) {
-    constexpr bool f32_nn = !TA_ && !TB_ && std::is_same<TA, float>::value && std::is_same<TB, float>::value;
+    constexpr bool f32 = !TB_ && std::is_same<TA, float>::value && std::is_same<TB, float>::value;
     if (p.bn == 64) {
         launch_shape<128, 64, 4, 1, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
     } else {
         bool eight = false;
-        if constexpr (f32_nn) {
-            eight = g.splits == 1 && va && vb && g.K >= 256;
+        if constexpr (f32) {
+            eight = va && vb && (TA_ ? (g.splits > 1 ? g.kper : g.K) >= 256 : g.splits == 1 && g.K >= 256);
             if (eight) launch_shape<128, 128, 2, 4, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
         }
         if (!eight) launch_shape<128, 128, 2, 2, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
