@@ -668,7 +668,8 @@ void launch_shape(GemmArgs& g, bool va, bool vb, hipStream_t st) {
 
 template <bool TA_, bool TB_, typename TA, typename TB, typename TC, int R1 = 0>
 void launch_types(GemmArgs& g, const Plan& p, bool va, bool vb, hipStream_t st) {
-    constexpr bool f32 = !TB_ && std::is_same<TA, float>::value && std::is_same<TB, float>::value;
+    constexpr bool f32 = !TB_ && std::is_same<TB, float>::value &&
+                         (std::is_same<TA, float>::value || (!TA_ && std::is_same<TA, bf16_t>::value));
     if (p.bn == 64) {
         launch_shape<128, 64, 4, 1, TA_, TB_, TA, TB, TC, R1>(g, va, vb, st);
     } else {
