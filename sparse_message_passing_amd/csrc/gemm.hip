@@ -691,7 +691,7 @@ template <bool TA_, bool TB_>
 gnn_status_t launch_trans(GemmArgs& g, const Plan& p, gnn_dtype_t a, gnn_dtype_t b, gnn_dtype_t c, bool va, bool vb,
                           int r1, hipStream_t st) {
     // binary32 products with a rank-1 operand term (the host checks the types)
-    if constexpr (!TA_ && !TB_) {
+    if constexpr (!TA_) {  // B transposed too when it is too large to transpose in the workspace
         if (r1 == 1) {
             launch_types<TA_, TB_, float, float, float, 1>(g, p, va, vb, st);
             return launch_status("gnn_gemm");

@@ -355,6 +355,24 @@ def _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r):
     check_close(from_dev(dX), bw["dX"], m_dHp @ np.abs(W).T, what="GAT dX")
 
 
+def test_gat_layer_bwd_wide_weight():
+    # d_in x heads*d_head above 2^22 elements: dX = dH' W^T takes W as given
+    # (too large to transpose in the workspace first), and the dD a_dst term
+    # of dH' must still enter that product
+    s, t = hub_edges(300, 3000, 120, 47)
+    g, og = graph_pair(s, t, 300, False, csc=True)
+    heads, dh, din, slope = 8, 128, 4104, 0.2
+    assert din * heads * dh > 1 << 22
+    r = np.random.default_rng(48)
+    X = r.standard_normal((og.n, din)).astype(np.float32)
+    W = synth.glorot(din, heads * dh, 3)
+    a_s = synth.glorot(dh, 1, 4, shape=(heads, dh))
+    a_d = synth.glorot(dh, 1, 5, shape=(heads, dh))
+    fw = oracle.gat_layer_fwd(og, X, W, a_s, a_d, heads, slope)
+    saved = torch.empty(gnnmp.gnn_gat_saved_size(g, heads, dh), dtype=torch.uint8, device="cuda")
+    _check_gat_bwd(g, og, fw, X, W, a_s, a_d, heads, dh, slope, saved, r)
+
+
 def test_gat_layer_bwd_by_head_slabs():
     # H' and dY over 256 MB (300K rows x 4 heads x 64), the out-edge pass one
     # head at a time.  A hub with 5000 in-neighbours and ~5000 out-neighbours
