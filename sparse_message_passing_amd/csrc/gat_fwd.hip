@@ -20,8 +20,8 @@
 // a slab's gathered rows share the caches), a group of L = d_head / 4 lanes
 // per destination row (lane i holds features 4i..4i+3 of the head), rows in
 // degree-descending order, rows over 512 in-edges cut into chunks whose
-// partial (maximum, sum, weighted row) are merged afterwards in chunk order.
-// No atomics: bitwise reproducible.
+// partial (maximum, sum, weighted row) are merged afterwards in a fixed
+// order.  No atomics: bitwise reproducible.
 
 #include "device.h"
 #include "internal.h"
@@ -138,10 +138,15 @@ __global__ __launch_bounds__(256) void gat_fwd_kernel(GatFwdArgs a) {
     }
 }
 
-// Hub destinations: merge the chunks' (maximum, sum, weighted row) in chunk
-// order -- the maximum over the chunks, then each chunk's sum and row scaled
-// by exp(its maximum - the maximum) -- and finish the row.  One wave per
-// (hub row, head).
+// Hub destinations: merge the chunks' (maximum, sum, weighted row) -- the
+// maximum over the chunks, then each chunk's sum and row scaled by
+// exp(its maximum - the maximum) -- and finish the row.  One wave per (hub
+// row, head); a hub row has up to a few hundred chunks, so the wave's lanes
+// split them: lane l takes chunks c0 + l, c0 + l + 64, ... for the maximum
+// and the sum (then a butterfly over the wave), and for the row each of the
+// G = 64 / (d_head / 4) lane groups takes every G-th chunk for its four
+// features (then a butterfly over the groups).  A fixed order: bitwise
+// reproducible.
 __global__ __launch_bounds__(256) void gat_fwd_fixup_kernel(GatFwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t w = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -152,22 +157,30 @@ __global__ __launch_bounds__(256) void gat_fwd_fixup_kernel(GatFwdArgs a) {
     const int64_t v = a.order[i];
     const int64_t c0 = a.chunk_first[i], c1 = a.chunk_first[i + 1];
     float m = -INFINITY;
-    for (int64_t c = c0; c < c1; ++c) m = fmaxf(m, a.pmz[(c * H + k) * 2]);
+    for (int64_t c = c0 + lane; c < c1; c += 64) m = fmaxf(m, a.pmz[(c * H + k) * 2]);
+    m = group_max<64>(m);
     float z = 0.0f;
-    for (int64_t c = c0; c < c1; ++c) {
+    for (int64_t c = c0 + lane; c < c1; c += 64) {
         const float2 mz = *reinterpret_cast<const float2*>(a.pmz + (c * H + k) * 2);
         z = fmaf(mz.y, __expf(mz.x - m), z);
     }
+    z = group_sum<64>(z);
     const float zi = z > 0.0f ? 1.0f / z : 0.0f;
-    const int64_t hd = H * a.dh;
-    for (int64_t f = lane * 4; f < a.dh; f += 256) {
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int64_t c = c0; c < c1; ++c) {
-            const float sc = __expf(a.pmz[(c * H + k) * 2] - m);
-            acc = f4_fma(sc, *reinterpret_cast<const float4*>(a.part + (c * H + k) * a.dh + f), acc);
-        }
-        *reinterpret_cast<float4*>(a.Y + v * hd + k * a.dh + f) = f4_scale(acc, zi);
+    const int q = static_cast<int>(a.dh / 4);  // feature quads (d_head <= 256: q <= 64)
+    const int fq = lane % q, grp = lane / q, G = 64 / q;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int64_t c = c0 + grp; c < c1; c += G) {
+        const float sc = __expf(a.pmz[(c * H + k) * 2] - m);
+        acc = f4_fma(sc, *reinterpret_cast<const float4*>(a.part + (c * H + k) * a.dh + fq * 4), acc);
     }
+    for (int o = q; o < 64; o <<= 1) {
+        acc.x += __shfl_xor(acc.x, o);
+        acc.y += __shfl_xor(acc.y, o);
+        acc.z += __shfl_xor(acc.z, o);
+        acc.w += __shfl_xor(acc.w, o);
+    }
+    const int64_t hd = H * a.dh;
+    if (grp == 0) *reinterpret_cast<float4*>(a.Y + v * hd + k * a.dh + fq * 4) = f4_scale(acc, zi);
     if (lane == 0) {
         a.M[v * H + k] = m;
         a.Z[v * H + k] = zi;
