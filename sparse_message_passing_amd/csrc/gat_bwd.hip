@@ -35,12 +35,15 @@ namespace gnnmp {
 
 namespace {
 
-// c = <dY[v, head k], Y[v, head k]> and the record {D, m, 1/z, c} of (v, k),
-// head-major: rec[k * n + v].  One wave per row, HL = d_head / 4 lanes a head.
+// c = <dY[v, head k], Y[v, head k]> and the 12-byte record {D, m - log(1/z),
+// c} of (v, k), head-major: rec[3 (k n + v) ..].  alpha = exp(E - m) / z =
+// exp(E - (m - log(1/z))): one exponential, and a record that covers fewer
+// cache lines per gathered destination.  One wave per row, HL = d_head / 4
+// lanes a head.
 template <int HL>
 __global__ __launch_bounds__(256) void gat_rec_kernel(int64_t n, int heads, int64_t dh, const float* Y,
                                                       const float* dY, const float* D, const float* M,
-                                                      const float* Z, float4* rec) {
+                                                      const float* Z, float* rec) {
     const int lane = threadIdx.x & 63;
     const int64_t v = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (v >= n) return;
@@ -60,10 +63,17 @@ __global__ __launch_bounds__(256) void gat_rec_kernel(int64_t n, int heads, int6
         if (f < d && (lane % HL) == 0) {
             const int64_t k = f / dh;
             const int64_t i = v * heads + k;
-            rec[k * n + v] = make_float4(D[i], M[i], Z[i], c);
+            float* r = rec + (k * n + v) * 3;
+            r[0] = D[i];
+            r[1] = M[i] - __logf(Z[i]);  // Z = 1/sum > 0: v has an in-edge wherever it is read
+            r[2] = c;
         }
     }
 }
+
+struct Rec3 {
+    float x, y, z;
+};
 
 struct GatBwdArgs {
     int64_t n;
@@ -78,7 +88,7 @@ struct GatBwdArgs {
     int64_t slab_blocks;         // workgroups per head (grid = slab_blocks x heads)
     const float* Hp;             // H' [n, heads*dh]
     const float* S;              // [n, heads]
-    const float4* rec;           // [heads, n] {D, m, 1/z, c}
+    const float* rec;            // [heads, n, 3] {D, m - log(1/z), c}
     const float* dY;             // [n, heads*dh]
     const float* a_src;          // [heads, dh]
     float slope;
@@ -124,7 +134,7 @@ __global__ __launch_bounds__(256) void gat_bwd_csc_kernel(GatBwdArgs a) {
     const int64_t fo = static_cast<int64_t>(k) * a.dh + lane * 4;
     const float4 hu = *reinterpret_cast<const float4*>(a.Hp + u * hd + fo);
     const float su = a.S[u * H + k];
-    const float4* rk = a.rec + static_cast<int64_t>(k) * a.n;
+    const float* rk = a.rec + static_cast<int64_t>(k) * a.n * 3;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float dsl = 0.0f;
     for (int64_t e0 = eb; e0 < ee; e0 += L) {
@@ -134,12 +144,12 @@ __global__ __launch_bounds__(256) void gat_bwd_csc_kernel(GatBwdArgs a) {
         bool neg_my = false;
         if (lane < cnt) {
             v_my = a.idx[e0 + lane];
-            const float4 r = rk[v_my];
+            const Rec3 r = *reinterpret_cast<const Rec3*>(rk + static_cast<int64_t>(v_my) * 3);
             const float p = su + r.x;
             neg_my = a.act && !(p > 0.0f);
             const float x = neg_my ? a.slope * p : p;
-            a_my = __expf(x - r.y) * r.z;
-            c_my = r.w;
+            a_my = __expf(x - r.y);
+            c_my = r.z;
         }
         for (int j = 0; j < cnt; j += 4) {
             int vq[4];
@@ -343,7 +353,7 @@ size_t gat_fused_bwd_partial_bytes(const RowPlan& csc_plan, int heads, int64_t d
 gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const int32_t* cpos, int64_t nnz, int heads,
                                   int64_t d_head, float slope, const float* Hp, const float* S, const float* D,
                                   const float* M, const float* Z, const float* Y, const float* dY,
-                                  const float* a_src, float4* rec, float* dEh, float* dEc,
+                                  const float* a_src, float* rec, float* dEh, float* dEc,
                                   float* part, float* dS, float* dD, float* dHp, hipStream_t st) {
     const int64_t n = csr.n;
     if (n == 0) return GNN_OK;

@@ -243,7 +243,7 @@ size_t gnn_gat_workspace_size(gnn_graph_t h, int64_t d_in, int heads, int64_t d_
     // backward: dE (CSC order: per-head planes, then per-edge records), the
     // per-destination records, dD, dS, dH', the CSC pass's chunk partials,
     // the column-sum partials, the GEMM workspace
-    size_t bwd = 2 * align_up(e * heads * 4) + align_up(n * heads * 16) + 2 * align_up(n * heads * 4) +
+    size_t bwd = 2 * align_up(e * heads * 4) + align_up(n * heads * 12) + 2 * align_up(n * heads * 4) +
                  align_up(n * hd * 4) + align_up(head_colsum_partial_bytes(g.n, heads, d_head)) + align_up(gemm);
     if (g.has_csc) bwd += align_up(gat_fused_bwd_partial_bytes(g.plan[1], heads, d_head));
     return std::max(fwd, bwd);
@@ -328,7 +328,7 @@ gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     Carver c(ws);
     float* dEh = static_cast<float*>(c.take(e * heads * 4));
     float* dEc = static_cast<float*>(c.take(e * heads * 4));
-    float4* rec = static_cast<float4*>(c.take(n * heads * 16));
+    float* rec = static_cast<float*>(c.take(n * heads * 12));
     float* dD = static_cast<float*>(c.take(n * heads * 4));
     float* dS = static_cast<float*>(c.take(n * heads * 4));
     float* dHp = static_cast<float*>(c.take(n * hd * 4));
