@@ -35,6 +35,10 @@ namespace gnnmp {
 
 namespace {
 
+struct Rec3 {  // a per-destination record, stored and loaded with one 12-byte access
+    float x, y, z;
+};
+
 // c = <dY[v, head k], Y[v, head k]> and the 12-byte record {D, m - log(1/z),
 // c} of (v, k), head-major: rec[3 (k n + v) ..].  alpha = exp(E - m) / z =
 // exp(E - (m - log(1/z))): one exponential, and a record that covers fewer
@@ -63,17 +67,11 @@ __global__ __launch_bounds__(256) void gat_rec_kernel(int64_t n, int heads, int6
         if (f < d && (lane % HL) == 0) {
             const int64_t k = f / dh;
             const int64_t i = v * heads + k;
-            float* r = rec + (k * n + v) * 3;
-            r[0] = D[i];
-            r[1] = M[i] - __logf(Z[i]);  // Z = 1/sum > 0: v has an in-edge wherever it is read
-            r[2] = c;
+            // Z = 1/sum > 0 wherever the record is read (v has an in-edge there)
+            *reinterpret_cast<Rec3*>(rec + (k * n + v) * 3) = Rec3{D[i], M[i] - __logf(Z[i]), c};
         }
     }
 }
-
-struct Rec3 {
-    float x, y, z;
-};
 
 struct GatBwdArgs {
     int64_t n;
