@@ -85,7 +85,6 @@ struct GatBwdArgs {
     int64_t dh;
     int64_t slab_blocks;         // workgroups per head (grid = slab_blocks x heads)
     const float* Hp;             // H' [n, heads*dh]
-    const float* S;              // [n, heads]
     const float* rec;            // [heads, n, 3] {D, m - log(1/z), c}
     const float* dY;             // [n, heads*dh]
     const float* a_src;          // [heads, dh]
@@ -131,7 +130,15 @@ __global__ __launch_bounds__(256) void gat_bwd_csc_kernel(GatBwdArgs a) {
     const int64_t hd = H * a.dh;
     const int64_t fo = static_cast<int64_t>(k) * a.dh + lane * 4;
     const float4 hu = *reinterpret_cast<const float4*>(a.Hp + u * hd + fo);
-    const float su = a.S[u * H + k];
+    const float4 as = *reinterpret_cast<const float4*>(a.a_src + fo);
+    // S[u] = <H'[u, head k], a_src[k]> again from the row in registers, in
+    // the scores pass's order (the same bits as the saved S), instead of a
+    // scattered 4-byte read per source row
+    float su = hu.x * as.x;
+    su = fmaf(hu.y, as.y, su);
+    su = fmaf(hu.z, as.z, su);
+    su = fmaf(hu.w, as.w, su);
+    su = group_sum<L>(su);
     const float* rk = a.rec + static_cast<int64_t>(k) * a.n * 3;
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float dsl = 0.0f;
@@ -188,7 +195,6 @@ __global__ __launch_bounds__(256) void gat_bwd_csc_kernel(GatBwdArgs a) {
         return;
     }
     if (lane == 0) a.dS[u * H + k] = ds;
-    const float4 as = *reinterpret_cast<const float4*>(a.a_src + fo);
     *reinterpret_cast<float4*>(a.dHp + u * hd + fo) =
         make_float4(fmaf(ds, as.x, acc.x), fmaf(ds, as.y, acc.y), fmaf(ds, as.z, acc.z), fmaf(ds, as.w, acc.w));
 }
@@ -349,7 +355,7 @@ size_t gat_fused_bwd_partial_bytes(const RowPlan& csc_plan, int heads, int64_t d
 }
 
 gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const int32_t* cpos, int64_t nnz, int heads,
-                                  int64_t d_head, float slope, const float* Hp, const float* S, const float* D,
+                                  int64_t d_head, float slope, const float* Hp, const float* D,
                                   const float* M, const float* Z, const float* Y, const float* dY,
                                   const float* a_src, float* rec, float* dEh, float* dEc,
                                   float* part, float* dS, float* dD, float* dHp, hipStream_t st) {
@@ -388,7 +394,6 @@ gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const 
     a.heads = heads;
     a.dh = d_head;
     a.Hp = Hp;
-    a.S = S;
     a.rec = rec;
     a.dY = dY;
     a.a_src = a_src;

@@ -198,8 +198,8 @@ gnn_status_t launch_edge_softmax(const AggView& v, const float* E, float* alpha,
 bool gat_fused_bwd_supported(int heads, int64_t d_head);
 size_t gat_fused_bwd_partial_bytes(const RowPlan& csc_plan, int heads, int64_t d_head);
 gnn_status_t launch_gat_bwd_fused(const AggView& csr, const AggView& csc, const int32_t* cpos, int64_t nnz,
-                                  int heads, int64_t d_head, float slope, const float* Hp, const float* S,
-                                  const float* D, const float* M, const float* Z, const float* Y, const float* dY,
+                                  int heads, int64_t d_head, float slope, const float* Hp, const float* D,
+                                  const float* M, const float* Z, const float* Y, const float* dY,
                                   const float* a_src, float* rec, float* dEh, float* dEc,
                                   float* part, float* dS, float* dD, float* dHp, hipStream_t st);
 // GAT forward edge pass (gat_fwd.hip): per destination and head, the scores from the gathered H' rows,

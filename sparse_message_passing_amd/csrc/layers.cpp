@@ -339,8 +339,8 @@ gnn_status_t gnn_gat_layer_bwd(gnn_graph_t h, const float* X, int64_t d_in, cons
     void* gws = c.take(gemm);
     // dalpha, dE, dS and P = (G . alpha)^T dY + dS a_src in one pass over the
     // out-edges; dD in one pass over the in-edges
-    GNN_TRY(launch_gat_bwd_fused(csr_view(g), csc_view(g), g.csr_cpos, g.nnz, heads, d_head, slope, s.Hp, s.S, s.D,
-                                 s.M, s.Z, Y, dY, a_src, rec, dEh, dEc, part, dS, dD, dHp, st));
+    GNN_TRY(launch_gat_bwd_fused(csr_view(g), csc_view(g), g.csr_cpos, g.nnz, heads, d_head, slope, s.Hp, s.D, s.M,
+                                 s.Z, Y, dY, a_src, rec, dEh, dEc, part, dS, dD, dHp, st));
     // da_src = sum_v dS[v] H'[v], da_dst = sum_v dD[v] H'[v] per head
     GNN_TRY(launch_head_colsum(g.n, dS, dD, s.Hp, heads, d_head, da_src, da_dst, cps, st));
     // dW = X^T dH',  dX = dH' W^T, with dH' = P + dD a_dst (per head) formed
