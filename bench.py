@@ -189,9 +189,9 @@ def spmm_compulsory_bytes(n, nnz, d, s_in=4, s_out=4, edge_weights=True, heads=1
 
 def gat_bwd_csc_bytes(n, nnz, h, dh):
     """Per head slab: col_ptr, destination ids, the order, the H' and dY
-    slices read once, dH' slice written once, S and dS, the 12-byte
-    per-destination records, the dE plane written."""
-    return h * (8 * (n + 1) + 8 * nnz + 12 * n * dh + 24 * n)
+    slices read once, dH' slice written once, dS written (S is formed from
+    the H' row), the 12-byte per-destination records, the dE plane written."""
+    return h * (8 * (n + 1) + 8 * nnz + 12 * n * dh + 20 * n)
 
 
 def gat_fwd_bytes(n, nnz, h, dh):
